@@ -1,0 +1,213 @@
+/* sparsekv.h — C ABI of the MI355X (gfx950) sparse top-k decode step.
+ *
+ * One decode step of top-k sparse attention over a paged KV history:
+ *   score every history key for the current query      (sparsekv_score)
+ *   select an exact top-k, lowest index winning ties   (sparsekv_topk)
+ *   gather the selected K/V through the slot / block table and run softmax
+ *   attention over selected + sink + local tokens      (sparsekv_gather_attend)
+ * and ParisKV's compressed-code retrieval variant     (sparsekv_encode,
+ *                                                      sparsekv_retrieve).
+ *
+ * Conventions (all entry points)
+ * ------------------------------
+ * - Pointers inside the structs and pointer arguments are DEVICE pointers
+ *   unless marked (host).  The structs themselves are host memory, read
+ *   during the call only.
+ * - Every call only enqueues work on `stream` and returns: it never
+ *   synchronises, never allocates device memory and keeps no state between
+ *   calls.  Outputs are valid once the stream reaches them.  The caller owns
+ *   every buffer.  Temporary device memory comes from the caller through
+ *   (ws, ws_bytes); sparsekv_workspace_size() tells how much.
+ * - Errors are returned as skv_status; nothing aborts.  Host-visible
+ *   arguments are validated (null pointers, sizes, modes, workspace size).
+ *   Device-resident data is NOT validated: table entries must point inside
+ *   the pools, token-table slots of live tokens must be unique, and
+ *   0 <= lo <= hi <= seq_len <= L_max must hold for every sequence.
+ * - bf16 is the IEEE-754 binary32 upper half (uint16 storage).  Products are
+ *   accumulated in fp32; outputs are fp32.
+ *
+ * Storage layouts (skv_kv)
+ * ------------------------
+ * block == 16, block_table: paged pool [n_blocks][H][16][d], logical token t
+ *     of sequence b lives in slot block_table[b][t/16]*16 + t%16
+ *     (PagedAttention block table; vToken reading notes, background section).
+ * block == 16, token_table: the same pool addressed per token,
+ *     slot = token_table[b][t] (-1 = dead token)
+ *     (vToken reading notes, section 3.2 token table and section 3.4 Eq. (2)).
+ * block == 0: contiguous [B][H][L_max][d].
+ * In the pools the row of (slot, head h) starts at element
+ *     ((slot/16)*H + h)*16*d + (slot%16)*d.
+ * v == NULL means the value is the first d_v dims of the key row (a latent
+ * KV shared by all query heads, as in MLA: ECHO-OSDI26 wiki page, problem
+ * and motivation).
+ */
+#ifndef SPARSEKV_H
+#define SPARSEKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SKV_OK = 0,
+  SKV_EINVAL = 1,        /* bad argument (null pointer, size, mode) */
+  SKV_EUNSUPPORTED = 2,  /* valid but not implemented for this shape / dtype */
+  SKV_EWORKSPACE = 3,    /* ws_bytes below sparsekv_workspace_size() */
+  SKV_ELAUNCH = 4        /* a kernel launch failed (hipGetLastError) */
+} skv_status;
+
+typedef enum { SKV_F32 = 0, SKV_BF16 = 1 } skv_dtype;
+
+typedef enum {
+  SKV_OP_SCORE = 0,
+  SKV_OP_TOPK = 1,
+  SKV_OP_GATHER_ATTEND = 2,
+  SKV_OP_ENCODE = 3,
+  SKV_OP_RETRIEVE = 4
+} skv_op;
+
+/* Caller-owned KV storage (host struct, device pointers). */
+typedef struct {
+  const void* k;                /* pool or contiguous keys (dtype)            */
+  const void* v;                /* values, same layout as k; NULL => latent   */
+  skv_dtype dtype;
+  int32_t B, H, d_k, d_v;       /* d_v <= d_k when v == NULL                  */
+  int32_t block;                /* 16 (paged / token table) or 0 (contiguous) */
+  int32_t L_max;                /* logical capacity per sequence              */
+  const int32_t* block_table;   /* [B][L_max/16] or NULL                      */
+  const int32_t* token_table;   /* [B][L_max] slot or -1, or NULL             */
+  const int32_t* seq_len;       /* [B] logical lengths                        */
+} skv_kv;
+
+/* Per-sequence windows (device [B] arrays): candidates for top-k are the live
+ * t with lo[b] <= t < hi[b]; the sink is live t < lo[b], the local window is
+ * live t >= hi[b] (t < seq_len[b]).  ParisKV close-reading, section 2.5: sink
+ * and local regions are attended densely, the region between is searched. */
+typedef struct {
+  const int32_t* lo;
+  const int32_t* hi;
+} skv_window;
+
+/* ---------------------------------------------------------------- scoring --
+ * scores[b][h][t] = max over the G query heads g of KV head h of
+ *                   sum_j q[b][h*G+g][j] * K(b, h, t)[j]
+ * for every t < L_max; -inf where t >= seq_len[b] or the token is dead.
+ * Raw dot product, no scale (ParisKV close-reading, section 一: s_i = <k_i, q>;
+ * ECHO-OSDI26 wiki page: the indexer scores every history key before exact
+ * top-k).  With kv = an indexer key cache and G = 1 this is the indexer score.
+ *   q       [B][H*G][d_k], same dtype as kv->k
+ *   scores  [B][H][L_max] fp32 (written in full)
+ * Supports: bf16 (G <= 16, d_k % 32 == 0 uses matrix cores for G >= 2) and
+ * f32 (G <= 8); every addressing mode; d_k % 8 == 0. */
+skv_status sparsekv_score(const skv_kv* kv, const void* q, int32_t G, float* scores,
+                          hipStream_t stream);
+
+/* ------------------------------------------------------------ exact top-k --
+ * For each row (b, h) of scores [B][H][L_max]: the k largest finite scores
+ * among t in [lo[b], hi[b]), ties broken toward the lower t, -0.0 == +0.0.
+ * ECHO-OSDI26 wiki page, observation 5: the final selection is an exact
+ * top-k.  Output has set semantics, written in ascending t:
+ *   idx   [B][H][k] int32, entries past count[b][h] are -1
+ *   count [B][H]    int32 = min(k, number of finite candidates)
+ * ws may be NULL when sparsekv_workspace_size(SKV_OP_TOPK, ...) is 0. */
+skv_status sparsekv_topk(const float* scores, int32_t B, int32_t H, int32_t L_max,
+                         skv_window win, int32_t k, int32_t* idx, int32_t* count, void* ws,
+                         size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------- gather + attention --
+ * For each sequence b, KV head h and query head g:
+ *   A = {idx[b][h][i] : lo <= idx < hi, live} ∪ {live t < lo} ∪ {live t >= hi}
+ *   out[b][h*G+g] = sum_{t in A} softmax_t(scale * q . K_t) V_t
+ * ParisKV close-reading, section 一 (paper Eqs. (1)-(3)): softmax is
+ * recomputed over the full-precision KV of the chosen set; vToken reading
+ * notes, section 3.4 Eq. (2): rows are reached through the slot mapping.
+ * Computed as split-k online softmax (per split: running max, sum, weighted
+ * values) merged exactly by log-sum-exp.  idx entries of -1 are skipped.
+ *   q   [B][H*G][d_k] (kv dtype);  idx [B][H][k] int32 logical positions
+ *   out [B][H*G][d_v] fp32; an empty A gives 0.
+ * Supports d_k == d_v in {64, 128, 256} with G <= 8 (split-k vector path),
+ * and the latent case v == NULL, bf16, d_k = 576, d_v = 512, H = 1,
+ * G % 16 == 0 (matrix-core path). */
+skv_status sparsekv_gather_attend(const skv_kv* kv, const void* q, int32_t G, const int32_t* idx,
+                                  int32_t k, skv_window win, float scale, float* out, void* ws,
+                                  size_t ws_bytes, hipStream_t stream);
+
+/* --------------------------------------------- compressed-code retrieval --
+ * ParisKV close-reading, sections 2.2-2.5: keys and the query are normalised
+ * and rotated by one SRHT R = H_d diag(signs) / sqrt(d); each of n_sub
+ * subspaces of m = 8 dims stores the id of its sign-pattern centroid
+ * (2^m = 256 fixed centroids), a 4-bit code per coordinate (1 sign bit + 3
+ * magnitude bits from Lloyd-Max levels) and a correction weight
+ * w = |k| r_b / <v_b, u_b>. */
+typedef struct {                /* host struct */
+  int32_t d, n_sub, m;          /* d = n_sub * m; supported: d = 128, m = 8  */
+  const int8_t* signs;          /* device [d], +1 / -1                        */
+  float levels[8];              /* magnitude reconstruction values, ascending */
+  float thresh[7];              /* |u| >= thresh[i] moves past level i        */
+} skv_codebook;
+
+typedef struct {                /* host struct, device arrays */
+  uint8_t* ids;                 /* [H][cap][n_sub] centroid id per subspace   */
+  uint8_t* codes;               /* [H][cap][d/2]   coordinate 2c = low nibble */
+  float* w;                     /* [H][cap][n_sub] correction weights         */
+  int32_t* hist;                /* [H][n_sub][256] entries per centroid       */
+  int32_t* pos;                 /* [cap] logical position of each entry       */
+  int32_t n, cap, H;            /* n entries in use (host-side count)         */
+} skv_index;
+
+/* Fill the codebook's levels / thresholds: the library's own Lloyd-Max fixed
+ * point (float64, rounded once to fp32) for |u_j| with (u_j)^2 ~
+ * Beta(1/2, (m-1)/2) (ParisKV close-reading, section 2.4, Prop. 4.1).
+ * Host only; m in [3, 16]. */
+skv_status sparsekv_codebook_init(int32_t m, float levels[8], float thresh[7]);
+
+/* Append the keys at logical positions [t0, t1) of sequence b (contiguous or
+ * block-table kv, bf16, d_k == cb->d) of every KV head to the index as
+ * entries [index->n, index->n + t1 - t0); adds their ids to index->hist
+ * (which the caller zeroes once when the index is created) and advances the
+ * host-side index->n.  Fails with SKV_EINVAL if the index would overflow. */
+skv_status sparsekv_encode(const skv_codebook* cb, const skv_kv* kv, int32_t b, int32_t t0,
+                           int32_t t1, skv_index* index, hipStream_t stream);
+
+/* Optional intermediate outputs of a retrieval (device arrays, NULL = skip). */
+typedef struct {
+  uint8_t* votes;               /* [H][n] collision score S_i (0..6*n_sub)   */
+  int32_t* cand;                /* [H][C] candidate entry numbers, ascending  */
+  float* est;                   /* [H][C] rerank estimate of each candidate   */
+} skv_retrieve_trace;
+
+/* Collision vote + bucket top-C + 4-bit rerank + exact top-k_final.
+ *   q      [H*G][d] bf16 query heads (G per KV head)
+ *   C      = min(n, ceil(beta * n)) candidates per KV head
+ *   idx    [H][k_final] int32 logical positions (index->pos of the winners),
+ *          ascending; -1 past n_cand
+ *   n_cand [H] int32 = min(k_final, C)
+ * Tier bounds: T_rho = ceil(rho n), T_l = ceil(p_l T_rho), p = .05 .15 .30
+ * .50 .75 1.0, computed in float64 on the host (ParisKV close-reading,
+ * section 2.3, paper Eq. (15)).  Requires rho >= beta > 0. */
+skv_status sparsekv_retrieve(const skv_codebook* cb, const skv_index* index, const void* q,
+                             int32_t G, float rho, float beta, int32_t k_final, int32_t* idx,
+                             int32_t* n_cand, const skv_retrieve_trace* trace, void* ws,
+                             size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes for an op.  Arguments an op does not use may be NULL / 0:
+ *   SCORE, ENCODE: 0;   TOPK: kv->B, kv->H, kv->L_max, k;
+ *   GATHER_ATTEND: kv, G, k;   RETRIEVE: index, G, k (= k_final), and beta
+ *   through sparsekv_retrieve_workspace_size(). */
+size_t sparsekv_workspace_size(skv_op op, const skv_kv* kv, int32_t G, int32_t k,
+                               const skv_index* index);
+size_t sparsekv_retrieve_workspace_size(const skv_index* index, int32_t G, float beta,
+                                        int32_t k_final);
+
+const char* sparsekv_status_string(skv_status s);
+int32_t sparsekv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPARSEKV_H */

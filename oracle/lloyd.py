@@ -36,7 +36,7 @@ def _cells(m: int):
     return mass, moment
 
 
-def lloyd_max_abs_coord(m: int, n_levels: int = 8, tol: float = 1e-16, max_iter: int = 200000):
+def lloyd_max_abs_coord(m: int, n_levels: int = 8, tol: float = 1e-15, max_iter: int = 20000):
     """Float64 Lloyd-Max fixed point: (levels[n_levels], thresholds[n_levels-1])."""
     mass, moment = _cells(m)
     levels = (np.arange(n_levels) + 0.5) / n_levels

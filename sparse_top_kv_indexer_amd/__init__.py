@@ -1,0 +1,256 @@
+"""Python binding of libsparsekv.so (the MI355X sparse top-k decode step).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  The functions keep the C names (``sparsekv_score``,
+``sparsekv_topk``, ``sparsekv_gather_attend``, ``sparsekv_encode``,
+``sparsekv_retrieve``, ...); they take torch tensors that live on the GPU,
+check dtype / shape / contiguity, pass ``data_ptr()`` values and torch's
+current HIP stream, and raise ``SkvError`` on a non-zero status.  Nothing here
+computes on the CPU, and nothing falls back: without the built library every
+call raises.
+
+torch is imported before the library is loaded so that the process has a
+single HIP runtime (torch's); the library resolves its HIP symbols against it.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsparsekv.so")
+
+SKV_OK, SKV_EINVAL, SKV_EUNSUPPORTED, SKV_EWORKSPACE, SKV_ELAUNCH = range(5)
+SKV_F32, SKV_BF16 = 0, 1
+SKV_OP_SCORE, SKV_OP_TOPK, SKV_OP_GATHER_ATTEND, SKV_OP_ENCODE, SKV_OP_RETRIEVE = range(5)
+
+c_vp, c_i32, c_f32, c_sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+
+
+class SkvError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__("%s failed: %s (status %d)" % (fn, msg, status))
+        self.status = status
+
+
+class skv_kv(ctypes.Structure):
+    _fields_ = [("k", c_vp), ("v", c_vp), ("dtype", ctypes.c_int), ("B", c_i32), ("H", c_i32),
+                ("d_k", c_i32), ("d_v", c_i32), ("block", c_i32), ("L_max", c_i32),
+                ("block_table", c_vp), ("token_table", c_vp), ("seq_len", c_vp)]
+
+
+class skv_window(ctypes.Structure):
+    _fields_ = [("lo", c_vp), ("hi", c_vp)]
+
+
+class skv_codebook(ctypes.Structure):
+    _fields_ = [("d", c_i32), ("n_sub", c_i32), ("m", c_i32), ("signs", c_vp),
+                ("levels", c_f32 * 8), ("thresh", c_f32 * 7)]
+
+
+class skv_index(ctypes.Structure):
+    _fields_ = [("ids", c_vp), ("codes", c_vp), ("w", c_vp), ("hist", c_vp), ("pos", c_vp),
+                ("n", c_i32), ("cap", c_i32), ("H", c_i32)]
+
+
+class skv_retrieve_trace(ctypes.Structure):
+    _fields_ = [("votes", c_vp), ("cand", c_vp), ("est", c_vp)]
+
+
+# symbol -> (restype, argtypes)
+_SIGS = {
+    "sparsekv_score": (c_i32, [ctypes.POINTER(skv_kv), c_vp, c_i32, c_vp, c_vp]),
+    "sparsekv_topk": (c_i32, [c_vp, c_i32, c_i32, c_i32, skv_window, c_i32, c_vp, c_vp, c_vp,
+                              c_sz, c_vp]),
+    "sparsekv_gather_attend": (c_i32, [ctypes.POINTER(skv_kv), c_vp, c_i32, c_vp, c_i32,
+                                       skv_window, c_f32, c_vp, c_vp, c_sz, c_vp]),
+    "sparsekv_codebook_init": (c_i32, [c_i32, ctypes.POINTER(c_f32), ctypes.POINTER(c_f32)]),
+    "sparsekv_encode": (c_i32, [ctypes.POINTER(skv_codebook), ctypes.POINTER(skv_kv), c_i32,
+                                c_i32, c_i32, ctypes.POINTER(skv_index), c_vp]),
+    "sparsekv_retrieve": (c_i32, [ctypes.POINTER(skv_codebook), ctypes.POINTER(skv_index), c_vp,
+                                  c_i32, c_f32, c_f32, c_i32, c_vp, c_vp,
+                                  ctypes.POINTER(skv_retrieve_trace), c_vp, c_sz, c_vp]),
+    "sparsekv_workspace_size": (c_sz, [ctypes.c_int, ctypes.POINTER(skv_kv), c_i32, c_i32,
+                                       ctypes.POINTER(skv_index)]),
+    "sparsekv_retrieve_workspace_size": (c_sz, [ctypes.POINTER(skv_index), c_i32, c_f32, c_i32]),
+    "sparsekv_status_string": (ctypes.c_char_p, [c_i32]),
+    "sparsekv_version": (c_i32, []),
+}
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libsparsekv.so is not built (run __graft_entry__.build()); "
+                               "there is no fallback path")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype, f.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, st: int):
+    if st != SKV_OK:
+        raise SkvError(fn, st, lib().sparsekv_status_string(st).decode())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None):
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    return t
+
+
+# ---------------------------------------------------------------------------
+@dataclass
+class KVTensors:
+    """Device-resident KV storage matching skv_kv."""
+    k: torch.Tensor
+    v: Optional[torch.Tensor]
+    dtype: str          # "bf16" | "f32"
+    B: int
+    H: int
+    d_k: int
+    d_v: int
+    block: int
+    L_max: int
+    block_table: Optional[torch.Tensor]
+    token_table: Optional[torch.Tensor]
+    seq_len: torch.Tensor
+
+    @property
+    def torch_dtype(self):
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+    def c(self) -> skv_kv:
+        td = self.torch_dtype
+        _dev(self.k, "k", td)
+        if self.v is not None:
+            _dev(self.v, "v", td)
+        _dev(self.seq_len, "seq_len", torch.int32)
+        for nm in ("block_table", "token_table"):
+            t = getattr(self, nm)
+            if t is not None:
+                _dev(t, nm, torch.int32)
+        return skv_kv(_ptr(self.k), _ptr(self.v), SKV_BF16 if self.dtype == "bf16" else SKV_F32,
+                      self.B, self.H, self.d_k, self.d_v, self.block, self.L_max,
+                      _ptr(self.block_table), _ptr(self.token_table), _ptr(self.seq_len))
+
+
+def to_device(arr: np.ndarray, device, bf16: bool = False) -> torch.Tensor:
+    """Host array -> contiguous device tensor (uint16 bf16 bits -> torch.bfloat16)."""
+    a = np.ascontiguousarray(arr)
+    if bf16:
+        return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(a).to(device)
+
+
+def kv_to_device(kv, device="cuda") -> KVTensors:
+    """Upload any object with the skv_kv fields (numpy arrays) to the GPU."""
+    bf = kv.dtype == "bf16"
+    opt = lambda x: None if x is None else to_device(np.asarray(x, np.int32), device)
+    return KVTensors(k=to_device(kv.k, device, bf), v=None if kv.v is None else to_device(kv.v, device, bf),
+                     dtype=kv.dtype, B=kv.B, H=kv.H, d_k=kv.d_k, d_v=kv.d_v, block=kv.block,
+                     L_max=kv.L_max, block_table=opt(kv.block_table), token_table=opt(kv.token_table),
+                     seq_len=opt(kv.seq_len))
+
+
+# ---------------------------------------------------------------------------
+def sparsekv_score(kv: KVTensors, q: torch.Tensor, G: int, scores: Optional[torch.Tensor] = None):
+    """scores[b][h][t] = max_g q[b][h*G+g] . K(b,h,t)  (fp32, -inf for dead / past seq_len)."""
+    _dev(q, "q", kv.torch_dtype)
+    if q.shape != (kv.B, kv.H * G, kv.d_k):
+        raise ValueError("q must be [B][H*G][d_k]")
+    if scores is None:
+        scores = torch.empty((kv.B, kv.H, kv.L_max), dtype=torch.float32, device=q.device)
+    _dev(scores, "scores", torch.float32)
+    c = kv.c()
+    _check("sparsekv_score", lib().sparsekv_score(ctypes.byref(c), _ptr(q), G, _ptr(scores), _stream()))
+    return scores
+
+
+def sparsekv_topk(scores: torch.Tensor, lo: torch.Tensor, hi: torch.Tensor, k: int,
+                  idx: Optional[torch.Tensor] = None, count: Optional[torch.Tensor] = None,
+                  ws: Optional[torch.Tensor] = None):
+    """Exact top-k per row, ascending positions, -1 padded; returns (idx, count)."""
+    _dev(scores, "scores", torch.float32)
+    B, H, L = scores.shape
+    _dev(lo, "lo", torch.int32)
+    _dev(hi, "hi", torch.int32)
+    if idx is None:
+        idx = torch.empty((B, H, k), dtype=torch.int32, device=scores.device)
+    if count is None:
+        count = torch.empty((B, H), dtype=torch.int32, device=scores.device)
+    _dev(idx, "idx", torch.int32)
+    _dev(count, "count", torch.int32)
+    wsz = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("sparsekv_topk", lib().sparsekv_topk(_ptr(scores), B, H, L, skv_window(_ptr(lo), _ptr(hi)),
+                                                 k, _ptr(idx), _ptr(count), _ptr(ws), wsz, _stream()))
+    return idx, count
+
+
+def sparsekv_workspace_size(op: int, kv: Optional[KVTensors], G: int, k: int, index=None) -> int:
+    c = kv.c() if kv is not None else None
+    return int(lib().sparsekv_workspace_size(op, ctypes.byref(c) if c is not None else None, G, k,
+                                             ctypes.byref(index) if index is not None else None))
+
+
+def sparsekv_gather_attend(kv: KVTensors, q: torch.Tensor, G: int, idx: Optional[torch.Tensor], k: int,
+                           lo: torch.Tensor, hi: torch.Tensor, scale: float,
+                           out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None):
+    """out[b][h*G+g] = softmax attention over selected + sink + local (fp32)."""
+    _dev(q, "q", kv.torch_dtype)
+    if idx is not None:
+        _dev(idx, "idx", torch.int32)
+    if out is None:
+        out = torch.empty((kv.B, kv.H * G, kv.d_v), dtype=torch.float32, device=q.device)
+    _dev(out, "out", torch.float32)
+    if ws is None:
+        n = sparsekv_workspace_size(SKV_OP_GATHER_ATTEND, kv, G, k)
+        ws = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    c = kv.c()
+    _check("sparsekv_gather_attend",
+           lib().sparsekv_gather_attend(ctypes.byref(c), _ptr(q), G, _ptr(idx), k,
+                                        skv_window(_ptr(lo), _ptr(hi)), float(scale), _ptr(out),
+                                        _ptr(ws), ws.numel() * ws.element_size(), _stream()))
+    return out
+
+
+def sparsekv_codebook_init(m: int):
+    """(levels[8], thresh[7]) as float32 numpy arrays, from the library's own
+    Lloyd-Max derivation (host only)."""
+    lv = (c_f32 * 8)()
+    th = (c_f32 * 7)()
+    _check("sparsekv_codebook_init", lib().sparsekv_codebook_init(m, lv, th))
+    return np.array(lv[:], np.float32), np.array(th[:], np.float32)
+
+
+def sparsekv_status_string(s: int) -> str:
+    return lib().sparsekv_status_string(s).decode()
+
+
+def sparsekv_version() -> int:
+    return int(lib().sparsekv_version())

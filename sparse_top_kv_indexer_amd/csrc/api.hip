@@ -1,0 +1,143 @@
+// C ABI of the sparse decode step: argument validation, workspace sizing and
+// kernel launches.  Every entry point only enqueues on the caller's stream.
+#include <math.h>
+
+#include <algorithm>
+
+#include "../../include/sparsekv.h"
+#include "skv_internal.h"
+
+using namespace skv;
+
+namespace {
+
+bool kv_ok(const skv_kv* kv) {
+  if (!kv || !kv->k || !kv->seq_len) return false;
+  if (kv->dtype != SKV_F32 && kv->dtype != SKV_BF16) return false;
+  if (kv->B < 1 || kv->H < 1 || kv->L_max < 1) return false;
+  if (kv->d_k < 8 || kv->d_k % 8 || kv->d_v < 1) return false;
+  if (kv->block == 0) {
+    if (kv->block_table || kv->token_table) return false;
+  } else if (kv->block == 16) {
+    if ((kv->block_table == nullptr) == (kv->token_table == nullptr)) return false;
+    if (kv->L_max % 16) return false;
+  } else {
+    return false;
+  }
+  if (kv->v == nullptr && kv->d_v > kv->d_k) return false;
+  if (kv->v != nullptr && kv->d_v != kv->d_k) return false;
+  return true;
+}
+
+KvArgs to_args(const skv_kv* kv) {
+  KvArgs a;
+  a.k = kv->k;
+  a.v = kv->v;
+  a.bf16 = kv->dtype == SKV_BF16;
+  a.B = kv->B;
+  a.H = kv->H;
+  a.d_k = kv->d_k;
+  a.d_v = kv->d_v;
+  a.block = kv->block;
+  a.L_max = kv->L_max;
+  a.block_table = kv->block_table;
+  a.token_table = kv->token_table;
+  a.seq_len = kv->seq_len;
+  return a;
+}
+
+bool score_supported(const skv_kv* kv, int G) {
+  if (kv->dtype == SKV_BF16) {
+    if (G >= 2 && G <= 16 && kv->d_k % 32 == 0) {
+      const int nc = kv->d_k / 32;
+      return nc == 2 || nc == 4 || nc == 8 || nc == 18;
+    }
+    const int npl = (kv->d_k / 8 + 15) / 16;
+    if (npl == 1) return G <= 8;
+    if (npl == 2) return G <= 4;
+    if (npl <= 5) return G == 1;
+    return false;
+  }
+  const int npl = (kv->d_k / 4 + 15) / 16;
+  if (npl <= 2) return G <= 8;
+  if (npl <= 4) return G <= 2;
+  return false;
+}
+
+skv_status launched(hipError_t e) {
+  if (e == hipErrorInvalidValue) return SKV_EUNSUPPORTED;
+  return e == hipSuccess ? SKV_OK : SKV_ELAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+skv_status sparsekv_score(const skv_kv* kv, const void* q, int32_t G, float* scores,
+                          hipStream_t stream) {
+  if (!kv_ok(kv) || !q || !scores || G < 1) return SKV_EINVAL;
+  if (!score_supported(kv, G)) return SKV_EUNSUPPORTED;
+  return launched(launch_score(to_args(kv), q, G, scores, stream));
+}
+
+skv_status sparsekv_topk(const float* scores, int32_t B, int32_t H, int32_t L_max,
+                         skv_window win, int32_t k, int32_t* idx, int32_t* count, void* ws,
+                         size_t ws_bytes, hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (!scores || !idx || !count || !win.lo || !win.hi) return SKV_EINVAL;
+  if (B < 1 || H < 1 || L_max < 1 || k < 1) return SKV_EINVAL;
+  return launched(launch_topk(scores, B * H, H, L_max, win.lo, win.hi, k, idx, count, stream));
+}
+
+skv_status sparsekv_gather_attend(const skv_kv* kv, const void* q, int32_t G, const int32_t* idx,
+                                  int32_t k, skv_window win, float scale, float* out, void* ws,
+                                  size_t ws_bytes, hipStream_t stream) {
+  if (!kv_ok(kv) || !q || !out || G < 1 || k < 0 || (k > 0 && !idx)) return SKV_EINVAL;
+  if (!win.lo || !win.hi || !isfinite(scale)) return SKV_EINVAL;
+  const KvArgs a = to_args(kv);
+  if (kv->v == nullptr) {
+    if (!mla_supported(a, G)) return SKV_EUNSUPPORTED;
+    const size_t need = mla_workspace_bytes(a, G, k);
+    if (need && (!ws || ws_bytes < need)) return SKV_EWORKSPACE;
+    return launched(launch_mla_attend(a, q, G, idx, k, win.lo, win.hi, scale, out, ws, ws_bytes,
+                                      stream));
+  }
+  if (!attend_supported(a, G)) return SKV_EUNSUPPORTED;
+  const size_t need = attend_workspace_bytes(a, G, k);
+  if (!ws || ws_bytes < need) return SKV_EWORKSPACE;
+  return launched(
+      launch_gather_attend(a, q, G, idx, k, win.lo, win.hi, scale, out, ws, ws_bytes, stream));
+}
+
+size_t sparsekv_workspace_size(skv_op op, const skv_kv* kv, int32_t G, int32_t k,
+                               const skv_index* index) {
+  switch (op) {
+    case SKV_OP_SCORE:
+    case SKV_OP_TOPK:
+    case SKV_OP_ENCODE:
+      return 0;
+    case SKV_OP_GATHER_ATTEND:
+      if (!kv_ok(kv) || G < 1 || k < 0) return 0;
+      if (kv->v == nullptr) return mla_workspace_bytes(to_args(kv), G, k);
+      return attend_workspace_bytes(to_args(kv), G, k);
+    case SKV_OP_RETRIEVE:
+      return sparsekv_retrieve_workspace_size(index, G, 1.0f, k);
+  }
+  return 0;
+}
+
+const char* sparsekv_status_string(skv_status s) {
+  switch (s) {
+    case SKV_OK: return "ok";
+    case SKV_EINVAL: return "invalid argument";
+    case SKV_EUNSUPPORTED: return "unsupported shape or dtype";
+    case SKV_EWORKSPACE: return "workspace too small";
+    case SKV_ELAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+int32_t sparsekv_version(void) { return 1; }
+
+}  // extern "C"

@@ -1,0 +1,282 @@
+// Gather + split-k sparse attention and the exact split merge.
+//
+// What is computed, for each sequence b, KV head h and query head g:
+//   A   = {idx[b][h][i] in [lo, hi), live} ∪ {live t < lo} ∪ {live t >= hi}
+//   out = sum_{t in A} softmax_t(scale q.K_t) V_t
+// ParisKV close-reading, section 一 (paper Eqs. (1)-(3)): softmax is
+// recomputed over the full-precision KV of the selected set; section 2.5:
+// sink and local regions are attended densely next to the retrieved set.
+// Rows are reached through the slot mapping (vToken reading notes, section
+// 3.4, Eq. (2)).
+//
+// gfx950 design.  The positions of A form a virtual list
+// [idx[0..k) | 0..lo-1 | hi..seq_len-1] that is cut into n_split contiguous
+// splits; a 256-thread workgroup owns one (b, h, split).  Inside it, sixteen
+// 16-lane rows each stream their own tokens (16 B of K and 16 B of V per lane
+// for d = 128 bf16), finish the G dot products with a DPP butterfly and keep a
+// running (max, sum, weighted values) per query head in the log2 domain.  The
+// rows and waves are merged by log-sum-exp at the end and written as one
+// partial per split; attend_reduce_kernel merges the splits exactly.
+#include "skv_device.h"
+
+namespace skv {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRows = kThreads / 16;   // 16-lane rows per workgroup
+
+__device__ __forceinline__ u32x4_t ld16(const char* p) { return *(const u32x4_t*)p; }
+
+template <bool BF16>
+__device__ __forceinline__ void unpack(const u32x4_t w, float* f) {
+  if constexpr (BF16) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f[2 * e] = bf16_lo(w[e]);
+      f[2 * e + 1] = bf16_hi(w[e]);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f[e] = __uint_as_float(w[e]);
+  }
+}
+
+// Merge (m2, l2, a2) into (m1, l1, a1); log2-domain maxima, -inf = empty.
+__device__ __forceinline__ void lse_merge(float& m1, float& l1, float* a1, float m2, float l2,
+                                          const float* a2, int n) {
+  const float m = fmaxf(m1, m2);
+  if (m == -INFINITY) return;
+  const float c1 = exp2f(m1 - m), c2 = exp2f(m2 - m);
+  l1 = l1 * c1 + l2 * c2;
+  for (int i = 0; i < n; ++i) a1[i] = a1[i] * c1 + a2[i] * c2;
+  m1 = m;
+}
+
+template <bool BF16, int NPL, int GMAX>
+__global__ __launch_bounds__(kThreads) void attend_split_kernel(
+    KvArgs kv, const void* qv, int G, const int32_t* idx, int k, const int32_t* lo_p,
+    const int32_t* hi_p, float scale_log2, int n_split, float* part) {
+  constexpr int E = BF16 ? 8 : 4;
+  constexpr int ES = BF16 ? 2 : 4;
+  constexpr int PE = NPL * E;            // elements of a row held by one lane
+  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int p = lane & 15;
+  const int row = wave * 4 + (lane >> 4);
+  const int D = kv.d_k;
+
+  float qr[GMAX][PE];
+#pragma unroll
+  for (int g = 0; g < GMAX; ++g)
+#pragma unroll
+    for (int r = 0; r < NPL; ++r) {
+      const bool on = g < G;
+      const char* src = (const char*)qv +
+          ((((int64_t)b * kv.H + h) * G + (on ? g : 0)) * D + (p + 16 * r) * E) * ES;
+      u32x4_t w = on ? ld16(src) : u32x4_t{0, 0, 0, 0};
+      unpack<BF16>(w, &qr[g][r * E]);
+    }
+
+  const int seq = kv.seq_len[b];
+  const int lo = max(0, min(lo_p[b], seq));
+  const int hi = max(lo, min(hi_p[b], seq));
+  const int n_list = k + lo + (seq - hi);
+  const int chunk = (n_list + n_split - 1) / n_split;
+  const int p0 = s * chunk, p1 = min(n_list, p0 + chunk);
+  const int32_t* irow = idx + ((int64_t)b * kv.H + h) * k;
+
+  float m[GMAX], l[GMAX], acc[GMAX][PE];
+#pragma unroll
+  for (int g = 0; g < GMAX; ++g) {
+    m[g] = -INFINITY;
+    l[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < PE; ++e) acc[g][e] = 0.f;
+  }
+
+  const char* kb = (const char*)kv.k;
+  const char* vb = (const char*)kv.v;
+  for (int pos = p0 + row; pos < p1; pos += kRows) {
+    int t;
+    if (pos < k) {
+      t = irow[pos];
+      if (t < lo || t >= hi) t = -1;
+    } else if (pos - k < lo) {
+      t = pos - k;
+    } else {
+      t = hi + (pos - k - lo);
+    }
+    const int64_t slot = t >= 0 ? slot_of(kv, b, t) : -1;
+    if (slot < 0) continue;               // uniform within the 16-lane row
+    const int64_t base = row_elem(kv, b, h, slot, D);
+    u32x4_t kd[NPL], vd[NPL];
+#pragma unroll
+    for (int r = 0; r < NPL; ++r) {
+      kd[r] = ld16(kb + (base + (p + 16 * r) * E) * ES);
+      vd[r] = ld16(vb + (base + (p + 16 * r) * E) * ES);
+    }
+    float kf[PE], vf[PE];
+#pragma unroll
+    for (int r = 0; r < NPL; ++r) {
+      unpack<BF16>(kd[r], &kf[r * E]);
+      unpack<BF16>(vd[r], &vf[r * E]);
+    }
+#pragma unroll
+    for (int g = 0; g < GMAX; ++g) {
+      if (g >= G) break;
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < PE; ++e) d = fmaf(qr[g][e], kf[e], d);
+      const float z = row16_sum(d) * scale_log2;
+      const float mn = fmaxf(m[g], z);
+      const float corr = exp2f(m[g] - mn);   // 0 when m was -inf
+      const float pz = exp2f(z - mn);
+      l[g] = l[g] * corr + pz;
+#pragma unroll
+      for (int e = 0; e < PE; ++e) acc[g][e] = fmaf(pz, vf[e], acc[g][e] * corr);
+      m[g] = mn;
+    }
+  }
+
+  // merge the four rows of each wave (lanes p, p+16, p+32, p+48)
+#pragma unroll
+  for (int g = 0; g < GMAX; ++g) {
+    if (g >= G) break;
+#pragma unroll
+    for (int x = 16; x <= 32; x <<= 1) {
+      const float m2 = __shfl_xor(m[g], x, 64);
+      const float l2 = __shfl_xor(l[g], x, 64);
+      float a2[PE];
+#pragma unroll
+      for (int e = 0; e < PE; ++e) a2[e] = __shfl_xor(acc[g][e], x, 64);
+      lse_merge(m[g], l[g], acc[g], m2, l2, a2, PE);
+    }
+  }
+
+  // merge the four waves through LDS: [wave][g][D + 2]
+  extern __shared__ float red[];
+  const int stride = D + 2;
+  if ((lane >> 4) == 0) {
+#pragma unroll
+    for (int g = 0; g < GMAX; ++g) {
+      if (g >= G) break;
+      float* dst = red + ((size_t)wave * G + g) * stride;
+#pragma unroll
+      for (int r = 0; r < NPL; ++r)
+#pragma unroll
+        for (int e = 0; e < E; ++e) dst[(p + 16 * r) * E + e] = acc[g][r * E + e];
+      if (p == 0) {
+        dst[D] = m[g];
+        dst[D + 1] = l[g];
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < G * D; i += kThreads) {
+    const int g = i / D, j = i - g * D;
+    float mm = -INFINITY;
+    for (int w = 0; w < 4; ++w) mm = fmaxf(mm, red[((size_t)w * G + g) * stride + D]);
+    float ll = 0.f, aa = 0.f;
+    if (mm != -INFINITY) {
+      for (int w = 0; w < 4; ++w) {
+        const float* src = red + ((size_t)w * G + g) * stride;
+        const float c = exp2f(src[D] - mm);
+        ll += src[D + 1] * c;
+        aa += src[j] * c;
+      }
+    }
+    float* dst = part + ((((int64_t)b * kv.H + h) * G + g) * n_split + s) * stride;
+    dst[j] = aa;
+    if (j == 0) {
+      dst[D] = mm;
+      dst[D + 1] = ll;
+    }
+  }
+}
+
+// out[b][hq][j] = sum_s acc_s[j] 2^(m_s - M) / sum_s l_s 2^(m_s - M)
+__global__ __launch_bounds__(256) void attend_reduce_kernel(const float* part, int n_split, int D,
+                                                           int HG, float* out) {
+  const int hq = blockIdx.x, b = blockIdx.y;
+  const int stride = D + 2;
+  const float* base = part + ((int64_t)b * HG + hq) * n_split * stride;
+  float M = -INFINITY;
+  for (int s = 0; s < n_split; ++s) M = fmaxf(M, base[s * stride + D]);
+  for (int j = threadIdx.x; j < D; j += blockDim.x) {
+    float L = 0.f, a = 0.f;
+    if (M != -INFINITY) {
+      for (int s = 0; s < n_split; ++s) {
+        const float* ps = base + s * stride;
+        const float c = exp2f(ps[D] - M);
+        L += ps[D + 1] * c;
+        a += ps[j] * c;
+      }
+    }
+    out[((int64_t)b * HG + hq) * D + j] = L > 0.f ? a / L : 0.f;
+  }
+}
+
+template <bool BF16, int NPL>
+hipError_t launch_split(const KvArgs& kv, const void* q, int G, const int32_t* idx, int k,
+                        const int32_t* lo, const int32_t* hi, float scale_log2, int n_split,
+                        float* part, hipStream_t st) {
+  dim3 grid(n_split, kv.H, kv.B);
+  const size_t lds = (size_t)4 * G * (kv.d_k + 2) * sizeof(float);
+  if (G == 1)
+    attend_split_kernel<BF16, NPL, 1><<<grid, kThreads, lds, st>>>(kv, q, G, idx, k, lo, hi, scale_log2, n_split, part);
+  else if (G == 2)
+    attend_split_kernel<BF16, NPL, 2><<<grid, kThreads, lds, st>>>(kv, q, G, idx, k, lo, hi, scale_log2, n_split, part);
+  else if (G <= 4)
+    attend_split_kernel<BF16, NPL, 4><<<grid, kThreads, lds, st>>>(kv, q, G, idx, k, lo, hi, scale_log2, n_split, part);
+  else if (G <= 8 && NPL == 1)
+    attend_split_kernel<BF16, NPL, (NPL == 1 ? 8 : 4)><<<grid, kThreads, lds, st>>>(kv, q, G, idx, k, lo, hi, scale_log2, n_split, part);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+int pieces_per_lane(const KvArgs& kv) {
+  const int E = kv.bf16 ? 8 : 4;
+  if (kv.d_k % (16 * E)) return 0;
+  return kv.d_k / (16 * E);
+}
+
+}  // namespace
+
+int attend_num_splits(int k) { return std::max(1, std::min(64, (k + 511) / 128)); }
+
+bool attend_supported(const KvArgs& kv, int G) {
+  if (kv.v == nullptr || kv.d_k != kv.d_v) return false;
+  const int npl = pieces_per_lane(kv);
+  if (npl != 1 && npl != 2) return false;
+  if (G < 1 || G > 8 || (npl == 2 && G > 4)) return false;
+  return true;
+}
+
+size_t attend_workspace_bytes(const KvArgs& kv, int G, int k) {
+  return (size_t)kv.B * kv.H * G * attend_num_splits(k) * (kv.d_v + 2) * sizeof(float);
+}
+
+hipError_t launch_gather_attend(const KvArgs& kv, const void* q, int G, const int32_t* idx, int k,
+                                const int32_t* lo, const int32_t* hi, float scale, float* out,
+                                void* ws, size_t ws_bytes, hipStream_t st) {
+  const int n_split = attend_num_splits(k);
+  float* part = (float*)ws;
+  const float scale_log2 = scale * 1.4426950408889634f;
+  hipError_t e;
+  const int npl = pieces_per_lane(kv);
+  if (kv.bf16)
+    e = npl == 1 ? launch_split<true, 1>(kv, q, G, idx, k, lo, hi, scale_log2, n_split, part, st)
+                 : launch_split<true, 2>(kv, q, G, idx, k, lo, hi, scale_log2, n_split, part, st);
+  else
+    e = npl == 1 ? launch_split<false, 1>(kv, q, G, idx, k, lo, hi, scale_log2, n_split, part, st)
+                 : launch_split<false, 2>(kv, q, G, idx, k, lo, hi, scale_log2, n_split, part, st);
+  if (e != hipSuccess) return e;
+  dim3 grid(kv.H * G, kv.B);
+  attend_reduce_kernel<<<grid, 128, 0, st>>>(part, n_split, kv.d_v, kv.H * G, out);
+  (void)ws_bytes;
+  return hipGetLastError();
+}
+
+}  // namespace skv

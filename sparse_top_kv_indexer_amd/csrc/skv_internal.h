@@ -1,0 +1,45 @@
+// Internal launch interface between the C-ABI layer (api.hip) and the kernel
+// files.  Plain structs passed to kernels by value.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace skv {
+
+struct KvArgs {
+  const void* k;
+  const void* v;        // nullptr => value = first d_v dims of the key row
+  int bf16;             // 1: bf16 storage, 0: fp32
+  int B, H, d_k, d_v;
+  int block;            // 16 or 0
+  int L_max;
+  const int32_t* block_table;
+  const int32_t* token_table;
+  const int32_t* seq_len;
+};
+
+// score.hip
+hipError_t launch_score(const KvArgs& kv, const void* q, int G, float* scores, hipStream_t s);
+
+// topk.hip
+hipError_t launch_topk(const float* scores, int rows, int H, int L_max, const int32_t* lo,
+                       const int32_t* hi, int k, int32_t* idx, int32_t* count, hipStream_t s);
+
+// attend.hip
+int attend_num_splits(int k);
+size_t attend_workspace_bytes(const KvArgs& kv, int G, int k);
+hipError_t launch_gather_attend(const KvArgs& kv, const void* q, int G, const int32_t* idx, int k,
+                                const int32_t* lo, const int32_t* hi, float scale, float* out,
+                                void* ws, size_t ws_bytes, hipStream_t s);
+bool attend_supported(const KvArgs& kv, int G);
+
+// mla.hip: shared-latent attention on matrix cores (v == nullptr)
+bool mla_supported(const KvArgs& kv, int G);
+size_t mla_workspace_bytes(const KvArgs& kv, int G, int k);
+hipError_t launch_mla_attend(const KvArgs& kv, const void* q, int G, const int32_t* idx, int k,
+                             const int32_t* lo, const int32_t* hi, float scale, float* out,
+                             void* ws, size_t ws_bytes, hipStream_t s);
+
+}  // namespace skv

@@ -1,0 +1,112 @@
+"""Boundary checks that need no GPU: the library loads, exports every entry
+point the header declares, validates host-visible arguments, and its own
+codebook derivation agrees bit for bit with the oracle's."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import sparse_top_kv_indexer_amd as S
+from oracle import lloyd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparsekv.h")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(sparsekv_\w+)\s*\(", txt)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert "sparsekv_score" in names and "sparsekv_retrieve" in names
+    L = ctypes.CDLL(S.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+    # the binding wraps the same names
+    for n in ("sparsekv_score", "sparsekv_topk", "sparsekv_gather_attend",
+              "sparsekv_codebook_init", "sparsekv_status_string", "sparsekv_version"):
+        assert callable(getattr(S, n))
+    assert set(S._SIGS) == set(names)
+
+
+def test_status_strings():
+    assert S.sparsekv_status_string(0) == "ok"
+    assert S.sparsekv_status_string(1) == "invalid argument"
+    assert S.sparsekv_status_string(3) == "workspace too small"
+    assert S.sparsekv_version() >= 1
+
+
+@pytest.mark.parametrize("m", [3, 4, 8])
+def test_codebook_matches_oracle_bits(m):
+    lv, th = S.sparsekv_codebook_init(m)
+    olv, oth = lloyd.codebook_f32(m)
+    assert lv.view(np.uint32).tolist() == olv.view(np.uint32).tolist()
+    assert th.view(np.uint32).tolist() == oth.view(np.uint32).tolist()
+
+
+def test_codebook_rejects_bad_m():
+    lv = (ctypes.c_float * 8)()
+    th = (ctypes.c_float * 7)()
+    assert S.lib().sparsekv_codebook_init(2, lv, th) == S.SKV_EINVAL
+
+
+def _kv(**over):
+    base = dict(k=1, v=1, dtype=S.SKV_BF16, B=1, H=1, d_k=128, d_v=128, block=0, L_max=64,
+                block_table=None, token_table=None, seq_len=1)
+    base.update(over)
+    return S.skv_kv(**base)
+
+
+@pytest.mark.parametrize("over", [dict(k=None), dict(seq_len=None), dict(B=0), dict(d_k=12),
+                                  dict(block=8), dict(block=16, L_max=64),
+                                  dict(block=0, block_table=1), dict(dtype=7),
+                                  dict(block=16, block_table=1, token_table=1),
+                                  dict(d_v=64)])
+def test_score_rejects_bad_kv_without_launching(over):
+    kv = _kv(**over)
+    st = S.lib().sparsekv_score(ctypes.byref(kv), ctypes.c_void_p(1), 1, ctypes.c_void_p(1), None)
+    assert st == S.SKV_EINVAL
+
+
+def test_argument_validation_paths():
+    L = S.lib()
+    kv = _kv()
+    assert L.sparsekv_score(ctypes.byref(kv), None, 1, ctypes.c_void_p(1), None) == S.SKV_EINVAL
+    assert L.sparsekv_score(ctypes.byref(kv), ctypes.c_void_p(1), 0, ctypes.c_void_p(1), None) == S.SKV_EINVAL
+    assert L.sparsekv_score(ctypes.byref(kv), ctypes.c_void_p(1), 64, ctypes.c_void_p(1), None) == S.SKV_EUNSUPPORTED
+    win = S.skv_window(ctypes.c_void_p(1), ctypes.c_void_p(1))
+    assert L.sparsekv_topk(None, 1, 1, 64, win, 4, ctypes.c_void_p(1), ctypes.c_void_p(1), None, 0, None) == S.SKV_EINVAL
+    assert L.sparsekv_topk(ctypes.c_void_p(1), 1, 1, 64, win, 0, ctypes.c_void_p(1), ctypes.c_void_p(1), None, 0, None) == S.SKV_EINVAL
+    bad_win = S.skv_window(None, ctypes.c_void_p(1))
+    assert L.sparsekv_topk(ctypes.c_void_p(1), 1, 1, 64, bad_win, 4, ctypes.c_void_p(1), ctypes.c_void_p(1), None, 0, None) == S.SKV_EINVAL
+    # gather_attend: missing / undersized workspace is reported before any launch
+    need = L.sparsekv_workspace_size(S.SKV_OP_GATHER_ATTEND, ctypes.byref(kv), 4, 256, None)
+    assert need > 0
+    st = L.sparsekv_gather_attend(ctypes.byref(kv), ctypes.c_void_p(1), 4, ctypes.c_void_p(1), 256, win,
+                                  0.1, ctypes.c_void_p(1), ctypes.c_void_p(1), need - 1, None)
+    assert st == S.SKV_EWORKSPACE
+    st = L.sparsekv_gather_attend(ctypes.byref(kv), ctypes.c_void_p(1), 4, None, 256, win,
+                                  0.1, ctypes.c_void_p(1), ctypes.c_void_p(1), need, None)
+    assert st == S.SKV_EINVAL
+    st = L.sparsekv_gather_attend(ctypes.byref(kv), ctypes.c_void_p(1), 4, ctypes.c_void_p(1), 256, win,
+                                  float("nan"), ctypes.c_void_p(1), ctypes.c_void_p(1), need, None)
+    assert st == S.SKV_EINVAL
+    # unsupported attention shape (G > 8 on the vector path)
+    st = L.sparsekv_gather_attend(ctypes.byref(kv), ctypes.c_void_p(1), 9, ctypes.c_void_p(1), 256, win,
+                                  0.1, ctypes.c_void_p(1), ctypes.c_void_p(1), 1 << 30, None)
+    assert st == S.SKV_EUNSUPPORTED
+
+
+def test_workspace_sizes():
+    L = S.lib()
+    kv = _kv(B=4, H=8)
+    n = L.sparsekv_workspace_size(S.SKV_OP_GATHER_ATTEND, ctypes.byref(kv), 4, 2048, None)
+    splits = n // (4 * 8 * 4 * (128 + 2) * 4)
+    assert n == 4 * 8 * 4 * splits * 130 * 4 and 1 <= splits <= 64
+    assert L.sparsekv_workspace_size(S.SKV_OP_SCORE, ctypes.byref(kv), 4, 2048, None) == 0
+    assert L.sparsekv_workspace_size(S.SKV_OP_TOPK, ctypes.byref(kv), 4, 2048, None) == 0

@@ -17,7 +17,11 @@
  *   synchronises, never allocates device memory and keeps no state between
  *   calls.  Outputs are valid once the stream reaches them.  The caller owns
  *   every buffer.  Temporary device memory comes from the caller through
- *   (ws, ws_bytes); sparsekv_workspace_size() tells how much.
+ *   (ws, ws_bytes); sparsekv_workspace_size() tells how much.  A workspace
+ *   must be zero-filled once when it is allocated; every call leaves it
+ *   zero-filled again (its counters are reset on the device), so it can be
+ *   reused by any number of calls that are ordered on one stream.  Calls that
+ *   share a workspace must not overlap.
  * - Errors are returned as skv_status; nothing aborts.  Host-visible
  *   arguments are validated (null pointers, sizes, modes, workspace size).
  *   Device-resident data is NOT validated: table entries must point inside
@@ -68,7 +72,8 @@ typedef enum {
   SKV_OP_TOPK = 1,
   SKV_OP_GATHER_ATTEND = 2,
   SKV_OP_ENCODE = 3,
-  SKV_OP_RETRIEVE = 4
+  SKV_OP_RETRIEVE = 4,
+  SKV_OP_SELECT = 5
 } skv_op;
 
 /* Caller-owned KV storage (host struct, device pointers). */
@@ -114,10 +119,32 @@ skv_status sparsekv_score(const skv_kv* kv, const void* q, int32_t G, float* sco
  * top-k.  Output has set semantics, written in ascending t:
  *   idx   [B][H][k] int32, entries past count[b][h] are -1
  *   count [B][H]    int32 = min(k, number of finite candidates)
- * ws may be NULL when sparsekv_workspace_size(SKV_OP_TOPK, ...) is 0. */
+ * ws: sparsekv_workspace_size(SKV_OP_TOPK, kv, 0, k, NULL) bytes, where only
+ * kv->B, kv->H and kv->L_max are read.  Supports L_max <= 4194304. */
 skv_status sparsekv_topk(const float* scores, int32_t B, int32_t H, int32_t L_max,
                          skv_window win, int32_t k, int32_t* idx, int32_t* count, void* ws,
                          size_t ws_bytes, hipStream_t stream);
+
+/* sparsekv_score followed by sparsekv_topk (same scores, idx and count), with
+ * the top-k's first radix digit (a histogram of the score keys) accumulated
+ * inside the score scan instead of a second pass over the scores.
+ * ws: sparsekv_workspace_size(SKV_OP_SELECT, kv, G, k, NULL) bytes.
+ * Equivalent to sparsekv_score_hist + sparsekv_topk_resume on one ws. */
+skv_status sparsekv_select(const skv_kv* kv, const void* q, int32_t G, skv_window win, int32_t k,
+                           float* scores, int32_t* idx, int32_t* count, void* ws,
+                           size_t ws_bytes, hipStream_t stream);
+
+/* The two halves of sparsekv_select, for callers that time or schedule them
+ * separately: sparsekv_score_hist is sparsekv_score that also adds the key
+ * histogram of the candidates in [lo, hi) into ws (a top-k workspace);
+ * sparsekv_topk_resume finishes the exact top-k from that histogram.  They
+ * must run in this order on the same scores and ws, with no other top-k call
+ * on that ws in between. */
+skv_status sparsekv_score_hist(const skv_kv* kv, const void* q, int32_t G, skv_window win,
+                               float* scores, void* ws, size_t ws_bytes, hipStream_t stream);
+skv_status sparsekv_topk_resume(const float* scores, int32_t B, int32_t H, int32_t L_max,
+                                skv_window win, int32_t k, int32_t* idx, int32_t* count,
+                                void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------- gather + attention --
  * For each sequence b, KV head h and query head g:
@@ -196,7 +223,7 @@ skv_status sparsekv_retrieve(const skv_codebook* cb, const skv_index* index, con
                              size_t ws_bytes, hipStream_t stream);
 
 /* Workspace bytes for an op.  Arguments an op does not use may be NULL / 0:
- *   SCORE, ENCODE: 0;   TOPK: kv->B, kv->H, kv->L_max, k;
+ *   SCORE, ENCODE: 0;   TOPK, SELECT: kv->B, kv->H, kv->L_max;
  *   GATHER_ATTEND: kv, G, k;   RETRIEVE: index, G, k (= k_final), and beta
  *   through sparsekv_retrieve_workspace_size(). */
 size_t sparsekv_workspace_size(skv_op op, const skv_kv* kv, int32_t G, int32_t k,

@@ -28,7 +28,7 @@ LIB_PATH = os.path.join(_HERE, "libsparsekv.so")
 
 SKV_OK, SKV_EINVAL, SKV_EUNSUPPORTED, SKV_EWORKSPACE, SKV_ELAUNCH = range(5)
 SKV_F32, SKV_BF16 = 0, 1
-SKV_OP_SCORE, SKV_OP_TOPK, SKV_OP_GATHER_ATTEND, SKV_OP_ENCODE, SKV_OP_RETRIEVE = range(5)
+SKV_OP_SCORE, SKV_OP_TOPK, SKV_OP_GATHER_ATTEND, SKV_OP_ENCODE, SKV_OP_RETRIEVE, SKV_OP_SELECT = range(6)
 
 c_vp, c_i32, c_f32, c_sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
 
@@ -68,6 +68,12 @@ _SIGS = {
     "sparsekv_score": (c_i32, [ctypes.POINTER(skv_kv), c_vp, c_i32, c_vp, c_vp]),
     "sparsekv_topk": (c_i32, [c_vp, c_i32, c_i32, c_i32, skv_window, c_i32, c_vp, c_vp, c_vp,
                               c_sz, c_vp]),
+    "sparsekv_select": (c_i32, [ctypes.POINTER(skv_kv), c_vp, c_i32, skv_window, c_i32, c_vp,
+                                c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "sparsekv_score_hist": (c_i32, [ctypes.POINTER(skv_kv), c_vp, c_i32, skv_window, c_vp, c_vp,
+                                    c_sz, c_vp]),
+    "sparsekv_topk_resume": (c_i32, [c_vp, c_i32, c_i32, c_i32, skv_window, c_i32, c_vp, c_vp,
+                                     c_vp, c_sz, c_vp]),
     "sparsekv_gather_attend": (c_i32, [ctypes.POINTER(skv_kv), c_vp, c_i32, c_vp, c_i32,
                                        skv_window, c_f32, c_vp, c_vp, c_sz, c_vp]),
     "sparsekv_codebook_init": (c_i32, [c_i32, ctypes.POINTER(c_f32), ctypes.POINTER(c_f32)]),
@@ -192,6 +198,16 @@ def sparsekv_score(kv: KVTensors, q: torch.Tensor, G: int, scores: Optional[torc
     return scores
 
 
+def workspace(nbytes: int, device) -> torch.Tensor:
+    """A zero-filled device workspace (the library keeps it zero between calls)."""
+    return torch.zeros(max(1, int(nbytes)), dtype=torch.uint8, device=device)
+
+
+def topk_workspace_size(B: int, H: int, L_max: int, k: int) -> int:
+    c = skv_kv(None, None, SKV_F32, B, H, 8, 8, 0, L_max, None, None, None)
+    return int(lib().sparsekv_workspace_size(SKV_OP_TOPK, ctypes.byref(c), 0, k, None))
+
+
 def sparsekv_topk(scores: torch.Tensor, lo: torch.Tensor, hi: torch.Tensor, k: int,
                   idx: Optional[torch.Tensor] = None, count: Optional[torch.Tensor] = None,
                   ws: Optional[torch.Tensor] = None):
@@ -206,9 +222,62 @@ def sparsekv_topk(scores: torch.Tensor, lo: torch.Tensor, hi: torch.Tensor, k: i
         count = torch.empty((B, H), dtype=torch.int32, device=scores.device)
     _dev(idx, "idx", torch.int32)
     _dev(count, "count", torch.int32)
-    wsz = 0 if ws is None else ws.numel() * ws.element_size()
+    if ws is None:
+        ws = workspace(topk_workspace_size(B, H, L, k), scores.device)
+    wsz = ws.numel() * ws.element_size()
     _check("sparsekv_topk", lib().sparsekv_topk(_ptr(scores), B, H, L, skv_window(_ptr(lo), _ptr(hi)),
                                                  k, _ptr(idx), _ptr(count), _ptr(ws), wsz, _stream()))
+    return idx, count
+
+
+def sparsekv_select(kv: KVTensors, q: torch.Tensor, G: int, lo: torch.Tensor, hi: torch.Tensor,
+                    k: int, scores: Optional[torch.Tensor] = None, idx: Optional[torch.Tensor] = None,
+                    count: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None):
+    """Score scan + exact top-k in one call; returns (scores, idx, count)."""
+    _dev(q, "q", kv.torch_dtype)
+    if q.shape != (kv.B, kv.H * G, kv.d_k):
+        raise ValueError("q must be [B][H*G][d_k]")
+    dev = q.device
+    if scores is None:
+        scores = torch.empty((kv.B, kv.H, kv.L_max), dtype=torch.float32, device=dev)
+    if idx is None:
+        idx = torch.empty((kv.B, kv.H, k), dtype=torch.int32, device=dev)
+    if count is None:
+        count = torch.empty((kv.B, kv.H), dtype=torch.int32, device=dev)
+    for t, nm, dt in ((scores, "scores", torch.float32), (idx, "idx", torch.int32),
+                      (count, "count", torch.int32), (lo, "lo", torch.int32), (hi, "hi", torch.int32)):
+        _dev(t, nm, dt)
+    if ws is None:
+        ws = workspace(sparsekv_workspace_size(SKV_OP_SELECT, kv, G, k), dev)
+    c = kv.c()
+    _check("sparsekv_select",
+           lib().sparsekv_select(ctypes.byref(c), _ptr(q), G, skv_window(_ptr(lo), _ptr(hi)), k,
+                                 _ptr(scores), _ptr(idx), _ptr(count), _ptr(ws),
+                                 ws.numel() * ws.element_size(), _stream()))
+    return scores, idx, count
+
+
+def sparsekv_score_hist(kv: KVTensors, q: torch.Tensor, G: int, lo: torch.Tensor,
+                        hi: torch.Tensor, scores: torch.Tensor, ws: torch.Tensor):
+    """sparsekv_score that also accumulates the top-k key histogram into ws."""
+    _dev(q, "q", kv.torch_dtype)
+    _dev(scores, "scores", torch.float32)
+    c = kv.c()
+    _check("sparsekv_score_hist",
+           lib().sparsekv_score_hist(ctypes.byref(c), _ptr(q), G, skv_window(_ptr(lo), _ptr(hi)),
+                                     _ptr(scores), _ptr(ws), ws.numel() * ws.element_size(),
+                                     _stream()))
+    return scores
+
+
+def sparsekv_topk_resume(scores: torch.Tensor, lo: torch.Tensor, hi: torch.Tensor, k: int,
+                         idx: torch.Tensor, count: torch.Tensor, ws: torch.Tensor):
+    """Finish the exact top-k from the histogram sparsekv_score_hist left in ws."""
+    B, H, L = scores.shape
+    _check("sparsekv_topk_resume",
+           lib().sparsekv_topk_resume(_ptr(scores), B, H, L, skv_window(_ptr(lo), _ptr(hi)), k,
+                                      _ptr(idx), _ptr(count), _ptr(ws),
+                                      ws.numel() * ws.element_size(), _stream()))
     return idx, count
 
 
@@ -229,8 +298,7 @@ def sparsekv_gather_attend(kv: KVTensors, q: torch.Tensor, G: int, idx: Optional
         out = torch.empty((kv.B, kv.H * G, kv.d_v), dtype=torch.float32, device=q.device)
     _dev(out, "out", torch.float32)
     if ws is None:
-        n = sparsekv_workspace_size(SKV_OP_GATHER_ATTEND, kv, G, k)
-        ws = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+        ws = workspace(sparsekv_workspace_size(SKV_OP_GATHER_ATTEND, kv, G, k), q.device)
     c = kv.c()
     _check("sparsekv_gather_attend",
            lib().sparsekv_gather_attend(ctypes.byref(c), _ptr(q), G, _ptr(idx), k,

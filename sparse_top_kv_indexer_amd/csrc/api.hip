@@ -77,17 +77,51 @@ skv_status sparsekv_score(const skv_kv* kv, const void* q, int32_t G, float* sco
                           hipStream_t stream) {
   if (!kv_ok(kv) || !q || !scores || G < 1) return SKV_EINVAL;
   if (!score_supported(kv, G)) return SKV_EUNSUPPORTED;
-  return launched(launch_score(to_args(kv), q, G, scores, stream));
+  return launched(launch_score(to_args(kv), q, G, scores, nullptr, nullptr, nullptr, stream));
 }
 
 skv_status sparsekv_topk(const float* scores, int32_t B, int32_t H, int32_t L_max,
                          skv_window win, int32_t k, int32_t* idx, int32_t* count, void* ws,
                          size_t ws_bytes, hipStream_t stream) {
-  (void)ws;
-  (void)ws_bytes;
   if (!scores || !idx || !count || !win.lo || !win.hi) return SKV_EINVAL;
   if (B < 1 || H < 1 || L_max < 1 || k < 1) return SKV_EINVAL;
-  return launched(launch_topk(scores, B * H, H, L_max, win.lo, win.hi, k, idx, count, stream));
+  if (!topk_supported(L_max)) return SKV_EUNSUPPORTED;
+  if (!ws || ws_bytes < topk_workspace_bytes(B * H, L_max)) return SKV_EWORKSPACE;
+  return launched(launch_topk(scores, B * H, H, L_max, win.lo, win.hi, k, idx, count, ws, false,
+                              stream));
+}
+
+skv_status sparsekv_score_hist(const skv_kv* kv, const void* q, int32_t G, skv_window win,
+                               float* scores, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!kv_ok(kv) || !q || !scores || G < 1 || !win.lo || !win.hi) return SKV_EINVAL;
+  if (!score_supported(kv, G) || !topk_supported(kv->L_max)) return SKV_EUNSUPPORTED;
+  if (!ws || ws_bytes < topk_workspace_bytes(kv->B * kv->H, kv->L_max)) return SKV_EWORKSPACE;
+  return launched(launch_score(to_args(kv), q, G, scores, win.lo, win.hi, (uint32_t*)ws, stream));
+}
+
+skv_status sparsekv_topk_resume(const float* scores, int32_t B, int32_t H, int32_t L_max,
+                                skv_window win, int32_t k, int32_t* idx, int32_t* count,
+                                void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!scores || !idx || !count || !win.lo || !win.hi) return SKV_EINVAL;
+  if (B < 1 || H < 1 || L_max < 1 || k < 1) return SKV_EINVAL;
+  if (!topk_supported(L_max)) return SKV_EUNSUPPORTED;
+  if (!ws || ws_bytes < topk_workspace_bytes(B * H, L_max)) return SKV_EWORKSPACE;
+  return launched(launch_topk(scores, B * H, H, L_max, win.lo, win.hi, k, idx, count, ws, true,
+                              stream));
+}
+
+skv_status sparsekv_select(const skv_kv* kv, const void* q, int32_t G, skv_window win, int32_t k,
+                           float* scores, int32_t* idx, int32_t* count, void* ws,
+                           size_t ws_bytes, hipStream_t stream) {
+  if (!kv_ok(kv) || !q || !scores || !idx || !count || G < 1 || k < 1) return SKV_EINVAL;
+  if (!win.lo || !win.hi) return SKV_EINVAL;
+  if (!score_supported(kv, G) || !topk_supported(kv->L_max)) return SKV_EUNSUPPORTED;
+  const int rows = kv->B * kv->H;
+  if (!ws || ws_bytes < topk_workspace_bytes(rows, kv->L_max)) return SKV_EWORKSPACE;
+  hipError_t e = launch_score(to_args(kv), q, G, scores, win.lo, win.hi, (uint32_t*)ws, stream);
+  if (e != hipSuccess) return launched(e);
+  return launched(launch_topk(scores, rows, kv->H, kv->L_max, win.lo, win.hi, k, idx, count, ws,
+                              true, stream));
 }
 
 skv_status sparsekv_gather_attend(const skv_kv* kv, const void* q, int32_t G, const int32_t* idx,
@@ -114,9 +148,12 @@ size_t sparsekv_workspace_size(skv_op op, const skv_kv* kv, int32_t G, int32_t k
                                const skv_index* index) {
   switch (op) {
     case SKV_OP_SCORE:
-    case SKV_OP_TOPK:
     case SKV_OP_ENCODE:
       return 0;
+    case SKV_OP_TOPK:
+    case SKV_OP_SELECT:
+      if (!kv || kv->B < 1 || kv->H < 1 || kv->L_max < 1) return 0;
+      return topk_workspace_bytes(kv->B * kv->H, kv->L_max);
     case SKV_OP_GATHER_ATTEND:
       if (!kv_ok(kv) || G < 1 || k < 0) return 0;
       if (kv->v == nullptr) return mla_workspace_bytes(to_args(kv), G, k);

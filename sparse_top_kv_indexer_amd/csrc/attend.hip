@@ -60,6 +60,8 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(
   constexpr int E = BF16 ? 8 : 4;
   constexpr int ES = BF16 ? 2 : 4;
   constexpr int PE = NPL * E;            // elements of a row held by one lane
+  constexpr int NB = NPL == 1 ? 8 : 4;   // tokens whose loads are in flight per row
+  __shared__ int64_t rows_sh[kThreads];  // element offsets of this piece's rows (-1 = skip)
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int p = lane & 15;
@@ -78,7 +80,7 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(
       unpack<BF16>(w, &qr[g][r * E]);
     }
 
-  const int seq = kv.seq_len[b];
+  const int seq = min(kv.seq_len[b], kv.L_max);
   const int lo = max(0, min(lo_p[b], seq));
   const int hi = max(lo, min(hi_p[b], seq));
   const int n_list = k + lo + (seq - hi);
@@ -97,46 +99,69 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(
 
   const char* kb = (const char*)kv.k;
   const char* vb = (const char*)kv.v;
-  for (int pos = p0 + row; pos < p1; pos += kRows) {
-    int t;
-    if (pos < k) {
-      t = irow[pos];
-      if (t < lo || t >= hi) t = -1;
-    } else if (pos - k < lo) {
-      t = pos - k;
-    } else {
-      t = hi + (pos - k - lo);
+  for (int q0 = p0; q0 < p1; q0 += kThreads) {
+    const int cnt = min(kThreads, p1 - q0);
+    // resolve this piece's positions to row offsets, one position per thread
+    if ((int)threadIdx.x < cnt) {
+      const int pos = q0 + threadIdx.x;
+      int t;
+      if (pos < k) {
+        t = irow[pos];
+        if (t < lo || t >= hi) t = -1;
+      } else if (pos - k < lo) {
+        t = pos - k;
+      } else {
+        t = hi + (pos - k - lo);
+      }
+      const int64_t slot = t >= 0 ? slot_of(kv, b, t) : -1;
+      rows_sh[threadIdx.x] = slot >= 0 ? row_elem(kv, b, h, slot, D) : -1;
     }
-    const int64_t slot = t >= 0 ? slot_of(kv, b, t) : -1;
-    if (slot < 0) continue;               // uniform within the 16-lane row
-    const int64_t base = row_elem(kv, b, h, slot, D);
-    u32x4_t kd[NPL], vd[NPL];
+    __syncthreads();
+    for (int j0 = row; j0 < cnt; j0 += kRows * NB) {
+      u32x4_t kd[NB][NPL], vd[NB][NPL];
+      int64_t ro[NB];
 #pragma unroll
-    for (int r = 0; r < NPL; ++r) {
-      kd[r] = ld16(kb + (base + (p + 16 * r) * E) * ES);
-      vd[r] = ld16(vb + (base + (p + 16 * r) * E) * ES);
+      for (int u = 0; u < NB; ++u) {
+        const int j = j0 + u * kRows;
+        ro[u] = j < cnt ? rows_sh[j] : -1;
+#pragma unroll
+        for (int r = 0; r < NPL; ++r) {
+          if (ro[u] >= 0) {
+            kd[u][r] = ld16(kb + (ro[u] + (p + 16 * r) * E) * ES);
+            vd[u][r] = ld16(vb + (ro[u] + (p + 16 * r) * E) * ES);
+          } else {
+            kd[u][r] = u32x4_t{0, 0, 0, 0};
+            vd[u][r] = u32x4_t{0, 0, 0, 0};
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        if (ro[u] < 0) continue;            // uniform within the 16-lane row
+        float kf[PE], vf[PE];
+#pragma unroll
+        for (int r = 0; r < NPL; ++r) {
+          unpack<BF16>(kd[u][r], &kf[r * E]);
+          unpack<BF16>(vd[u][r], &vf[r * E]);
+        }
+#pragma unroll
+        for (int g = 0; g < GMAX; ++g) {
+          if (g >= G) break;
+          float d = 0.f;
+#pragma unroll
+          for (int e = 0; e < PE; ++e) d = fmaf(qr[g][e], kf[e], d);
+          const float z = row16_sum(d) * scale_log2;
+          const float mn = fmaxf(m[g], z);
+          const float corr = exp2f(m[g] - mn);   // 0 when m was -inf
+          const float pz = exp2f(z - mn);
+          l[g] = l[g] * corr + pz;
+#pragma unroll
+          for (int e = 0; e < PE; ++e) acc[g][e] = fmaf(pz, vf[e], acc[g][e] * corr);
+          m[g] = mn;
+        }
+      }
     }
-    float kf[PE], vf[PE];
-#pragma unroll
-    for (int r = 0; r < NPL; ++r) {
-      unpack<BF16>(kd[r], &kf[r * E]);
-      unpack<BF16>(vd[r], &vf[r * E]);
-    }
-#pragma unroll
-    for (int g = 0; g < GMAX; ++g) {
-      if (g >= G) break;
-      float d = 0.f;
-#pragma unroll
-      for (int e = 0; e < PE; ++e) d = fmaf(qr[g][e], kf[e], d);
-      const float z = row16_sum(d) * scale_log2;
-      const float mn = fmaxf(m[g], z);
-      const float corr = exp2f(m[g] - mn);   // 0 when m was -inf
-      const float pz = exp2f(z - mn);
-      l[g] = l[g] * corr + pz;
-#pragma unroll
-      for (int e = 0; e < PE; ++e) acc[g][e] = fmaf(pz, vf[e], acc[g][e] * corr);
-      m[g] = mn;
-    }
+    __syncthreads();
   }
 
   // merge the four rows of each wave (lanes p, p+16, p+32, p+48)
@@ -196,24 +221,35 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(
 }
 
 // out[b][hq][j] = sum_s acc_s[j] 2^(m_s - M) / sum_s l_s 2^(m_s - M)
+// One workgroup per (b, query head); the split partials are staged in LDS with
+// all loads issued at once.
 __global__ __launch_bounds__(256) void attend_reduce_kernel(const float* part, int n_split, int D,
                                                            int HG, float* out) {
+  extern __shared__ float ps[];          // [n_split][D + 2]
+  __shared__ float wts[64];
+  __shared__ float inv_l;
   const int hq = blockIdx.x, b = blockIdx.y;
   const int stride = D + 2;
-  const float* base = part + ((int64_t)b * HG + hq) * n_split * stride;
-  float M = -INFINITY;
-  for (int s = 0; s < n_split; ++s) M = fmaxf(M, base[s * stride + D]);
+  const int n = n_split * stride;
+  const float* base = part + ((int64_t)b * HG + hq) * n;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) ps[i] = base[i];
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const int s = threadIdx.x;
+    const float ms = s < n_split ? ps[s * stride + D] : -INFINITY;
+    float M = ms;
+    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+    const float w = (s < n_split && M != -INFINITY) ? exp2f(ms - M) : 0.f;
+    float L = s < n_split ? ps[s * stride + D + 1] * w : 0.f;
+    for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o, 64);
+    wts[s] = w;
+    if (s == 0) inv_l = L > 0.f ? 1.f / L : 0.f;
+  }
+  __syncthreads();
   for (int j = threadIdx.x; j < D; j += blockDim.x) {
-    float L = 0.f, a = 0.f;
-    if (M != -INFINITY) {
-      for (int s = 0; s < n_split; ++s) {
-        const float* ps = base + s * stride;
-        const float c = exp2f(ps[D] - M);
-        L += ps[D + 1] * c;
-        a += ps[j] * c;
-      }
-    }
-    out[((int64_t)b * HG + hq) * D + j] = L > 0.f ? a / L : 0.f;
+    float a = 0.f;
+    for (int s = 0; s < n_split; ++s) a += ps[s * stride + j] * wts[s];
+    out[((int64_t)b * HG + hq) * D + j] = a * inv_l;
   }
 }
 
@@ -274,7 +310,15 @@ hipError_t launch_gather_attend(const KvArgs& kv, const void* q, int G, const in
                  : launch_split<false, 2>(kv, q, G, idx, k, lo, hi, scale_log2, n_split, part, st);
   if (e != hipSuccess) return e;
   dim3 grid(kv.H * G, kv.B);
-  attend_reduce_kernel<<<grid, 128, 0, st>>>(part, n_split, kv.d_v, kv.H * G, out);
+  const size_t lds = (size_t)n_split * (kv.d_v + 2) * sizeof(float);
+  static bool attr_set = false;
+  if (!attr_set) {
+    e = hipFuncSetAttribute((const void*)attend_reduce_kernel,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 64 * (256 + 2) * 4);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  attend_reduce_kernel<<<grid, 256, lds, st>>>(part, n_split, kv.d_v, kv.H * G, out);
   (void)ws_bytes;
   return hipGetLastError();
 }

@@ -28,9 +28,40 @@ constexpr int kTile = 512;  // tokens per workgroup (multiple of 16)
 
 __device__ __forceinline__ u32x4_t ld16(const char* p) { return *(const u32x4_t*)p; }
 
-template <bool BF16, int NPL, int GMAX, int U>
+// Score-key histogram of the tile (top 12 bits of the order-preserving key),
+// built in LDS while scoring and added into the row's global histogram: the
+// first digit of the exact top-k, fused into the scan.
+struct HistArgs {
+  const int32_t* lo;
+  const int32_t* hi;
+  uint32_t* hist;   // [B*H][4096]
+};
+
+__device__ __forceinline__ void hist_add(uint32_t* lh, float s, int t, int lo, int hi) {
+  uint32_t u = __float_as_uint(s);
+  if (t < lo || t >= hi || (u & 0x7f800000u) == 0x7f800000u) return;
+  if (u == 0x80000000u) u = 0u;
+  const uint32_t key = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  atomicAdd(&lh[key >> 20], 1u);
+}
+
+__device__ __forceinline__ void hist_begin(uint32_t* lh) {
+  for (int i = threadIdx.x; i < 4096; i += kThreads) lh[i] = 0u;
+  __syncthreads();
+}
+
+__device__ __forceinline__ void hist_flush(uint32_t* lh, uint32_t* g) {
+  __syncthreads();
+  for (int i = threadIdx.x; i < 4096; i += kThreads) {
+    const uint32_t c = lh[i];
+    if (c) atomicAdd(&g[i], c);
+  }
+}
+
+template <bool BF16, int NPL, int GMAX, int U, bool HIST>
 __global__ __launch_bounds__(kThreads) void score_valu_kernel(KvArgs kv, const void* qv, int G,
-                                                               float* scores) {
+                                                               float* scores, HistArgs ha) {
+  __shared__ uint32_t lh[HIST ? 4096 : 1];
   constexpr int E = BF16 ? 8 : 4;      // elements per 16-byte piece
   constexpr int ES = BF16 ? 2 : 4;     // bytes per element
   const int b = blockIdx.z, h = blockIdx.y;
@@ -65,6 +96,12 @@ __global__ __launch_bounds__(kThreads) void score_valu_kernel(KvArgs kv, const v
   const char* kbase = (const char*)kv.k;
   float* srow = scores + ((int64_t)b * kv.H + h) * kv.L_max;
   const int n_groups = (t_end - t_begin + 3) >> 2;   // groups of 4 tokens
+  int wlo = 0, whi = 0;
+  if constexpr (HIST) {
+    hist_begin(lh);
+    wlo = ha.lo[b];
+    whi = ha.hi[b];
+  }
 
   for (int g0 = wave; g0 < n_groups; g0 += 4 * U) {
     u32x4_t kd[U][NPL];
@@ -112,15 +149,22 @@ __global__ __launch_bounds__(kThreads) void score_valu_kernel(KvArgs kv, const v
         const float d = row16_sum(acc[g]);
         if (g < G) s = fmaxf(s, d);
       }
-      if (p == 0 && tok[u] < t_end) srow[tok[u]] = ok[u] ? s : -INFINITY;
+      if (p == 0 && tok[u] < t_end) {
+        srow[tok[u]] = ok[u] ? s : -INFINITY;
+        if constexpr (HIST) {
+          if (ok[u]) hist_add(lh, s, tok[u], wlo, whi);
+        }
+      }
     }
   }
+  if constexpr (HIST) hist_flush(lh, ha.hist + ((int64_t)b * kv.H + h) * 4096);
 }
 
 // bf16 keys, 2 <= G <= 16, d_k = 32 * NC.
-template <int NC, int U>
+template <int NC, int U, bool HIST>
 __global__ __launch_bounds__(kThreads) void score_mfma_kernel(KvArgs kv, const uint16_t* q, int G,
-                                                               float* scores) {
+                                                               float* scores, HistArgs ha) {
+  __shared__ uint32_t lh[HIST ? 4096 : 1];
   const int b = blockIdx.z, h = blockIdx.y;
   const int t_begin = blockIdx.x * kTile;
   const int t_end = min(kv.L_max, t_begin + kTile);
@@ -141,6 +185,12 @@ __global__ __launch_bounds__(kThreads) void score_mfma_kernel(KvArgs kv, const u
   const char* kbase = (const char*)kv.k;
   float* srow = scores + ((int64_t)b * kv.H + h) * kv.L_max;
   const int n_chunks = (t_end - t_begin + 15) >> 4;
+  int wlo = 0, whi = 0;
+  if constexpr (HIST) {
+    hist_begin(lh);
+    wlo = ha.lo[b];
+    whi = ha.hi[b];
+  }
 
   for (int c0 = wave; c0 < n_chunks; c0 += 4 * U) {
     bf16x8_t Bm[U][NC];
@@ -175,37 +225,63 @@ __global__ __launch_bounds__(kThreads) void score_mfma_kernel(KvArgs kv, const u
         s = fmaxf(s, __shfl_xor(s, 16, 64));
         s = fmaxf(s, __shfl_xor(s, 32, 64));
       }
-      if (g4 == 0 && tok[u] < t_end) srow[tok[u]] = ok[u] ? s : -INFINITY;
+      if (g4 == 0 && tok[u] < t_end) {
+        srow[tok[u]] = ok[u] ? s : -INFINITY;
+        if constexpr (HIST) {
+          if (ok[u]) hist_add(lh, s, tok[u], wlo, whi);
+        }
+      }
     }
   }
+  if constexpr (HIST) hist_flush(lh, ha.hist + ((int64_t)b * kv.H + h) * 4096);
+}
+
+template <bool BF16, int NPL, int GMAX, int U>
+void launch_valu_k(const KvArgs& kv, const void* q, int G, float* scores, const HistArgs& ha,
+                   dim3 grid, hipStream_t s) {
+  if (ha.hist)
+    score_valu_kernel<BF16, NPL, GMAX, U, true><<<grid, kThreads, 0, s>>>(kv, q, G, scores, ha);
+  else
+    score_valu_kernel<BF16, NPL, GMAX, U, false><<<grid, kThreads, 0, s>>>(kv, q, G, scores, ha);
 }
 
 template <bool BF16, int NPL, int GCAP>
-hipError_t launch_valu(const KvArgs& kv, const void* q, int G, float* scores, dim3 grid,
-                       hipStream_t s) {
+hipError_t launch_valu(const KvArgs& kv, const void* q, int G, float* scores, const HistArgs& ha,
+                       dim3 grid, hipStream_t s) {
   if (G == 1)
-    score_valu_kernel<BF16, NPL, 1, 4><<<grid, kThreads, 0, s>>>(kv, q, G, scores);
+    launch_valu_k<BF16, NPL, 1, 4>(kv, q, G, scores, ha, grid, s);
   else if (GCAP >= 2 && G == 2)
-    score_valu_kernel<BF16, NPL, (GCAP >= 2 ? 2 : 1), 4><<<grid, kThreads, 0, s>>>(kv, q, G, scores);
+    launch_valu_k<BF16, NPL, (GCAP >= 2 ? 2 : 1), 4>(kv, q, G, scores, ha, grid, s);
   else if (GCAP >= 4 && G <= 4)
-    score_valu_kernel<BF16, NPL, (GCAP >= 4 ? 4 : 1), 2><<<grid, kThreads, 0, s>>>(kv, q, G, scores);
+    launch_valu_k<BF16, NPL, (GCAP >= 4 ? 4 : 1), 2>(kv, q, G, scores, ha, grid, s);
   else if (GCAP >= 8 && G <= 8)
-    score_valu_kernel<BF16, NPL, (GCAP >= 8 ? 8 : 1), 2><<<grid, kThreads, 0, s>>>(kv, q, G, scores);
+    launch_valu_k<BF16, NPL, (GCAP >= 8 ? 8 : 1), 2>(kv, q, G, scores, ha, grid, s);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
+template <int NC, int U>
+void launch_mfma_k(const KvArgs& kv, const void* q, int G, float* scores, const HistArgs& ha,
+                   dim3 grid, hipStream_t s) {
+  if (ha.hist)
+    score_mfma_kernel<NC, U, true><<<grid, kThreads, 0, s>>>(kv, (const uint16_t*)q, G, scores, ha);
+  else
+    score_mfma_kernel<NC, U, false><<<grid, kThreads, 0, s>>>(kv, (const uint16_t*)q, G, scores, ha);
+}
+
 }  // namespace
 
-hipError_t launch_score(const KvArgs& kv, const void* q, int G, float* scores, hipStream_t s) {
+hipError_t launch_score(const KvArgs& kv, const void* q, int G, float* scores, const int32_t* lo,
+                        const int32_t* hi, uint32_t* hist, hipStream_t s) {
   dim3 grid((kv.L_max + kTile - 1) / kTile, kv.H, kv.B);
+  HistArgs ha{lo, hi, hist};
   if (kv.bf16 && G >= 2 && G <= 16 && kv.d_k % 32 == 0) {
     switch (kv.d_k / 32) {
-      case 2: score_mfma_kernel<2, 2><<<grid, kThreads, 0, s>>>(kv, (const uint16_t*)q, G, scores); break;
-      case 4: score_mfma_kernel<4, 2><<<grid, kThreads, 0, s>>>(kv, (const uint16_t*)q, G, scores); break;
-      case 8: score_mfma_kernel<8, 2><<<grid, kThreads, 0, s>>>(kv, (const uint16_t*)q, G, scores); break;
-      case 18: score_mfma_kernel<18, 1><<<grid, kThreads, 0, s>>>(kv, (const uint16_t*)q, G, scores); break;
+      case 2: launch_mfma_k<2, 2>(kv, q, G, scores, ha, grid, s); break;
+      case 4: launch_mfma_k<4, 2>(kv, q, G, scores, ha, grid, s); break;
+      case 8: launch_mfma_k<8, 2>(kv, q, G, scores, ha, grid, s); break;
+      case 18: launch_mfma_k<18, 1>(kv, q, G, scores, ha, grid, s); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -213,13 +289,13 @@ hipError_t launch_score(const KvArgs& kv, const void* q, int G, float* scores, h
   const int E = kv.bf16 ? 8 : 4;
   const int npl = (kv.d_k / E + 15) / 16;
   if (kv.bf16) {
-    if (npl == 1) return launch_valu<true, 1, 8>(kv, q, G, scores, grid, s);
-    if (npl == 2) return launch_valu<true, 2, 4>(kv, q, G, scores, grid, s);
-    if (npl <= 5) return launch_valu<true, 5, 1>(kv, q, G, scores, grid, s);
+    if (npl == 1) return launch_valu<true, 1, 8>(kv, q, G, scores, ha, grid, s);
+    if (npl == 2) return launch_valu<true, 2, 4>(kv, q, G, scores, ha, grid, s);
+    if (npl <= 5) return launch_valu<true, 5, 1>(kv, q, G, scores, ha, grid, s);
   } else {
-    if (npl == 1) return launch_valu<false, 1, 8>(kv, q, G, scores, grid, s);
-    if (npl == 2) return launch_valu<false, 2, 8>(kv, q, G, scores, grid, s);
-    if (npl <= 4) return launch_valu<false, 4, 2>(kv, q, G, scores, grid, s);
+    if (npl == 1) return launch_valu<false, 1, 8>(kv, q, G, scores, ha, grid, s);
+    if (npl == 2) return launch_valu<false, 2, 8>(kv, q, G, scores, ha, grid, s);
+    if (npl <= 4) return launch_valu<false, 4, 2>(kv, q, G, scores, ha, grid, s);
   }
   return hipErrorInvalidValue;
 }

@@ -20,12 +20,18 @@ struct KvArgs {
   const int32_t* seq_len;
 };
 
-// score.hip
-hipError_t launch_score(const KvArgs& kv, const void* q, int G, float* scores, hipStream_t s);
+// score.hip; with hist != nullptr the scan also adds the key histogram of
+// the candidates in [lo, hi) into hist [B*H][4096] (first top-k digit)
+hipError_t launch_score(const KvArgs& kv, const void* q, int G, float* scores, const int32_t* lo,
+                        const int32_t* hi, uint32_t* hist, hipStream_t s);
 
-// topk.hip
+// topk.hip (workspace layout in skv_topk.h); hist_ready: the row histograms
+// were already accumulated by the score scan
+size_t topk_workspace_bytes(int rows, int L_max);
+bool topk_supported(int L_max);
 hipError_t launch_topk(const float* scores, int rows, int H, int L_max, const int32_t* lo,
-                       const int32_t* hi, int k, int32_t* idx, int32_t* count, hipStream_t s);
+                       const int32_t* hi, int k, int32_t* idx, int32_t* count, void* ws,
+                       bool hist_ready, hipStream_t s);
 
 // attend.hip
 int attend_num_splits(int k);

@@ -47,13 +47,20 @@ class Run:
     def topk(self, scores):
         return S.sparsekv_topk(scores, self.lo, self.hi, self.st.k)
 
+    def select(self):
+        """score + top-k in one call (histogram fused into the scan)."""
+        return S.sparsekv_select(self.skv, self.sq, self.st.score_G, self.lo, self.hi, self.st.k)
+
     def attend(self, idx):
         return S.sparsekv_gather_attend(self.kv, self.q, self.st.G, idx, self.st.k, self.lo, self.hi,
                                         self.st.scale)
 
-    def step(self):
-        sc = self.score()
-        idx, cnt = self.topk(sc)
+    def step(self, fused=True):
+        if fused:
+            sc, idx, cnt = self.select()
+        else:
+            sc = self.score()
+            idx, cnt = self.topk(sc)
         out = self.attend(idx)
         torch.cuda.synchronize()
         return sc, idx, cnt, out

@@ -109,4 +109,26 @@ def test_workspace_sizes():
     splits = n // (4 * 8 * 4 * (128 + 2) * 4)
     assert n == 4 * 8 * 4 * splits * 130 * 4 and 1 <= splits <= 64
     assert L.sparsekv_workspace_size(S.SKV_OP_SCORE, ctypes.byref(kv), 4, 2048, None) == 0
-    assert L.sparsekv_workspace_size(S.SKV_OP_TOPK, ctypes.byref(kv), 4, 2048, None) == 0
+    t = L.sparsekv_workspace_size(S.SKV_OP_TOPK, ctypes.byref(kv), 4, 2048, None)
+    assert t >= 32 * 64 * 8                      # candidate lists hold a whole row
+    assert t == L.sparsekv_workspace_size(S.SKV_OP_SELECT, ctypes.byref(kv), 4, 2048, None)
+    assert t == S.topk_workspace_size(4, 8, 64, 2048)
+
+
+def test_topk_and_select_check_workspace_before_launch():
+    L = S.lib()
+    win = S.skv_window(ctypes.c_void_p(1), ctypes.c_void_p(1))
+    need = S.topk_workspace_size(2, 2, 4096, 16)
+    st = L.sparsekv_topk(ctypes.c_void_p(1), 2, 2, 4096, win, 16, ctypes.c_void_p(1),
+                         ctypes.c_void_p(1), ctypes.c_void_p(1), need - 1, None)
+    assert st == S.SKV_EWORKSPACE
+    st = L.sparsekv_topk(ctypes.c_void_p(1), 2, 2, 4096, win, 16, ctypes.c_void_p(1),
+                         ctypes.c_void_p(1), None, need, None)
+    assert st == S.SKV_EWORKSPACE
+    kv = _kv(B=2, H=2, L_max=4096)
+    st = L.sparsekv_select(ctypes.byref(kv), ctypes.c_void_p(1), 4, win, 16, ctypes.c_void_p(1),
+                           ctypes.c_void_p(1), ctypes.c_void_p(1), ctypes.c_void_p(1), need - 1, None)
+    assert st == S.SKV_EWORKSPACE
+    st = L.sparsekv_select(ctypes.byref(kv), ctypes.c_void_p(1), 4, win, 0, ctypes.c_void_p(1),
+                           ctypes.c_void_p(1), ctypes.c_void_p(1), ctypes.c_void_p(1), need, None)
+    assert st == S.SKV_EINVAL

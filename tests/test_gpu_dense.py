@@ -17,13 +17,13 @@ def _all_rows(st):
     return [(b, h) for b in range(st.score_kv.B) for h in range(st.score_kv.H)]
 
 
-def _end_to_end(st, rows=None, check_all_rows=True, attend=True):
+def _end_to_end(st, rows=None, check_all_rows=True, attend=True, fused=True):
     rows = _all_rows(st) if rows is None else rows
     say("case", st.name, "B", st.kv.B, "H", st.kv.H, "G", st.G, "L", st.kv.L_max, "k", st.k,
         "mode", st.kv.mode)
     r = Run(st)
     if attend:
-        sc, idx, cnt, out = r.step()
+        sc, idx, cnt, out = r.step(fused=fused)
         out = out.cpu().numpy()
     else:
         sc = r.score()
@@ -69,6 +69,7 @@ def test_gqa_paged_small(G):
     st = W.make_gqa_paged(tag=100 + G, B=2, H=3, G=G, L=2048, k=256, sink=4, local=64,
                           seq_len=[2048, 1509])
     assert _end_to_end(st) == 0
+    assert _end_to_end(st, fused=False) == 0
 
 
 def test_gqa_paged_g16_mfma_cross_lane_max():
@@ -76,6 +77,28 @@ def test_gqa_paged_g16_mfma_cross_lane_max():
     scoring and selection only (the vector attention path stops at G = 8)."""
     st = W.make_gqa_paged(tag=116, B=1, H=2, G=16, L=1024, k=128, sink=4, local=64)
     assert _end_to_end(st, attend=False) == 0
+
+
+@pytest.mark.parametrize("tag", [201, 202])
+def test_select_equals_score_then_topk(tag):
+    """The fused scan + top-k returns the same scores and the same selection as
+    the two separate calls (several calls reuse one workspace)."""
+    st = W.make_gqa_paged(tag=tag, B=2, H=2, G=4, L=8192, k=700, sink=4, local=64,
+                          seq_len=[8192, 5000])
+    r = Run(st)
+    ws = S.workspace(S.sparsekv_workspace_size(S.SKV_OP_SELECT, r.skv, 4, st.k), DEV)
+    for _ in range(3):
+        sc1, idx1, cnt1 = S.sparsekv_select(r.skv, r.sq, 4, r.lo, r.hi, st.k, ws=ws)
+        sc2 = r.score()
+        idx2, cnt2 = S.sparsekv_topk(sc2, r.lo, r.hi, st.k, ws=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(sc1, sc2)
+        assert torch.equal(idx1, idx2) and torch.equal(cnt1, cnt2)
+    # the counters at the front of the workspace are back to zero
+    rows = 4
+    al = lambda x: (x + 255) // 256 * 256
+    zero_region = al(rows * 4096 * 4)
+    assert torch.count_nonzero(ws[:zero_region]).item() == 0
 
 
 def test_token_pool_small():

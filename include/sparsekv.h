@@ -208,27 +208,38 @@ typedef struct {
   float* est;                   /* [H][C] rerank estimate of each candidate   */
 } skv_retrieve_trace;
 
-/* Collision vote + bucket top-C + 4-bit rerank + exact top-k_final.
- *   q      [H*G][d] bf16 query heads (G per KV head)
- *   C      = min(n, ceil(beta * n)) candidates per KV head
+
+/* Collision vote + bucket top-C + 4-bit rerank + exact top-k_final for the
+ * index entries [0, index->n) of every KV head (ParisKV close-reading,
+ * sections 2.3-2.5):
+ *   1. the query heads are normalised and rotated like the keys; per
+ *      subspace the 256 centroids are ranked by similarity (ties: lower id)
+ *      and, walking that ranking with the exclusive prefix count P of the
+ *      index histogram, a centroid gets tier weight 7 - l for the smallest
+ *      l with P < T_l (0 if P >= T_rho), T_rho = ceil(rho n),
+ *      T_l = ceil(p_l T_rho), p = .05 .15 .30 .50 .75 1.0 (float64, host);
+ *   2. S_i = max over the G query heads of sum_b weight[b][id_ib];
+ *   3. the C = min(n, ceil(beta n)) largest S_i, ties to the lower entry;
+ *   4. est_i = max_g |q_g| sum_b w_ib <v_ib, q~_gb> (fp32, tree sums);
+ *   5. the k_final largest est_i, ties to the lower entry.
+ *   q      [H*G][d] bf16 query heads (G per KV head, G <= 4)
  *   idx    [H][k_final] int32 logical positions (index->pos of the winners),
  *          ascending; -1 past n_cand
  *   n_cand [H] int32 = min(k_final, C)
- * Tier bounds: T_rho = ceil(rho n), T_l = ceil(p_l T_rho), p = .05 .15 .30
- * .50 .75 1.0, computed in float64 on the host (ParisKV close-reading,
- * section 2.3, paper Eq. (15)).  Requires rho >= beta > 0. */
+ * Requires rho >= beta > 0, d = 128, m = 8. */
 skv_status sparsekv_retrieve(const skv_codebook* cb, const skv_index* index, const void* q,
-                             int32_t G, float rho, float beta, int32_t k_final, int32_t* idx,
+                             int32_t G, double rho, double beta, int32_t k_final, int32_t* idx,
                              int32_t* n_cand, const skv_retrieve_trace* trace, void* ws,
                              size_t ws_bytes, hipStream_t stream);
 
 /* Workspace bytes for an op.  Arguments an op does not use may be NULL / 0:
  *   SCORE, ENCODE: 0;   TOPK, SELECT: kv->B, kv->H, kv->L_max;
- *   GATHER_ATTEND: kv, G, k;   RETRIEVE: index, G, k (= k_final), and beta
- *   through sparsekv_retrieve_workspace_size(). */
+ *   GATHER_ATTEND: kv, G, k;   RETRIEVE: index, G, k (= k_final) with
+ *   beta = 1 (an upper bound); sparsekv_retrieve_workspace_size() takes the
+ *   actual beta. */
 size_t sparsekv_workspace_size(skv_op op, const skv_kv* kv, int32_t G, int32_t k,
                                const skv_index* index);
-size_t sparsekv_retrieve_workspace_size(const skv_index* index, int32_t G, float beta,
+size_t sparsekv_retrieve_workspace_size(const skv_index* index, int32_t G, double beta,
                                         int32_t k_final);
 
 const char* sparsekv_status_string(skv_status s);

@@ -80,11 +80,12 @@ _SIGS = {
     "sparsekv_encode": (c_i32, [ctypes.POINTER(skv_codebook), ctypes.POINTER(skv_kv), c_i32,
                                 c_i32, c_i32, ctypes.POINTER(skv_index), c_vp]),
     "sparsekv_retrieve": (c_i32, [ctypes.POINTER(skv_codebook), ctypes.POINTER(skv_index), c_vp,
-                                  c_i32, c_f32, c_f32, c_i32, c_vp, c_vp,
+                                  c_i32, ctypes.c_double, ctypes.c_double, c_i32, c_vp, c_vp,
                                   ctypes.POINTER(skv_retrieve_trace), c_vp, c_sz, c_vp]),
     "sparsekv_workspace_size": (c_sz, [ctypes.c_int, ctypes.POINTER(skv_kv), c_i32, c_i32,
                                        ctypes.POINTER(skv_index)]),
-    "sparsekv_retrieve_workspace_size": (c_sz, [ctypes.POINTER(skv_index), c_i32, c_f32, c_i32]),
+    "sparsekv_retrieve_workspace_size": (c_sz, [ctypes.POINTER(skv_index), c_i32, ctypes.c_double,
+                                                c_i32]),
     "sparsekv_status_string": (ctypes.c_char_p, [c_i32]),
     "sparsekv_version": (c_i32, []),
 }
@@ -322,3 +323,108 @@ def sparsekv_status_string(s: int) -> str:
 
 def sparsekv_version() -> int:
     return int(lib().sparsekv_version())
+
+
+# ------------------------------------------------------------ retrieval ----
+@dataclass
+class IndexTensors:
+    """Device arrays of a compressed-code index (skv_index)."""
+    ids: torch.Tensor     # uint8 [H][cap][n_sub]
+    codes: torch.Tensor   # uint8 [H][cap][d/2]
+    w: torch.Tensor       # float32 [H][cap][n_sub]
+    hist: torch.Tensor    # int32 [H][n_sub][256]
+    pos: torch.Tensor     # int32 [cap]
+    n: int
+    cap: int
+    H: int
+
+    def c(self) -> skv_index:
+        for t, nm in ((self.ids, "ids"), (self.codes, "codes"), (self.w, "w"), (self.hist, "hist"),
+                      (self.pos, "pos")):
+            _dev(t, nm)
+        return skv_index(_ptr(self.ids), _ptr(self.codes), _ptr(self.w), _ptr(self.hist),
+                         _ptr(self.pos), self.n, self.cap, self.H)
+
+
+def new_index(H: int, cap: int, d: int = 128, n_sub: int = 16, device="cuda") -> IndexTensors:
+    """An empty index (histogram zeroed) with room for `cap` entries per head."""
+    return IndexTensors(ids=torch.empty((H, cap, n_sub), dtype=torch.uint8, device=device),
+                        codes=torch.empty((H, cap, d // 2), dtype=torch.uint8, device=device),
+                        w=torch.empty((H, cap, n_sub), dtype=torch.float32, device=device),
+                        hist=torch.zeros((H, n_sub, 256), dtype=torch.int32, device=device),
+                        pos=torch.empty((cap,), dtype=torch.int32, device=device),
+                        n=0, cap=cap, H=H)
+
+
+@dataclass
+class Codebook:
+    signs: torch.Tensor   # int8 [d] on the GPU
+    levels: np.ndarray    # float32 [8]
+    thresh: np.ndarray    # float32 [7]
+    d: int = 128
+    n_sub: int = 16
+    m: int = 8
+
+    def c(self) -> skv_codebook:
+        _dev(self.signs, "signs", torch.int8)
+        cb = skv_codebook(self.d, self.n_sub, self.m, _ptr(self.signs))
+        for i in range(8):
+            cb.levels[i] = float(self.levels[i])
+        for i in range(7):
+            cb.thresh[i] = float(self.thresh[i])
+        return cb
+
+
+def new_codebook(signs: torch.Tensor, d: int = 128, n_sub: int = 16) -> Codebook:
+    """Codebook with the library's own Lloyd-Max levels for m = d / n_sub."""
+    lv, th = sparsekv_codebook_init(d // n_sub)
+    return Codebook(signs=signs, levels=lv, thresh=th, d=d, n_sub=n_sub, m=d // n_sub)
+
+
+def sparsekv_encode(cb: Codebook, kv: KVTensors, b: int, t0: int, t1: int, index: IndexTensors):
+    """Append the keys at logical positions [t0, t1) of sequence b to the index."""
+    c = cb.c()
+    kc = kv.c()
+    ic = index.c()
+    _check("sparsekv_encode", lib().sparsekv_encode(ctypes.byref(c), ctypes.byref(kc), b, t0, t1,
+                                                     ctypes.byref(ic), _stream()))
+    index.n = ic.n
+    return index
+
+
+def sparsekv_retrieve(cb: Codebook, index: IndexTensors, q: torch.Tensor, G: int, rho: float,
+                      beta: float, k_final: int, idx: Optional[torch.Tensor] = None,
+                      n_cand: Optional[torch.Tensor] = None, trace: bool = False,
+                      ws: Optional[torch.Tensor] = None):
+    """Returns (idx [H][k_final] logical ids, n_cand [H], trace dict or None)."""
+    _dev(q, "q", torch.bfloat16)
+    dev = q.device
+    H = index.H
+    if idx is None:
+        idx = torch.empty((H, k_final), dtype=torch.int32, device=dev)
+    if n_cand is None:
+        n_cand = torch.empty((H,), dtype=torch.int32, device=dev)
+    ic = index.c()
+    if ws is None:
+        ws = workspace(lib().sparsekv_retrieve_workspace_size(ctypes.byref(ic), G, float(beta),
+                                                              k_final), dev)
+    tr = None
+    trc = None
+    if trace:
+        C = max(1, min(index.n, int(math.ceil(float(beta) * index.n))))
+        tr = {"votes": torch.empty((H, index.n), dtype=torch.uint8, device=dev),
+              "cand": torch.empty((H, C), dtype=torch.int32, device=dev),
+              "est": torch.empty((H, C), dtype=torch.float32, device=dev)}
+        trc = skv_retrieve_trace(_ptr(tr["votes"]), _ptr(tr["cand"]), _ptr(tr["est"]))
+    c = cb.c()
+    _check("sparsekv_retrieve",
+           lib().sparsekv_retrieve(ctypes.byref(c), ctypes.byref(ic), _ptr(q), G, float(rho),
+                                   float(beta), k_final, _ptr(idx), _ptr(n_cand),
+                                   ctypes.byref(trc) if trc is not None else None, _ptr(ws),
+                                   ws.numel() * ws.element_size(), _stream()))
+    return idx, n_cand, tr
+
+
+def retrieve_workspace_size(index: IndexTensors, G: int, beta: float, k_final: int) -> int:
+    ic = index.c()
+    return int(lib().sparsekv_retrieve_workspace_size(ctypes.byref(ic), G, float(beta), k_final))

@@ -1,0 +1,117 @@
+"""GPU parity of ParisKV compressed-code retrieval (encode bit-exact; votes,
+candidates, rerank estimates and the final top-k identical) against the fp32
+oracle, plus attention over the retrieved set."""
+import numpy as np
+import pytest
+import torch
+
+import sparse_top_kv_indexer_amd as S
+import workloads as W
+from oracle import dense as D
+from oracle import lloyd
+from oracle import paris as P
+
+from gpu_helpers import ATTN_TOL, DEV, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_index(p, cb):
+    kv = S.kv_to_device(p.kv(), DEV)
+    index = S.new_index(p.H, p.n + 7, device=DEV)
+    S.sparsekv_encode(cb, kv, 0, p.sink, p.L - p.local, index)
+    torch.cuda.synchronize()
+    return kv, index
+
+
+def _codebook(p):
+    cb = S.new_codebook(torch.from_numpy(p.signs).to(DEV))
+    lv, th = lloyd.codebook_f32(8)
+    assert cb.levels.view(np.uint32).tolist() == lv.view(np.uint32).tolist()
+    return cb, lv, th
+
+
+@pytest.mark.parametrize("L,tag", [(3000, 11), (9000, 12)])
+def test_encode_bit_exact(L, tag):
+    p = W.make_paris(tag=tag, H=2, G=4, L=L, sink=4, local=64)
+    say("encode", p.name, "n", p.n)
+    cb, lv, th = _codebook(p)
+    _, index = _gpu_index(p, cb)
+    ref = P.build_index(p, lv, th)
+    n = p.n
+    assert index.n == n
+    ids = index.ids[:, :n].cpu().numpy()
+    codes = index.codes[:, :n].cpu().numpy()
+    w = index.w[:, :n].cpu().numpy()
+    assert np.array_equal(ids, ref["ids"])
+    assert np.array_equal(codes, ref["codes"])
+    bad = (w.view(np.uint32) != ref["w"].view(np.uint32))
+    assert not bad.any(), (int(bad.sum()), w[bad][:4], ref["w"][bad][:4])
+    assert np.array_equal(index.hist.cpu().numpy(), ref["hist"])
+    assert np.array_equal(index.pos[:n].cpu().numpy(), ref["pos"])
+
+
+def test_encode_appends_in_pieces():
+    """Two appends give the same index as one."""
+    p = W.make_paris(tag=13, H=2, G=4, L=5000, sink=4, local=64)
+    cb, lv, th = _codebook(p)
+    kv = S.kv_to_device(p.kv(), DEV)
+    index = S.new_index(p.H, p.n, device=DEV)
+    mid = 1234
+    S.sparsekv_encode(cb, kv, 0, p.sink, mid, index)
+    S.sparsekv_encode(cb, kv, 0, mid, p.L - p.local, index)
+    ref = P.build_index(p, lv, th)
+    assert index.n == p.n
+    assert np.array_equal(index.ids.cpu().numpy(), ref["ids"])
+    assert np.array_equal(index.w.cpu().numpy().view(np.uint32), ref["w"].view(np.uint32))
+    assert np.array_equal(index.hist.cpu().numpy(), ref["hist"])
+    with pytest.raises(S.SkvError):
+        S.sparsekv_encode(cb, kv, 0, 4, 10, index)          # index is full
+
+
+@pytest.mark.parametrize("L,tag,beta,k_final", [(6000, 21, 0.05, 100), (20000, 22, 0.02, 100),
+                                                (3000, 23, 1.0, 64)])
+def test_retrieve_identical(L, tag, beta, k_final):
+    p = W.make_paris(tag=tag, H=2, G=4, L=L, sink=4, local=64, beta=beta, rho=beta,
+                     k_final=k_final)
+    say("retrieve", p.name, "n", p.n, "beta", beta)
+    cb, lv, th = _codebook(p)
+    _, index = _gpu_index(p, cb)
+    q = S.to_device(p.q, DEV, bf16=True)
+    idx, n_cand, tr = S.sparsekv_retrieve(cb, index, q, p.G, p.rho, p.beta, p.k_final, trace=True)
+    torch.cuda.synchronize()
+    ref_index = P.build_index(p, lv, th)
+    ref = P.retrieve(p, ref_index, lv)
+    votes, cand, est = (tr["votes"].cpu().numpy(), tr["cand"].cpu().numpy(),
+                        tr["est"].cpu().numpy())
+    idx, n_cand = idx.cpu().numpy(), n_cand.cpu().numpy()
+    true = P.exact_top(p, 100)
+    for h in range(p.H):
+        assert np.array_equal(votes[h], ref["S"][h]), h
+        assert np.array_equal(cand[h], ref["cand"][h]), h
+        assert np.array_equal(est[h].view(np.uint32), ref["est"][h].view(np.uint32)), h
+        got = idx[h][: n_cand[h]]
+        assert n_cand[h] == len(ref["idx"][h])
+        assert got.tolist() == sorted(ref["idx"][h].tolist()), h
+        assert np.all(idx[h][n_cand[h]:] == -1)
+        say("  h", h, "recall@100", P.recall_at(got, true[h]))
+
+
+def test_attention_over_retrieved_set():
+    p = W.make_paris(tag=31, H=2, G=4, L=12000, sink=4, local=512)
+    cb, lv, th = _codebook(p)
+    kv, index = _gpu_index(p, cb)
+    q = S.to_device(p.q, DEV, bf16=True)
+    idx, n_cand, _ = S.sparsekv_retrieve(cb, index, q, p.G, p.rho, p.beta, p.k_final)
+    lo = torch.tensor([p.sink], dtype=torch.int32, device=DEV)
+    hi = torch.tensor([p.L - p.local], dtype=torch.int32, device=DEV)
+    out = S.sparsekv_gather_attend(kv, q.view(1, p.H * p.G, p.d), p.G, idx.view(1, p.H, -1),
+                                   p.k_final, lo, hi, p.scale)
+    out = out.cpu().numpy()[0]
+    ref = P.retrieve(p, P.build_index(p, lv, th), lv)
+    kvn = p.kv()
+    qn = p.q.reshape(1, p.H * p.G, p.d)
+    for h in range(p.H):
+        o = D.attend_row(kvn, qn, p.G, 0, h, ref["idx"][h], p.sink, p.L - p.local, p.scale)
+        err = np.abs(out[h * p.G:(h + 1) * p.G] - o).max()
+        assert err <= ATTN_TOL, (h, err)

@@ -309,17 +309,22 @@ hipError_t launch_gather_attend(const KvArgs& kv, const void* q, int G, const in
     e = npl == 1 ? launch_split<false, 1>(kv, q, G, idx, k, lo, hi, scale_log2, n_split, part, st)
                  : launch_split<false, 2>(kv, q, G, idx, k, lo, hi, scale_log2, n_split, part, st);
   if (e != hipSuccess) return e;
-  dim3 grid(kv.H * G, kv.B);
-  const size_t lds = (size_t)n_split * (kv.d_v + 2) * sizeof(float);
+  return launch_attend_reduce(part, n_split, kv.d_v, kv.H * G, kv.B, out, st);
+}
+
+hipError_t launch_attend_reduce(const float* part, int n_split, int D, int HG, int B, float* out,
+                                hipStream_t st) {
+  dim3 grid(HG, B);
+  const size_t lds = (size_t)n_split * (D + 2) * sizeof(float);
   static bool attr_set = false;
   if (!attr_set) {
-    e = hipFuncSetAttribute((const void*)attend_reduce_kernel,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 64 * (256 + 2) * 4);
+    hipError_t e = hipFuncSetAttribute((const void*)attend_reduce_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       64 * (512 + 2) * 4);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  attend_reduce_kernel<<<grid, 256, lds, st>>>(part, n_split, kv.d_v, kv.H * G, out);
-  (void)ws_bytes;
+  attend_reduce_kernel<<<grid, 256, lds, st>>>(part, n_split, D, HG, out);
   return hipGetLastError();
 }
 

@@ -40,6 +40,10 @@ hipError_t launch_gather_attend(const KvArgs& kv, const void* q, int G, const in
                                 const int32_t* lo, const int32_t* hi, float scale, float* out,
                                 void* ws, size_t ws_bytes, hipStream_t s);
 bool attend_supported(const KvArgs& kv, int G);
+// merge of split partials [B][HG][n_split][D + 2] (acc[D], max, sum; log2
+// domain) into out [B][HG][D]
+hipError_t launch_attend_reduce(const float* part, int n_split, int D, int HG, int B, float* out,
+                                hipStream_t s);
 
 // mla.hip: shared-latent attention on matrix cores (v == nullptr)
 bool mla_supported(const KvArgs& kv, int G);

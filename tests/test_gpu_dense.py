@@ -212,3 +212,34 @@ def test_token_pool_full_size_sampled_rows():
     st = W.make_token_pool()
     rows = [(0, 0), (13, 4), (31, 7)]
     assert _end_to_end(st, rows=rows) == 0
+
+
+# ------------------------------------------- indexer + shared-latent attention
+@pytest.mark.parametrize("L,k,heads", [(4096, 256, 128), (2048, 300, 16), (1024, 77, 64)])
+def test_indexer_mla_small(L, k, heads):
+    st = W.make_indexer_mla(tag=300 + heads, L=L, k=k, n_heads=heads)
+    assert _end_to_end(st) == 0
+
+
+def test_mla_with_sink_local_and_ragged_tail():
+    st = W.make_indexer_mla(tag=310, L=2048, k=200, n_heads=32)
+    st.lo = np.array([4], np.int32)
+    st.hi = np.array([2048 - 70], np.int32)
+    assert _end_to_end(st) == 0
+
+
+def test_mla_attend_kernel_on_oracle_selection():
+    st = W.make_indexer_mla(tag=311, L=8192, k=1000, n_heads=128)
+    ref = D.step(st)
+    r = Run(st)
+    idx = torch.from_numpy(ref["idx"].astype(np.int32)).to(DEV)
+    out = r.attend(idx).cpu().numpy()
+    err = np.abs(out - ref["out"]).max()
+    say("  mla max err", err)
+    assert err <= ATTN_TOL
+
+
+@pytest.mark.slow
+def test_indexer_mla_full_size():
+    st = W.make_indexer_mla()
+    assert _end_to_end(st) == 0

@@ -115,3 +115,49 @@ def test_attention_over_retrieved_set():
         o = D.attend_row(kvn, qn, p.G, 0, h, ref["idx"][h], p.sink, p.L - p.local, p.scale)
         err = np.abs(out[h * p.G:(h + 1) * p.G] - o).max()
         assert err <= ATTN_TOL, (h, err)
+
+
+@pytest.mark.slow
+def test_full_size_against_stored_oracle_results():
+    """The full compressed-code workload (8 x 1,048,576 keys): GPU encode and
+    retrieval against the oracle's results stored by
+    tests/golden/make_paris_full.py (votes, candidate set and rerank
+    estimates by hash, final ids, attention outputs)."""
+    import hashlib
+    import json
+    import os
+    gold = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                       "paris_full_expected.json")))
+    p = W.make_paris()
+    assert p.n == gold["n"]
+    cb, lv, th = _codebook(p)
+    assert lv.view(np.uint32).tolist() == gold["levels_bits"]
+    kv, index = _gpu_index(p, cb)
+    q = S.to_device(p.q, DEV, bf16=True)
+    idx, n_cand, tr = S.sparsekv_retrieve(cb, index, q, p.G, p.rho, p.beta, p.k_final, trace=True)
+    lo = torch.tensor([p.sink], dtype=torch.int32, device=DEV)
+    hi = torch.tensor([p.L - p.local], dtype=torch.int32, device=DEV)
+    out = S.sparsekv_gather_attend(kv, q.view(1, p.H * p.G, p.d), p.G, idx.view(1, p.H, -1),
+                                   p.k_final, lo, hi, p.scale)
+    torch.cuda.synchronize()
+    sha = lambda a: hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()
+    idx, n_cand, out = idx.cpu().numpy(), n_cand.cpu().numpy(), out.cpu().numpy()[0]
+    hist = index.hist.cpu().numpy()
+    for h, g in enumerate(gold["heads"]):
+        say("head", h)
+        assert sha(hist[h].astype(np.int32)) == g["index_hist_sha256"]
+        for e, smp in g["samples"].items():
+            e = int(e)
+            assert index.ids[h, e].cpu().numpy().tolist() == smp["ids"]
+            assert index.codes[h, e].cpu().numpy().tolist() == smp["codes"]
+            assert index.w[h, e].cpu().numpy().view(np.uint32).tolist() == smp["w_bits"]
+        votes = tr["votes"][h].cpu().numpy()
+        assert np.bincount(votes, minlength=97).tolist() == g["vote_hist"]
+        assert sha(votes) == g["votes_sha256"]
+        assert sha(tr["cand"][h].cpu().numpy().astype(np.int32)) == g["cand_sha256"]
+        assert sha(tr["est"][h].cpu().numpy().astype(np.float32)) == g["est_sha256"]
+        assert n_cand[h] == g["n_cand"]
+        assert idx[h][: n_cand[h]].tolist() == g["idx"]
+        err = np.abs(out[h * p.G:(h + 1) * p.G] - np.array(g["out"])).max()
+        assert err <= ATTN_TOL, (h, err)
+        say("  recall@100 (oracle and GPU)", g["recall_at_100"])

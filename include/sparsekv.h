@@ -157,8 +157,9 @@ skv_status sparsekv_topk_resume(const float* scores, int32_t B, int32_t H, int32
  * values) merged exactly by log-sum-exp.  idx entries of -1 are skipped.
  *   q   [B][H*G][d_k] (kv dtype);  idx [B][H][k] int32 logical positions
  *   out [B][H*G][d_v] fp32; an empty A gives 0.
- * Supports d_k == d_v in {64, 128, 256} with G <= 8 (split-k vector path),
- * and the latent case v == NULL, bf16, d_k = 576, d_v = 512, H = 1,
+ * Supports d_k == d_v with: bf16, d = 128, G <= 16 (matrix-core scores);
+ * bf16, d = 256, G <= 4; fp32, d = 64, G <= 8; fp32, d = 128, G <= 4
+ * (split-k vector path); and the latent case v == NULL, bf16, d_k = 576, d_v = 512, H = 1,
  * G % 16 == 0 (matrix-core path). */
 skv_status sparsekv_gather_attend(const skv_kv* kv, const void* q, int32_t G, const int32_t* idx,
                                   int32_t k, skv_window win, float scale, float* out, void* ws,

@@ -220,6 +220,181 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(
   }
 }
 
+// bf16, d_k = d_v = 128, 1 <= G <= GMAX <= 16.  A wave takes 16 attended
+// tokens at a time: the logits come from matrix cores as
+//   S^T[16 tokens x 16 heads] = K_chunk . Q^T   (4 x v_mfma_f32_16x16x32_bf16)
+// so lane (n, g4) holds the four logits of query head n for tokens 4 g4 .. +3,
+// the softmax statistics need only a max / sum over the lane and its three
+// partners, and the value product runs on the vector ALUs with every lane
+// owning two output dims of every head: per token one 256-byte value row is
+// read by the whole wave (4 B per lane) and each probability is broadcast from
+// the lane that holds it (v_readlane).  Two chunks' rows are in flight per
+// wave.
+template <int GMAX>
+__global__ __launch_bounds__(kThreads) void attend_mfma_kernel(
+    KvArgs kv, const uint16_t* q, int G, const int32_t* idx, int k, const int32_t* lo_p,
+    const int32_t* hi_p, float scale_log2, int n_split, float* part) {
+  constexpr int D = 128;
+  constexpr int CH = 2;                  // chunks of 16 tokens in flight per wave
+  __shared__ int64_t rows_sh[kThreads];
+  __shared__ float red[4][GMAX][D + 2];
+  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, g4 = lane >> 4;
+
+  bf16x8_t Qf[4];
+  {
+    const uint16_t* qrow = q + (((int64_t)b * kv.H + h) * G + (n < G ? n : 0)) * D;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const u32x4_t w = n < G ? ld16((const char*)(qrow + 8 * (4 * j + g4))) : u32x4_t{0, 0, 0, 0};
+      Qf[j] = __builtin_bit_cast(bf16x8_t, w);
+    }
+  }
+  const int seq = min(kv.seq_len[b], kv.L_max);
+  const int lo = max(0, min(lo_p[b], seq));
+  const int hi = max(lo, min(hi_p[b], seq));
+  const int n_list = k + lo + (seq - hi);
+  const int chunk = (n_list + n_split - 1) / n_split;
+  const int p0 = s * chunk, p1 = min(n_list, p0 + chunk);
+  const int32_t* irow = idx + ((int64_t)b * kv.H + h) * k;
+
+  float m_run = -INFINITY, l_run = 0.f;     // head n (lanes n < G)
+  float acc[GMAX][2];                       // dims 2 lane, 2 lane + 1 of every head
+#pragma unroll
+  for (int g = 0; g < GMAX; ++g) acc[g][0] = acc[g][1] = 0.f;
+
+  const uint16_t* kb = (const uint16_t*)kv.k;
+  const uint16_t* vb = (const uint16_t*)kv.v;
+  for (int q0 = p0; q0 < p1; q0 += kThreads) {
+    const int cnt = min(kThreads, p1 - q0);
+    if ((int)threadIdx.x < cnt) {
+      const int pos = q0 + threadIdx.x;
+      int t;
+      if (pos < k) {
+        t = irow[pos];
+        if (t < lo || t >= hi) t = -1;
+      } else if (pos - k < lo) {
+        t = pos - k;
+      } else {
+        t = hi + (pos - k - lo);
+      }
+      const int64_t slot = t >= 0 ? slot_of(kv, b, t) : -1;
+      rows_sh[threadIdx.x] = slot >= 0 ? row_elem(kv, b, h, slot, D) : -1;
+    } else {
+      rows_sh[threadIdx.x] = -1;
+    }
+    __syncthreads();
+    const int n_ch = (cnt + 15) >> 4;
+    for (int c0 = wave; c0 < n_ch; c0 += 4 * CH) {
+      bf16x8_t Kf[CH][4];
+      uint32_t Vw[CH][16];
+#pragma unroll
+      for (int u = 0; u < CH; ++u) {
+        const int c = c0 + 4 * u;
+        const int64_t rk = c < n_ch ? rows_sh[c * 16 + n] : -1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const u32x4_t w = rk >= 0 ? ld16((const char*)(kb + rk + 8 * (4 * j + g4)))
+                                    : u32x4_t{0, 0, 0, 0};
+          Kf[u][j] = __builtin_bit_cast(bf16x8_t, w);
+        }
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          const int64_t rv = c < n_ch ? rows_sh[c * 16 + t] : -1;
+          Vw[u][t] = rv >= 0 ? *(const uint32_t*)(vb + rv + 2 * lane) : 0u;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < CH; ++u) {
+        const int c = c0 + 4 * u;
+        if (c < n_ch) {                             // uniform over the wave
+        f32x4_t S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Kf[u][j], Qf[j], S, 0, 0, 0);
+        float z[4], cm = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool ok = rows_sh[c * 16 + 4 * g4 + i] >= 0;
+          z[i] = ok ? S[i] * scale_log2 : -INFINITY;
+          cm = fmaxf(cm, z[i]);
+        }
+        cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
+        cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
+        const float m_new = fmaxf(m_run, cm);
+        float p[4], ps = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[i] = m_new == -INFINITY ? 0.f : exp2f(z[i] - m_new);
+          ps += p[i];
+        }
+        ps += __shfl_xor(ps, 16, 64);
+        ps += __shfl_xor(ps, 32, 64);
+        const float corr = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
+        l_run = l_run * corr + ps;
+        m_run = m_new;
+        float vf[16][2];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          vf[t][0] = bf16_lo(Vw[u][t]);
+          vf[t][1] = bf16_hi(Vw[u][t]);
+        }
+#pragma unroll
+        for (int g = 0; g < GMAX; ++g) {
+          if (g < G) {
+          const float cg = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(corr), g));
+          float a0 = acc[g][0] * cg, a1 = acc[g][1] * cg;
+#pragma unroll
+          for (int t = 0; t < 16; ++t) {
+            const float pg = __int_as_float(
+                __builtin_amdgcn_readlane(__float_as_int(p[t & 3]), g + 16 * (t >> 2)));
+            a0 = fmaf(pg, vf[t][0], a0);
+            a1 = fmaf(pg, vf[t][1], a1);
+          }
+          acc[g][0] = a0;
+          acc[g][1] = a1;
+          }
+        }
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // merge the four waves through LDS
+#pragma unroll
+  for (int g = 0; g < GMAX; ++g) {
+    if (g >= G) continue;
+    red[wave][g][2 * lane] = acc[g][0];
+    red[wave][g][2 * lane + 1] = acc[g][1];
+    if (lane == g) {
+      red[wave][g][D] = m_run;
+      red[wave][g][D + 1] = l_run;
+    }
+  }
+  __syncthreads();
+  const int stride = D + 2;
+  for (int i = threadIdx.x; i < G * D; i += kThreads) {
+    const int g = i / D, j = i - g * D;
+    float mm = -INFINITY;
+    for (int w = 0; w < 4; ++w) mm = fmaxf(mm, red[w][g][D]);
+    float ll = 0.f, aa = 0.f;
+    if (mm != -INFINITY) {
+      for (int w = 0; w < 4; ++w) {
+        const float cw = exp2f(red[w][g][D] - mm);
+        ll += red[w][g][D + 1] * cw;
+        aa += red[w][g][j] * cw;
+      }
+    }
+    float* dst = part + ((((int64_t)b * kv.H + h) * G + g) * n_split + s) * stride;
+    dst[j] = aa;
+    if (j == 0) {
+      dst[D] = mm;
+      dst[D + 1] = ll;
+    }
+  }
+}
+
 // out[b][hq][j] = sum_s acc_s[j] 2^(m_s - M) / sum_s l_s 2^(m_s - M)
 // One workgroup per (b, query head); the split partials are staged in LDS with
 // all loads issued at once.
@@ -232,7 +407,7 @@ __global__ __launch_bounds__(256) void attend_reduce_kernel(const float* part, i
   const int stride = D + 2;
   const int n = n_split * stride;
   const float* base = part + ((int64_t)b * HG + hq) * n;
-  for (int i = threadIdx.x; i < n; i += blockDim.x) ps[i] = base[i];
+  stage_words<16>((uint32_t*)ps, (const uint32_t*)base, n, threadIdx.x, blockDim.x);
   __syncthreads();
   if (threadIdx.x < 64) {
     const int s = threadIdx.x;
@@ -286,6 +461,7 @@ bool attend_supported(const KvArgs& kv, int G) {
   if (kv.v == nullptr || kv.d_k != kv.d_v) return false;
   const int npl = pieces_per_lane(kv);
   if (npl != 1 && npl != 2) return false;
+  if (kv.bf16 && kv.d_k == 128) return G >= 1 && G <= 16;    // matrix-core path
   if (G < 1 || G > 8 || (npl == 2 && G > 4)) return false;
   return true;
 }
@@ -302,7 +478,19 @@ hipError_t launch_gather_attend(const KvArgs& kv, const void* q, int G, const in
   const float scale_log2 = scale * 1.4426950408889634f;
   hipError_t e;
   const int npl = pieces_per_lane(kv);
-  if (kv.bf16)
+  if (kv.bf16 && kv.d_k == 128 && G <= 16) {
+    dim3 grid(n_split, kv.H, kv.B);
+    const uint16_t* qq = (const uint16_t*)q;
+    if (G <= 1)
+      attend_mfma_kernel<1><<<grid, kThreads, 0, st>>>(kv, qq, G, idx, k, lo, hi, scale_log2, n_split, part);
+    else if (G <= 4)
+      attend_mfma_kernel<4><<<grid, kThreads, 0, st>>>(kv, qq, G, idx, k, lo, hi, scale_log2, n_split, part);
+    else if (G <= 8)
+      attend_mfma_kernel<8><<<grid, kThreads, 0, st>>>(kv, qq, G, idx, k, lo, hi, scale_log2, n_split, part);
+    else
+      attend_mfma_kernel<16><<<grid, kThreads, 0, st>>>(kv, qq, G, idx, k, lo, hi, scale_log2, n_split, part);
+    e = hipGetLastError();
+  } else if (kv.bf16)
     e = npl == 1 ? launch_split<true, 1>(kv, q, G, idx, k, lo, hi, scale_log2, n_split, part, st)
                  : launch_split<true, 2>(kv, q, G, idx, k, lo, hi, scale_log2, n_split, part, st);
   else

@@ -99,12 +99,37 @@ __global__ __launch_bounds__(WAVES * 64) void mla_split_kernel(
       roff[tid] = ro;
     }
     __syncthreads();
-    // stage the rows: 72 pieces of 16 B per row, all loads in flight together
-    for (int i = tid; i < kStage * (kDk / 8); i += WAVES * 64) {
-      const int r = i / (kDk / 8), pc = i - r * (kDk / 8);
-      const int64_t ro = roff[r];
-      const u32x4_t v = ro >= 0 ? *(const u32x4_t*)(kb + ro + 8 * pc) : u32x4_t{0, 0, 0, 0};
-      *(u32x4_t*)(rows + r * kRowPad + 8 * pc) = v;
+    // stage the rows: 72 pieces of 16 B per row.  With up to four waves each
+    // thread keeps four loads in flight before their LDS stores; eight waves
+    // have no registers to spare and issue one load per store.
+    {
+      constexpr int kPieces = kStage * (kDk / 8);
+      if constexpr (WAVES >= 8) {
+        for (int i = tid; i < kPieces; i += WAVES * 64) {
+          const int r = i / (kDk / 8), pc = i - r * (kDk / 8);
+          const int64_t ro = roff[r];
+          const u32x4_t v = ro >= 0 ? *(const u32x4_t*)(kb + ro + 8 * pc) : u32x4_t{0, 0, 0, 0};
+          *(u32x4_t*)(rows + r * kRowPad + 8 * pc) = v;
+        }
+      } else {
+        constexpr int kB = 4;
+        for (int i0 = 0; i0 < kPieces; i0 += kB * WAVES * 64) {
+          u32x4_t v[kB];
+#pragma unroll
+          for (int u = 0; u < kB; ++u) {
+            const int i = i0 + u * WAVES * 64 + tid;
+            const int r = i / (kDk / 8), pc = i - r * (kDk / 8);
+            const int64_t ro = i < kPieces ? roff[r] : -1;
+            v[u] = ro >= 0 ? *(const u32x4_t*)(kb + ro + 8 * pc) : u32x4_t{0, 0, 0, 0};
+          }
+#pragma unroll
+          for (int u = 0; u < kB; ++u) {
+            const int i = i0 + u * WAVES * 64 + tid;
+            const int r = i / (kDk / 8), pc = i - r * (kDk / 8);
+            if (i < kPieces) *(u32x4_t*)(rows + r * kRowPad + 8 * pc) = v[u];
+          }
+        }
+      }
     }
     __syncthreads();
 

@@ -24,7 +24,7 @@ namespace skv {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTile = 512;  // tokens per workgroup (multiple of 16)
+constexpr int kTile = 256;  // tokens per workgroup (multiple of 16)
 
 __device__ __forceinline__ u32x4_t ld16(const char* p) { return *(const u32x4_t*)p; }
 

@@ -74,6 +74,27 @@ __device__ __forceinline__ int wave_excl_scan(int v, int lane) {
   return x - v;
 }
 
+// Copy n 4-byte words from global memory to LDS with up to PER loads per
+// thread in flight at once (a plain copy loop waits for every load before its
+// LDS store, one memory latency per iteration).
+template <int PER>
+__device__ __forceinline__ void stage_words(uint32_t* dst, const uint32_t* src, int n, int tid,
+                                            int nthreads) {
+  for (int base = 0; base < n; base += PER * nthreads) {
+    uint32_t v[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = base + u * nthreads + tid;
+      v[u] = i < n ? src[i] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = base + u * nthreads + tid;
+      if (i < n) dst[i] = v[u];
+    }
+  }
+}
+
 __device__ __forceinline__ uint64_t lanemask_lt(int lane) {
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }

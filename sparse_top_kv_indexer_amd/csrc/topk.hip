@@ -16,7 +16,7 @@
 //                keys inside b0 in its own candidate block;
 //   3. write     every tile gathers its row's candidates (a few hundred keys
 //                for smooth score distributions) into LDS, resolves the exact
-//                32-bit threshold T with two more radix digits (12 + 8 bits),
+//                32-bit threshold T with three more radix digits (8 + 8 + 4 bits),
 //                decides how many keys equal to T each tile takes (lowest
 //                indices first) and prefix-sums the tiles' output offsets,
 //                then writes its own selected positions in index order with
@@ -78,28 +78,33 @@ __device__ __forceinline__ int block_excl_scan(int v, int* wsum, int& total) {
   return before;
 }
 
-// The bin holding the need-th largest entry of hist[kBins] (1 <= need <=
-// sum); *above_out receives the number of entries in higher bins.
+// The bin holding the need-th largest entry of hist[NB] (1 <= need <= sum);
+// *above_out receives the number of entries in higher bins.
+template <int NB>
 __device__ int find_bin(const uint32_t* hist, int need, int* above_out, int* wsum, int* pair) {
-  constexpr int per = kBins / kThreads;
+  constexpr int per = NB >= kThreads ? NB / kThreads : 1;
   const int b0 = threadIdx.x * per;
   if (threadIdx.x == 0) {
     pair[0] = 0;
     pair[1] = 0;
   }
   int tot = 0;
+  if (b0 < NB) {
 #pragma unroll
-  for (int j = 0; j < per; ++j) tot += (int)hist[b0 + j];
+    for (int j = 0; j < per; ++j) tot += (int)hist[b0 + j];
+  }
   int all;
   const int before = block_excl_scan(tot, wsum, all);
   int above = all - before - tot;
-  for (int j = per - 1; j >= 0; --j) {
-    const int c = (int)hist[b0 + j];
-    if (above < need && need <= above + c) {
-      pair[0] = b0 + j;
-      pair[1] = above;
+  if (b0 < NB) {
+    for (int j = per - 1; j >= 0; --j) {
+      const int c = (int)hist[b0 + j];
+      if (above < need && need <= above + c) {
+        pair[0] = b0 + j;
+        pair[1] = above;
+      }
+      above += c;
     }
-    above += c;
   }
   __syncthreads();
   const int bin = pair[0];
@@ -163,8 +168,7 @@ __global__ __launch_bounds__(kThreads) void topk_classify_kernel(
     const int i = u * kThreads + threadIdx.x;
     sv[u] = i < cnt ? s[i] : -INFINITY;
   }
-  const uint32_t* g = ws.hist + (int64_t)row * kBins;
-  for (int i = threadIdx.x; i < kBins; i += kThreads) hist[i] = g[i];
+  stage_words<kBins / kThreads>(hist, ws.hist + (int64_t)row * kBins, kBins, threadIdx.x, kThreads);
   if (threadIdx.x == 0) s_in = 0;
   __syncthreads();
   int tot_local = 0;
@@ -177,7 +181,7 @@ __global__ __launch_bounds__(kThreads) void topk_classify_kernel(
   // 2: keys above b0 are taken and the threshold lies inside b0
   int mode = 0, b0 = 0, above0 = 0;
   if (k_sel < n_cand) {
-    b0 = find_bin(hist, k_sel, &above0, wsum, pair);
+    b0 = find_bin<kBins>(hist, k_sel, &above0, wsum, pair);
     mode = (k_sel - above0 == (int)hist[b0]) ? 1 : 2;
   }
   if (tile == 0 && threadIdx.x == 0) {
@@ -311,12 +315,14 @@ __global__ __launch_bounds__(kThreads) void topk_write_kernel(const float* score
   if (mode == 1) {
     T = ((uint32_t)b0 << 20) - 1u;
   } else if (mode == 2) {
+    // the low 20 bits in three digits of 8, 8 and 4 bits over the few
+    // candidates of the threshold bin
     int need = k_sel - above0;
     uint32_t prefix = (uint32_t)b0 << 20, mask = 0xfff00000u;
-    for (int pass = 0; pass < 2; ++pass) {
-      const int shift = pass == 0 ? 8 : 0;
-      const uint32_t nbm = pass == 0 ? 4095u : 255u;
-      for (int i = threadIdx.x; i < kBins; i += kThreads) hist[i] = 0;
+    for (int pass = 0; pass < 3; ++pass) {
+      const int shift = pass == 0 ? 12 : (pass == 1 ? 4 : 0);
+      const uint32_t nbm = pass < 2 ? 255u : 15u;
+      for (int i = threadIdx.x; i < 256; i += kThreads) hist[i] = 0;
       __syncthreads();
       if (in_lds) {
         for (int f = threadIdx.x; f < n_c; f += kThreads) {
@@ -332,7 +338,7 @@ __global__ __launch_bounds__(kThreads) void topk_write_kernel(const float* score
       }
       __syncthreads();
       int above;
-      const int bin = find_bin(hist, need, &above, wsum, pair);
+      const int bin = find_bin<256>(hist, need, &above, wsum, pair);
       const int in_bin = (int)hist[bin];
       need -= above;
       prefix |= (uint32_t)bin << shift;

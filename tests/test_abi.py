@@ -97,7 +97,7 @@ def test_argument_validation_paths():
                                   float("nan"), ctypes.c_void_p(1), ctypes.c_void_p(1), need, None)
     assert st == S.SKV_EINVAL
     # unsupported attention shape (G > 8 on the vector path)
-    st = L.sparsekv_gather_attend(ctypes.byref(kv), ctypes.c_void_p(1), 9, ctypes.c_void_p(1), 256, win,
+    st = L.sparsekv_gather_attend(ctypes.byref(kv), ctypes.c_void_p(1), 17, ctypes.c_void_p(1), 256, win,
                                   0.1, ctypes.c_void_p(1), ctypes.c_void_p(1), 1 << 30, None)
     assert st == S.SKV_EUNSUPPORTED
 

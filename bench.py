@@ -11,15 +11,27 @@ Default workload (the GQA paged decode the metric is quoted on):
   permutation, 4 outlier channels per KV head scaled x8, top-k = 2048 per KV
   head plus 4 sink and 64 local tokens.
 
+Successive steps use distinct device copies of the KV pool in turn (four by
+default, like four layers), so that a step never finds its keys in the 256 MB
+last-level cache left by the step before.  The K timed steps are captured
+into one HIP graph and replayed once, as a serving loop would (--eager
+launches every kernel from the host instead).  Per-kernel durations come from
+HIP events: with --eager inside the timed region; otherwise from a second
+graph of the same K steps with event-record nodes around each call, replayed
+right after the timed one (event nodes cost about 14 us per step on this
+runtime, so the timed graph carries none).
+
 Prints ONE JSON line (rank 0, N = 1) with the throughput in history keys
 scanned per second, the per-step time, the roofline entry of the dominant
 kernel (the score scan) and the CPU oracle timed on a bounded sample.
 
-  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--kv-copies C] [--eager]
+                  [--no-cpu-baseline]
 """
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -40,6 +52,13 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gqa_paged", choices=WORKLOADS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kv-copies", type=int, default=4,
+                    help="distinct device copies of the KV pool, used in turn by successive "
+                         "steps (like successive layers), so that no step finds its keys in "
+                         "the 256 MB last-level cache")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every kernel from the host instead of replaying one HIP graph "
+                         "that holds the K timed steps")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -94,6 +113,57 @@ def traffic_entry(kernel_src, n_launch_bytes_alg):
         return rec["hbm_bytes_per_launch"]
     except Exception:
         return None
+
+
+class HipEvents:
+    """HIP events through the runtime torch already loaded.  graph_record()
+    inserts an event-record node into the graph being captured on the
+    current stream (torch does not offer external events on ROCm)."""
+
+    def __init__(self):
+        import ctypes
+        import torch
+        self.ct = ctypes
+        self.torch = torch
+        self.lib = ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
+        self.events = []
+
+    def _ok(self, rc, what):
+        if rc != 0:
+            raise RuntimeError("%s failed with HIP error %d" % (what, rc))
+
+    def _stream(self):
+        return self.ct.c_void_p(self.torch.cuda.current_stream().cuda_stream)
+
+    def create(self):
+        e = self.ct.c_void_p()
+        self._ok(self.lib.hipEventCreate(self.ct.byref(e)), "hipEventCreate")
+        self.events.append(e)
+        return e
+
+    def record(self, e):
+        self._ok(self.lib.hipEventRecord(e, self._stream()), "hipEventRecord")
+
+    def graph_record(self, e):
+        ct, s = self.ct, self._stream()
+        status, cid, graph = ct.c_int(), ct.c_ulonglong(), ct.c_void_p()
+        deps, nd = ct.POINTER(ct.c_void_p)(), ct.c_size_t()
+        self._ok(self.lib.hipStreamGetCaptureInfo_v2(s, ct.byref(status), ct.byref(cid), ct.byref(graph),
+                                                     ct.byref(deps), ct.byref(nd)),
+                 "hipStreamGetCaptureInfo_v2")
+        if status.value != 1:
+            raise RuntimeError("graph_record outside a stream capture")
+        node = ct.c_void_p()
+        self._ok(self.lib.hipGraphAddEventRecordNode(ct.byref(node), graph, deps, nd, e),
+                 "hipGraphAddEventRecordNode")
+        # the new node becomes the only dependency of what is captured next
+        self._ok(self.lib.hipStreamUpdateCaptureDependencies(s, ct.byref(node), ct.c_size_t(1), 1),
+                 "hipStreamUpdateCaptureDependencies")
+
+    def elapsed_ms(self, a, b):
+        ms = self.ct.c_float()
+        self._ok(self.lib.hipEventElapsedTime(self.ct.byref(ms), a, b), "hipEventElapsedTime")
+        return ms.value
 
 
 def cpu_baseline(st, n_keys_step):
@@ -153,41 +223,84 @@ def main():
     out = torch.empty((B, H * G, kv.d_v), dtype=torch.float32, device=dev)
     ws = S.workspace(S.sparsekv_workspace_size(S.SKV_OP_GATHER_ATTEND, kv, G, k), dev)
     ws_sel = S.workspace(S.sparsekv_workspace_size(S.SKV_OP_SELECT, kv, G, k), dev)
-    stream = torch.cuda.current_stream()
+    copies = [kv] + [dataclasses.replace(kv, k=kv.k.clone(), v=None if kv.v is None else kv.v.clone())
+                     for _ in range(max(1, args.kv_copies) - 1)]
+    hip = HipEvents()
 
-    def step(ev=None):
+    def step(i, ev=None, in_graph=False):
         # sparsekv_select in its two halves (score scan with the first top-k
         # digit fused, then the rest of the exact top-k), so that the events
         # time the scan alone
+        c = copies[i % len(copies)]
+        mark = (lambda e: hip.graph_record(e)) if in_graph else (lambda e: hip.record(e))
         if ev is not None:
-            ev[0].record(stream)
-        S.sparsekv_score_hist(kv, q, G, lo, hi, scores, ws_sel)
+            mark(ev[0])
+        S.sparsekv_score_hist(c, q, G, lo, hi, scores, ws_sel)
         if ev is not None:
-            ev[1].record(stream)
+            mark(ev[1])
         S.sparsekv_topk_resume(scores, lo, hi, k, idx, cnt, ws_sel)
         if ev is not None:
-            ev[2].record(stream)
-        S.sparsekv_gather_attend(kv, q, G, idx, k, lo, hi, st.scale, out, ws)
+            mark(ev[2])
+        S.sparsekv_gather_attend(c, q, G, idx, k, lo, hi, st.scale, out, ws)
         if ev is not None:
-            ev[3].record(stream)
+            mark(ev[3])
 
-    for _ in range(args.warmup):
-        step()
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
 
-    # timed region: exactly K steps, synchronised on both sides
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    evs = [[hip.create() for _ in range(4)] for _ in range(args.steps)]
+    bracket = [hip.create(), hip.create()]
+    if args.eager:
+        # timed region: exactly K steps launched from the host, with events
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        hip.record(bracket[0])
+        for i in range(args.steps):
+            step(i, evs[i])
+        hip.record(bracket[1])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        timing_note = "per-kernel events recorded inside the timed region"
+    else:
+        # The K steps are captured into one HIP graph and replayed (as a
+        # serving loop would).  Event-record nodes inside a graph cost about
+        # 14 us per step on this runtime, so the timed replay carries none;
+        # the per-kernel durations come from a second graph of the same K
+        # steps, identical except for event-record nodes around each call,
+        # replayed right after.
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step(0)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph, graph_ev = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(args.steps):
+                step(i)
+        with torch.cuda.graph(graph_ev):
+            for i in range(args.steps):
+                step(i, evs[i], in_graph=True)
+        graph.replay()
+        torch.cuda.synchronize()
+        # timed region: exactly K steps (one replay), synchronised on both sides
+        t0 = time.perf_counter()
+        hip.record(bracket[0])
+        graph.replay()
+        hip.record(bracket[1])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        graph_ev.replay()
+        torch.cuda.synchronize()
+        timing_note = ("per-kernel events from a replay of the same K steps with "
+                       "event-record graph nodes, right after the timed replay")
 
-    score_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    topk_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    attn_ms = [e[2].elapsed_time(e[3]) for e in evs]
-    step_ms = [e[0].elapsed_time(e[3]) for e in evs]
+    score_ms = [hip.elapsed_ms(e[0], e[1]) for e in evs]
+    topk_ms = [hip.elapsed_ms(e[1], e[2]) for e in evs]
+    attn_ms = [hip.elapsed_ms(e[2], e[3]) for e in evs]
+    step_ms = [hip.elapsed_ms(e[0], e[3]) for e in evs]
+    gpu_ms_per_step = hip.elapsed_ms(bracket[0], bracket[1]) / args.steps
     ms_per_step = wall * 1e3 / args.steps
     n_keys = live_keys(st)
     per_key = scan_bytes_per_key(st)
@@ -215,8 +328,11 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if bf else "f32",
         "data": "synthetic",
-        "config": workload_config(st),
+        "config": dict(workload_config(st), kv_copies=len(copies),
+                       launch="eager" if args.eager else "hip_graph"),
         "us_per_step": ms_per_step * 1e3,
+        "us_per_step_gpu": gpu_ms_per_step * 1e3,
+        "timing": timing_note,
         "us_per_step_events": {"median": float(np.median(step_ms)) * 1e3,
                                "p10": float(np.percentile(step_ms, 10)) * 1e3,
                                "p90": float(np.percentile(step_ms, 90)) * 1e3},
@@ -227,7 +343,7 @@ def main():
         "step_algorithmic_bytes": step_bytes,
         "step_GBps": step_bytes / (ms_per_step * 1e-3) / 1e9,
         "step_frac_of_hbm_peak": step_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,
-        "roofline": {"kernel": "score scan (sparsekv_score_hist: score_mfma_kernel with the "
+        "roofline": {"kernel": "score scan (sparsekv_score_hist: score_stream_kernel with the "
                                "fused top-k histogram)", "bound": "hbm",
                      "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": tr,

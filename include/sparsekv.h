@@ -34,7 +34,8 @@
  * ------------------------
  * block == 16, block_table: paged pool [n_blocks][H][16][d], logical token t
  *     of sequence b lives in slot block_table[b][t/16]*16 + t%16
- *     (PagedAttention block table; vToken reading notes, background section).
+ *     (PagedAttention block table; vToken reading notes, background section);
+ *     a negative entry marks an unmapped block, whose 16 tokens are dead.
  * block == 16, token_table: the same pool addressed per token,
  *     slot = token_table[b][t] (-1 = dead token)
  *     (vToken reading notes, section 3.2 token table and section 3.4 Eq. (2)).

@@ -58,7 +58,8 @@ def live_slots(kv, b: int):
         return t[keep], slot[keep]
     if kv.block_table is not None:                 # block table, 16-token blocks
         blk = kv.block_table[b, t // 16].astype(np.int64)
-        return t, blk * 16 + t % 16
+        keep = blk >= 0                            # negative entry: unmapped block, dead
+        return t[keep], (blk * 16 + t % 16)[keep]
     return t, t                                    # contiguous storage
 
 

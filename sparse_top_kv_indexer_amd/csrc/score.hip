@@ -8,15 +8,23 @@
 // gfx950 design.  The scan is HBM-bound: 256 B per bf16 key of d = 128.
 //  * GQA groups (bf16, 2 <= G <= 16) use v_mfma_f32_16x16x32_bf16: the 16x32
 //    A operand holds the G query rows (zero-padded), the 32x16 B operand holds
-//    16 keys, four instructions cover d = 128.  A wave consumes one 16-token
-//    block (4 KB) per step; each lane loads 4 x 16 B.  With G <= 4 the G scores
-//    of a key land in one lane (C rows 0..3), so the group max needs no
-//    cross-lane traffic.
+//    16 keys, d/32 instructions cover a key row.  A wave consumes one 16-token
+//    chunk (4 KB at d = 128) per step; each lane loads d/32 x 16 B.  With
+//    G <= 4 the G scores of a key land in one lane (C rows 0..3), so the
+//    group max needs no cross-lane traffic.
+//    The scan is persistent and software pipelined (score_stream_kernel):
+//    one workgroup per resident slot, each owning a contiguous range of
+//    (row, chunk) work; the table entries of a row segment are staged in LDS
+//    once, so no key load waits on a table load; D chunks of loads are in
+//    flight per wave, and the next chunk's loads are issued between the
+//    matrix instructions and the score store (which would otherwise pin
+//    them, as the two pointers may alias).
 //  * G = 1 and fp32 keys use the vector ALUs: 16 lanes share a key, each lane
 //    owns one 16-byte piece, a wave loads 4 keys (1 KB contiguous in a pool
 //    block) per instruction, and a 4-step DPP butterfly finishes each dot.
-//  * Address resolution (block table / token table) happens per key inside
-//    the scan; dead tokens are never read.
+//  * Dead tokens (past seq_len, negative table entries) never read KV memory.
+#include <algorithm>
+
 #include "skv_device.h"
 
 namespace skv {
@@ -160,80 +168,160 @@ __global__ __launch_bounds__(kThreads) void score_valu_kernel(KvArgs kv, const v
   if constexpr (HIST) hist_flush(lh, ha.hist + ((int64_t)b * kv.H + h) * 4096);
 }
 
-// bf16 keys, 2 <= G <= 16, d_k = 32 * NC.
-template <int NC, int U, bool HIST>
-__global__ __launch_bounds__(kThreads) void score_mfma_kernel(KvArgs kv, const uint16_t* q, int G,
-                                                               float* scores, HistArgs ha) {
+// Persistent pipelined scan (bf16, 2 <= G <= 16, d_k = 32 * NC).  The work is
+// the list of (row r = b * H + h, chunk c of 16 tokens) pairs in row-major
+// order, cpr = ceil(L_max / 16) chunks per row; workgroup w owns the slice
+// [N w / W, N (w + 1) / W), at most kStageEntries / (entries per chunk)
+// chunks.  For each row segment of its slice the workgroup stages the
+// segment's table entries in LDS, then each wave scans a contiguous quarter
+// of the segment with D chunks of loads in flight.  Lanes whose token is dead
+// load the query row instead (always valid memory) and their score is -inf.
+constexpr int kStageEntries = 4096;
+
+template <int NC, int D, int GMAX, bool HIST>
+__global__ __launch_bounds__(kThreads) void score_stream_kernel(KvArgs kv, const uint16_t* q, int G,
+                                                                 float* scores, HistArgs ha,
+                                                                 int cpr) {
   __shared__ uint32_t lh[HIST ? 4096 : 1];
-  const int b = blockIdx.z, h = blockIdx.y;
-  const int t_begin = blockIdx.x * kTile;
-  const int t_end = min(kv.L_max, t_begin + kTile);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ int32_t tab[kStageEntries];
+  constexpr int d_k = 32 * NC;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, g4 = lane >> 4;
-  const int d_k = kv.d_k;
-
-  // A operand: row m = n is query head n of the group (zero when n >= G);
-  // lane group g4 of instruction j covers dims 8*(4j+g4) .. +8.
-  bf16x8_t A[NC];
-  const uint16_t* qrow = q + (((int64_t)b * kv.H + h) * G + (n < G ? n : 0)) * d_k;
-#pragma unroll
-  for (int j = 0; j < NC; ++j) {
-    u32x4_t w = (n < G) ? ld16((const char*)(qrow + (4 * j + g4) * 8)) : u32x4_t{0, 0, 0, 0};
-    A[j] = __builtin_bit_cast(bf16x8_t, w);
-  }
-
+  const int loff = g4 * 16;   // this lane's 16-byte piece inside each 64-byte quarter
+  const int64_t N = (int64_t)kv.B * kv.H * cpr;
+  const int64_t w0 = N * blockIdx.x / gridDim.x, w1 = N * (blockIdx.x + 1) / gridDim.x;
   const char* kbase = (const char*)kv.k;
-  float* srow = scores + ((int64_t)b * kv.H + h) * kv.L_max;
-  const int n_chunks = (t_end - t_begin + 15) >> 4;
-  int wlo = 0, whi = 0;
-  if constexpr (HIST) {
-    hist_begin(lh);
-    wlo = ha.lo[b];
-    whi = ha.hi[b];
-  }
+  const int mode = kv.token_table ? 2 : kv.block_table ? 1 : 0;   // token / block table / none
+  const int per_chunk = mode == 2 ? 16 : 1;                        // staged entries per chunk
+  if ((w1 - w0) * per_chunk > kStageEntries) return;               // the host never launches this
 
-  for (int c0 = wave; c0 < n_chunks; c0 += 4 * U) {
-    bf16x8_t Bm[U][NC];
-    int tok[U];
-    bool ok[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c = c0 + 4 * u;
-      const int t = t_begin + c * 16 + n;
-      tok[u] = (c < n_chunks) ? t : t_end;
-      const int64_t slot = (c < n_chunks && t < t_end) ? slot_of(kv, b, t) : -1;
-      ok[u] = slot >= 0;
-      const int64_t base = ok[u] ? row_elem(kv, b, h, slot, d_k) : 0;
-#pragma unroll
-      for (int j = 0; j < NC; ++j) {
-        u32x4_t w = ok[u] ? ld16(kbase + (base + (4 * j + g4) * 8) * 2) : u32x4_t{0, 0, 0, 0};
-        Bm[u][j] = __builtin_bit_cast(bf16x8_t, w);
-      }
+  for (int64_t wu = w0; wu < w1;) {
+    const int r = (int)(wu / cpr);
+    const int c_lo = (int)(wu - (int64_t)r * cpr);
+    const int c_hi = (int)min((int64_t)cpr, w1 - (int64_t)r * cpr);
+    wu = (int64_t)r * cpr + c_hi;
+    const int b = r / kv.H, h = r - b * kv.H;
+    const int n_seg = c_hi - c_lo;
+
+    __syncthreads();   // the previous segment is done with lh and tab
+    if (mode == 1) {
+      const int32_t* src = kv.block_table + (int64_t)b * cpr + c_lo;
+      for (int i = threadIdx.x; i < n_seg; i += kThreads) tab[i] = src[i];
+    } else if (mode == 2) {
+      const int32_t* src = kv.token_table + (int64_t)b * kv.L_max + (int64_t)c_lo * 16;
+      for (int i = threadIdx.x; i < n_seg * 16; i += kThreads) tab[i] = src[i];
     }
+    int wlo = 0, whi = 0;
+    if constexpr (HIST) {
+      for (int i = threadIdx.x; i < 4096; i += kThreads) lh[i] = 0u;
+      wlo = ha.lo[b];
+      whi = ha.hi[b];
+    }
+    __syncthreads();
+
+    // A operand: row n = query head n of the group (zero rows for n >= G)
+    const char* qrow = (const char*)(q + ((int64_t)r * G + (n < G ? n : 0)) * d_k);
+    bf16x8_t A[NC];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int j = 0; j < NC; ++j) {
+      u32x4_t w = ld16(qrow + j * 64 + loff);
+      if (n >= G) w = u32x4_t{0, 0, 0, 0};
+      A[j] = __builtin_bit_cast(bf16x8_t, w);
+    }
+    const int live = min(kv.seq_len[b], kv.L_max);   // tokens t < live are addressable
+    const int i_lo = (n_seg * wave) / 4;              // this wave's chunks, relative to c_lo
+    const int n_w = (n_seg * (wave + 1)) / 4 - i_lo;
+    float* srow = scores + (int64_t)r * kv.L_max;
+    const int64_t hrow = (int64_t)h * 16 + n;         // row of (head h, token n) in a pool block
+    u32x4_t Bm[D][NC];
+
+    // physical key row of this lane's token in chunk i (relative to i_lo), or -1
+    auto key_row = [&](int i) -> int64_t {
+      const int c = i_lo + i;
+      const int t = (c_lo + c) * 16 + n;
+      if (t >= live) return -1;
+      if (mode == 0) return (int64_t)r * kv.L_max + t;
+      if (mode == 1) {
+        const int e = tab[c];   // same address in every lane: one broadcast read
+        return e < 0 ? -1 : (int64_t)e * kv.H * 16 + hrow;
+      }
+      const int slot = tab[c * 16 + n];
+      return slot < 0 ? -1 : (((int64_t)(slot >> 4) * kv.H + h) * 16 + (slot & 15));
+    };
+    auto issue = [&](int s, int i) {
+      const int64_t row = key_row(i);
+      const char* p = row >= 0 ? kbase + row * (2 * d_k) : qrow;
+#pragma unroll
+      for (int j = 0; j < NC; ++j) Bm[s][j] = ld16(p + j * 64 + loff);
+    };
+    auto mfma = [&](int s) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < NC; ++j)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[j], Bm[u][j], acc, 0, 0, 0);
-      // lane (n, g4) holds C[4*g4 + i][n]: query head 4*g4+i against key n
-      float s = -INFINITY;
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[j], __builtin_bit_cast(bf16x8_t, Bm[s][j]),
+                                                      acc, 0, 0, 0);
+      return acc;
+    };
+    // lane (n, g4) holds C[4 g4 + k][n]: query head 4 g4 + k against key n
+    auto finish = [&](f32x4_t acc, int i) {
+      float sc;
+      if constexpr (GMAX <= 4) {
+        sc = acc[0];
+        if (G > 1) sc = fmaxf(sc, acc[1]);
+        if (G > 2) sc = fmaxf(sc, acc[2]);
+        if (G > 3) sc = fmaxf(sc, acc[3]);
+      } else {
+        sc = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (4 * g4 + i < G) s = fmaxf(s, acc[i]);
-      if (G > 4) {
-        s = fmaxf(s, __shfl_xor(s, 16, 64));
-        s = fmaxf(s, __shfl_xor(s, 32, 64));
+        for (int k = 0; k < 4; ++k)
+          if (4 * g4 + k < G) sc = fmaxf(sc, acc[k]);
+        sc = fmaxf(sc, __shfl_xor(sc, 16, 64));
+        sc = fmaxf(sc, __shfl_xor(sc, 32, 64));
       }
-      if (g4 == 0 && tok[u] < t_end) {
-        srow[tok[u]] = ok[u] ? s : -INFINITY;
+      const int t = (c_lo + i_lo + i) * 16 + n;
+      const bool ok = key_row(i) >= 0;
+      if (g4 == 0 && t < kv.L_max) {
+        srow[t] = ok ? sc : -INFINITY;
         if constexpr (HIST) {
-          if (ok[u]) hist_add(lh, s, tok[u], wlo, whi);
+          if (ok) hist_add(lh, sc, t, wlo, whi);
         }
       }
+    };
+
+    // software pipeline: D chunks in flight; the next chunk's loads are
+    // issued between the matrix instructions and the score store
+    if (n_w >= D) {
+#pragma unroll
+      for (int s = 0; s < D; ++s) issue(s, s);
+      int i0 = 0;
+      for (; i0 + 2 * D <= n_w; i0 += D) {
+#pragma unroll
+        for (int s = 0; s < D; ++s) {
+          const f32x4_t acc = mfma(s);
+          issue(s, i0 + s + D);
+          finish(acc, i0 + s);
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < D; ++s) {
+        const f32x4_t acc = mfma(s);
+        if (i0 + s + D < n_w) issue(s, i0 + s + D);
+        finish(acc, i0 + s);
+      }
+#pragma unroll
+      for (int s = 0; s < D; ++s)
+        if (i0 + D + s < n_w) finish(mfma(s), i0 + D + s);
+    } else {
+#pragma unroll
+      for (int s = 0; s < D; ++s)
+        if (s < n_w) issue(s, s);
+#pragma unroll
+      for (int s = 0; s < D; ++s)
+        if (s < n_w) finish(mfma(s), s);
     }
+    if constexpr (HIST) hist_flush(lh, ha.hist + (int64_t)r * 4096);
   }
-  if constexpr (HIST) hist_flush(lh, ha.hist + ((int64_t)b * kv.H + h) * 4096);
 }
 
 template <bool BF16, int NPL, int GMAX, int U>
@@ -261,13 +349,50 @@ hipError_t launch_valu(const KvArgs& kv, const void* q, int G, float* scores, co
   return hipGetLastError();
 }
 
-template <int NC, int U>
-void launch_mfma_k(const KvArgs& kv, const void* q, int G, float* scores, const HistArgs& ha,
-                   dim3 grid, hipStream_t s) {
-  if (ha.hist)
-    score_mfma_kernel<NC, U, true><<<grid, kThreads, 0, s>>>(kv, (const uint16_t*)q, G, scores, ha);
-  else
-    score_mfma_kernel<NC, U, false><<<grid, kThreads, 0, s>>>(kv, (const uint16_t*)q, G, scores, ha);
+// Workgroups of `kernel` that fit on the current device at once (occupancy x
+// compute units), cached per device in `cache`.
+template <typename K>
+int resident_wgs(K kernel, int* cache, int n_cache) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= n_cache) return 1024;
+  if (cache[dev] == 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) != hipSuccess ||
+        per_cu < 1)
+      per_cu = 1;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 1)
+      cus = 1;
+    cache[dev] = per_cu * cus;
+  }
+  return cache[dev];
+}
+
+template <int NC, int D, int GMAX, bool HIST>
+hipError_t launch_stream_k(const KvArgs& kv, const void* q, int G, float* scores,
+                           const HistArgs& ha, hipStream_t s) {
+  static int cache[64] = {0};
+  auto kern = score_stream_kernel<NC, D, GMAX, HIST>;
+  const int cpr = (kv.L_max + 15) / 16;
+  const int64_t n_work = (int64_t)kv.B * kv.H * cpr;
+  // at least 16 chunks per workgroup and at most one workgroup per resident
+  // slot, unless a slice would then stage more table entries than fit in LDS
+  const int64_t cap = kStageEntries / (kv.token_table ? 16 : 1);
+  int64_t w = std::min<int64_t>(resident_wgs(kern, cache, 64), (n_work + 15) / 16);
+  w = std::max<int64_t>(std::max<int64_t>(w, (n_work + cap - 1) / cap), 1);
+  if (w > 0x7fffffff) return hipErrorInvalidValue;
+  kern<<<dim3((unsigned)w), kThreads, 0, s>>>(kv, (const uint16_t*)q, G, scores, ha, cpr);
+  return hipGetLastError();
+}
+
+template <int NC, int D>
+hipError_t launch_stream(const KvArgs& kv, const void* q, int G, float* scores, const HistArgs& ha,
+                         hipStream_t s) {
+  if (G <= 4)
+    return ha.hist ? launch_stream_k<NC, D, 4, true>(kv, q, G, scores, ha, s)
+                   : launch_stream_k<NC, D, 4, false>(kv, q, G, scores, ha, s);
+  return ha.hist ? launch_stream_k<NC, D, 16, true>(kv, q, G, scores, ha, s)
+                 : launch_stream_k<NC, D, 16, false>(kv, q, G, scores, ha, s);
 }
 
 }  // namespace
@@ -278,13 +403,12 @@ hipError_t launch_score(const KvArgs& kv, const void* q, int G, float* scores, c
   HistArgs ha{lo, hi, hist};
   if (kv.bf16 && G >= 2 && G <= 16 && kv.d_k % 32 == 0) {
     switch (kv.d_k / 32) {
-      case 2: launch_mfma_k<2, 2>(kv, q, G, scores, ha, grid, s); break;
-      case 4: launch_mfma_k<4, 2>(kv, q, G, scores, ha, grid, s); break;
-      case 8: launch_mfma_k<8, 2>(kv, q, G, scores, ha, grid, s); break;
-      case 18: launch_mfma_k<18, 1>(kv, q, G, scores, ha, grid, s); break;
+      case 2: return launch_stream<2, 4>(kv, q, G, scores, ha, s);
+      case 4: return launch_stream<4, 4>(kv, q, G, scores, ha, s);
+      case 8: return launch_stream<8, 2>(kv, q, G, scores, ha, s);
+      case 18: return launch_stream<18, 1>(kv, q, G, scores, ha, s);
       default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
   }
   const int E = kv.bf16 ? 8 : 4;
   const int npl = (kv.d_k / E + 15) / 16;

@@ -120,6 +120,58 @@ def test_contiguous_bf16_and_fp32_g4():
     assert _end_to_end(st32) == 0
 
 
+@pytest.mark.parametrize("G", [2, 4, 8, 16])
+def test_scan_slices_cross_rows_and_ragged_lengths(G):
+    """Row lengths that are not a multiple of the per-workgroup slice, so
+    workgroup slices of the persistent scan straddle rows; ragged seq_len
+    (including one shorter than a chunk)."""
+    st = W.make_gqa_paged(tag=150 + G, B=3, H=5, G=G, L=1040, k=100, sink=4, local=16,
+                          seq_len=[1040, 777, 33])
+    assert _end_to_end(st, attend=G <= 16) == 0
+
+
+def test_scan_contiguous_ragged_tail_chunk():
+    """Contiguous store with L_max = 1000 (last chunk of each row is partial)."""
+    st = W.make_gqa_paged(tag=157, B=2, H=2, G=4, L=1008, k=64, seq_len=[1008, 611])
+    Lc = 1000
+    for name in ("k", "v"):
+        pool = getattr(st.kv, name)
+        logical = pool[st.kv.block_table]                    # [B][nb][H][16][d]
+        cont = logical.transpose(0, 2, 1, 3, 4).reshape(2, 2, 1008, 128)[:, :, :Lc]
+        setattr(st.kv, name, np.ascontiguousarray(cont))
+    st.kv.block, st.kv.block_table, st.kv.L_max = 0, None, Lc
+    st.kv.seq_len = np.array([1000, 611], np.int32)
+    st.hi = (st.kv.seq_len - 64).astype(np.int32)
+    assert _end_to_end(st) == 0
+
+
+def test_scan_token_table_gqa_and_unmapped_blocks():
+    """G = 4 through a per-token table with holes, and through a block table
+    with unmapped (negative) blocks."""
+    st = W.make_gqa_paged(tag=158, B=2, H=3, G=4, L=2048, k=200, sink=4, local=64,
+                          seq_len=[2048, 1500])
+    bt = st.kv.block_table
+    t = np.arange(st.kv.L_max)
+    tt = (bt[:, t // 16] * 16 + t % 16).astype(np.int32)
+    holes = np.random.default_rng(9).random(tt.shape) < 0.3
+    tt[holes] = -1
+    tt[:, :4] = bt[:, :1] * 16 + np.arange(4)                # keep the sink live
+    st.kv.token_table, st.kv.block_table = tt, None
+    assert _end_to_end(st) == 0
+    st = W.make_gqa_paged(tag=159, B=2, H=3, G=4, L=2048, k=200, sink=4, local=64,
+                          seq_len=[2048, 1500])
+    st.kv.block_table[0, [3, 4, 50, 127]] = -1
+    st.kv.block_table[1, [0, 20]] = -1
+    assert _end_to_end(st) == 0
+
+
+@pytest.mark.parametrize("d,attend", [(64, False), (256, True)])
+def test_scan_other_head_dims(d, attend):
+    st = W.make_gqa_paged(tag=160 + d // 64, B=2, H=2, G=4, d=d, L=1024, k=100, sink=4, local=16,
+                          seq_len=[1024, 999])
+    assert _end_to_end(st, attend=attend) == 0
+
+
 def test_edges_k_ge_candidates_empty_window_and_k1():
     st = W.make_gqa_paged(tag=130, B=3, H=2, G=4, L=512, k=512, sink=4, local=64)
     st.lo = np.array([4, 100, 0], np.int32)

@@ -62,6 +62,35 @@ def test_token_table_addressing_and_dead_tokens():
             np.testing.assert_array_equal(K[:, 0], (slot // 16) * 1000.0 + h * 100.0 + slot % 16)
 
 
+def test_unmapped_block_equals_token_table_with_dead_tokens():
+    """A negative block-table entry makes its 16 tokens dead: the logical KV
+    equals the one read through the per-token table with those tokens at -1."""
+    B, H, d, L = 2, 2, 4, 64
+    n_blocks = B * L // 16
+    pool = _coded_pool(n_blocks, H, d)
+    bt = np.random.default_rng(2).permutation(n_blocks).astype(np.int32).reshape(B, L // 16)
+    bt[0, 1] = -1
+    bt[1, 3] = -7
+    seq = np.array([L, 60], np.int32)
+    kvb = W.KV(k=pool, v=pool, dtype="f32", B=B, H=H, d_k=d, d_v=d, block=16, L_max=L,
+               block_table=bt, seq_len=seq)
+    t = np.arange(L)
+    tt = np.where(bt[:, t // 16] >= 0, bt[:, t // 16] * 16 + t % 16, -1).astype(np.int32)
+    kvt = W.KV(k=pool, v=pool, dtype="f32", B=B, H=H, d_k=d, d_v=d, block=16, L_max=L,
+               token_table=tt, seq_len=seq)
+    for b in range(B):
+        for h in range(H):
+            tb, Kb, _ = D.logical_kv(kvb, b, h)
+            tk, Kt, _ = D.logical_kv(kvt, b, h)
+            np.testing.assert_array_equal(tb, tk)
+            np.testing.assert_array_equal(Kb, Kt)
+    dead0 = set(range(16, 32))
+    assert dead0.isdisjoint(D.logical_kv(kvb, 0, 0)[0].tolist())
+    q = np.ones((B, H, d), np.float32)
+    s0 = D.scores_row(kvb, q, 1, 0, 0)
+    assert np.all(np.isneginf(s0[16:32])) and np.all(np.isfinite(s0[:16]))
+
+
 def test_contiguous_addressing_and_latent_value():
     B, H, L, d = 2, 2, 10, 6
     k = np.arange(B * H * L * d, dtype=np.float32).reshape(B, H, L, d)

@@ -55,11 +55,11 @@ __device__ __forceinline__ void hist_add(uint32_t* lh, float s, int t, int lo, i
 
 __device__ __forceinline__ void hist_begin(uint32_t* lh) {
   for (int i = threadIdx.x; i < 4096; i += kThreads) lh[i] = 0u;
-  __syncthreads();
+  lds_barrier();
 }
 
 __device__ __forceinline__ void hist_flush(uint32_t* lh, uint32_t* g) {
-  __syncthreads();
+  lds_barrier();
   for (int i = threadIdx.x; i < 4096; i += kThreads) {
     const uint32_t c = lh[i];
     if (c) atomicAdd(&g[i], c);
@@ -204,7 +204,7 @@ __global__ __launch_bounds__(kThreads) void score_stream_kernel(KvArgs kv, const
     const int b = r / kv.H, h = r - b * kv.H;
     const int n_seg = c_hi - c_lo;
 
-    __syncthreads();   // the previous segment is done with lh and tab
+    lds_barrier();   // the previous segment is done with lh and tab
     if (mode == 1) {
       const int32_t* src = kv.block_table + (int64_t)b * cpr + c_lo;
       for (int i = threadIdx.x; i < n_seg; i += kThreads) tab[i] = src[i];
@@ -218,7 +218,7 @@ __global__ __launch_bounds__(kThreads) void score_stream_kernel(KvArgs kv, const
       wlo = ha.lo[b];
       whi = ha.hi[b];
     }
-    __syncthreads();
+    lds_barrier();
 
     // A operand: row n = query head n of the group (zero rows for n >= G)
     const char* qrow = (const char*)(q + ((int64_t)r * G + (n < G ? n : 0)) * d_k);

@@ -74,6 +74,28 @@ __device__ __forceinline__ int wave_excl_scan(int v, int lane) {
   return x - v;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP: Hillis-Steele
+// shifts of 1, 2, 4, 8 inside each 16-lane row (lanes without a source add
+// 0), then lane 15 of each row into the next row and lane 31 into rows 2, 3.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  int x = v;
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);    // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);    // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);    // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);    // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31
+  return x;
+}
+
+// Workgroup barrier for data exchanged through LDS only: waits for this
+// wave's LDS operations and meets the other waves, without waiting for its
+// outstanding global loads, stores or atomics (__syncthreads() waits for
+// those as well).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Copy n 4-byte words from global memory to LDS with up to PER loads per
 // thread in flight at once (a plain copy loop waits for every load before its
 // LDS store, one memory latency per iteration).

@@ -212,7 +212,8 @@ def test_exact_ties_lowest_index_wins():
 
 # --------------------------------------------------------------- top-k alone
 @pytest.mark.parametrize("L,k,seed", [(1000, 37, 0), (4096, 2048, 1), (32768, 2048, 2),
-                                      (40000, 700, 3), (131072, 2048, 4), (5000, 4999, 5)])
+                                      (40000, 700, 3), (131072, 2048, 4), (5000, 4999, 5),
+                                      (32768, 2048, 6), (70001, 3000, 7)])
 def test_topk_kernel_on_oracle_inputs(L, k, seed):
     """Synthetic rows with ties, -0.0 / +0.0, -inf and windows; the GPU set must
     equal the oracle's set exactly."""
@@ -224,6 +225,8 @@ def test_topk_kernel_on_oracle_inputs(L, k, seed):
     s[1, 0, ::7] = -0.0
     s[1, 0, 3::7] = 0.0
     s[1, 1, rng.random(L) < 0.3] = -np.inf                   # dead tokens
+    if seed >= 6:
+        s[0, 0] = 1.5                                        # one value: every key ties
     lo = np.array([3, 0], np.int32)
     hi = np.array([L - 5, L], np.int32)
     sd = torch.from_numpy(s).to(DEV)

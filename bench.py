@@ -56,6 +56,10 @@ def parse():
                     help="distinct device copies of the KV pool, used in turn by successive "
                          "steps (like successive layers), so that no step finds its keys in "
                          "the 256 MB last-level cache")
+    ap.add_argument("--path", default="fused", choices=("fused", "separate"),
+                    help="fused: sparsekv_score_hist + sparsekv_select_attend_resume (top-k "
+                         "fused with the attention); separate: sparsekv_score_hist + "
+                         "sparsekv_topk_resume + sparsekv_gather_attend")
     ap.add_argument("--eager", action="store_true",
                     help="launch every kernel from the host instead of replaying one HIP graph "
                          "that holds the K timed steps")
@@ -221,8 +225,12 @@ def main():
     idx = torch.empty((B, H, k), dtype=torch.int32, device=dev)
     cnt = torch.empty((B, H), dtype=torch.int32, device=dev)
     out = torch.empty((B, H * G, kv.d_v), dtype=torch.float32, device=dev)
-    ws = S.workspace(S.sparsekv_workspace_size(S.SKV_OP_GATHER_ATTEND, kv, G, k), dev)
-    ws_sel = S.workspace(S.sparsekv_workspace_size(S.SKV_OP_SELECT, kv, G, k), dev)
+    fused = args.path == "fused"
+    if fused:
+        ws_sel = S.workspace(S.sparsekv_workspace_size(S.SKV_OP_SELECT_ATTEND, kv, G, k), dev)
+    else:
+        ws = S.workspace(S.sparsekv_workspace_size(S.SKV_OP_GATHER_ATTEND, kv, G, k), dev)
+        ws_sel = S.workspace(S.sparsekv_workspace_size(S.SKV_OP_SELECT, kv, G, k), dev)
     copies = [kv] + [dataclasses.replace(kv, k=kv.k.clone(), v=None if kv.v is None else kv.v.clone())
                      for _ in range(max(1, args.kv_copies) - 1)]
     hip = HipEvents()
@@ -238,10 +246,16 @@ def main():
         S.sparsekv_score_hist(c, q, G, lo, hi, scores, ws_sel)
         if ev is not None:
             mark(ev[1])
-        S.sparsekv_topk_resume(scores, lo, hi, k, idx, cnt, ws_sel)
-        if ev is not None:
-            mark(ev[2])
-        S.sparsekv_gather_attend(c, q, G, idx, k, lo, hi, st.scale, out, ws)
+        if fused:
+            S.sparsekv_select_attend_resume(c, q, G, lo, hi, k, st.scale, scores, idx, cnt, out,
+                                            ws_sel)
+            if ev is not None:
+                mark(ev[2])
+        else:
+            S.sparsekv_topk_resume(scores, lo, hi, k, idx, cnt, ws_sel)
+            if ev is not None:
+                mark(ev[2])
+            S.sparsekv_gather_attend(c, q, G, idx, k, lo, hi, st.scale, out, ws)
         if ev is not None:
             mark(ev[3])
 
@@ -329,16 +343,18 @@ def main():
         "dtype": "bf16" if bf else "f32",
         "data": "synthetic",
         "config": dict(workload_config(st), kv_copies=len(copies),
-                       launch="eager" if args.eager else "hip_graph"),
+                       launch="eager" if args.eager else "hip_graph", path=args.path),
         "us_per_step": ms_per_step * 1e3,
         "us_per_step_gpu": gpu_ms_per_step * 1e3,
         "timing": timing_note,
         "us_per_step_events": {"median": float(np.median(step_ms)) * 1e3,
                                "p10": float(np.percentile(step_ms, 10)) * 1e3,
                                "p90": float(np.percentile(step_ms, 90)) * 1e3},
-        "kernels_us": {"score": float(np.mean(score_ms)) * 1e3,
-                       "topk": float(np.mean(topk_ms)) * 1e3,
-                       "gather_attend": float(np.mean(attn_ms)) * 1e3},
+        "kernels_us": ({"score": float(np.mean(score_ms)) * 1e3,
+                        "topk_attend_merge": float(np.mean(topk_ms)) * 1e3} if fused else
+                       {"score": float(np.mean(score_ms)) * 1e3,
+                        "topk": float(np.mean(topk_ms)) * 1e3,
+                        "gather_attend": float(np.mean(attn_ms)) * 1e3}),
         "keys_scanned_per_step": n_keys,
         "step_algorithmic_bytes": step_bytes,
         "step_GBps": step_bytes / (ms_per_step * 1e-3) / 1e9,

@@ -74,7 +74,8 @@ typedef enum {
   SKV_OP_GATHER_ATTEND = 2,
   SKV_OP_ENCODE = 3,
   SKV_OP_RETRIEVE = 4,
-  SKV_OP_SELECT = 5
+  SKV_OP_SELECT = 5,
+  SKV_OP_SELECT_ATTEND = 6
 } skv_op;
 
 /* Caller-owned KV storage (host struct, device pointers). */
@@ -121,7 +122,8 @@ skv_status sparsekv_score(const skv_kv* kv, const void* q, int32_t G, float* sco
  *   idx   [B][H][k] int32, entries past count[b][h] are -1
  *   count [B][H]    int32 = min(k, number of finite candidates)
  * ws: sparsekv_workspace_size(SKV_OP_TOPK, kv, 0, k, NULL) bytes, where only
- * kv->B, kv->H and kv->L_max are read.  Supports L_max <= 4194304. */
+ * kv->B, kv->H and kv->L_max are read.  Any L_max (rows of more than 32768
+ * scores are re-read from memory once per radix pass). */
 skv_status sparsekv_topk(const float* scores, int32_t B, int32_t H, int32_t L_max,
                          skv_window win, int32_t k, int32_t* idx, int32_t* count, void* ws,
                          size_t ws_bytes, hipStream_t stream);
@@ -165,6 +167,35 @@ skv_status sparsekv_topk_resume(const float* scores, int32_t B, int32_t H, int32
 skv_status sparsekv_gather_attend(const skv_kv* kv, const void* q, int32_t G, const int32_t* idx,
                                   int32_t k, skv_window win, float scale, float* out, void* ws,
                                   size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------ fused decode step --
+ * One whole sparse decode step: sparsekv_score_hist, then the exact top-k and
+ * the gather + attention fused into one kernel, then the split merge.
+ * Results equal sparsekv_select followed by sparsekv_gather_attend on the
+ * same inputs: scores [B][H][L_max], idx [B][H][k] (ascending, -1 padded),
+ * count [B][H] and out [B][H*G][d_v] fp32 (definitions above: ParisKV
+ * close-reading, section 一, Eqs. (1)-(3); ECHO-OSDI26 wiki page,
+ * observation 5; vToken reading notes, section 3.4 Eq. (2)).
+ * Supports bf16 keys and values with d_k == d_v == 128, 1 <= G <= 8 and
+ * L_max <= 32768 (SKV_EUNSUPPORTED otherwise: use the separate calls).
+ * ws: sparsekv_workspace_size(SKV_OP_SELECT_ATTEND, kv, G, k, NULL) bytes,
+ * zero-filled before its first use; every call leaves its first region (the
+ * key histograms) zero again. */
+skv_status sparsekv_select_attend(const skv_kv* kv, const void* q, int32_t G, skv_window win,
+                                  int32_t k, float scale, float* scores, int32_t* idx,
+                                  int32_t* count, float* out, void* ws, size_t ws_bytes,
+                                  hipStream_t stream);
+
+/* The second half of sparsekv_select_attend, for callers that time or
+ * schedule the score scan separately: after sparsekv_score_hist(kv, q, G, win,
+ * scores, ws, ...) on the same ws, the exact top-k, gather + attention and
+ * split merge (same arguments and results as sparsekv_select_attend; scores
+ * is read, not written). */
+skv_status sparsekv_select_attend_resume(const skv_kv* kv, const void* q, int32_t G,
+                                         skv_window win, int32_t k, float scale,
+                                         const float* scores, int32_t* idx, int32_t* count,
+                                         float* out, void* ws, size_t ws_bytes,
+                                         hipStream_t stream);
 
 /* --------------------------------------------- compressed-code retrieval --
  * ParisKV close-reading, sections 2.2-2.5: keys and the query are normalised

@@ -28,7 +28,8 @@ LIB_PATH = os.path.join(_HERE, "libsparsekv.so")
 
 SKV_OK, SKV_EINVAL, SKV_EUNSUPPORTED, SKV_EWORKSPACE, SKV_ELAUNCH = range(5)
 SKV_F32, SKV_BF16 = 0, 1
-SKV_OP_SCORE, SKV_OP_TOPK, SKV_OP_GATHER_ATTEND, SKV_OP_ENCODE, SKV_OP_RETRIEVE, SKV_OP_SELECT = range(6)
+(SKV_OP_SCORE, SKV_OP_TOPK, SKV_OP_GATHER_ATTEND, SKV_OP_ENCODE, SKV_OP_RETRIEVE, SKV_OP_SELECT,
+ SKV_OP_SELECT_ATTEND) = range(7)
 
 c_vp, c_i32, c_f32, c_sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
 
@@ -76,6 +77,11 @@ _SIGS = {
                                      c_vp, c_sz, c_vp]),
     "sparsekv_gather_attend": (c_i32, [ctypes.POINTER(skv_kv), c_vp, c_i32, c_vp, c_i32,
                                        skv_window, c_f32, c_vp, c_vp, c_sz, c_vp]),
+    "sparsekv_select_attend": (c_i32, [ctypes.POINTER(skv_kv), c_vp, c_i32, skv_window, c_i32,
+                                       c_f32, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "sparsekv_select_attend_resume": (c_i32, [ctypes.POINTER(skv_kv), c_vp, c_i32, skv_window,
+                                              c_i32, c_f32, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz,
+                                              c_vp]),
     "sparsekv_codebook_init": (c_i32, [c_i32, ctypes.POINTER(c_f32), ctypes.POINTER(c_f32)]),
     "sparsekv_encode": (c_i32, [ctypes.POINTER(skv_codebook), ctypes.POINTER(skv_kv), c_i32,
                                 c_i32, c_i32, ctypes.POINTER(skv_index), c_vp]),
@@ -256,6 +262,57 @@ def sparsekv_select(kv: KVTensors, q: torch.Tensor, G: int, lo: torch.Tensor, hi
                                  _ptr(scores), _ptr(idx), _ptr(count), _ptr(ws),
                                  ws.numel() * ws.element_size(), _stream()))
     return scores, idx, count
+
+
+def sparsekv_select_attend(kv: KVTensors, q: torch.Tensor, G: int, lo: torch.Tensor,
+                           hi: torch.Tensor, k: int, scale: float,
+                           scores: Optional[torch.Tensor] = None, idx: Optional[torch.Tensor] = None,
+                           count: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                           ws: Optional[torch.Tensor] = None):
+    """One fused decode step (score scan, exact top-k, gather + attention);
+    returns (scores, idx, count, out), the results of sparsekv_select followed
+    by sparsekv_gather_attend."""
+    _dev(q, "q", kv.torch_dtype)
+    if q.shape != (kv.B, kv.H * G, kv.d_k):
+        raise ValueError("q must be [B][H*G][d_k]")
+    dev = q.device
+    if scores is None:
+        scores = torch.empty((kv.B, kv.H, kv.L_max), dtype=torch.float32, device=dev)
+    if idx is None:
+        idx = torch.empty((kv.B, kv.H, k), dtype=torch.int32, device=dev)
+    if count is None:
+        count = torch.empty((kv.B, kv.H), dtype=torch.int32, device=dev)
+    if out is None:
+        out = torch.empty((kv.B, kv.H * G, kv.d_v), dtype=torch.float32, device=dev)
+    for t, nm, dt in ((scores, "scores", torch.float32), (idx, "idx", torch.int32),
+                      (count, "count", torch.int32), (out, "out", torch.float32),
+                      (lo, "lo", torch.int32), (hi, "hi", torch.int32)):
+        _dev(t, nm, dt)
+    if ws is None:
+        ws = workspace(sparsekv_workspace_size(SKV_OP_SELECT_ATTEND, kv, G, k), dev)
+    c = kv.c()
+    _check("sparsekv_select_attend",
+           lib().sparsekv_select_attend(ctypes.byref(c), _ptr(q), G, skv_window(_ptr(lo), _ptr(hi)), k,
+                                        float(scale), _ptr(scores), _ptr(idx), _ptr(count), _ptr(out),
+                                        _ptr(ws), ws.numel() * ws.element_size(), _stream()))
+    return scores, idx, count, out
+
+
+def sparsekv_select_attend_resume(kv: KVTensors, q: torch.Tensor, G: int, lo: torch.Tensor,
+                                  hi: torch.Tensor, k: int, scale: float, scores: torch.Tensor,
+                                  idx: torch.Tensor, count: torch.Tensor, out: torch.Tensor,
+                                  ws: torch.Tensor):
+    """The second half of sparsekv_select_attend, after sparsekv_score_hist on ws."""
+    for t, nm, dt in ((scores, "scores", torch.float32), (idx, "idx", torch.int32),
+                      (count, "count", torch.int32), (out, "out", torch.float32)):
+        _dev(t, nm, dt)
+    c = kv.c()
+    _check("sparsekv_select_attend_resume",
+           lib().sparsekv_select_attend_resume(ctypes.byref(c), _ptr(q), G,
+                                               skv_window(_ptr(lo), _ptr(hi)), k, float(scale),
+                                               _ptr(scores), _ptr(idx), _ptr(count), _ptr(out),
+                                               _ptr(ws), ws.numel() * ws.element_size(), _stream()))
+    return idx, count, out
 
 
 def sparsekv_score_hist(kv: KVTensors, q: torch.Tensor, G: int, lo: torch.Tensor,

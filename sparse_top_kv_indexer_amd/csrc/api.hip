@@ -144,6 +144,39 @@ skv_status sparsekv_gather_attend(const skv_kv* kv, const void* q, int32_t G, co
       launch_gather_attend(a, q, G, idx, k, win.lo, win.hi, scale, out, ws, ws_bytes, stream));
 }
 
+skv_status sparsekv_select_attend(const skv_kv* kv, const void* q, int32_t G, skv_window win,
+                                  int32_t k, float scale, float* scores, int32_t* idx,
+                                  int32_t* count, float* out, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+  if (!kv_ok(kv) || !q || !scores || !idx || !count || !out || G < 1 || k < 1) return SKV_EINVAL;
+  if (!win.lo || !win.hi || !isfinite(scale)) return SKV_EINVAL;
+  const KvArgs a = to_args(kv);
+  if (!score_supported(kv, G) || !select_attend_supported(a, G)) return SKV_EUNSUPPORTED;
+  const size_t th = topk_workspace_bytes(kv->B * kv->H, kv->L_max);
+  if (!ws || ws_bytes < th + select_attend_partial_bytes(a, G)) return SKV_EWORKSPACE;
+  uint32_t* hist = (uint32_t*)ws;
+  float* part = (float*)((char*)ws + th);
+  const hipError_t e = launch_score(a, q, G, scores, win.lo, win.hi, hist, stream);
+  if (e != hipSuccess) return launched(e);
+  return launched(launch_select_attend(a, q, G, scores, win.lo, win.hi, k, hist, scale, idx, count,
+                                       part, out, stream));
+}
+
+skv_status sparsekv_select_attend_resume(const skv_kv* kv, const void* q, int32_t G,
+                                         skv_window win, int32_t k, float scale,
+                                         const float* scores, int32_t* idx, int32_t* count,
+                                         float* out, void* ws, size_t ws_bytes,
+                                         hipStream_t stream) {
+  if (!kv_ok(kv) || !q || !scores || !idx || !count || !out || G < 1 || k < 1) return SKV_EINVAL;
+  if (!win.lo || !win.hi || !isfinite(scale)) return SKV_EINVAL;
+  const KvArgs a = to_args(kv);
+  if (!score_supported(kv, G) || !select_attend_supported(a, G)) return SKV_EUNSUPPORTED;
+  const size_t th = topk_workspace_bytes(kv->B * kv->H, kv->L_max);
+  if (!ws || ws_bytes < th + select_attend_partial_bytes(a, G)) return SKV_EWORKSPACE;
+  return launched(launch_select_attend(a, q, G, scores, win.lo, win.hi, k, (uint32_t*)ws, scale,
+                                       idx, count, (float*)((char*)ws + th), out, stream));
+}
+
 size_t sparsekv_workspace_size(skv_op op, const skv_kv* kv, int32_t G, int32_t k,
                                const skv_index* index) {
   switch (op) {
@@ -160,6 +193,10 @@ size_t sparsekv_workspace_size(skv_op op, const skv_kv* kv, int32_t G, int32_t k
       return attend_workspace_bytes(to_args(kv), G, k);
     case SKV_OP_RETRIEVE:
       return sparsekv_retrieve_workspace_size(index, G, 1.0f, k);
+    case SKV_OP_SELECT_ATTEND:
+      if (!kv_ok(kv) || G < 1 || k < 0) return 0;
+      return topk_workspace_bytes(kv->B * kv->H, kv->L_max) +
+             select_attend_partial_bytes(to_args(kv), G);
   }
   return 0;
 }

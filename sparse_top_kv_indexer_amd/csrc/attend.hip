@@ -26,7 +26,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kRows = kThreads / 16;   // 16-lane rows per workgroup
 
-__device__ __forceinline__ u32x4_t ld16(const char* p) { return *(const u32x4_t*)p; }
 
 template <bool BF16>
 __device__ __forceinline__ void unpack(const u32x4_t w, float* f) {
@@ -398,12 +397,20 @@ __global__ __launch_bounds__(kThreads) void attend_mfma_kernel(
 // out[b][hq][j] = sum_s acc_s[j] 2^(m_s - M) / sum_s l_s 2^(m_s - M)
 // One workgroup per (b, query head); the split partials are staged in LDS with
 // all loads issued at once.
+// With zero_hist != nullptr, the workgroup of the first query head of each KV
+// head also zeroes that row's 4096-bin key histogram (the fused select +
+// attend path leaves it for this kernel, which runs after every reader).
 __global__ __launch_bounds__(256) void attend_reduce_kernel(const float* part, int n_split, int D,
-                                                           int HG, float* out) {
+                                                           int HG, float* out, uint32_t* zero_hist,
+                                                           int G) {
   extern __shared__ float ps[];          // [n_split][D + 2]
   __shared__ float wts[64];
   __shared__ float inv_l;
   const int hq = blockIdx.x, b = blockIdx.y;
+  if (zero_hist && hq % G == 0) {
+    uint4* z = (uint4*)(zero_hist + ((int64_t)b * (HG / G) + hq / G) * 4096);
+    for (int i = threadIdx.x; i < 1024; i += blockDim.x) z[i] = make_uint4(0u, 0u, 0u, 0u);
+  }
   const int stride = D + 2;
   const int n = n_split * stride;
   const float* base = part + ((int64_t)b * HG + hq) * n;
@@ -501,7 +508,7 @@ hipError_t launch_gather_attend(const KvArgs& kv, const void* q, int G, const in
 }
 
 hipError_t launch_attend_reduce(const float* part, int n_split, int D, int HG, int B, float* out,
-                                hipStream_t st) {
+                                hipStream_t st, uint32_t* zero_hist, int G) {
   dim3 grid(HG, B);
   const size_t lds = (size_t)n_split * (D + 2) * sizeof(float);
   static bool attr_set = false;
@@ -512,7 +519,7 @@ hipError_t launch_attend_reduce(const float* part, int n_split, int D, int HG, i
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  attend_reduce_kernel<<<grid, 256, lds, st>>>(part, n_split, D, HG, out);
+  attend_reduce_kernel<<<grid, 256, lds, st>>>(part, n_split, D, HG, out, zero_hist, G);
   return hipGetLastError();
 }
 

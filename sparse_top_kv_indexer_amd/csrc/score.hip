@@ -34,7 +34,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kTile = 256;  // tokens per workgroup (multiple of 16)
 
-__device__ __forceinline__ u32x4_t ld16(const char* p) { return *(const u32x4_t*)p; }
 
 // Score-key histogram of the tile (top 12 bits of the order-preserving key),
 // built in LDS while scoring and added into the row's global histogram: the

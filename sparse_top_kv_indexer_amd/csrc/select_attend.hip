@@ -1,0 +1,281 @@
+// Fused exact top-k + gather + split-k attention of one decode step, after the
+// score scan has written the scores and the rows' top-12-bit key histograms.
+//
+// What is computed, per sequence b and KV head h (row r = b H + h):
+//   idx[r]  = the k largest finite scores of t in [lo, hi), ascending t, ties
+//             to the lower t (ECHO-OSDI26 wiki page, observation 5);
+//   out[b][h G + g] = softmax attention of query head g over
+//             {idx[r]} U {live t < lo} U {live t >= hi}
+//             (ParisKV close-reading, section 一, Eqs. (1)-(3); vToken reading
+//             notes, section 3.4 Eq. (2) for the slot mapping);
+// exactly what sparsekv_topk_resume followed by sparsekv_gather_attend
+// compute, in one kernel plus the split merge instead of three kernels.
+//
+// gfx950 design.  Grid (kSplits, rows), 1024 threads.  Every workgroup of a
+// row loads the whole row of scores (coalesced, into registers) and finds the
+// row's threshold redundantly, so no workgroup waits for another; workgroup s
+// then owns the positions of waves 2s and 2s + 1 (one eighth of the row):
+// it writes those positions' entries of idx and attends over them plus its
+// share of the sink and local tokens.  Per wave, 16 attended tokens at a time:
+// logits from matrix cores as S^T[16 tokens x 16 heads] = K_chunk . Q^T
+// (4 x v_mfma_f32_16x16x32_bf16), online softmax in the log2 domain, and the
+// value product on the vector ALUs with every lane owning two output dims of
+// every head.  The 16 waves' (max, sum, weighted values) merge through LDS
+// into the workgroup's split partial; attend_reduce_kernel merges the splits
+// and zeroes the rows' histograms for the next call.
+#include "skv_internal.h"
+#include "skv_rowsel.h"
+
+namespace skv {
+
+namespace {
+
+constexpr int kSplits = 8;                        // workgroups per row
+constexpr int kWavesPerSplit = kRowWaves / kSplits;
+constexpr int kSegPos = kWavesPerSplit * kSeg;    // positions per workgroup segment
+constexpr int kD = 128;
+
+template <int GMAX>
+__global__ __launch_bounds__(kRowThreads) void select_attend_kernel(
+    KvArgs kv, const uint16_t* q, int G, const float* scores, const int32_t* lo_p,
+    const int32_t* hi_p, int k, const uint32_t* ghist, float scale_log2, int32_t* idx,
+    int32_t* count, float* part) {
+  __shared__ RowSelLds L;
+  __shared__ int32_t lst[kSegPos];                  // this segment's selected positions
+  __shared__ int64_t rows_sh[kRowWaves][16];        // per wave: key-row offsets of a chunk
+  __shared__ float red[kRowWaves][kD + 2];          // per-head merge of the waves
+  const int s = blockIdx.x, row = blockIdx.y;
+  const int b = row / kv.H, h = row - b * kv.H;
+  const int lane = threadIdx.x & 63, wave = row_wave();
+  const int n = lane & 15, g4 = lane >> 4;
+  const RowWindow w = row_window(lo_p, hi_p, b, kv.L_max);
+  const float* srow = scores + (int64_t)row * kv.L_max + w.lo;
+  const bool vec = ((uintptr_t)srow & 15) == 0;
+
+  // 1. the row's threshold (histogram first, then the scores)
+  const uint4 gv = ((const uint4*)(ghist + (int64_t)row * kBins))[threadIdx.x];
+  float fv[kGroups][4];
+  row_load(srow, w, vec, 0, fv);
+  uint32_t kr[kGroups][4];
+  *(uint4*)(L.hist + 4 * threadIdx.x) = gv;
+  if (threadIdx.x < 256) L.dh[threadIdx.x] = 0u;
+  lds_barrier();
+  uint32_t T;
+  int need_eq, k_sel;
+  row_threshold(
+      L, k, [&]() { row_keys(fv, kr); },
+      [&](auto&& f) {
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) f(kr[g][e]);
+      },
+      &T, &need_eq, &k_sel);
+
+  // 2. ranks; this workgroup's segment (waves 2s, 2s + 1) is written to idx
+  //    and listed in LDS for the attention
+  int cg[kGroups];
+  const int lt = row_counts(kr, T, cg);
+  int oa, oe, ta, te;
+  row_wave_offsets(L, lt, &oa, &oe, &ta, &te);
+  int a_pre = 0, e_pre = 0;   // keys above / equal to T before this segment
+#pragma unroll
+  for (int v = 0; v < kRowWaves; ++v)
+    if (v < s * kWavesPerSplit) {
+      a_pre += L.wa[v];
+      e_pre += L.we[v];
+    }
+  const int seg_base = a_pre + min(e_pre, need_eq);   // rank of the segment's first key
+  int32_t* orow = idx + (int64_t)row * k;
+  if (wave / kWavesPerSplit == s) {
+    const int pos0 = wave * kSeg + 4 * lane;          // relative to lo
+    row_emit(kr, cg, T, need_eq, oa, oe, [&](int dst, int g, int e) {
+      const int t = w.lo + pos0 + 256 * g + e;
+      orow[dst] = t;
+      lst[dst - seg_base] = t;
+    });
+  }
+  int a_end = 0, e_end = 0;
+#pragma unroll
+  for (int v = 0; v < kRowWaves; ++v)
+    if (v < (s + 1) * kWavesPerSplit) {
+      a_end += L.wa[v];
+      e_end += L.we[v];
+    }
+  const int n_seg = a_end + min(e_end, need_eq) - seg_base;
+  if (s == 0) {
+    const int n_sel = min(k, ta + min(te, need_eq));   // == k_sel
+    for (int i = n_sel + threadIdx.x; i < k; i += kRowThreads) orow[i] = -1;
+    if (threadIdx.x == 0) count[row] = n_sel;
+  }
+  (void)k_sel;
+
+  // 3. attention over the listed positions plus this split's share of the
+  //    always-attended tokens t < lo and t >= hi (live ones)
+  const int seq = min(kv.seq_len[b], kv.L_max);
+  const int a_lo = min(w.lo, seq);
+  const int a_hi = max(a_lo, min(w.hi, seq));
+  const int n_extra = a_lo + (seq - a_hi);
+  const int x0 = (int)((int64_t)n_extra * s / kSplits);
+  const int x1 = (int)((int64_t)n_extra * (s + 1) / kSplits);
+  const int n_att = n_seg + (x1 - x0);
+  lds_barrier();   // lst is complete
+
+  bf16x8_t Qf[4];
+  {
+    const uint16_t* qrow = q + ((int64_t)row * G + (n < G ? n : 0)) * kD;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const u32x4_t v = n < G ? ld16((const char*)(qrow + 8 * (4 * j + g4))) : u32x4_t{0, 0, 0, 0};
+      Qf[j] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+  float m_run = -INFINITY, l_run = 0.f;   // head n (lanes n < G, every g4)
+  float acc[GMAX][2];                     // dims 2 lane, 2 lane + 1 of every head
+#pragma unroll
+  for (int g = 0; g < GMAX; ++g) acc[g][0] = acc[g][1] = 0.f;
+  const uint16_t* kb = (const uint16_t*)kv.k;
+  const uint16_t* vb = (const uint16_t*)kv.v;
+  const int n_ch = (n_att + 15) >> 4;
+  for (int c = wave; c < n_ch; c += kRowWaves) {
+    if (lane < 16) {
+      const int i = c * 16 + lane;
+      int t = -1;
+      if (i < n_seg) {
+        t = lst[i];
+      } else if (i < n_att) {
+        const int x = x0 + (i - n_seg);
+        t = x < a_lo ? x : a_hi + (x - a_lo);
+      }
+      const int64_t slot = t >= 0 ? slot_of(kv, b, t) : -1;
+      rows_sh[wave][lane] = slot >= 0 ? row_elem(kv, b, h, slot, kD) : -1;
+    }
+    const int64_t rk = rows_sh[wave][n];
+    bf16x8_t Kf[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const u32x4_t v = rk >= 0 ? ld16((const char*)(kb + rk + 8 * (4 * j + g4))) : u32x4_t{0, 0, 0, 0};
+      Kf[j] = __builtin_bit_cast(bf16x8_t, v);
+    }
+    uint32_t Vw[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int64_t rv = rows_sh[wave][t];
+      Vw[t] = rv >= 0 ? *(const uint32_t*)(vb + rv + 2 * lane) : 0u;
+    }
+    f32x4_t S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Kf[j], Qf[j], S, 0, 0, 0);
+    // lane (n, g4) holds the logits of query head n for tokens 4 g4 .. 4 g4 + 3
+    float z[4], cm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = rows_sh[wave][4 * g4 + i] >= 0;
+      z[i] = ok ? S[i] * scale_log2 : -INFINITY;
+      cm = fmaxf(cm, z[i]);
+    }
+    cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
+    cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
+    const float m_new = fmaxf(m_run, cm);
+    float p[4], ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = m_new == -INFINITY ? 0.f : exp2f(z[i] - m_new);
+      ps += p[i];
+    }
+    ps += __shfl_xor(ps, 16, 64);
+    ps += __shfl_xor(ps, 32, 64);
+    const float corr = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
+    l_run = l_run * corr + ps;
+    m_run = m_new;
+#pragma unroll
+    for (int g = 0; g < GMAX; ++g) {
+      if (g < G) {
+        const float cgr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(corr), g));
+        float a0 = acc[g][0] * cgr, a1 = acc[g][1] * cgr;
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          const float pg =
+              __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p[t & 3]), g + 16 * (t >> 2)));
+          a0 = fmaf(pg, bf16_lo(Vw[t]), a0);
+          a1 = fmaf(pg, bf16_hi(Vw[t]), a1);
+        }
+        acc[g][0] = a0;
+        acc[g][1] = a1;
+      }
+    }
+  }
+
+  // 4. merge the waves, one head at a time, into this split's partial
+  const int stride = kD + 2;
+  for (int g = 0; g < G; ++g) {
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int gg = 0; gg < GMAX; ++gg)
+      if (gg == g) {
+        a0 = acc[gg][0];
+        a1 = acc[gg][1];
+      }
+    red[wave][2 * lane] = a0;
+    red[wave][2 * lane + 1] = a1;
+    const float mg = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m_run), g));
+    const float lg = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l_run), g));
+    if (lane == 0) {
+      red[wave][kD] = mg;
+      red[wave][kD + 1] = lg;
+    }
+    lds_barrier();
+    if (threadIdx.x < kD) {
+      const int j = threadIdx.x;
+      float mm = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < kRowWaves; ++v) mm = fmaxf(mm, red[v][kD]);
+      float ll = 0.f, aa = 0.f;
+      if (mm != -INFINITY) {
+#pragma unroll
+        for (int v = 0; v < kRowWaves; ++v) {
+          const float cw = exp2f(red[v][kD] - mm);
+          ll += red[v][kD + 1] * cw;
+          aa += red[v][j] * cw;
+        }
+      }
+      float* dst = part + (((int64_t)row * G + g) * kSplits + s) * stride;
+      dst[j] = aa;
+      if (j == 0) {
+        dst[kD] = mm;
+        dst[kD + 1] = ll;
+      }
+    }
+    lds_barrier();
+  }
+}
+
+}  // namespace
+
+bool select_attend_supported(const KvArgs& kv, int G) {
+  return kv.bf16 && kv.v != nullptr && kv.d_k == kD && kv.d_v == kD && G >= 1 && G <= 8 &&
+         kv.L_max <= kSweep;
+}
+
+size_t select_attend_partial_bytes(const KvArgs& kv, int G) {
+  return (size_t)kv.B * kv.H * G * kSplits * (kD + 2) * sizeof(float);
+}
+
+hipError_t launch_select_attend(const KvArgs& kv, const void* q, int G, const float* scores,
+                                const int32_t* lo, const int32_t* hi, int k, uint32_t* hist,
+                                float scale, int32_t* idx, int32_t* count, float* part,
+                                float* out, hipStream_t st) {
+  const float scale_log2 = scale * 1.4426950408889634f;
+  dim3 grid(kSplits, kv.B * kv.H);
+  if (G <= 4)
+    select_attend_kernel<4><<<grid, kRowThreads, 0, st>>>(kv, (const uint16_t*)q, G, scores, lo, hi,
+                                                          k, hist, scale_log2, idx, count, part);
+  else
+    select_attend_kernel<8><<<grid, kRowThreads, 0, st>>>(kv, (const uint16_t*)q, G, scores, lo, hi,
+                                                          k, hist, scale_log2, idx, count, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_attend_reduce(part, kSplits, kD, kv.H * G, kv.B, out, st, hist, G);
+}
+
+}  // namespace skv

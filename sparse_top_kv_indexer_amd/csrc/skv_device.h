@@ -74,6 +74,9 @@ __device__ __forceinline__ int wave_excl_scan(int v, int lane) {
   return x - v;
 }
 
+// One 16-byte global load.
+__device__ __forceinline__ u32x4_t ld16(const char* p) { return *(const u32x4_t*)p; }
+
 // Inclusive prefix sum over the 64 lanes of a wave with DPP: Hillis-Steele
 // shifts of 1, 2, 4, 8 inside each 16-lane row (lanes without a source add
 // 0), then lane 15 of each row into the next row and lane 31 into rows 2, 3.

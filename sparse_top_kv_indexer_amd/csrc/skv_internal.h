@@ -43,7 +43,16 @@ bool attend_supported(const KvArgs& kv, int G);
 // merge of split partials [B][HG][n_split][D + 2] (acc[D], max, sum; log2
 // domain) into out [B][HG][D]
 hipError_t launch_attend_reduce(const float* part, int n_split, int D, int HG, int B, float* out,
-                                hipStream_t s);
+                                hipStream_t s, uint32_t* zero_hist = nullptr, int G = 1);
+
+// select_attend.hip: exact top-k fused with gather + split attention (after
+// launch_score with a histogram); bf16, d = 128, G <= 8, L_max <= 32768
+bool select_attend_supported(const KvArgs& kv, int G);
+size_t select_attend_partial_bytes(const KvArgs& kv, int G);
+hipError_t launch_select_attend(const KvArgs& kv, const void* q, int G, const float* scores,
+                                const int32_t* lo, const int32_t* hi, int k, uint32_t* hist,
+                                float scale, int32_t* idx, int32_t* count, float* part,
+                                float* out, hipStream_t s);
 
 // mla.hip: shared-latent attention on matrix cores (v == nullptr)
 bool mla_supported(const KvArgs& kv, int G);

@@ -1,0 +1,268 @@
+// Exact top-k selection of one row of fp32 scores by one 1024-thread
+// workgroup: the building blocks shared by the standalone top-k kernel and the
+// fused select + attend kernel.
+//
+// Keys: an order-preserving 32-bit image of the score (sign-flipped float
+// bits; -0.0 maps to +0.0; inf and nan map to 0, which is never selected).
+// Selected: every key > T plus the first need_eq keys equal to T, in
+// position order (ties go to the lower position).
+//
+// Layout: in sweep s, lane l of wave w holds the keys of the positions
+// s * kSweep + w * kSeg + 256 g + 4 l + e (g < kGroups, e < 4) relative to the
+// window start, so every load instruction reads 1 KB of consecutive scores.
+#pragma once
+
+#include "skv_device.h"
+
+namespace skv {
+
+constexpr int kRowThreads = 1024;
+constexpr int kRowWaves = kRowThreads / 64;
+constexpr int kGroups = 8;                    // groups of 4 consecutive keys per lane per sweep
+constexpr int kSeg = 256 * kGroups;           // positions per wave per sweep
+constexpr int kSweep = kRowWaves * kSeg;      // positions per sweep (32768)
+constexpr int kBins = 4096;
+
+__device__ __forceinline__ uint32_t score_key(float s) {
+  uint32_t u = __float_as_uint(s);
+  if ((u & 0x7f800000u) == 0x7f800000u) return 0u;   // inf / nan: not a candidate
+  if (u == 0x80000000u) u = 0u;                        // -0.0 == +0.0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);   // finite keys are >= 0x00800000
+}
+
+struct RowWindow {
+  int lo, hi, n;
+};
+
+__device__ __forceinline__ RowWindow row_window(const int32_t* lo_p, const int32_t* hi_p, int b,
+                                                int L_max) {
+  RowWindow w;
+  w.lo = max(0, min(lo_p[b], L_max));
+  w.hi = max(w.lo, min(hi_p[b], L_max));
+  w.n = w.hi - w.lo;
+  return w;
+}
+
+__device__ __forceinline__ int wave_total(int incl) { return __builtin_amdgcn_readlane(incl, 63); }
+
+// This thread's wave index, known to the compiler to be uniform.
+__device__ __forceinline__ int row_wave() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// In a wave whose lane holds the counts c of 4 bins first_bin .. first_bin + 3
+// and `above` = entries in bins above them: if the need-th largest entry lies
+// in one of these bins, write {bin, entries above it, entries in it} to trio.
+__device__ __forceinline__ void pick_bin(const uint4& c, int first_bin, int above, int need,
+                                         int* trio) {
+  const int cs[4] = {(int)c.x, (int)c.y, (int)c.z, (int)c.w};
+#pragma unroll
+  for (int j = 3; j >= 0; --j) {
+    if (above < need && need <= above + cs[j]) {
+      trio[0] = first_bin + j;
+      trio[1] = above;
+      trio[2] = cs[j];
+    }
+    above += cs[j];
+  }
+}
+
+struct RowSelLds {
+  uint32_t hist[kBins];   // top 12 key bits, then bits 19..8 of bin b0's keys
+  uint32_t dh[256];       // bits 7..0 of the keys matching the top 24 bits
+  int wt[kRowWaves], wa[kRowWaves], we[kRowWaves];
+  int trio[3];
+};
+
+// Scores of sweep sw; positions past the window read as -inf.
+__device__ __forceinline__ void row_load(const float* s, const RowWindow& w, bool vec, int sw,
+                                         float (&v)[kGroups][4]) {
+  const int lane = threadIdx.x & 63, wave = row_wave();
+  const int p0 = sw * kSweep + wave * kSeg + 4 * lane;
+#pragma unroll
+  for (int g = 0; g < kGroups; ++g) {
+    const int p = p0 + 256 * g;
+    if (vec && p + 4 <= w.n) {
+      const float4 f = *(const float4*)(s + p);
+      v[g][0] = f.x;
+      v[g][1] = f.y;
+      v[g][2] = f.z;
+      v[g][3] = f.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[g][e] = p + e < w.n ? s[p + e] : -INFINITY;
+    }
+  }
+}
+
+__device__ __forceinline__ void row_keys(const float (&v)[kGroups][4], uint32_t (&kk)[kGroups][4]) {
+#pragma unroll
+  for (int g = 0; g < kGroups; ++g)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) kk[g][e] = score_key(v[g][e]);
+}
+
+// The need-th largest entry of the kBins-bin histogram in L.hist (wave w
+// covers bins 256 w .. 256 w + 255): two barriers; *total receives the
+// histogram's total.  need < 0 asks for the min(-need, total)-th; the
+// effective rank is returned and, when 1 <= rank < total, L.trio holds
+// {bin, entries above it, entries in it} afterwards.
+__device__ __forceinline__ int row_search4096(RowSelLds& L, int need, int* total) {
+  const int lane = threadIdx.x & 63, wave = row_wave();
+  const uint4 c4 = *(const uint4*)(L.hist + 4 * threadIdx.x);
+  const int incl = wave_incl_scan((int)(c4.x + c4.y + c4.z + c4.w));
+  const int tot_w = wave_total(incl);
+  if (lane == 0) L.wt[wave] = tot_w;
+  lds_barrier();
+  int all = 0, above_w = 0;
+#pragma unroll
+  for (int v = 0; v < kRowWaves; ++v) {
+    all += L.wt[v];
+    if (v > wave) above_w += L.wt[v];
+  }
+  *total = all;
+  const int nd = need < 0 ? min(-need, all) : need;
+  if (nd >= 1 && nd < all) pick_bin(c4, 4 * threadIdx.x, above_w + (tot_w - incl), nd, L.trio);
+  lds_barrier();
+  return nd;
+}
+
+// Threshold of the row once L.hist holds its top-12-bit histogram (and a
+// barrier has passed).  keys_ready() runs after the first search (callers
+// convert resident scores to keys there, overlapping their arrival);
+// for_keys(f) calls f(key) for every key of the window.
+template <class KeysReady, class ForKeys>
+__device__ __forceinline__ void row_threshold(RowSelLds& L, int k, KeysReady&& keys_ready,
+                                              ForKeys&& for_keys, uint32_t* T_out,
+                                              int* need_eq_out, int* k_sel_out) {
+  const int lane = threadIdx.x & 63, wave = row_wave();
+  int n_cand;
+  const int k_sel = row_search4096(L, -k, &n_cand);   // min(k, n_cand)
+  keys_ready();
+  uint32_t T = 0u;   // k_sel == n_cand: every finite key (key > 0)
+  int need_eq = 0;
+  if (k_sel <= 0) {
+    T = 0xffffffffu;   // nothing: finite keys are below 0xff800000
+  } else if (k_sel < n_cand) {
+    const int b0 = L.trio[0], above = L.trio[1], in_bin = L.trio[2];
+    int need = k_sel - above;
+    T = ((uint32_t)b0 << 20) - 1u;   // the whole bin b0 is taken
+    if (need < in_bin) {
+      // bits 19..8 of the keys of bin b0 (finite keys have top bits >= 8, so
+      // b0 >= 8 and empty slots never match)
+      lds_barrier();   // everyone has read trio and the top-bit counts
+      *(uint4*)(L.hist + 4 * threadIdx.x) = make_uint4(0u, 0u, 0u, 0u);
+      lds_barrier();
+      for_keys([&](uint32_t key) {
+        if ((key >> 20) == (uint32_t)b0) atomicAdd(&L.hist[(key >> 8) & 0xfffu], 1u);
+      });
+      lds_barrier();
+      int unused;
+      row_search4096(L, need, &unused);
+      const int b1 = L.trio[0], ab1 = L.trio[1], ib1 = L.trio[2];
+      need -= ab1;
+      const uint32_t pre24 = ((uint32_t)b0 << 12) | (uint32_t)b1;
+      if (need == ib1) {
+        T = (pre24 << 8) - 1u;
+        need = 0;
+      } else {
+        // bits 7..0 of the keys matching the top 24 bits
+        for_keys([&](uint32_t key) {
+          if ((key >> 8) == pre24) atomicAdd(&L.dh[key & 0xffu], 1u);
+        });
+        lds_barrier();
+        if (wave == 0) {
+          const uint4 d4 = *(const uint4*)(L.dh + 4 * lane);
+          const int il = wave_incl_scan((int)(d4.x + d4.y + d4.z + d4.w));
+          pick_bin(d4, 4 * lane, wave_total(il) - il, need, L.trio);
+        }
+        lds_barrier();
+        const int b2 = L.trio[0], ab2 = L.trio[1], ib2 = L.trio[2];
+        need -= ab2;
+        T = (pre24 << 8) | (uint32_t)b2;
+        if (need == ib2) {
+          T -= 1u;
+          need = 0;
+        }
+      }
+      need_eq = need;
+    }
+  }
+  *T_out = T;
+  *need_eq_out = need_eq;
+  *k_sel_out = k_sel;
+}
+
+// Per group g, the lane's counts of keys above T (low 16 bits) and equal to T
+// (high 16 bits); returns the lane's total, packed the same way.
+__device__ __forceinline__ int row_counts(const uint32_t (&kk)[kGroups][4], uint32_t T,
+                                          int (&cg)[kGroups]) {
+  int tot = 0;
+#pragma unroll
+  for (int g = 0; g < kGroups; ++g) {
+    int c = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      c += (kk[g][e] > T) ? 1 : ((kk[g][e] != 0u && kk[g][e] == T) ? 0x10000 : 0);
+    cg[g] = c;
+    tot += c;
+  }
+  return tot;
+}
+
+// Exchange the waves' packed totals (two barriers): *oa / *oe receive the keys
+// above / equal to T in the waves before this one, *ta / *te the workgroup's.
+__device__ __forceinline__ void row_wave_offsets(RowSelLds& L, int lane_tot, int* oa, int* oe,
+                                                 int* ta, int* te) {
+  const int lane = threadIdx.x & 63, wave = row_wave();
+  const int wt_pk = wave_total(wave_incl_scan(lane_tot));
+  lds_barrier();   // earlier readers of wa / we are done
+  if (lane == 0) {
+    L.wa[wave] = wt_pk & 0xffff;
+    L.we[wave] = wt_pk >> 16;
+  }
+  lds_barrier();
+  int a = 0, e = 0, sa = 0, se = 0;
+#pragma unroll
+  for (int v = 0; v < kRowWaves; ++v) {
+    if (v < wave) {
+      a += L.wa[v];
+      e += L.we[v];
+    }
+    sa += L.wa[v];
+    se += L.we[v];
+  }
+  *oa = a;
+  *oe = e;
+  *ta = sa;
+  *te = se;
+}
+
+// The wave's selected keys in position order: emit(dst, g, e) for every key
+// taken, dst = its rank among the selected keys of the row.  oa / oe: keys
+// above / equal to T before this wave's positions.
+template <class Emit>
+__device__ __forceinline__ void row_emit(const uint32_t (&kk)[kGroups][4], const int (&cg)[kGroups],
+                                         uint32_t T, int need_eq, int oa, int oe, Emit&& emit) {
+#pragma unroll
+  for (int g = 0; g < kGroups; ++g) {
+    const int ig = wave_incl_scan(cg[g]);
+    const int gt = wave_total(ig);
+    int ab = oa + ((ig - cg[g]) & 0xffff), eb = oe + ((ig - cg[g]) >> 16);
+    if ((cg[g] & 0xffff) || ((cg[g] >> 16) && eb < need_eq)) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t key = kk[g][e];
+        if (key > T) {
+          emit(ab + min(eb, need_eq), g, e);
+          ++ab;
+        } else if (key != 0u && key == T) {
+          if (eb < need_eq) emit(ab + eb, g, e);
+          ++eb;
+        }
+      }
+    }
+    oa += gt & 0xffff;
+    oe += gt >> 16;
+  }
+}
+
+}  // namespace skv

@@ -55,7 +55,16 @@ class Run:
         return S.sparsekv_gather_attend(self.kv, self.q, self.st.G, idx, self.st.k, self.lo, self.hi,
                                         self.st.scale)
 
+    def select_attend(self, ws=None):
+        """the fused decode step: scan, top-k and attention in one call"""
+        r = S.sparsekv_select_attend(self.kv, self.q, self.st.G, self.lo, self.hi, self.st.k,
+                                     self.st.scale, ws=ws)
+        torch.cuda.synchronize()
+        return r
+
     def step(self, fused=True):
+        if fused == "all":
+            return self.select_attend()
         if fused:
             sc, idx, cnt = self.select()
         else:

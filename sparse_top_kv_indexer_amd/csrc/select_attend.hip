@@ -43,7 +43,8 @@ __global__ __launch_bounds__(kRowThreads) void select_attend_kernel(
   __shared__ RowSelLds L;
   __shared__ int32_t lst[kSegPos];                  // this segment's selected positions
   __shared__ int64_t rows_sh[kRowWaves][16];        // per wave: key-row offsets of a chunk
-  __shared__ float red[kRowWaves][kD + 2];          // per-head merge of the waves
+  __shared__ float red[kRowWaves][4][kD + 2];       // merge of the waves, 4 heads a round
+  __shared__ int32_t tbl[kSweep / 16];              // the row's block-table entries (paged)
   const int s = blockIdx.x, row = blockIdx.y;
   const int b = row / kv.H, h = row - b * kv.H;
   const int lane = threadIdx.x & 63, wave = row_wave();
@@ -56,6 +57,24 @@ __global__ __launch_bounds__(kRowThreads) void select_attend_kernel(
   const uint4 gv = ((const uint4*)(ghist + (int64_t)row * kBins))[threadIdx.x];
   float fv[kGroups][4];
   row_load(srow, w, vec, 0, fv);
+  // the block-table row, kept in registers until the attention needs it
+  const int n_blk = kv.block_table ? kv.L_max >> 4 : 0;
+  int32_t tb[kSweep / 16 / kRowThreads];
+#pragma unroll
+  for (int u = 0; u < kSweep / 16 / kRowThreads; ++u) {
+    const int i = threadIdx.x + u * kRowThreads;
+    tb[u] = i < n_blk ? kv.block_table[(int64_t)b * n_blk + i] : -1;
+  }
+  // the query rows (MFMA B operand of the logits), also needed only later
+  bf16x8_t Qf[4];
+  {
+    const uint16_t* qrow = q + ((int64_t)row * G + (n < G ? n : 0)) * kD;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const u32x4_t v = n < G ? ld16((const char*)(qrow + 8 * (4 * j + g4))) : u32x4_t{0, 0, 0, 0};
+      Qf[j] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
   uint32_t kr[kGroups][4];
   *(uint4*)(L.hist + 4 * threadIdx.x) = gv;
   if (threadIdx.x < 256) L.dh[threadIdx.x] = 0u;
@@ -119,17 +138,10 @@ __global__ __launch_bounds__(kRowThreads) void select_attend_kernel(
   const int x0 = (int)((int64_t)n_extra * s / kSplits);
   const int x1 = (int)((int64_t)n_extra * (s + 1) / kSplits);
   const int n_att = n_seg + (x1 - x0);
-  lds_barrier();   // lst is complete
-
-  bf16x8_t Qf[4];
-  {
-    const uint16_t* qrow = q + ((int64_t)row * G + (n < G ? n : 0)) * kD;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const u32x4_t v = n < G ? ld16((const char*)(qrow + 8 * (4 * j + g4))) : u32x4_t{0, 0, 0, 0};
-      Qf[j] = __builtin_bit_cast(bf16x8_t, v);
-    }
-  }
+  for (int u = 0; u < kSweep / 16 / kRowThreads; ++u) tbl[threadIdx.x + u * kRowThreads] = tb[u];
+  lds_barrier();   // lst and tbl are complete
+
   float m_run = -INFINITY, l_run = 0.f;   // head n (lanes n < G, every g4)
   float acc[GMAX][2];                     // dims 2 lane, 2 lane + 1 of every head
 #pragma unroll
@@ -147,7 +159,15 @@ __global__ __launch_bounds__(kRowThreads) void select_attend_kernel(
         const int x = x0 + (i - n_seg);
         t = x < a_lo ? x : a_hi + (x - a_lo);
       }
-      const int64_t slot = t >= 0 ? slot_of(kv, b, t) : -1;
+      int64_t slot = -1;
+      if (t >= 0) {
+        if (n_blk) {
+          const int e = t < seq ? tbl[t >> 4] : -1;
+          slot = e < 0 ? -1 : (int64_t)e * 16 + (t & 15);
+        } else {
+          slot = slot_of(kv, b, t);
+        }
+      }
       rows_sh[wave][lane] = slot >= 0 ? row_elem(kv, b, h, slot, kD) : -1;
     }
     const int64_t rk = rows_sh[wave][n];
@@ -206,37 +226,44 @@ __global__ __launch_bounds__(kRowThreads) void select_attend_kernel(
     }
   }
 
-  // 4. merge the waves, one head at a time, into this split's partial
+  // 4. merge the waves into this split's partial, four heads per round
   const int stride = kD + 2;
-  for (int g = 0; g < G; ++g) {
-    float a0 = 0.f, a1 = 0.f;
+  for (int g0 = 0; g0 < G; g0 += 4) {
+    if (g0) lds_barrier();   // the previous round has read red
 #pragma unroll
-    for (int gg = 0; gg < GMAX; ++gg)
-      if (gg == g) {
-        a0 = acc[gg][0];
-        a1 = acc[gg][1];
+    for (int gi = 0; gi < 4; ++gi) {
+      const int g = g0 + gi;
+      if (g < G) {
+        float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+        for (int gg = 0; gg < GMAX; ++gg)
+          if (gg == g) {
+            a0 = acc[gg][0];
+            a1 = acc[gg][1];
+          }
+        red[wave][gi][2 * lane] = a0;
+        red[wave][gi][2 * lane + 1] = a1;
+        const float mg = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m_run), g));
+        const float lg = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l_run), g));
+        if (lane == 0) {
+          red[wave][gi][kD] = mg;
+          red[wave][gi][kD + 1] = lg;
+        }
       }
-    red[wave][2 * lane] = a0;
-    red[wave][2 * lane + 1] = a1;
-    const float mg = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m_run), g));
-    const float lg = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l_run), g));
-    if (lane == 0) {
-      red[wave][kD] = mg;
-      red[wave][kD + 1] = lg;
     }
     lds_barrier();
-    if (threadIdx.x < kD) {
-      const int j = threadIdx.x;
+    const int gi = threadIdx.x / kD, j = threadIdx.x - gi * kD, g = g0 + gi;
+    if (gi < 4 && g < G) {
       float mm = -INFINITY;
 #pragma unroll
-      for (int v = 0; v < kRowWaves; ++v) mm = fmaxf(mm, red[v][kD]);
+      for (int v = 0; v < kRowWaves; ++v) mm = fmaxf(mm, red[v][gi][kD]);
       float ll = 0.f, aa = 0.f;
       if (mm != -INFINITY) {
 #pragma unroll
         for (int v = 0; v < kRowWaves; ++v) {
-          const float cw = exp2f(red[v][kD] - mm);
-          ll += red[v][kD + 1] * cw;
-          aa += red[v][j] * cw;
+          const float cw = exp2f(red[v][gi][kD] - mm);
+          ll += red[v][gi][kD + 1] * cw;
+          aa += red[v][gi][j] * cw;
         }
       }
       float* dst = part + (((int64_t)row * G + g) * kSplits + s) * stride;
@@ -246,7 +273,6 @@ __global__ __launch_bounds__(kRowThreads) void select_attend_kernel(
         dst[kD + 1] = ll;
       }
     }
-    lds_barrier();
   }
 }
 

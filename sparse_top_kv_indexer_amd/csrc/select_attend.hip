@@ -11,12 +11,14 @@
 // exactly what sparsekv_topk_resume followed by sparsekv_gather_attend
 // compute, in one kernel plus the split merge instead of three kernels.
 //
-// gfx950 design.  Grid (kSplits, rows), 1024 threads.  Every workgroup of a
-// row loads the whole row of scores (coalesced, into registers) and finds the
+// gfx950 design.  Grid (kSplits, rows), 1024 threads: 256 workgroups, one
+// per CU, for the 32 rows of the GQA workload.  Every workgroup of a row
+// loads the whole row of scores (coalesced, into registers) and finds the
 // row's threshold redundantly, so no workgroup waits for another; workgroup s
-// then owns the positions of waves 2s and 2s + 1 (one eighth of the row):
-// it writes those positions' entries of idx and attends over them plus its
-// share of the sink and local tokens.  Per wave, 16 attended tokens at a time:
+// then takes the selected keys of ranks [s k_sel / kSplits, (s + 1) k_sel /
+// kSplits) -- an equal share -- writes their entries of idx and attends over
+// them plus an equal share of the sink and local tokens (17 chunks of 16
+// tokens at k = 2048; every wave issues the loads of its two chunks at once).  Per wave, 16 attended tokens at a time:
 // logits from matrix cores as S^T[16 tokens x 16 heads] = K_chunk . Q^T
 // (4 x v_mfma_f32_16x16x32_bf16), online softmax in the log2 domain, and the
 // value product on the vector ALUs with every lane owning two output dims of
@@ -30,9 +32,8 @@ namespace skv {
 
 namespace {
 
-constexpr int kSplits = 8;                        // workgroups per row
-constexpr int kWavesPerSplit = kRowWaves / kSplits;
-constexpr int kSegPos = kWavesPerSplit * kSeg;    // positions per workgroup segment
+constexpr int kSplits = 8;                        // selection workgroups per row
+constexpr int kListCap = kSweep / kSplits;        // listed keys per workgroup (k <= 32768)
 constexpr int kD = 128;
 
 template <int GMAX>
@@ -41,8 +42,8 @@ __global__ __launch_bounds__(kRowThreads) void select_attend_kernel(
     const int32_t* hi_p, int k, const uint32_t* ghist, float scale_log2, int32_t* idx,
     int32_t* count, float* part) {
   __shared__ RowSelLds L;
-  __shared__ int32_t lst[kSegPos];                  // this segment's selected positions
-  __shared__ int64_t rows_sh[kRowWaves][16];        // per wave: key-row offsets of a chunk
+  __shared__ int32_t lst[kListCap];                 // this workgroup's share of the selection
+  __shared__ int64_t rows_sh[kRowWaves][2][16];     // per wave: key-row offsets of two chunks
   __shared__ float red[kRowWaves][4][kD + 2];       // merge of the waves, 4 heads a round
   __shared__ int32_t tbl[kSweep / 16];              // the row's block-table entries (paged)
   const int s = blockIdx.x, row = blockIdx.y;
@@ -91,53 +92,46 @@ __global__ __launch_bounds__(kRowThreads) void select_attend_kernel(
       },
       &T, &need_eq, &k_sel);
 
-  // 2. ranks; this workgroup's segment (waves 2s, 2s + 1) is written to idx
-  //    and listed in LDS for the attention
-  int cg[kGroups];
-  const int lt = row_counts(kr, T, cg);
-  int oa, oe, ta, te;
-  row_wave_offsets(L, lt, &oa, &oe, &ta, &te);
-  int a_pre = 0, e_pre = 0;   // keys above / equal to T before this segment
-#pragma unroll
-  for (int v = 0; v < kRowWaves; ++v)
-    if (v < s * kWavesPerSplit) {
-      a_pre += L.wa[v];
-      e_pre += L.we[v];
-    }
-  const int seg_base = a_pre + min(e_pre, need_eq);   // rank of the segment's first key
+  // 2. ranks.  Workgroup s writes idx and lists in LDS the selected keys of
+  //    ranks [r0, r1), an equal share of the k_sel selected keys
   int32_t* orow = idx + (int64_t)row * k;
-  if (wave / kWavesPerSplit == s) {
-    const int pos0 = wave * kSeg + 4 * lane;          // relative to lo
-    row_emit(kr, cg, T, need_eq, oa, oe, [&](int dst, int g, int e) {
-      const int t = w.lo + pos0 + 256 * g + e;
-      orow[dst] = t;
-      lst[dst - seg_base] = t;
-    });
-  }
-  int a_end = 0, e_end = 0;
-#pragma unroll
-  for (int v = 0; v < kRowWaves; ++v)
-    if (v < (s + 1) * kWavesPerSplit) {
-      a_end += L.wa[v];
-      e_end += L.we[v];
+  int n_list;
+  {
+    int cg[kGroups];
+    const int lt = row_counts(kr, T, cg);
+    int oa, oe, ta, te;
+    row_wave_offsets(L, lt, &oa, &oe, &ta, &te);
+    const int r0 = (int)((int64_t)k_sel * s / kSplits);
+    const int r1 = (int)((int64_t)k_sel * (s + 1) / kSplits);
+    n_list = r1 - r0;
+    // ranks of this wave's selected keys: [first, last)
+    const int first = oa + min(oe, need_eq);
+    const int last = oa + L.wa[wave] + min(oe + L.we[wave], need_eq);
+    if (first < r1 && last > r0) {
+      const int pos0 = wave * kSeg + 4 * lane;          // relative to lo
+      row_emit(kr, cg, T, need_eq, oa, oe, [&](int dst, int g, int e) {
+        if (dst >= r0 && dst < r1) {
+          const int t = w.lo + pos0 + 256 * g + e;
+          orow[dst] = t;
+          lst[dst - r0] = t;
+        }
+      });
     }
-  const int n_seg = a_end + min(e_end, need_eq) - seg_base;
-  if (s == 0) {
-    const int n_sel = min(k, ta + min(te, need_eq));   // == k_sel
-    for (int i = n_sel + threadIdx.x; i < k; i += kRowThreads) orow[i] = -1;
-    if (threadIdx.x == 0) count[row] = n_sel;
+    if (s == 0) {
+      const int n_sel = min(k, ta + min(te, need_eq));   // == k_sel
+      for (int i = n_sel + threadIdx.x; i < k; i += kRowThreads) orow[i] = -1;
+      if (threadIdx.x == 0) count[row] = n_sel;
+    }
   }
-  (void)k_sel;
 
-  // 3. attention over the listed positions plus this split's share of the
+  // 3. attention over the listed keys plus this workgroup's share of the
   //    always-attended tokens t < lo and t >= hi (live ones)
   const int seq = min(kv.seq_len[b], kv.L_max);
   const int a_lo = min(w.lo, seq);
   const int a_hi = max(a_lo, min(w.hi, seq));
   const int n_extra = a_lo + (seq - a_hi);
   const int x0 = (int)((int64_t)n_extra * s / kSplits);
-  const int x1 = (int)((int64_t)n_extra * (s + 1) / kSplits);
-  const int n_att = n_seg + (x1 - x0);
+  const int n_att = n_list + (int)((int64_t)n_extra * (s + 1) / kSplits) - x0;
 #pragma unroll
   for (int u = 0; u < kSweep / 16 / kRowThreads; ++u) tbl[threadIdx.x + u * kRowThreads] = tb[u];
   lds_barrier();   // lst and tbl are complete
@@ -148,16 +142,21 @@ __global__ __launch_bounds__(kRowThreads) void select_attend_kernel(
   for (int g = 0; g < GMAX; ++g) acc[g][0] = acc[g][1] = 0.f;
   const uint16_t* kb = (const uint16_t*)kv.k;
   const uint16_t* vb = (const uint16_t*)kv.v;
+  // chunks c and c + kRowWaves of this wave: both chunks' loads are issued
+  // before either is used
   const int n_ch = (n_att + 15) >> 4;
-  for (int c = wave; c < n_ch; c += kRowWaves) {
-    if (lane < 16) {
-      const int i = c * 16 + lane;
+  for (int c0 = wave; c0 < n_ch; c0 += 2 * kRowWaves) {
+    if (lane < 32) {
+      const int u = lane >> 4;
+      const int i = (c0 + u * kRowWaves) * 16 + (lane & 15);
       int t = -1;
-      if (i < n_seg) {
-        t = lst[i];
-      } else if (i < n_att) {
-        const int x = x0 + (i - n_seg);
-        t = x < a_lo ? x : a_hi + (x - a_lo);
+      if (i < n_att) {
+        if (i < n_list) {
+          t = lst[i];
+        } else {
+          const int x = x0 + (i - n_list);
+          t = x < a_lo ? x : a_hi + (x - a_lo);
+        }
       }
       int64_t slot = -1;
       if (t >= 0) {
@@ -168,60 +167,67 @@ __global__ __launch_bounds__(kRowThreads) void select_attend_kernel(
           slot = slot_of(kv, b, t);
         }
       }
-      rows_sh[wave][lane] = slot >= 0 ? row_elem(kv, b, h, slot, kD) : -1;
+      rows_sh[wave][u][lane & 15] = slot >= 0 ? row_elem(kv, b, h, slot, kD) : -1;
     }
-    const int64_t rk = rows_sh[wave][n];
-    bf16x8_t Kf[4];
+    bf16x8_t Kf[2][4];
+    uint32_t Vw[2][16];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const u32x4_t v = rk >= 0 ? ld16((const char*)(kb + rk + 8 * (4 * j + g4))) : u32x4_t{0, 0, 0, 0};
-      Kf[j] = __builtin_bit_cast(bf16x8_t, v);
+    for (int u = 0; u < 2; ++u) {
+      const int64_t rk = rows_sh[wave][u][n];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const u32x4_t v = rk >= 0 ? ld16((const char*)(kb + rk + 8 * (4 * j + g4))) : u32x4_t{0, 0, 0, 0};
+        Kf[u][j] = __builtin_bit_cast(bf16x8_t, v);
+      }
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const int64_t rv = rows_sh[wave][u][t];
+        Vw[u][t] = rv >= 0 ? *(const uint32_t*)(vb + rv + 2 * lane) : 0u;
+      }
     }
-    uint32_t Vw[16];
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const int64_t rv = rows_sh[wave][t];
-      Vw[t] = rv >= 0 ? *(const uint32_t*)(vb + rv + 2 * lane) : 0u;
-    }
-    f32x4_t S = {0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < 2; ++u) {
+      if (c0 + u * kRowWaves >= n_ch) break;
+      f32x4_t S = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Kf[j], Qf[j], S, 0, 0, 0);
-    // lane (n, g4) holds the logits of query head n for tokens 4 g4 .. 4 g4 + 3
-    float z[4], cm = -INFINITY;
+      for (int j = 0; j < 4; ++j) S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Kf[u][j], Qf[j], S, 0, 0, 0);
+      // lane (n, g4) holds the logits of query head n for tokens 4 g4 .. 4 g4 + 3
+      float z[4], cm = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool ok = rows_sh[wave][4 * g4 + i] >= 0;
-      z[i] = ok ? S[i] * scale_log2 : -INFINITY;
-      cm = fmaxf(cm, z[i]);
-    }
-    cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
-    cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
-    const float m_new = fmaxf(m_run, cm);
-    float p[4], ps = 0.f;
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = rows_sh[wave][u][4 * g4 + i] >= 0;
+        z[i] = ok ? S[i] * scale_log2 : -INFINITY;
+        cm = fmaxf(cm, z[i]);
+      }
+      cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
+      cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
+      const float m_new = fmaxf(m_run, cm);
+      float p[4], ps = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[i] = m_new == -INFINITY ? 0.f : exp2f(z[i] - m_new);
-      ps += p[i];
-    }
-    ps += __shfl_xor(ps, 16, 64);
-    ps += __shfl_xor(ps, 32, 64);
-    const float corr = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
-    l_run = l_run * corr + ps;
-    m_run = m_new;
+      for (int i = 0; i < 4; ++i) {
+        p[i] = m_new == -INFINITY ? 0.f : exp2f(z[i] - m_new);
+        ps += p[i];
+      }
+      ps += __shfl_xor(ps, 16, 64);
+      ps += __shfl_xor(ps, 32, 64);
+      const float corr = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
+      l_run = l_run * corr + ps;
+      m_run = m_new;
 #pragma unroll
-    for (int g = 0; g < GMAX; ++g) {
-      if (g < G) {
-        const float cgr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(corr), g));
-        float a0 = acc[g][0] * cgr, a1 = acc[g][1] * cgr;
+      for (int g = 0; g < GMAX; ++g) {
+        if (g < G) {
+          const float cgr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(corr), g));
+          float a0 = acc[g][0] * cgr, a1 = acc[g][1] * cgr;
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
-          const float pg =
-              __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p[t & 3]), g + 16 * (t >> 2)));
-          a0 = fmaf(pg, bf16_lo(Vw[t]), a0);
-          a1 = fmaf(pg, bf16_hi(Vw[t]), a1);
+          for (int t = 0; t < 16; ++t) {
+            const float pg = __int_as_float(
+                __builtin_amdgcn_readlane(__float_as_int(p[t & 3]), g + 16 * (t >> 2)));
+            a0 = fmaf(pg, bf16_lo(Vw[u][t]), a0);
+            a1 = fmaf(pg, bf16_hi(Vw[u][t]), a1);
+          }
+          acc[g][0] = a0;
+          acc[g][1] = a1;
         }
-        acc[g][0] = a0;
-        acc[g][1] = a1;
       }
     }
   }

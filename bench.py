@@ -2,31 +2,41 @@
 """Benchmark of one sparse top-k decode step on one MI355X.
 
 A step is one pass of the whole hot path over one batch of synthetic input
-already resident in HBM: score scan -> exact top-k -> gather + split-k
-attention (+ split merge), all through the C ABI of libsparsekv.so.
+already resident in HBM, all through the C ABI of libsparsekv.so.
 
 Default workload (the GQA paged decode the metric is quoted on):
   B = 4 sequences, 8 KV heads x 4 query heads, d = 128, L = 32768 bf16 keys
   and values in a 16-token paged pool whose block order is a seeded
   permutation, 4 outlier channels per KV head scaled x8, top-k = 2048 per KV
-  head plus 4 sink and 64 local tokens.
+  head plus 4 sink and 64 local tokens.  Step: score scan (with the first
+  top-k digit) -> exact top-k fused with gather + split attention -> merge.
 
-Successive steps use distinct device copies of the KV pool in turn (four by
-default, like four layers), so that a step never finds its keys in the 256 MB
-last-level cache left by the step before.  The K timed steps are captured
-into one HIP graph and replayed once, as a serving loop would (--eager
-launches every kernel from the host instead).  Per-kernel durations come from
-HIP events: with --eager inside the timed region; otherwise from a second
-graph of the same K steps with event-record nodes around each call, replayed
-right after the timed one (event nodes cost about 14 us per step on this
-runtime, so the timed graph carries none).
+Other workloads (--workload), each timed the same way:
+  single_head   B=1, L=4096 fp32 contiguous, planted query, top-64
+  token_pool    B=32, 8 KV heads, G=1, L=65536, token table, 50 % dead
+  indexer_mla   B=1, indexer keys d=128 + shared latent 576 (value 512),
+                128 query heads, L=131072 paged, top-2048 by the indexer
+  paris         compressed-code retrieval over 8 x 1,048,060 encoded keys
+                (query LUT, collision vote, top-C, rerank, top-100) + the
+                attention over retrieved + sink 4 + local 512
+  paris_encode  the off-step encode of that history (SRHT, ids, codes, w)
 
-Prints ONE JSON line (rank 0, N = 1) with the throughput in history keys
-scanned per second, the per-step time, the roofline entry of the dominant
-kernel (the score scan) and the CPU oracle timed on a bounded sample.
+Successive steps use distinct device copies of the inputs they stream (four
+by default, like four layers), so that a step never finds its data in the
+256 MB last-level cache left by the step before.  The K timed steps are
+captured into one HIP graph and replayed once, as a serving loop would
+(--eager launches every kernel from the host instead).  Per-call durations
+come from HIP events: with --eager inside the timed region; otherwise from a
+second graph of the same K steps with event-record nodes around each call,
+replayed right after the timed one (event nodes cost about 14 us per step on
+this runtime, so the timed graph carries none).
 
-  python bench.py [--steps K] [--warmup W] [--workload NAME] [--kv-copies C] [--eager]
-                  [--no-cpu-baseline]
+Prints ONE JSON line (rank 0, N = 1) with the throughput in keys per second,
+the per-step time, the roofline entry of the dominant kernel and the CPU
+oracle timed on a bounded sample of the same workload.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--kv-copies C]
+                  [--path fused|separate] [--eager] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -34,6 +44,7 @@ import argparse
 import dataclasses
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -42,7 +53,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, HERE)
 
 PEAK_HBM_GBPS = 8000.0
-WORKLOADS = ("gqa_paged", "token_pool", "single_head")
+PEAK_BF16_TFLOPS = 2500.0
+DENSE = ("gqa_paged", "token_pool", "single_head", "indexer_mla")
+WORKLOADS = DENSE + ("paris", "paris_encode")
 
 
 def parse():
@@ -53,70 +66,21 @@ def parse():
     ap.add_argument("--workload", default="gqa_paged", choices=WORKLOADS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kv-copies", type=int, default=4,
-                    help="distinct device copies of the KV pool, used in turn by successive "
-                         "steps (like successive layers), so that no step finds its keys in "
-                         "the 256 MB last-level cache")
+                    help="distinct device copies of the streamed inputs, used in turn by "
+                         "successive steps (like successive layers), so that no step finds "
+                         "its data in the 256 MB last-level cache")
     ap.add_argument("--path", default="fused", choices=("fused", "separate"),
-                    help="fused: sparsekv_score_hist + sparsekv_select_attend_resume (top-k "
-                         "fused with the attention); separate: sparsekv_score_hist + "
-                         "sparsekv_topk_resume + sparsekv_gather_attend")
+                    help="dense workloads: fused = sparsekv_score_hist + "
+                         "sparsekv_select_attend_resume (top-k fused with the attention); "
+                         "separate = sparsekv_score_hist + sparsekv_topk_resume + "
+                         "sparsekv_gather_attend (always used where the fused call does not "
+                         "support the shape)")
     ap.add_argument("--eager", action="store_true",
                     help="launch every kernel from the host instead of replaying one HIP graph "
                          "that holds the K timed steps")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
-
-
-def make(name):
-    import workloads as W
-    if name == "gqa_paged":
-        return W.make_gqa_paged()
-    if name == "token_pool":
-        return W.make_token_pool()
-    return W.make_single_head()
-
-
-def workload_config(st):
-    kv = st.kv
-    return {"workload": {"gqa_paged": "gqa_paged_decode", "token_pool": "token_table_decode",
-                         "single_head": "single_head_fp32"}[st.meta.get("bench_name", "gqa_paged")],
-            "B": kv.B, "H_kv": kv.H, "G": st.G, "d": kv.d_k, "L": kv.L_max, "k": st.k,
-            "sink": int(st.lo[0]), "local": int(kv.seq_len[0] - st.hi[0]),
-            "layout": kv.mode, "kv_dtype": kv.dtype}
-
-
-def scan_bytes_per_key(st):
-    """Algorithmic bytes the score scan must move per live key: the key row,
-    the fp32 score written, and the 4-byte table entry of token-level pools."""
-    es = 2 if st.kv.dtype == "bf16" else 4
-    b = st.kv.d_k * es + 4
-    if st.kv.token_table is not None:
-        b += 4
-    return b
-
-
-def live_keys(st):
-    kv = st.kv
-    if kv.token_table is not None:
-        return int((kv.token_table >= 0).sum()) * kv.H
-    return int(kv.seq_len.sum()) * kv.H
-
-
-def traffic_entry(kernel_src, n_launch_bytes_alg):
-    """HBM bytes per score-scan launch from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel source; else None."""
-    path = os.path.join(HERE, "profiles", "score_scan_gqa_paged_pmc.json")
-    if not os.path.exists(path):
-        return None
-    try:
-        rec = json.load(open(path))
-        h = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
-        if rec.get("source_sha256") != h:
-            return None
-        return rec["hbm_bytes_per_launch"]
-    except Exception:
-        return None
 
 
 class HipEvents:
@@ -130,7 +94,6 @@ class HipEvents:
         self.ct = ctypes
         self.torch = torch
         self.lib = ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
-        self.events = []
 
     def _ok(self, rc, what):
         if rc != 0:
@@ -142,7 +105,6 @@ class HipEvents:
     def create(self):
         e = self.ct.c_void_p()
         self._ok(self.lib.hipEventCreate(self.ct.byref(e)), "hipEventCreate")
-        self.events.append(e)
         return e
 
     def record(self, e):
@@ -170,29 +132,379 @@ class HipEvents:
         return ms.value
 
 
-def cpu_baseline(st, n_keys_step, min_seconds=10.0):
-    """The oracle as it stands, on whole steps of the same workload (every
-    (sequence, KV head) row: float64 scores, full sort, dense masked
-    softmax), repeated until at least min_seconds of CPU work."""
+def timed_steps(step, n_calls, args, hip):
+    """Warm up, then time exactly args.steps calls of step(i, mark).  step
+    calls mark(j) after its j-th ABI call (j = 0 .. n_calls - 1).  Returns wall seconds of the timed region, GPU ms per step
+    between events bracketing it, and per-call ms [steps][n_calls]."""
+    import torch
+    K = args.steps
+    for i in range(args.warmup):
+        step(i, None)
+    torch.cuda.synchronize()
+    evs = [[hip.create() for _ in range(n_calls + 1)] for _ in range(K)]
+    bracket = [hip.create(), hip.create()]
+
+    def marker(i, in_graph):
+        rec = hip.graph_record if in_graph else hip.record
+        return lambda j: rec(evs[i][j + 1])
+
+    def run(i, in_graph):
+        # evs[i][0] opens the step; step() marks the end of each of its calls
+        (hip.graph_record if in_graph else hip.record)(evs[i][0])
+        step(i, marker(i, in_graph))
+
+    if args.eager:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        hip.record(bracket[0])
+        for i in range(K):
+            run(i, False)
+        hip.record(bracket[1])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        note = "per-call events recorded inside the timed region"
+    else:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step(0, None)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph, graph_ev = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(K):
+                step(i, None)
+        with torch.cuda.graph(graph_ev):
+            for i in range(K):
+                run(i, True)
+        graph.replay()
+        torch.cuda.synchronize()
+        # timed region: exactly K steps (one replay), synchronised on both sides
+        t0 = time.perf_counter()
+        hip.record(bracket[0])
+        graph.replay()
+        hip.record(bracket[1])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        graph_ev.replay()
+        torch.cuda.synchronize()
+        note = ("per-call events from a replay of the same K steps with event-record graph "
+                "nodes, right after the timed replay")
+    calls = [[hip.elapsed_ms(evs[i][j], evs[i][j + 1]) for j in range(n_calls)] for i in range(K)]
+    return wall, hip.elapsed_ms(bracket[0], bracket[1]) / K, calls, note
+
+
+def traffic_entry(name, kernel_src):
+    """HBM bytes per launch of a kernel from its committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else None."""
+    path = os.path.join(HERE, "profiles", name)
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+        h = hashlib.sha256(open(os.path.join(HERE, kernel_src), "rb").read()).hexdigest()
+        if rec.get("source_sha256") != h:
+            return None
+        return rec["hbm_bytes_per_launch"]
+    except Exception:
+        return None
+
+
+def base_record(metric, value, unit, args, ms_per_step, dtype, config):
+    return {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+            "data": "synthetic (seeded, shaped like the pages' workloads)", "config": config}
+
+
+def roofline(kernel, bound, alg, seconds, traffic, extra=None):
+    if bound == "hbm":
+        achieved, peak, unit = alg / seconds / 1e9, PEAK_HBM_GBPS, "GB/s"
+    else:
+        achieved, peak, unit = alg / seconds / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+    r = {"kernel": kernel, "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+         "frac": achieved / peak, "traffic": traffic}
+    if extra:
+        r.update(extra)
+    return r
+
+
+# ------------------------------------------------------------------ dense
+def make_dense(name):
+    import workloads as W
+    return {"gqa_paged": W.make_gqa_paged, "token_pool": W.make_token_pool,
+            "single_head": W.make_single_head, "indexer_mla": W.make_indexer_mla}[name]()
+
+
+def dense_cpu_baseline(st, min_seconds=10.0):
+    """The oracle as it stands on (sequence, KV head) rows of the same
+    workload, taken in order and repeated until at least min_seconds of CPU
+    work: float64 scores, full sort, dense masked softmax."""
     from oracle import dense as D
     from threadpoolctl import threadpool_info
-    rows = [(b, h) for b in range(st.kv.B) for h in range(st.kv.H)]
-    n_steps = 0
+    kv = st.score_kv
+    rows = [(b, h) for b in range(kv.B) for h in range(kv.H)]
+    keys = 0
+    n_rows = 0
     t0 = time.perf_counter()
     while True:
-        for r in rows:
-            D.step(st, rows=[r])
-        n_steps += 1
+        b, h = rows[n_rows % len(rows)]
+        D.step(st, rows=[(b, h)])
+        keys += int(D.live_slots(kv, b)[0].size)
+        n_rows += 1
         if time.perf_counter() - t0 >= min_seconds:
             break
     dt = time.perf_counter() - t0
     blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
     cores = max([1] + blas)
-    return {"value": n_steps * n_keys_step / dt, "unit": "keys/s", "cores": cores, "kind": "oracle",
-            "sample": "%d whole steps of the same workload (%d rows, %d keys each), %.1f s; "
+    return {"value": keys / dt, "unit": "keys/s", "cores": cores, "kind": "oracle",
+            "sample": "%d (sequence, KV head) rows of the same workload in order (%d keys), %.1f s; "
                       "numpy float64, BLAS threads=%d, other ops single-threaded"
-                      % (n_steps, len(rows), n_keys_step, dt, cores),
-            "seconds_per_step": dt / n_steps}
+                      % (n_rows, keys, dt, cores)}
+
+
+def bench_dense(args, hip):
+    import numpy as np
+    import torch
+    import sparse_top_kv_indexer_amd as S
+    dev = torch.device("cuda:0")
+    st = make_dense(args.workload)
+    mla = st.kv.v is None
+    kv = S.kv_to_device(st.kv, dev)
+    skv = kv if st.score_kv is st.kv else S.kv_to_device(st.score_kv, dev)
+    bf = st.kv.dtype == "bf16"
+    q = S.to_device(st.q, dev, bf)
+    sq = q if st.score_q is st.q else S.to_device(st.score_q, dev, st.score_kv.dtype == "bf16")
+    lo = S.to_device(st.lo.astype(np.int32), dev)
+    hi = S.to_device(st.hi.astype(np.int32), dev)
+    B, H, L, k = skv.B, skv.H, skv.L_max, st.k
+    G, sG = st.G, st.score_G
+    scores = torch.empty((B, H, L), dtype=torch.float32, device=dev)
+    idx = torch.empty((B, H, k), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, H), dtype=torch.int32, device=dev)
+    out = torch.empty((kv.B, kv.H * G, kv.d_v), dtype=torch.float32, device=dev)
+    fused = (args.path == "fused" and skv is kv and sG == G and bf and not mla and kv.d_k == 128
+             and G <= 8 and L <= 32768)
+    if fused:
+        ws_sel = S.workspace(S.sparsekv_workspace_size(S.SKV_OP_SELECT_ATTEND, kv, G, k), dev)
+    else:
+        ws_sel = S.workspace(S.sparsekv_workspace_size(S.SKV_OP_SELECT, skv, sG, k), dev)
+        ws_att = S.workspace(S.sparsekv_workspace_size(S.SKV_OP_GATHER_ATTEND, kv, G, k), dev)
+
+    def copy_kv(t):
+        return dataclasses.replace(t, k=t.k.clone(), v=None if t.v is None else t.v.clone())
+
+    pairs = [(skv, kv)]
+    for _ in range(max(1, args.kv_copies) - 1):
+        c = copy_kv(kv)
+        pairs.append((c if skv is kv else copy_kv(skv), c))
+
+    def step(i, mark):
+        s_kv, a_kv = pairs[i % len(pairs)]
+        S.sparsekv_score_hist(s_kv, sq, sG, lo, hi, scores, ws_sel)
+        if mark:
+            mark(0)
+        if fused:
+            S.sparsekv_select_attend_resume(a_kv, q, G, lo, hi, k, st.scale, scores, idx, cnt, out,
+                                            ws_sel)
+        else:
+            S.sparsekv_topk_resume(scores, lo, hi, k, idx, cnt, ws_sel)
+            if mark:
+                mark(1)
+            S.sparsekv_gather_attend(a_kv, q, G, idx, k, lo, hi, st.scale, out, ws_att)
+        if mark:
+            mark(1 if fused else 2)
+
+    wall, gpu_ms, calls, note = timed_steps(step, 2 if fused else 3, args, hip)
+    calls = np.array(calls)
+    ms_per_step = wall * 1e3 / args.steps
+    # live keys and algorithmic bytes of the scan and the gather
+    from oracle import dense as D
+    n_keys = sum(int(D.live_slots(st.score_kv, b)[0].size) for b in range(B)) * H
+    es = 2 if st.score_kv.dtype == "bf16" else 4
+    per_key = st.score_kv.d_k * es + 4 + (4 if st.score_kv.token_table is not None else 0)
+    scan_bytes = n_keys * per_key + sq.numel() * sq.element_size()
+    cnt_np = cnt.cpu().numpy()
+    n_att = int(cnt_np.sum())
+    for b in range(B):
+        t_live = D.live_slots(st.kv, b)[0]
+        n_att += int(((t_live < st.lo[b]) | (t_live >= st.hi[b])).sum()) * kv.H
+    row_bytes = (kv.d_k * (2 if bf else 4)) * (1 if mla else 2)
+    gather_bytes = n_att * row_bytes
+    step_bytes = scan_bytes + gather_bytes
+    scan_s = float(np.mean(calls[:, 0])) * 1e-3
+    src = "sparse_top_kv_indexer_amd/csrc/score.hip"
+    kname = ("score_stream_kernel" if (bf and sG >= 2) else "score_valu_kernel")
+    tr = traffic_entry("score_scan_%s_pmc.json" % args.workload, src)
+    cfg = {"workload": args.workload, "B": B, "H_kv": kv.H, "G": G, "d": kv.d_k,
+           "L": L, "k": k, "layout": st.kv.mode, "kv_dtype": st.kv.dtype,
+           "kv_copies": len(pairs), "launch": "eager" if args.eager else "hip_graph",
+           "path": "fused" if fused else "separate"}
+    if args.workload != "indexer_mla":
+        cfg.update(sink=int(st.lo[0]), local=int(st.kv.seq_len[0] - st.hi[0]))
+    else:
+        cfg.update(d_latent=kv.d_k, d_value=kv.d_v, d_indexer=skv.d_k)
+    rec = base_record("history keys scanned/s (one sparse top-k decode step of one layer)",
+                      n_keys / (ms_per_step * 1e-3), "keys/s", args, ms_per_step,
+                      "bf16" if bf else "f32", cfg)
+    rec.update({
+        "us_per_step": ms_per_step * 1e3,
+        "us_per_step_gpu": gpu_ms * 1e3,
+        "timing": note,
+        "us_per_call": ({"score_scan": float(np.mean(calls[:, 0])) * 1e3,
+                         "select_attend_merge": float(np.mean(calls[:, 1])) * 1e3} if fused else
+                        {"score_scan": float(np.mean(calls[:, 0])) * 1e3,
+                         "topk": float(np.mean(calls[:, 1])) * 1e3,
+                         "gather_attend": float(np.mean(calls[:, 2])) * 1e3}),
+        "keys_scanned_per_step": n_keys,
+        "step_algorithmic_bytes": step_bytes,
+        "step_GBps": step_bytes / (ms_per_step * 1e-3) / 1e9,
+        "step_frac_of_hbm_peak": step_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+        "roofline": roofline("score scan (sparsekv_score_hist: %s with the fused top-k histogram)"
+                             % kname, "hbm", scan_bytes, scan_s, tr,
+                             {"algorithmic_bytes_per_launch": scan_bytes, "bytes_per_key": per_key}),
+    })
+    if mla:
+        # the latent attention is a dense contraction on matrix cores:
+        # per selected token and head, 576 + 512 multiply-adds
+        att_s = float(np.mean(calls[:, 2])) * 1e-3
+        flops = 2.0 * n_att * G * (kv.d_k + kv.d_v)
+        rec["roofline_attention"] = roofline("latent attention (sparsekv_gather_attend: "
+                                             "mla_split_kernel + merge)", "mfma", flops, att_s, None,
+                                             {"algorithmic_flops_per_launch": flops,
+                                              "gathered_bytes": gather_bytes})
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = dense_cpu_baseline(st)
+    return rec
+
+
+# ------------------------------------------------------------------ paris
+def paris_cpu_baseline(min_seconds=10.0):
+    """The oracle's encode + retrieval on a bounded sample of the same
+    workload: one KV head (4 query heads) of a 65,536-token history drawn the
+    same way, repeated until at least min_seconds of CPU work."""
+    import workloads as W
+    from oracle import lloyd
+    from oracle import paris as P
+    p = W.make_paris(tag=55, H=1, L=65536 + 516)
+    lv, th = lloyd.codebook_f32(8)
+    n_runs = 0
+    t0 = time.perf_counter()
+    while True:
+        P.retrieve(p, P.build_index(p, lv, th), lv)
+        n_runs += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
+    dt = time.perf_counter() - t0
+    from threadpoolctl import threadpool_info
+    blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+    cores = max([1] + blas)
+    return {"value": n_runs * p.H * p.n / dt, "unit": "keys/s", "cores": cores, "kind": "oracle",
+            "sample": "%d x (encode + retrieve) of 1 KV head x %d keys of the same distribution, "
+                      "%.1f s; numpy fp32 in the prescribed operation order, BLAS threads=%d"
+                      % (n_runs, p.n, dt, cores)}
+
+
+def bench_paris(args, hip):
+    import numpy as np
+    import torch
+    import sparse_top_kv_indexer_amd as S
+    import workloads as W
+    dev = torch.device("cuda:0")
+    p = W.make_paris()
+    cb = S.new_codebook(torch.from_numpy(p.signs).to(dev))
+    kv = S.kv_to_device(p.kv(), dev)
+    encode_only = args.workload == "paris_encode"
+    indexes = [S.new_index(p.H, p.n, device=dev) for _ in range(max(1, args.kv_copies)
+                                                              if encode_only else 1)]
+    for ix in indexes:
+        S.sparsekv_encode(cb, kv, 0, p.sink, p.L - p.local, ix)
+    torch.cuda.synchronize()
+    if encode_only:
+        kvs = [kv] + [dataclasses.replace(kv, k=kv.k.clone(), v=None)
+                      for _ in range(max(1, args.kv_copies) - 1)]
+
+        def step(i, mark):
+            ix = indexes[i % len(indexes)]
+            ix.n = 0
+            S.sparsekv_encode(cb, kvs[i % len(kvs)], 0, p.sink, p.L - p.local, ix)
+            if mark:
+                mark(0)
+
+        wall, gpu_ms, calls, note = timed_steps(step, 1, args, hip)
+        ms = wall * 1e3 / args.steps
+        n = p.H * p.n
+        # per key: 256 B row in; 16 B ids + 64 B codes + 64 B w out
+        alg = n * (256 + 16 + 64 + 64)
+        t_s = float(np.mean(np.array(calls)[:, 0])) * 1e-3
+        rec = base_record("keys encoded/s (compressed-code index build, off the decode step)",
+                          n / (ms * 1e-3), "keys/s", args, ms, "f32",
+                          {"workload": "paris_encode", "H_kv": p.H, "d": p.d, "L": p.L, "n": p.n,
+                           "n_sub": p.n_sub, "m": p.m, "copies": len(kvs),
+                           "launch": "eager" if args.eager else "hip_graph"})
+        rec.update({"us_per_step": ms * 1e3, "us_per_step_gpu": gpu_ms * 1e3, "timing": note,
+                    "roofline": roofline("encode (sparsekv_encode: encode_kernel)", "hbm", alg, t_s,
+                                         None, {"algorithmic_bytes_per_launch": alg,
+                                                "bytes_per_key": 400})})
+        return rec
+
+    # retrieval step: index copies (the id arrays, 134 MB, would otherwise sit
+    # in the last-level cache) and the attention over the result
+    base = indexes[0]
+    ixs = [base]
+    for _ in range(max(1, args.kv_copies) - 1):
+        ixs.append(dataclasses.replace(base, ids=base.ids.clone(), codes=base.codes.clone(),
+                                       w=base.w.clone(), hist=base.hist.clone(), pos=base.pos.clone()))
+    kvs = [kv] + [dataclasses.replace(kv, k=kv.k.clone(), v=kv.v.clone())
+                  for _ in range(max(1, args.kv_copies) - 1)]
+    q = S.to_device(p.q, dev, bf16=True)
+    qa = q.view(1, p.H * p.G, p.d)
+    lo = torch.tensor([p.sink], dtype=torch.int32, device=dev)
+    hi = torch.tensor([p.L - p.local], dtype=torch.int32, device=dev)
+    ridx = torch.empty((p.H, p.k_final), dtype=torch.int32, device=dev)
+    ncand = torch.empty((p.H,), dtype=torch.int32, device=dev)
+    out = torch.empty((1, p.H * p.G, p.d), dtype=torch.float32, device=dev)
+    ws_r = S.workspace(S.retrieve_workspace_size(base, p.G, p.beta, p.k_final), dev)
+    ws_a = S.workspace(S.sparsekv_workspace_size(S.SKV_OP_GATHER_ATTEND, kv, p.G, p.k_final), dev)
+
+    def step(i, mark):
+        S.sparsekv_retrieve(cb, ixs[i % len(ixs)], q, p.G, p.rho, p.beta, p.k_final, idx=ridx,
+                            n_cand=ncand, ws=ws_r)
+        if mark:
+            mark(0)
+        S.sparsekv_gather_attend(kvs[i % len(kvs)], qa, p.G, ridx.view(1, p.H, -1), p.k_final, lo, hi,
+                                 p.scale, out, ws_a)
+        if mark:
+            mark(1)
+
+    wall, gpu_ms, calls, note = timed_steps(step, 2, args, hip)
+    calls = np.array(calls)
+    ms = wall * 1e3 / args.steps
+    n_keys = p.H * p.n
+    C = int(math.ceil(p.beta * p.n))
+    ret_bytes = n_keys * 16 + p.H * C * 128      # ids scanned + codes and w of the candidates
+    gather = p.H * (p.k_final + p.sink + p.local) * 512
+    t_ret = float(np.mean(calls[:, 0])) * 1e-3
+    rec = base_record("history keys voted/s (one compressed-code retrieval decode step)",
+                      n_keys / (ms * 1e-3), "keys/s", args, ms, "u8/f32",
+                      {"workload": "paris", "B": 1, "H_kv": p.H, "G": p.G, "d": p.d, "L": p.L,
+                       "n": p.n, "beta": p.beta, "rho": p.rho, "C": C, "k_final": p.k_final,
+                       "sink": p.sink, "local": p.local, "copies": len(ixs),
+                       "launch": "eager" if args.eager else "hip_graph"})
+    rec.update({
+        "us_per_step": ms * 1e3, "us_per_step_gpu": gpu_ms * 1e3, "timing": note,
+        "us_per_call": {"retrieve": t_ret * 1e6, "gather_attend": float(np.mean(calls[:, 1])) * 1e3},
+        "keys_voted_per_step": n_keys,
+        "step_algorithmic_bytes": ret_bytes + gather,
+        "step_GBps": (ret_bytes + gather) / (ms * 1e-3) / 1e9,
+        "roofline": roofline("retrieval (sparsekv_retrieve: query LUT, collision vote, top-C, "
+                             "rerank, top-100; the vote kernel moves 94 % of the bytes)", "hbm",
+                             ret_bytes, t_ret, None,
+                             {"algorithmic_bytes_per_launch": ret_bytes}),
+    })
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = paris_cpu_baseline()
+    return rec
 
 
 def main():
@@ -201,9 +513,8 @@ def main():
         print("bench.py measures the single-GPU hot path only; run it with --gpus 1 "
               "(multi-GPU sharding is a design note, not built)", file=sys.stderr)
         sys.exit(2)
-    import numpy as np
     import torch
-    import sparse_top_kv_indexer_amd as S
+    import sparse_top_kv_indexer_amd as S  # noqa: F401  (fails loudly without the library)
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -216,162 +527,8 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calib_copy_bytes": n, "launches": 5}))
         return
-
-    st = make(args.workload)
-    st.meta["bench_name"] = args.workload
-    kv = S.kv_to_device(st.kv, dev)
-    bf = st.kv.dtype == "bf16"
-    q = S.to_device(st.q, dev, bf)
-    lo = S.to_device(st.lo.astype(np.int32), dev)
-    hi = S.to_device(st.hi.astype(np.int32), dev)
-    B, H, L, G, k = kv.B, kv.H, kv.L_max, st.G, st.k
-    scores = torch.empty((B, H, L), dtype=torch.float32, device=dev)
-    idx = torch.empty((B, H, k), dtype=torch.int32, device=dev)
-    cnt = torch.empty((B, H), dtype=torch.int32, device=dev)
-    out = torch.empty((B, H * G, kv.d_v), dtype=torch.float32, device=dev)
-    fused = args.path == "fused"
-    if fused:
-        ws_sel = S.workspace(S.sparsekv_workspace_size(S.SKV_OP_SELECT_ATTEND, kv, G, k), dev)
-    else:
-        ws = S.workspace(S.sparsekv_workspace_size(S.SKV_OP_GATHER_ATTEND, kv, G, k), dev)
-        ws_sel = S.workspace(S.sparsekv_workspace_size(S.SKV_OP_SELECT, kv, G, k), dev)
-    copies = [kv] + [dataclasses.replace(kv, k=kv.k.clone(), v=None if kv.v is None else kv.v.clone())
-                     for _ in range(max(1, args.kv_copies) - 1)]
     hip = HipEvents()
-
-    def step(i, ev=None, in_graph=False):
-        # sparsekv_select in its two halves (score scan with the first top-k
-        # digit fused, then the rest of the exact top-k), so that the events
-        # time the scan alone
-        c = copies[i % len(copies)]
-        mark = (lambda e: hip.graph_record(e)) if in_graph else (lambda e: hip.record(e))
-        if ev is not None:
-            mark(ev[0])
-        S.sparsekv_score_hist(c, q, G, lo, hi, scores, ws_sel)
-        if ev is not None:
-            mark(ev[1])
-        if fused:
-            S.sparsekv_select_attend_resume(c, q, G, lo, hi, k, st.scale, scores, idx, cnt, out,
-                                            ws_sel)
-            if ev is not None:
-                mark(ev[2])
-        else:
-            S.sparsekv_topk_resume(scores, lo, hi, k, idx, cnt, ws_sel)
-            if ev is not None:
-                mark(ev[2])
-            S.sparsekv_gather_attend(c, q, G, idx, k, lo, hi, st.scale, out, ws)
-        if ev is not None:
-            mark(ev[3])
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    evs = [[hip.create() for _ in range(4)] for _ in range(args.steps)]
-    bracket = [hip.create(), hip.create()]
-    if args.eager:
-        # timed region: exactly K steps launched from the host, with events
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        hip.record(bracket[0])
-        for i in range(args.steps):
-            step(i, evs[i])
-        hip.record(bracket[1])
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        timing_note = "per-kernel events recorded inside the timed region"
-    else:
-        # The K steps are captured into one HIP graph and replayed (as a
-        # serving loop would).  Event-record nodes inside a graph cost about
-        # 14 us per step on this runtime, so the timed replay carries none;
-        # the per-kernel durations come from a second graph of the same K
-        # steps, identical except for event-record nodes around each call,
-        # replayed right after.
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            step(0)
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        graph, graph_ev = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for i in range(args.steps):
-                step(i)
-        with torch.cuda.graph(graph_ev):
-            for i in range(args.steps):
-                step(i, evs[i], in_graph=True)
-        graph.replay()
-        torch.cuda.synchronize()
-        # timed region: exactly K steps (one replay), synchronised on both sides
-        t0 = time.perf_counter()
-        hip.record(bracket[0])
-        graph.replay()
-        hip.record(bracket[1])
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        graph_ev.replay()
-        torch.cuda.synchronize()
-        timing_note = ("per-kernel events from a replay of the same K steps with "
-                       "event-record graph nodes, right after the timed replay")
-
-    score_ms = [hip.elapsed_ms(e[0], e[1]) for e in evs]
-    topk_ms = [hip.elapsed_ms(e[1], e[2]) for e in evs]
-    attn_ms = [hip.elapsed_ms(e[2], e[3]) for e in evs]
-    step_ms = [hip.elapsed_ms(e[0], e[3]) for e in evs]
-    gpu_ms_per_step = hip.elapsed_ms(bracket[0], bracket[1]) / args.steps
-    ms_per_step = wall * 1e3 / args.steps
-    n_keys = live_keys(st)
-    per_key = scan_bytes_per_key(st)
-    score_bytes = n_keys * per_key + q.numel() * q.element_size()
-    score_avg_s = float(np.mean(score_ms)) * 1e-3
-    achieved = score_bytes / score_avg_s / 1e9
-    gather_bytes = 0
-    if True:
-        cnt_np = cnt.cpu().numpy()
-        n_att = cnt_np.sum() + (st.lo.astype(np.int64).sum() + (st.kv.seq_len - st.hi).astype(np.int64).sum()) * H
-        gather_bytes = int(n_att) * kv.d_k * (2 if bf else 4) * 2
-    step_bytes = score_bytes + gather_bytes
-    tr = traffic_entry(os.path.join(HERE, "sparse_top_kv_indexer_amd", "csrc", "score.hip"),
-                       score_bytes)
-    rec = {
-        "metric": "history keys scanned/s (one sparse top-k decode step of one layer)",
-        "value": n_keys / (ms_per_step * 1e-3),
-        "unit": "keys/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16" if bf else "f32",
-        "data": "synthetic",
-        "config": dict(workload_config(st), kv_copies=len(copies),
-                       launch="eager" if args.eager else "hip_graph", path=args.path),
-        "us_per_step": ms_per_step * 1e3,
-        "us_per_step_gpu": gpu_ms_per_step * 1e3,
-        "timing": timing_note,
-        "us_per_step_events": {"median": float(np.median(step_ms)) * 1e3,
-                               "p10": float(np.percentile(step_ms, 10)) * 1e3,
-                               "p90": float(np.percentile(step_ms, 90)) * 1e3},
-        "kernels_us": ({"score": float(np.mean(score_ms)) * 1e3,
-                        "topk_attend_merge": float(np.mean(topk_ms)) * 1e3} if fused else
-                       {"score": float(np.mean(score_ms)) * 1e3,
-                        "topk": float(np.mean(topk_ms)) * 1e3,
-                        "gather_attend": float(np.mean(attn_ms)) * 1e3}),
-        "keys_scanned_per_step": n_keys,
-        "step_algorithmic_bytes": step_bytes,
-        "step_GBps": step_bytes / (ms_per_step * 1e-3) / 1e9,
-        "step_frac_of_hbm_peak": step_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,
-        "roofline": {"kernel": "score scan (sparsekv_score_hist: score_stream_kernel with the "
-                               "fused top-k histogram)", "bound": "hbm",
-                     "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBPS, "traffic": tr,
-                     "algorithmic_bytes_per_launch": score_bytes,
-                     "bytes_per_key": per_key},
-    }
-    if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(st, n_keys)
+    rec = bench_dense(args, hip) if args.workload in DENSE else bench_paris(args, hip)
     print(json.dumps(rec))
 
 

@@ -27,6 +27,7 @@
 
 #include "../../include/sparsekv.h"
 #include "skv_device.h"
+#include "skv_rowsel.h"
 #include "skv_topk.h"
 
 namespace skv {
@@ -35,7 +36,8 @@ namespace {
 
 constexpr int kD = 128, kSub = 16, kM = 8, kCent = 256;
 constexpr int kVoteBins = 6 * kSub + 1;   // S in [0, 96]
-constexpr int kChunk = 2048;              // index entries per vote workgroup
+constexpr int kGe = kVoteBins + 1;        // suffix counts #(S >= v), v = 0..97
+constexpr int kChunk = 8192;              // index entries per vote / compaction workgroup
 constexpr int kEncPerWG = 2048;           // keys per encode workgroup
 
 struct CodebookArgs {
@@ -198,22 +200,36 @@ __global__ __launch_bounds__(256) void encode_kernel(KvArgs kv, int b, int t0, i
 }
 
 // --------------------------------------------------------------- query LUT --
-// One workgroup per query head: rotate the query, rank the 256 centroids of
-// each subspace by similarity (ties: lower id) and assign tier weights from
-// the exclusive prefix counts of the index histogram.
+// Grid (16 subspaces, H KV heads, 4), 256 threads: workgroup (b, h, g) serves
+// query head h G + g in subspace b, one centroid per thread.  It rotates the
+// query (16 lanes) and keeps subspace b, ranks the 256 centroids by
+// similarity (ties: lower id), walks the ranking with the exclusive prefix
+// count of the index histogram and assigns the tier weights.  A rank is a
+// count of larger keys, the key being the similarity's order-preserving bits
+// (-0 = +0) above 255 - id, so ties need no second compare.  The LUT word of
+// (h, b, centroid) packs the G heads' weights into its bytes (byte g written
+// by workgroup g; 0 in bytes G..3), so the vote takes one lookup per subspace
+// for the whole group.
 __global__ __launch_bounds__(256) void query_lut_kernel(const uint16_t* q, int G,
                                                         const int8_t* signs, float c,
                                                         const int32_t* hist, TierArgs ta,
                                                         float* qt_out, float* qn_out,
                                                         uint8_t* lut) {
-  __shared__ float qt[kD];
-  __shared__ float sims[kCent];
-  __shared__ int cnt_sorted[kCent];
+  __shared__ float qsub[8];
+  __shared__ __align__(16) uint64_t keys[kCent];
+  __shared__ int ranked[kCent];
   __shared__ int wsum[4];
-  const int hq = blockIdx.x, h = hq / G;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid < 16) {
-    const int j = tid;
+  const int sb = blockIdx.x, h = blockIdx.y, g = blockIdx.z;
+  const int cid = threadIdx.x, lane = cid & 63, wave = cid >> 6;
+  uint8_t* dst = lut + (((int64_t)h * kSub + sb) * kCent + cid) * 4 + g;
+  if (g >= G) {   // uniform over the workgroup
+    *dst = 0;
+    return;
+  }
+  const int hq = h * G + g;
+  const int cnt = hist[((int64_t)h * kSub + sb) * kCent + cid];
+  if (cid < 16) {
+    const int j = cid;
     float x[8], sg[8];
     const u32x4_t wv = *(const u32x4_t*)(q + (int64_t)hq * kD + 8 * j);
 #pragma unroll
@@ -224,299 +240,356 @@ __global__ __launch_bounds__(256) void query_lut_kernel(const uint16_t* q, int G
 #pragma unroll
     for (int e = 0; e < 8; ++e) sg[e] = (float)signs[8 * j + e];
     const float nrm = rotate_row(x, j, sg, c);
+    if (j == sb) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      qt[8 * j + e] = x[e];
-      qt_out[(int64_t)hq * kD + 8 * j + e] = x[e];
+      for (int e = 0; e < 8; ++e) qsub[e] = x[e];
     }
-    if (j == 0) qn_out[hq] = nrm;
+    if (sb == 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qt_out[(int64_t)hq * kD + 8 * j + e] = x[e];
+      if (j == 0) qn_out[hq] = nrm;
+    }
   }
   __syncthreads();
-  const int cid = tid;   // centroid of this thread
-  for (int sb = 0; sb < kSub; ++sb) {
-    float pr[8];
+  float pr[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float v = qt[8 * sb + e];
-      pr[e] = ((cid >> e) & 1) ? -v : v;
-    }
-    const float sim = tree8(pr);
-    sims[cid] = sim;
-    __syncthreads();
-    int rank = 0;
-    for (int c2 = 0; c2 < kCent; ++c2) {
-      const float s2 = sims[c2];
-      rank += (s2 > sim) || (s2 == sim && c2 < cid);
-    }
-    const int cnt = hist[((int64_t)h * kSub + sb) * kCent + cid];
-    cnt_sorted[rank] = cnt;
-    __syncthreads();
-    // exclusive prefix over the ranked order
-    const int v = cnt_sorted[tid];
-    const int ex = wave_excl_scan(v, lane);
-    if (lane == 63) wsum[wave] = ex + v;
-    __syncthreads();
-    int before = ex;
-    for (int w2 = 0; w2 < wave; ++w2) before += wsum[w2];
-    cnt_sorted[tid] = before;           // now P at ranked position tid
-    __syncthreads();
-    const int P = cnt_sorted[rank];
-    int wt = 0;
-    if (P < ta.t_rho) {
-      int ell = 0;
-#pragma unroll
-      for (int i = 0; i < 6; ++i) ell += ta.T[i] <= P;
-      wt = 6 - ell;
-    }
-    lut[((int64_t)hq * kSub + sb) * kCent + cid] = (uint8_t)wt;
-    __syncthreads();
+  for (int e = 0; e < 8; ++e) {
+    const float v = qsub[e];
+    pr[e] = ((cid >> e) & 1) ? -v : v;
   }
+  uint32_t u = __float_as_uint(tree8(pr));
+  if (u == 0x80000000u) u = 0u;   // -0 ranks with +0
+  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint64_t key = ((uint64_t)ord << 8) | (uint64_t)(255 - cid);
+  keys[cid] = key;
+  lds_barrier();
+  int rank = 0;
+  const ulonglong2* k2 = (const ulonglong2*)keys;
+#pragma unroll 8
+  for (int i = 0; i < kCent / 2; ++i) {
+    const ulonglong2 kk = k2[i];
+    rank += kk.x > key;
+    rank += kk.y > key;
+  }
+  ranked[rank] = cnt;
+  lds_barrier();
+  // exclusive prefix of the counts in ranked order
+  const int v = ranked[cid];
+  const int incl = wave_incl_scan(v);
+  if (lane == 63) wsum[wave] = incl;
+  lds_barrier();
+  int before = incl - v;
+  for (int w2 = 0; w2 < wave; ++w2) before += wsum[w2];
+  ranked[cid] = before;   // now P at ranked position cid
+  lds_barrier();
+  const int P = ranked[rank];
+  int wt = 0;
+  if (P < ta.t_rho) {
+    int ell = 0;
+#pragma unroll
+    for (int i = 0; i < 6; ++i) ell += ta.T[i] <= P;
+    wt = 6 - ell;
+  }
+  *dst = (uint8_t)wt;
 }
 
 // -------------------------------------------------------------------- vote --
-// S_i = max_g sum_b LUT_g[b][id_ib]: the G <= 4 query heads' tier bytes are
-// packed into one u32 per (subspace, centroid), so one LDS lookup per
-// subspace serves the whole group (a byte never exceeds 96).  Each
-// workgroup also histograms its S values (32 bank-spread copies in LDS).
-__global__ __launch_bounds__(256) void vote_kernel(const uint8_t* ids, int cap, int n, int G,
-                                                   const uint8_t* lut, uint8_t* votes,
-                                                   int32_t* chunk_hist, int n_chunks) {
-  __shared__ uint32_t lut4[kSub * kCent];
+// Grid (n_chunks, H), 256 threads, kChunk entries per workgroup:
+// S_i = max_g sum_b LUT_g[b][id_ib] from one packed-LUT lookup per subspace
+// into votes [H][ldv] (ldv: n rounded up to 16 bytes; also into the caller's
+// [H][n] trace array when one is given)
+// (a byte never exceeds 96, so the four sums never carry into each other).
+// The workgroup histograms its S values (32 bank-spread copies in LDS) and
+// writes the suffix counts ge[v] = #(S >= v), v = 0..97, of its chunk, which
+// it also adds into the head's totals.
+__global__ __launch_bounds__(256) void vote_kernel(const uint8_t* ids, int cap, int n,
+                                                   const uint32_t* lut, uint8_t* votes, int ldv,
+                                                   uint8_t* votes_trace, int32_t* chunk_ge,
+                                                   int n_chunks, int32_t* tot_ge) {
+  __shared__ __align__(16) uint32_t lut4[kSub * kCent];
   __shared__ uint32_t vh[kVoteBins * 32];
-  const int h = blockIdx.y, chunk = blockIdx.x;
-  for (int i = threadIdx.x; i < kSub * kCent; i += 256) {
-    uint32_t p = 0u;
-    for (int g = 0; g < G; ++g) p |= (uint32_t)lut[(int64_t)(h * G + g) * kSub * kCent + i] << (8 * g);
-    lut4[i] = p;
-  }
-  for (int i = threadIdx.x; i < kVoteBins * 32; i += 256) vh[i] = 0u;
-  __syncthreads();
-  const int copy = threadIdx.x & 31;
+  __shared__ int cnt[128];
+  const int h = blockIdx.y, chunk = blockIdx.x, tid = threadIdx.x;
+  const uint4* lsrc = (const uint4*)(lut + (int64_t)h * kSub * kCent);
+  uint4 lv[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) lv[u] = lsrc[u * 256 + tid];
   const int i0 = chunk * kChunk;
   const u32x4_t* idrow = (const u32x4_t*)(ids + (int64_t)h * cap * kSub);
-  constexpr int U = kChunk / 256;
-  u32x4_t idv[U];
+  constexpr int U = 8;                        // entries per thread per round
+  constexpr int R = kChunk / (256 * U);       // rounds
+  u32x4_t cur[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const int i = i0 + u * 256 + threadIdx.x;
-    idv[u] = i < n ? idrow[i] : u32x4_t{0, 0, 0, 0};
+    const int i = i0 + u * 256 + tid;
+    cur[u] = i < n ? idrow[i] : u32x4_t{0, 0, 0, 0};
   }
+  for (int i = tid; i < kVoteBins * 32; i += 256) vh[i] = 0u;
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int i = i0 + u * 256 + threadIdx.x;
-    if (i >= n) continue;
-    uint32_t acc = 0u;
+  for (int u = 0; u < 4; ++u) ((uint4*)lut4)[u * 256 + tid] = lv[u];
+  lds_barrier();
+  const int copy = tid & 31;
+  uint8_t* vrow = votes + (int64_t)h * ldv;
+  uint8_t* trow = votes_trace ? votes_trace + (int64_t)h * n : nullptr;
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4)
+  for (int r = 0; r < R; ++r) {
+    u32x4_t nxt[U];
+    if (r + 1 < R) {
 #pragma unroll
-      for (int bb = 0; bb < 4; ++bb) {
-        const int sb = q4 * 4 + bb;
-        acc += lut4[sb * kCent + ((idv[u][q4] >> (8 * bb)) & 0xffu)];
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + ((r + 1) * U + u) * 256 + tid;
+        nxt[u] = i < n ? idrow[i] : u32x4_t{0, 0, 0, 0};
       }
-    uint32_t S = acc & 0xffu;
-    for (int g = 1; g < G; ++g) S = max(S, (acc >> (8 * g)) & 0xffu);
-    votes[(int64_t)h * n + i] = (uint8_t)S;
-    atomicAdd(&vh[S * 32 + copy], 1u);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + (r * U + u) * 256 + tid;
+      if (i >= n) continue;
+      uint32_t acc = 0u;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb)
+          acc += lut4[(q4 * 4 + bb) * kCent + ((cur[u][q4] >> (8 * bb)) & 0xffu)];
+      const uint32_t S = max(max(acc & 0xffu, (acc >> 8) & 0xffu),
+                             max((acc >> 16) & 0xffu, acc >> 24));
+      vrow[i] = (uint8_t)S;
+      if (trow) trow[i] = (uint8_t)S;
+      atomicAdd(&vh[S * 32 + copy], 1u);
+    }
+    if (r + 1 < R) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+    }
   }
-  __syncthreads();
-  for (int v = threadIdx.x; v < kVoteBins; v += 256) {
-    uint32_t sum = 0u;
-    for (int cp = 0; cp < 32; ++cp) sum += vh[v * 32 + cp];
-    chunk_hist[((int64_t)h * n_chunks + chunk) * kVoteBins + v] = (int32_t)sum;
-  }
-}
-
-// -------------------------------------------------------------------- scan --
-// One workgroup per KV head: the vote threshold s* and, per chunk, the
-// output offset of its candidates and how many S == s* entries it takes
-// (lowest entries first).
-__global__ __launch_bounds__(256) void cand_scan_kernel(const int32_t* chunk_hist, int n_chunks,
-                                                        int C, int32_t* chunk_off,
-                                                        int32_t* chunk_take, int32_t* win,
-                                                        int32_t* sstar) {
-  __shared__ int tot[kVoteBins];
-  __shared__ int s_star, s_need;
-  __shared__ int wsum[4];
-  const int h = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int32_t* ch = chunk_hist + (int64_t)h * n_chunks * kVoteBins;
-  for (int v = tid; v < kVoteBins; v += 256) {
+  lds_barrier();
+  if (tid < 128) {
     int s = 0;
-    for (int c = 0; c < n_chunks; ++c) s += ch[(int64_t)c * kVoteBins + v];
-    tot[v] = s;
+    if (tid < kVoteBins) {
+#pragma unroll 8
+      for (int k = 0; k < 32; ++k) s += (int)vh[tid * 32 + ((k + tid) & 31)];
+    }
+    cnt[tid] = s;
   }
-  __syncthreads();
-  if (tid == 0) {
-    int above = 0, star = -1, need = 0;
-    for (int v = kVoteBins - 1; v >= 0; --v) {
-      if (above + tot[v] >= C) {
-        star = v;
-        need = C - above;
-        break;
-      }
-      above += tot[v];
+  lds_barrier();
+  if (tid < 64) {
+    const int c0 = cnt[2 * tid], c1 = cnt[2 * tid + 1];
+    const int incl = wave_incl_scan(c0 + c1);
+    const int ge0 = wave_total(incl) - (incl - c0 - c1), ge1 = ge0 - c0;
+    int32_t* out = chunk_ge + ((int64_t)h * n_chunks + chunk) * kGe;
+    int32_t* tot = tot_ge + (int64_t)h * kGe;
+    if (2 * tid < kGe) {
+      out[2 * tid] = ge0;
+      if (ge0) atomicAdd(&tot[2 * tid], ge0);
     }
-    s_star = star;      // -1: every entry is a candidate (C >= n)
-    s_need = need;
-    sstar[h] = star;
-    if (h == 0) {
-      win[0] = 0;
-      win[1] = C;
+    if (2 * tid + 1 < kGe) {
+      out[2 * tid + 1] = ge1;
+      if (ge1) atomicAdd(&tot[2 * tid + 1], ge1);
     }
-  }
-  __syncthreads();
-  const int star = s_star, need = s_need;
-  // per-chunk counts above s* and equal to s*, exclusive scans over chunks
-  int run_gt = 0, run_eq = 0;
-  for (int c0 = 0; c0 < n_chunks; c0 += 256) {
-    const int c = c0 + tid;
-    int gt = 0, eq = 0;
-    if (c < n_chunks) {
-      for (int v = 0; v < kVoteBins; ++v) {
-        const int x = ch[(int64_t)c * kVoteBins + v];
-        if (star < 0 || v > star) gt += x;
-        else if (v == star) eq += x;
-      }
-    }
-    const int egt = wave_excl_scan(gt, lane), eeq = wave_excl_scan(eq, lane);
-    __syncthreads();
-    if (lane == 63) wsum[wave] = egt + gt;
-    __syncthreads();
-    int bgt = egt;
-    int tgt = 0;
-    for (int w2 = 0; w2 < 4; ++w2) {
-      if (w2 < wave) bgt += wsum[w2];
-      tgt += wsum[w2];
-    }
-    __syncthreads();
-    if (lane == 63) wsum[wave] = eeq + eq;
-    __syncthreads();
-    int beq = eeq;
-    int teq = 0;
-    for (int w2 = 0; w2 < 4; ++w2) {
-      if (w2 < wave) beq += wsum[w2];
-      teq += wsum[w2];
-    }
-    if (c < n_chunks) {
-      const int eq_before = run_eq + beq;
-      const int take = max(0, min(eq, need - eq_before));
-      chunk_off[(int64_t)h * n_chunks + c] = run_gt + bgt + min(eq_before, need);
-      chunk_take[(int64_t)h * n_chunks + c] = star < 0 ? 0 : take;
-    }
-    run_gt += tgt;
-    run_eq += teq;
-    __syncthreads();
   }
 }
 
 // ------------------------------------------------------------------ compact --
-// Ordered compaction of each chunk's candidates: S > s*, or S == s* among the
-// chunk's first `take` such entries.
-__global__ __launch_bounds__(256) void cand_write_kernel(const uint8_t* votes, int n, int n_chunks,
-                                                         int C, const int32_t* sstar,
-                                                         const int32_t* chunk_off,
-                                                         const int32_t* chunk_take,
+// Grid (n_chunks, H), 256 threads.  The vote threshold s* of head h is the
+// largest v with #(S >= v) >= C; the candidates are the entries with S > s*
+// and the first need = C - #(S > s*) entries with S == s*, in entry order.
+// Each workgroup finds s* from the head's totals, counts the candidates of
+// the earlier chunks from their suffix counts and writes its own chunk's:
+// wave w owns entries [2048 w, 2048 w + 2048) of the chunk, read in two
+// rounds of one 16-byte load per lane (lane l: 16 l .. 16 l + 15 of the
+// round's 1024); per-lane packed counts (above s* | at s* << 16) and a wave
+// prefix sum place every lane's candidates.
+__device__ __forceinline__ uint32_t vote_counts(const u32x4_t& vv, int i, int n, int star) {
+  uint32_t c = 0u;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int b = (int)((vv[e >> 2] >> (8 * (e & 3))) & 0xffu);
+    if (i + e < n) c += b > star ? 1u : (b == star ? 0x10000u : 0u);
+  }
+  return c;
+}
+
+__global__ __launch_bounds__(256) void cand_write_kernel(const uint8_t* votes, int ldv, int n,
+                                                         int n_chunks, int C,
+                                                         const int32_t* tot_ge,
+                                                         const int32_t* chunk_ge, int32_t* win,
                                                          int32_t* cand) {
-  __shared__ int wa[4], we[4];
-  const int h = blockIdx.y, chunk = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ int tg[kGe + 1];
   __shared__ int s_star;
-  if (threadIdx.x == 0) s_star = sstar[h];
-  __syncthreads();
+  __shared__ int pa[4], pb[4], wt[4];
+  const int h = blockIdx.y, chunk = blockIdx.x, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  int tgv = 0;
+  if (tid < kGe) tgv = tot_ge[(int64_t)h * kGe + tid];
+  const int i0 = chunk * kChunk + wave * (kChunk / 4);
+  const uint8_t* vr = votes + (int64_t)h * ldv;
+  u32x4_t vv[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int i = i0 + r * 1024 + 16 * lane;
+    vv[r] = i < n ? *(const u32x4_t*)(vr + i) : u32x4_t{0, 0, 0, 0};
+  }
+  if (tid < kGe) tg[tid] = tgv;
+  if (tid == 0) {
+    tg[kGe] = 0;
+    s_star = -1;   // stays -1 only if C exceeds the entry count
+    if (h == 0 && chunk == 0) {
+      win[0] = 0;
+      win[1] = C;
+    }
+  }
+  lds_barrier();
+  if (tid < kGe && tg[tid] >= C && tg[tid + 1] < C) s_star = tid;
+  lds_barrier();
   const int star = s_star;
-  const int off = chunk_off[(int64_t)h * n_chunks + chunk];
-  const int take = chunk_take[(int64_t)h * n_chunks + chunk];
-  constexpr int kSeg = kChunk / 4;   // entries per wave
-  const int i0 = chunk * kChunk + wave * kSeg;
-  const uint8_t* vr = votes + (int64_t)h * n;
-  int sv[kSeg / 64];
-#pragma unroll
-  for (int u = 0; u < kSeg / 64; ++u) {
-    const int i = i0 + u * 64 + lane;
-    sv[u] = i < n ? (int)vr[i] : -1;
+  const int need = star < 0 ? 0 : C - tg[star + 1];
+  // candidates above / at s* in the earlier chunks and at s* in this one
+  const int32_t* cg = chunk_ge + (int64_t)h * n_chunks * kGe;
+  int pg = 0, pe = 0;
+  for (int c2 = tid; c2 < chunk; c2 += 256) {
+    const int gt = cg[(int64_t)c2 * kGe + star + 1];
+    pg += gt;
+    if (star >= 0) pe += cg[(int64_t)c2 * kGe + star] - gt;
   }
-  int ca = 0, ce = 0;
+  const int eq_own = star < 0 ? 0
+                              : cg[(int64_t)chunk * kGe + star] - cg[(int64_t)chunk * kGe + star + 1];
+  const int sg = wave_total(wave_incl_scan(pg)), se = wave_total(wave_incl_scan(pe));
+  // this wave's counts, both rounds
+  uint32_t cnt[2];
+  int incl[2];
 #pragma unroll
-  for (int u = 0; u < kSeg / 64; ++u) {
-    ca += __popcll(__ballot(sv[u] >= 0 && (star < 0 || sv[u] > star)));
-    ce += __popcll(__ballot(star >= 0 && sv[u] == star));
+  for (int r = 0; r < 2; ++r) {
+    cnt[r] = vote_counts(vv[r], i0 + r * 1024 + 16 * lane, n, star);
+    incl[r] = wave_incl_scan((int)cnt[r]);
   }
+  const int r0_tot = wave_total(incl[0]);
   if (lane == 0) {
-    wa[wave] = ca;
-    we[wave] = ce;
+    pa[wave] = sg;
+    pb[wave] = se;
+    wt[wave] = r0_tot + wave_total(incl[1]);
   }
-  __syncthreads();
-  int oa = 0, oe = 0;
-  for (int v = 0; v < wave; ++v) {
-    oa += wa[v];
-    oe += we[v];
+  lds_barrier();
+  int gt_before = 0, eq_before = 0, ow = 0;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    gt_before += pa[v];
+    eq_before += pb[v];
+    if (v < wave) ow += wt[v];
   }
-  const uint64_t lt = lanemask_lt(lane);
+  const int off = gt_before + min(eq_before, need);
+  const int take = max(0, min(eq_own, need - eq_before));
   int32_t* crow = cand + (int64_t)h * C;
 #pragma unroll
-  for (int u = 0; u < kSeg / 64; ++u) {
-    const bool is_gt = sv[u] >= 0 && (star < 0 || sv[u] > star);
-    const bool is_eq = star >= 0 && sv[u] == star;
-    const uint64_t ba = __ballot(is_gt), be = __ballot(is_eq);
-    const int a_before = oa + __popcll(ba & lt);
-    const int e_before = oe + __popcll(be & lt);
-    const bool sel = is_gt || (is_eq && e_before < take);
-    const int dst = off + a_before + min(e_before, take);
-    if (sel && dst < C) crow[dst] = i0 + u * 64 + lane;
-    oa += __popcll(ba);
-    oe += __popcll(be);
+  for (int r = 0; r < 2; ++r) {
+    const int before = ow + (incl[r] - (int)cnt[r]) + (r ? r0_tot : 0);
+    int ab = before & 0xffff, eb = before >> 16;
+    if ((cnt[r] & 0xffffu) || ((cnt[r] >> 16) && eb < take)) {
+      const int i = i0 + r * 1024 + 16 * lane;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int b = i + e < n ? (int)((vv[r][e >> 2] >> (8 * (e & 3))) & 0xffu) : -1;
+        if (b < 0) {
+        } else if (b > star) {
+          const int d = off + ab + min(eb, take);
+          if (d < C) crow[d] = i + e;
+          ++ab;
+        } else if (b == star) {
+          if (eb < take && off + ab + eb < C) crow[off + ab + eb] = i + e;
+          ++eb;
+        }
+      }
+    }
   }
 }
 
 // ------------------------------------------------------------------ rerank --
-// est_i = max_g fl(|q_g| * tree16_b fl(w_ib * tree8_j fl(v_ibj * q~_gbj)));
-// a 16-lane group per candidate, lane b = subspace b.
+// est_i = max_g fl(|q_g| * tree16_b fl(w_ib * tree8_j fl(v_ibj * q~_gbj))).
+// Grid (ceil(C / 256), H), 256 threads: a 16-lane group takes 16 consecutive
+// candidates, lane b holding subspace b of each.  A nibble's signed level
+// comes from a 16-entry LDS table (one lookup instead of a compare/select
+// chain).  The tree16 over the subspaces is a butterfly in which every level
+// halves the candidates a lane carries (lanes b, b ^ m add the same operands
+// as the tree's level m), so a group's 16 sums take 15 lane exchanges per
+// query head and lane u ends with candidate u's.  Each estimate's key also
+// goes into the head's 4096-bin top-12-bit histogram for the exact top-k
+// that follows.
+template <int G>
 __global__ __launch_bounds__(256) void rerank_kernel(const uint8_t* codes, const float* w, int cap,
-                                                     int n, const int32_t* cand, int C, int G,
+                                                     int n, const int32_t* cand, int C,
                                                      const float* qt, const float* qn,
-                                                     CodebookArgs cb, float* est) {
-  const int h = blockIdx.y;
-  const int j = threadIdx.x & 15, grp = threadIdx.x >> 4;
-  float qv[4][8], qs[4];
+                                                     CodebookArgs cb, float* est,
+                                                     int32_t* tot_ge) {
+  __shared__ float vtab[16];
+  const int h = blockIdx.y, tid = threadIdx.x, j = tid & 15;
+  const int base = (tid & 63) & ~15;   // first lane of the group
+  if (blockIdx.x == 0 && tid < kGe) tot_ge[(int64_t)h * kGe + tid] = 0;   // zero for the next call
+  if (tid < 16) {
+    float lv = cb.levels[0];
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int hq = h * G + min(g, G - 1);
+    for (int i = 1; i < 8; ++i)
+      if ((tid & 7) == i) lv = cb.levels[i];
+    vtab[tid] = (tid & 8) ? -lv : lv;
+  }
+  const int ci = blockIdx.x * 256 + tid;   // lane j's own candidate (u = j)
+  const int mine = min(max(cand[(int64_t)h * C + min(ci, C - 1)], 0), n - 1);
+  float qv[G][8], qs[G];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) qv[g][e] = qt[(int64_t)hq * kD + 8 * j + e];
+  for (int g = 0; g < G; ++g) {
+    const int hq = h * G + g;
+    const float4 a = *(const float4*)(qt + (int64_t)hq * kD + 8 * j);
+    const float4 b = *(const float4*)(qt + (int64_t)hq * kD + 8 * j + 4);
+    qv[g][0] = a.x; qv[g][1] = a.y; qv[g][2] = a.z; qv[g][3] = a.w;
+    qv[g][4] = b.x; qv[g][5] = b.y; qv[g][6] = b.z; qv[g][7] = b.w;
     qs[g] = qn[hq];
   }
-  const int per_wg = 64;
-  const int c0 = blockIdx.x * per_wg;
-  for (int ci = c0 + grp; ci < min(C, c0 + per_wg); ci += 16) {
-    const int64_t ent = (int64_t)h * cap + min(max(cand[(int64_t)h * C + ci], 0), n - 1);
-    const uint32_t code = ((const uint32_t*)codes)[ent * kSub + j];
-    const float wb = w[ent * kSub + j];
+  uint32_t code[16];
+  float wb[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int64_t ent = (int64_t)h * cap + __shfl(mine, base + u, 64);
+    code[u] = ((const uint32_t*)codes)[ent * kSub + j];
+    wb[u] = w[ent * kSub + j];
+  }
+  lds_barrier();   // vtab
+  float x[G][16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
     float v[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t nib = (code >> (4 * e)) & 0xfu;
-      const uint32_t mag = nib & 7u;
-      float lv = cb.levels[0];
+    for (int e = 0; e < 8; ++e) v[e] = vtab[(code[u] >> (4 * e)) & 0xfu];
 #pragma unroll
-      for (int i = 1; i < 8; ++i)
-        if (mag == (uint32_t)i) lv = cb.levels[i];
-      v[e] = (nib & 8u) ? -lv : lv;
-    }
-    float best = -INFINITY;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      if (g >= G) break;
+    for (int g = 0; g < G; ++g) {
       float pr[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) pr[e] = v[e] * qv[g][e];
-      float x = wb * tree8(pr);
-#pragma unroll
-      for (int m = 8; m >= 1; m >>= 1) x = x + xor16(x, m);
-      const float e_g = qs[g] * x;
-      best = g == 0 ? e_g : fmaxf(best, e_g);
+      x[g][u] = wb[u] * tree8(pr);
     }
-    if (j == 0) est[(int64_t)h * C + ci] = best;
   }
+  float best = 0.f;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+#pragma unroll
+    for (int m = 8, nn = 16; m >= 1; m >>= 1, nn >>= 1) {
+      const bool up = (j & m) != 0;
+#pragma unroll
+      for (int i = 0; i < nn / 2; ++i) {
+        const float keep = up ? x[g][nn / 2 + i] : x[g][i];
+        const float give = up ? x[g][i] : x[g][nn / 2 + i];
+        x[g][i] = keep + xor16(give, m);
+      }
+    }
+    const float e_g = qs[g] * x[g][0];
+    best = g == 0 ? e_g : fmaxf(best, e_g);
+  }
+  if (ci < C) est[(int64_t)h * C + ci] = best;
+}
+
+template <int G>
+void launch_rerank(const skv_index* ix, int n, const int32_t* cand, int C, const float* qt,
+                   const float* qn, const CodebookArgs& ca, float* est, int32_t* tot_ge,
+                   hipStream_t st) {
+  rerank_kernel<G><<<dim3((C + 255) / 256, ix->H), 256, 0, st>>>(
+      ix->codes, ix->w, ix->cap, n, cand, C, qt, qn, ca, est, tot_ge);
 }
 
 // An empty index retrieves nothing.
@@ -526,42 +599,21 @@ __global__ void empty_kernel(int k_final, int32_t* idx, int32_t* n_cand) {
   if (threadIdx.x == 0) n_cand[h] = 0;
 }
 
-// --------------------------------------------------------------------- map --
-__global__ void map_kernel(const int32_t* tk_idx, const int32_t* tk_cnt, const int32_t* cand,
-                           int C, const int32_t* pos, int k_final, int32_t* idx,
-                           int32_t* n_cand) {
-  const int h = blockIdx.x;
-  const int cnt = tk_cnt[h];
-  for (int i = threadIdx.x; i < k_final; i += blockDim.x) {
-    int v = -1;
-    if (i < cnt) {
-      const int p = tk_idx[(int64_t)h * k_final + i];
-      v = pos[cand[(int64_t)h * C + p]];
-    }
-    idx[(int64_t)h * k_final + i] = v;
-  }
-  if (threadIdx.x == 0) n_cand[h] = cnt;
-}
-
-// workspace of a retrieval; the top-k part comes first (zero-filled region)
+// workspace of a retrieval; the first region (the vote totals) is zero when
+// a call starts and is left zero
 struct RetrieveWs {
-  void* topk;
-  uint8_t* lut;       // [Hq][16][256]
+  int32_t* tot_ge;    // [H][98]: #(S >= v) over all entries
+  uint32_t* lut;      // [H][16][256] packed tier weights of the G query heads
   float* qt;          // [Hq][128]
   float* qn;          // [Hq]
-  uint8_t* votes;     // [H][n]
-  int32_t* chunk_hist;  // [H][n_chunks][97]
-  int32_t* chunk_off;   // [H][n_chunks]
-  int32_t* chunk_take;  // [H][n_chunks]
+  uint8_t* votes;     // [H][ldv], ldv = n rounded up to 16
+  int32_t* chunk_ge;  // [H][n_chunks][98]: #(S >= v) per chunk
   int32_t* win;       // [2]: top-k window over the candidates
-  int32_t* sstar;     // [H]: vote threshold
   int32_t* cand;      // [H][C]
   float* est;         // [H][C]
-  int32_t* tk_idx;    // [H][k_final]
-  int32_t* tk_cnt;    // [H]
 
   static size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
-  static size_t layout(RetrieveWs* w, char* base, int H, int G, int n, int C, int k_final) {
+  static size_t layout(RetrieveWs* w, char* base, int H, int G, int n, int C) {
     const int n_chunks = (n + kChunk - 1) / kChunk;
     const int Hq = H * G;
     size_t o = 0;
@@ -570,35 +622,25 @@ struct RetrieveWs {
       o += al(bytes);
       return p;
     };
-    void* tk = take(topk_workspace_bytes(H, std::max(C, 1)));
-    uint8_t* lut = (uint8_t*)take((size_t)Hq * kSub * kCent);
+    int32_t* tot = (int32_t*)take((size_t)H * kGe * 4);
+    uint32_t* lut = (uint32_t*)take((size_t)H * kSub * kCent * 4);
     float* qt = (float*)take((size_t)Hq * kD * 4);
     float* qn = (float*)take((size_t)Hq * 4);
-    uint8_t* votes = (uint8_t*)take((size_t)H * n);
-    int32_t* chh = (int32_t*)take((size_t)H * n_chunks * kVoteBins * 4);
-    int32_t* cho = (int32_t*)take((size_t)H * n_chunks * 4);
-    int32_t* cht = (int32_t*)take((size_t)H * n_chunks * 4);
+    uint8_t* votes = (uint8_t*)take((size_t)H * ((n + 15) & ~15));
+    int32_t* cge = (int32_t*)take((size_t)H * n_chunks * kGe * 4);
     int32_t* win = (int32_t*)take(8);
-    int32_t* sst = (int32_t*)take((size_t)H * 4);
     int32_t* cand = (int32_t*)take((size_t)H * C * 4);
     float* est = (float*)take((size_t)H * C * 4);
-    int32_t* tki = (int32_t*)take((size_t)H * k_final * 4);
-    int32_t* tkc = (int32_t*)take((size_t)H * 4);
     if (w) {
-      w->topk = tk;
+      w->tot_ge = tot;
       w->lut = lut;
       w->qt = qt;
       w->qn = qn;
       w->votes = votes;
-      w->chunk_hist = chh;
-      w->chunk_off = cho;
-      w->chunk_take = cht;
+      w->chunk_ge = cge;
       w->win = win;
-      w->sstar = sst;
       w->cand = cand;
       w->est = est;
-      w->tk_idx = tki;
-      w->tk_cnt = tkc;
     }
     return o;
   }
@@ -675,7 +717,7 @@ size_t sparsekv_retrieve_workspace_size(const skv_index* index, int32_t G, doubl
                                         int32_t k_final) {
   if (!index || index->H < 1 || index->n < 0 || G < 1 || k_final < 1 || !(beta > 0)) return 0;
   const int C = n_candidates(index->n, beta);
-  return RetrieveWs::layout(nullptr, nullptr, index->H, G, index->n, std::max(C, 1), k_final);
+  return RetrieveWs::layout(nullptr, nullptr, index->H, G, index->n, std::max(C, 1));
 }
 
 skv_status sparsekv_retrieve(const skv_codebook* cb, const skv_index* index, const void* q,
@@ -696,11 +738,11 @@ skv_status sparsekv_retrieve(const skv_codebook* cb, const skv_index* index, con
   if (!ws || ws_bytes < need) return SKV_EWORKSPACE;
   if (!topk_supported(C)) return SKV_EUNSUPPORTED;
   RetrieveWs w;
-  RetrieveWs::layout(&w, (char*)ws, H, G, n, C, k_final);
-  uint8_t* votes = (trace && trace->votes) ? trace->votes : w.votes;
+  RetrieveWs::layout(&w, (char*)ws, H, G, n, C);
+  const int ldv = (n + 15) & ~15;
   int32_t* cand = (trace && trace->cand) ? trace->cand : w.cand;
   float* est = (trace && trace->est) ? trace->est : w.est;
-  const int n_chunks = std::max(1, (n + kChunk - 1) / kChunk);
+  const int n_chunks = (n + kChunk - 1) / kChunk;
 
   TierArgs ta;
   ta.t_rho = (int)ceil(rho * (double)n);
@@ -708,20 +750,23 @@ skv_status sparsekv_retrieve(const skv_codebook* cb, const skv_index* index, con
   for (int i = 0; i < 6; ++i) ta.T[i] = (int)ceil(fr[i] * (double)ta.t_rho);
   const CodebookArgs ca = cb_args(cb);
 
-  query_lut_kernel<<<H * G, 256, 0, stream>>>((const uint16_t*)q, G, cb->signs, ca.c, index->hist,
-                                              ta, w.qt, w.qn, w.lut);
-  vote_kernel<<<dim3(n_chunks, H), 256, 0, stream>>>(index->ids, index->cap, n, G, w.lut, votes,
-                                                     w.chunk_hist, n_chunks);
-  cand_scan_kernel<<<H, 256, 0, stream>>>(w.chunk_hist, n_chunks, C, w.chunk_off, w.chunk_take,
-                                          w.win, w.sstar);
-  cand_write_kernel<<<dim3(n_chunks, H), 256, 0, stream>>>(votes, n, n_chunks, C, w.sstar,
-                                                           w.chunk_off, w.chunk_take, cand);
-  rerank_kernel<<<dim3((C + 63) / 64, H), 256, 0, stream>>>(index->codes, index->w, index->cap,
-                                                            n, cand, C, G, w.qt, w.qn, ca, est);
-  hipError_t e = launch_topk(est, H, H, C, w.win, w.win + 1, k_final, w.tk_idx, w.tk_cnt, w.topk,
-                             false, stream);
+  query_lut_kernel<<<dim3(kSub, H, 4), 256, 0, stream>>>((const uint16_t*)q, G, cb->signs, ca.c,
+                                                         index->hist, ta, w.qt, w.qn,
+                                                         (uint8_t*)w.lut);
+  vote_kernel<<<dim3(n_chunks, H), 256, 0, stream>>>(index->ids, index->cap, n, w.lut, w.votes,
+                                                     ldv, trace ? trace->votes : nullptr,
+                                                     w.chunk_ge, n_chunks, w.tot_ge);
+  cand_write_kernel<<<dim3(n_chunks, H), 256, 0, stream>>>(w.votes, ldv, n, n_chunks, C, w.tot_ge,
+                                                           w.chunk_ge, w.win, cand);
+  switch (G) {
+    case 1: launch_rerank<1>(index, n, cand, C, w.qt, w.qn, ca, est, w.tot_ge, stream); break;
+    case 2: launch_rerank<2>(index, n, cand, C, w.qt, w.qn, ca, est, w.tot_ge, stream); break;
+    case 3: launch_rerank<3>(index, n, cand, C, w.qt, w.qn, ca, est, w.tot_ge, stream); break;
+    default: launch_rerank<4>(index, n, cand, C, w.qt, w.qn, ca, est, w.tot_ge, stream); break;
+  }
+  hipError_t e = launch_topk(est, H, H, C, w.win, w.win + 1, k_final, idx, n_cand, nullptr, false,
+                             stream, cand, index->pos, C);
   if (e != hipSuccess) return SKV_ELAUNCH;
-  map_kernel<<<H, 128, 0, stream>>>(w.tk_idx, w.tk_cnt, cand, C, index->pos, k_final, idx, n_cand);
   return hipGetLastError() == hipSuccess ? SKV_OK : SKV_ELAUNCH;
 }
 

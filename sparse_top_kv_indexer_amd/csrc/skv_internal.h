@@ -26,12 +26,14 @@ hipError_t launch_score(const KvArgs& kv, const void* q, int G, float* scores, c
                         const int32_t* hi, uint32_t* hist, hipStream_t s);
 
 // topk.hip (workspace layout in skv_topk.h); hist_ready: the row histograms
-// were already accumulated by the score scan
+// were already accumulated by the producer of the scores.  With map_a set,
+// a selected position p of row r is written as map_b[map_a[r * map_ld + p]].
 size_t topk_workspace_bytes(int rows, int L_max);
 bool topk_supported(int L_max);
 hipError_t launch_topk(const float* scores, int rows, int H, int L_max, const int32_t* lo,
                        const int32_t* hi, int k, int32_t* idx, int32_t* count, void* ws,
-                       bool hist_ready, hipStream_t s);
+                       bool hist_ready, hipStream_t s, const int32_t* map_a = nullptr,
+                       const int32_t* map_b = nullptr, int map_ld = 0);
 
 // attend.hip
 int attend_num_splits(int k);

@@ -40,7 +40,9 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* scor
                                                                int L_max, const int32_t* lo_p,
                                                                const int32_t* hi_p, int k,
                                                                uint32_t* ghist, int32_t* idx,
-                                                               int32_t* count) {
+                                                               int32_t* count,
+                                                               const int32_t* map_a,
+                                                               const int32_t* map_b, int map_ld) {
   __shared__ RowSelLds L;
   const int row = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = row_wave();
@@ -105,6 +107,10 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* scor
 
   // 3. ordered write
   int32_t* orow = idx + (int64_t)row * k;
+  // mapped positions: the selected positions are collected in LDS (the
+  // histogram is no longer needed) and mapped in one pass at the end, so the
+  // two dependent loads per key are not serialised inside the emit loop
+  const bool map_lds = map_a && k <= kBins;
   int a_base = 0, e_base = 0;   // keys above / equal to T in earlier sweeps
   auto emit_sweep = [&](const uint32_t (&kk)[kGroups][4], int sw) {
     int cg[kGroups];
@@ -113,7 +119,12 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* scor
     row_wave_offsets(L, lt, &oa, &oe, &ta, &te);
     const int pos0 = w.lo + sw * kSweep + wave * kSeg + 4 * lane;
     row_emit(kk, cg, T, need_eq, a_base + oa, e_base + oe, [&](int dst, int g, int e) {
-      if (dst < k) orow[dst] = pos0 + 256 * g + e;
+      if (dst < k) {
+        const int p = pos0 + 256 * g + e;
+        if (!map_a) orow[dst] = p;
+        else if (map_lds) L.hist[dst] = (uint32_t)p;
+        else orow[dst] = map_b[map_a[(int64_t)row * map_ld + p]];
+      }
     });
     a_base += ta;
     e_base += te;
@@ -130,6 +141,11 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* scor
     }
   }
   const int n_sel = min(k, a_base + min(e_base, need_eq));
+  if (map_lds) {
+    lds_barrier();
+    for (int i = threadIdx.x; i < n_sel; i += kRowThreads)
+      orow[i] = map_b[map_a[(int64_t)row * map_ld + (int)L.hist[i]]];
+  }
   for (int i = n_sel + threadIdx.x; i < k; i += kRowThreads) orow[i] = -1;
   if (threadIdx.x == 0) count[row] = n_sel;
   if (gh4) gh4[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);   // zero for the next call
@@ -146,13 +162,16 @@ bool topk_supported(int L_max) { return L_max >= 1; }
 
 hipError_t launch_topk(const float* scores, int rows, int H, int L_max, const int32_t* lo,
                        const int32_t* hi, int k, int32_t* idx, int32_t* count, void* wsp,
-                       bool hist_ready, hipStream_t s) {
+                       bool hist_ready, hipStream_t s, const int32_t* map_a,
+                       const int32_t* map_b, int map_ld) {
   if (rows <= 0) return hipSuccess;
   uint32_t* gh = hist_ready ? TopkWs::carve(wsp).hist : nullptr;
   if (L_max <= kSweep)
-    topk_row_kernel<true><<<rows, kRowThreads, 0, s>>>(scores, H, L_max, lo, hi, k, gh, idx, count);
+    topk_row_kernel<true><<<rows, kRowThreads, 0, s>>>(scores, H, L_max, lo, hi, k, gh, idx, count,
+                                                          map_a, map_b, map_ld);
   else
-    topk_row_kernel<false><<<rows, kRowThreads, 0, s>>>(scores, H, L_max, lo, hi, k, gh, idx, count);
+    topk_row_kernel<false><<<rows, kRowThreads, 0, s>>>(scores, H, L_max, lo, hi, k, gh, idx, count,
+                                                          map_a, map_b, map_ld);
   return hipGetLastError();
 }
 

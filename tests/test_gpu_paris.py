@@ -1,6 +1,8 @@
 """GPU parity of ParisKV compressed-code retrieval (encode bit-exact; votes,
 candidates, rerank estimates and the final top-k identical) against the fp32
 oracle, plus attention over the retrieved set."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -69,8 +71,21 @@ def test_encode_appends_in_pieces():
         S.sparsekv_encode(cb, kv, 0, 4, 10, index)          # index is full
 
 
+def _check_retrieval(p, ref, idx, n_cand, tr):
+    votes, cand, est = (tr["votes"].cpu().numpy(), tr["cand"].cpu().numpy(),
+                        tr["est"].cpu().numpy())
+    idx, n_cand = idx.cpu().numpy(), n_cand.cpu().numpy()
+    for h in range(p.H):
+        assert np.array_equal(votes[h], ref["S"][h]), h
+        assert np.array_equal(cand[h], ref["cand"][h]), h
+        assert np.array_equal(est[h].view(np.uint32), ref["est"][h].view(np.uint32)), h
+        assert n_cand[h] == len(ref["idx"][h])
+        assert idx[h][: n_cand[h]].tolist() == sorted(ref["idx"][h].tolist()), h
+        assert np.all(idx[h][n_cand[h]:] == -1)
+
+
 @pytest.mark.parametrize("L,tag,beta,k_final", [(6000, 21, 0.05, 100), (20000, 22, 0.02, 100),
-                                                (3000, 23, 1.0, 64)])
+                                                (3000, 23, 1.0, 64), (9000, 29, 1.0, 5000)])
 def test_retrieve_identical(L, tag, beta, k_final):
     p = W.make_paris(tag=tag, H=2, G=4, L=L, sink=4, local=64, beta=beta, rho=beta,
                      k_final=k_final)
@@ -95,6 +110,45 @@ def test_retrieve_identical(L, tag, beta, k_final):
         assert got.tolist() == sorted(ref["idx"][h].tolist()), h
         assert np.all(idx[h][n_cand[h]:] == -1)
         say("  h", h, "recall@100", P.recall_at(got, true[h]))
+
+
+@pytest.mark.parametrize("G,L,tag,beta,rho", [(1, 17000, 24, 0.03, 0.1), (3, 26000, 25, 0.02, 0.02),
+                                              (2, 9000, 26, 0.2, 0.5)])
+def test_retrieve_group_sizes_and_chunk_tails(G, L, tag, beta, rho):
+    """G < 4 leaves bytes of the packed tier table unused; n spans several
+    8192-entry vote chunks with a ragged last one."""
+    p = W.make_paris(tag=tag, H=3, G=G, L=L, sink=4, local=64, beta=beta, rho=rho, k_final=100)
+    say("retrieve", p.name, "G", G, "n", p.n, "beta", beta, "rho", rho)
+    cb, lv, th = _codebook(p)
+    _, index = _gpu_index(p, cb)
+    q = S.to_device(p.q, DEV, bf16=True)
+    idx, n_cand, tr = S.sparsekv_retrieve(cb, index, q, p.G, p.rho, p.beta, p.k_final, trace=True)
+    torch.cuda.synchronize()
+    ref = P.retrieve(p, P.build_index(p, lv, th), lv)
+    _check_retrieval(p, ref, idx, n_cand, tr)
+
+
+def test_retrieve_repeated_on_one_workspace():
+    """Calls that share a workspace: the vote totals are left zero by every
+    call, so a second call (another query, a smaller beta) on the same
+    workspace gives its own exact result."""
+    p = W.make_paris(tag=27, H=2, G=4, L=20000, sink=4, local=64, beta=0.05, rho=0.05)
+    cb, lv, th = _codebook(p)
+    _, index = _gpu_index(p, cb)
+    ref_index = P.build_index(p, lv, th)
+    ws = S.workspace(S.retrieve_workspace_size(index, p.G, 0.05, p.k_final), DEV)
+    for call, (tag_q, beta) in enumerate([(27, 0.05), (28, 0.02), (27, 0.05)]):
+        pq = W.make_paris(tag=tag_q, H=2, G=4, L=20000, sink=4, local=64, beta=beta, rho=beta)
+        pc = dataclasses.replace(p, q=pq.q, beta=beta, rho=beta)
+        say("call", call, "query tag", tag_q, "beta", beta)
+        q = S.to_device(pc.q, DEV, bf16=True)
+        idx, n_cand, tr = S.sparsekv_retrieve(cb, index, q, pc.G, pc.rho, pc.beta, pc.k_final,
+                                              trace=True, ws=ws)
+        torch.cuda.synchronize()
+        _check_retrieval(pc, P.retrieve(pc, ref_index, lv), idx, n_cand, tr)
+    # the region kept zero between calls: the vote totals [H][98] i32
+    zero_bytes = p.H * 98 * 4
+    assert not ws.view(torch.uint8)[:zero_bytes].cpu().numpy().any()
 
 
 def test_attention_over_retrieved_set():

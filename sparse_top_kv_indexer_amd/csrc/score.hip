@@ -177,7 +177,12 @@ __global__ __launch_bounds__(kThreads) void score_valu_kernel(KvArgs kv, const v
 // load the query row instead (always valid memory) and their score is -inf.
 constexpr int kStageEntries = 4096;
 
-template <int NC, int D, int GMAX, bool HIST>
+//
+// VALU (G = 1): one query row is no contraction, so the same pipeline feeds
+// the vector ALUs instead: lane (n, g4) holds the query elements of its d/32
+// 16-byte pieces in registers, forms a partial dot of key n, and two lane
+// exchanges (lanes n, n + 16, n + 32, n + 48) complete it.
+template <int NC, int D, int GMAX, bool HIST, bool VALU>
 __global__ __launch_bounds__(kThreads) void score_stream_kernel(KvArgs kv, const uint16_t* q, int G,
                                                                  float* scores, HistArgs ha,
                                                                  int cpr) {
@@ -221,12 +226,21 @@ __global__ __launch_bounds__(kThreads) void score_stream_kernel(KvArgs kv, const
 
     // A operand: row n = query head n of the group (zero rows for n >= G)
     const char* qrow = (const char*)(q + ((int64_t)r * G + (n < G ? n : 0)) * d_k);
-    bf16x8_t A[NC];
+    bf16x8_t A[VALU ? 1 : NC];
+    float qf[VALU ? NC : 1][8];
 #pragma unroll
     for (int j = 0; j < NC; ++j) {
       u32x4_t w = ld16(qrow + j * 64 + loff);
-      if (n >= G) w = u32x4_t{0, 0, 0, 0};
-      A[j] = __builtin_bit_cast(bf16x8_t, w);
+      if constexpr (VALU) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          qf[j][2 * e] = bf16_lo(w[e]);
+          qf[j][2 * e + 1] = bf16_hi(w[e]);
+        }
+      } else {
+        if (n >= G) w = u32x4_t{0, 0, 0, 0};
+        A[j] = __builtin_bit_cast(bf16x8_t, w);
+      }
     }
     const int live = min(kv.seq_len[b], kv.L_max);   // tokens t < live are addressable
     const int i_lo = (n_seg * wave) / 4;              // this wave's chunks, relative to c_lo
@@ -256,16 +270,33 @@ __global__ __launch_bounds__(kThreads) void score_stream_kernel(KvArgs kv, const
     };
     auto mfma = [&](int s) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (VALU) {
 #pragma unroll
-      for (int j = 0; j < NC; ++j)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[j], __builtin_bit_cast(bf16x8_t, Bm[s][j]),
-                                                      acc, 0, 0, 0);
+        for (int j = 0; j < NC; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[e] = fmaf(qf[j][2 * e], bf16_lo(Bm[s][j][e]), acc[e]);
+            acc[e] = fmaf(qf[j][2 * e + 1], bf16_hi(Bm[s][j][e]), acc[e]);
+          }
+        float d = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+        d += __shfl_xor(d, 16, 64);
+        d += __shfl_xor(d, 32, 64);
+        acc[0] = d;
+      } else {
+#pragma unroll
+        for (int j = 0; j < NC; ++j)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[j], __builtin_bit_cast(bf16x8_t, Bm[s][j]),
+                                                        acc, 0, 0, 0);
+      }
       return acc;
     };
     // lane (n, g4) holds C[4 g4 + k][n]: query head 4 g4 + k against key n
+    // (VALU: every lane of key n holds its score in element 0)
     auto finish = [&](f32x4_t acc, int i) {
       float sc;
-      if constexpr (GMAX <= 4) {
+      if constexpr (VALU) {
+        sc = acc[0];
+      } else if constexpr (GMAX <= 4) {
         sc = acc[0];
         if (G > 1) sc = fmaxf(sc, acc[1]);
         if (G > 2) sc = fmaxf(sc, acc[2]);
@@ -367,11 +398,11 @@ int resident_wgs(K kernel, int* cache, int n_cache) {
   return cache[dev];
 }
 
-template <int NC, int D, int GMAX, bool HIST>
+template <int NC, int D, int GMAX, bool HIST, bool VALU = false>
 hipError_t launch_stream_k(const KvArgs& kv, const void* q, int G, float* scores,
                            const HistArgs& ha, hipStream_t s) {
   static int cache[64] = {0};
-  auto kern = score_stream_kernel<NC, D, GMAX, HIST>;
+  auto kern = score_stream_kernel<NC, D, GMAX, HIST, VALU>;
   const int cpr = (kv.L_max + 15) / 16;
   const int64_t n_work = (int64_t)kv.B * kv.H * cpr;
   // at least 16 chunks per workgroup and at most one workgroup per resident
@@ -387,6 +418,11 @@ hipError_t launch_stream_k(const KvArgs& kv, const void* q, int G, float* scores
 template <int NC, int D>
 hipError_t launch_stream(const KvArgs& kv, const void* q, int G, float* scores, const HistArgs& ha,
                          hipStream_t s) {
+  if constexpr (NC <= 8) {
+    if (G == 1)
+      return ha.hist ? launch_stream_k<NC, D, 1, true, true>(kv, q, G, scores, ha, s)
+                     : launch_stream_k<NC, D, 1, false, true>(kv, q, G, scores, ha, s);
+  }
   if (G <= 4)
     return ha.hist ? launch_stream_k<NC, D, 4, true>(kv, q, G, scores, ha, s)
                    : launch_stream_k<NC, D, 4, false>(kv, q, G, scores, ha, s);
@@ -400,13 +436,13 @@ hipError_t launch_score(const KvArgs& kv, const void* q, int G, float* scores, c
                         const int32_t* hi, uint32_t* hist, hipStream_t s) {
   dim3 grid((kv.L_max + kTile - 1) / kTile, kv.H, kv.B);
   HistArgs ha{lo, hi, hist};
-  if (kv.bf16 && G >= 2 && G <= 16 && kv.d_k % 32 == 0) {
+  if (kv.bf16 && G >= 1 && G <= 16 && kv.d_k % 32 == 0 && (G >= 2 || kv.d_k <= 256)) {
     switch (kv.d_k / 32) {
       case 2: return launch_stream<2, 4>(kv, q, G, scores, ha, s);
       case 4: return launch_stream<4, 4>(kv, q, G, scores, ha, s);
       case 8: return launch_stream<8, 2>(kv, q, G, scores, ha, s);
       case 18: return launch_stream<18, 1>(kv, q, G, scores, ha, s);
-      default: return hipErrorInvalidValue;
+      default: break;
     }
   }
   const int E = kv.bf16 ? 8 : 4;

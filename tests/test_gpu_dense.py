@@ -120,7 +120,7 @@ def test_contiguous_bf16_and_fp32_g4():
     assert _end_to_end(st32) == 0
 
 
-@pytest.mark.parametrize("G", [2, 4, 8, 16])
+@pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
 def test_scan_slices_cross_rows_and_ragged_lengths(G):
     """Row lengths that are not a multiple of the per-workgroup slice, so
     workgroup slices of the persistent scan straddle rows; ragged seq_len
@@ -163,6 +163,22 @@ def test_scan_token_table_gqa_and_unmapped_blocks():
     st.kv.block_table[0, [3, 4, 50, 127]] = -1
     st.kv.block_table[1, [0, 20]] = -1
     assert _end_to_end(st) == 0
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_scan_single_query_head_dims_and_tables(d):
+    """G = 1 (vector-ALU dot in the persistent scan) for d = 64, 128, 256,
+    through the block table and through a token table with holes."""
+    st = W.make_gqa_paged(tag=170 + d // 64, B=2, H=3, G=1, d=d, L=1040, k=90, sink=4, local=16,
+                          seq_len=[1040, 517])
+    assert _end_to_end(st, attend=d == 128) == 0
+    bt = st.kv.block_table
+    t = np.arange(st.kv.L_max)
+    tt = (bt[:, t // 16] * 16 + t % 16).astype(np.int32)
+    tt[np.random.default_rng(d).random(tt.shape) < 0.4] = -1
+    tt[:, :4] = bt[:, :1] * 16 + np.arange(4)
+    st.kv.token_table, st.kv.block_table = tt, None
+    assert _end_to_end(st, attend=d == 128) == 0
 
 
 @pytest.mark.parametrize("d,attend", [(64, False), (256, True)])

@@ -122,8 +122,10 @@ skv_status sparsekv_score(const skv_kv* kv, const void* q, int32_t G, float* sco
  *   idx   [B][H][k] int32, entries past count[b][h] are -1
  *   count [B][H]    int32 = min(k, number of finite candidates)
  * ws: sparsekv_workspace_size(SKV_OP_TOPK, kv, 0, k, NULL) bytes, where only
- * kv->B, kv->H and kv->L_max are read.  Any L_max (rows of more than 32768
- * scores are re-read from memory once per radix pass). */
+ * kv->B, kv->H and kv->L_max are read.  Any L_max (a row of more than 32768
+ * scores is read twice more: once to list the keys of the threshold's top
+ * 12-bit bin, once to write the selection; a bin of more than 16384 keys is
+ * resolved by re-reading the row per radix digit). */
 skv_status sparsekv_topk(const float* scores, int32_t B, int32_t H, int32_t L_max,
                          skv_window win, int32_t k, int32_t* idx, int32_t* count, void* ws,
                          size_t ws_bytes, hipStream_t stream);
@@ -177,7 +179,8 @@ skv_status sparsekv_gather_attend(const skv_kv* kv, const void* q, int32_t G, co
  * close-reading, section 一, Eqs. (1)-(3); ECHO-OSDI26 wiki page,
  * observation 5; vToken reading notes, section 3.4 Eq. (2)).
  * Supports bf16 keys and values with d_k == d_v == 128, 1 <= G <= 8 and
- * L_max <= 32768 (SKV_EUNSUPPORTED otherwise: use the separate calls).
+ * L_max <= 32768, or L_max <= 32765 when L_max is not a multiple of 4
+ * (SKV_EUNSUPPORTED otherwise: use the separate calls).
  * ws: sparsekv_workspace_size(SKV_OP_SELECT_ATTEND, kv, G, k, NULL) bytes,
  * zero-filled before its first use; every call leaves its first region (the
  * key histograms) zero again. */

@@ -599,9 +599,10 @@ __global__ void empty_kernel(int k_final, int32_t* idx, int32_t* n_cand) {
   if (threadIdx.x == 0) n_cand[h] = 0;
 }
 
-// workspace of a retrieval; the first region (the vote totals) is zero when
-// a call starts and is left zero
+// workspace of a retrieval; the zero-kept part of the top-k workspace and
+// the vote totals are zero when a call starts and are left zero
 struct RetrieveWs {
+  void* topk;         // top-k workspace (its first region is kept zero)
   int32_t* tot_ge;    // [H][98]: #(S >= v) over all entries
   uint32_t* lut;      // [H][16][256] packed tier weights of the G query heads
   float* qt;          // [Hq][128]
@@ -622,6 +623,7 @@ struct RetrieveWs {
       o += al(bytes);
       return p;
     };
+    void* tk = take(topk_workspace_bytes(H, std::max(C, 1)));
     int32_t* tot = (int32_t*)take((size_t)H * kGe * 4);
     uint32_t* lut = (uint32_t*)take((size_t)H * kSub * kCent * 4);
     float* qt = (float*)take((size_t)Hq * kD * 4);
@@ -632,6 +634,7 @@ struct RetrieveWs {
     int32_t* cand = (int32_t*)take((size_t)H * C * 4);
     float* est = (float*)take((size_t)H * C * 4);
     if (w) {
+      w->topk = tk;
       w->tot_ge = tot;
       w->lut = lut;
       w->qt = qt;
@@ -764,7 +767,7 @@ skv_status sparsekv_retrieve(const skv_codebook* cb, const skv_index* index, con
     case 3: launch_rerank<3>(index, n, cand, C, w.qt, w.qn, ca, est, w.tot_ge, stream); break;
     default: launch_rerank<4>(index, n, cand, C, w.qt, w.qn, ca, est, w.tot_ge, stream); break;
   }
-  hipError_t e = launch_topk(est, H, H, C, w.win, w.win + 1, k_final, idx, n_cand, nullptr, false,
+  hipError_t e = launch_topk(est, H, H, C, w.win, w.win + 1, k_final, idx, n_cand, w.topk, false,
                              stream, cand, index->pos, C);
   if (e != hipSuccess) return SKV_ELAUNCH;
   return hipGetLastError() == hipSuccess ? SKV_OK : SKV_ELAUNCH;

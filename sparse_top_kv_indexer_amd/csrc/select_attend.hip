@@ -50,9 +50,9 @@ __global__ __launch_bounds__(kRowThreads) void select_attend_kernel(
   const int b = row / kv.H, h = row - b * kv.H;
   const int lane = threadIdx.x & 63, wave = row_wave();
   const int n = lane & 15, g4 = lane >> 4;
-  const RowWindow w = row_window(lo_p, hi_p, b, kv.L_max);
-  const float* srow = scores + (int64_t)row * kv.L_max + w.lo;
-  const bool vec = ((uintptr_t)srow & 15) == 0;
+  RowWindow w = row_window(lo_p, hi_p, b, kv.L_max);
+  bool vec;
+  const float* srow = row_base(scores, (int64_t)row * kv.L_max, w, &vec);
 
   // 1. the row's threshold (histogram first, then the scores)
   const uint4 gv = ((const uint4*)(ghist + (int64_t)row * kBins))[threadIdx.x];
@@ -108,10 +108,10 @@ __global__ __launch_bounds__(kRowThreads) void select_attend_kernel(
     const int first = oa + min(oe, need_eq);
     const int last = oa + L.wa[wave] + min(oe + L.we[wave], need_eq);
     if (first < r1 && last > r0) {
-      const int pos0 = wave * kSeg + 4 * lane;          // relative to lo
+      const int pos0 = w.lo - w.o + wave * kSeg + 4 * lane;
       row_emit(kr, cg, T, need_eq, oa, oe, [&](int dst, int g, int e) {
         if (dst >= r0 && dst < r1) {
-          const int t = w.lo + pos0 + 256 * g + e;
+          const int t = pos0 + 256 * g + e;
           orow[dst] = t;
           lst[dst - r0] = t;
         }
@@ -286,7 +286,7 @@ __global__ __launch_bounds__(kRowThreads) void select_attend_kernel(
 
 bool select_attend_supported(const KvArgs& kv, int G) {
   return kv.bf16 && kv.v != nullptr && kv.d_k == kD && kv.d_v == kD && G >= 1 && G <= 8 &&
-         kv.L_max <= kSweep;
+         row_slots_max(kv.L_max) <= kSweep;
 }
 
 size_t select_attend_partial_bytes(const KvArgs& kv, int G) {

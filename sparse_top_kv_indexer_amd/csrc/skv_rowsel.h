@@ -7,9 +7,12 @@
 // Selected: every key > T plus the first need_eq keys equal to T, in
 // position order (ties go to the lower position).
 //
-// Layout: in sweep s, lane l of wave w holds the keys of the positions
-// s * kSweep + w * kSeg + 256 g + 4 l + e (g < kGroups, e < 4) relative to the
-// window start, so every load instruction reads 1 KB of consecutive scores.
+// Layout: the row is read from the 16-byte boundary at or below the window
+// start, w.o slots before it; in sweep s, lane l of wave w holds the slots
+// j = s * kSweep + w * kSeg + 256 g + 4 l + e (g < kGroups, e < 4), slot j
+// being position lo - o + j, so every load instruction reads 1 KB of
+// consecutive scores with 16-byte loads whatever the window's alignment.
+// Slots outside [o, o + n) read as -inf.
 #pragma once
 
 #include "skv_device.h"
@@ -32,6 +35,8 @@ __device__ __forceinline__ uint32_t score_key(float s) {
 
 struct RowWindow {
   int lo, hi, n;
+  int o;    // slots between the 16-byte boundary and the window start
+  int ns;   // slots to read: o + n
 };
 
 __device__ __forceinline__ RowWindow row_window(const int32_t* lo_p, const int32_t* hi_p, int b,
@@ -40,7 +45,28 @@ __device__ __forceinline__ RowWindow row_window(const int32_t* lo_p, const int32
   w.lo = max(0, min(lo_p[b], L_max));
   w.hi = max(w.lo, min(hi_p[b], L_max));
   w.n = w.hi - w.lo;
+  w.o = 0;
+  w.ns = w.n;
   return w;
+}
+
+// The pointer rows are read from: the window start itself, or, when the
+// scores array starts on a 16-byte boundary (*vec = true), the boundary at
+// or below it (never before the array), with w.o / w.ns set accordingly.
+__device__ __forceinline__ const float* row_base(const float* scores, int64_t row_off,
+                                                 RowWindow& w, bool* vec) {
+  const float* start = scores + row_off + w.lo;
+  *vec = ((uintptr_t)scores & 15) == 0;
+  if (!*vec) return start;
+  w.o = (int)(((uintptr_t)start & 15) >> 2);
+  w.ns = w.o + w.n;
+  return start - w.o;
+}
+
+// Sweeps needed for rows of at most L_max slots whose window start may sit up
+// to 3 slots past a 16-byte boundary that lies before the row start.
+__host__ __device__ __forceinline__ int row_slots_max(int L_max) {
+  return L_max % 4 == 0 ? L_max : L_max + 3;
 }
 
 __device__ __forceinline__ int wave_total(int incl) { return __builtin_amdgcn_readlane(incl, 63); }
@@ -72,25 +98,38 @@ struct RowSelLds {
   int trio[3];
 };
 
-// Scores of sweep sw; positions past the window read as -inf.
-__device__ __forceinline__ void row_load(const float* s, const RowWindow& w, bool vec, int sw,
-                                         float (&v)[kGroups][4]) {
-  const int lane = threadIdx.x & 63, wave = row_wave();
-  const int p0 = sw * kSweep + wave * kSeg + 4 * lane;
+// Scores of the slots p0 + 256 g + e (s from row_base); slots outside the
+// window read as -inf.  A 16-byte load covers slots j .. j + 3 only when all
+// of them lie before the window end, so nothing past the row is read.
+__device__ __forceinline__ void slots_load(const float* s, const RowWindow& w, bool vec, int p0,
+                                           float (&v)[kGroups][4]) {
 #pragma unroll
   for (int g = 0; g < kGroups; ++g) {
     const int p = p0 + 256 * g;
-    if (vec && p + 4 <= w.n) {
+    if (vec && p + 4 <= w.ns) {
       const float4 f = *(const float4*)(s + p);
       v[g][0] = f.x;
       v[g][1] = f.y;
       v[g][2] = f.z;
       v[g][3] = f.w;
+      if (p < w.o) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (p + e < w.o) v[g][e] = -INFINITY;
+      }
     } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[g][e] = p + e < w.n ? s[p + e] : -INFINITY;
+      for (int e = 0; e < 4; ++e)
+        v[g][e] = (p + e >= w.o && p + e < w.ns) ? s[p + e] : -INFINITY;
     }
   }
+}
+
+// The slots p0 + 256 g + e of sweep sw for this lane (see the layout above).
+__device__ __forceinline__ void row_load(const float* s, const RowWindow& w, bool vec, int sw,
+                                         float (&v)[kGroups][4]) {
+  const int lane = threadIdx.x & 63, wave = row_wave();
+  slots_load(s, w, vec, sw * kSweep + wave * kSeg + 4 * lane, v);
 }
 
 __device__ __forceinline__ void row_keys(const float (&v)[kGroups][4], uint32_t (&kk)[kGroups][4]) {
@@ -128,11 +167,14 @@ __device__ __forceinline__ int row_search4096(RowSelLds& L, int need, int* total
 // Threshold of the row once L.hist holds its top-12-bit histogram (and a
 // barrier has passed).  keys_ready() runs after the first search (callers
 // convert resident scores to keys there, overlapping their arrival);
-// for_keys(f) calls f(key) for every key of the window.
-template <class KeysReady, class ForKeys>
-__device__ __forceinline__ void row_threshold(RowSelLds& L, int k, KeysReady&& keys_ready,
-                                              ForKeys&& for_keys, uint32_t* T_out,
-                                              int* need_eq_out, int* k_sel_out) {
+// prepare(b0, in_bin) runs (by the whole workgroup) before the lower digits
+// are resolved within bin b0 of in_bin keys; for_keys(f) then calls f(key)
+// for every key of the window, or at least for every key of bin b0.
+template <class KeysReady, class Prepare, class ForKeys>
+__device__ __forceinline__ void row_threshold_p(RowSelLds& L, int k, KeysReady&& keys_ready,
+                                                Prepare&& prepare, ForKeys&& for_keys,
+                                                uint32_t* T_out, int* need_eq_out,
+                                                int* k_sel_out) {
   const int lane = threadIdx.x & 63, wave = row_wave();
   int n_cand;
   const int k_sel = row_search4096(L, -k, &n_cand);   // min(k, n_cand)
@@ -146,6 +188,7 @@ __device__ __forceinline__ void row_threshold(RowSelLds& L, int k, KeysReady&& k
     int need = k_sel - above;
     T = ((uint32_t)b0 << 20) - 1u;   // the whole bin b0 is taken
     if (need < in_bin) {
+      prepare(b0, in_bin);
       // bits 19..8 of the keys of bin b0 (finite keys have top bits >= 8, so
       // b0 >= 8 and empty slots never match)
       lds_barrier();   // everyone has read trio and the top-bit counts
@@ -189,6 +232,13 @@ __device__ __forceinline__ void row_threshold(RowSelLds& L, int k, KeysReady&& k
   *T_out = T;
   *need_eq_out = need_eq;
   *k_sel_out = k_sel;
+}
+
+template <class KeysReady, class ForKeys>
+__device__ __forceinline__ void row_threshold(RowSelLds& L, int k, KeysReady&& keys_ready,
+                                              ForKeys&& for_keys, uint32_t* T_out,
+                                              int* need_eq_out, int* k_sel_out) {
+  row_threshold_p(L, k, keys_ready, [](int, int) {}, for_keys, T_out, need_eq_out, k_sel_out);
 }
 
 // Per group g, the lane's counts of keys above T (low 16 bits) and equal to T

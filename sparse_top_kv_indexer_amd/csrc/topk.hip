@@ -6,25 +6,32 @@
 // final selection is an exact top-k, whatever was prefetched).
 //
 // gfx950 design: a radix select on an order-preserving 32-bit key
-// (sign-flipped float bits), one 1024-thread workgroup per row.  The row's
-// keys stay in registers (32 per lane for rows of up to 32768 scores; longer
-// rows are re-read per pass) while the workgroup
-//   1. takes the histogram of the top 12 key bits (built by the score scan
-//      when the two are fused, else here with LDS atomics) and finds the bin
-//      b0 that holds the k-th largest key while the row's scores arrive;
-//   2. resolves the exact 32-bit threshold T and the number of keys equal to
-//      T to take (lowest positions first) with two more digits of 12 and 8
-//      bits, histogramming only the keys whose prefix still matches;
-//   3. writes the selected positions in ascending order: per group of 4
-//      consecutive keys per lane, one DPP prefix sum of the packed counts of
-//      keys above and equal to T places every lane's keys; one barrier
-//      exchanges the waves' totals.
-// Everything after the one load of the row happens in registers and LDS with
-// DPP scans, so the kernel is a short chain of barriers rather than a chain
-// of memory round trips.  ECHO describes an 8-bit, 256-bin histogram of the top score
-// bits as prior art; a 12-bit first digit splits each fp32 octave into 8
-// bins, which keeps the threshold bin small for score distributions that span
-// a few octaves.  The kernel zeroes the row histogram it read, so a
+// (sign-flipped float bits) whose first digit is the top 12 bits.  ECHO
+// describes an 8-bit, 256-bin histogram of the top score bits as prior art; a
+// 12-bit first digit splits each fp32 octave into 8 bins, which keeps the
+// threshold bin small for score distributions that span a few octaves.
+//   0. the row's top-12-bit histogram: built by the score scan when the two
+//      are fused, else by topk_hist_kernel (one 256-thread workgroup per
+//      8192-slot slice, LDS atomics, non-zero bins added into the row's);
+//   1. topk_compact_kernel, one workgroup per slice: every workgroup finds
+//      the bin b0 that holds the k-th largest key from the histogram and
+//      lists its slice's keys in bins >= b0, with their positions, in
+//      position order (a DPP prefix sum per group of 4 slots and one atomic
+//      per workgroup on the row's list counter place them); the list holds
+//      the keys above b0 plus the bin's, typically k plus a few hundred;
+//   2. topk_finish_kernel, one 1024-thread workgroup per row: reads the list
+//      slice by slice (16 entries per lane), resolves the exact threshold T
+//      and the number of keys equal to T to take (lowest positions first)
+//      with two more digits of 12 and 8 bits over the listed keys of bin b0,
+//      and writes the selected positions in ascending order with one prefix
+//      sum over the list.
+// The per-key work over the whole row is spread over all compute units and
+// the row is read once (twice without the fused histogram).  A row whose
+// list would exceed kRowList keys (many keys tied around the threshold) is
+// selected by the finishing workgroup alone, re-reading the row per digit;
+// so are rows of at most one 32768-slot sweep without a fused histogram,
+// where one kernel beats three.
+// The finishing kernel zeroes the row's histogram and list counter, so a
 // zero-filled workspace stays valid across calls.
 #include "skv_rowsel.h"
 #include "skv_topk.h"
@@ -33,91 +40,306 @@ namespace skv {
 
 namespace {
 
-// RES: the whole window fits one sweep and stays in registers; otherwise the
-// scores are re-read from memory for every pass over the keys.
-template <bool RES>
-__global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* scores, int H,
-                                                               int L_max, const int32_t* lo_p,
-                                                               const int32_t* hi_p, int k,
-                                                               uint32_t* ghist, int32_t* idx,
-                                                               int32_t* count,
-                                                               const int32_t* map_a,
-                                                               const int32_t* map_b, int map_ld) {
-  __shared__ RowSelLds L;
-  const int row = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = row_wave();
-  const RowWindow w = row_window(lo_p, hi_p, row / H, L_max);
-  const float* s = scores + (int64_t)row * L_max + w.lo;
-  const int n_sweeps = (w.n + kSweep - 1) / kSweep;
-  const bool vec = ((uintptr_t)s & 15) == 0;   // 16-byte loads where aligned
+constexpr int kSliceThreads = 256;           // 4 waves x kSeg slots = kSlice
+static_assert(kSliceThreads / 64 * kSeg == kSlice, "slice layout");
+constexpr int kListCap = 16384;              // fallback: LDS list of the threshold bin's keys
 
-  // the row histogram is loaded first and the resident scores next, so the
-  // threshold-bin search overlaps the scores' arrival
-  uint4* gh4 = ghist ? (uint4*)(ghist + (int64_t)row * kBins) : nullptr;
-  uint4 gv = make_uint4(0u, 0u, 0u, 0u);
-  if (gh4) gv = gh4[threadIdx.x];
-  float fv[RES ? kGroups : 1][4];
-  if constexpr (RES) row_load(s, w, vec, 0, fv);
+// Window of row `row`, its read base and this lane's first slot in slice sl
+// (slots sl * kSlice + wave * kSeg + 256 g + 4 lane + e).
+struct SliceView {
+  RowWindow w;
+  const float* s;
+  bool vec;
+  int p0;
+};
+
+__device__ __forceinline__ SliceView slice_view(const float* scores, int row, int H, int L_max,
+                                                const int32_t* lo_p, const int32_t* hi_p, int sl) {
+  SliceView v;
+  v.w = row_window(lo_p, hi_p, row / H, L_max);
+  v.s = row_base(scores, (int64_t)row * L_max, v.w, &v.vec);
+  v.p0 = sl * kSlice + (threadIdx.x >> 6) * kSeg + 4 * (threadIdx.x & 63);
+  return v;
+}
+
+// ------------------------------------------------------------ histogram --
+// Grid rows * slices, 256 threads: the slice's top-12-bit key counts.
+__global__ __launch_bounds__(kSliceThreads) void topk_hist_kernel(const float* scores, int H,
+                                                                  int L_max, const int32_t* lo_p,
+                                                                  const int32_t* hi_p,
+                                                                  uint32_t* ghist, int n_slices) {
+  __shared__ uint32_t lh[kBins];
+  const int row = blockIdx.x / n_slices, sl = blockIdx.x - row * n_slices;
+  const SliceView v = slice_view(scores, row, H, L_max, lo_p, hi_p, sl);
+  if (sl * kSlice >= v.w.ns) return;   // the whole slice lies past the window
+  float f[kGroups][4];
+  slots_load(v.s, v.w, v.vec, v.p0, f);
+#pragma unroll
+  for (int u = 0; u < kBins / 4 / kSliceThreads; ++u)
+    ((uint4*)lh)[threadIdx.x + u * kSliceThreads] = make_uint4(0u, 0u, 0u, 0u);
+  lds_barrier();
+#pragma unroll
+  for (int g = 0; g < kGroups; ++g)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t key = score_key(f[g][e]);
+      if (key) atomicAdd(&lh[key >> 20], 1u);
+    }
+  lds_barrier();
+  uint32_t* gh = ghist + (int64_t)row * kBins;
+  for (int i = threadIdx.x; i < kBins; i += kSliceThreads) {
+    const uint32_t c = lh[i];
+    if (c) atomicAdd(&gh[i], c);
+  }
+}
+
+// -------------------------------------------------------------- listing --
+// Grid rows * slices, 256 threads.
+__global__ __launch_bounds__(kSliceThreads) void topk_compact_kernel(
+    const float* scores, int H, int L_max, const int32_t* lo_p, const int32_t* hi_p, int k,
+    TopkWs ws, int n_slices) {
+  __shared__ int wsum[4], wlist[4];
+  __shared__ int sh[3];   // smallest listed key, listed count, this slice's list offset
+  const int row = blockIdx.x / n_slices, sl = blockIdx.x - row * n_slices;
+  const int lane = threadIdx.x & 63, wave = row_wave();
+  const SliceView v = slice_view(scores, row, H, L_max, lo_p, hi_p, sl);
+  const bool any = sl * kSlice < v.w.ns;
+  float f[kGroups][4];
+  if (any) slots_load(v.s, v.w, v.vec, v.p0, f);
+
+  // the bin of the k-th largest key: thread t holds bins 16 t .. 16 t + 15
+  const uint4* gh = (const uint4*)(ws.hist + (int64_t)row * kBins) + 4 * threadIdx.x;
+  int c[16];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const uint4 x = gh[u];
+    c[4 * u] = (int)x.x;
+    c[4 * u + 1] = (int)x.y;
+    c[4 * u + 2] = (int)x.z;
+    c[4 * u + 3] = (int)x.w;
+  }
+  int tsum = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) tsum += c[j];
+  const int incl = wave_incl_scan(tsum);
+  if (lane == 63) wsum[wave] = incl;
+  lds_barrier();
+  int total = 0, upto = incl;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    total += wsum[u];
+    if (u < wave) upto += wsum[u];
+  }
+  const int k_sel = min(k, total);
+  if (threadIdx.x == 0 && (k_sel <= 0 || k_sel == total)) {
+    sh[0] = k_sel <= 0 ? -1 : 1;   // nothing, or every finite key (key >= 1)
+    sh[1] = k_sel <= 0 ? 0 : total;
+  }
+  if (k_sel > 0 && k_sel < total) {
+    int above = total - upto;   // keys in the bins above this thread's
+#pragma unroll
+    for (int j = 15; j >= 0; --j) {
+      if (above < k_sel && k_sel <= above + c[j]) {
+        sh[0] = (int)((uint32_t)(16 * threadIdx.x + j) << 20);
+        sh[1] = above + c[j];
+      }
+      above += c[j];
+    }
+  }
+  lds_barrier();
+  const uint32_t lower = (uint32_t)sh[0];
+  const int listed = sh[1];
+  if (listed > kRowList) {   // the finishing workgroup selects this row alone
+    if (sl == 0 && threadIdx.x == 0) {
+      ws.meta[2 * row] = (int)lower;
+      ws.meta[2 * row + 1] = -1;
+    }
+    return;
+  }
+  if (sl == 0 && threadIdx.x == 0) {
+    ws.meta[2 * row] = (int)lower;
+    ws.meta[2 * row + 1] = listed;
+  }
+
+  // this slice's keys >= lower, in position order
+  uint32_t kk[kGroups][4];
+  int cg[kGroups], ig[kGroups], wt = 0;
+#pragma unroll
+  for (int g = 0; g < kGroups; ++g) {
+    int n = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      kk[g][e] = any ? score_key(f[g][e]) : 0u;
+      n += kk[g][e] >= lower && kk[g][e] != 0u;
+    }
+    cg[g] = n;
+    ig[g] = wave_incl_scan(n);
+    wt += wave_total(ig[g]);
+  }
+  if (lane == 0) wlist[wave] = wt;
+  lds_barrier();
+  int o = 0, t_wg = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    if (u < wave) o += wlist[u];
+    t_wg += wlist[u];
+  }
+  if (threadIdx.x == 0) {
+    const int base = t_wg ? atomicAdd(&ws.ctr[row], t_wg) : 0;
+    sh[2] = base;
+    ws.slc[((int64_t)row * n_slices + sl) * 2] = base;
+    ws.slc[((int64_t)row * n_slices + sl) * 2 + 1] = t_wg;
+  }
+  lds_barrier();
+  o += sh[2];
+  uint32_t* lk = ws.lkey + (int64_t)row * kRowList;
+  int32_t* lp = ws.lpos + (int64_t)row * kRowList;
+  const int pos0 = v.w.lo - v.w.o + v.p0;
+#pragma unroll
+  for (int g = 0; g < kGroups; ++g) {
+    int d = o + ig[g] - cg[g];
+    if (cg[g]) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (kk[g][e] >= lower && kk[g][e] != 0u) {
+          if (d < kRowList) {
+            lk[d] = kk[g][e];
+            lp[d] = pos0 + 256 * g + e;
+          }
+          ++d;
+        }
+    }
+    o += wave_total(ig[g]);
+  }
+}
+
+// ------------------------------------------------------------ finishing --
+// The whole selection of one row by one workgroup, re-reading the row from
+// memory for every pass (rows whose list would overflow).  The threshold
+// bin's keys are compacted into an LDS list when they fit, so the lower
+// digits need no further pass over the row.
+// RES: the row is one sweep, whose keys stay in registers across the passes.
+template <bool RES>
+__device__ void row_select_alone(const float* scores, int row, int H, int L_max,
+                                 const int32_t* lo_p, const int32_t* hi_p, int k,
+                                 uint32_t* ghist_row, bool hist_ready, int32_t* orow,
+                                 int32_t* count, const int32_t* map_a, const int32_t* map_b,
+                                 int map_ld, RowSelLds& L, uint32_t* klist, int& klist_n) {
+  const int lane = threadIdx.x & 63, wave = row_wave();
+  RowWindow w = row_window(lo_p, hi_p, row / H, L_max);
+  bool vec;
+  const float* s = row_base(scores, (int64_t)row * L_max, w, &vec);
+  const int n_sweeps = RES ? 1 : (w.ns + kSweep - 1) / kSweep;
+  uint4* gh4 = (uint4*)ghist_row;
+  const uint4 gv = hist_ready ? gh4[threadIdx.x] : make_uint4(0u, 0u, 0u, 0u);
   uint32_t kr[RES ? kGroups : 1][4];
-  auto for_keys = [&](auto&& f) {
+  if constexpr (RES) {
+    float f[kGroups][4];
+    row_load(s, w, vec, 0, f);
+    row_keys(f, kr);
+  }
+
+  // F(keys, sweep) for every sweep, the next sweep's loads in flight while
+  // one is processed
+  auto for_sweeps = [&](auto&& F) {
     if constexpr (RES) {
-#pragma unroll
-      for (int g = 0; g < kGroups; ++g)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) f(kr[g][e]);
-    } else {
-      for (int sw = 0; sw < n_sweeps; ++sw) {
-        float v[kGroups][4];
+      F(kr, 0);
+      return;
+    }
+    float va[kGroups][4], vb[kGroups][4];
+    row_load(s, w, vec, 0, va);
+    for (int sw = 0; sw < n_sweeps; sw += 2) {
+      if (sw + 1 < n_sweeps) row_load(s, w, vec, sw + 1, vb);
+      {
         uint32_t kk[kGroups][4];
-        row_load(s, w, vec, sw, v);
-        row_keys(v, kk);
+        row_keys(va, kk);
+        F(kk, sw);
+      }
+      if (sw + 1 < n_sweeps) {
+        if (sw + 2 < n_sweeps) row_load(s, w, vec, sw + 2, va);
+        uint32_t kk[kGroups][4];
+        row_keys(vb, kk);
+        F(kk, sw + 1);
+      }
+    }
+  };
+  bool use_list = false;
+  auto for_keys = [&](auto&& f) {
+    if (use_list) {
+      const int nl = min(klist_n, kListCap);
+      for (int i = threadIdx.x; i < nl; i += kRowThreads) f(klist[i]);
+    } else {
+      for_sweeps([&](const uint32_t (&kk)[kGroups][4], int) {
 #pragma unroll
         for (int g = 0; g < kGroups; ++g)
 #pragma unroll
           for (int e = 0; e < 4; ++e) f(kk[g][e]);
-      }
+      });
     }
   };
-
-  // 1. histogram of the top 12 bits
-  if (gh4) {
-    *(uint4*)(L.hist + 4 * threadIdx.x) = gv;
-  } else {
-    if constexpr (RES) row_keys(fv, kr);
-    *(uint4*)(L.hist + 4 * threadIdx.x) = make_uint4(0u, 0u, 0u, 0u);
+  // one pass compacts the keys of bin b0 into klist (a wave prefix sum of
+  // the lanes' match counts places them; one LDS atomic per wave and sweep)
+  auto prepare = [&](int b0, int in_bin) {
+    if (RES || in_bin > kListCap) return;
+    if (threadIdx.x == 0) klist_n = 0;
     lds_barrier();
+    for_sweeps([&](const uint32_t (&kk)[kGroups][4], int) {
+      int c = 0;
+#pragma unroll
+      for (int g = 0; g < kGroups; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) c += (kk[g][e] >> 20) == (uint32_t)b0;
+      const int incl = wave_incl_scan(c);
+      int base = 0;
+      if (lane == 63) base = atomicAdd(&klist_n, incl);
+      int o = __builtin_amdgcn_readlane(base, 63) + incl - c;
+      if (c) {
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if ((kk[g][e] >> 20) == (uint32_t)b0) {
+              if (o < kListCap) klist[o] = kk[g][e];
+              ++o;
+            }
+      }
+    });
+    lds_barrier();
+    use_list = true;
+  };
+
+  *(uint4*)(L.hist + 4 * threadIdx.x) = gv;
+  if (threadIdx.x < 256) L.dh[threadIdx.x] = 0u;
+  lds_barrier();
+  if (!hist_ready) {   // the top-12-bit histogram, with LDS atomics
     for_keys([&](uint32_t key) {
       if (key) atomicAdd(&L.hist[key >> 20], 1u);
     });
+    lds_barrier();
   }
-  if (threadIdx.x < 256) L.dh[threadIdx.x] = 0u;
-  lds_barrier();
-
-  // 2. threshold
   uint32_t T;
   int need_eq, k_sel;
-  row_threshold(
-      L, k,
-      [&]() {
-        if constexpr (RES) {
-          if (gh4) row_keys(fv, kr);
-        }
-      },
-      for_keys, &T, &need_eq, &k_sel);
+  row_threshold_p(L, k, []() {}, prepare, for_keys, &T, &need_eq, &k_sel);
 
-  // 3. ordered write
-  int32_t* orow = idx + (int64_t)row * k;
-  // mapped positions: the selected positions are collected in LDS (the
-  // histogram is no longer needed) and mapped in one pass at the end, so the
-  // two dependent loads per key are not serialised inside the emit loop
   const bool map_lds = map_a && k <= kBins;
   int a_base = 0, e_base = 0;   // keys above / equal to T in earlier sweeps
-  auto emit_sweep = [&](const uint32_t (&kk)[kGroups][4], int sw) {
+  for (int sw = 0; sw < n_sweeps; ++sw) {
+    uint32_t kk[kGroups][4];
+    if constexpr (RES) {
+#pragma unroll
+      for (int g = 0; g < kGroups; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) kk[g][e] = kr[g][e];
+    } else {
+      float f[kGroups][4];
+      row_load(s, w, vec, sw, f);
+      row_keys(f, kk);
+    }
     int cg[kGroups];
     const int lt = row_counts(kk, T, cg);
     int oa, oe, ta, te;
     row_wave_offsets(L, lt, &oa, &oe, &ta, &te);
-    const int pos0 = w.lo + sw * kSweep + wave * kSeg + 4 * lane;
+    const int pos0 = w.lo - w.o + sw * kSweep + wave * kSeg + 4 * lane;
     row_emit(kk, cg, T, need_eq, a_base + oa, e_base + oe, [&](int dst, int g, int e) {
       if (dst < k) {
         const int p = pos0 + 256 * g + e;
@@ -128,17 +350,6 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* scor
     });
     a_base += ta;
     e_base += te;
-  };
-  if constexpr (RES) {
-    emit_sweep(kr, 0);
-  } else {
-    for (int sw = 0; sw < n_sweeps; ++sw) {
-      float v[kGroups][4];
-      uint32_t kk[kGroups][4];
-      row_load(s, w, vec, sw, v);
-      row_keys(v, kk);
-      emit_sweep(kk, sw);
-    }
   }
   const int n_sel = min(k, a_base + min(e_base, need_eq));
   if (map_lds) {
@@ -148,30 +359,185 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* scor
   }
   for (int i = n_sel + threadIdx.x; i < k; i += kRowThreads) orow[i] = -1;
   if (threadIdx.x == 0) count[row] = n_sel;
-  if (gh4) gh4[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);   // zero for the next call
+  if (hist_ready) gh4[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// Grid rows, 1024 threads: short rows without a fused histogram, each
+// selected by its workgroup alone (one kernel instead of three).
+__global__ __launch_bounds__(kRowThreads) void topk_alone_kernel(
+    const float* scores, int H, int L_max, const int32_t* lo_p, const int32_t* hi_p, int k,
+    int32_t* idx, int32_t* count, const int32_t* map_a, const int32_t* map_b, int map_ld) {
+  __shared__ RowSelLds L;
+  __shared__ int klist_n;
+  const int row = blockIdx.x;
+  row_select_alone<true>(scores, row, H, L_max, lo_p, hi_p, k, nullptr, false,
+                         idx + (int64_t)row * k, count, map_a, map_b, map_ld, L, nullptr, klist_n);
+}
+
+// Grid rows, 1024 threads.
+__global__ __launch_bounds__(kRowThreads) void topk_finish_kernel(
+    const float* scores, int H, int L_max, const int32_t* lo_p, const int32_t* hi_p, int k,
+    TopkWs ws, int n_slices, int32_t* idx, int32_t* count, const int32_t* map_a,
+    const int32_t* map_b, int map_ld) {
+  __shared__ RowSelLds L;
+  __shared__ uint32_t klist[kListCap];
+  __shared__ int klist_n;
+  __shared__ int s_off[kMaxSlices + 1], s_at[kMaxSlices];
+  constexpr int kPer = kRowList / kRowThreads;   // list entries per lane
+  const int row = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = row_wave();
+  int32_t* orow = idx + (int64_t)row * k;
+  uint32_t* ghist_row = ws.hist + (int64_t)row * kBins;
+  uint4* gh4 = (uint4*)ghist_row;
+  const uint4 gv = gh4[threadIdx.x];   // issued with the loads below, before the branch
+  const int32_t* slc = ws.slc + (int64_t)row * n_slices * 2;
+  const int sl0 = threadIdx.x;
+  const int n0 = sl0 < n_slices ? slc[2 * sl0 + 1] : 0;
+  const int at0 = sl0 < n_slices ? slc[2 * sl0] : 0;
+  if (ws.meta[2 * row + 1] < 0) {
+    row_select_alone<false>(scores, row, H, L_max, lo_p, hi_p, k, ghist_row, true, orow, count,
+                            map_a, map_b, map_ld, L, klist, klist_n);
+    return;
+  }
+
+  // 1. the list, slice by slice: s_off = first list rank of each slice
+  int run = 0;
+  for (int b0 = 0; b0 < n_slices; b0 += kRowThreads) {
+    const int sl = b0 + threadIdx.x;
+    const int n = b0 == 0 ? n0 : (sl < n_slices ? slc[2 * sl + 1] : 0);
+    if (sl < n_slices) s_at[sl] = b0 == 0 ? at0 : slc[2 * sl];
+    const int inc = wave_incl_scan(n);
+    if (lane == 63) L.wt[wave] = inc;
+    lds_barrier();
+    int before = run + inc - n, all = 0;
+#pragma unroll
+    for (int u = 0; u < kRowWaves; ++u) {
+      if (u < wave) before += L.wt[u];
+      all += L.wt[u];
+    }
+    if (sl < n_slices) s_off[sl] = before;
+    run += all;
+    lds_barrier();
+  }
+  const int m = min(run, kRowList);
+  if (threadIdx.x == 0) {
+    s_off[n_slices] = run;
+    ws.ctr[row] = 0;   // for the next call
+  }
+  lds_barrier();
+  // list ranks kPer * tid .. kPer * tid + kPer - 1: the slice holding a rank
+  // is the last one whose first rank is not above it
+  uint32_t key[kPer];
+  int pos[kPer];
+  const uint32_t* lk = ws.lkey + (int64_t)row * kRowList;
+  const int32_t* lp = ws.lpos + (int64_t)row * kRowList;
+  {
+    const int r0 = kPer * threadIdx.x;
+    int sl = 0;
+    if (r0 < m) {
+      int a = 0, b = n_slices - 1;
+      while (a < b) {
+        const int mid = (a + b + 1) >> 1;
+        if (s_off[mid] <= r0) a = mid;
+        else b = mid - 1;
+      }
+      sl = a;
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int r = r0 + u;
+      key[u] = 0u;
+      pos[u] = 0;
+      if (r < m) {
+        while (s_off[sl + 1] <= r) ++sl;
+        const int at = s_at[sl] + (r - s_off[sl]);
+        if (at < kRowList) {
+          key[u] = lk[at];
+          pos[u] = lp[at];
+        }
+      }
+    }
+  }
+
+  // 2. threshold over the listed keys (all keys of bins >= b0)
+  *(uint4*)(L.hist + 4 * threadIdx.x) = gv;
+  if (threadIdx.x < 256) L.dh[threadIdx.x] = 0u;
+  lds_barrier();
+  uint32_t T;
+  int need_eq, k_sel;
+  row_threshold(
+      L, k, []() {},
+      [&](auto&& f) {
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) f(key[u]);
+      },
+      &T, &need_eq, &k_sel);
+
+  // 3. ordered write: the lane's entries are consecutive list ranks
+  int c = 0;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u)
+    c += key[u] > T ? 1 : ((key[u] != 0u && key[u] == T) ? 0x10000 : 0);
+  const int inc = wave_incl_scan(c);
+  int oa, oe, ta, te;
+  row_wave_offsets(L, c, &oa, &oe, &ta, &te);
+  const bool map_lds = map_a && k <= kBins;
+  int ab = oa + ((inc - c) & 0xffff), eb = oe + ((inc - c) >> 16);
+  if (c) {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      int dst = -1;
+      if (key[u] > T) {
+        dst = ab + min(eb, need_eq);
+        ++ab;
+      } else if (key[u] != 0u && key[u] == T) {
+        if (eb < need_eq) dst = ab + eb;
+        ++eb;
+      }
+      if (dst >= 0 && dst < k) {
+        if (!map_a) orow[dst] = pos[u];
+        else if (map_lds) L.hist[dst] = (uint32_t)pos[u];
+        else orow[dst] = map_b[map_a[(int64_t)row * map_ld + pos[u]]];
+      }
+    }
+  }
+  const int n_sel = min(k, ta + min(te, need_eq));
+  if (map_lds) {
+    lds_barrier();
+    for (int i = threadIdx.x; i < n_sel; i += kRowThreads)
+      orow[i] = map_b[map_a[(int64_t)row * map_ld + (int)L.hist[i]]];
+  }
+  for (int i = n_sel + threadIdx.x; i < k; i += kRowThreads) orow[i] = -1;
+  if (threadIdx.x == 0) count[row] = n_sel;
+  gh4[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);   // zero for the next call
 }
 
 }  // namespace
 
-size_t topk_workspace_bytes(int rows, int L_max) {
-  (void)L_max;
-  return TopkWs::bytes(rows);
-}
+size_t topk_workspace_bytes(int rows, int L_max) { return TopkWs::bytes(rows, L_max); }
 
-bool topk_supported(int L_max) { return L_max >= 1; }
+bool topk_supported(int L_max) { return L_max >= 1 && topk_slices(L_max) <= kMaxSlices; }
 
 hipError_t launch_topk(const float* scores, int rows, int H, int L_max, const int32_t* lo,
                        const int32_t* hi, int k, int32_t* idx, int32_t* count, void* wsp,
                        bool hist_ready, hipStream_t s, const int32_t* map_a,
                        const int32_t* map_b, int map_ld) {
   if (rows <= 0) return hipSuccess;
-  uint32_t* gh = hist_ready ? TopkWs::carve(wsp).hist : nullptr;
-  if (L_max <= kSweep)
-    topk_row_kernel<true><<<rows, kRowThreads, 0, s>>>(scores, H, L_max, lo, hi, k, gh, idx, count,
-                                                          map_a, map_b, map_ld);
-  else
-    topk_row_kernel<false><<<rows, kRowThreads, 0, s>>>(scores, H, L_max, lo, hi, k, gh, idx, count,
-                                                          map_a, map_b, map_ld);
+  const TopkWs ws = TopkWs::carve(wsp, rows, L_max);
+  const int ns = topk_slices(L_max);
+  if (ns > kMaxSlices || (int64_t)rows * ns > 0x7fffffff) return hipErrorInvalidValue;
+  const unsigned grid = (unsigned)(rows * ns);
+  if (!hist_ready && row_slots_max(L_max) <= kSweep) {
+    // rows of one sweep without a fused histogram: one workgroup per row
+    topk_alone_kernel<<<rows, kRowThreads, 0, s>>>(scores, H, L_max, lo, hi, k, idx, count, map_a,
+                                                   map_b, map_ld);
+    return hipGetLastError();
+  }
+  if (!hist_ready)
+    topk_hist_kernel<<<grid, kSliceThreads, 0, s>>>(scores, H, L_max, lo, hi, ws.hist, ns);
+  topk_compact_kernel<<<grid, kSliceThreads, 0, s>>>(scores, H, L_max, lo, hi, k, ws, ns);
+  topk_finish_kernel<<<rows, kRowThreads, 0, s>>>(scores, H, L_max, lo, hi, k, ws, ns, idx, count,
+                                                  map_a, map_b, map_ld);
   return hipGetLastError();
 }
 

@@ -229,10 +229,12 @@ def test_exact_ties_lowest_index_wins():
 # --------------------------------------------------------------- top-k alone
 @pytest.mark.parametrize("L,k,seed", [(1000, 37, 0), (4096, 2048, 1), (32768, 2048, 2),
                                       (40000, 700, 3), (131072, 2048, 4), (5000, 4999, 5),
-                                      (32768, 2048, 6), (70001, 3000, 7)])
+                                      (32768, 2048, 6), (70001, 3000, 7), (32767, 1000, 8),
+                                      (32765, 2048, 9), (4097, 100, 10)])
 def test_topk_kernel_on_oracle_inputs(L, k, seed):
     """Synthetic rows with ties, -0.0 / +0.0, -inf and windows; the GPU set must
-    equal the oracle's set exactly."""
+    equal the oracle's set exactly.  Row lengths that are not multiples of 4
+    put row and window starts at every offset from a 16-byte boundary."""
     say("topk", L, k, seed)
     rng = np.random.default_rng(seed)
     B, H = 2, 2

@@ -11,16 +11,24 @@
 // gfx950 design.  With 128 query heads sharing one latent row the step is a
 // real dense contraction: 2 x 128 x 576 x k flops for the logits and the same
 // order for P.V, on 1152-byte rows.  A workgroup (G/16 waves, 16 heads per
-// wave) owns one split of the position list: it stages up to 64 latent rows
-// in LDS once, then per 16-token chunk
-//   S^T[16 tokens x 16 heads] = K_chunk . Q^T     18 x v_mfma_f32_16x16x32_bf16
-// so each lane ends up with P[head][4 tokens] in exactly the A-operand layout
-// of the value product, and
-//   O[16 heads x 512] += P . V                    32 x v_mfma_f32_16x16x16_bf16
+// wave) owns one split of the position list, at most 128 rows at a time:
+// threads resolve the rows' addresses together, then the load unit copies
+// the rows global -> LDS itself (global_load_lds_dwordx4, no registers
+// involved), so a block costs one chain of table load, copy and wait.  Per
+// 32-token chunk
+//   S^T[16 tokens x 16 heads] = K_half . Q^T     2 x 18 v_mfma_f32_16x16x32_bf16
+// leaves each lane P[head][8 tokens] (4 of each half), which is the A operand
+// of the value product with k slot 8 g4 + e <-> token 4 g4 + e (e < 4) or
+// 16 + 4 g4 + e - 4, and
+//   O[16 heads x 512] += P . V                    32 x v_mfma_f32_16x16x32_bf16
 // with P split into a bf16 head and a bf16 tail (two products), which keeps
-// the probabilities to ~16 significant bits.  The value operand is read from
-// a transposed copy of the chunk in LDS.  An online softmax (log2 domain)
-// runs across chunks; the split partials are merged exactly by log-sum-exp.
+// the probabilities to ~16 significant bits.  The value operand (8 tokens x
+// 1 dim per lane, same k mapping) is read straight from the token-major rows
+// with two transposing LDS reads ds_read_b64_tr_b16: within 16 lanes, lane j
+// receives element j % 4 of the 8-byte pieces addressed by lanes j / 4 + 4 i,
+// so lane (p, g4) addresses token 4 g4 + p / 4 of a half, dims
+// 16 c + 4 (p % 4).  An online softmax (log2 domain) runs across chunks; the
+// split partials are merged exactly by log-sum-exp.
 #include <algorithm>
 
 #include "skv_device.h"
@@ -30,13 +38,15 @@ namespace skv {
 namespace {
 
 constexpr int kDk = 576, kDv = 512;
-constexpr int kRowPad = kDk + 8;        // LDS row stride (bf16 elements)
-constexpr int kStage = 64;              // latent rows staged per LDS fill
+constexpr int kRowPad = kDk + 8;        // LDS row stride (bf16 elements; 1168 B, 16-byte aligned)
+constexpr int kBlock = 128;             // latent rows resident in LDS at a time
 constexpr int kNC = kDk / 32;           // 18 MFMA k-steps for the logits
 constexpr int kVB = kDv / 16;           // 32 value column blocks
 
-typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
 typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_void_t;
+typedef __attribute__((address_space(1))) void* gbl_void_t;
 
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
@@ -44,24 +54,32 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return u >> 16;
 }
 
+// Copy one 1152-byte latent row into LDS with the load unit: lanes 0..63
+// move bytes 0..1023, lanes 0..7 the last 128.
+__device__ __forceinline__ void row_to_lds(const uint16_t* src, uint16_t* dst, int lane) {
+  __builtin_amdgcn_global_load_lds((gbl_void_t)(src + 8 * lane), (lds_void_t)dst, 16, 0, 0);
+  if (lane < 8)
+    __builtin_amdgcn_global_load_lds((gbl_void_t)(src + 512 + 8 * lane), (lds_void_t)(dst + 512),
+                                     16, 0, 0);
+}
+
+// 4 tokens x 1 dim of the value operand from token-major LDS rows
+__device__ __forceinline__ u32x2_t value_tr(const uint16_t* p) {
+  const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)p);
+  return __builtin_bit_cast(u32x2_t, v);
+}
+
 template <int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void mla_split_kernel(
     KvArgs kv, const uint16_t* q, int G, const int32_t* idx, int k, const int32_t* lo_p,
     const int32_t* hi_p, float scale_log2, int n_split, float* part) {
-  __shared__ __attribute__((aligned(16))) uint16_t rows[kStage * kRowPad];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[kDv * 16];    // [dim][token]
-  __shared__ int64_t roff[kStage];
+  __shared__ __attribute__((aligned(16))) uint16_t rows[kBlock * kRowPad];
+  __shared__ int64_t roff[kBlock];
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g4 = lane >> 4;
   const int head0 = wave * 16;                    // this wave's first query head
-
-  // Q^T operand: lane (n, g4), step j holds q[head0 + n][8 (4j + g4) .. +8]
-  bf16x8_t Qf[kNC];
-  const uint16_t* qrow = q + (((int64_t)b * kv.H + h) * G + head0 + n) * kDk;
-#pragma unroll
-  for (int j = 0; j < kNC; ++j)
-    Qf[j] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(qrow + 8 * (4 * j + g4)));
 
   const int seq = min(kv.seq_len[b], kv.L_max);
   const int lo = max(0, min(lo_p[b], seq));
@@ -70,6 +88,15 @@ __global__ __launch_bounds__(WAVES * 64) void mla_split_kernel(
   const int chunk = (n_list + n_split - 1) / n_split;
   const int p0 = s * chunk, p1 = min(n_list, p0 + chunk);
   const int32_t* irow = idx + ((int64_t)b * kv.H + h) * k;
+  const uint16_t* kb = (const uint16_t*)kv.k;
+  const uint16_t* qhead = q + ((int64_t)b * kv.H + h) * G * kDk;   // a finite stand-in row
+
+  // Q^T operand: lane (n, g4), step j holds q[head0 + n][8 (4j + g4) .. +8]
+  bf16x8_t Qf[kNC];
+  const uint16_t* qrow = qhead + (int64_t)(head0 + n) * kDk;
+#pragma unroll
+  for (int j = 0; j < kNC; ++j)
+    Qf[j] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(qrow + 8 * (4 * j + g4)));
 
   // online softmax state for head head0 + n (replicated over g4)
   float m_run = -INFINITY, l_run = 0.f;
@@ -77,13 +104,14 @@ __global__ __launch_bounds__(WAVES * 64) void mla_split_kernel(
 #pragma unroll
   for (int c = 0; c < kVB; ++c) O[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const uint16_t* kb = (const uint16_t*)kv.k;
-  for (int q0 = p0; q0 < p1; q0 += kStage) {
-    const int cnt = min(kStage, p1 - q0);
-    if (tid < kStage) {
+  for (int q0 = p0; q0 < p1; q0 += kBlock) {
+    const int cnt = min(kBlock, p1 - q0);
+    const int n_rows = (cnt + 31) & ~31;          // rows staged: whole 32-token chunks
+    // element offset of each latent row, or -1 (dead, or past the split)
+    for (int r = tid; r < kBlock; r += WAVES * 64) {
       int64_t ro = -1;
-      if (tid < cnt) {
-        const int pos = q0 + tid;
+      if (r < cnt) {
+        const int pos = q0 + r;
         int t;
         if (pos < k) {
           t = irow[pos];
@@ -96,80 +124,49 @@ __global__ __launch_bounds__(WAVES * 64) void mla_split_kernel(
         const int64_t slot = t >= 0 ? slot_of(kv, b, t) : -1;
         ro = slot >= 0 ? row_elem(kv, b, h, slot, kDk) : -1;
       }
-      roff[tid] = ro;
+      roff[r] = ro;
     }
-    __syncthreads();
-    // stage the rows: 72 pieces of 16 B per row.  With up to four waves each
-    // thread keeps four loads in flight before their LDS stores; eight waves
-    // have no registers to spare and issue one load per store.
-    {
-      constexpr int kPieces = kStage * (kDk / 8);
-      if constexpr (WAVES >= 8) {
-        for (int i = tid; i < kPieces; i += WAVES * 64) {
-          const int r = i / (kDk / 8), pc = i - r * (kDk / 8);
-          const int64_t ro = roff[r];
-          const u32x4_t v = ro >= 0 ? *(const u32x4_t*)(kb + ro + 8 * pc) : u32x4_t{0, 0, 0, 0};
-          *(u32x4_t*)(rows + r * kRowPad + 8 * pc) = v;
-        }
-      } else {
-        constexpr int kB = 4;
-        for (int i0 = 0; i0 < kPieces; i0 += kB * WAVES * 64) {
-          u32x4_t v[kB];
-#pragma unroll
-          for (int u = 0; u < kB; ++u) {
-            const int i = i0 + u * WAVES * 64 + tid;
-            const int r = i / (kDk / 8), pc = i - r * (kDk / 8);
-            const int64_t ro = i < kPieces ? roff[r] : -1;
-            v[u] = ro >= 0 ? *(const u32x4_t*)(kb + ro + 8 * pc) : u32x4_t{0, 0, 0, 0};
-          }
-#pragma unroll
-          for (int u = 0; u < kB; ++u) {
-            const int i = i0 + u * WAVES * 64 + tid;
-            const int r = i / (kDk / 8), pc = i - r * (kDk / 8);
-            if (i < kPieces) *(u32x4_t*)(rows + r * kRowPad + 8 * pc) = v[u];
-          }
-        }
-      }
+    __syncthreads();   // also: every wave is done with the previous block's rows
+    // wave w copies rows w, w + WAVES, ...; dead rows get the query row
+    // instead (finite; their weight is zero)
+    for (int r = wave; r < n_rows; r += WAVES) {
+      const int64_t ro = roff[r];
+      row_to_lds(ro >= 0 ? kb + ro : qhead, rows + r * kRowPad, lane);
     }
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    for (int c0 = 0; c0 < cnt; c0 += 16) {
-      // transposed value copy of this chunk: vt[dim][token]
-      for (int d = tid; d < kDv; d += WAVES * 64) {
-        uint32_t pk[8];
+    for (int c0 = 0; c0 < cnt; c0 += 32) {
+      // S^T[token 16 hf + 4 g4 + i][head n] for the two 16-token halves
+      f32x4_t S[2];
 #pragma unroll
-        for (int t2 = 0; t2 < 8; ++t2)
-          pk[t2] = (uint32_t)rows[(c0 + 2 * t2) * kRowPad + d] |
-                   ((uint32_t)rows[(c0 + 2 * t2 + 1) * kRowPad + d] << 16);
-        *(u32x4_t*)(vt + d * 16) = u32x4_t{pk[0], pk[1], pk[2], pk[3]};
-        *(u32x4_t*)(vt + d * 16 + 8) = u32x4_t{pk[4], pk[5], pk[6], pk[7]};
-      }
-      __syncthreads();
-      // S^T[token 4 g4 + i][head n] for the 16 tokens of the chunk
-      f32x4_t S = {0.f, 0.f, 0.f, 0.f};
+      for (int hf = 0; hf < 2; ++hf) {
+        S[hf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < kNC; ++j) {
-        const bf16x8_t Kf = __builtin_bit_cast(
-            bf16x8_t, *(const u32x4_t*)(rows + (c0 + n) * kRowPad + 8 * (4 * j + g4)));
-        S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Kf, Qf[j], S, 0, 0, 0);
+        for (int j = 0; j < kNC; ++j) {
+          const bf16x8_t Kf = __builtin_bit_cast(
+              bf16x8_t,
+              *(const u32x4_t*)(rows + (c0 + 16 * hf + n) * kRowPad + 8 * (4 * j + g4)));
+          S[hf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Kf, Qf[j], S[hf], 0, 0, 0);
+        }
       }
-      float z[4];
+      float z[8];
       float cm = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tk = c0 + 4 * g4 + i;
+      for (int e = 0; e < 8; ++e) {
+        const int tk = c0 + 16 * (e >> 2) + 4 * g4 + (e & 3);
         const bool ok = tk < cnt && roff[tk] >= 0;
-        z[i] = ok ? S[i] * scale_log2 : -INFINITY;
-        cm = fmaxf(cm, z[i]);
+        z[e] = ok ? S[e >> 2][e & 3] * scale_log2 : -INFINITY;
+        cm = fmaxf(cm, z[e]);
       }
       cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
       cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
       const float m_new = fmaxf(m_run, cm);
-      float p[4], ps = 0.f;
+      float p[8], ps = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[i] = m_new == -INFINITY ? 0.f : exp2f(z[i] - m_new);
-        ps += p[i];
+      for (int e = 0; e < 8; ++e) {
+        p[e] = m_new == -INFINITY ? 0.f : exp2f(z[e] - m_new);
+        ps += p[e];
       }
       ps += __shfl_xor(ps, 16, 64);
       ps += __shfl_xor(ps, 32, 64);
@@ -180,29 +177,31 @@ __global__ __launch_bounds__(WAVES * 64) void mla_split_kernel(
       float oc[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) oc[i] = __shfl(corr, 4 * g4 + i, 64);
-      // P as the A operand (head n, tokens 4 g4 .. +3), split into head + tail
-      uint32_t hi16[4], lo16[4];
+      // P as the A operand (head n, k slots 8 g4 .. +7), split into head + tail
+      uint32_t ph[4], pl[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        hi16[i] = f32_to_bf16_rne(p[i]);
-        lo16[i] = f32_to_bf16_rne(p[i] - __uint_as_float(hi16[i] << 16));
+      for (int e = 0; e < 8; e += 2) {
+        const uint32_t h0 = f32_to_bf16_rne(p[e]), h1 = f32_to_bf16_rne(p[e + 1]);
+        const uint32_t l0 = f32_to_bf16_rne(p[e] - __uint_as_float(h0 << 16));
+        const uint32_t l1 = f32_to_bf16_rne(p[e + 1] - __uint_as_float(h1 << 16));
+        ph[e >> 1] = h0 | (h1 << 16);
+        pl[e >> 1] = l0 | (l1 << 16);
       }
-      const bf16x4_t Ph = __builtin_bit_cast(
-          bf16x4_t, u32x2_t{hi16[0] | (hi16[1] << 16), hi16[2] | (hi16[3] << 16)});
-      const bf16x4_t Pl = __builtin_bit_cast(
-          bf16x4_t, u32x2_t{lo16[0] | (lo16[1] << 16), lo16[2] | (lo16[3] << 16)});
+      const bf16x8_t Ph = __builtin_bit_cast(bf16x8_t, u32x4_t{ph[0], ph[1], ph[2], ph[3]});
+      const bf16x8_t Pl = __builtin_bit_cast(bf16x8_t, u32x4_t{pl[0], pl[1], pl[2], pl[3]});
+      // value operand: lane (n, g4) addresses token 16 hf + 4 g4 + n / 4, dims 4 (n % 4) .. + 3
+      const uint16_t* v0 = rows + (c0 + 4 * g4 + (n >> 2)) * kRowPad + 4 * (n & 3);
+      const uint16_t* v1 = v0 + 16 * kRowPad;
 #pragma unroll
       for (int c = 0; c < kVB; ++c) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) O[c][i] *= oc[i];
-        const bf16x4_t Vf = __builtin_bit_cast(
-            bf16x4_t, *(const u32x2_t*)(vt + (16 * c + n) * 16 + 4 * g4));
-        O[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(Ph, Vf, O[c], 0, 0, 0);
-        O[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(Pl, Vf, O[c], 0, 0, 0);
+        const u32x2_t a = value_tr(v0 + 16 * c), bb = value_tr(v1 + 16 * c);
+        const bf16x8_t Vf = __builtin_bit_cast(bf16x8_t, u32x4_t{a[0], a[1], bb[0], bb[1]});
+        O[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ph, Vf, O[c], 0, 0, 0);
+        O[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Pl, Vf, O[c], 0, 0, 0);
       }
-      __syncthreads();
     }
-    __syncthreads();
   }
 
   // partial of this split: O[head][512], max, sum (lane holds rows 4 g4 + i)
@@ -221,7 +220,7 @@ __global__ __launch_bounds__(WAVES * 64) void mla_split_kernel(
   }
 }
 
-int mla_splits(int k) { return std::max(1, std::min(64, (k + kStage - 1) / kStage)); }
+int mla_splits(int k) { return std::max(1, std::min(64, (k + 63) / 64)); }
 
 }  // namespace
 

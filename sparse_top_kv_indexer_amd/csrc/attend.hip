@@ -395,15 +395,17 @@ __global__ __launch_bounds__(kThreads) void attend_mfma_kernel(
 }
 
 // out[b][hq][j] = sum_s acc_s[j] 2^(m_s - M) / sum_s l_s 2^(m_s - M)
-// One workgroup per (b, query head); the split partials are staged in LDS with
-// all loads issued at once.
+// One workgroup per (b, query head); a thread owns two dims and loads them
+// from 16 splits at a time, the first 16 in flight while the split weights
+// are formed (n_split <= 64, D <= 512).
 // With zero_hist != nullptr, the workgroup of the first query head of each KV
 // head also zeroes that row's 4096-bin key histogram (the fused select +
 // attend path leaves it for this kernel, which runs after every reader).
 __global__ __launch_bounds__(256) void attend_reduce_kernel(const float* part, int n_split, int D,
                                                            int HG, float* out, uint32_t* zero_hist,
                                                            int G) {
-  extern __shared__ float ps[];          // [n_split][D + 2]
+  constexpr int SG = 16;                 // splits whose values are loaded together
+  constexpr int ND = 2;                  // dims per thread (D <= 512)
   __shared__ float wts[64];
   __shared__ float inv_l;
   const int hq = blockIdx.x, b = blockIdx.y;
@@ -412,26 +414,46 @@ __global__ __launch_bounds__(256) void attend_reduce_kernel(const float* part, i
     for (int i = threadIdx.x; i < 1024; i += blockDim.x) z[i] = make_uint4(0u, 0u, 0u, 0u);
   }
   const int stride = D + 2;
-  const int n = n_split * stride;
-  const float* base = part + ((int64_t)b * HG + hq) * n;
-  stage_words<16>((uint32_t*)ps, (const uint32_t*)base, n, threadIdx.x, blockDim.x);
-  __syncthreads();
+  const float* base = part + ((int64_t)b * HG + hq) * n_split * stride;
+  // the first group's values are in flight while the split weights are formed
+  float v[SG][ND];
+  auto load_group = [&](int s0) {
+#pragma unroll
+    for (int u = 0; u < SG; ++u)
+#pragma unroll
+      for (int d = 0; d < ND; ++d) {
+        const int j = threadIdx.x + 256 * d;
+        v[u][d] = (s0 + u < n_split && j < D) ? base[(int64_t)(s0 + u) * stride + j] : 0.f;
+      }
+  };
+  load_group(0);
   if (threadIdx.x < 64) {
     const int s = threadIdx.x;
-    const float ms = s < n_split ? ps[s * stride + D] : -INFINITY;
+    const float ms = s < n_split ? base[(int64_t)s * stride + D] : -INFINITY;
+    const float ls = s < n_split ? base[(int64_t)s * stride + D + 1] : 0.f;
     float M = ms;
     for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
     const float w = (s < n_split && M != -INFINITY) ? exp2f(ms - M) : 0.f;
-    float L = s < n_split ? ps[s * stride + D + 1] * w : 0.f;
+    float L = ls * w;
     for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o, 64);
     wts[s] = w;
     if (s == 0) inv_l = L > 0.f ? 1.f / L : 0.f;
   }
   __syncthreads();
-  for (int j = threadIdx.x; j < D; j += blockDim.x) {
-    float a = 0.f;
-    for (int s = 0; s < n_split; ++s) a += ps[s * stride + j] * wts[s];
-    out[((int64_t)b * HG + hq) * D + j] = a * inv_l;
+  float acc[ND] = {0.f, 0.f};
+  for (int s0 = 0; s0 < n_split; s0 += SG) {
+    if (s0) load_group(s0);
+#pragma unroll
+    for (int u = 0; u < SG; ++u) {
+      const float w = s0 + u < n_split ? wts[s0 + u] : 0.f;
+#pragma unroll
+      for (int d = 0; d < ND; ++d) acc[d] += v[u][d] * w;
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < ND; ++d) {
+    const int j = threadIdx.x + 256 * d;
+    if (j < D) out[((int64_t)b * HG + hq) * D + j] = acc[d] * inv_l;
   }
 }
 
@@ -509,17 +531,9 @@ hipError_t launch_gather_attend(const KvArgs& kv, const void* q, int G, const in
 
 hipError_t launch_attend_reduce(const float* part, int n_split, int D, int HG, int B, float* out,
                                 hipStream_t st, uint32_t* zero_hist, int G) {
+  if (n_split > 64 || D > 512) return hipErrorInvalidValue;
   dim3 grid(HG, B);
-  const size_t lds = (size_t)n_split * (D + 2) * sizeof(float);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)attend_reduce_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       64 * (512 + 2) * 4);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  attend_reduce_kernel<<<grid, 256, lds, st>>>(part, n_split, D, HG, out, zero_hist, G);
+  attend_reduce_kernel<<<grid, 256, 0, st>>>(part, n_split, D, HG, out, zero_hist, G);
   return hipGetLastError();
 }
 

@@ -11,8 +11,10 @@
 // exactly what sparsekv_topk_resume followed by sparsekv_gather_attend
 // compute, in one kernel plus the split merge instead of three kernels.
 //
-// gfx950 design.  Grid (kSplits, rows), 1024 threads: 256 workgroups, one
-// per CU, for the 32 rows of the GQA workload.  Every workgroup of a row
+// gfx950 design.  Grid kSplits x rows, 1024 threads: 256 workgroups, one
+// per CU, for the 32 rows of the GQA workload; the kSplits workgroups of a
+// row are placed on one XCD (workgroups go to the 8 XCDs round-robin by id),
+// so the row's scores come from memory once and then from that XCD's L2.  Every workgroup of a row
 // loads the whole row of scores (coalesced, into registers) and finds the
 // row's threshold redundantly, so no workgroup waits for another; workgroup s
 // then takes the selected keys of ranks [s k_sel / kSplits, (s + 1) k_sel /
@@ -46,7 +48,9 @@ __global__ __launch_bounds__(kRowThreads) void select_attend_kernel(
   __shared__ int64_t rows_sh[kRowWaves][2][16];     // per wave: key-row offsets of two chunks
   __shared__ float red[kRowWaves][4][kD + 2];       // merge of the waves, 4 heads a round
   __shared__ int32_t tbl[kSweep / 16];              // the row's block-table entries (paged)
-  const int s = blockIdx.x, row = blockIdx.y;
+  // the kSplits workgroups of a row run on one XCD and share its scores in L2
+  const int vid = xcd_remap(blockIdx.x, gridDim.x);
+  const int s = vid % kSplits, row = vid / kSplits;
   const int b = row / kv.H, h = row - b * kv.H;
   const int lane = threadIdx.x & 63, wave = row_wave();
   const int n = lane & 15, g4 = lane >> 4;
@@ -298,7 +302,7 @@ hipError_t launch_select_attend(const KvArgs& kv, const void* q, int G, const fl
                                 float scale, int32_t* idx, int32_t* count, float* part,
                                 float* out, hipStream_t st) {
   const float scale_log2 = scale * 1.4426950408889634f;
-  dim3 grid(kSplits, kv.B * kv.H);
+  const dim3 grid(kSplits * kv.B * kv.H);   // a multiple of 8
   if (G <= 4)
     select_attend_kernel<4><<<grid, kRowThreads, 0, st>>>(kv, (const uint16_t*)q, G, scores, lo, hi,
                                                           k, hist, scale_log2, idx, count, part);

@@ -120,6 +120,16 @@ __device__ __forceinline__ void stage_words(uint32_t* dst, const uint32_t* src, 
   }
 }
 
+// Workgroups are dispatched to the 8 XCDs round-robin by linear id (XCD =
+// id % 8), and each XCD has its own L2.  For n (a multiple of 8) workgroups,
+// xcd_remap(id, n) gives the virtual index under which XCD x runs the
+// consecutive virtual indices [x n / 8, (x + 1) n / 8), so workgroups that
+// read the same data can be placed on one XCD.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_remap(int id, int n) {
+  return (id % kXcds) * (n / kXcds) + id / kXcds;
+}
+
 __device__ __forceinline__ uint64_t lanemask_lt(int lane) {
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }

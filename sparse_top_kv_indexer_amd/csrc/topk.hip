@@ -28,9 +28,9 @@
 // The per-key work over the whole row is spread over all compute units and
 // the row is read once (twice without the fused histogram).  A row whose
 // list would exceed kRowList keys (many keys tied around the threshold) is
-// selected by the finishing workgroup alone, re-reading the row per digit;
-// so are rows of at most one 32768-slot sweep without a fused histogram,
-// where one kernel beats three.
+// selected by the finishing workgroup alone, re-reading the row per digit.
+// Rows of at most one 32768-slot sweep are selected by one workgroup each,
+// with the keys in registers: one kernel beats two or three there.
 // The finishing kernel zeroes the row's histogram and list counter, so a
 // zero-filled workspace stays valid across calls.
 #include "skv_rowsel.h"
@@ -219,8 +219,12 @@ __global__ __launch_bounds__(kSliceThreads) void topk_compact_kernel(
 // bin's keys are compacted into an LDS list when they fit, so the lower
 // digits need no further pass over the row.
 // RES: the row is one sweep, whose keys stay in registers across the passes.
-template <bool RES>
-__device__ void row_select_alone(const float* scores, int row, int H, int L_max,
+// MAP: how a selected position p is written: 0 as p; 1 (k <= 4096) as
+// map_b[map_a[row][p]], the positions gathered in LDS first and mapped in one
+// pass; 2 mapped as each key is emitted.  A compile-time choice, so every
+// instantiation has one kind of store in its emission loop.
+template <bool RES, int MAP>
+__device__ __forceinline__ void row_select_alone(const float* scores, int row, int H, int L_max,
                                  const int32_t* lo_p, const int32_t* hi_p, int k,
                                  uint32_t* ghist_row, bool hist_ready, int32_t* orow,
                                  int32_t* count, const int32_t* map_a, const int32_t* map_b,
@@ -232,12 +236,12 @@ __device__ void row_select_alone(const float* scores, int row, int H, int L_max,
   const int n_sweeps = RES ? 1 : (w.ns + kSweep - 1) / kSweep;
   uint4* gh4 = (uint4*)ghist_row;
   const uint4 gv = hist_ready ? gh4[threadIdx.x] : make_uint4(0u, 0u, 0u, 0u);
+  // RES: the row's scores are loaded now and turned into keys once the
+  // first digit's search (from the scan's histogram) has overlapped their
+  // arrival
   uint32_t kr[RES ? kGroups : 1][4];
-  if constexpr (RES) {
-    float f[kGroups][4];
-    row_load(s, w, vec, 0, f);
-    row_keys(f, kr);
-  }
+  float fr[RES ? kGroups : 1][4];
+  if constexpr (RES) row_load(s, w, vec, 0, fr);
 
   // F(keys, sweep) for every sweep, the next sweep's loads in flight while
   // one is processed
@@ -312,6 +316,7 @@ __device__ void row_select_alone(const float* scores, int row, int H, int L_max,
   if (threadIdx.x < 256) L.dh[threadIdx.x] = 0u;
   lds_barrier();
   if (!hist_ready) {   // the top-12-bit histogram, with LDS atomics
+    if constexpr (RES) row_keys(fr, kr);
     for_keys([&](uint32_t key) {
       if (key) atomicAdd(&L.hist[key >> 20], 1u);
     });
@@ -319,9 +324,15 @@ __device__ void row_select_alone(const float* scores, int row, int H, int L_max,
   }
   uint32_t T;
   int need_eq, k_sel;
-  row_threshold_p(L, k, []() {}, prepare, for_keys, &T, &need_eq, &k_sel);
+  row_threshold_p(
+      L, k,
+      [&]() {
+        if constexpr (RES) {
+          if (hist_ready) row_keys(fr, kr);
+        }
+      },
+      prepare, for_keys, &T, &need_eq, &k_sel);
 
-  const bool map_lds = map_a && k <= kBins;
   int a_base = 0, e_base = 0;   // keys above / equal to T in earlier sweeps
   for (int sw = 0; sw < n_sweeps; ++sw) {
     uint32_t kk[kGroups][4];
@@ -343,8 +354,8 @@ __device__ void row_select_alone(const float* scores, int row, int H, int L_max,
     row_emit(kk, cg, T, need_eq, a_base + oa, e_base + oe, [&](int dst, int g, int e) {
       if (dst < k) {
         const int p = pos0 + 256 * g + e;
-        if (!map_a) orow[dst] = p;
-        else if (map_lds) L.hist[dst] = (uint32_t)p;
+        if constexpr (MAP == 0) orow[dst] = p;
+        else if constexpr (MAP == 1) L.hist[dst] = (uint32_t)p;
         else orow[dst] = map_b[map_a[(int64_t)row * map_ld + p]];
       }
     });
@@ -352,7 +363,7 @@ __device__ void row_select_alone(const float* scores, int row, int H, int L_max,
     e_base += te;
   }
   const int n_sel = min(k, a_base + min(e_base, need_eq));
-  if (map_lds) {
+  if constexpr (MAP == 1) {
     lds_barrier();
     for (int i = threadIdx.x; i < n_sel; i += kRowThreads)
       orow[i] = map_b[map_a[(int64_t)row * map_ld + (int)L.hist[i]]];
@@ -362,19 +373,24 @@ __device__ void row_select_alone(const float* scores, int row, int H, int L_max,
   if (hist_ready) gh4[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
 }
 
-// Grid rows, 1024 threads: short rows without a fused histogram, each
-// selected by its workgroup alone (one kernel instead of three).
+// Grid rows, 1024 threads: rows of one sweep, each selected by its workgroup
+// alone with the keys in registers (one kernel instead of two or three);
+// ghist: the rows' histograms from the scan, or null.
+template <int MAP>
 __global__ __launch_bounds__(kRowThreads) void topk_alone_kernel(
     const float* scores, int H, int L_max, const int32_t* lo_p, const int32_t* hi_p, int k,
-    int32_t* idx, int32_t* count, const int32_t* map_a, const int32_t* map_b, int map_ld) {
+    uint32_t* ghist, int32_t* idx, int32_t* count, const int32_t* map_a, const int32_t* map_b,
+    int map_ld) {
   __shared__ RowSelLds L;
   __shared__ int klist_n;
   const int row = blockIdx.x;
-  row_select_alone<true>(scores, row, H, L_max, lo_p, hi_p, k, nullptr, false,
+  row_select_alone<true, MAP>(scores, row, H, L_max, lo_p, hi_p, k,
+                         ghist ? ghist + (int64_t)row * kBins : nullptr, ghist != nullptr,
                          idx + (int64_t)row * k, count, map_a, map_b, map_ld, L, nullptr, klist_n);
 }
 
 // Grid rows, 1024 threads.
+template <int MAP>
 __global__ __launch_bounds__(kRowThreads) void topk_finish_kernel(
     const float* scores, int H, int L_max, const int32_t* lo_p, const int32_t* hi_p, int k,
     TopkWs ws, int n_slices, int32_t* idx, int32_t* count, const int32_t* map_a,
@@ -395,7 +411,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_finish_kernel(
   const int n0 = sl0 < n_slices ? slc[2 * sl0 + 1] : 0;
   const int at0 = sl0 < n_slices ? slc[2 * sl0] : 0;
   if (ws.meta[2 * row + 1] < 0) {
-    row_select_alone<false>(scores, row, H, L_max, lo_p, hi_p, k, ghist_row, true, orow, count,
+    row_select_alone<false, MAP>(scores, row, H, L_max, lo_p, hi_p, k, ghist_row, true, orow, count,
                             map_a, map_b, map_ld, L, klist, klist_n);
     return;
   }
@@ -481,7 +497,6 @@ __global__ __launch_bounds__(kRowThreads) void topk_finish_kernel(
   const int inc = wave_incl_scan(c);
   int oa, oe, ta, te;
   row_wave_offsets(L, c, &oa, &oe, &ta, &te);
-  const bool map_lds = map_a && k <= kBins;
   int ab = oa + ((inc - c) & 0xffff), eb = oe + ((inc - c) >> 16);
   if (c) {
 #pragma unroll
@@ -495,14 +510,14 @@ __global__ __launch_bounds__(kRowThreads) void topk_finish_kernel(
         ++eb;
       }
       if (dst >= 0 && dst < k) {
-        if (!map_a) orow[dst] = pos[u];
-        else if (map_lds) L.hist[dst] = (uint32_t)pos[u];
+        if constexpr (MAP == 0) orow[dst] = pos[u];
+        else if constexpr (MAP == 1) L.hist[dst] = (uint32_t)pos[u];
         else orow[dst] = map_b[map_a[(int64_t)row * map_ld + pos[u]]];
       }
     }
   }
   const int n_sel = min(k, ta + min(te, need_eq));
-  if (map_lds) {
+  if constexpr (MAP == 1) {
     lds_barrier();
     for (int i = threadIdx.x; i < n_sel; i += kRowThreads)
       orow[i] = map_b[map_a[(int64_t)row * map_ld + (int)L.hist[i]]];
@@ -527,17 +542,33 @@ hipError_t launch_topk(const float* scores, int rows, int H, int L_max, const in
   const int ns = topk_slices(L_max);
   if (ns > kMaxSlices || (int64_t)rows * ns > 0x7fffffff) return hipErrorInvalidValue;
   const unsigned grid = (unsigned)(rows * ns);
-  if (!hist_ready && row_slots_max(L_max) <= kSweep) {
-    // rows of one sweep without a fused histogram: one workgroup per row
-    topk_alone_kernel<<<rows, kRowThreads, 0, s>>>(scores, H, L_max, lo, hi, k, idx, count, map_a,
-                                                   map_b, map_ld);
+  const int map = map_a ? (k <= kBins ? 1 : 2) : 0;
+  if (row_slots_max(L_max) <= kSweep) {
+    // rows of one sweep: one workgroup per row
+    uint32_t* gh = hist_ready ? ws.hist : nullptr;
+    if (map == 0)
+      topk_alone_kernel<0><<<rows, kRowThreads, 0, s>>>(scores, H, L_max, lo, hi, k, gh, idx, count,
+                                                        map_a, map_b, map_ld);
+    else if (map == 1)
+      topk_alone_kernel<1><<<rows, kRowThreads, 0, s>>>(scores, H, L_max, lo, hi, k, gh, idx, count,
+                                                        map_a, map_b, map_ld);
+    else
+      topk_alone_kernel<2><<<rows, kRowThreads, 0, s>>>(scores, H, L_max, lo, hi, k, gh, idx, count,
+                                                        map_a, map_b, map_ld);
     return hipGetLastError();
   }
   if (!hist_ready)
     topk_hist_kernel<<<grid, kSliceThreads, 0, s>>>(scores, H, L_max, lo, hi, ws.hist, ns);
   topk_compact_kernel<<<grid, kSliceThreads, 0, s>>>(scores, H, L_max, lo, hi, k, ws, ns);
-  topk_finish_kernel<<<rows, kRowThreads, 0, s>>>(scores, H, L_max, lo, hi, k, ws, ns, idx, count,
-                                                  map_a, map_b, map_ld);
+  if (map == 0)
+    topk_finish_kernel<0><<<rows, kRowThreads, 0, s>>>(scores, H, L_max, lo, hi, k, ws, ns, idx,
+                                                       count, map_a, map_b, map_ld);
+  else if (map == 1)
+    topk_finish_kernel<1><<<rows, kRowThreads, 0, s>>>(scores, H, L_max, lo, hi, k, ws, ns, idx,
+                                                       count, map_a, map_b, map_ld);
+  else
+    topk_finish_kernel<2><<<rows, kRowThreads, 0, s>>>(scores, H, L_max, lo, hi, k, ws, ns, idx,
+                                                       count, map_a, map_b, map_ld);
   return hipGetLastError();
 }
 

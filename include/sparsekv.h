@@ -151,6 +151,39 @@ skv_status sparsekv_topk_resume(const float* scores, int32_t B, int32_t H, int32
                                 skv_window win, int32_t k, int32_t* idx, int32_t* count,
                                 void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* ------------------------------------------ threshold-prefiltered top-k --
+ * The k-th largest index score of a decode step moves smoothly from step to
+ * step, so an EMA (alpha = 0.5) of the past steps' k-th scores predicts the
+ * next one (ECHO-OSDI26 wiki page, observation 3 and core method 3; there it
+ * decides what to prefetch, the exact top-k still following the scan).  Here
+ * the scan lists the keys that reach the prediction, and the exact top-k is
+ * resolved over them when at least k survive; the result is always the exact
+ * top-k of sparsekv_topk.
+ *
+ * sparsekv_score_prefilter: sparsekv_score that also lists, per row (b, h),
+ * the candidates t in [lo[b], hi[b]) with score >= thr[b][h] into the top-k
+ * workspace (at most 16384 per row; more marks the row as overflowed).
+ *   thr  [B][H] fp32 predicted threshold, read; -inf lists every candidate.
+ * bf16 keys with d_k in {64, 128, 256} and 1 <= G <= 16 (SKV_EUNSUPPORTED
+ * otherwise).  ws: sparsekv_workspace_size(SKV_OP_TOPK, kv, 0, k, NULL)
+ * bytes, zero-filled before its first use (the list counters stay zero
+ * between calls: sparsekv_topk_prefiltered resets them).
+ *
+ * sparsekv_topk_prefiltered: after sparsekv_score_prefilter on the same ws,
+ * the exact top-k of every row (same results as sparsekv_topk), from the
+ * survivors when at least k survived and the window spans at most 131072
+ * positions, else from the whole row.  Then
+ *   thr[b][h] = alpha kth + (1 - alpha) thr[b][h]   (kth if thr was -inf),
+ * kth being the row's k-th largest score (-inf with fewer than k candidates).
+ *   used [B][H] int32 (optional, may be NULL): 1 where the survivors sufficed. */
+skv_status sparsekv_score_prefilter(const skv_kv* kv, const void* q, int32_t G, skv_window win,
+                                    const float* thr, float* scores, void* ws, size_t ws_bytes,
+                                    hipStream_t stream);
+skv_status sparsekv_topk_prefiltered(const float* scores, int32_t B, int32_t H, int32_t L_max,
+                                     skv_window win, int32_t k, float* thr, float alpha,
+                                     int32_t* idx, int32_t* count, int32_t* used, void* ws,
+                                     size_t ws_bytes, hipStream_t stream);
+
 /* ---------------------------------------------------- gather + attention --
  * For each sequence b, KV head h and query head g:
  *   A = {idx[b][h][i] : lo <= idx < hi, live} ∪ {live t < lo} ∪ {live t >= hi}

@@ -75,6 +75,10 @@ _SIGS = {
                                     c_sz, c_vp]),
     "sparsekv_topk_resume": (c_i32, [c_vp, c_i32, c_i32, c_i32, skv_window, c_i32, c_vp, c_vp,
                                      c_vp, c_sz, c_vp]),
+    "sparsekv_score_prefilter": (c_i32, [ctypes.POINTER(skv_kv), c_vp, c_i32, skv_window, c_vp,
+                                         c_vp, c_vp, c_sz, c_vp]),
+    "sparsekv_topk_prefiltered": (c_i32, [c_vp, c_i32, c_i32, c_i32, skv_window, c_i32, c_vp,
+                                          c_f32, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "sparsekv_gather_attend": (c_i32, [ctypes.POINTER(skv_kv), c_vp, c_i32, c_vp, c_i32,
                                        skv_window, c_f32, c_vp, c_vp, c_sz, c_vp]),
     "sparsekv_select_attend": (c_i32, [ctypes.POINTER(skv_kv), c_vp, c_i32, skv_window, c_i32,
@@ -336,6 +340,39 @@ def sparsekv_topk_resume(scores: torch.Tensor, lo: torch.Tensor, hi: torch.Tenso
            lib().sparsekv_topk_resume(_ptr(scores), B, H, L, skv_window(_ptr(lo), _ptr(hi)), k,
                                       _ptr(idx), _ptr(count), _ptr(ws),
                                       ws.numel() * ws.element_size(), _stream()))
+    return idx, count
+
+
+def sparsekv_score_prefilter(kv: KVTensors, q: torch.Tensor, G: int, lo: torch.Tensor,
+                             hi: torch.Tensor, thr: torch.Tensor, scores: torch.Tensor,
+                             ws: torch.Tensor):
+    """sparsekv_score that also lists, per row, the candidates whose score is
+    >= thr[b][h] (fp32 [B][H]) into the top-k workspace ws."""
+    _dev(q, "q", kv.torch_dtype)
+    _dev(scores, "scores", torch.float32)
+    _dev(thr, "thr", torch.float32)
+    c = kv.c()
+    _check("sparsekv_score_prefilter",
+           lib().sparsekv_score_prefilter(ctypes.byref(c), _ptr(q), G,
+                                          skv_window(_ptr(lo), _ptr(hi)), _ptr(thr), _ptr(scores),
+                                          _ptr(ws), ws.numel() * ws.element_size(), _stream()))
+    return scores
+
+
+def sparsekv_topk_prefiltered(scores: torch.Tensor, lo: torch.Tensor, hi: torch.Tensor, k: int,
+                              thr: torch.Tensor, idx: torch.Tensor, count: torch.Tensor,
+                              ws: torch.Tensor, alpha: float = 0.5,
+                              used: Optional[torch.Tensor] = None):
+    """Exact top-k from the survivors sparsekv_score_prefilter listed in ws
+    (the whole row where they do not suffice); thr is updated in place by the
+    EMA of the rows' k-th scores.  used[b][h] = 1 where the survivors sufficed."""
+    B, H, L = scores.shape
+    _dev(thr, "thr", torch.float32)
+    _check("sparsekv_topk_prefiltered",
+           lib().sparsekv_topk_prefiltered(_ptr(scores), B, H, L, skv_window(_ptr(lo), _ptr(hi)),
+                                           k, _ptr(thr), float(alpha), _ptr(idx), _ptr(count),
+                                           _ptr(used) if used is not None else None, _ptr(ws),
+                                           ws.numel() * ws.element_size(), _stream()))
     return idx, count
 
 

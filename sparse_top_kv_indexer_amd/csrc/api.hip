@@ -6,6 +6,7 @@
 
 #include "../../include/sparsekv.h"
 #include "skv_internal.h"
+#include "skv_topk.h"
 
 using namespace skv;
 
@@ -108,6 +109,32 @@ skv_status sparsekv_topk_resume(const float* scores, int32_t B, int32_t H, int32
   if (!ws || ws_bytes < topk_workspace_bytes(B * H, L_max)) return SKV_EWORKSPACE;
   return launched(launch_topk(scores, B * H, H, L_max, win.lo, win.hi, k, idx, count, ws, true,
                               stream));
+}
+
+skv_status sparsekv_score_prefilter(const skv_kv* kv, const void* q, int32_t G, skv_window win,
+                                    const float* thr, float* scores, void* ws, size_t ws_bytes,
+                                    hipStream_t stream) {
+  if (!kv_ok(kv) || !q || !scores || !thr || G < 1 || !win.lo || !win.hi) return SKV_EINVAL;
+  const KvArgs a = to_args(kv);
+  if (!score_supported(kv, G) || !score_prefilter_supported(a, G) || !topk_supported(kv->L_max))
+    return SKV_EUNSUPPORTED;
+  const int rows = kv->B * kv->H;
+  if (!ws || ws_bytes < topk_workspace_bytes(rows, kv->L_max)) return SKV_EWORKSPACE;
+  const TopkWs w = TopkWs::carve(ws, rows, kv->L_max);
+  return launched(launch_score_prefilter(a, q, G, scores, win.lo, win.hi, thr, w.lkey, w.lpos,
+                                         w.ctr, kRowList, stream));
+}
+
+skv_status sparsekv_topk_prefiltered(const float* scores, int32_t B, int32_t H, int32_t L_max,
+                                     skv_window win, int32_t k, float* thr, float alpha,
+                                     int32_t* idx, int32_t* count, int32_t* used, void* ws,
+                                     size_t ws_bytes, hipStream_t stream) {
+  if (!scores || !idx || !count || !thr || !win.lo || !win.hi) return SKV_EINVAL;
+  if (B < 1 || H < 1 || L_max < 1 || k < 1 || !(alpha >= 0.f && alpha <= 1.f)) return SKV_EINVAL;
+  if (!topk_survivors_supported(L_max)) return SKV_EUNSUPPORTED;
+  if (!ws || ws_bytes < topk_workspace_bytes(B * H, L_max)) return SKV_EWORKSPACE;
+  return launched(launch_topk_survivors(scores, B * H, H, L_max, win.lo, win.hi, k, idx, count,
+                                        ws, thr, alpha, used, stream));
 }
 
 skv_status sparsekv_select(const skv_kv* kv, const void* q, int32_t G, skv_window win, int32_t k,

@@ -42,7 +42,19 @@ struct HistArgs {
   const int32_t* lo;
   const int32_t* hi;
   uint32_t* hist;   // [B*H][4096]
+  // survivors (threshold prefilter): keys of the window with score >= thr[row]
+  // go to the row's list [row][cap] through the fill counter ctr[row]
+  const float* thr;
+  uint32_t* lkey;
+  int32_t* lpos;
+  int32_t* ctr;
+  int cap;
 };
+
+// Survivor staging per workgroup and row segment; a segment with more is
+// reported to the consumer as an overflow (its row then takes the full top-k).
+constexpr int kSvCap = 2048;
+constexpr int kSvOverflow = 1 << 24;
 
 __device__ __forceinline__ void hist_add(uint32_t* lh, float s, int t, int lo, int hi) {
   uint32_t u = __float_as_uint(s);
@@ -182,12 +194,21 @@ constexpr int kStageEntries = 4096;
 // the vector ALUs instead: lane (n, g4) holds the query elements of its d/32
 // 16-byte pieces in registers, forms a partial dot of key n, and two lane
 // exchanges (lanes n, n + 16, n + 32, n + 48) complete it.
-template <int NC, int D, int GMAX, bool HIST, bool VALU>
+//
+// MODE 1 adds the top-12-bit key histogram of the window (first digit of the
+// exact top-k); MODE 2 lists the window's keys whose score reaches the row's
+// predicted threshold (threshold-prefiltered top-k), staged in LDS and added
+// to the row's list with one atomic per workgroup and row segment.
+template <int NC, int D, int GMAX, int MODE, bool VALU>
 __global__ __launch_bounds__(kThreads) void score_stream_kernel(KvArgs kv, const uint16_t* q, int G,
                                                                  float* scores, HistArgs ha,
                                                                  int cpr) {
+  constexpr bool HIST = MODE == 1, SURV = MODE == 2;
   __shared__ uint32_t lh[HIST ? 4096 : 1];
   __shared__ int32_t tab[kStageEntries];
+  __shared__ uint32_t svk[SURV ? kSvCap : 1];
+  __shared__ int32_t svp[SURV ? kSvCap : 1];
+  __shared__ int sv_n, sv_base;
   constexpr int d_k = 32 * NC;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -217,10 +238,17 @@ __global__ __launch_bounds__(kThreads) void score_stream_kernel(KvArgs kv, const
       for (int i = threadIdx.x; i < n_seg * 16; i += kThreads) tab[i] = src[i];
     }
     int wlo = 0, whi = 0;
+    float thr = 0.f;
     if constexpr (HIST) {
       for (int i = threadIdx.x; i < 4096; i += kThreads) lh[i] = 0u;
       wlo = ha.lo[b];
       whi = ha.hi[b];
+    }
+    if constexpr (SURV) {
+      if (threadIdx.x == 0) sv_n = 0;
+      wlo = ha.lo[b];
+      whi = ha.hi[b];
+      thr = ha.thr[r];
     }
     lds_barrier();
 
@@ -316,6 +344,17 @@ __global__ __launch_bounds__(kThreads) void score_stream_kernel(KvArgs kv, const
         if constexpr (HIST) {
           if (ok) hist_add(lh, sc, t, wlo, whi);
         }
+        if constexpr (SURV) {
+          uint32_t u = __float_as_uint(sc);
+          if (ok && t >= wlo && t < whi && sc >= thr && (u & 0x7f800000u) != 0x7f800000u) {
+            if (u == 0x80000000u) u = 0u;
+            const int i = atomicAdd(&sv_n, 1);
+            if (i < kSvCap) {
+              svk[i] = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+              svp[i] = t;
+            }
+          }
+        }
       }
     };
 
@@ -351,6 +390,19 @@ __global__ __launch_bounds__(kThreads) void score_stream_kernel(KvArgs kv, const
         if (s < n_w) finish(mfma(s), s);
     }
     if constexpr (HIST) hist_flush(lh, ha.hist + (int64_t)r * 4096);
+    if constexpr (SURV) {
+      lds_barrier();
+      const int nsv = sv_n;
+      if (threadIdx.x == 0)
+        sv_base = nsv ? atomicAdd(&ha.ctr[r], nsv > kSvCap ? kSvOverflow : nsv) : 0;
+      lds_barrier();
+      const int base = sv_base;
+      for (int i = threadIdx.x; i < min(nsv, kSvCap); i += kThreads)
+        if (base + i < ha.cap) {
+          ha.lkey[(int64_t)r * ha.cap + base + i] = svk[i];
+          ha.lpos[(int64_t)r * ha.cap + base + i] = svp[i];
+        }
+    }
   }
 }
 
@@ -398,11 +450,11 @@ int resident_wgs(K kernel, int* cache, int n_cache) {
   return cache[dev];
 }
 
-template <int NC, int D, int GMAX, bool HIST, bool VALU = false>
+template <int NC, int D, int GMAX, int MODE, bool VALU = false>
 hipError_t launch_stream_k(const KvArgs& kv, const void* q, int G, float* scores,
                            const HistArgs& ha, hipStream_t s) {
   static int cache[64] = {0};
-  auto kern = score_stream_kernel<NC, D, GMAX, HIST, VALU>;
+  auto kern = score_stream_kernel<NC, D, GMAX, MODE, VALU>;
   const int cpr = (kv.L_max + 15) / 16;
   const int64_t n_work = (int64_t)kv.B * kv.H * cpr;
   // at least 16 chunks per workgroup and at most one workgroup per resident
@@ -415,19 +467,25 @@ hipError_t launch_stream_k(const KvArgs& kv, const void* q, int G, float* scores
   return hipGetLastError();
 }
 
+template <int NC, int D, int MODE>
+hipError_t launch_stream_m(const KvArgs& kv, const void* q, int G, float* scores,
+                           const HistArgs& ha, hipStream_t s) {
+  if constexpr (NC <= 8) {
+    if (G == 1) return launch_stream_k<NC, D, 1, MODE, true>(kv, q, G, scores, ha, s);
+  }
+  if (G <= 4) return launch_stream_k<NC, D, 4, MODE>(kv, q, G, scores, ha, s);
+  return launch_stream_k<NC, D, 16, MODE>(kv, q, G, scores, ha, s);
+}
+
 template <int NC, int D>
 hipError_t launch_stream(const KvArgs& kv, const void* q, int G, float* scores, const HistArgs& ha,
                          hipStream_t s) {
-  if constexpr (NC <= 8) {
-    if (G == 1)
-      return ha.hist ? launch_stream_k<NC, D, 1, true, true>(kv, q, G, scores, ha, s)
-                     : launch_stream_k<NC, D, 1, false, true>(kv, q, G, scores, ha, s);
+  if (ha.lkey) {
+    if constexpr (NC <= 8) return launch_stream_m<NC, D, 2>(kv, q, G, scores, ha, s);
+    return hipErrorInvalidValue;
   }
-  if (G <= 4)
-    return ha.hist ? launch_stream_k<NC, D, 4, true>(kv, q, G, scores, ha, s)
-                   : launch_stream_k<NC, D, 4, false>(kv, q, G, scores, ha, s);
-  return ha.hist ? launch_stream_k<NC, D, 16, true>(kv, q, G, scores, ha, s)
-                 : launch_stream_k<NC, D, 16, false>(kv, q, G, scores, ha, s);
+  if (ha.hist) return launch_stream_m<NC, D, 1>(kv, q, G, scores, ha, s);
+  return launch_stream_m<NC, D, 0>(kv, q, G, scores, ha, s);
 }
 
 }  // namespace
@@ -457,6 +515,24 @@ hipError_t launch_score(const KvArgs& kv, const void* q, int G, float* scores, c
     if (npl <= 4) return launch_valu<false, 4, 2>(kv, q, G, scores, ha, grid, s);
   }
   return hipErrorInvalidValue;
+}
+
+bool score_prefilter_supported(const KvArgs& kv, int G) {
+  const int nc = kv.d_k / 32;
+  return kv.bf16 && G >= 1 && G <= 16 && kv.d_k % 32 == 0 && (nc == 2 || nc == 4 || nc == 8);
+}
+
+hipError_t launch_score_prefilter(const KvArgs& kv, const void* q, int G, float* scores,
+                                  const int32_t* lo, const int32_t* hi, const float* thr,
+                                  uint32_t* lkey, int32_t* lpos, int32_t* ctr, int cap,
+                                  hipStream_t s) {
+  HistArgs ha{lo, hi, nullptr, thr, lkey, lpos, ctr, cap};
+  switch (kv.d_k / 32) {
+    case 2: return launch_stream<2, 4>(kv, q, G, scores, ha, s);
+    case 4: return launch_stream<4, 4>(kv, q, G, scores, ha, s);
+    case 8: return launch_stream<8, 2>(kv, q, G, scores, ha, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace skv

@@ -25,6 +25,21 @@ struct KvArgs {
 hipError_t launch_score(const KvArgs& kv, const void* q, int G, float* scores, const int32_t* lo,
                         const int32_t* hi, uint32_t* hist, hipStream_t s);
 
+// score.hip, threshold prefilter: the scan also lists, per row, the keys of
+// [lo, hi) whose score is >= thr[row] (into the top-k workspace's lists)
+bool score_prefilter_supported(const KvArgs& kv, int G);
+hipError_t launch_score_prefilter(const KvArgs& kv, const void* q, int G, float* scores,
+                                  const int32_t* lo, const int32_t* hi, const float* thr,
+                                  uint32_t* lkey, int32_t* lpos, int32_t* ctr, int cap,
+                                  hipStream_t s);
+// topk.hip: exact top-k from those survivors (the full row when fewer than
+// k survive or the list overflowed), thr updated by the EMA of the k-th score
+hipError_t launch_topk_survivors(const float* scores, int rows, int H, int L_max,
+                                 const int32_t* lo, const int32_t* hi, int k, int32_t* idx,
+                                 int32_t* count, void* ws, float* thr, float alpha,
+                                 int32_t* used_list, hipStream_t s);
+bool topk_survivors_supported(int L_max);
+
 // topk.hip (workspace layout in skv_topk.h); hist_ready: the row histograms
 // were already accumulated by the producer of the scores.  With map_a set,
 // a selected position p of row r is written as map_b[map_a[r * map_ld + p]].

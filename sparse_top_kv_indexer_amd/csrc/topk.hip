@@ -214,6 +214,51 @@ __global__ __launch_bounds__(kSliceThreads) void topk_compact_kernel(
 }
 
 // ------------------------------------------------------------ finishing --
+// The score whose order-preserving key is `key`.
+__device__ __forceinline__ float key_score(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+}
+
+// Minimum of v over the 1024-thread workgroup (two barriers; red: 16 words).
+__device__ __forceinline__ uint32_t block_min_u32(uint32_t v, uint32_t* red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o, 64));
+  lds_barrier();   // earlier readers of red are done
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  lds_barrier();
+  uint32_t m = 0xffffffffu;
+#pragma unroll
+  for (int i = 0; i < kRowWaves; ++i) m = min(m, red[i]);
+  return m;
+}
+
+// pre[w] = set bits of map[0 .. w) for the W <= 4096 words of a position
+// bitmap, 4 words per thread (two barriers).
+__device__ __forceinline__ void bitmap_prefix(const uint32_t* map, int* pre, int W, RowSelLds& L) {
+  const int lane = threadIdx.x & 63, wave = row_wave();
+  const int w0 = 4 * threadIdx.x;
+  int c[4], tot = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    c[u] = w0 + u < W ? __popc(map[w0 + u]) : 0;
+    tot += c[u];
+  }
+  const int inc = wave_incl_scan(tot);
+  lds_barrier();   // earlier readers of L.wt are done
+  if (lane == 63) L.wt[wave] = inc;
+  lds_barrier();
+  int before = inc - tot;
+#pragma unroll
+  for (int v = 0; v < kRowWaves; ++v)
+    if (v < wave) before += L.wt[v];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    if (w0 + u < W) {
+      pre[w0 + u] = before;
+      before += c[u];
+    }
+  lds_barrier();
+}
 // The whole selection of one row by one workgroup, re-reading the row from
 // memory for every pass (rows whose list would overflow).  The threshold
 // bin's keys are compacted into an LDS list when they fit, so the lower
@@ -228,7 +273,8 @@ __device__ __forceinline__ void row_select_alone(const float* scores, int row, i
                                  const int32_t* lo_p, const int32_t* hi_p, int k,
                                  uint32_t* ghist_row, bool hist_ready, int32_t* orow,
                                  int32_t* count, const int32_t* map_a, const int32_t* map_b,
-                                 int map_ld, RowSelLds& L, uint32_t* klist, int& klist_n) {
+                                 int map_ld, RowSelLds& L, uint32_t* klist, int& klist_n,
+                                 uint32_t* min_key = nullptr) {
   const int lane = threadIdx.x & 63, wave = row_wave();
   RowWindow w = row_window(lo_p, hi_p, row / H, L_max);
   bool vec;
@@ -334,6 +380,7 @@ __device__ __forceinline__ void row_select_alone(const float* scores, int row, i
       prepare, for_keys, &T, &need_eq, &k_sel);
 
   int a_base = 0, e_base = 0;   // keys above / equal to T in earlier sweeps
+  uint32_t mk = 0xffffffffu;    // smallest selected key of this lane
   for (int sw = 0; sw < n_sweeps; ++sw) {
     uint32_t kk[kGroups][4];
     if constexpr (RES) {
@@ -357,6 +404,7 @@ __device__ __forceinline__ void row_select_alone(const float* scores, int row, i
         if constexpr (MAP == 0) orow[dst] = p;
         else if constexpr (MAP == 1) L.hist[dst] = (uint32_t)p;
         else orow[dst] = map_b[map_a[(int64_t)row * map_ld + p]];
+        mk = min(mk, kk[g][e]);
       }
     });
     a_base += ta;
@@ -371,6 +419,10 @@ __device__ __forceinline__ void row_select_alone(const float* scores, int row, i
   for (int i = n_sel + threadIdx.x; i < k; i += kRowThreads) orow[i] = -1;
   if (threadIdx.x == 0) count[row] = n_sel;
   if (hist_ready) gh4[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
+  if (min_key) {
+    const uint32_t m = block_min_u32(mk, (uint32_t*)L.wt);
+    if (threadIdx.x == 0) *min_key = m;
+  }
 }
 
 // Grid rows, 1024 threads: rows of one sweep, each selected by its workgroup
@@ -527,6 +579,136 @@ __global__ __launch_bounds__(kRowThreads) void topk_finish_kernel(
   gh4[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);   // zero for the next call
 }
 
+// --------------------------------------------------- prefiltered top-k --
+// Threshold-prefiltered exact top-k (ECHO-OSDI26 wiki page, observation 3 and
+// core method 3: the k-th largest index score of a step moves smoothly, so an
+// EMA with alpha = 0.5 of the past steps' k-th scores predicts the next
+// step's).  The scan listed the window's keys whose score reaches the row's
+// prediction thr[row] (ws.lkey / ws.lpos, count ws.ctr).  If at least k keys
+// survived, the k-th largest key of the row is among them together with every
+// key at or above it, so the exact selection is resolved over the survivors
+// alone: threshold digits over their histogram, equal keys ranked by position
+// through a bitmap of the window, and the output placed in ascending order
+// by prefix popcounts of a second bitmap.  Fewer than k survivors, a list
+// overflow or a window over 131072 slots: the full row is selected by this
+// workgroup, re-reading it per pass.  Either way thr[row] becomes
+// alpha kth + (1 - alpha) thr[row] (kth when thr[row] is -inf; -inf when the
+// window has fewer than k candidates), and the list counter is zeroed.
+constexpr int kMapWords = 4096;   // position bitmaps: windows of up to 131072 slots
+
+template <int MAP>
+__global__ __launch_bounds__(kRowThreads) void topk_survivor_kernel(
+    const float* scores, int H, int L_max, const int32_t* lo_p, const int32_t* hi_p, int k,
+    TopkWs ws, float* thr, float alpha, int32_t* used, int32_t* idx, int32_t* count,
+    const int32_t* map_a, const int32_t* map_b, int map_ld) {
+  __shared__ RowSelLds L;
+  __shared__ uint32_t klist[kListCap];
+  __shared__ int klist_n;
+  __shared__ uint32_t selmap[kMapWords], eqmap[kMapWords];
+  __shared__ int wpre[kMapWords];
+  __shared__ uint32_t s_min;
+  constexpr int kPer = kRowList / kRowThreads;   // survivors per lane
+  const int row = blockIdx.x;
+  int32_t* orow = idx + (int64_t)row * k;
+  const int m = ws.ctr[row];
+  const float thr_old = thr[row];
+  const RowWindow w = row_window(lo_p, hi_p, row / H, L_max);
+  const bool listed = m >= k && m <= kRowList && w.n <= kMapWords * 32;
+  int k_sel;
+  uint32_t mink;
+  if (!listed) {
+    row_select_alone<false, MAP>(scores, row, H, L_max, lo_p, hi_p, k, nullptr, false, orow,
+                                 count, map_a, map_b, map_ld, L, klist, klist_n, &s_min);
+    lds_barrier();
+    mink = s_min;
+    k_sel = count[row];   // written by thread 0, which alone reads it below
+  } else {
+    uint32_t key[kPer];
+    int pos[kPer];
+    const uint32_t* lk = ws.lkey + (int64_t)row * kRowList;
+    const int32_t* lp = ws.lpos + (int64_t)row * kRowList;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int r = kPer * threadIdx.x + u;
+      key[u] = r < m ? lk[r] : 0u;
+      pos[u] = r < m ? lp[r] : 0;
+      if (pos[u] < w.lo || pos[u] >= w.hi) key[u] = 0u;   // only window positions were listed
+    }
+    *(uint4*)(L.hist + 4 * threadIdx.x) = make_uint4(0u, 0u, 0u, 0u);
+    if (threadIdx.x < 256) L.dh[threadIdx.x] = 0u;
+    *(uint4*)(selmap + 4 * threadIdx.x) = make_uint4(0u, 0u, 0u, 0u);
+    *(uint4*)(eqmap + 4 * threadIdx.x) = make_uint4(0u, 0u, 0u, 0u);
+    lds_barrier();
+#pragma unroll
+    for (int u = 0; u < kPer; ++u)
+      if (key[u]) atomicAdd(&L.hist[key[u] >> 20], 1u);
+    lds_barrier();
+    uint32_t T;
+    int need_eq;
+    row_threshold(
+        L, k, []() {},
+        [&](auto&& f) {
+#pragma unroll
+          for (int u = 0; u < kPer; ++u) f(key[u]);
+        },
+        &T, &need_eq, &k_sel);
+    const int W = (w.n + 31) >> 5;
+    // keys equal to T: the first need_eq by position are taken
+    if (need_eq > 0) {
+#pragma unroll
+      for (int u = 0; u < kPer; ++u)
+        if (key[u] != 0u && key[u] == T) {
+          const int b = pos[u] - w.lo;
+          atomicOr(&eqmap[b >> 5], 1u << (b & 31));
+        }
+      lds_barrier();
+      bitmap_prefix(eqmap, wpre, W, L);
+    }
+    bool sel[kPer];
+    uint32_t mk = 0xffffffffu;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int b = pos[u] - w.lo;
+      bool t = key[u] > T;
+      if (!t && need_eq > 0 && key[u] != 0u && key[u] == T)
+        t = wpre[b >> 5] + __popc(eqmap[b >> 5] & ((1u << (b & 31)) - 1u)) < need_eq;
+      sel[u] = t;
+      if (t) {
+        atomicOr(&selmap[b >> 5], 1u << (b & 31));
+        mk = min(mk, key[u]);
+      }
+    }
+    lds_barrier();
+    bitmap_prefix(selmap, wpre, W, L);
+#pragma unroll
+    for (int u = 0; u < kPer; ++u)
+      if (sel[u]) {
+        const int b = pos[u] - w.lo;
+        const int dst = wpre[b >> 5] + __popc(selmap[b >> 5] & ((1u << (b & 31)) - 1u));
+        if (dst < k) {
+          if constexpr (MAP == 0) orow[dst] = pos[u];
+          else if constexpr (MAP == 1) L.hist[dst] = (uint32_t)pos[u];
+          else orow[dst] = map_b[map_a[(int64_t)row * map_ld + pos[u]]];
+        }
+      }
+    if constexpr (MAP == 1) {
+      lds_barrier();
+      for (int i = threadIdx.x; i < k_sel; i += kRowThreads)
+        orow[i] = map_b[map_a[(int64_t)row * map_ld + (int)L.hist[i]]];
+    }
+    for (int i = k_sel + threadIdx.x; i < k; i += kRowThreads) orow[i] = -1;
+    if (threadIdx.x == 0) count[row] = k_sel;
+    mink = block_min_u32(mk, (uint32_t*)L.wt);
+  }
+  if (threadIdx.x == 0) {
+    const float kth = (k_sel >= k && mink != 0xffffffffu) ? key_score(mink) : -INFINITY;
+    thr[row] = (thr_old == -INFINITY || kth == -INFINITY) ? kth
+                                                          : alpha * kth + (1.f - alpha) * thr_old;
+    if (used) used[row] = listed ? 1 : 0;
+    ws.ctr[row] = 0;
+  }
+}
+
 }  // namespace
 
 size_t topk_workspace_bytes(int rows, int L_max) { return TopkWs::bytes(rows, L_max); }
@@ -569,6 +751,19 @@ hipError_t launch_topk(const float* scores, int rows, int H, int L_max, const in
   else
     topk_finish_kernel<2><<<rows, kRowThreads, 0, s>>>(scores, H, L_max, lo, hi, k, ws, ns, idx,
                                                        count, map_a, map_b, map_ld);
+  return hipGetLastError();
+}
+
+bool topk_survivors_supported(int L_max) { return topk_supported(L_max); }
+
+hipError_t launch_topk_survivors(const float* scores, int rows, int H, int L_max,
+                                 const int32_t* lo, const int32_t* hi, int k, int32_t* idx,
+                                 int32_t* count, void* wsp, float* thr, float alpha,
+                                 int32_t* used, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  const TopkWs ws = TopkWs::carve(wsp, rows, L_max);
+  topk_survivor_kernel<0><<<rows, kRowThreads, 0, s>>>(scores, H, L_max, lo, hi, k, ws, thr, alpha,
+                                                       used, idx, count, nullptr, nullptr, 0);
   return hipGetLastError();
 }
 

@@ -69,12 +69,14 @@ def parse():
                     help="distinct device copies of the streamed inputs, used in turn by "
                          "successive steps (like successive layers), so that no step finds "
                          "its data in the 256 MB last-level cache")
-    ap.add_argument("--path", default="fused", choices=("fused", "separate"),
+    ap.add_argument("--path", default="fused", choices=("fused", "separate", "prefilter"),
                     help="dense workloads: fused = sparsekv_score_hist + "
                          "sparsekv_select_attend_resume (top-k fused with the attention); "
                          "separate = sparsekv_score_hist + sparsekv_topk_resume + "
                          "sparsekv_gather_attend (always used where the fused call does not "
-                         "support the shape)")
+                         "support the shape); prefilter = sparsekv_score_prefilter + "
+                         "sparsekv_topk_prefiltered (threshold predicted by the EMA of the "
+                         "previous steps' k-th scores) + sparsekv_gather_attend")
     ap.add_argument("--eager", action="store_true",
                     help="launch every kernel from the host instead of replaying one HIP graph "
                          "that holds the K timed steps")
@@ -285,6 +287,9 @@ def bench_dense(args, hip):
     out = torch.empty((kv.B, kv.H * G, kv.d_v), dtype=torch.float32, device=dev)
     fused = (args.path == "fused" and skv is kv and sG == G and bf and not mla and kv.d_k == 128
              and G <= 8 and L <= 32768)
+    prefilter = args.path == "prefilter"
+    thr = torch.full((B, H), float("-inf"), dtype=torch.float32, device=dev)
+    used = torch.zeros((B, H), dtype=torch.int32, device=dev)
     if fused:
         ws_sel = S.workspace(S.sparsekv_workspace_size(S.SKV_OP_SELECT_ATTEND, kv, G, k), dev)
     else:
@@ -301,10 +306,18 @@ def bench_dense(args, hip):
 
     def step(i, mark):
         s_kv, a_kv = pairs[i % len(pairs)]
-        S.sparsekv_score_hist(s_kv, sq, sG, lo, hi, scores, ws_sel)
+        if prefilter:
+            S.sparsekv_score_prefilter(s_kv, sq, sG, lo, hi, thr, scores, ws_sel)
+        else:
+            S.sparsekv_score_hist(s_kv, sq, sG, lo, hi, scores, ws_sel)
         if mark:
             mark(0)
-        if fused:
+        if prefilter:
+            S.sparsekv_topk_prefiltered(scores, lo, hi, k, thr, idx, cnt, ws_sel, used=used)
+            if mark:
+                mark(1)
+            S.sparsekv_gather_attend(a_kv, q, G, idx, k, lo, hi, st.scale, out, ws_att)
+        elif fused:
             S.sparsekv_select_attend_resume(a_kv, q, G, lo, hi, k, st.scale, scores, idx, cnt, out,
                                             ws_sel)
         else:
@@ -334,12 +347,14 @@ def bench_dense(args, hip):
     step_bytes = scan_bytes + gather_bytes
     scan_s = float(np.mean(calls[:, 0])) * 1e-3
     src = "sparse_top_kv_indexer_amd/csrc/score.hip"
-    kname = ("score_stream_kernel" if (bf and sG >= 2) else "score_valu_kernel")
-    tr = traffic_entry("score_scan_%s_pmc.json" % args.workload, src)
+    kname = ("score_stream_kernel" if (bf and skv.d_k % 32 == 0 and skv.d_k <= 256) else
+             "score_valu_kernel")
+    # the counter record holds the histogram scan; the survivor scan has none
+    tr = None if prefilter else traffic_entry("score_scan_%s_pmc.json" % args.workload, src)
     cfg = {"workload": args.workload, "B": B, "H_kv": kv.H, "G": G, "d": kv.d_k,
            "L": L, "k": k, "layout": st.kv.mode, "kv_dtype": st.kv.dtype,
            "kv_copies": len(pairs), "launch": "eager" if args.eager else "hip_graph",
-           "path": "fused" if fused else "separate"}
+           "path": "fused" if fused else ("prefilter" if prefilter else "separate")}
     if args.workload != "indexer_mla":
         cfg.update(sink=int(st.lo[0]), local=int(st.kv.seq_len[0] - st.hi[0]))
     else:
@@ -357,10 +372,16 @@ def bench_dense(args, hip):
                          "topk": float(np.mean(calls[:, 1])) * 1e3,
                          "gather_attend": float(np.mean(calls[:, 2])) * 1e3}),
         "keys_scanned_per_step": n_keys,
+        **({"prefilter_rows_from_survivors": float(used.float().mean().item()),
+            "prefilter_note": "the same query every step, so after the first step the "
+                              "predicted threshold is the exact k-th score"}
+           if prefilter else {}),
         "step_algorithmic_bytes": step_bytes,
         "step_GBps": step_bytes / (ms_per_step * 1e-3) / 1e9,
         "step_frac_of_hbm_peak": step_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,
-        "roofline": roofline("score scan (sparsekv_score_hist: %s with the fused top-k histogram)"
+        "roofline": roofline(("score scan (sparsekv_score_prefilter: %s listing the keys above "
+                              "the predicted threshold)" if prefilter else
+                              "score scan (sparsekv_score_hist: %s with the fused top-k histogram)")
                              % kname, "hbm", scan_bytes, scan_s, tr,
                              {"algorithmic_bytes_per_launch": scan_bytes, "bytes_per_key": per_key}),
     })

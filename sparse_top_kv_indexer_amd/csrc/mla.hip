@@ -75,11 +75,16 @@ __global__ __launch_bounds__(WAVES * 64) void mla_split_kernel(
     const int32_t* hi_p, float scale_log2, int n_split, float* part) {
   __shared__ __attribute__((aligned(16))) uint16_t rows[kBlock * kRowPad];
   __shared__ int64_t roff[kBlock];
-  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // grid (n_split, H x head groups, B): a workgroup serves WAVES x 16 of the
+  // G query heads; the head groups of a split sit 8-aligned apart in the
+  // dispatch order (n_split is a multiple of 8), so they share an XCD and its
+  // L2 copy of the split's latent rows
+  const int n_hg = G / (16 * WAVES);
+  const int s = blockIdx.x, h = blockIdx.y / n_hg, hg = blockIdx.y - h * n_hg, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g4 = lane >> 4;
-  const int head0 = wave * 16;                    // this wave's first query head
+  const int head0 = (hg * WAVES + wave) * 16;     // this wave's first query head
 
   const int seq = min(kv.seq_len[b], kv.L_max);
   const int lo = max(0, min(lo_p[b], seq));
@@ -220,7 +225,8 @@ __global__ __launch_bounds__(WAVES * 64) void mla_split_kernel(
   }
 }
 
-int mla_splits(int k) { return std::max(1, std::min(64, (k + 63) / 64)); }
+// splits: a multiple of 8 (see the head-group placement), ~64 rows each
+int mla_splits(int k) { return std::max(8, std::min(64, (k + 63) / 64 + 7) / 8 * 8); }
 
 }  // namespace
 
@@ -240,14 +246,16 @@ hipError_t launch_mla_attend(const KvArgs& kv, const void* q, int G, const int32
   const int n_split = mla_splits(k);
   float* part = (float*)ws;
   const float scale_log2 = scale * 1.4426950408889634f;
-  dim3 grid(n_split, kv.H, kv.B);
+  // 32 heads (2 waves) per workgroup, 16 when G = 16
   const uint16_t* qq = (const uint16_t*)q;
-  switch (G / 16) {
-    case 1: mla_split_kernel<1><<<grid, 64, 0, st>>>(kv, qq, G, idx, k, lo, hi, scale_log2, n_split, part); break;
-    case 2: mla_split_kernel<2><<<grid, 128, 0, st>>>(kv, qq, G, idx, k, lo, hi, scale_log2, n_split, part); break;
-    case 4: mla_split_kernel<4><<<grid, 256, 0, st>>>(kv, qq, G, idx, k, lo, hi, scale_log2, n_split, part); break;
-    case 8: mla_split_kernel<8><<<grid, 512, 0, st>>>(kv, qq, G, idx, k, lo, hi, scale_log2, n_split, part); break;
-    default: return hipErrorInvalidValue;
+  if (G == 16) {
+    mla_split_kernel<1><<<dim3(n_split, kv.H, kv.B), 64, 0, st>>>(kv, qq, G, idx, k, lo, hi,
+                                                                  scale_log2, n_split, part);
+  } else if (G == 32 || G == 64 || G == 128) {
+    mla_split_kernel<2><<<dim3(n_split, kv.H * (G / 32), kv.B), 128, 0, st>>>(
+        kv, qq, G, idx, k, lo, hi, scale_log2, n_split, part);
+  } else {
+    return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -14,6 +14,9 @@ dense         exact definition of the step (score every key, exact top-k with
 paris         ParisKV compressed-code retrieval (normalise, SRHT, fixed
               sign-pattern centroids, collision vote, 4-bit rerank, top-k),
               as an exact fp32 operation sequence in numpy.
+blocks        block-summary scoring (per-block coordinate-wise min / max of
+              the keys, Quest's upper bound as the block score, exact top-K
+              blocks, attention over their tokens), float64.
 lloyd         Lloyd-Max levels for |u_j| under the Beta prior, float64.
 closed_forms  byte / capacity formulas the pages state.
 

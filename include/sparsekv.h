@@ -75,7 +75,8 @@ typedef enum {
   SKV_OP_ENCODE = 3,
   SKV_OP_RETRIEVE = 4,
   SKV_OP_SELECT = 5,
-  SKV_OP_SELECT_ATTEND = 6
+  SKV_OP_SELECT_ATTEND = 6,
+  SKV_OP_BLOCK_SELECT = 7
 } skv_op;
 
 /* Caller-owned KV storage (host struct, device pointers). */
@@ -233,6 +234,54 @@ skv_status sparsekv_select_attend_resume(const skv_kv* kv, const void* q, int32_
                                          float* out, void* ws, size_t ws_bytes,
                                          hipStream_t stream);
 
+/* -------------------------------------------------- block-summary scoring --
+ * OasisKV reading notes, section 3.2 (after Quest): each logical 16-token
+ * block keeps, per KV head, the coordinate-wise minimum mn and maximum mx of
+ * its live keys; a query ranks the blocks from these summaries alone (1/8 of
+ * the key bytes of a full scan) and the top K blocks per KV head are
+ * attended.  The page gives no score formula; this library takes Quest's
+ * upper bound of q . k over the block, max over the G query heads of
+ *   sum_i max(q_i mn_i, q_i mx_i) = [max(q,0), min(q,0)] . [mx, mn].
+ *
+ * Summary pool (caller-owned, bf16): the summary of physical block p, KV head
+ * h is the 2 d_k-wide row [mx, mn] at element
+ *   ((p/16)*H + h)*16*2*d_k + (p%16)*2*d_k,
+ * i.e. a pool of ceil(n_blocks/16) 16-row blocks of width 2 d_k;
+ * sparsekv_block_summary_bytes(n_blocks, H, d_k) bytes.  Rows of blocks no
+ * call has summarised are never read.
+ *
+ * sparsekv_block_summarize: (re)builds the summaries of logical blocks
+ * j0 <= j < j1 of sequence b (every KV head) from the keys: the block's live
+ * tokens are 16 j <= t < min(16 j + 16, seq_len[b], L_max); blocks with no
+ * such token or a negative table entry are skipped.  Call it for the blocks
+ * whose tokens changed (while decoding: the last block) before the next
+ * sparsekv_block_select.  Requires a bf16 paged pool with a block table and
+ * d_k in {32, 64, 128}.
+ *
+ * sparsekv_block_select: for every row (b, h),
+ *   blk_scores [B][H][L_max/16] fp32: the bound above for blocks holding a
+ *                live token, -inf elsewhere (written in full);
+ *   blk_idx    [B][H][K] int32: the K best blocks among those lying wholly
+ *                inside [lo[b], hi[b]) (block ceil(lo/16) up to but excluding
+ *                floor(hi/16)), exact, ties to the lower block, ascending,
+ *                -1 padded;  blk_count [B][H] = min(K, finite candidates);
+ *   tok_idx    [B][H][16 K] int32: token 16 blk_idx[u] + e of every chosen
+ *                block u, at 16 u + e, -1 where the token is not live or
+ *                u >= blk_count -- the idx argument (k = 16 K) of
+ *                sparsekv_gather_attend with the same window, which adds the
+ *                sink and local tokens.
+ *   q [B][H*G][d_k] bf16.  Requires bf16 keys in a block-table pool,
+ *   d_k in {32, 64, 128}, 1 <= G <= 16, L_max % 256 == 0.
+ * ws: sparsekv_workspace_size(SKV_OP_BLOCK_SELECT, kv, G, K, NULL) bytes,
+ * zero-filled before its first use (every call leaves it so). */
+size_t sparsekv_block_summary_bytes(int32_t n_blocks, int32_t H, int32_t d_k);
+skv_status sparsekv_block_summarize(const skv_kv* kv, int32_t b, int32_t j0, int32_t j1,
+                                    void* summ, hipStream_t stream);
+skv_status sparsekv_block_select(const skv_kv* kv, const void* summ, const void* q, int32_t G,
+                                 skv_window win, int32_t K, float* blk_scores, int32_t* blk_idx,
+                                 int32_t* blk_count, int32_t* tok_idx, void* ws, size_t ws_bytes,
+                                 hipStream_t stream);
+
 /* --------------------------------------------- compressed-code retrieval --
  * ParisKV close-reading, sections 2.2-2.5: keys and the query are normalised
  * and rotated by one SRHT R = H_d diag(signs) / sqrt(d); each of n_sub
@@ -303,6 +352,7 @@ skv_status sparsekv_retrieve(const skv_codebook* cb, const skv_index* index, con
 
 /* Workspace bytes for an op.  Arguments an op does not use may be NULL / 0:
  *   SCORE, ENCODE: 0;   TOPK, SELECT: kv->B, kv->H, kv->L_max;
+ *   BLOCK_SELECT: kv, G (K is not read);
  *   GATHER_ATTEND: kv, G, k;   RETRIEVE: index, G, k (= k_final) with
  *   beta = 1 (an upper bound); sparsekv_retrieve_workspace_size() takes the
  *   actual beta. */

@@ -29,7 +29,7 @@ LIB_PATH = os.path.join(_HERE, "libsparsekv.so")
 SKV_OK, SKV_EINVAL, SKV_EUNSUPPORTED, SKV_EWORKSPACE, SKV_ELAUNCH = range(5)
 SKV_F32, SKV_BF16 = 0, 1
 (SKV_OP_SCORE, SKV_OP_TOPK, SKV_OP_GATHER_ATTEND, SKV_OP_ENCODE, SKV_OP_RETRIEVE, SKV_OP_SELECT,
- SKV_OP_SELECT_ATTEND) = range(7)
+ SKV_OP_SELECT_ATTEND, SKV_OP_BLOCK_SELECT) = range(8)
 
 c_vp, c_i32, c_f32, c_sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
 
@@ -86,6 +86,10 @@ _SIGS = {
     "sparsekv_select_attend_resume": (c_i32, [ctypes.POINTER(skv_kv), c_vp, c_i32, skv_window,
                                               c_i32, c_f32, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz,
                                               c_vp]),
+    "sparsekv_block_summary_bytes": (c_sz, [c_i32, c_i32, c_i32]),
+    "sparsekv_block_summarize": (c_i32, [ctypes.POINTER(skv_kv), c_i32, c_i32, c_i32, c_vp, c_vp]),
+    "sparsekv_block_select": (c_i32, [ctypes.POINTER(skv_kv), c_vp, c_vp, c_i32, skv_window, c_i32,
+                                      c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "sparsekv_codebook_init": (c_i32, [c_i32, ctypes.POINTER(c_f32), ctypes.POINTER(c_f32)]),
     "sparsekv_encode": (c_i32, [ctypes.POINTER(skv_codebook), ctypes.POINTER(skv_kv), c_i32,
                                 c_i32, c_i32, ctypes.POINTER(skv_index), c_vp]),
@@ -317,6 +321,72 @@ def sparsekv_select_attend_resume(kv: KVTensors, q: torch.Tensor, G: int, lo: to
                                                _ptr(scores), _ptr(idx), _ptr(count), _ptr(out),
                                                _ptr(ws), ws.numel() * ws.element_size(), _stream()))
     return idx, count, out
+
+
+def sparsekv_block_summary_bytes(n_blocks: int, H: int, d_k: int) -> int:
+    return int(lib().sparsekv_block_summary_bytes(n_blocks, H, d_k))
+
+
+def block_summary_pool(kv: KVTensors) -> torch.Tensor:
+    """A summary pool for every physical block of kv's pool (bf16 rows of 2 d_k)."""
+    n_blocks = kv.k.numel() // (kv.H * 16 * kv.d_k)
+    nb = sparsekv_block_summary_bytes(n_blocks, kv.H, kv.d_k)
+    return torch.zeros(nb // 2, dtype=torch.bfloat16, device=kv.k.device)
+
+
+def sparsekv_block_summarize(kv: KVTensors, b: int, j0: int, j1: int, summ: torch.Tensor):
+    """(Re)build the min / max summaries of logical blocks [j0, j1) of sequence b."""
+    _dev(summ, "summ", torch.bfloat16)
+    n_blocks = kv.k.numel() // (kv.H * 16 * kv.d_k)
+    if summ.numel() * 2 < sparsekv_block_summary_bytes(n_blocks, kv.H, kv.d_k):
+        raise ValueError("summ is smaller than the summary pool of kv's blocks")
+    c = kv.c()
+    _check("sparsekv_block_summarize",
+           lib().sparsekv_block_summarize(ctypes.byref(c), b, j0, j1, _ptr(summ), _stream()))
+    return summ
+
+
+def sparsekv_block_select(kv: KVTensors, summ: torch.Tensor, q: torch.Tensor, G: int,
+                          lo: torch.Tensor, hi: torch.Tensor, K: int,
+                          blk_scores: Optional[torch.Tensor] = None,
+                          blk_idx: Optional[torch.Tensor] = None,
+                          blk_count: Optional[torch.Tensor] = None,
+                          tok_idx: Optional[torch.Tensor] = None,
+                          ws: Optional[torch.Tensor] = None):
+    """Block scores from the summaries, the exact top-K blocks and their
+    tokens; returns (blk_scores, blk_idx, blk_count, tok_idx)."""
+    _dev(q, "q", kv.torch_dtype)
+    _dev(summ, "summ", torch.bfloat16)
+    if q.shape != (kv.B, kv.H * G, kv.d_k):
+        raise ValueError("q must be [B][H*G][d_k]")
+    dev = q.device
+    Lb = kv.L_max // 16
+    if blk_scores is None:
+        blk_scores = torch.empty((kv.B, kv.H, Lb), dtype=torch.float32, device=dev)
+    if blk_idx is None:
+        blk_idx = torch.empty((kv.B, kv.H, K), dtype=torch.int32, device=dev)
+    if blk_count is None:
+        blk_count = torch.empty((kv.B, kv.H), dtype=torch.int32, device=dev)
+    if tok_idx is None:
+        tok_idx = torch.empty((kv.B, kv.H, 16 * K), dtype=torch.int32, device=dev)
+    for t, nm, dt, shp in ((blk_scores, "blk_scores", torch.float32, (kv.B, kv.H, Lb)),
+                           (blk_idx, "blk_idx", torch.int32, (kv.B, kv.H, K)),
+                           (blk_count, "blk_count", torch.int32, (kv.B, kv.H)),
+                           (tok_idx, "tok_idx", torch.int32, (kv.B, kv.H, 16 * K))):
+        _dev(t, nm, dt)
+        if tuple(t.shape) != shp:
+            raise ValueError("%s must be %s" % (nm, shp))
+    _dev(lo, "lo", torch.int32)
+    _dev(hi, "hi", torch.int32)
+    if ws is None:
+        ws = workspace(sparsekv_workspace_size(SKV_OP_BLOCK_SELECT, kv, G, K), dev)
+    c = kv.c()
+    _check("sparsekv_block_select",
+           lib().sparsekv_block_select(ctypes.byref(c), _ptr(summ), _ptr(q), G,
+                                       skv_window(_ptr(lo), _ptr(hi)), K, _ptr(blk_scores),
+                                       _ptr(blk_idx), _ptr(blk_count), _ptr(tok_idx), _ptr(ws),
+                                       ws.numel() * ws.element_size(), _stream()))
+    return blk_scores, blk_idx, blk_count, tok_idx
 
 
 def sparsekv_score_hist(kv: KVTensors, q: torch.Tensor, G: int, lo: torch.Tensor,

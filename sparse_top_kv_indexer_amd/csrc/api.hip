@@ -204,6 +204,33 @@ skv_status sparsekv_select_attend_resume(const skv_kv* kv, const void* q, int32_
                                        idx, count, (float*)((char*)ws + th), out, stream));
 }
 
+size_t sparsekv_block_summary_bytes(int32_t n_blocks, int32_t H, int32_t d_k) {
+  if (n_blocks < 1 || H < 1 || d_k < 1) return 0;
+  return (size_t)((n_blocks + 15) / 16) * H * 16 * 2 * d_k * 2;
+}
+
+skv_status sparsekv_block_summarize(const skv_kv* kv, int32_t b, int32_t j0, int32_t j1,
+                                    void* summ, hipStream_t stream) {
+  if (!kv_ok(kv) || !summ || b < 0 || b >= kv->B || j0 < 0 || j1 < j0) return SKV_EINVAL;
+  if (j1 > kv->L_max / 16) return SKV_EINVAL;
+  if (!block_summary_supported(to_args(kv))) return SKV_EUNSUPPORTED;
+  return launched(launch_block_summaries(to_args(kv), b, j0, j1, summ, stream));
+}
+
+skv_status sparsekv_block_select(const skv_kv* kv, const void* summ, const void* q, int32_t G,
+                                 skv_window win, int32_t K, float* blk_scores, int32_t* blk_idx,
+                                 int32_t* blk_count, int32_t* tok_idx, void* ws, size_t ws_bytes,
+                                 hipStream_t stream) {
+  if (!kv_ok(kv) || !summ || !q || !blk_scores || !blk_idx || !blk_count || !tok_idx)
+    return SKV_EINVAL;
+  if (G < 1 || K < 1 || !win.lo || !win.hi) return SKV_EINVAL;
+  const KvArgs a = to_args(kv);
+  if (!block_select_supported(a, G)) return SKV_EUNSUPPORTED;
+  if (!ws || ws_bytes < block_select_ws_bytes(a, G)) return SKV_EWORKSPACE;
+  return launched(launch_block_select(a, summ, q, G, win.lo, win.hi, K, blk_scores, blk_idx,
+                                      blk_count, tok_idx, ws, stream));
+}
+
 size_t sparsekv_workspace_size(skv_op op, const skv_kv* kv, int32_t G, int32_t k,
                                const skv_index* index) {
   switch (op) {
@@ -224,6 +251,9 @@ size_t sparsekv_workspace_size(skv_op op, const skv_kv* kv, int32_t G, int32_t k
       if (!kv_ok(kv) || G < 1 || k < 0) return 0;
       return topk_workspace_bytes(kv->B * kv->H, kv->L_max) +
              select_attend_partial_bytes(to_args(kv), G);
+    case SKV_OP_BLOCK_SELECT:
+      if (!kv_ok(kv) || G < 1) return 0;
+      return block_select_ws_bytes(to_args(kv), G);
   }
   return 0;
 }

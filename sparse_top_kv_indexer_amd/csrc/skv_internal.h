@@ -40,6 +40,18 @@ hipError_t launch_topk_survivors(const float* scores, int rows, int H, int L_max
                                  int32_t* used_list, hipStream_t s);
 bool topk_survivors_supported(int L_max);
 
+// blocks.hip: block-summary scoring (summaries, then scan + exact top-K of
+// blocks + expansion into tokens)
+bool block_summary_supported(const KvArgs& kv);
+bool block_select_supported(const KvArgs& kv, int G);
+size_t block_select_ws_bytes(const KvArgs& kv, int G);
+hipError_t launch_block_summaries(const KvArgs& kv, int b, int j0, int j1, void* summ,
+                                  hipStream_t s);
+hipError_t launch_block_select(const KvArgs& kv, const void* summ, const void* q, int G,
+                               const int32_t* lo, const int32_t* hi, int K, float* blk_scores,
+                               int32_t* blk_idx, int32_t* blk_cnt, int32_t* tok_idx, void* ws,
+                               hipStream_t s);
+
 // topk.hip (workspace layout in skv_topk.h); hist_ready: the row histograms
 // were already accumulated by the producer of the scores.  With map_a set,
 // a selected position p of row r is written as map_b[map_a[r * map_ld + p]].

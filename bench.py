@@ -36,7 +36,8 @@ the per-step time, the roofline entry of the dominant kernel and the CPU
 oracle timed on a bounded sample of the same workload.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--kv-copies C]
-                  [--path fused|separate] [--eager] [--no-cpu-baseline]
+                  [--path fused|separate|prefilter|blocks] [--eager]
+                  [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -69,7 +70,7 @@ def parse():
                     help="distinct device copies of the streamed inputs, used in turn by "
                          "successive steps (like successive layers), so that no step finds "
                          "its data in the 256 MB last-level cache")
-    ap.add_argument("--path", default="fused", choices=("fused", "separate", "prefilter"),
+    ap.add_argument("--path", default="fused", choices=("fused", "separate", "prefilter", "blocks"),
                     help="dense workloads: fused = sparsekv_score_hist + "
                          "sparsekv_select_attend_resume (top-k fused with the attention); "
                          "separate = sparsekv_score_hist + sparsekv_topk_resume + "
@@ -288,6 +289,9 @@ def bench_dense(args, hip):
     fused = (args.path == "fused" and skv is kv and sG == G and bf and not mla and kv.d_k == 128
              and G <= 8 and L <= 32768)
     prefilter = args.path == "prefilter"
+    blocks = args.path == "blocks"
+    if blocks:
+        return bench_blocks(args, hip, st, kv, q, lo, hi)
     thr = torch.full((B, H), float("-inf"), dtype=torch.float32, device=dev)
     used = torch.zeros((B, H), dtype=torch.int32, device=dev)
     if fused:
@@ -396,6 +400,85 @@ def bench_dense(args, hip):
                                               "gathered_bytes": gather_bytes})
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = dense_cpu_baseline(st)
+    return rec
+
+
+def bench_blocks(args, hip, st, kv, q, lo, hi):
+    """Block-summary step: re-summarise the block of each sequence's last
+    token, scan the summaries (Quest's bound per 16-token block), exact top-K
+    blocks (K = k / 16) and their tokens (one call), then gather + attention
+    with sink and local.  The summary pools of the KV copies are built before
+    timing."""
+    import numpy as np
+    import torch
+    import sparse_top_kv_indexer_amd as S
+    dev = q.device
+    B, H, G, L, k = kv.B, kv.H, st.G, kv.L_max, st.k
+    K = k // 16
+    bsc = torch.empty((B, H, L // 16), dtype=torch.float32, device=dev)
+    bidx = torch.empty((B, H, K), dtype=torch.int32, device=dev)
+    bcnt = torch.empty((B, H), dtype=torch.int32, device=dev)
+    tok = torch.empty((B, H, 16 * K), dtype=torch.int32, device=dev)
+    out = torch.empty((B, H * G, kv.d_v), dtype=torch.float32, device=dev)
+    ws_blk = S.workspace(S.sparsekv_workspace_size(S.SKV_OP_BLOCK_SELECT, kv, G, K), dev)
+    ws_att = S.workspace(S.sparsekv_workspace_size(S.SKV_OP_GATHER_ATTEND, kv, G, 16 * K), dev)
+    copies = [kv] + [dataclasses.replace(kv, k=kv.k.clone(), v=kv.v.clone())
+                     for _ in range(max(1, args.kv_copies) - 1)]
+    pools = []
+    for c in copies:
+        summ = S.block_summary_pool(c)
+        for b in range(B):
+            S.sparsekv_block_summarize(c, b, 0, L // 16, summ)
+        pools.append(summ)
+    torch.cuda.synchronize()
+
+    def step(i, mark):
+        c, summ = copies[i % len(copies)], pools[i % len(copies)]
+        # re-summarises each sequence's last block, then scans, selects, expands
+        S.sparsekv_block_select(c, summ, q, G, lo, hi, K, bsc, bidx, bcnt, tok, ws_blk)
+        if mark:
+            mark(0)
+        S.sparsekv_gather_attend(c, q, G, tok, 16 * K, lo, hi, st.scale, out, ws_att)
+        if mark:
+            mark(1)
+
+    wall, gpu_ms, calls, note = timed_steps(step, 2, args, hip)
+    calls = np.array(calls)
+    ms_per_step = wall * 1e3 / args.steps
+    from oracle import dense as D
+    live = [D.live_slots(st.kv, b)[0] for b in range(B)]
+    n_keys = sum(int(t.size) for t in live) * H
+    n_blocks = sum(int(np.unique(t // 16).size) for t in live) * H
+    # per live block row: the [mx, mn] summary, its score and its table entry
+    per_block = 2 * kv.d_k * 2 + 4 + 4
+    scan_bytes = n_blocks * per_block + B * H * G * 2 * kv.d_k * 2
+    tok_np = tok.cpu().numpy()
+    n_att = int((tok_np >= 0).sum())
+    for b in range(B):
+        n_att += int(((live[b] < st.lo[b]) | (live[b] >= st.hi[b])).sum()) * H
+    gather_bytes = n_att * kv.d_k * 2 * 2
+    sel_s = float(np.mean(calls[:, 0])) * 1e-3
+    cfg = {"workload": args.workload, "B": B, "H_kv": H, "G": G, "d": kv.d_k, "L": L,
+           "k": k, "K_blocks": K, "layout": st.kv.mode, "kv_dtype": st.kv.dtype,
+           "kv_copies": len(copies), "launch": "eager" if args.eager else "hip_graph",
+           "path": "blocks", "sink": int(st.lo[0]), "local": int(st.kv.seq_len[0] - st.hi[0])}
+    rec = base_record("history keys ranked/s (block-summary sparse decode step of one layer)",
+                      n_keys / (ms_per_step * 1e-3), "keys/s", args, ms_per_step, "bf16", cfg)
+    rec.update({
+        "us_per_step": ms_per_step * 1e3,
+        "us_per_step_gpu": gpu_ms * 1e3,
+        "timing": note,
+        "us_per_call": {"block_select": float(np.mean(calls[:, 0])) * 1e3,
+                        "gather_attend": float(np.mean(calls[:, 1])) * 1e3},
+        "keys_covered_per_step": n_keys,
+        "live_block_rows_per_step": n_blocks,
+        "tokens_attended_per_step": n_att,
+        "step_algorithmic_bytes": scan_bytes + gather_bytes,
+        "roofline": roofline("block selection (sparsekv_block_select: summary scan, top-K "
+                             "blocks, expansion)", "hbm", scan_bytes, sel_s, None,
+                             {"algorithmic_bytes_per_launch": scan_bytes,
+                              "bytes_per_block_row": per_block}),
+    })
     return rec
 
 

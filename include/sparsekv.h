@@ -258,7 +258,15 @@ skv_status sparsekv_select_attend_resume(const skv_kv* kv, const void* q, int32_
  * sparsekv_block_select.  Requires a bf16 paged pool with a block table and
  * d_k in {32, 64, 128}.
  *
- * sparsekv_block_select: for every row (b, h),
+ * sparsekv_block_summarize_last: the same for the block holding token
+ * min(seq_len[b], L_max) - 1 of every sequence b (none where that is -1): the
+ * one block a decode step's appended token changes, all sequences in one
+ * launch.
+ *
+ * sparsekv_block_select: first brings the summary of the block holding each
+ * sequence's last token up to date (as sparsekv_block_summarize_last, so a
+ * decode step that appended one token per sequence needs no separate
+ * summary call; summ is written there only), then for every row (b, h),
  *   blk_scores [B][H][L_max/16] fp32: the bound above for blocks holding a
  *                live token, -inf elsewhere (written in full);
  *   blk_idx    [B][H][K] int32: the K best blocks among those lying wholly
@@ -277,7 +285,8 @@ skv_status sparsekv_select_attend_resume(const skv_kv* kv, const void* q, int32_
 size_t sparsekv_block_summary_bytes(int32_t n_blocks, int32_t H, int32_t d_k);
 skv_status sparsekv_block_summarize(const skv_kv* kv, int32_t b, int32_t j0, int32_t j1,
                                     void* summ, hipStream_t stream);
-skv_status sparsekv_block_select(const skv_kv* kv, const void* summ, const void* q, int32_t G,
+skv_status sparsekv_block_summarize_last(const skv_kv* kv, void* summ, hipStream_t stream);
+skv_status sparsekv_block_select(const skv_kv* kv, void* summ, const void* q, int32_t G,
                                  skv_window win, int32_t K, float* blk_scores, int32_t* blk_idx,
                                  int32_t* blk_count, int32_t* tok_idx, void* ws, size_t ws_bytes,
                                  hipStream_t stream);

@@ -88,6 +88,7 @@ _SIGS = {
                                               c_vp]),
     "sparsekv_block_summary_bytes": (c_sz, [c_i32, c_i32, c_i32]),
     "sparsekv_block_summarize": (c_i32, [ctypes.POINTER(skv_kv), c_i32, c_i32, c_i32, c_vp, c_vp]),
+    "sparsekv_block_summarize_last": (c_i32, [ctypes.POINTER(skv_kv), c_vp, c_vp]),
     "sparsekv_block_select": (c_i32, [ctypes.POINTER(skv_kv), c_vp, c_vp, c_i32, skv_window, c_i32,
                                       c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "sparsekv_codebook_init": (c_i32, [c_i32, ctypes.POINTER(c_f32), ctypes.POINTER(c_f32)]),
@@ -343,6 +344,18 @@ def sparsekv_block_summarize(kv: KVTensors, b: int, j0: int, j1: int, summ: torc
     c = kv.c()
     _check("sparsekv_block_summarize",
            lib().sparsekv_block_summarize(ctypes.byref(c), b, j0, j1, _ptr(summ), _stream()))
+    return summ
+
+
+def sparsekv_block_summarize_last(kv: KVTensors, summ: torch.Tensor):
+    """(Re)build the summary of the block holding each sequence's last token."""
+    _dev(summ, "summ", torch.bfloat16)
+    n_blocks = kv.k.numel() // (kv.H * 16 * kv.d_k)
+    if summ.numel() * 2 < sparsekv_block_summary_bytes(n_blocks, kv.H, kv.d_k):
+        raise ValueError("summ is smaller than the summary pool of kv's blocks")
+    c = kv.c()
+    _check("sparsekv_block_summarize_last",
+           lib().sparsekv_block_summarize_last(ctypes.byref(c), _ptr(summ), _stream()))
     return summ
 
 

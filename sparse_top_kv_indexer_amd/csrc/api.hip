@@ -217,7 +217,13 @@ skv_status sparsekv_block_summarize(const skv_kv* kv, int32_t b, int32_t j0, int
   return launched(launch_block_summaries(to_args(kv), b, j0, j1, summ, stream));
 }
 
-skv_status sparsekv_block_select(const skv_kv* kv, const void* summ, const void* q, int32_t G,
+skv_status sparsekv_block_summarize_last(const skv_kv* kv, void* summ, hipStream_t stream) {
+  if (!kv_ok(kv) || !summ) return SKV_EINVAL;
+  if (!block_summary_supported(to_args(kv))) return SKV_EUNSUPPORTED;
+  return launched(launch_block_summaries_last(to_args(kv), summ, stream));
+}
+
+skv_status sparsekv_block_select(const skv_kv* kv, void* summ, const void* q, int32_t G,
                                  skv_window win, int32_t K, float* blk_scores, int32_t* blk_idx,
                                  int32_t* blk_count, int32_t* tok_idx, void* ws, size_t ws_bytes,
                                  hipStream_t stream) {

@@ -27,24 +27,27 @@ namespace skv {
 
 namespace {
 
-// Grid (ceil((j1 - j0) / 4), H), 256 threads: one wave per (logical block,
-// head), lane l owning dims 2l, 2l + 1.
-__global__ __launch_bounds__(256) void block_summary_kernel(KvArgs kv, int b, int j0, int j1,
-                                                            uint16_t* summ) {
-  const int h = blockIdx.y;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int j = j0 + blockIdx.x * 4 + wave;
+// Summary row [mx, mn] of logical block j of sequence b, KV head h, by one
+// wave: lane l owns dims 2l, 2l + 1; live tokens are 16 j .. min(16 j + 16,
+// seq_len, L_max) - 1.  Unmapped and empty blocks are left alone.
+__device__ __forceinline__ void summarize_block(const KvArgs& kv, int b, int h, int j,
+                                                uint16_t* summ, int lane) {
   const int d = kv.d_k;
   const int seq = min(kv.seq_len[b], kv.L_max);
-  if (j >= j1 || 16 * j >= seq || 2 * lane >= d) return;
+  if (16 * j >= seq || 2 * lane >= d) return;
   const int p = kv.block_table[(int64_t)b * (kv.L_max >> 4) + j];
-  if (p < 0) return;   // unmapped: its tokens are dead, the block is never scored
+  if (p < 0) return;
   const int nt = min(16, seq - 16 * j);
   const uint16_t* kb = (const uint16_t*)kv.k + ((int64_t)p * kv.H + h) * 16 * d + 2 * lane;
+  // all 16 loads in flight at once; rows past the live ones re-read row 0,
+  // which leaves the extremes unchanged
+  uint32_t w[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) w[e] = *(const uint32_t*)(kb + (int64_t)(e < nt ? e : 0) * d);
   float mx0 = -INFINITY, mx1 = -INFINITY, mn0 = INFINITY, mn1 = INFINITY;
-  for (int e = 0; e < nt; ++e) {
-    const uint32_t w = *(const uint32_t*)(kb + (int64_t)e * d);
-    const float a = bf16_lo(w), c = bf16_hi(w);
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const float a = bf16_lo(w[e]), c = bf16_hi(w[e]);
     mx0 = fmaxf(mx0, a);
     mx1 = fmaxf(mx1, c);
     mn0 = fminf(mn0, a);
@@ -56,26 +59,51 @@ __global__ __launch_bounds__(256) void block_summary_kernel(KvArgs kv, int b, in
       (__float_as_uint(mn0) >> 16) | (__float_as_uint(mn1) & 0xffff0000u);
 }
 
-// Grid B: the block query [max(q, 0), min(q, 0)] of every query head, the
-// candidate block window [ceil(lo / 16), floor(hi / 16)) and the number of
-// blocks holding a token below seq_len.
-__global__ __launch_bounds__(256) void block_prep_kernel(const uint16_t* q, int HG, int d,
+// Grid (ceil((j1 - j0) / 4), H), 256 threads: one wave per (logical block, head).
+__global__ __launch_bounds__(256) void block_summary_kernel(KvArgs kv, int b, int j0, int j1,
+                                                            uint16_t* summ) {
+  const int j = j0 + blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (j < j1) summarize_block(kv, b, blockIdx.y, j, summ, threadIdx.x & 63);
+}
+
+// Grid (B, ceil(H / 4)), 256 threads: the block holding each sequence's last
+// token (the one a decode step has just appended), one wave per head.
+__global__ __launch_bounds__(256) void block_summary_last_kernel(KvArgs kv, uint16_t* summ) {
+  const int b = blockIdx.x, h = blockIdx.y * 4 + (threadIdx.x >> 6);
+  const int seq = min(kv.seq_len[b], kv.L_max);
+  if (h < kv.H && seq > 0) summarize_block(kv, b, h, (seq - 1) >> 4, summ, threadIdx.x & 63);
+}
+
+// Grid (B, ceil(H / 4)), 256 threads, before the scan of sequence b:
+// wave w re-summarises, for KV head h = 4 blockIdx.y + w, the block holding
+// the sequence's last token (the one a decode step has just appended);
+// the workgroup writes the block queries [max(q, 0), min(q, 0)] of these
+// heads' G query heads; and workgroup (b, 0) the candidate block window
+// [ceil(lo / 16), floor(hi / 16)) and the number of blocks below seq_len.
+__global__ __launch_bounds__(256) void block_prep_kernel(KvArgs kv, uint16_t* summ,
+                                                         const uint16_t* q, int G,
                                                          const int32_t* lo, const int32_t* hi,
-                                                         const int32_t* seq_len, int L_max,
                                                          uint16_t* q2, int32_t* lob, int32_t* hib,
                                                          int32_t* seqb) {
-  const int b = blockIdx.x;
-  for (int i = threadIdx.x; i < HG * d; i += blockDim.x) {
-    const int r = i / d, c = i - r * d;
-    const uint16_t v = q[((int64_t)b * HG + r) * d + c];
-    const bool neg = v & 0x8000u;
-    uint16_t* row = q2 + ((int64_t)b * HG + r) * 2 * d;
-    row[c] = neg ? (uint16_t)0 : v;
-    row[d + c] = neg ? v : (uint16_t)0;
+  const int b = blockIdx.x, h0 = blockIdx.y * 4;
+  const int d = kv.d_k;
+  const int s = min(kv.seq_len[b], kv.L_max);
+  const int h = h0 + (threadIdx.x >> 6);
+  if (h < kv.H && s > 0) summarize_block(kv, b, h, (s - 1) >> 4, summ, threadIdx.x & 63);
+  // query rows (b, h0 G) .. (b, min(h0 + 4, H) G - 1), two dims per thread
+  const int n_pairs = (min(h0 + 4, kv.H) - h0) * G * (d / 2);
+  const int64_t r0 = (int64_t)b * kv.H * G + (int64_t)h0 * G;
+  for (int i = threadIdx.x; i < n_pairs; i += blockDim.x) {
+    const int r = i / (d / 2), c = 2 * (i - r * (d / 2));
+    const uint32_t v = *(const uint32_t*)(q + (r0 + r) * d + c);
+    // per bf16 half: sign bit set -> negative (or -0) part, else positive part
+    const uint32_t neg = ((v >> 15) & 1u) * 0xffffu | ((v >> 31) & 1u) * 0xffff0000u;
+    uint16_t* row = q2 + (r0 + r) * 2 * d;
+    *(uint32_t*)(row + c) = v & ~neg;
+    *(uint32_t*)(row + d + c) = v & neg;
   }
-  if (threadIdx.x == 0) {
-    const int s = min(seq_len[b], L_max);
-    const int l = max(0, min(lo[b], L_max)), e = max(l, min(hi[b], L_max));
+  if (blockIdx.y == 0 && threadIdx.x == 0) {
+    const int l = max(0, min(lo[b], kv.L_max)), e = max(l, min(hi[b], kv.L_max));
     const int lb = (l + 15) / 16;
     lob[b] = lb;
     hib[b] = max(lb, e / 16);
@@ -159,15 +187,20 @@ hipError_t launch_block_summaries(const KvArgs& kv, int b, int j0, int j1, void*
   return hipGetLastError();
 }
 
-hipError_t launch_block_select(const KvArgs& kv, const void* summ, const void* q, int G,
+hipError_t launch_block_summaries_last(const KvArgs& kv, void* summ, hipStream_t s) {
+  block_summary_last_kernel<<<dim3(kv.B, (kv.H + 3) / 4), 256, 0, s>>>(kv, (uint16_t*)summ);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_select(const KvArgs& kv, void* summ, const void* q, int G,
                                const int32_t* lo, const int32_t* hi, int K, float* blk_scores,
                                int32_t* blk_idx, int32_t* blk_cnt, int32_t* tok_idx, void* ws,
                                hipStream_t s) {
   BlockWs w;
   BlockWs::layout(&w, (char*)ws, kv, G);
   const int rows = kv.B * kv.H, Lb = kv.L_max / 16;
-  block_prep_kernel<<<kv.B, 256, 0, s>>>((const uint16_t*)q, kv.H * G, kv.d_k, lo, hi, kv.seq_len,
-                                         kv.L_max, w.q2, w.lob, w.hib, w.seqb);
+  block_prep_kernel<<<dim3(kv.B, (kv.H + 3) / 4), 256, 0, s>>>(
+      kv, (uint16_t*)summ, (const uint16_t*)q, G, lo, hi, w.q2, w.lob, w.hib, w.seqb);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // the summary pool scanned like a key pool: logical block j of sequence b is

@@ -47,7 +47,8 @@ bool block_select_supported(const KvArgs& kv, int G);
 size_t block_select_ws_bytes(const KvArgs& kv, int G);
 hipError_t launch_block_summaries(const KvArgs& kv, int b, int j0, int j1, void* summ,
                                   hipStream_t s);
-hipError_t launch_block_select(const KvArgs& kv, const void* summ, const void* q, int G,
+hipError_t launch_block_summaries_last(const KvArgs& kv, void* summ, hipStream_t s);
+hipError_t launch_block_select(const KvArgs& kv, void* summ, const void* q, int G,
                                const int32_t* lo, const int32_t* hi, int K, float* blk_scores,
                                int32_t* blk_idx, int32_t* blk_cnt, int32_t* tok_idx, void* ws,
                                hipStream_t s);

@@ -169,3 +169,27 @@ def test_blocks_rejects_unsupported():
     with pytest.raises(S.SkvError) as e:      # block range past the table
         S.sparsekv_block_summarize(kv_d, 0, 0, 2064 // 16 + 1, summ)
     assert e.value.status == S.SKV_EINVAL
+
+
+def test_blocks_summarize_last_follows_decode_appends():
+    """One token appended per step to every sequence (across a block edge):
+    re-summarising the block of each sequence's last token keeps the pool
+    equal to the oracle's summaries of the grown history."""
+    st = W.make_gqa_paged(tag=985, B=3, H=5, G=1, d=64, L=512, k=32, sink=4, local=16,
+                          seq_len=[62, 15, 300])
+    kv_d = S.kv_to_device(st.kv, DEV)
+    summ = _summarize_all(kv_d, st)
+    lens = st.kv.seq_len.astype(np.int32).copy()
+    for _ in range(4):
+        lens = lens + 1
+        kv_d.seq_len.copy_(torch.from_numpy(lens))
+        S.sparsekv_block_summarize_last(kv_d, summ)
+    torch.cuda.synchronize()
+    st.kv.seq_len = lens
+    for b in range(3):
+        for h in range(5):
+            got = _summary_rows(summ, st, b, h)
+            mn, mx, live = BL.block_summaries(st.kv, b, h)
+            for j in np.nonzero(live)[0]:
+                assert np.array_equal(got[j][0], mx[j]), (b, h, j)
+                assert np.array_equal(got[j][1], mn[j]), (b, h, j)

@@ -17,6 +17,9 @@ paris         ParisKV compressed-code retrieval (normalise, SRHT, fixed
 blocks        block-summary scoring (per-block coordinate-wise min / max of
               the keys, Quest's upper bound as the block score, exact top-K
               blocks, attention over their tokens), float64.
+update        the compressed path's Update Buffer (full buffers move into
+              Local, the Local tokens they push out are encoded into the
+              index) and its multi-step decode loop.
 lloyd         Lloyd-Max levels for |u_j| under the Beta prior, float64.
 closed_forms  byte / capacity formulas the pages state.
 

@@ -322,6 +322,14 @@ def make_paris(tag=5, H=8, G=4, d=128, L=1048576, n_sub=16, sink=4, local=512, r
                  local, rho, beta, k_final, 1.0 / np.sqrt(d))
 
 
+def paris_step_queries(p: Paris, steps: int, tag=5) -> np.ndarray:
+    """Per-step query heads for a multi-step decode over a Paris workload:
+    [steps][H*G][d] bf16 ~ N(0,1), drawn from the query stream after the
+    workload's own query."""
+    hg = p.H * p.G
+    return normal_bf16(seed_of(tag), S_Q, (steps, hg, p.d), offset=hg * p.d)
+
+
 # Full-size workloads by id (1..5), as measured in the bench and the
 # full-size parity tests.
 FULL = {

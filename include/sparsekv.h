@@ -328,6 +328,27 @@ skv_status sparsekv_codebook_init(int32_t m, float levels[8], float thresh[7]);
 skv_status sparsekv_encode(const skv_codebook* cb, const skv_kv* kv, int32_t b, int32_t t0,
                            int32_t t1, skv_index* index, hipStream_t stream);
 
+/* Update buffer of the compressed path (ParisKV close-reading, section 2.5).
+ * The history of sequence b is laid out as
+ *   Sink [0, sink) | Retrieval [sink, sink + index->n) (encoded in the index)
+ *   | Local (`local` tokens) | Update buffer (the newest tokens)
+ * and Sink, Local and the buffer are attended densely.  New tokens enter the
+ * buffer; when it holds `update` tokens they join Local, and the `update`
+ * oldest Local tokens are encoded into the index (the page amortises index
+ * updates this way, with update = 256 or 512).  Call this after appending
+ * tokens, with the sequence's new length seq_len (host value; the device
+ * seq_len[b] must already hold it): it applies the rule for every full buffer
+ * (seq_len - sink - index->n >= local + update), appending the tokens
+ * [sink + index->n, sink + index->n + f * update) as sparsekv_encode does, and
+ * writes f to *flushed (host, may be NULL).  The retrieval window for
+ * sparsekv_gather_attend is then lo = sink, hi = sink + index->n.  The index
+ * must hold exactly positions [sink, sink + index->n) of sequence b.
+ * Errors as sparsekv_encode; SKV_EINVAL also when seq_len < sink + index->n
+ * or update < 1 (nothing is encoded then). */
+skv_status sparsekv_update_buffer(const skv_codebook* cb, const skv_kv* kv, int32_t b,
+                                  int32_t seq_len, int32_t sink, int32_t local, int32_t update,
+                                  skv_index* index, int32_t* flushed, hipStream_t stream);
+
 /* Optional intermediate outputs of a retrieval (device arrays, NULL = skip). */
 typedef struct {
   uint8_t* votes;               /* [H][n] collision score S_i (0..6*n_sub)   */
@@ -353,7 +374,11 @@ typedef struct {
  *   idx    [H][k_final] int32 logical positions (index->pos of the winners),
  *          ascending; -1 past n_cand
  *   n_cand [H] int32 = min(k_final, C)
- * Requires rho >= beta > 0, d = 128, m = 8. */
+ * Requires rho >= beta > 0, d = 128, m = 8.
+ * ws: sparsekv_retrieve_workspace_size(index, G, beta, k_final) bytes for the
+ * largest index->n it will serve, zero-filled once; the regions kept zero
+ * between calls sit at fixed offsets, so an index that grows between calls
+ * (sparsekv_update_buffer) keeps its workspace. */
 skv_status sparsekv_retrieve(const skv_codebook* cb, const skv_index* index, const void* q,
                              int32_t G, double rho, double beta, int32_t k_final, int32_t* idx,
                              int32_t* n_cand, const skv_retrieve_trace* trace, void* ws,

@@ -94,6 +94,9 @@ _SIGS = {
     "sparsekv_codebook_init": (c_i32, [c_i32, ctypes.POINTER(c_f32), ctypes.POINTER(c_f32)]),
     "sparsekv_encode": (c_i32, [ctypes.POINTER(skv_codebook), ctypes.POINTER(skv_kv), c_i32,
                                 c_i32, c_i32, ctypes.POINTER(skv_index), c_vp]),
+    "sparsekv_update_buffer": (c_i32, [ctypes.POINTER(skv_codebook), ctypes.POINTER(skv_kv), c_i32,
+                                       c_i32, c_i32, c_i32, c_i32, ctypes.POINTER(skv_index),
+                                       ctypes.POINTER(c_i32), c_vp]),
     "sparsekv_retrieve": (c_i32, [ctypes.POINTER(skv_codebook), ctypes.POINTER(skv_index), c_vp,
                                   c_i32, ctypes.c_double, ctypes.c_double, c_i32, c_vp, c_vp,
                                   ctypes.POINTER(skv_retrieve_trace), c_vp, c_sz, c_vp]),
@@ -567,6 +570,22 @@ def sparsekv_encode(cb: Codebook, kv: KVTensors, b: int, t0: int, t1: int, index
                                                      ctypes.byref(ic), _stream()))
     index.n = ic.n
     return index
+
+
+def sparsekv_update_buffer(cb: Codebook, kv: KVTensors, b: int, seq_len: int, sink: int,
+                           local: int, update: int, index: IndexTensors) -> int:
+    """Apply the update-buffer rule after appends (seq_len = the sequence's new
+    length, already in kv.seq_len[b] on the device); returns the number of
+    buffers flushed into the index."""
+    c = cb.c()
+    kc = kv.c()
+    ic = index.c()
+    f = c_i32(0)
+    _check("sparsekv_update_buffer",
+           lib().sparsekv_update_buffer(ctypes.byref(c), ctypes.byref(kc), b, seq_len, sink, local,
+                                        update, ctypes.byref(ic), ctypes.byref(f), _stream()))
+    index.n = ic.n
+    return int(f.value)
 
 
 def sparsekv_retrieve(cb: Codebook, index: IndexTensors, q: torch.Tensor, G: int, rho: float,

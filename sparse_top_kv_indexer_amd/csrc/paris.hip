@@ -602,8 +602,8 @@ __global__ void empty_kernel(int k_final, int32_t* idx, int32_t* n_cand) {
 // workspace of a retrieval; the zero-kept part of the top-k workspace and
 // the vote totals are zero when a call starts and are left zero
 struct RetrieveWs {
+  int32_t* tot_ge;    // [H][98]: #(S >= v) over all entries (kept zero)
   void* topk;         // top-k workspace (its first region is kept zero)
-  int32_t* tot_ge;    // [H][98]: #(S >= v) over all entries
   uint32_t* lut;      // [H][16][256] packed tier weights of the G query heads
   float* qt;          // [Hq][128]
   float* qn;          // [Hq]
@@ -623,8 +623,11 @@ struct RetrieveWs {
       o += al(bytes);
       return p;
     };
-    void* tk = take(topk_workspace_bytes(H, std::max(C, 1)));
+    // the regions kept zero between calls (the vote totals, then the top-k
+    // workspace's own) come first, at offsets that do not depend on n or C,
+    // so one workspace serves an index that grows between calls
     int32_t* tot = (int32_t*)take((size_t)H * kGe * 4);
+    void* tk = take(topk_workspace_bytes(H, std::max(C, 1)));
     uint32_t* lut = (uint32_t*)take((size_t)H * kSub * kCent * 4);
     float* qt = (float*)take((size_t)Hq * kD * 4);
     float* qn = (float*)take((size_t)Hq * 4);
@@ -714,6 +717,22 @@ skv_status sparsekv_encode(const skv_codebook* cb, const skv_kv* kv, int32_t b, 
   if (hipGetLastError() != hipSuccess) return SKV_ELAUNCH;
   index->n += n_keys;
   return SKV_OK;
+}
+
+skv_status sparsekv_update_buffer(const skv_codebook* cb, const skv_kv* kv, int32_t b,
+                                  int32_t seq_len, int32_t sink, int32_t local, int32_t update,
+                                  skv_index* index, int32_t* flushed, hipStream_t stream) {
+  if (!kv || !index) return SKV_EINVAL;
+  if (sink < 0 || local < 0 || update < 1 || seq_len < 0 || seq_len > kv->L_max) return SKV_EINVAL;
+  const int64_t end = (int64_t)sink + index->n;   // retrieval region [sink, end)
+  if (seq_len < end) return SKV_EINVAL;
+  // whole buffers of `update` tokens that are full move into Local; as many
+  // of the oldest Local tokens move on into the index
+  const int64_t tail = seq_len - end;
+  const int64_t n_buf = tail >= (int64_t)local + update ? (tail - local) / update : 0;
+  if (flushed) *flushed = (int32_t)n_buf;
+  if (n_buf == 0) return SKV_OK;
+  return sparsekv_encode(cb, kv, b, (int32_t)end, (int32_t)(end + n_buf * update), index, stream);
 }
 
 size_t sparsekv_retrieve_workspace_size(const skv_index* index, int32_t G, double beta,

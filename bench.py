@@ -56,14 +56,17 @@ sys.path.insert(0, HERE)
 PEAK_HBM_GBPS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 DENSE = ("gqa_paged", "token_pool", "single_head", "indexer_mla")
-WORKLOADS = DENSE + ("paris", "paris_encode")
+WORKLOADS = DENSE + ("paris", "paris_encode", "paris_decode")
+PARIS_UPDATE = 512      # Update Buffer tokens (the page's experiments use 256 or 512)
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 50; paris_decode: 4 x 512, one Update Buffer "
+                         "cycle of each of the four layers)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 10; paris_decode 16)")
     ap.add_argument("--workload", default="gqa_paged", choices=WORKLOADS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kv-copies", type=int, default=4,
@@ -83,7 +86,13 @@ def parse():
                          "that holds the K timed steps")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
-    return ap.parse_args()
+    args = ap.parse_args()
+    decode = args.workload == "paris_decode"
+    if args.steps is None:
+        args.steps = 4 * PARIS_UPDATE if decode else 50
+    if args.warmup is None:
+        args.warmup = 16 if decode else 10
+    return args
 
 
 class HipEvents:
@@ -611,6 +620,127 @@ def bench_paris(args, hip):
     return rec
 
 
+def bench_paris_decode(args, hip):
+    """Multi-step decode over the compressed path with the Update Buffer.
+    Four layers (index and KV copies) append the same token each decode
+    step; a timed step is one layer's work: sparsekv_update_buffer (encodes
+    512 tokens into that layer's index when its buffer is full, else nothing),
+    sparsekv_retrieve over the index as it stands, sparsekv_gather_attend
+    over retrieved + sink + Local + buffer.  The prefill leaves the buffers
+    so that every layer flushes once inside the timed steps; launched eagerly
+    (the flush is a host decision and the index grows between steps)."""
+    import numpy as np
+    import torch
+    import sparse_top_kv_indexer_amd as S
+    import workloads as W
+    dev = torch.device("cuda:0")
+    p = W.make_paris()
+    U = PARIS_UPDATE
+    n_layers = max(1, args.kv_copies)
+    total = args.warmup + args.steps
+    n_tok = (total + n_layers - 1) // n_layers          # tokens appended per layer
+    cap = p.L - p.sink - p.local
+    # the decode starts from an earlier step's state: the buffer already
+    # holds b0 tokens, chosen so that the token appended in the middle of the
+    # timed steps fills it
+    t_flush = (args.warmup + args.steps // 2) // n_layers + 1
+    b0 = max(0, U - t_flush) % U
+    L0 = p.L - n_tok
+    n0 = L0 - p.sink - p.local - b0
+    assert n0 > 0 and n0 + U * ((n_tok + b0) // U) <= cap, "decode does not fit"
+    cb = S.new_codebook(torch.from_numpy(p.signs).to(dev))
+    kv0 = S.kv_to_device(p.kv(), dev)
+    seqs = torch.arange(L0 + 1, L0 + 1 + n_tok, dtype=torch.int32, device=dev)
+    kvs = [kv0] + [dataclasses.replace(kv0, k=kv0.k.clone(), v=kv0.v.clone())
+                   for _ in range(n_layers - 1)]
+    idxs = []
+    for c in kvs:
+        ix = S.new_index(p.H, cap, device=dev)
+        c.seq_len.fill_(L0)
+        S.sparsekv_encode(cb, c, 0, p.sink, p.sink + n0, ix)
+        idxs.append(ix)
+    # per-token retrieval end (host rule, the same for every layer) and its device copy
+    n_of = []
+    n = n0
+    for j in range(n_tok):
+        seq = L0 + 1 + j
+        if seq - (p.sink + n) >= p.local + U:
+            n += U * ((seq - p.sink - n - p.local) // U)
+        n_of.append(n)
+    his = torch.tensor([p.sink + x for x in n_of], dtype=torch.int32, device=dev)
+    lo = torch.tensor([p.sink], dtype=torch.int32, device=dev)
+    q = S.to_device(p.q, dev, bf16=True)
+    qa = q.view(1, p.H * p.G, p.d)
+    ridx = torch.empty((p.H, p.k_final), dtype=torch.int32, device=dev)
+    ncand = torch.empty((p.H,), dtype=torch.int32, device=dev)
+    out = torch.empty((1, p.H * p.G, p.d), dtype=torch.float32, device=dev)
+    ws_r = S.workspace(S.retrieve_workspace_size(dataclasses.replace(idxs[0], n=cap), p.G, p.beta,
+                                                 p.k_final), dev)
+    ws_a = S.workspace(S.sparsekv_workspace_size(S.SKV_OP_GATHER_ATTEND, kv0, p.G, p.k_final), dev)
+    torch.cuda.synchronize()
+    state = {"call": 0, "flushes": 0, "flush_calls": []}
+
+    def step(i, mark):
+        c = state["call"]
+        state["call"] += 1
+        layer, j = c % n_layers, c // n_layers
+        kv = dataclasses.replace(kvs[layer], seq_len=seqs[j:j + 1])
+        f = S.sparsekv_update_buffer(cb, kv, 0, L0 + 1 + j, p.sink, p.local, U, idxs[layer])
+        assert idxs[layer].n == n_of[j]
+        if f:
+            state["flushes"] += f
+            state["flush_calls"].append((c, i))
+        if mark:
+            mark(0)
+        S.sparsekv_retrieve(cb, idxs[layer], q, p.G, p.rho, p.beta, p.k_final, idx=ridx,
+                            n_cand=ncand, ws=ws_r)
+        if mark:
+            mark(1)
+        S.sparsekv_gather_attend(kv, qa, p.G, ridx.view(1, p.H, -1), p.k_final, lo,
+                                 his[j:j + 1], p.scale, out, ws_a)
+        if mark:
+            mark(2)
+
+    args.eager = True
+    wall, gpu_ms, calls, note = timed_steps(step, 3, args, hip)
+    calls = np.array(calls)
+    ms = wall * 1e3 / args.steps
+    timed = [i for (c, i) in state["flush_calls"] if c >= args.warmup]
+    t_flush_us = float(np.mean(calls[timed, 0])) * 1e3 if timed else None
+    keys = p.H * float(np.mean([n_of[(args.warmup + i) // n_layers] for i in range(args.steps)]))
+    t_ret = float(np.mean(calls[:, 1])) * 1e-3
+    C = int(math.ceil(p.beta * keys / p.H))
+    ret_bytes = keys * 16 + p.H * C * 128
+    no_flush = [i for i in range(args.steps) if i not in set(timed)]
+    step_no_flush_us = float(np.mean(calls[no_flush].sum(axis=1))) * 1e3
+    rec = base_record("history keys voted/s (compressed-code decode loop with the Update Buffer)",
+                      keys / (ms * 1e-3), "keys/s", args, ms, "u8/f32",
+                      {"workload": "paris_decode", "B": 1, "H_kv": p.H, "G": p.G, "d": p.d,
+                       "L": p.L, "start_len": L0, "n_start": n0, "buffer_start": b0,
+                       "update": U, "beta": p.beta,
+                       "rho": p.rho, "k_final": p.k_final, "sink": p.sink, "local": p.local,
+                       "layers": n_layers, "tokens_appended": n_tok, "launch": "eager"})
+    rec.update({
+        "us_per_step": ms * 1e3, "us_per_step_gpu": gpu_ms * 1e3, "timing": note,
+        "us_per_call": {"update_buffer_flush": t_flush_us,
+                        "retrieve": t_ret * 1e6,
+                        "gather_attend": float(np.mean(calls[:, 2])) * 1e3},
+        "flushes_in_timed_steps": len(timed),
+        "us_per_step_without_flush": step_no_flush_us,
+        "us_per_layer_token_amortised": (step_no_flush_us + (t_flush_us or 0.0) / U),
+        "roofline": roofline("retrieval (sparsekv_retrieve over the growing index)", "hbm",
+                             ret_bytes, t_ret, None, {"algorithmic_bytes_per_launch": ret_bytes}),
+    })
+    if t_flush_us:
+        enc_bytes = p.H * U * (256 + 16 + 64 + 64)
+        rec["roofline_flush"] = roofline("flush (sparsekv_update_buffer: encode_kernel over 512 "
+                                         "tokens x 8 heads)", "hbm", enc_bytes, t_flush_us * 1e-6,
+                                         None, {"algorithmic_bytes_per_launch": enc_bytes})
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = paris_cpu_baseline()
+    return rec
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -632,7 +762,12 @@ def main():
         print(json.dumps({"calib_copy_bytes": n, "launches": 5}))
         return
     hip = HipEvents()
-    rec = bench_dense(args, hip) if args.workload in DENSE else bench_paris(args, hip)
+    if args.workload in DENSE:
+        rec = bench_dense(args, hip)
+    elif args.workload == "paris_decode":
+        rec = bench_paris_decode(args, hip)
+    else:
+        rec = bench_paris(args, hip)
     print(json.dumps(rec))
 
 

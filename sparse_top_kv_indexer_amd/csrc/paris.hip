@@ -38,7 +38,7 @@ constexpr int kD = 128, kSub = 16, kM = 8, kCent = 256;
 constexpr int kVoteBins = 6 * kSub + 1;   // S in [0, 96]
 constexpr int kGe = kVoteBins + 1;        // suffix counts #(S >= v), v = 0..97
 constexpr int kChunk = 8192;              // index entries per vote / compaction workgroup
-constexpr int kEncPerWG = 2048;           // keys per encode workgroup
+constexpr int kEncPerWG = 2048;           // most keys per encode workgroup
 
 struct CodebookArgs {
   float levels[8];
@@ -141,19 +141,28 @@ __device__ __forceinline__ void load_row8(const KvArgs& kv, int b, int h, int t,
 }
 
 // ------------------------------------------------------------------ encode --
+// Grid (ceil(n_keys / per_wg), H): a workgroup encodes per_wg keys of one
+// head, 16 lanes per key.  Large appends (per_wg = 2048) count centroid ids
+// in LDS and add the counts once per workgroup; small ones (an Update Buffer
+// flush: per_wg <= 64, many workgroups with a few keys each) add each key's
+// 16 ids straight to the index histogram.
 __global__ __launch_bounds__(256) void encode_kernel(KvArgs kv, int b, int t0, int n_keys, int n0,
-                                                     int cap, const int8_t* signs, CodebookArgs cb,
-                                                     uint8_t* ids, uint8_t* codes, float* w,
-                                                     int32_t* hist, int32_t* pos) {
+                                                     int cap, int per_wg, const int8_t* signs,
+                                                     CodebookArgs cb, uint8_t* ids, uint8_t* codes,
+                                                     float* w, int32_t* hist, int32_t* pos) {
   __shared__ uint32_t lh[kSub * kCent];
   const int h = blockIdx.y;
   const int j = threadIdx.x & 15, grp = threadIdx.x >> 4;
-  for (int i = threadIdx.x; i < kSub * kCent; i += 256) lh[i] = 0u;
-  __syncthreads();
+  const bool direct = per_wg <= 64;
+  int32_t* gh = hist + (int64_t)h * kSub * kCent;
+  if (!direct) {
+    for (int i = threadIdx.x; i < kSub * kCent; i += 256) lh[i] = 0u;
+    __syncthreads();
+  }
   float sg[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) sg[e] = (float)signs[8 * j + e];
-  const int k0 = blockIdx.x * kEncPerWG, k1 = min(n_keys, k0 + kEncPerWG);
+  const int k0 = blockIdx.x * per_wg, k1 = min(n_keys, k0 + per_wg);
   for (int key = k0 + grp; key < k1; key += 16) {
     const int t = t0 + key;
     float x[8];
@@ -190,11 +199,14 @@ __global__ __launch_bounds__(256) void encode_kernel(KvArgs kv, int b, int t0, i
     ids[ent * kSub + j] = (uint8_t)id;
     ((uint32_t*)codes)[ent * kSub + j] = code;
     w[ent * kSub + j] = wv;
-    atomicAdd(&lh[j * kCent + id], 1u);
+    if (direct)
+      atomicAdd(&gh[j * kCent + id], 1);
+    else
+      atomicAdd(&lh[j * kCent + id], 1u);
     if (h == 0 && j == 0) pos[n0 + key] = t;
   }
+  if (direct) return;
   __syncthreads();
-  int32_t* gh = hist + (int64_t)h * kSub * kCent;
   for (int i = threadIdx.x; i < kSub * kCent; i += 256)
     if (lh[i]) atomicAdd(&gh[i], (int32_t)lh[i]);
 }
@@ -710,10 +722,14 @@ skv_status sparsekv_encode(const skv_codebook* cb, const skv_kv* kv, int32_t b, 
   a.block_table = kv->block_table;
   a.token_table = nullptr;
   a.seq_len = kv->seq_len;
-  dim3 grid((n_keys + kEncPerWG - 1) / kEncPerWG, kv->H);
-  encode_kernel<<<grid, 256, 0, stream>>>(a, b, t0, n_keys, index->n, index->cap, cb->signs,
-                                          cb_args(cb), index->ids, index->codes, index->w,
-                                          index->hist, index->pos);
+  // about 512 workgroups or more: 16 keys each for an Update Buffer flush,
+  // up to 2048 for a prefill
+  const int64_t want = ((int64_t)n_keys * kv->H + 511) / 512;
+  const int per_wg = (int)std::min<int64_t>(kEncPerWG, std::max<int64_t>(16, (want + 15) / 16 * 16));
+  dim3 grid((n_keys + per_wg - 1) / per_wg, kv->H);
+  encode_kernel<<<grid, 256, 0, stream>>>(a, b, t0, n_keys, index->n, index->cap, per_wg,
+                                          cb->signs, cb_args(cb), index->ids, index->codes,
+                                          index->w, index->hist, index->pos);
   if (hipGetLastError() != hipSuccess) return SKV_ELAUNCH;
   index->n += n_keys;
   return SKV_OK;

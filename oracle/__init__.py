@@ -20,6 +20,10 @@ blocks        block-summary scoring (per-block coordinate-wise min / max of
 update        the compressed path's Update Buffer (full buffers move into
               Local, the Local tokens they push out are encoded into the
               index) and its multi-step decode loop.
+compact       token-table compaction: waste ratio, relocation plan (threshold,
+              headroom, net-freeing gates), applying moves, and the I1 / I2
+              checks (a position-independent hash of the retained tokens,
+              duplicate-slot counts).
 lloyd         Lloyd-Max levels for |u_j| under the Beta prior, float64.
 closed_forms  byte / capacity formulas the pages state.
 

@@ -249,21 +249,23 @@ def make_gqa_paged(tag=2, B=4, H=8, G=4, d=128, L=32768, k=2048, sink=4, local=6
 
 
 def make_token_pool(tag=3, B=32, H=8, d=128, L=65536, k=2048, sink=4, local=128,
-                    dead_frac=0.5) -> Step:
+                    dead_frac=0.5, spare_blocks=0) -> Step:
     """Token-level eviction pool: a 16-token paged pool with permuted blocks;
     exactly `dead_frac` of each sequence's tokens are dead, drawn uniformly
     without replacement and left as holes inside their blocks; a token table
     maps live logical tokens to physical slots (-1 = dead).  Sink = the first
-    `sink` live tokens, local = the last `local` live tokens; G = 1."""
+    `sink` live tokens, local = the last `local` live tokens; G = 1.
+    `spare_blocks` free blocks follow the sequences' blocks in the pool
+    (meta["free_blocks"]); the rest of the workload does not depend on it."""
     assert L % 16 == 0
     seed = seed_of(tag)
     r = rngs_of(tag)
     nb_seq = L // 16
-    n_blocks = B * nb_seq
+    n_blocks = B * nb_seq + spare_blocks
     Kp = normal_bf16(seed, S_K, (n_blocks, H, 16, d))
     Vp = normal_bf16(seed, S_V, (n_blocks, H, 16, d))
     q = normal_bf16(seed, S_Q, (B, H, d))
-    perm = r[S_PERM].permutation(n_blocks).astype(np.int64)
+    perm = r[S_PERM].permutation(B * nb_seq).astype(np.int64)
     n_dead = int(round(L * dead_frac))
     tt = np.empty((B, L), np.int32)
     lo = np.empty(B, np.int32)
@@ -280,7 +282,8 @@ def make_token_pool(tag=3, B=32, H=8, d=128, L=65536, k=2048, sink=4, local=128,
         hi[b] = live_idx[live_idx.size - local] if local > 0 else L
     kv = KV(k=Kp, v=Vp, dtype="bf16", B=B, H=H, d_k=d, d_v=d, block=16, L_max=L,
             token_table=tt, seq_len=np.full(B, L, np.int32))
-    return Step("token_pool_B%d_L%d" % (B, L), kv, q, 1, kv, q, 1, lo, hi, k, 1.0 / np.sqrt(d))
+    return Step("token_pool_B%d_L%d" % (B, L), kv, q, 1, kv, q, 1, lo, hi, k, 1.0 / np.sqrt(d),
+                meta={"free_blocks": np.arange(B * nb_seq, n_blocks, dtype=np.int64)})
 
 
 def make_indexer_mla(tag=4, L=131072, d_idx=128, d_lat=576, d_v=512, n_heads=128, k=2048) -> Step:

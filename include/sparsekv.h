@@ -291,6 +291,76 @@ skv_status sparsekv_block_select(const skv_kv* kv, void* summ, const void* q, in
                                  int32_t* blk_count, int32_t* tok_idx, void* ws, size_t ws_bytes,
                                  hipStream_t stream);
 
+/* ------------------------------------------------ token-table compaction --
+ * vToken reading notes, sections 3.2-3.5 and 4.6.  Token-level eviction
+ * leaves holes in the pool's blocks (the intra-block waste ratio of Eq. (1),
+ * F = 1 - sum_i n_i / (N S), S = 16); lazy compaction packs the live tokens
+ * of a sequence's emptiest private blocks into fewer free blocks, in logical
+ * order, and frees the sources.  Planning works on a host copy of the token
+ * table (the page keeps the canonical table on the CPU); the copy, the
+ * table update and the invariant checks run on the GPU. */
+typedef struct {
+  int32_t b;                    /* sequence                                   */
+  int32_t t;                    /* logical token                              */
+  int32_t src, dst;             /* slots before and after the move            */
+} skv_move;
+
+/* Eq. (1) over n blocks with n_live[i] live tokens each (host, no GPU). */
+double sparsekv_waste_ratio(const int32_t* n_live, int32_t n);
+
+/* Relocation plan for sequence b (host only; no GPU work).
+ *   token_table [B][L_max], seq_len [B]: HOST copies; slots < n_blocks * 16.
+ *   counts      [n_blocks] live tokens per block over every sequence (host,
+ *               the caller's running counts), or NULL to count them here.
+ *   free_blocks [n_free] free blocks (host), consumed in this order; n_free
+ *               is what the plan may take (free pool + evacuation headroom).
+ * Stage 1: F over the blocks holding the sequence's live tokens must exceed
+ * theta_F (the page's default is 0.25).  Stage 3: the candidates are the
+ * sequence's private blocks (every live token in them is its own) that are
+ * not full, emptiest first (ties: lower block), at most max_src; while they
+ * would not free strictly more blocks than the ceil(T_live / 16) targets they
+ * fill, or need more than n_free targets, the fullest is dropped (stage 2 and
+ * invariant I4).  Output (host): moves [n_moves] (room for 16 * max_src), in
+ * ascending t, move i going to slot free_blocks[i / 16] * 16 + i % 16;
+ * src_blocks [n_src] the freed blocks (ascending); n_dst = targets used.
+ * n_moves = 0 when no plan passes.  SKV_EINVAL on a slot outside the pool. */
+skv_status sparsekv_compact_plan(const int32_t* token_table, const int32_t* seq_len, int32_t B,
+                                 int32_t L_max, int32_t n_blocks, const int32_t* counts, int32_t b,
+                                 const int32_t* free_blocks, int32_t n_free, double theta_F,
+                                 int32_t max_src, skv_move* moves, int32_t* n_moves,
+                                 int32_t* src_blocks, int32_t* n_src, int32_t* n_dst);
+
+/* apply_moves with its copy: for every move (device array), the K row (and
+ * the V row when kv->v is set) of every head is copied from slot src to slot
+ * dst, then token_table[b][t] = dst.  WRITES kv->k, kv->v and
+ * kv->token_table (their const in skv_kv notwithstanding).  Readers ordered
+ * after the call on the stream see the moved tokens; the source slots keep
+ * their bytes until the caller reuses their blocks.  Requires a token-table
+ * pool (block = 16) with rows a multiple of 16 bytes; destination slots must
+ * be distinct and hold no live token. */
+skv_status sparsekv_compact_apply(const skv_kv* kv, const skv_move* moves, int32_t n_moves,
+                                  hipStream_t stream);
+
+/* Invariant I1 check (section 4.6: the retained token ids and their K/V
+ * contents hashed before and after a migration).  For each sequence b:
+ *   hash[b]  = sum mod 2^64 over live t, heads h, rows r (0 = K, 1 = V when
+ *              v is stored), 32-bit words i of the stored row (W words) of
+ *              mix64(mix64(((t H + h) R + r) W + i) ^ word),
+ *   count[b] = live tokens,
+ * mix64 being the SplitMix64 finaliser (Steele, Lea, Flood 2014).  The hash
+ * does not depend on where tokens are stored.  hash, count: device [B]. */
+skv_status sparsekv_live_hash(const skv_kv* kv, uint64_t* hash, int32_t* count,
+                              hipStream_t stream);
+
+/* Invariant I2 check over every sequence of a paged or token-table pool of
+ * n_blocks blocks: result[0] = live tokens whose slot another live token
+ * already claims, result[1] = live tokens whose slot is outside the pool
+ * (device int32 [2]).  ws: sparsekv_check_unique_ws_bytes(n_blocks) bytes
+ * (any content; it is rewritten by every call). */
+size_t sparsekv_check_unique_ws_bytes(int32_t n_blocks);
+skv_status sparsekv_check_unique(const skv_kv* kv, int32_t n_blocks, int32_t* result, void* ws,
+                                 size_t ws_bytes, hipStream_t stream);
+
 /* --------------------------------------------- compressed-code retrieval --
  * ParisKV close-reading, sections 2.2-2.5: keys and the query are normalised
  * and rotated by one SRHT R = H_d diag(signs) / sqrt(d); each of n_sub

@@ -64,6 +64,10 @@ class skv_retrieve_trace(ctypes.Structure):
     _fields_ = [("votes", c_vp), ("cand", c_vp), ("est", c_vp)]
 
 
+class skv_move(ctypes.Structure):
+    _fields_ = [("b", c_i32), ("t", c_i32), ("src", c_i32), ("dst", c_i32)]
+
+
 # symbol -> (restype, argtypes)
 _SIGS = {
     "sparsekv_score": (c_i32, [ctypes.POINTER(skv_kv), c_vp, c_i32, c_vp, c_vp]),
@@ -91,6 +95,14 @@ _SIGS = {
     "sparsekv_block_summarize_last": (c_i32, [ctypes.POINTER(skv_kv), c_vp, c_vp]),
     "sparsekv_block_select": (c_i32, [ctypes.POINTER(skv_kv), c_vp, c_vp, c_i32, skv_window, c_i32,
                                       c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "sparsekv_waste_ratio": (ctypes.c_double, [c_vp, c_i32]),
+    "sparsekv_compact_plan": (c_i32, [c_vp, c_vp, c_i32, c_i32, c_i32, c_vp, c_i32, c_vp, c_i32,
+                                      ctypes.c_double, c_i32, c_vp, ctypes.POINTER(c_i32), c_vp,
+                                      ctypes.POINTER(c_i32), ctypes.POINTER(c_i32)]),
+    "sparsekv_compact_apply": (c_i32, [ctypes.POINTER(skv_kv), c_vp, c_i32, c_vp]),
+    "sparsekv_live_hash": (c_i32, [ctypes.POINTER(skv_kv), c_vp, c_vp, c_vp]),
+    "sparsekv_check_unique_ws_bytes": (c_sz, [c_i32]),
+    "sparsekv_check_unique": (c_i32, [ctypes.POINTER(skv_kv), c_i32, c_vp, c_vp, c_sz, c_vp]),
     "sparsekv_codebook_init": (c_i32, [c_i32, ctypes.POINTER(c_f32), ctypes.POINTER(c_f32)]),
     "sparsekv_encode": (c_i32, [ctypes.POINTER(skv_codebook), ctypes.POINTER(skv_kv), c_i32,
                                 c_i32, c_i32, ctypes.POINTER(skv_index), c_vp]),
@@ -403,6 +415,76 @@ def sparsekv_block_select(kv: KVTensors, summ: torch.Tensor, q: torch.Tensor, G:
                                        _ptr(blk_idx), _ptr(blk_count), _ptr(tok_idx), _ptr(ws),
                                        ws.numel() * ws.element_size(), _stream()))
     return blk_scores, blk_idx, blk_count, tok_idx
+
+
+def sparsekv_waste_ratio(n_live) -> float:
+    a = np.ascontiguousarray(n_live, np.int32)
+    return float(lib().sparsekv_waste_ratio(a.ctypes.data_as(c_vp), a.size))
+
+
+def sparsekv_compact_plan(token_table: np.ndarray, seq_len: np.ndarray, n_blocks: int, b: int,
+                          free_blocks, n_free: int, theta_F: float, max_src: int,
+                          counts: Optional[np.ndarray] = None):
+    """Host-side relocation plan for sequence b.  Returns (moves int32 [n][4]
+    = (b, t, src, dst), freed source blocks, number of target blocks)."""
+    tt = np.ascontiguousarray(token_table, np.int32)
+    sl = np.ascontiguousarray(seq_len, np.int32)
+    fb = np.ascontiguousarray(free_blocks, np.int32)
+    cn = None if counts is None else np.ascontiguousarray(counts, np.int32)
+    B, L = tt.shape
+    moves = np.empty((16 * max_src, 4), np.int32)
+    src = np.empty(max_src, np.int32)
+    nm, ns, nd = c_i32(0), c_i32(0), c_i32(0)
+    _check("sparsekv_compact_plan",
+           lib().sparsekv_compact_plan(tt.ctypes.data_as(c_vp), sl.ctypes.data_as(c_vp), B, L,
+                                       n_blocks, None if cn is None else cn.ctypes.data_as(c_vp),
+                                       b, fb.ctypes.data_as(c_vp) if fb.size else None, n_free,
+                                       float(theta_F), max_src, moves.ctypes.data_as(c_vp),
+                                       ctypes.byref(nm), src.ctypes.data_as(c_vp), ctypes.byref(ns),
+                                       ctypes.byref(nd)))
+    return moves[: nm.value].copy(), src[: ns.value].copy(), int(nd.value)
+
+
+def sparsekv_compact_apply(kv: KVTensors, moves: torch.Tensor):
+    """Copy the moved rows and rewrite kv.token_table (device, in place)."""
+    _dev(moves, "moves", torch.int32)
+    if moves.dim() != 2 or moves.shape[1] != 4:
+        raise ValueError("moves must be int32 [n][4]")
+    c = kv.c()
+    _check("sparsekv_compact_apply",
+           lib().sparsekv_compact_apply(ctypes.byref(c), _ptr(moves), moves.shape[0], _stream()))
+
+
+def sparsekv_live_hash(kv: KVTensors, hash_out: Optional[torch.Tensor] = None,
+                       count: Optional[torch.Tensor] = None):
+    """(hash [B] as int64 bit patterns of the uint64 sums, live count [B])."""
+    dev = kv.k.device
+    if hash_out is None:
+        hash_out = torch.empty(kv.B, dtype=torch.int64, device=dev)
+    if count is None:
+        count = torch.empty(kv.B, dtype=torch.int32, device=dev)
+    _dev(hash_out, "hash", torch.int64)
+    _dev(count, "count", torch.int32)
+    c = kv.c()
+    _check("sparsekv_live_hash",
+           lib().sparsekv_live_hash(ctypes.byref(c), _ptr(hash_out), _ptr(count), _stream()))
+    return hash_out, count
+
+
+def sparsekv_check_unique(kv: KVTensors, n_blocks: int, result: Optional[torch.Tensor] = None,
+                          ws: Optional[torch.Tensor] = None):
+    """I2 check: int32 [2] = (duplicate claims, slots outside the pool)."""
+    dev = kv.k.device
+    if result is None:
+        result = torch.empty(2, dtype=torch.int32, device=dev)
+    if ws is None:
+        ws = torch.empty(max(1, int(lib().sparsekv_check_unique_ws_bytes(n_blocks))),
+                         dtype=torch.uint8, device=dev)
+    c = kv.c()
+    _check("sparsekv_check_unique",
+           lib().sparsekv_check_unique(ctypes.byref(c), n_blocks, _ptr(result), _ptr(ws),
+                                       ws.numel() * ws.element_size(), _stream()))
+    return result
 
 
 def sparsekv_score_hist(kv: KVTensors, q: torch.Tensor, G: int, lo: torch.Tensor,

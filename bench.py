@@ -56,7 +56,7 @@ sys.path.insert(0, HERE)
 PEAK_HBM_GBPS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 DENSE = ("gqa_paged", "token_pool", "single_head", "indexer_mla")
-WORKLOADS = DENSE + ("paris", "paris_encode", "paris_decode")
+WORKLOADS = DENSE + ("paris", "paris_encode", "paris_decode", "compact")
 PARIS_UPDATE = 512      # Update Buffer tokens (the page's experiments use 256 or 512)
 
 
@@ -741,6 +741,101 @@ def bench_paris_decode(args, hip):
     return rec
 
 
+def bench_compact(args, hip):
+    """Token-table compaction of the token-pool workload (32 sequences x
+    65,536 logical tokens, half of them dead, 8 heads, d = 128) with 2,048
+    spare blocks as headroom: the host planner makes one plan per sequence
+    (at most 64 source blocks each, theta_F = 0.25), and a timed step applies
+    all of them in one sparsekv_compact_apply launch, then the reverse moves
+    in a second one (so that every step moves the same tokens); the I1 hash
+    and I2 check over the whole pool are timed once each."""
+    import numpy as np
+    import torch
+    import sparse_top_kv_indexer_amd as S
+    import workloads as W
+    dev = torch.device("cuda:0")
+    st = W.make_token_pool(spare_blocks=2048)
+    kv = st.kv
+    n_blocks = kv.k.shape[0]
+    kv_d = S.kv_to_device(kv, dev)
+    from oracle import compact as C
+    counts = C.occupancy(kv.token_table, kv.seq_len, n_blocks).astype(np.int32)
+    free = [int(x) for x in st.meta["free_blocks"]]
+    F_before = S.sparsekv_waste_ratio(counts[counts > 0])
+    t0 = time.perf_counter()
+    plans = []
+    n_freed = n_used = 0
+    for b in range(kv.B):
+        moves, src, n_dst = S.sparsekv_compact_plan(kv.token_table, kv.seq_len, n_blocks, b, free,
+                                                    len(free), 0.25, 64, counts=counts)
+        for p_ in src:
+            counts[p_] = 0
+        for j, p_ in enumerate(free[:n_dst]):
+            counts[p_] = min(16, len(moves) - 16 * j)
+        free = free[n_dst:]
+        plans.append(moves)
+        n_freed += len(src)
+        n_used += n_dst
+    plan_s = time.perf_counter() - t0
+    fwd = np.concatenate(plans)
+    rev = fwd[:, [0, 1, 3, 2]].copy()
+    n_mv = int(fwd.shape[0])
+    fwd_d, rev_d = torch.from_numpy(fwd).to(dev), torch.from_numpy(rev).to(dev)
+    h0, c0 = S.sparsekv_live_hash(kv_d)
+    torch.cuda.synchronize()
+    h0 = h0.clone()
+
+    def step(i, mark):
+        S.sparsekv_compact_apply(kv_d, fwd_d)
+        if mark:
+            mark(0)
+        S.sparsekv_compact_apply(kv_d, rev_d)
+        if mark:
+            mark(1)
+
+    args.eager = True
+    wall, gpu_ms, calls, note = timed_steps(step, 2, args, hip)
+    calls = np.array(calls)
+    ms = wall * 1e3 / args.steps
+    # the checks, once each, with events around them
+    e = [hip.create() for _ in range(3)]
+    hip.record(e[0])
+    h1, c1 = S.sparsekv_live_hash(kv_d)
+    hip.record(e[1])
+    dup = S.sparsekv_check_unique(kv_d, n_blocks)
+    hip.record(e[2])
+    torch.cuda.synchronize()
+    hash_us, uniq_us = hip.elapsed_ms(e[0], e[1]) * 1e3, hip.elapsed_ms(e[1], e[2]) * 1e3
+    assert torch.equal(h0, h1) and dup.cpu().tolist() == [0, 0], "compaction broke an invariant"
+    row = kv.d_k * 2
+    per_move = kv.H * 2 * row * 2 + 16 + 4       # K and V rows read + written, move, table entry
+    t_apply = float(np.mean(calls[:, 0])) * 1e-3
+    live = int(c1.sum().item())
+    hash_bytes = live * kv.H * 2 * row
+    F_after = S.sparsekv_waste_ratio(counts[counts > 0])
+    rec = base_record("tokens relocated/s (token-table compaction, sparsekv_compact_apply)",
+                      2 * n_mv / (ms * 1e-3), "tokens/s", args, ms, "bf16",
+                      {"workload": "compact", "B": kv.B, "H_kv": kv.H, "d": kv.d_k, "L": kv.L_max,
+                       "dead_frac": 0.5, "spare_blocks": 2048, "max_src": 64, "theta_F": 0.25,
+                       "launch": "eager"})
+    rec.update({
+        "us_per_step": ms * 1e3, "us_per_step_gpu": gpu_ms * 1e3, "timing": note,
+        "moves_per_launch": n_mv, "source_blocks_freed": n_freed, "target_blocks_used": n_used,
+        "us_per_call": {"apply_forward": t_apply * 1e6,
+                        "apply_reverse": float(np.mean(calls[:, 1])) * 1e3,
+                        "live_hash_all": hash_us, "check_unique_all": uniq_us},
+        "plan_host_ms": plan_s * 1e3,
+        "waste_ratio_before": F_before, "waste_ratio_after_one_round": F_after,
+        "roofline": roofline("compaction copy (sparsekv_compact_apply)", "hbm", n_mv * per_move,
+                             t_apply, None, {"algorithmic_bytes_per_launch": n_mv * per_move,
+                                             "bytes_per_move": per_move}),
+        "roofline_hash": roofline("I1 hash (sparsekv_live_hash over all live tokens)", "hbm",
+                                  hash_bytes, hash_us * 1e-6, None,
+                                  {"algorithmic_bytes_per_launch": hash_bytes}),
+    })
+    return rec
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -766,6 +861,8 @@ def main():
         rec = bench_dense(args, hip)
     elif args.workload == "paris_decode":
         rec = bench_paris_decode(args, hip)
+    elif args.workload == "compact":
+        rec = bench_compact(args, hip)
     else:
         rec = bench_paris(args, hip)
     print(json.dumps(rec))

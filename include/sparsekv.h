@@ -342,13 +342,17 @@ skv_status sparsekv_compact_apply(const skv_kv* kv, const skv_move* moves, int32
                                   hipStream_t stream);
 
 /* Invariant I1 check (section 4.6: the retained token ids and their K/V
- * contents hashed before and after a migration).  For each sequence b:
+ * contents hashed before and after a migration; the page names no hash).
+ * For each sequence b:
  *   hash[b]  = sum mod 2^64 over live t, heads h, rows r (0 = K, 1 = V when
- *              v is stored), 32-bit words i of the stored row (W words) of
- *              mix64(mix64(((t H + h) R + r) W + i) ^ word),
+ *              v is stored; R rows), 64-bit words w_j of the stored row
+ *              (32-bit words 2j, 2j + 1, low first) of
+ *              mix64((s + (j + 1) * 0x9e3779b97f4a7c15) ^ w_j),
+ *              s = mix64((t H + h) R + r),
  *   count[b] = live tokens,
  * mix64 being the SplitMix64 finaliser (Steele, Lea, Flood 2014).  The hash
- * does not depend on where tokens are stored.  hash, count: device [B]. */
+ * does not depend on where tokens are stored.  hash, count: device [B].
+ * Rows of 16 * 2^i bytes (i <= 8); SKV_EUNSUPPORTED otherwise. */
 skv_status sparsekv_live_hash(const skv_kv* kv, uint64_t* hash, int32_t* count,
                               hipStream_t stream);
 

@@ -25,19 +25,21 @@ Readings where the page is silent:
   * moves take the sources' live tokens in ascending logical order and fill
     target block after target block: move i goes to
     free_blocks[i // 16] * 16 + i % 16;
-  * the hash of a sequence's retained tokens is a sum, modulo 2^64, of one
-    term per stored 32-bit word of every live token's K row (and V row when
+  * the page names no hash; the one used is a sum, modulo 2^64, of one term
+    per stored 64-bit word of every live token's K row (and V row when
     values are stored separately), over all heads:
-        term = mix64(mix64(key) ^ word),
-        key  = ((t * H + h) * R + r) * W + i,
-    t the logical token, h the head, r the row (0 = K, 1 = V; R rows), i the
-    word in the row (W words), and mix64 the SplitMix64 finaliser (Steele,
+        s    = mix64((t * H + h) * R + r),
+        term = mix64((s + (j + 1) * gamma) ^ w_j),
+    t the logical token, h the head, r the row (0 = K, 1 = V; R rows), w_j
+    the row's 64-bit word j (its 32-bit words 2j and 2j + 1, low first),
+    gamma = 0x9e3779b97f4a7c15 and mix64 the SplitMix64 finaliser (Steele,
     Lea and Flood, "Fast splittable pseudorandom number generators", 2014):
         z ^= z >> 30; z *= 0xbf58476d1ce4e5b9; z ^= z >> 27;
         z *= 0x94d049bb133111eb; z ^= z >> 31.
-    The sum is independent of where a token is stored and of the order the
-    terms are added in, and changes when a live token, its position or one
-    stored word changes (with probability 1 - 2^-64 per change).
+    One mix per 8 stored bytes keeps a GPU pass over the pool bound by
+    memory.  The sum is independent of where a token is stored and of the
+    order the terms are added in, and changes when a live token, its
+    position or one stored word changes (barring a 2^-64 coincidence).
 """
 from __future__ import annotations
 
@@ -48,6 +50,7 @@ import numpy as np
 S = 16
 M1 = np.uint64(0xBF58476D1CE4E5B9)
 M2 = np.uint64(0x94D049BB133111EB)
+GAMMA = np.uint64(0x9E3779B97F4A7C15)
 
 
 def waste_ratio(n_live) -> float:
@@ -129,14 +132,14 @@ def live_hash(kv, b: int) -> tuple[int, int]:
     total = np.uint64(0)
     for r, arr in enumerate(rows):
         data = arr[slots // S, :, slots % S]                 # [n][H][d] as stored
-        words = np.ascontiguousarray(data).view(np.uint32)   # [n][H][W]
+        words = np.ascontiguousarray(data).view(np.uint64)   # [n][H][W64], little endian
         n, H, W = words.shape
         t = live_t.astype(np.uint64)[:, None, None]
         h = np.arange(H, dtype=np.uint64)[None, :, None]
-        i = np.arange(W, dtype=np.uint64)[None, None, :]
+        j1 = np.arange(1, W + 1, dtype=np.uint64)[None, None, :]
         with np.errstate(over="ignore"):
-            key = ((t * np.uint64(H) + h) * np.uint64(R) + np.uint64(r)) * np.uint64(W) + i
-            terms = mix64(mix64(key) ^ words.astype(np.uint64))
+            seed = mix64((t * np.uint64(H) + h) * np.uint64(R) + np.uint64(r))
+            terms = mix64((seed + j1 * GAMMA) ^ words)
             total = total + terms.sum(dtype=np.uint64)
     return int(total), int(live_t.size)
 

@@ -7,8 +7,8 @@
 // stored, and I2, the number of live tokens that share a slot or point
 // outside the pool.
 //
-// The copy runs one workgroup per 16 consecutive moves: a plan fills one
-// target block per 16 moves, and a block's 16 rows of one head are one
+// The copy runs one workgroup per 16 consecutive moves and head: a plan fills
+// one target block per 16 moves, and a block's 16 rows of one head are one
 // contiguous run in the pool, so the writes are whole 4 KB runs (d = 128,
 // bf16) while the reads gather the scattered source rows.
 #include <math.h>
@@ -27,31 +27,44 @@ namespace {
 
 constexpr int kS = 16;   // tokens per block
 
-// One workgroup per 16 moves; thread work item (h, r, m, c): head h, row r
-// (0 = K, 1 = V), move m of the group, 16-byte chunk c of the row.
+// Grid (ceil(n_moves / 16), H): one workgroup per 16 moves and head; thread
+// work item (r, m, c): row r (0 = K, 1 = V), move m of the group, 16-byte
+// chunk c of the row.  Four items' loads are issued before their stores.
+// The workgroups of head 0 then point the token table at the targets.
 __global__ __launch_bounds__(256) void compact_copy_kernel(char* k, char* v, int H, int row_k,
                                                            int row_v, const skv_move* moves,
                                                            int n_moves, int32_t* token_table,
                                                            int L_max) {
-  const int m0 = blockIdx.x * 16;
+  const int m0 = blockIdx.x * 16, h = blockIdx.y;
   const int nm = min(16, n_moves - m0);
   const int ck = row_k / 16, cv = row_v / 16;
-  const int per_head = nm * (ck + cv);
-  for (int it = threadIdx.x; it < H * per_head; it += blockDim.x) {
-    const int h = it / per_head;
-    int rem = it - h * per_head;
-    const bool is_v = rem >= nm * ck;
-    if (is_v) rem -= nm * ck;
-    const int cpr = is_v ? cv : ck;
-    const int m = rem / cpr, c = rem - m * cpr;
-    const skv_move mv = moves[m0 + m];
-    char* base = is_v ? v : k;
-    const int row = is_v ? row_v : row_k;
-    const int64_t so = (((int64_t)(mv.src / kS) * H + h) * kS + mv.src % kS) * row + 16 * c;
-    const int64_t dO = (((int64_t)(mv.dst / kS) * H + h) * kS + mv.dst % kS) * row + 16 * c;
-    *(u32x4_t*)(base + dO) = *(const u32x4_t*)(base + so);
+  const int n_items = nm * (ck + cv);
+  for (int i0 = threadIdx.x; i0 < n_items; i0 += 4 * 256) {
+    u32x4_t w[4];
+    int64_t dst[4];
+    char* base[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int it = i0 + u * 256;
+      dst[u] = -1;
+      if (it >= n_items) continue;
+      int rem = it;
+      const bool is_v = rem >= nm * ck;
+      if (is_v) rem -= nm * ck;
+      const int cpr = is_v ? cv : ck;
+      const int m = rem / cpr, c = rem - m * cpr;
+      const skv_move mv = moves[m0 + m];
+      const int row = is_v ? row_v : row_k;
+      base[u] = is_v ? v : k;
+      const int64_t so = (((int64_t)(mv.src / kS) * H + h) * kS + mv.src % kS) * row + 16 * c;
+      dst[u] = (((int64_t)(mv.dst / kS) * H + h) * kS + mv.dst % kS) * row + 16 * c;
+      w[u] = *(const u32x4_t*)(base[u] + so);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (dst[u] >= 0) *(u32x4_t*)(base[u] + dst[u]) = w[u];
   }
-  if (threadIdx.x < nm) {
+  if (h == 0 && threadIdx.x < nm) {
     const skv_move mv = moves[m0 + threadIdx.x];
     token_table[(int64_t)mv.b * L_max + mv.t] = mv.dst;
   }
@@ -75,38 +88,53 @@ __global__ __launch_bounds__(256) void zero_hash_kernel(uint64_t* hash, int32_t*
   }
 }
 
-// Grid (ceil(L_max / 32), B): tokens 32 x .. 32 x + 31 of sequence b.  Wave w
-// takes the items (token, head, row) w, w + 4, ...; its lanes walk the row's
-// 32-bit words.  Per-lane sums, a wave sum, one 64-bit atomic per wave.
-__global__ __launch_bounds__(256) void live_hash_kernel(KvArgs kv, uint64_t* hash,
+// Grid (ceil(L_max / 32), B): tokens 32 x .. 32 x + 31 of sequence b.  A
+// row (token, head h, K or V) is cut into P 16-byte pieces (P divides 256);
+// thread i takes piece i % P of the rows hr = i / P, i / P + 256 / P, ...
+// (hr = h R + r) of every token, four tokens' loads in flight at a time.
+// Per 64-bit word j of a row: mix64((s + (j + 1) gamma) ^ w_j) with
+// s = mix64((t H + h) R + r); per-thread sums, a wave sum, one 64-bit atomic
+// per wave.
+__global__ __launch_bounds__(256) void live_hash_kernel(KvArgs kv, int P, uint64_t* hash,
                                                         int32_t* count) {
+  __shared__ int64_t sl[32];
   const int b = blockIdx.y, t0 = blockIdx.x * 32;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int R = kv.v ? 2 : 1;
+  if (threadIdx.x < 32) sl[threadIdx.x] = slot_of(kv, b, t0 + threadIdx.x);
+  __syncthreads();
+  const int R = kv.v ? 2 : 1, HR = kv.H * R;
   const int es = kv.bf16 ? 2 : 4;
-  const int Wk = kv.d_k * es / 4, Wv = kv.d_v * es / 4;
+  const int p = threadIdx.x % P, q0 = threadIdx.x / P, rows_par = 256 / P;
+  const uint64_t gamma = 0x9e3779b97f4a7c15ull;
   uint64_t acc = 0;
-  const int n_items = 32 * kv.H * R;
-  for (int it = wave; it < n_items; it += 4) {
-    const int tok = it / (kv.H * R);
-    const int hr = it - tok * kv.H * R;
-    const int h = hr / R, r = hr - h * R;
-    const int t = t0 + tok;
-    const int64_t slot = slot_of(kv, b, t);
-    if (slot < 0) continue;   // same value in every lane of the wave
-    const int W = r ? Wv : Wk;
-    const int d = r ? kv.d_v : kv.d_k;
-    const uint32_t* row =
-        (const uint32_t*)((const char*)(r ? kv.v : kv.k) + row_elem(kv, b, h, slot, d) * es);
-    const uint64_t kb = (((uint64_t)t * kv.H + h) * R + r) * (uint64_t)W;
-    for (int i = lane; i < W; i += 64) acc += mix64(mix64(kb + i) ^ (uint64_t)row[i]);
+  for (int tb = 0; tb < 32; tb += 4) {
+    for (int hr = q0; hr < HR; hr += rows_par) {
+      const int h = hr / R, r = hr - h * R;
+      const int d = r ? kv.d_v : kv.d_k;
+      const char* base = (const char*)(r ? kv.v : kv.k);
+      u32x4_t w[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t slot = sl[tb + u];
+        if (slot >= 0)
+          w[u] = *(const u32x4_t*)(base + row_elem(kv, b, h, slot, d) * es + 16 * p);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (sl[tb + u] < 0) continue;
+        const uint64_t s = mix64(((uint64_t)(t0 + tb + u) * kv.H + h) * R + r);
+        const uint64_t w0 = (uint64_t)w[u][0] | ((uint64_t)w[u][1] << 32);
+        const uint64_t w1 = (uint64_t)w[u][2] | ((uint64_t)w[u][3] << 32);
+        acc += mix64((s + (uint64_t)(2 * p + 1) * gamma) ^ w0);
+        acc += mix64((s + (uint64_t)(2 * p + 2) * gamma) ^ w1);
+      }
+    }
   }
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) acc += shfl_xor64(acc, m);
+  const int lane = threadIdx.x & 63;
   if (lane == 0 && acc) atomicAdd((unsigned long long*)&hash[b], (unsigned long long)acc);
-  if (wave == 0) {
-    const bool live = lane < 32 && slot_of(kv, b, t0 + lane) >= 0;
-    const int n = __popcll(__ballot(live));
+  if (threadIdx.x < 64) {
+    const int n = __popcll(__ballot(lane < 32 && sl[lane & 31] >= 0));
     if (lane == 0 && n) atomicAdd(&count[b], n);
   }
 }
@@ -262,7 +290,7 @@ skv_status sparsekv_compact_apply(const skv_kv* kv, const skv_move* moves, int32
   const int row_k = kv->d_k * es, row_v = kv->v ? kv->d_v * es : 0;
   if (row_k % 16 || row_v % 16) return SKV_EUNSUPPORTED;
   if (n_moves == 0) return SKV_OK;
-  compact_copy_kernel<<<(n_moves + 15) / 16, 256, 0, stream>>>(
+  compact_copy_kernel<<<dim3((n_moves + 15) / 16, kv->H), 256, 0, stream>>>(
       (char*)kv->k, (char*)kv->v, kv->H, row_k, row_v, moves, n_moves,
       (int32_t*)kv->token_table, kv->L_max);
   return hipGetLastError() == hipSuccess ? SKV_OK : SKV_ELAUNCH;
@@ -276,12 +304,15 @@ skv_status sparsekv_live_hash(const skv_kv* kv, uint64_t* hash, int32_t* count,
   if (kv->dtype != SKV_BF16 && kv->dtype != SKV_F32) return SKV_EINVAL;
   if (kv->block != 0 && kv->block != kS) return SKV_EINVAL;
   if (kv->v && kv->d_v != kv->d_k) return SKV_EINVAL;
+  // rows of P 16-byte pieces, P a power of two up to 256
   const int es = kv->dtype == SKV_BF16 ? 2 : 4;
-  if ((kv->d_k * es) % 4 || (kv->v && (kv->d_v * es) % 4)) return SKV_EUNSUPPORTED;
+  const int row = kv->d_k * es;
+  if (row % 16 || row / 16 > 256 || ((row / 16) & (row / 16 - 1))) return SKV_EUNSUPPORTED;
   KvArgs a = kv_args(kv);
   if (!kv->v) a.d_v = kv->d_k;
   zero_hash_kernel<<<1, 256, 0, stream>>>(hash, count, kv->B);
-  live_hash_kernel<<<dim3((kv->L_max + 31) / 32, kv->B), 256, 0, stream>>>(a, hash, count);
+  live_hash_kernel<<<dim3((kv->L_max + 31) / 32, kv->B), 256, 0, stream>>>(a, row / 16, hash,
+                                                                          count);
   return hipGetLastError() == hipSuccess ? SKV_OK : SKV_ELAUNCH;
 }
 

@@ -84,6 +84,8 @@ def parse():
     ap.add_argument("--eager", action="store_true",
                     help="launch every kernel from the host instead of replaying one HIP graph "
                          "that holds the K timed steps")
+    ap.add_argument("--no-stream-reference", action="store_true",
+                    help="skip the streaming-read reference measured after the timed steps")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -239,6 +241,40 @@ def roofline(kernel, bound, alg, seconds, traffic, extra=None):
     if extra:
         r.update(extra)
     return r
+
+
+def stream_reference():
+    """Streaming rates measured on this GPU, a second yardstick beside the
+    8 TB/s peak: the library's read probe over 2 GiB (reads only; best over
+    a few grid sizes) and torch's 1 GiB device copy (reads + writes), best
+    of 10 runs each."""
+    import torch
+    import sparse_top_kv_indexer_amd as S
+    n = (2 << 30) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty(n // 2, dtype=torch.float32, device="cuda")
+    sink = torch.empty(8192, dtype=torch.int32, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def best(fn, nbytes):
+        fn()
+        torch.cuda.synchronize()
+        t = []
+        for _ in range(10):
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            t.append(e0.elapsed_time(e1) * 1e-3)
+        return nbytes / min(t) / 1e9
+
+    read = max(best(lambda: S.sparsekv_read_probe(x, g, sink), 4 * n) for g in (1024, 2048, 4096, 8192))
+    copy = best(lambda: y.copy_(x[: n // 2]), 2 * 4 * (n // 2))
+    del x, y, sink
+    torch.cuda.empty_cache()
+    return {"stream_read_GBps": read, "stream_copy_GBps": copy,
+            "stream_note": "sparsekv_read_probe over 2 GiB (reads only, best grid of 1024..8192 "
+                           "workgroups) and a torch 1 GiB device copy (read + write), best of 10"}
 
 
 # ------------------------------------------------------------------ dense
@@ -865,6 +901,11 @@ def main():
         rec = bench_compact(args, hip)
     else:
         rec = bench_paris(args, hip)
+    ro = rec.get("roofline")
+    if ro and ro.get("bound") == "hbm" and not args.no_stream_reference:
+        ref = stream_reference()
+        ro.update(ref)
+        ro["frac_of_stream_read"] = ro["achieved"] / ref["stream_read_GBps"]
     print(json.dumps(rec))
 
 

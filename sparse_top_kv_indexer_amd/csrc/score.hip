@@ -461,6 +461,10 @@ hipError_t launch_stream_k(const KvArgs& kv, const void* q, int G, float* scores
   // slot, unless a slice would then stage more table entries than fit in LDS
   const int64_t cap = kStageEntries / (kv.token_table ? 16 : 1);
   int64_t w = std::min<int64_t>(resident_wgs(kern, cache, 64), (n_work + 15) / 16);
+  // each workgroup flushes its histogram of a row with one atomic per bin it
+  // holds; few long rows spread over every resident workgroup would make
+  // hundreds of them contend for the same bins, so a row gets at most 256
+  if (MODE == 1) w = std::min<int64_t>(w, (int64_t)kv.B * kv.H * 256);
   w = std::max<int64_t>(std::max<int64_t>(w, (n_work + cap - 1) / cap), 1);
   if (w > 0x7fffffff) return hipErrorInvalidValue;
   kern<<<dim3((unsigned)w), kThreads, 0, s>>>(kv, (const uint16_t*)q, G, scores, ha, cpr);

@@ -277,6 +277,27 @@ def stream_reference():
                            "workgroups) and a torch 1 GiB device copy (read + write), best of 10"}
 
 
+def host_cpu():
+    """The host the oracle ran on: CPU model and the cores this process may use."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"cpu_model": model, "affinity_cores": len(os.sched_getaffinity(0))}
+
+
+def step_percentiles(calls):
+    """p10 / p50 / p90 of the per-step GPU time (sum of a step's call events), us."""
+    import numpy as np
+    t = np.asarray(calls).sum(axis=1) * 1e3
+    return {"p10": float(np.percentile(t, 10)), "p50": float(np.percentile(t, 50)),
+            "p90": float(np.percentile(t, 90))}
+
+
 # ------------------------------------------------------------------ dense
 def make_dense(name):
     import workloads as W
@@ -305,7 +326,7 @@ def dense_cpu_baseline(st, min_seconds=10.0):
     dt = time.perf_counter() - t0
     blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
     cores = max([1] + blas)
-    return {"value": keys / dt, "unit": "keys/s", "cores": cores, "kind": "oracle",
+    return {"value": keys / dt, "unit": "keys/s", "cores": cores, "kind": "oracle", **host_cpu(),
             "sample": "%d (sequence, KV head) rows of the same workload in order (%d keys), %.1f s; "
                       "numpy float64, BLAS threads=%d, other ops single-threaded"
                       % (n_rows, keys, dt, cores)}
@@ -415,6 +436,7 @@ def bench_dense(args, hip):
         "us_per_step": ms_per_step * 1e3,
         "us_per_step_gpu": gpu_ms * 1e3,
         "timing": note,
+        "us_per_step_events": step_percentiles(calls),
         "us_per_call": ({"score_scan": float(np.mean(calls[:, 0])) * 1e3,
                          "select_attend_merge": float(np.mean(calls[:, 1])) * 1e3} if fused else
                         {"score_scan": float(np.mean(calls[:, 0])) * 1e3,
@@ -513,6 +535,7 @@ def bench_blocks(args, hip, st, kv, q, lo, hi):
         "us_per_step": ms_per_step * 1e3,
         "us_per_step_gpu": gpu_ms * 1e3,
         "timing": note,
+        "us_per_step_events": step_percentiles(calls),
         "us_per_call": {"block_select": float(np.mean(calls[:, 0])) * 1e3,
                         "gather_attend": float(np.mean(calls[:, 1])) * 1e3},
         "keys_covered_per_step": n_keys,
@@ -549,6 +572,7 @@ def paris_cpu_baseline(min_seconds=10.0):
     blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
     cores = max([1] + blas)
     return {"value": n_runs * p.H * p.n / dt, "unit": "keys/s", "cores": cores, "kind": "oracle",
+            **host_cpu(),
             "sample": "%d x (encode + retrieve) of 1 KV head x %d keys of the same distribution, "
                       "%.1f s; numpy fp32 in the prescribed operation order, BLAS threads=%d"
                       % (n_runs, p.n, dt, cores)}
@@ -642,6 +666,7 @@ def bench_paris(args, hip):
                        "launch": "eager" if args.eager else "hip_graph"})
     rec.update({
         "us_per_step": ms * 1e3, "us_per_step_gpu": gpu_ms * 1e3, "timing": note,
+        "us_per_step_events": step_percentiles(calls),
         "us_per_call": {"retrieve": t_ret * 1e6, "gather_attend": float(np.mean(calls[:, 1])) * 1e3},
         "keys_voted_per_step": n_keys,
         "step_algorithmic_bytes": ret_bytes + gather,
@@ -758,6 +783,7 @@ def bench_paris_decode(args, hip):
                        "layers": n_layers, "tokens_appended": n_tok, "launch": "eager"})
     rec.update({
         "us_per_step": ms * 1e3, "us_per_step_gpu": gpu_ms * 1e3, "timing": note,
+        "us_per_step_events": step_percentiles(calls),
         "us_per_call": {"update_buffer_flush": t_flush_us,
                         "retrieve": t_ret * 1e6,
                         "gather_attend": float(np.mean(calls[:, 2])) * 1e3},
@@ -857,6 +883,7 @@ def bench_compact(args, hip):
     rec.update({
         "us_per_step": ms * 1e3, "us_per_step_gpu": gpu_ms * 1e3, "timing": note,
         "moves_per_launch": n_mv, "source_blocks_freed": n_freed, "target_blocks_used": n_used,
+        "us_per_step_events": step_percentiles(calls),
         "us_per_call": {"apply_forward": t_apply * 1e6,
                         "apply_reverse": float(np.mean(calls[:, 1])) * 1e3,
                         "live_hash_all": hash_us, "check_unique_all": uniq_us},

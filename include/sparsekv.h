@@ -352,7 +352,7 @@ skv_status sparsekv_compact_apply(const skv_kv* kv, const skv_move* moves, int32
  *   count[b] = live tokens,
  * mix64 being the SplitMix64 finaliser (Steele, Lea, Flood 2014).  The hash
  * does not depend on where tokens are stored.  hash, count: device [B].
- * Rows of 16 * 2^i bytes (i <= 8); SKV_EUNSUPPORTED otherwise. */
+ * Rows of a multiple of 16 bytes, at most 4 KB; SKV_EUNSUPPORTED otherwise. */
 skv_status sparsekv_live_hash(const skv_kv* kv, uint64_t* hash, int32_t* count,
                               hipStream_t stream);
 

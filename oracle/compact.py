@@ -122,16 +122,19 @@ def mix64(z: np.ndarray) -> np.ndarray:
 
 def live_hash(kv, b: int) -> tuple[int, int]:
     """(hash, live count) of sequence b's retained tokens, from the logical
-    view: the token table decides which t are live and where their rows are."""
-    L = int(kv.seq_len[b])
-    row = kv.token_table[b, :L].astype(np.int64)
-    live_t = np.nonzero(row >= 0)[0]
-    slots = row[live_t]
+    view: the table (token or block table, or none for contiguous storage)
+    decides which t are live and where their rows are."""
+    from .dense import live_slots
+    live_t, slots = live_slots(kv, b)
+    live_t, slots = live_t[live_t < kv.L_max], slots[live_t < kv.L_max]
     rows = [kv.k] + ([kv.v] if kv.v is not None else [])
     R = len(rows)
     total = np.uint64(0)
     for r, arr in enumerate(rows):
-        data = arr[slots // S, :, slots % S]                 # [n][H][d] as stored
+        if kv.block:
+            data = arr[slots // S, :, slots % S]             # [n][H][d] as stored
+        else:
+            data = np.moveaxis(arr[b][:, slots], 0, 1)       # [H][n][d] -> [n][H][d]
         words = np.ascontiguousarray(data).view(np.uint64)   # [n][H][W64], little endian
         n, H, W = words.shape
         t = live_t.astype(np.uint64)[:, None, None]

@@ -89,9 +89,9 @@ __global__ __launch_bounds__(256) void zero_hash_kernel(uint64_t* hash, int32_t*
 }
 
 // Grid (ceil(L_max / 32), B): tokens 32 x .. 32 x + 31 of sequence b.  A
-// row (token, head h, K or V) is cut into P 16-byte pieces (P divides 256);
-// thread i takes piece i % P of the rows hr = i / P, i / P + 256 / P, ...
-// (hr = h R + r) of every token, four tokens' loads in flight at a time.
+// row (token, head h, K or V) is cut into P <= 256 16-byte pieces; thread
+// i < (256 / P) P takes piece i % P of the rows hr = i / P, i / P + 256 / P,
+// ... (hr = h R + r) of every token, four tokens' loads in flight at a time.
 // Per 64-bit word j of a row: mix64((s + (j + 1) gamma) ^ w_j) with
 // s = mix64((t H + h) R + r); per-thread sums, a wave sum, one 64-bit atomic
 // per wave.
@@ -103,7 +103,8 @@ __global__ __launch_bounds__(256) void live_hash_kernel(KvArgs kv, int P, uint64
   __syncthreads();
   const int R = kv.v ? 2 : 1, HR = kv.H * R;
   const int es = kv.bf16 ? 2 : 4;
-  const int p = threadIdx.x % P, q0 = threadIdx.x / P, rows_par = 256 / P;
+  const int p = threadIdx.x % P, rows_par = 256 / P;
+  const int q0 = threadIdx.x < rows_par * P ? threadIdx.x / P : HR;   // the rest sit out
   const uint64_t gamma = 0x9e3779b97f4a7c15ull;
   uint64_t acc = 0;
   for (int tb = 0; tb < 32; tb += 4) {
@@ -304,10 +305,10 @@ skv_status sparsekv_live_hash(const skv_kv* kv, uint64_t* hash, int32_t* count,
   if (kv->dtype != SKV_BF16 && kv->dtype != SKV_F32) return SKV_EINVAL;
   if (kv->block != 0 && kv->block != kS) return SKV_EINVAL;
   if (kv->v && kv->d_v != kv->d_k) return SKV_EINVAL;
-  // rows of P 16-byte pieces, P a power of two up to 256
+  // rows of at most 256 16-byte pieces
   const int es = kv->dtype == SKV_BF16 ? 2 : 4;
   const int row = kv->d_k * es;
-  if (row % 16 || row / 16 > 256 || ((row / 16) & (row / 16 - 1))) return SKV_EUNSUPPORTED;
+  if (row % 16 || row / 16 > 256) return SKV_EUNSUPPORTED;
   KvArgs a = kv_args(kv);
   if (!kv->v) a.d_v = kv->d_k;
   zero_hash_kernel<<<1, 256, 0, stream>>>(hash, count, kv->B);

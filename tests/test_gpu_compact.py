@@ -124,3 +124,21 @@ def test_checks_detect_broken_invariants():
     kv_d.token_table.copy_(torch.from_numpy(kv.token_table))
     got = S.sparsekv_check_unique(kv_d, n_blocks).cpu().tolist()
     assert got == list(C.duplicate_slots(kv.token_table, kv.seq_len, n_blocks)) == [1, 1]
+
+
+@pytest.mark.parametrize("layout", ["paged", "contiguous", "latent"])
+def test_live_hash_every_layout(layout):
+    """sparsekv_live_hash against the oracle on a block-table pool (with an
+    unmapped block), contiguous storage and a latent pool without values."""
+    if layout == "paged":
+        st = W.make_gqa_paged(tag=992, B=2, H=3, G=2, d=128, L=512, k=16, sink=4, local=16,
+                              seq_len=[512, 301])
+        st.kv.block_table[1, 2] = -1
+        kv = st.kv
+    elif layout == "contiguous":
+        kv = W.make_paris(tag=993, H=2, G=1, L=1000, sink=4, local=16).kv()
+        kv.seq_len = np.array([777], np.int32)
+    else:
+        kv = W.make_indexer_mla(tag=994, L=1024, n_heads=16, k=64).kv
+    kv_d = S.kv_to_device(kv, DEV)
+    assert _hashes(kv_d) == _oracle_hashes(kv)

@@ -138,3 +138,33 @@ def test_hash_primitive_and_sensitivity():
     kv.token_table[0, live[5]] = f
     kv.token_table[0, dead[0]] = f + 1
     assert C.live_hash(kv, 0)[1] == h0[1] + 1
+
+
+def test_hash_same_for_every_addressing_mode():
+    """The hash follows the logical view: a paged pool read through its
+    block table, the same pool through the equivalent token table, and the
+    same keys and values laid out contiguously hash alike."""
+    import dataclasses
+    st = W.make_gqa_paged(tag=991, B=2, H=2, G=2, d=64, L=256, k=16, sink=4, local=16,
+                          seq_len=[256, 173])
+    kv = st.kv
+    kv.block_table[0, 5] = -1                        # an unmapped block: 16 dead tokens
+    tt = np.full((2, 256), -1, np.int32)
+    Kc = np.zeros((2, 2, 256, 64), np.uint16)
+    Vc = np.zeros((2, 2, 256, 64), np.uint16)
+    for b in range(2):
+        for t in range(int(kv.seq_len[b])):
+            p = int(kv.block_table[b, t // 16])
+            if p >= 0:
+                tt[b, t] = p * 16 + t % 16
+                Kc[b, :, t] = kv.k[p, :, t % 16]
+                Vc[b, :, t] = kv.v[p, :, t % 16]
+    via_bt = [C.live_hash(kv, b) for b in range(2)]
+    via_tt = [C.live_hash(dataclasses.replace(kv, block_table=None, token_table=tt), b)
+              for b in range(2)]
+    assert via_bt == via_tt
+    # contiguous storage has no dead tokens inside seq_len: compare sequence 1,
+    # whose blocks are all mapped
+    contig = dataclasses.replace(kv, k=Kc, v=Vc, block=0, block_table=None, token_table=None)
+    assert C.live_hash(contig, 1) == via_bt[1]
+    assert via_bt[0][1] == int(kv.seq_len[0]) - 16

@@ -342,13 +342,17 @@ __global__ __launch_bounds__(kThreads) void attend_mfma_kernel(
         for (int g = 0; g < GMAX; ++g) {
           if (g < G) {
           const float cg = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(corr), g));
+          // the 16 weights of head g first (scalars read back to back)
+          float pg[16];
+#pragma unroll
+          for (int t = 0; t < 16; ++t)
+            pg[t] = __int_as_float(
+                __builtin_amdgcn_readlane(__float_as_int(p[t & 3]), g + 16 * (t >> 2)));
           float a0 = acc[g][0] * cg, a1 = acc[g][1] * cg;
 #pragma unroll
           for (int t = 0; t < 16; ++t) {
-            const float pg = __int_as_float(
-                __builtin_amdgcn_readlane(__float_as_int(p[t & 3]), g + 16 * (t >> 2)));
-            a0 = fmaf(pg, vf[t][0], a0);
-            a1 = fmaf(pg, vf[t][1], a1);
+            a0 = fmaf(pg[t], vf[t][0], a0);
+            a1 = fmaf(pg[t], vf[t][1], a1);
           }
           acc[g][0] = a0;
           acc[g][1] = a1;

@@ -12,7 +12,9 @@
 // j = s * kSweep + w * kSeg + 256 g + 4 l + e (g < kGroups, e < 4), slot j
 // being position lo - o + j, so every load instruction reads 1 KB of
 // consecutive scores with 16-byte loads whatever the window's alignment.
-// Slots outside [o, o + n) read as -inf.
+// Slots outside [o, o + n) read as -inf.  Short rows use NG < kGroups groups
+// per lane (a wave then holds 256 NG slots of a 4096 NG-slot sweep), so every
+// wave still holds a share of the row and each pass runs over NG groups.
 #pragma once
 
 #include "skv_device.h"
@@ -101,10 +103,11 @@ struct RowSelLds {
 // Scores of the slots p0 + 256 g + e (s from row_base); slots outside the
 // window read as -inf.  A 16-byte load covers slots j .. j + 3 only when all
 // of them lie before the window end, so nothing past the row is read.
+template <int NG>
 __device__ __forceinline__ void slots_load(const float* s, const RowWindow& w, bool vec, int p0,
-                                           float (&v)[kGroups][4]) {
+                                           float (&v)[NG][4]) {
 #pragma unroll
-  for (int g = 0; g < kGroups; ++g) {
+  for (int g = 0; g < NG; ++g) {
     const int p = p0 + 256 * g;
     if (vec && p + 4 <= w.ns) {
       const float4 f = *(const float4*)(s + p);
@@ -125,16 +128,24 @@ __device__ __forceinline__ void slots_load(const float* s, const RowWindow& w, b
   }
 }
 
-// The slots p0 + 256 g + e of sweep sw for this lane (see the layout above).
-__device__ __forceinline__ void row_load(const float* s, const RowWindow& w, bool vec, int sw,
-                                         float (&v)[kGroups][4]) {
+// This lane's first slot of sweep sw with NG groups per lane.
+template <int NG>
+__device__ __forceinline__ int row_slot0(int sw) {
   const int lane = threadIdx.x & 63, wave = row_wave();
-  slots_load(s, w, vec, sw * kSweep + wave * kSeg + 4 * lane, v);
+  return sw * (kRowWaves * 256 * NG) + wave * (256 * NG) + 4 * lane;
 }
 
-__device__ __forceinline__ void row_keys(const float (&v)[kGroups][4], uint32_t (&kk)[kGroups][4]) {
+// The slots p0 + 256 g + e of sweep sw for this lane (see the layout above).
+template <int NG>
+__device__ __forceinline__ void row_load(const float* s, const RowWindow& w, bool vec, int sw,
+                                         float (&v)[NG][4]) {
+  slots_load(s, w, vec, row_slot0<NG>(sw), v);
+}
+
+template <int NG>
+__device__ __forceinline__ void row_keys(const float (&v)[NG][4], uint32_t (&kk)[NG][4]) {
 #pragma unroll
-  for (int g = 0; g < kGroups; ++g)
+  for (int g = 0; g < NG; ++g)
 #pragma unroll
     for (int e = 0; e < 4; ++e) kk[g][e] = score_key(v[g][e]);
 }
@@ -243,11 +254,12 @@ __device__ __forceinline__ void row_threshold(RowSelLds& L, int k, KeysReady&& k
 
 // Per group g, the lane's counts of keys above T (low 16 bits) and equal to T
 // (high 16 bits); returns the lane's total, packed the same way.
-__device__ __forceinline__ int row_counts(const uint32_t (&kk)[kGroups][4], uint32_t T,
-                                          int (&cg)[kGroups]) {
+template <int NG>
+__device__ __forceinline__ int row_counts(const uint32_t (&kk)[NG][4], uint32_t T,
+                                          int (&cg)[NG]) {
   int tot = 0;
 #pragma unroll
-  for (int g = 0; g < kGroups; ++g) {
+  for (int g = 0; g < NG; ++g) {
     int c = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
@@ -289,11 +301,11 @@ __device__ __forceinline__ void row_wave_offsets(RowSelLds& L, int lane_tot, int
 // The wave's selected keys in position order: emit(dst, g, e) for every key
 // taken, dst = its rank among the selected keys of the row.  oa / oe: keys
 // above / equal to T before this wave's positions.
-template <class Emit>
-__device__ __forceinline__ void row_emit(const uint32_t (&kk)[kGroups][4], const int (&cg)[kGroups],
+template <int NG, class Emit>
+__device__ __forceinline__ void row_emit(const uint32_t (&kk)[NG][4], const int (&cg)[NG],
                                          uint32_t T, int need_eq, int oa, int oe, Emit&& emit) {
 #pragma unroll
-  for (int g = 0; g < kGroups; ++g) {
+  for (int g = 0; g < NG; ++g) {
     const int ig = wave_incl_scan(cg[g]);
     const int gt = wave_total(ig);
     int ab = oa + ((ig - cg[g]) & 0xffff), eb = oe + ((ig - cg[g]) >> 16);

@@ -33,6 +33,8 @@
 // with the keys in registers: one kernel beats two or three there.
 // The finishing kernel zeroes the row's histogram and list counter, so a
 // zero-filled workspace stays valid across calls.
+#include <type_traits>
+
 #include "skv_rowsel.h"
 #include "skv_topk.h"
 
@@ -268,14 +270,14 @@ __device__ __forceinline__ void bitmap_prefix(const uint32_t* map, int* pre, int
 // map_b[map_a[row][p]], the positions gathered in LDS first and mapped in one
 // pass; 2 mapped as each key is emitted.  A compile-time choice, so every
 // instantiation has one kind of store in its emission loop.
-template <bool RES, int MAP>
+template <bool RES, int MAP, int NG = kGroups>
 __device__ __forceinline__ void row_select_alone(const float* scores, int row, int H, int L_max,
                                  const int32_t* lo_p, const int32_t* hi_p, int k,
                                  uint32_t* ghist_row, bool hist_ready, int32_t* orow,
                                  int32_t* count, const int32_t* map_a, const int32_t* map_b,
                                  int map_ld, RowSelLds& L, uint32_t* klist, int& klist_n,
                                  uint32_t* min_key = nullptr) {
-  const int lane = threadIdx.x & 63, wave = row_wave();
+  const int lane = threadIdx.x & 63;
   RowWindow w = row_window(lo_p, hi_p, row / H, L_max);
   bool vec;
   const float* s = row_base(scores, (int64_t)row * L_max, w, &vec);
@@ -285,8 +287,9 @@ __device__ __forceinline__ void row_select_alone(const float* scores, int row, i
   // RES: the row's scores are loaded now and turned into keys once the
   // first digit's search (from the scan's histogram) has overlapped their
   // arrival
-  uint32_t kr[RES ? kGroups : 1][4];
-  float fr[RES ? kGroups : 1][4];
+  static_assert(RES || NG == kGroups, "short rows keep their keys in registers");
+  uint32_t kr[RES ? NG : 1][4];
+  float fr[RES ? NG : 1][4];
   if constexpr (RES) row_load(s, w, vec, 0, fr);
 
   // F(keys, sweep) for every sweep, the next sweep's loads in flight while
@@ -319,9 +322,10 @@ __device__ __forceinline__ void row_select_alone(const float* scores, int row, i
       const int nl = min(klist_n, kListCap);
       for (int i = threadIdx.x; i < nl; i += kRowThreads) f(klist[i]);
     } else {
-      for_sweeps([&](const uint32_t (&kk)[kGroups][4], int) {
+      for_sweeps([&](const auto& kk, int) {
+        constexpr int ng = sizeof(kk) / sizeof(kk[0]);
 #pragma unroll
-        for (int g = 0; g < kGroups; ++g)
+        for (int g = 0; g < ng; ++g)
 #pragma unroll
           for (int e = 0; e < 4; ++e) f(kk[g][e]);
       });
@@ -333,10 +337,11 @@ __device__ __forceinline__ void row_select_alone(const float* scores, int row, i
     if (RES || in_bin > kListCap) return;
     if (threadIdx.x == 0) klist_n = 0;
     lds_barrier();
-    for_sweeps([&](const uint32_t (&kk)[kGroups][4], int) {
+    for_sweeps([&](const auto& kk, int) {
+      constexpr int ng = sizeof(kk) / sizeof(kk[0]);
       int c = 0;
 #pragma unroll
-      for (int g = 0; g < kGroups; ++g)
+      for (int g = 0; g < ng; ++g)
 #pragma unroll
         for (int e = 0; e < 4; ++e) c += (kk[g][e] >> 20) == (uint32_t)b0;
       const int incl = wave_incl_scan(c);
@@ -345,7 +350,7 @@ __device__ __forceinline__ void row_select_alone(const float* scores, int row, i
       int o = __builtin_amdgcn_readlane(base, 63) + incl - c;
       if (c) {
 #pragma unroll
-        for (int g = 0; g < kGroups; ++g)
+        for (int g = 0; g < ng; ++g)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             if ((kk[g][e] >> 20) == (uint32_t)b0) {
@@ -382,22 +387,22 @@ __device__ __forceinline__ void row_select_alone(const float* scores, int row, i
   int a_base = 0, e_base = 0;   // keys above / equal to T in earlier sweeps
   uint32_t mk = 0xffffffffu;    // smallest selected key of this lane
   for (int sw = 0; sw < n_sweeps; ++sw) {
-    uint32_t kk[kGroups][4];
+    uint32_t kk[NG][4];
     if constexpr (RES) {
 #pragma unroll
-      for (int g = 0; g < kGroups; ++g)
+      for (int g = 0; g < NG; ++g)
 #pragma unroll
         for (int e = 0; e < 4; ++e) kk[g][e] = kr[g][e];
     } else {
-      float f[kGroups][4];
+      float f[NG][4];
       row_load(s, w, vec, sw, f);
       row_keys(f, kk);
     }
-    int cg[kGroups];
+    int cg[NG];
     const int lt = row_counts(kk, T, cg);
     int oa, oe, ta, te;
     row_wave_offsets(L, lt, &oa, &oe, &ta, &te);
-    const int pos0 = w.lo - w.o + sw * kSweep + wave * kSeg + 4 * lane;
+    const int pos0 = w.lo - w.o + row_slot0<NG>(sw);
     row_emit(kk, cg, T, need_eq, a_base + oa, e_base + oe, [&](int dst, int g, int e) {
       if (dst < k) {
         const int p = pos0 + 256 * g + e;
@@ -427,8 +432,9 @@ __device__ __forceinline__ void row_select_alone(const float* scores, int row, i
 
 // Grid rows, 1024 threads: rows of one sweep, each selected by its workgroup
 // alone with the keys in registers (one kernel instead of two or three);
-// ghist: the rows' histograms from the scan, or null.
-template <int MAP>
+// ghist: the rows' histograms from the scan, or null.  NG groups of 4 keys
+// per lane: rows of up to 4096 NG slots.
+template <int MAP, int NG>
 __global__ __launch_bounds__(kRowThreads) void topk_alone_kernel(
     const float* scores, int H, int L_max, const int32_t* lo_p, const int32_t* hi_p, int k,
     uint32_t* ghist, int32_t* idx, int32_t* count, const int32_t* map_a, const int32_t* map_b,
@@ -436,7 +442,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_alone_kernel(
   __shared__ RowSelLds L;
   __shared__ int klist_n;
   const int row = blockIdx.x;
-  row_select_alone<true, MAP>(scores, row, H, L_max, lo_p, hi_p, k,
+  row_select_alone<true, MAP, NG>(scores, row, H, L_max, lo_p, hi_p, k,
                          ghist ? ghist + (int64_t)row * kBins : nullptr, ghist != nullptr,
                          idx + (int64_t)row * k, count, map_a, map_b, map_ld, L, nullptr, klist_n);
 }
@@ -728,15 +734,26 @@ hipError_t launch_topk(const float* scores, int rows, int H, int L_max, const in
   if (row_slots_max(L_max) <= kSweep) {
     // rows of one sweep: one workgroup per row
     uint32_t* gh = hist_ready ? ws.hist : nullptr;
-    if (map == 0)
-      topk_alone_kernel<0><<<rows, kRowThreads, 0, s>>>(scores, H, L_max, lo, hi, k, gh, idx, count,
-                                                        map_a, map_b, map_ld);
-    else if (map == 1)
-      topk_alone_kernel<1><<<rows, kRowThreads, 0, s>>>(scores, H, L_max, lo, hi, k, gh, idx, count,
-                                                        map_a, map_b, map_ld);
-    else
-      topk_alone_kernel<2><<<rows, kRowThreads, 0, s>>>(scores, H, L_max, lo, hi, k, gh, idx, count,
-                                                        map_a, map_b, map_ld);
+    // the fewest groups per lane that hold the row: every pass over the
+    // keys is that much shorter
+    const int slots = row_slots_max(L_max);
+    const int ng = slots <= 4096 ? 1 : slots <= 8192 ? 2 : slots <= 16384 ? 4
+                 : slots <= 24576 ? 6 : kGroups;
+    auto go = [&](auto kern) {
+      kern<<<rows, kRowThreads, 0, s>>>(scores, H, L_max, lo, hi, k, gh, idx, count, map_a, map_b,
+                                        map_ld);
+    };
+    auto by_ng = [&](auto map_c) {
+      constexpr int M = decltype(map_c)::value;
+      if (ng == 1) go(topk_alone_kernel<M, 1>);
+      else if (ng == 2) go(topk_alone_kernel<M, 2>);
+      else if (ng == 4) go(topk_alone_kernel<M, 4>);
+      else if (ng == 6) go(topk_alone_kernel<M, 6>);
+      else go(topk_alone_kernel<M, kGroups>);
+    };
+    if (map == 0) by_ng(std::integral_constant<int, 0>{});
+    else if (map == 1) by_ng(std::integral_constant<int, 1>{});
+    else by_ng(std::integral_constant<int, 2>{});
     return hipGetLastError();
   }
   if (!hist_ready)

@@ -12,6 +12,7 @@ Default workload (the GQA paged decode the metric is quoted on):
   top-k digit) -> exact top-k fused with gather + split attention -> merge.
 
 Other workloads (--workload), each timed the same way:
+  gqa_paged_long  the same at L = 131072 (the long-context scan + gather)
   single_head   B=1, L=4096 fp32 contiguous, planted query, top-64
   token_pool    B=32, 8 KV heads, G=1, L=65536, token table, 50 % dead
   indexer_mla   B=1, indexer keys d=128 + shared latent 576 (value 512),
@@ -55,7 +56,7 @@ sys.path.insert(0, HERE)
 
 PEAK_HBM_GBPS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
-DENSE = ("gqa_paged", "token_pool", "single_head", "indexer_mla")
+DENSE = ("gqa_paged", "gqa_paged_long", "token_pool", "single_head", "indexer_mla")
 WORKLOADS = DENSE + ("paris", "paris_encode", "paris_decode", "compact")
 PARIS_UPDATE = 512      # Update Buffer tokens (the page's experiments use 256 or 512)
 
@@ -302,6 +303,7 @@ def step_percentiles(calls):
 def make_dense(name):
     import workloads as W
     return {"gqa_paged": W.make_gqa_paged, "token_pool": W.make_token_pool,
+            "gqa_paged_long": lambda: W.make_gqa_paged(L=131072),
             "single_head": W.make_single_head, "indexer_mla": W.make_indexer_mla}[name]()
 
 

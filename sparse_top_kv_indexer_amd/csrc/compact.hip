@@ -88,41 +88,57 @@ __global__ __launch_bounds__(256) void zero_hash_kernel(uint64_t* hash, int32_t*
   }
 }
 
-// Grid (ceil(L_max / 32), B): tokens 32 x .. 32 x + 31 of sequence b.  A
-// row (token, head h, K or V) is cut into P <= 256 16-byte pieces; thread
-// i < (256 / P) P takes piece i % P of the rows hr = i / P, i / P + 256 / P,
-// ... (hr = h R + r) of every token, four tokens' loads in flight at a time.
-// Per 64-bit word j of a row: mix64((s + (j + 1) gamma) ^ w_j) with
-// s = mix64((t H + h) R + r); per-thread sums, a wave sum, one 64-bit atomic
-// per wave.
+constexpr int kHashTok = 512;   // tokens per hashing workgroup
+
+// Grid (ceil(L_max / kHashTok), B): tokens kHashTok x .. of sequence b.  The
+// chunk's live tokens are gathered first (any order: the hash is a sum), so
+// dead tokens cost nothing after that.  A row (token, head h, K or V) is cut
+// into P <= 256 16-byte pieces; thread i < (256 / P) P takes piece i % P of
+// the rows hr = i / P, i / P + 256 / P, ... (hr = h R + r) of every live
+// token, eight tokens' loads in flight at a time.  Per 64-bit word j of a
+// row: mix64((s + (j + 1) gamma) ^ w_j) with s = mix64((t H + h) R + r);
+// per-thread sums, one workgroup sum, one 64-bit atomic per workgroup (the
+// sequence's sum is where every workgroup of the sequence meets, so the
+// atomics are kept few).
 __global__ __launch_bounds__(256) void live_hash_kernel(KvArgs kv, int P, uint64_t* hash,
                                                         int32_t* count) {
-  __shared__ int64_t sl[32];
-  const int b = blockIdx.y, t0 = blockIdx.x * 32;
-  if (threadIdx.x < 32) sl[threadIdx.x] = slot_of(kv, b, t0 + threadIdx.x);
+  __shared__ int64_t ls[kHashTok];   // live slots of the chunk
+  __shared__ int lt[kHashTok];       // their tokens
+  __shared__ uint64_t wsum[4];
+  __shared__ int n_live;
+  const int b = blockIdx.y, t0 = blockIdx.x * kHashTok;
+  if (threadIdx.x == 0) n_live = 0;
   __syncthreads();
+  for (int i = threadIdx.x; i < kHashTok; i += 256) {
+    const int64_t slot = slot_of(kv, b, t0 + i);
+    if (slot >= 0) {
+      const int j = atomicAdd(&n_live, 1);
+      ls[j] = slot;
+      lt[j] = t0 + i;
+    }
+  }
+  __syncthreads();
+  const int n = n_live;
   const int R = kv.v ? 2 : 1, HR = kv.H * R;
   const int es = kv.bf16 ? 2 : 4;
   const int p = threadIdx.x % P, rows_par = 256 / P;
   const int q0 = threadIdx.x < rows_par * P ? threadIdx.x / P : HR;   // the rest sit out
   const uint64_t gamma = 0x9e3779b97f4a7c15ull;
   uint64_t acc = 0;
-  for (int tb = 0; tb < 32; tb += 4) {
+  for (int tb = 0; tb < n; tb += 8) {
     for (int hr = q0; hr < HR; hr += rows_par) {
       const int h = hr / R, r = hr - h * R;
       const int d = r ? kv.d_v : kv.d_k;
       const char* base = (const char*)(r ? kv.v : kv.k);
-      u32x4_t w[4];
+      u32x4_t w[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int64_t slot = sl[tb + u];
-        if (slot >= 0)
-          w[u] = *(const u32x4_t*)(base + row_elem(kv, b, h, slot, d) * es + 16 * p);
-      }
+      for (int u = 0; u < 8; ++u)
+        if (tb + u < n)
+          w[u] = *(const u32x4_t*)(base + row_elem(kv, b, h, ls[tb + u], d) * es + 16 * p);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (sl[tb + u] < 0) continue;
-        const uint64_t s = mix64(((uint64_t)(t0 + tb + u) * kv.H + h) * R + r);
+      for (int u = 0; u < 8; ++u) {
+        if (tb + u >= n) continue;
+        const uint64_t s = mix64(((uint64_t)lt[tb + u] * kv.H + h) * R + r);
         const uint64_t w0 = (uint64_t)w[u][0] | ((uint64_t)w[u][1] << 32);
         const uint64_t w1 = (uint64_t)w[u][2] | ((uint64_t)w[u][3] << 32);
         acc += mix64((s + (uint64_t)(2 * p + 1) * gamma) ^ w0);
@@ -132,11 +148,12 @@ __global__ __launch_bounds__(256) void live_hash_kernel(KvArgs kv, int P, uint64
   }
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) acc += shfl_xor64(acc, m);
-  const int lane = threadIdx.x & 63;
-  if (lane == 0 && acc) atomicAdd((unsigned long long*)&hash[b], (unsigned long long)acc);
-  if (threadIdx.x < 64) {
-    const int n = __popcll(__ballot(lane < 32 && sl[lane & 31] >= 0));
-    if (lane == 0 && n) atomicAdd(&count[b], n);
+  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint64_t tot = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    if (tot) atomicAdd((unsigned long long*)&hash[b], (unsigned long long)tot);
+    if (n) atomicAdd(&count[b], n);
   }
 }
 
@@ -312,8 +329,8 @@ skv_status sparsekv_live_hash(const skv_kv* kv, uint64_t* hash, int32_t* count,
   KvArgs a = kv_args(kv);
   if (!kv->v) a.d_v = kv->d_k;
   zero_hash_kernel<<<1, 256, 0, stream>>>(hash, count, kv->B);
-  live_hash_kernel<<<dim3((kv->L_max + 31) / 32, kv->B), 256, 0, stream>>>(a, row / 16, hash,
-                                                                          count);
+  live_hash_kernel<<<dim3((kv->L_max + kHashTok - 1) / kHashTok, kv->B), 256, 0, stream>>>(
+      a, row / 16, hash, count);
   return hipGetLastError() == hipSuccess ? SKV_OK : SKV_ELAUNCH;
 }
 

@@ -26,6 +26,7 @@
 #include <algorithm>
 
 #include "skv_device.h"
+#include "skv_topk.h"
 
 namespace skv {
 
@@ -43,7 +44,7 @@ struct HistArgs {
   const int32_t* hi;
   uint32_t* hist;   // [B*H][4096]
   // survivors (threshold prefilter): keys of the window with score >= thr[row]
-  // go to the row's list [row][cap] through the fill counter ctr[row]
+  // go to the row's list [row][cap] through the fill counter ctr[row * kCtrStride]
   const float* thr;
   uint32_t* lkey;
   int32_t* lpos;
@@ -394,7 +395,7 @@ __global__ __launch_bounds__(kThreads) void score_stream_kernel(KvArgs kv, const
       lds_barrier();
       const int nsv = sv_n;
       if (threadIdx.x == 0)
-        sv_base = nsv ? atomicAdd(&ha.ctr[r], nsv > kSvCap ? kSvOverflow : nsv) : 0;
+        sv_base = nsv ? atomicAdd(&ha.ctr[(int64_t)r * kCtrStride], nsv > kSvCap ? kSvOverflow : nsv) : 0;
       lds_barrier();
       const int base = sv_base;
       for (int i = threadIdx.x; i < min(nsv, kSvCap); i += kThreads)

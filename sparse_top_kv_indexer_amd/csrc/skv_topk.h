@@ -10,18 +10,46 @@
 
 namespace skv {
 
-constexpr int kSlice = 8192;        // row slots per listing workgroup
+// A listing workgroup covers 1024 ng row slots (256 threads, ng groups of 4
+// slots per lane, ng in 1, 2, 4, 8): few long rows get small slices so the
+// listing still spreads over the whole chip, many rows get large ones so the
+// per-workgroup work (reading the row's histogram) stays small.
+constexpr int kSliceUnit = 1024;    // row slots per listing workgroup and group per lane
 constexpr int kRowList = 16384;     // keys a row's list holds
-constexpr int kMaxSlices = 4096;    // rows of up to kSlice * kMaxSlices slots
+constexpr int kMaxSlices = 4096;    // rows of up to 8 * kSliceUnit * kMaxSlices slots
+constexpr int kListWgs = 2048;      // listing workgroups a call aims for
+// A row's list counter sits alone in a 256-byte line: the listing workgroups
+// of every row add to their row's counter, and counters sharing a line would
+// queue behind each other at the one place device atomics are resolved.
+constexpr int kCtrStride = 64;
 
-__host__ __device__ inline int topk_slices(int L_max) {
+__host__ __device__ inline int topk_slices_ng(int L_max, int ng) {
   const int64_t slots = L_max % 4 == 0 ? (int64_t)L_max : (int64_t)L_max + 3;
-  return (int)((slots + kSlice - 1) / kSlice);
+  const int64_t per = (int64_t)kSliceUnit * ng;
+  return (int)((slots + per - 1) / per);
+}
+
+// Groups per lane of the listing workgroups of `rows` rows: the largest of
+// 8, 4, 2, 1 that still gives kListWgs workgroups, or the smallest that
+// keeps a row within kMaxSlices slices.
+inline int topk_slice_groups(int rows, int L_max) {
+  int ng = 8;
+  while (ng > 1 && (int64_t)rows * topk_slices_ng(L_max, ng) < kListWgs &&
+         topk_slices_ng(L_max, ng / 2) <= kMaxSlices)
+    ng /= 2;
+  return ng;
+}
+
+// Slice entries a row's workspace holds: the most any call may use.
+__host__ __device__ inline int topk_slices(int L_max) {
+  int ng = 1;
+  while (ng < 8 && topk_slices_ng(L_max, ng) > kMaxSlices) ng *= 2;
+  return topk_slices_ng(L_max, ng);
 }
 
 struct TopkWs {
   uint32_t* hist;   // [rows][4096]
-  int32_t* ctr;     // [rows] keys listed so far
+  int32_t* ctr;     // [rows][kCtrStride] keys listed so far (element 0 of each line)
   int32_t* meta;    // [rows][2]: smallest listed key, listed count (-1: too many)
   int32_t* slc;     // [rows][slices][2]: list offset and count of each slice
   uint32_t* lkey;   // [rows][kRowList] listed keys, slice by slice in position order
@@ -29,7 +57,7 @@ struct TopkWs {
 
   static size_t align(size_t x) { return (x + 255) & ~(size_t)255; }
   static size_t zero_bytes(int rows) {
-    return align((size_t)rows * 4096 * 4) + align((size_t)rows * 4);
+    return align((size_t)rows * 4096 * 4) + align((size_t)rows * kCtrStride * 4);
   }
   static size_t bytes(int rows, int L_max) {
     return zero_bytes(rows) + align((size_t)rows * 8) +
@@ -41,7 +69,7 @@ struct TopkWs {
     w.hist = (uint32_t*)c;
     c += align((size_t)rows * 4096 * 4);
     w.ctr = (int32_t*)c;
-    c += align((size_t)rows * 4);
+    c += align((size_t)rows * kCtrStride * 4);
     w.meta = (int32_t*)c;
     c += align((size_t)rows * 8);
     w.slc = (int32_t*)c;

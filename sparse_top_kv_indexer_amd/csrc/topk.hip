@@ -13,7 +13,9 @@
 //   0. the row's top-12-bit histogram: built by the score scan when the two
 //      are fused, else by topk_hist_kernel (one 256-thread workgroup per
 //      8192-slot slice, LDS atomics, non-zero bins added into the row's);
-//   1. topk_compact_kernel, one workgroup per slice: every workgroup finds
+//   1. topk_compact_kernel, one workgroup per slice of 1024, 2048, 4096 or
+//      8192 slots (the largest that still gives about 2048 workgroups, so a
+//      few long rows spread over every compute unit): every workgroup finds
 //      the bin b0 that holds the k-th largest key from the histogram and
 //      lists its slice's keys in bins >= b0, with their positions, in
 //      position order (a DPP prefix sum per group of 4 slots and one atomic
@@ -42,12 +44,13 @@ namespace skv {
 
 namespace {
 
-constexpr int kSliceThreads = 256;           // 4 waves x kSeg slots = kSlice
-static_assert(kSliceThreads / 64 * kSeg == kSlice, "slice layout");
+constexpr int kSliceThreads = 256;           // 4 waves x 256 NG slots = kSliceUnit NG
+static_assert(kSliceThreads * 4 == kSliceUnit, "slice layout");
 constexpr int kListCap = 16384;              // fallback: LDS list of the threshold bin's keys
 
 // Window of row `row`, its read base and this lane's first slot in slice sl
-// (slots sl * kSlice + wave * kSeg + 256 g + 4 lane + e).
+// of NG groups per lane (slots sl * kSliceUnit NG + wave * 256 NG + 256 g +
+// 4 lane + e, g < NG).
 struct SliceView {
   RowWindow w;
   const float* s;
@@ -55,12 +58,13 @@ struct SliceView {
   int p0;
 };
 
+template <int NG>
 __device__ __forceinline__ SliceView slice_view(const float* scores, int row, int H, int L_max,
                                                 const int32_t* lo_p, const int32_t* hi_p, int sl) {
   SliceView v;
   v.w = row_window(lo_p, hi_p, row / H, L_max);
   v.s = row_base(scores, (int64_t)row * L_max, v.w, &v.vec);
-  v.p0 = sl * kSlice + (threadIdx.x >> 6) * kSeg + 4 * (threadIdx.x & 63);
+  v.p0 = sl * kSliceUnit * NG + (threadIdx.x >> 6) * 256 * NG + 4 * (threadIdx.x & 63);
   return v;
 }
 
@@ -72,8 +76,8 @@ __global__ __launch_bounds__(kSliceThreads) void topk_hist_kernel(const float* s
                                                                   uint32_t* ghist, int n_slices) {
   __shared__ uint32_t lh[kBins];
   const int row = blockIdx.x / n_slices, sl = blockIdx.x - row * n_slices;
-  const SliceView v = slice_view(scores, row, H, L_max, lo_p, hi_p, sl);
-  if (sl * kSlice >= v.w.ns) return;   // the whole slice lies past the window
+  const SliceView v = slice_view<kGroups>(scores, row, H, L_max, lo_p, hi_p, sl);
+  if (sl * kSliceUnit * kGroups >= v.w.ns) return;   // the whole slice lies past the window
   float f[kGroups][4];
   slots_load(v.s, v.w, v.vec, v.p0, f);
 #pragma unroll
@@ -96,7 +100,8 @@ __global__ __launch_bounds__(kSliceThreads) void topk_hist_kernel(const float* s
 }
 
 // -------------------------------------------------------------- listing --
-// Grid rows * slices, 256 threads.
+// Grid rows * slices of NG groups per lane, 256 threads.
+template <int NG>
 __global__ __launch_bounds__(kSliceThreads) void topk_compact_kernel(
     const float* scores, int H, int L_max, const int32_t* lo_p, const int32_t* hi_p, int k,
     TopkWs ws, int n_slices) {
@@ -104,9 +109,9 @@ __global__ __launch_bounds__(kSliceThreads) void topk_compact_kernel(
   __shared__ int sh[3];   // smallest listed key, listed count, this slice's list offset
   const int row = blockIdx.x / n_slices, sl = blockIdx.x - row * n_slices;
   const int lane = threadIdx.x & 63, wave = row_wave();
-  const SliceView v = slice_view(scores, row, H, L_max, lo_p, hi_p, sl);
-  const bool any = sl * kSlice < v.w.ns;
-  float f[kGroups][4];
+  const SliceView v = slice_view<NG>(scores, row, H, L_max, lo_p, hi_p, sl);
+  const bool any = sl * kSliceUnit * NG < v.w.ns;
+  float f[NG][4];
   if (any) slots_load(v.s, v.w, v.vec, v.p0, f);
 
   // the bin of the k-th largest key: thread t holds bins 16 t .. 16 t + 15
@@ -164,10 +169,10 @@ __global__ __launch_bounds__(kSliceThreads) void topk_compact_kernel(
   }
 
   // this slice's keys >= lower, in position order
-  uint32_t kk[kGroups][4];
-  int cg[kGroups], ig[kGroups], wt = 0;
+  uint32_t kk[NG][4];
+  int cg[NG], ig[NG], wt = 0;
 #pragma unroll
-  for (int g = 0; g < kGroups; ++g) {
+  for (int g = 0; g < NG; ++g) {
     int n = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -187,7 +192,7 @@ __global__ __launch_bounds__(kSliceThreads) void topk_compact_kernel(
     t_wg += wlist[u];
   }
   if (threadIdx.x == 0) {
-    const int base = t_wg ? atomicAdd(&ws.ctr[row], t_wg) : 0;
+    const int base = t_wg ? atomicAdd(&ws.ctr[(int64_t)row * kCtrStride], t_wg) : 0;
     sh[2] = base;
     ws.slc[((int64_t)row * n_slices + sl) * 2] = base;
     ws.slc[((int64_t)row * n_slices + sl) * 2 + 1] = t_wg;
@@ -198,7 +203,7 @@ __global__ __launch_bounds__(kSliceThreads) void topk_compact_kernel(
   int32_t* lp = ws.lpos + (int64_t)row * kRowList;
   const int pos0 = v.w.lo - v.w.o + v.p0;
 #pragma unroll
-  for (int g = 0; g < kGroups; ++g) {
+  for (int g = 0; g < NG; ++g) {
     int d = o + ig[g] - cg[g];
     if (cg[g]) {
 #pragma unroll
@@ -496,7 +501,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_finish_kernel(
   const int m = min(run, kRowList);
   if (threadIdx.x == 0) {
     s_off[n_slices] = run;
-    ws.ctr[row] = 0;   // for the next call
+    ws.ctr[(int64_t)row * kCtrStride] = 0;   // for the next call
   }
   lds_barrier();
   // list ranks kPer * tid .. kPer * tid + kPer - 1: the slice holding a rank
@@ -616,7 +621,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_survivor_kernel(
   constexpr int kPer = kRowList / kRowThreads;   // survivors per lane
   const int row = blockIdx.x;
   int32_t* orow = idx + (int64_t)row * k;
-  const int m = ws.ctr[row];
+  const int m = ws.ctr[(int64_t)row * kCtrStride];
   const float thr_old = thr[row];
   const RowWindow w = row_window(lo_p, hi_p, row / H, L_max);
   const bool listed = m >= k && m <= kRowList && w.n <= kMapWords * 32;
@@ -711,7 +716,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_survivor_kernel(
     thr[row] = (thr_old == -INFINITY || kth == -INFINITY) ? kth
                                                           : alpha * kth + (1.f - alpha) * thr_old;
     if (used) used[row] = listed ? 1 : 0;
-    ws.ctr[row] = 0;
+    ws.ctr[(int64_t)row * kCtrStride] = 0;
   }
 }
 
@@ -727,9 +732,11 @@ hipError_t launch_topk(const float* scores, int rows, int H, int L_max, const in
                        const int32_t* map_b, int map_ld) {
   if (rows <= 0) return hipSuccess;
   const TopkWs ws = TopkWs::carve(wsp, rows, L_max);
-  const int ns = topk_slices(L_max);
-  if (ns > kMaxSlices || (int64_t)rows * ns > 0x7fffffff) return hipErrorInvalidValue;
-  const unsigned grid = (unsigned)(rows * ns);
+  const int ng_l = topk_slice_groups(rows, L_max);
+  const int ns = topk_slices_ng(L_max, ng_l);           // listing slices per row
+  const int ns_h = topk_slices_ng(L_max, kGroups);      // histogram slices per row
+  if (ns > kMaxSlices || ns > topk_slices(L_max) || (int64_t)rows * ns > 0x7fffffff)
+    return hipErrorInvalidValue;
   const int map = map_a ? (k <= kBins ? 1 : 2) : 0;
   if (row_slots_max(L_max) <= kSweep) {
     // rows of one sweep: one workgroup per row
@@ -757,8 +764,15 @@ hipError_t launch_topk(const float* scores, int rows, int H, int L_max, const in
     return hipGetLastError();
   }
   if (!hist_ready)
-    topk_hist_kernel<<<grid, kSliceThreads, 0, s>>>(scores, H, L_max, lo, hi, ws.hist, ns);
-  topk_compact_kernel<<<grid, kSliceThreads, 0, s>>>(scores, H, L_max, lo, hi, k, ws, ns);
+    topk_hist_kernel<<<(unsigned)(rows * ns_h), kSliceThreads, 0, s>>>(scores, H, L_max, lo, hi,
+                                                                         ws.hist, ns_h);
+  auto list = [&](auto kern) {
+    kern<<<(unsigned)(rows * ns), kSliceThreads, 0, s>>>(scores, H, L_max, lo, hi, k, ws, ns);
+  };
+  if (ng_l == 1) list(topk_compact_kernel<1>);
+  else if (ng_l == 2) list(topk_compact_kernel<2>);
+  else if (ng_l == 4) list(topk_compact_kernel<4>);
+  else list(topk_compact_kernel<kGroups>);
   if (map == 0)
     topk_finish_kernel<0><<<rows, kRowThreads, 0, s>>>(scores, H, L_max, lo, hi, k, ws, ns, idx,
                                                        count, map_a, map_b, map_ld);

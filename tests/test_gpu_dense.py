@@ -281,6 +281,15 @@ def test_gqa_paged_full_size_sampled_rows():
 
 
 @pytest.mark.slow
+def test_gqa_paged_long_context_sampled_rows():
+    """The GQA decode at L = 131072: rows longer than one workgroup's sweep go
+    through the sliced top-k."""
+    st = W.make_gqa_paged(L=131072)
+    rows = [(0, 2), (3, 6)]
+    assert _end_to_end(st, rows=rows) == 0
+
+
+@pytest.mark.slow
 def test_token_pool_full_size_sampled_rows():
     st = W.make_token_pool()
     rows = [(0, 0), (13, 4), (31, 7)]

@@ -147,10 +147,10 @@ def test_retrieve_repeated_on_one_workspace():
         torch.cuda.synchronize()
         _check_retrieval(pc, P.retrieve(pc, ref_index, lv), idx, n_cand, tr)
     # kept zero between calls: the vote totals [H][98] i32, then the top-k
-    # histograms [H][4096] u32 and list counters [H] i32
+    # histograms [H][4096] u32 and list counters (one 256-byte line per head)
     al = lambda x: (x + 255) // 256 * 256
     w = ws.view(torch.uint8).cpu().numpy()
-    assert not w[: al(p.H * 98 * 4) + al(p.H * 4096 * 4) + p.H * 4].any()
+    assert not w[: al(p.H * 98 * 4) + al(p.H * 4096 * 4) + p.H * 256].any()
 
 
 def test_attention_over_retrieved_set():

@@ -230,7 +230,8 @@ def test_exact_ties_lowest_index_wins():
 @pytest.mark.parametrize("L,k,seed", [(1000, 37, 0), (4096, 2048, 1), (32768, 2048, 2),
                                       (40000, 700, 3), (131072, 2048, 4), (5000, 4999, 5),
                                       (32768, 2048, 6), (70001, 3000, 7), (32767, 1000, 8),
-                                      (32765, 2048, 9), (4097, 100, 10)])
+                                      (32765, 2048, 9), (4097, 100, 10), (200003, 2500, 11),
+                                      (150001, 2048, 12)])
 def test_topk_kernel_on_oracle_inputs(L, k, seed):
     """Synthetic rows with ties, -0.0 / +0.0, -inf and windows; the GPU set must
     equal the oracle's set exactly.  Row lengths that are not multiples of 4
@@ -256,6 +257,25 @@ def test_topk_kernel_on_oracle_inputs(L, k, seed):
             assert cnt[b, h] == ref.size
             assert idx[b, h, : ref.size].tolist() == sorted(ref.tolist()), (b, h)
             assert np.all(idx[b, h, ref.size:] == -1)
+
+
+@pytest.mark.parametrize("B,H,L,k", [(32, 8, 65536, 2048), (16, 4, 131072, 2048),
+                                     (8, 4, 131072, 4000), (1, 1, 131072, 2048)])
+def test_topk_listing_slice_sizes(B, H, L, k):
+    """Many rows take 8192-slot listing slices, fewer rows smaller ones (4096,
+    2048, 1024 slots); every row's set equals the oracle's, windows ragged."""
+    say("topk slices", B, H, L, k)
+    s = W.normal_f32(W.seed_of(1100 + B), 0, (B, H, L)) * 10
+    lo = (np.arange(B, dtype=np.int32) * 37) % 1000
+    hi = (L - (np.arange(B, dtype=np.int32) * 53) % 999).astype(np.int32)
+    sd = torch.from_numpy(s).to(DEV)
+    idx, cnt = S.sparsekv_topk(sd, S.to_device(lo, DEV), S.to_device(hi, DEV), k)
+    idx, cnt = idx.cpu().numpy(), cnt.cpu().numpy()
+    for b in range(B):
+        for h in range(H):
+            ref = D.select_topk(s[b, h].astype(np.float64), int(lo[b]), int(hi[b]), k)
+            assert cnt[b, h] == ref.size
+            assert idx[b, h, : ref.size].tolist() == sorted(ref.tolist()), (b, h)
 
 
 # ------------------------------------------------------------ attention alone

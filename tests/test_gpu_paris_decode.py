@@ -88,8 +88,8 @@ def test_decode_loop_with_update_buffer():
 def test_decode_loop_candidate_slices_grow():
     """With beta = 1 every entry is a candidate, and the flush takes C from
     32760 to 32776: the top-k over the candidates goes from one workgroup per
-    row to the sliced path and its per-slice table grows (4 -> 5 slices of
-    8 heads), moving what follows it in the workspace -- the regions kept
+    row to the sliced path and its per-slice table grows (32 -> 33 entries
+    per head), moving what follows it in the workspace -- the regions kept
     zero between calls stay at fixed offsets."""
     p = W.make_paris(tag=72, H=8, G=1, L=33000, sink=4, local=32, rho=1.0, beta=1.0)
     say("paris decode", p.name, "L0 32796 steps 24 update 16")

@@ -142,7 +142,8 @@ __global__ __launch_bounds__(kSliceThreads) void topk_compact_kernel(
     sh[0] = k_sel <= 0 ? -1 : 1;   // nothing, or every finite key (key >= 1)
     sh[1] = k_sel <= 0 ? 0 : total;
   }
-  if (k_sel > 0 && k_sel < total) {
+  // only the thread whose 16 bins hold the k-th key walks them
+  if (k_sel > 0 && k_sel < total && total - upto < k_sel && k_sel <= total - upto + tsum) {
     int above = total - upto;   // keys in the bins above this thread's
 #pragma unroll
     for (int j = 15; j >= 0; --j) {
@@ -168,7 +169,8 @@ __global__ __launch_bounds__(kSliceThreads) void topk_compact_kernel(
     ws.meta[2 * row + 1] = listed;
   }
 
-  // this slice's keys >= lower, in position order
+  // this slice's keys >= lower, in position order (lower >= 1, so an empty
+  // slot's key 0 is never listed)
   uint32_t kk[NG][4];
   int cg[NG], ig[NG], wt = 0;
 #pragma unroll
@@ -177,7 +179,7 @@ __global__ __launch_bounds__(kSliceThreads) void topk_compact_kernel(
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       kk[g][e] = any ? score_key(f[g][e]) : 0u;
-      n += kk[g][e] >= lower && kk[g][e] != 0u;
+      n += kk[g][e] >= lower;
     }
     cg[g] = n;
     ig[g] = wave_incl_scan(n);
@@ -208,7 +210,7 @@ __global__ __launch_bounds__(kSliceThreads) void topk_compact_kernel(
     if (cg[g]) {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        if (kk[g][e] >= lower && kk[g][e] != 0u) {
+        if (kk[g][e] >= lower) {
           if (d < kRowList) {
             lk[d] = kk[g][e];
             lp[d] = pos0 + 256 * g + e;

@@ -157,7 +157,8 @@ __global__ __launch_bounds__(kSliceThreads) void topk_compact_kernel(
   lds_barrier();
   const uint32_t lower = (uint32_t)sh[0];
   const int listed = sh[1];
-  if (listed > kRowList) {   // the finishing workgroup selects this row alone
+  // every slice's share of the list is padded to a multiple of 4 entries
+  if (listed + 3 * n_slices > kRowList) {   // the finishing workgroup selects this row alone
     if (sl == 0 && threadIdx.x == 0) {
       ws.meta[2 * row] = (int)lower;
       ws.meta[2 * row + 1] = -1;
@@ -194,7 +195,10 @@ __global__ __launch_bounds__(kSliceThreads) void topk_compact_kernel(
     t_wg += wlist[u];
   }
   if (threadIdx.x == 0) {
-    const int base = t_wg ? atomicAdd(&ws.ctr[(int64_t)row * kCtrStride], t_wg) : 0;
+    // the share is padded to a multiple of 4 entries with key 0 (never
+    // selected), so the finishing workgroup reads it 16 bytes at a time
+    const int t_pad = (t_wg + 3) & ~3;
+    const int base = t_pad ? atomicAdd(&ws.ctr[(int64_t)row * kCtrStride], t_pad) : 0;
     sh[2] = base;
     ws.slc[((int64_t)row * n_slices + sl) * 2] = base;
     ws.slc[((int64_t)row * n_slices + sl) * 2 + 1] = t_wg;
@@ -203,6 +207,7 @@ __global__ __launch_bounds__(kSliceThreads) void topk_compact_kernel(
   o += sh[2];
   uint32_t* lk = ws.lkey + (int64_t)row * kRowList;
   int32_t* lp = ws.lpos + (int64_t)row * kRowList;
+  if (threadIdx.x < ((t_wg + 3) & ~3) - t_wg) lk[sh[2] + t_wg + threadIdx.x] = 0u;   // padding
   const int pos0 = v.w.lo - v.w.o + v.p0;
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
@@ -481,11 +486,12 @@ __global__ __launch_bounds__(kRowThreads) void topk_finish_kernel(
     return;
   }
 
-  // 1. the list, slice by slice: s_off = first list rank of each slice
+  // 1. the list, slice by slice: s_off = first list rank of each slice (ranks
+  // count every slice's share padded to a multiple of 4, as stored)
   int run = 0;
   for (int b0 = 0; b0 < n_slices; b0 += kRowThreads) {
     const int sl = b0 + threadIdx.x;
-    const int n = b0 == 0 ? n0 : (sl < n_slices ? slc[2 * sl + 1] : 0);
+    const int n = ((b0 == 0 ? n0 : (sl < n_slices ? slc[2 * sl + 1] : 0)) + 3) & ~3;
     if (sl < n_slices) s_at[sl] = b0 == 0 ? at0 : slc[2 * sl];
     const int inc = wave_incl_scan(n);
     if (lane == 63) L.wt[wave] = inc;
@@ -524,19 +530,29 @@ __global__ __launch_bounds__(kRowThreads) void topk_finish_kernel(
       }
       sl = a;
     }
+    // four ranks at a time: a slice's share starts on a multiple of 4 and
+    // holds a multiple of 4 entries, so they are 16 consecutive bytes
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
+    for (int u = 0; u < kPer; u += 4) {
       const int r = r0 + u;
-      key[u] = 0u;
-      pos[u] = 0;
+      uint4 kq = make_uint4(0u, 0u, 0u, 0u);
+      int4 pq = make_int4(0, 0, 0, 0);
       if (r < m) {
         while (s_off[sl + 1] <= r) ++sl;
         const int at = s_at[sl] + (r - s_off[sl]);
-        if (at < kRowList) {
-          key[u] = lk[at];
-          pos[u] = lp[at];
+        if (at + 4 <= kRowList) {
+          kq = *(const uint4*)(lk + at);
+          pq = *(const int4*)(lp + at);
         }
       }
+      key[u] = kq.x;
+      key[u + 1] = kq.y;
+      key[u + 2] = kq.z;
+      key[u + 3] = kq.w;
+      pos[u] = pq.x;
+      pos[u + 1] = pq.y;
+      pos[u + 2] = pq.z;
+      pos[u + 3] = pq.w;
     }
   }
 
@@ -554,7 +570,9 @@ __global__ __launch_bounds__(kRowThreads) void topk_finish_kernel(
       },
       &T, &need_eq, &k_sel);
 
-  // 3. ordered write: the lane's entries are consecutive list ranks
+  // 3. ordered write: the lane's entries are consecutive list ranks; the
+  // selection is staged in LDS (the list buffer of the fallback) when it fits
+  const bool stage = k <= kListCap;
   int c = 0;
 #pragma unroll
   for (int u = 0; u < kPer; ++u)
@@ -575,17 +593,19 @@ __global__ __launch_bounds__(kRowThreads) void topk_finish_kernel(
         ++eb;
       }
       if (dst >= 0 && dst < k) {
-        if constexpr (MAP == 0) orow[dst] = pos[u];
-        else if constexpr (MAP == 1) L.hist[dst] = (uint32_t)pos[u];
+        if (stage) klist[dst] = (uint32_t)pos[u];
+        else if constexpr (MAP == 0) orow[dst] = pos[u];
         else orow[dst] = map_b[map_a[(int64_t)row * map_ld + pos[u]]];
       }
     }
   }
   const int n_sel = min(k, ta + min(te, need_eq));
-  if constexpr (MAP == 1) {
+  if (stage) {   // one coalesced pass instead of a lane's 16 scattered stores
     lds_barrier();
-    for (int i = threadIdx.x; i < n_sel; i += kRowThreads)
-      orow[i] = map_b[map_a[(int64_t)row * map_ld + (int)L.hist[i]]];
+    for (int i = threadIdx.x; i < n_sel; i += kRowThreads) {
+      const int p = (int)klist[i];
+      orow[i] = MAP == 0 ? p : map_b[map_a[(int64_t)row * map_ld + p]];
+    }
   }
   for (int i = n_sel + threadIdx.x; i < k; i += kRowThreads) orow[i] = -1;
   if (threadIdx.x == 0) count[row] = n_sel;
@@ -640,9 +660,11 @@ __global__ __launch_bounds__(kRowThreads) void topk_survivor_kernel(
     int pos[kPer];
     const uint32_t* lk = ws.lkey + (int64_t)row * kRowList;
     const int32_t* lp = ws.lpos + (int64_t)row * kRowList;
+    // survivors in any order (bitmaps place them): lane-interleaved, so every
+    // load instruction reads consecutive words
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
-      const int r = kPer * threadIdx.x + u;
+      const int r = u * kRowThreads + threadIdx.x;
       key[u] = r < m ? lk[r] : 0u;
       pos[u] = r < m ? lp[r] : 0;
       if (pos[u] < w.lo || pos[u] >= w.hi) key[u] = 0u;   // only window positions were listed

@@ -260,10 +260,15 @@ def test_topk_kernel_on_oracle_inputs(L, k, seed):
 
 
 @pytest.mark.parametrize("B,H,L,k", [(32, 8, 65536, 2048), (16, 4, 131072, 2048),
-                                     (8, 4, 131072, 4000), (1, 1, 131072, 2048)])
+                                     (8, 4, 131072, 4000), (1, 1, 131072, 2048),
+                                     (1, 2, 131072, 14000), (1, 2, 131072, 15500),
+                                     (1, 1, 131072, 20000)])
 def test_topk_listing_slice_sizes(B, H, L, k):
     """Many rows take 8192-slot listing slices, fewer rows smaller ones (4096,
-    2048, 1024 slots); every row's set equals the oracle's, windows ragged."""
+    2048, 1024 slots); every row's set equals the oracle's, windows ragged.
+    Large k put the list (each slice's share padded to 4 entries) near and
+    past its 16,384-entry capacity, where the row is selected from the
+    scores instead."""
     say("topk slices", B, H, L, k)
     s = W.normal_f32(W.seed_of(1100 + B), 0, (B, H, L)) * 10
     lo = (np.arange(B, dtype=np.int32) * 37) % 1000

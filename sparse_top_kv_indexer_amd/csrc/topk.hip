@@ -19,14 +19,17 @@
 //      the bin b0 that holds the k-th largest key from the histogram and
 //      lists its slice's keys in bins >= b0, with their positions, in
 //      position order (a DPP prefix sum per group of 4 slots and one atomic
-//      per workgroup on the row's list counter place them); the list holds
-//      the keys above b0 plus the bin's, typically k plus a few hundred;
+//      per workgroup on the row's list counter place them; each slice's
+//      share is padded to a multiple of 4 entries with key 0); the list
+//      holds the keys above b0 plus the bin's, typically k plus a few
+//      hundred;
 //   2. topk_finish_kernel, one 1024-thread workgroup per row: reads the list
-//      slice by slice (16 entries per lane), resolves the exact threshold T
-//      and the number of keys equal to T to take (lowest positions first)
-//      with two more digits of 12 and 8 bits over the listed keys of bin b0,
-//      and writes the selected positions in ascending order with one prefix
-//      sum over the list.
+//      slice by slice (16 consecutive ranks per lane, as four 16-byte
+//      loads), resolves the exact threshold T and the number of keys equal
+//      to T to take (lowest positions first) with two more digits of 12 and
+//      8 bits over the listed keys of bin b0, and writes the selected
+//      positions in ascending order with one prefix sum over the list,
+//      staged in LDS so the stores to the output are consecutive words.
 // The per-key work over the whole row is spread over all compute units and
 // the row is read once (twice without the fused histogram).  A row whose
 // list would exceed kRowList keys (many keys tied around the threshold) is

@@ -4,23 +4,30 @@
 A step is one pass of the whole hot path over one batch of synthetic input
 already resident in HBM, all through the C ABI of libsparsekv.so.
 
-Default workload (the GQA paged decode the metric is quoted on):
-  B = 4 sequences, 8 KV heads x 4 query heads, d = 128, L = 32768 bf16 keys
-  and values in a 16-token paged pool whose block order is a seeded
-  permutation, 4 outlier channels per KV head scaled x8, top-k = 2048 per KV
-  head plus 4 sink and 64 local tokens.  Step: score scan (with the first
-  top-k digit) -> exact top-k fused with gather + split attention -> merge.
+Headline workload (the largest single-GPU configuration, token-level
+eviction pool): B = 32 sequences, 8 KV heads, G = 1, d = 128, L = 65536
+logical tokens of which exactly half are dead (holes scattered inside the
+16-token blocks), bf16 keys and values in a pool with permuted blocks reached
+through a per-token table, top-k = 2048 over the live tokens plus the first 4
+and last 128 live tokens.  Step: score scan (with the first top-k digit) ->
+exact top-k -> gather + split attention -> merge.
 
-Other workloads (--workload), each timed the same way:
-  gqa_paged_long  the same at L = 131072 (the long-context scan + gather)
-  single_head   B=1, L=4096 fp32 contiguous, planted query, top-64
-  token_pool    B=32, 8 KV heads, G=1, L=65536, token table, 50 % dead
-  indexer_mla   B=1, indexer keys d=128 + shared latent 576 (value 512),
-                128 query heads, L=131072 paged, top-2048 by the indexer
-  paris         compressed-code retrieval over 8 x 1,048,060 encoded keys
-                (query LUT, collision vote, top-C, rerank, top-100) + the
-                attention over retrieved + sink 4 + local 512
-  paris_encode  the off-step encode of that history (SRHT, ids, codes, w)
+With the headline, the same JSON line carries `other_configs`, each timed the
+same way in the same process (a shorter oracle sample each):
+  1   single_head     B=1, L=4096 fp32 contiguous, planted query, top-64
+  2   gqa_paged       B=4, 8 KV heads x 4 query heads, L=32768 bf16 paged
+                      (seeded block permutation), 4 outlier channels x8,
+                      top-2048 + 4 sink + 64 local
+  2L  gqa_paged_long  the same at L = 131072
+  4   indexer_mla     B=1, indexer keys d=128 + shared latent 576 (value 512),
+                      128 query heads, L=131072 paged, top-2048 by the indexer
+  5   paris           compressed-code retrieval over 8 x 1,048,060 encoded keys
+                      (query LUT, collision vote, top-C, rerank, top-100) + the
+                      attention over retrieved + sink 4 + local 512
+Other --workload values time one configuration alone (paris_encode: the
+off-step encode; paris_decode: the decode loop with the Update Buffer;
+compact: token-table compaction; --path prefilter / blocks: the
+threshold-prefiltered and block-summary variants).
 
 Successive steps use distinct device copies of the inputs they stream (four
 by default, like four layers), so that a step never finds its data in the
@@ -33,12 +40,13 @@ replayed right after the timed one (event nodes cost about 14 us per step on
 this runtime, so the timed graph carries none).
 
 Prints ONE JSON line (rank 0, N = 1) with the throughput in keys per second,
-the per-step time, the roofline entry of the dominant kernel and the CPU
-oracle timed on a bounded sample of the same workload.
+the per-step time, the roofline entry of the dominant kernel (its HBM traffic
+from the committed rocprofv3 counter record when that was taken on the
+kernel's current source) and the CPU oracle timed on a bounded sample.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--kv-copies C]
                   [--path fused|separate|prefilter|blocks] [--eager]
-                  [--no-cpu-baseline]
+                  [--no-cpu-baseline] [--no-other-configs]
 """
 from __future__ import annotations
 
@@ -68,8 +76,13 @@ def parse():
                     help="timed steps (default 50; paris_decode: 4 x 512, one Update Buffer "
                          "cycle of each of the four layers)")
     ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 10; paris_decode 16)")
-    ap.add_argument("--workload", default="gqa_paged", choices=WORKLOADS)
+    ap.add_argument("--workload", default="token_pool", choices=WORKLOADS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="with the headline workload: skip the other configurations")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="oracle sample length of the headline (other configurations: a "
+                         "third of it)")
     ap.add_argument("--kv-copies", type=int, default=4,
                     help="distinct device copies of the streamed inputs, used in turn by "
                          "successive steps (like successive layers), so that no step finds "
@@ -209,19 +222,51 @@ def timed_steps(step, n_calls, args, hip):
     return wall, hip.elapsed_ms(bracket[0], bracket[1]) / K, calls, note
 
 
-def traffic_entry(name, kernel_src):
-    """HBM bytes per launch of a kernel from its committed rocprofv3 counter
-    summary, if it was taken on the current kernel source; else None."""
-    path = os.path.join(HERE, "profiles", name)
+# Source files that define each timed kernel: a counter record counts only
+# while these files are byte-identical to the ones it was taken on.
+CSRC = "sparse_top_kv_indexer_amd/csrc/"
+_COMMON = [CSRC + "skv_device.h", CSRC + "skv_internal.h"]
+KERNEL_SOURCES = {
+    "score_stream_kernel": [CSRC + "score.hip", CSRC + "skv_topk.h"] + _COMMON,
+    "score_valu_kernel": [CSRC + "score.hip", CSRC + "skv_topk.h"] + _COMMON,
+    "attend_mfma_kernel": [CSRC + "attend.hip"] + _COMMON,
+    "attend_split_kernel": [CSRC + "attend.hip"] + _COMMON,
+    "attend_reduce_kernel": [CSRC + "attend.hip"] + _COMMON,
+    "select_attend_kernel": [CSRC + "select_attend.hip", CSRC + "skv_rowsel.h",
+                             CSRC + "skv_topk.h"] + _COMMON,
+    "mla_split_kernel": [CSRC + "mla.hip"] + _COMMON,
+    "vote_kernel": [CSRC + "paris.hip"] + _COMMON,
+    "rerank_kernel": [CSRC + "paris.hip"] + _COMMON,
+    "query_lut_kernel": [CSRC + "paris.hip"] + _COMMON,
+    "cand_write_kernel": [CSRC + "paris.hip"] + _COMMON,
+}
+
+
+def sources_sha256(files):
+    h = hashlib.sha256()
+    for f in files:
+        h.update(f.encode())
+        h.update(open(os.path.join(HERE, f), "rb").read())
+    return h.hexdigest()
+
+
+def traffic_entry(workload, kernels):
+    """HBM bytes per launch of the named kernels (summed), from the committed
+    rocprofv3 counter record of the workload (profiles/pmc_<workload>.json),
+    if every one was taken on the kernel's current source files; else None."""
+    path = os.path.join(HERE, "profiles", "pmc_%s.json" % workload)
     if not os.path.exists(path):
         return None
     try:
-        rec = json.load(open(path))
-        h = hashlib.sha256(open(os.path.join(HERE, kernel_src), "rb").read()).hexdigest()
-        if rec.get("source_sha256") != h:
-            return None
-        return rec["hbm_bytes_per_launch"]
-    except Exception:
+        rec = json.load(open(path))["kernels"]
+        total = 0.0
+        for k in kernels:
+            e = rec[k]
+            if e["source_sha256"] != sources_sha256(KERNEL_SOURCES[k]):
+                return None
+            total += e["hbm_bytes_per_launch"]
+        return total
+    except (KeyError, ValueError, OSError):
         return None
 
 
@@ -311,9 +356,11 @@ def dense_cpu_baseline(st, min_seconds=10.0):
     """The oracle as it stands on (sequence, KV head) rows of the same
     workload, taken in order and repeated until at least min_seconds of CPU
     work: float64 scores, full sort, dense masked softmax."""
+    import workloads as W
     from oracle import dense as D
     from threadpoolctl import threadpool_info
     kv = st.score_kv
+    live = [W.live_tokens(kv, b) for b in range(kv.B)]
     rows = [(b, h) for b in range(kv.B) for h in range(kv.H)]
     keys = 0
     n_rows = 0
@@ -321,7 +368,7 @@ def dense_cpu_baseline(st, min_seconds=10.0):
     while True:
         b, h = rows[n_rows % len(rows)]
         D.step(st, rows=[(b, h)])
-        keys += int(D.live_slots(kv, b)[0].size)
+        keys += int(live[b].size)
         n_rows += 1
         if time.perf_counter() - t0 >= min_seconds:
             break
@@ -403,26 +450,27 @@ def bench_dense(args, hip):
     wall, gpu_ms, calls, note = timed_steps(step, 2 if fused else 3, args, hip)
     calls = np.array(calls)
     ms_per_step = wall * 1e3 / args.steps
-    # live keys and algorithmic bytes of the scan and the gather
-    from oracle import dense as D
-    n_keys = sum(int(D.live_slots(st.score_kv, b)[0].size) for b in range(B)) * H
+    # live keys and algorithmic bytes of the scan and the gather, counted
+    # from the workload's own tables
+    import workloads as W
+    live = [W.live_tokens(st.score_kv, b) for b in range(B)]
+    n_keys = sum(int(t.size) for t in live) * H
     es = 2 if st.score_kv.dtype == "bf16" else 4
     per_key = st.score_kv.d_k * es + 4 + (4 if st.score_kv.token_table is not None else 0)
     scan_bytes = n_keys * per_key + sq.numel() * sq.element_size()
     cnt_np = cnt.cpu().numpy()
     n_att = int(cnt_np.sum())
     for b in range(B):
-        t_live = D.live_slots(st.kv, b)[0]
+        t_live = W.live_tokens(st.kv, b)
         n_att += int(((t_live < st.lo[b]) | (t_live >= st.hi[b])).sum()) * kv.H
     row_bytes = (kv.d_k * (2 if bf else 4)) * (1 if mla else 2)
     gather_bytes = n_att * row_bytes
     step_bytes = scan_bytes + gather_bytes
     scan_s = float(np.mean(calls[:, 0])) * 1e-3
-    src = "sparse_top_kv_indexer_amd/csrc/score.hip"
     kname = ("score_stream_kernel" if (bf and skv.d_k % 32 == 0 and skv.d_k <= 256) else
              "score_valu_kernel")
     # the counter record holds the histogram scan; the survivor scan has none
-    tr = None if prefilter else traffic_entry("score_scan_%s_pmc.json" % args.workload, src)
+    tr = None if prefilter else traffic_entry(args.workload, [kname])
     cfg = {"workload": args.workload, "B": B, "H_kv": kv.H, "G": G, "d": kv.d_k,
            "L": L, "k": k, "layout": st.kv.mode, "kv_dtype": st.kv.dtype,
            "kv_copies": len(pairs), "launch": "eager" if args.eager else "hip_graph",
@@ -464,11 +512,13 @@ def bench_dense(args, hip):
         att_s = float(np.mean(calls[:, 2])) * 1e-3
         flops = 2.0 * n_att * G * (kv.d_k + kv.d_v)
         rec["roofline_attention"] = roofline("latent attention (sparsekv_gather_attend: "
-                                             "mla_split_kernel + merge)", "mfma", flops, att_s, None,
+                                             "mla_split_kernel + merge)", "mfma", flops, att_s,
+                                             traffic_entry(args.workload, ["mla_split_kernel",
+                                                                           "attend_reduce_kernel"]),
                                              {"algorithmic_flops_per_launch": flops,
                                               "gathered_bytes": gather_bytes})
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = dense_cpu_baseline(st)
+        rec["cpu_baseline"] = dense_cpu_baseline(st, args.cpu_seconds)
     return rec
 
 
@@ -514,8 +564,8 @@ def bench_blocks(args, hip, st, kv, q, lo, hi):
     wall, gpu_ms, calls, note = timed_steps(step, 2, args, hip)
     calls = np.array(calls)
     ms_per_step = wall * 1e3 / args.steps
-    from oracle import dense as D
-    live = [D.live_slots(st.kv, b)[0] for b in range(B)]
+    import workloads as W
+    live = [W.live_tokens(st.kv, b) for b in range(B)]
     n_keys = sum(int(t.size) for t in live) * H
     n_blocks = sum(int(np.unique(t // 16).size) for t in live) * H
     # per live block row: the [mx, mn] summary, its score and its table entry
@@ -553,7 +603,10 @@ def bench_blocks(args, hip, st, kv, q, lo, hi):
 
 
 # ------------------------------------------------------------------ paris
-def paris_cpu_baseline(min_seconds=10.0):
+RETRIEVE_KERNELS = ("query_lut_kernel", "vote_kernel", "cand_write_kernel", "rerank_kernel")
+
+
+def paris_cpu_baseline(min_seconds):
     """The oracle's encode + retrieval on a bounded sample of the same
     workload: one KV head (4 query heads) of a 65,536-token history drawn the
     same way, repeated until at least min_seconds of CPU work."""
@@ -675,11 +728,12 @@ def bench_paris(args, hip):
         "step_GBps": (ret_bytes + gather) / (ms * 1e-3) / 1e9,
         "roofline": roofline("retrieval (sparsekv_retrieve: query LUT, collision vote, top-C, "
                              "rerank, top-100; the vote kernel moves 94 % of the bytes)", "hbm",
-                             ret_bytes, t_ret, None,
-                             {"algorithmic_bytes_per_launch": ret_bytes}),
+                             ret_bytes, t_ret, traffic_entry("paris", RETRIEVE_KERNELS),
+                             {"algorithmic_bytes_per_launch": ret_bytes,
+                              "traffic_kernels": list(RETRIEVE_KERNELS)}),
     })
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = paris_cpu_baseline()
+        rec["cpu_baseline"] = paris_cpu_baseline(args.cpu_seconds)
     return rec
 
 
@@ -801,7 +855,7 @@ def bench_paris_decode(args, hip):
                                          "tokens x 8 heads)", "hbm", enc_bytes, t_flush_us * 1e-6,
                                          None, {"algorithmic_bytes_per_launch": enc_bytes})
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = paris_cpu_baseline()
+        rec["cpu_baseline"] = paris_cpu_baseline(args.cpu_seconds)
     return rec
 
 
@@ -822,8 +876,7 @@ def bench_compact(args, hip):
     kv = st.kv
     n_blocks = kv.k.shape[0]
     kv_d = S.kv_to_device(kv, dev)
-    from oracle import compact as C
-    counts = C.occupancy(kv.token_table, kv.seq_len, n_blocks).astype(np.int32)
+    counts = W.block_occupancy(kv.token_table, kv.seq_len, n_blocks)
     free = [int(x) for x in st.meta["free_blocks"]]
     F_before = S.sparsekv_waste_ratio(counts[counts > 0])
     t0 = time.perf_counter()
@@ -901,12 +954,50 @@ def bench_compact(args, hip):
     return rec
 
 
+# configurations carried in the headline's line, by the ids the workloads
+# are known by (2L: workload 2 at L = 131072)
+CONFIG_ID = {"single_head": "1", "gqa_paged": "2", "gqa_paged_long": "2L", "token_pool": "3",
+             "indexer_mla": "4", "paris": "5"}
+OTHER_CONFIGS = ("single_head", "gqa_paged", "gqa_paged_long", "indexer_mla", "paris")
+
+
+def run_workload(args, hip):
+    if args.workload in DENSE:
+        return bench_dense(args, hip)
+    if args.workload == "paris_decode":
+        return bench_paris_decode(args, hip)
+    if args.workload == "compact":
+        return bench_compact(args, hip)
+    return bench_paris(args, hip)
+
+
+def add_stream_reference(rec, ref):
+    for key in ("roofline", "roofline_attention"):
+        ro = rec.get(key)
+        if ro and ro.get("bound") == "hbm" and ref:
+            ro.update(ref)
+            ro["frac_of_stream_read"] = ro["achieved"] / ref["stream_read_GBps"]
+
+
+def summary(rec):
+    """The entry of one configuration in other_configs: time per step, step
+    and dominant-kernel rates against the peaks, and the oracle baseline."""
+    keep = ("metric", "value", "unit", "dtype", "config", "us_per_step", "us_per_step_gpu",
+            "us_per_step_events", "us_per_call", "step_algorithmic_bytes", "step_GBps",
+            "step_frac_of_hbm_peak", "roofline", "roofline_attention", "cpu_baseline")
+    out = {k: rec[k] for k in keep if k in rec}
+    if "step_GBps" in out and "step_frac_of_hbm_peak" not in out:
+        out["step_frac_of_hbm_peak"] = out["step_GBps"] / PEAK_HBM_GBPS
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures the single-GPU hot path only; run it with --gpus 1 "
               "(multi-GPU sharding is a design note, not built)", file=sys.stderr)
         sys.exit(2)
+    import gc
     import torch
     import sparse_top_kv_indexer_amd as S  # noqa: F401  (fails loudly without the library)
 
@@ -922,19 +1013,27 @@ def main():
         print(json.dumps({"calib_copy_bytes": n, "launches": 5}))
         return
     hip = HipEvents()
-    if args.workload in DENSE:
-        rec = bench_dense(args, hip)
-    elif args.workload == "paris_decode":
-        rec = bench_paris_decode(args, hip)
-    elif args.workload == "compact":
-        rec = bench_compact(args, hip)
-    else:
-        rec = bench_paris(args, hip)
-    ro = rec.get("roofline")
-    if ro and ro.get("bound") == "hbm" and not args.no_stream_reference:
-        ref = stream_reference()
-        ro.update(ref)
-        ro["frac_of_stream_read"] = ro["achieved"] / ref["stream_read_GBps"]
+    rec = run_workload(args, hip)
+    rec["config"]["config_id"] = CONFIG_ID.get(args.workload)
+    gc.collect()
+    torch.cuda.empty_cache()
+    ref = None if args.no_stream_reference else stream_reference()
+    add_stream_reference(rec, ref)
+    if args.workload == "token_pool" and args.path == "fused" and not args.no_other_configs:
+        others = {}
+        for w in OTHER_CONFIGS:
+            a = argparse.Namespace(**vars(args))
+            a.workload = w
+            a.cpu_seconds = args.cpu_seconds / 3.0
+            print("other config %s (%s)" % (CONFIG_ID[w], w), file=sys.stderr, flush=True)
+            r = run_workload(a, hip)
+            r["config"]["config_id"] = CONFIG_ID[w]
+            add_stream_reference(r, ref)
+            others[CONFIG_ID[w]] = summary(r)
+            del r
+            gc.collect()
+            torch.cuda.empty_cache()
+        rec["other_configs"] = others
     print(json.dumps(rec))
 
 

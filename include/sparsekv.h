@@ -23,7 +23,9 @@
  *   reused by any number of calls that are ordered on one stream.  Calls that
  *   share a workspace must not overlap.
  * - Errors are returned as skv_status; nothing aborts.  Host-visible
- *   arguments are validated (null pointers, sizes, modes, workspace size).
+ *   arguments are validated (null pointers, sizes, modes, workspace size;
+ *   every selecting call requires 1 <= k <= L_max, sparsekv_gather_attend
+ *   0 <= k <= L_max, sparsekv_block_select 1 <= K <= L_max / 16).
  *   Device-resident data is NOT validated: table entries must point inside
  *   the pools, token-table slots of live tokens must be unique, and
  *   0 <= lo <= hi <= seq_len <= L_max must hold for every sequence.
@@ -323,7 +325,9 @@ double sparsekv_waste_ratio(const int32_t* n_live, int32_t n);
  * invariant I4).  Output (host): moves [n_moves] (room for 16 * max_src), in
  * ascending t, move i going to slot free_blocks[i / 16] * 16 + i % 16;
  * src_blocks [n_src] the freed blocks (ascending); n_dst = targets used.
- * n_moves = 0 when no plan passes.  SKV_EINVAL on a slot outside the pool. */
+ * n_moves = 0 when no plan passes.  SKV_EINVAL on a slot outside the pool, or
+ * on a free block outside [0, n_blocks), holding a live token (counts[p] > 0)
+ * or listed twice among the first n_free entries. */
 skv_status sparsekv_compact_plan(const int32_t* token_table, const int32_t* seq_len, int32_t B,
                                  int32_t L_max, int32_t n_blocks, const int32_t* counts, int32_t b,
                                  const int32_t* free_blocks, int32_t n_free, double theta_F,
@@ -336,10 +340,13 @@ skv_status sparsekv_compact_plan(const int32_t* token_table, const int32_t* seq_
  * kv->token_table (their const in skv_kv notwithstanding).  Readers ordered
  * after the call on the stream see the moved tokens; the source slots keep
  * their bytes until the caller reuses their blocks.  Requires a token-table
- * pool (block = 16) with rows a multiple of 16 bytes; destination slots must
- * be distinct and hold no live token. */
-skv_status sparsekv_compact_apply(const skv_kv* kv, const skv_move* moves, int32_t n_moves,
-                                  hipStream_t stream);
+ * pool (block = 16) of n_blocks blocks with rows a multiple of 16 bytes;
+ * destination slots must be distinct and hold no live token.  A move with
+ * b outside [0, B), t outside [0, L_max) or src / dst outside
+ * [0, 16 n_blocks) is skipped -- nothing is read or written for it -- and
+ * counted into *err (device int32, added to; may be NULL). */
+skv_status sparsekv_compact_apply(const skv_kv* kv, int32_t n_blocks, const skv_move* moves,
+                                  int32_t n_moves, int32_t* err, hipStream_t stream);
 
 /* Invariant I1 check (section 4.6: the retained token ids and their K/V
  * contents hashed before and after a migration; the page names no hash).

@@ -99,7 +99,7 @@ _SIGS = {
     "sparsekv_compact_plan": (c_i32, [c_vp, c_vp, c_i32, c_i32, c_i32, c_vp, c_i32, c_vp, c_i32,
                                       ctypes.c_double, c_i32, c_vp, ctypes.POINTER(c_i32), c_vp,
                                       ctypes.POINTER(c_i32), ctypes.POINTER(c_i32)]),
-    "sparsekv_compact_apply": (c_i32, [ctypes.POINTER(skv_kv), c_vp, c_i32, c_vp]),
+    "sparsekv_compact_apply": (c_i32, [ctypes.POINTER(skv_kv), c_i32, c_vp, c_i32, c_vp, c_vp]),
     "sparsekv_live_hash": (c_i32, [ctypes.POINTER(skv_kv), c_vp, c_vp, c_vp]),
     "sparsekv_check_unique_ws_bytes": (c_sz, [c_i32]),
     "sparsekv_check_unique": (c_i32, [ctypes.POINTER(skv_kv), c_i32, c_vp, c_vp, c_sz, c_vp]),
@@ -346,7 +346,7 @@ def sparsekv_block_summary_bytes(n_blocks: int, H: int, d_k: int) -> int:
 
 def block_summary_pool(kv: KVTensors) -> torch.Tensor:
     """A summary pool for every physical block of kv's pool (bf16 rows of 2 d_k)."""
-    n_blocks = kv.k.numel() // (kv.H * 16 * kv.d_k)
+    n_blocks = pool_blocks(kv)
     nb = sparsekv_block_summary_bytes(n_blocks, kv.H, kv.d_k)
     return torch.zeros(nb // 2, dtype=torch.bfloat16, device=kv.k.device)
 
@@ -354,7 +354,7 @@ def block_summary_pool(kv: KVTensors) -> torch.Tensor:
 def sparsekv_block_summarize(kv: KVTensors, b: int, j0: int, j1: int, summ: torch.Tensor):
     """(Re)build the min / max summaries of logical blocks [j0, j1) of sequence b."""
     _dev(summ, "summ", torch.bfloat16)
-    n_blocks = kv.k.numel() // (kv.H * 16 * kv.d_k)
+    n_blocks = pool_blocks(kv)
     if summ.numel() * 2 < sparsekv_block_summary_bytes(n_blocks, kv.H, kv.d_k):
         raise ValueError("summ is smaller than the summary pool of kv's blocks")
     c = kv.c()
@@ -366,7 +366,7 @@ def sparsekv_block_summarize(kv: KVTensors, b: int, j0: int, j1: int, summ: torc
 def sparsekv_block_summarize_last(kv: KVTensors, summ: torch.Tensor):
     """(Re)build the summary of the block holding each sequence's last token."""
     _dev(summ, "summ", torch.bfloat16)
-    n_blocks = kv.k.numel() // (kv.H * 16 * kv.d_k)
+    n_blocks = pool_blocks(kv)
     if summ.numel() * 2 < sparsekv_block_summary_bytes(n_blocks, kv.H, kv.d_k):
         raise ValueError("summ is smaller than the summary pool of kv's blocks")
     c = kv.c()
@@ -446,14 +446,24 @@ def sparsekv_compact_plan(token_table: np.ndarray, seq_len: np.ndarray, n_blocks
     return moves[: nm.value].copy(), src[: ns.value].copy(), int(nd.value)
 
 
-def sparsekv_compact_apply(kv: KVTensors, moves: torch.Tensor):
-    """Copy the moved rows and rewrite kv.token_table (device, in place)."""
+def pool_blocks(kv: KVTensors) -> int:
+    """Physical 16-token blocks in kv's pool (k is [n_blocks][H][16][d_k])."""
+    return kv.k.numel() // (kv.H * 16 * kv.d_k)
+
+
+def sparsekv_compact_apply(kv: KVTensors, moves: torch.Tensor, err: Optional[torch.Tensor] = None):
+    """Copy the moved rows and rewrite kv.token_table (device, in place).
+    Moves outside the table or the pool are skipped and counted into err
+    (device int32 [1], added to) when it is given."""
     _dev(moves, "moves", torch.int32)
     if moves.dim() != 2 or moves.shape[1] != 4:
         raise ValueError("moves must be int32 [n][4]")
+    if err is not None:
+        _dev(err, "err", torch.int32)
     c = kv.c()
     _check("sparsekv_compact_apply",
-           lib().sparsekv_compact_apply(ctypes.byref(c), _ptr(moves), moves.shape[0], _stream()))
+           lib().sparsekv_compact_apply(ctypes.byref(c), pool_blocks(kv), _ptr(moves),
+                                        moves.shape[0], _ptr(err), _stream()))
 
 
 def sparsekv_live_hash(kv: KVTensors, hash_out: Optional[torch.Tensor] = None,

@@ -85,7 +85,7 @@ skv_status sparsekv_topk(const float* scores, int32_t B, int32_t H, int32_t L_ma
                          skv_window win, int32_t k, int32_t* idx, int32_t* count, void* ws,
                          size_t ws_bytes, hipStream_t stream) {
   if (!scores || !idx || !count || !win.lo || !win.hi) return SKV_EINVAL;
-  if (B < 1 || H < 1 || L_max < 1 || k < 1) return SKV_EINVAL;
+  if (B < 1 || H < 1 || L_max < 1 || k < 1 || k > L_max) return SKV_EINVAL;
   if (!topk_supported(L_max)) return SKV_EUNSUPPORTED;
   if (!ws || ws_bytes < topk_workspace_bytes(B * H, L_max)) return SKV_EWORKSPACE;
   return launched(launch_topk(scores, B * H, H, L_max, win.lo, win.hi, k, idx, count, ws, false,
@@ -104,7 +104,7 @@ skv_status sparsekv_topk_resume(const float* scores, int32_t B, int32_t H, int32
                                 skv_window win, int32_t k, int32_t* idx, int32_t* count,
                                 void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!scores || !idx || !count || !win.lo || !win.hi) return SKV_EINVAL;
-  if (B < 1 || H < 1 || L_max < 1 || k < 1) return SKV_EINVAL;
+  if (B < 1 || H < 1 || L_max < 1 || k < 1 || k > L_max) return SKV_EINVAL;
   if (!topk_supported(L_max)) return SKV_EUNSUPPORTED;
   if (!ws || ws_bytes < topk_workspace_bytes(B * H, L_max)) return SKV_EWORKSPACE;
   return launched(launch_topk(scores, B * H, H, L_max, win.lo, win.hi, k, idx, count, ws, true,
@@ -130,7 +130,8 @@ skv_status sparsekv_topk_prefiltered(const float* scores, int32_t B, int32_t H, 
                                      int32_t* idx, int32_t* count, int32_t* used, void* ws,
                                      size_t ws_bytes, hipStream_t stream) {
   if (!scores || !idx || !count || !thr || !win.lo || !win.hi) return SKV_EINVAL;
-  if (B < 1 || H < 1 || L_max < 1 || k < 1 || !(alpha >= 0.f && alpha <= 1.f)) return SKV_EINVAL;
+  if (B < 1 || H < 1 || L_max < 1 || k < 1 || k > L_max || !(alpha >= 0.f && alpha <= 1.f))
+    return SKV_EINVAL;
   if (!topk_survivors_supported(L_max)) return SKV_EUNSUPPORTED;
   if (!ws || ws_bytes < topk_workspace_bytes(B * H, L_max)) return SKV_EWORKSPACE;
   return launched(launch_topk_survivors(scores, B * H, H, L_max, win.lo, win.hi, k, idx, count,
@@ -141,7 +142,7 @@ skv_status sparsekv_select(const skv_kv* kv, const void* q, int32_t G, skv_windo
                            float* scores, int32_t* idx, int32_t* count, void* ws,
                            size_t ws_bytes, hipStream_t stream) {
   if (!kv_ok(kv) || !q || !scores || !idx || !count || G < 1 || k < 1) return SKV_EINVAL;
-  if (!win.lo || !win.hi) return SKV_EINVAL;
+  if (k > kv->L_max || !win.lo || !win.hi) return SKV_EINVAL;
   if (!score_supported(kv, G) || !topk_supported(kv->L_max)) return SKV_EUNSUPPORTED;
   const int rows = kv->B * kv->H;
   if (!ws || ws_bytes < topk_workspace_bytes(rows, kv->L_max)) return SKV_EWORKSPACE;
@@ -155,6 +156,7 @@ skv_status sparsekv_gather_attend(const skv_kv* kv, const void* q, int32_t G, co
                                   int32_t k, skv_window win, float scale, float* out, void* ws,
                                   size_t ws_bytes, hipStream_t stream) {
   if (!kv_ok(kv) || !q || !out || G < 1 || k < 0 || (k > 0 && !idx)) return SKV_EINVAL;
+  if (k > kv->L_max) return SKV_EINVAL;
   if (!win.lo || !win.hi || !isfinite(scale)) return SKV_EINVAL;
   const KvArgs a = to_args(kv);
   if (kv->v == nullptr) {
@@ -176,7 +178,7 @@ skv_status sparsekv_select_attend(const skv_kv* kv, const void* q, int32_t G, sk
                                   int32_t* count, float* out, void* ws, size_t ws_bytes,
                                   hipStream_t stream) {
   if (!kv_ok(kv) || !q || !scores || !idx || !count || !out || G < 1 || k < 1) return SKV_EINVAL;
-  if (!win.lo || !win.hi || !isfinite(scale)) return SKV_EINVAL;
+  if (k > kv->L_max || !win.lo || !win.hi || !isfinite(scale)) return SKV_EINVAL;
   const KvArgs a = to_args(kv);
   if (!score_supported(kv, G) || !select_attend_supported(a, G)) return SKV_EUNSUPPORTED;
   const size_t th = topk_workspace_bytes(kv->B * kv->H, kv->L_max);
@@ -195,7 +197,7 @@ skv_status sparsekv_select_attend_resume(const skv_kv* kv, const void* q, int32_
                                          float* out, void* ws, size_t ws_bytes,
                                          hipStream_t stream) {
   if (!kv_ok(kv) || !q || !scores || !idx || !count || !out || G < 1 || k < 1) return SKV_EINVAL;
-  if (!win.lo || !win.hi || !isfinite(scale)) return SKV_EINVAL;
+  if (k > kv->L_max || !win.lo || !win.hi || !isfinite(scale)) return SKV_EINVAL;
   const KvArgs a = to_args(kv);
   if (!score_supported(kv, G) || !select_attend_supported(a, G)) return SKV_EUNSUPPORTED;
   const size_t th = topk_workspace_bytes(kv->B * kv->H, kv->L_max);
@@ -229,7 +231,7 @@ skv_status sparsekv_block_select(const skv_kv* kv, void* summ, const void* q, in
                                  hipStream_t stream) {
   if (!kv_ok(kv) || !summ || !q || !blk_scores || !blk_idx || !blk_count || !tok_idx)
     return SKV_EINVAL;
-  if (G < 1 || K < 1 || !win.lo || !win.hi) return SKV_EINVAL;
+  if (G < 1 || K < 1 || K > kv->L_max / 16 || !win.lo || !win.hi) return SKV_EINVAL;
   const KvArgs a = to_args(kv);
   if (!block_select_supported(a, G)) return SKV_EUNSUPPORTED;
   if (!ws || ws_bytes < block_select_ws_bytes(a, G)) return SKV_EWORKSPACE;

@@ -31,10 +31,19 @@ constexpr int kS = 16;   // tokens per block
 // work item (r, m, c): row r (0 = K, 1 = V), move m of the group, 16-byte
 // chunk c of the row.  Four items' loads are issued before their stores.
 // The workgroups of head 0 then point the token table at the targets.
+// A move whose sequence, token or either slot lies outside the table or the
+// pool of n_slots slots is skipped (no row is read or written for it) and,
+// once per move, counted into *err when err is given.
+__device__ __forceinline__ bool move_ok(const skv_move& mv, int B, int L_max, int64_t n_slots) {
+  return mv.b >= 0 && mv.b < B && mv.t >= 0 && mv.t < L_max && mv.src >= 0 && mv.src < n_slots &&
+         mv.dst >= 0 && mv.dst < n_slots;
+}
+
 __global__ __launch_bounds__(256) void compact_copy_kernel(char* k, char* v, int H, int row_k,
                                                            int row_v, const skv_move* moves,
                                                            int n_moves, int32_t* token_table,
-                                                           int L_max) {
+                                                           int B, int L_max, int64_t n_slots,
+                                                           int32_t* err) {
   const int m0 = blockIdx.x * 16, h = blockIdx.y;
   const int nm = min(16, n_moves - m0);
   const int ck = row_k / 16, cv = row_v / 16;
@@ -54,6 +63,7 @@ __global__ __launch_bounds__(256) void compact_copy_kernel(char* k, char* v, int
       const int cpr = is_v ? cv : ck;
       const int m = rem / cpr, c = rem - m * cpr;
       const skv_move mv = moves[m0 + m];
+      if (!move_ok(mv, B, L_max, n_slots)) continue;
       const int row = is_v ? row_v : row_k;
       base[u] = is_v ? v : k;
       const int64_t so = (((int64_t)(mv.src / kS) * H + h) * kS + mv.src % kS) * row + 16 * c;
@@ -66,7 +76,10 @@ __global__ __launch_bounds__(256) void compact_copy_kernel(char* k, char* v, int
   }
   if (h == 0 && threadIdx.x < nm) {
     const skv_move mv = moves[m0 + threadIdx.x];
-    token_table[(int64_t)mv.b * L_max + mv.t] = mv.dst;
+    if (move_ok(mv, B, L_max, n_slots))
+      token_table[(int64_t)mv.b * L_max + mv.t] = mv.dst;
+    else if (err)
+      atomicAdd(err, 1);
   }
 }
 
@@ -229,6 +242,8 @@ skv_status sparsekv_compact_plan(const int32_t* token_table, const int32_t* seq_
     return SKV_EINVAL;
   *n_moves = *n_src = *n_dst = 0;
   const int64_t n_slots = (int64_t)n_blocks * kS;
+  for (int i = 0; i < n_free; ++i)
+    if (free_blocks[i] < 0 || free_blocks[i] >= n_blocks) return SKV_EINVAL;
   // live tokens per block over every sequence (the caller's running counts
   // when given), and this sequence's own
   std::vector<int32_t> all;
@@ -244,6 +259,14 @@ skv_status sparsekv_compact_plan(const int32_t* token_table, const int32_t* seq_
         }
     }
     counts = all.data();
+  }
+  {
+    std::vector<char> seen(n_blocks, 0);
+    for (int i = 0; i < n_free; ++i) {
+      const int32_t p = free_blocks[i];
+      if (counts[p] != 0 || seen[p]) return SKV_EINVAL;
+      seen[p] = 1;
+    }
   }
   std::vector<int32_t> own(n_blocks, 0);
   const int len = std::min(seq_len[b], L_max);
@@ -300,9 +323,9 @@ skv_status sparsekv_compact_plan(const int32_t* token_table, const int32_t* seq_
   return SKV_OK;
 }
 
-skv_status sparsekv_compact_apply(const skv_kv* kv, const skv_move* moves, int32_t n_moves,
-                                  hipStream_t stream) {
-  if (!pool_ok(kv) || !kv->token_table || n_moves < 0 || (n_moves > 0 && !moves))
+skv_status sparsekv_compact_apply(const skv_kv* kv, int32_t n_blocks, const skv_move* moves,
+                                  int32_t n_moves, int32_t* err, hipStream_t stream) {
+  if (!pool_ok(kv) || !kv->token_table || n_blocks < 1 || n_moves < 0 || (n_moves > 0 && !moves))
     return SKV_EINVAL;
   const int es = kv->dtype == SKV_BF16 ? 2 : 4;
   const int row_k = kv->d_k * es, row_v = kv->v ? kv->d_v * es : 0;
@@ -310,7 +333,7 @@ skv_status sparsekv_compact_apply(const skv_kv* kv, const skv_move* moves, int32
   if (n_moves == 0) return SKV_OK;
   compact_copy_kernel<<<dim3((n_moves + 15) / 16, kv->H), 256, 0, stream>>>(
       (char*)kv->k, (char*)kv->v, kv->H, row_k, row_v, moves, n_moves,
-      (int32_t*)kv->token_table, kv->L_max);
+      (int32_t*)kv->token_table, kv->B, kv->L_max, (int64_t)n_blocks * kS, err);
   return hipGetLastError() == hipSuccess ? SKV_OK : SKV_ELAUNCH;
 }
 

@@ -75,7 +75,7 @@ def test_score_rejects_bad_kv_without_launching(over):
 
 def test_argument_validation_paths():
     L = S.lib()
-    kv = _kv()
+    kv = _kv(L_max=4096)
     assert L.sparsekv_score(ctypes.byref(kv), None, 1, ctypes.c_void_p(1), None) == S.SKV_EINVAL
     assert L.sparsekv_score(ctypes.byref(kv), ctypes.c_void_p(1), 0, ctypes.c_void_p(1), None) == S.SKV_EINVAL
     assert L.sparsekv_score(ctypes.byref(kv), ctypes.c_void_p(1), 64, ctypes.c_void_p(1), None) == S.SKV_EUNSUPPORTED
@@ -132,3 +132,39 @@ def test_topk_and_select_check_workspace_before_launch():
     st = L.sparsekv_select(ctypes.byref(kv), ctypes.c_void_p(1), 4, win, 0, ctypes.c_void_p(1),
                            ctypes.c_void_p(1), ctypes.c_void_p(1), ctypes.c_void_p(1), need, None)
     assert st == S.SKV_EINVAL
+
+
+def test_every_selecting_call_rejects_k_above_L_max():
+    """1 <= k <= L_max for every selecting entry point (checked before any
+    launch: the pointers below are never dereferenced)."""
+    L = S.lib()
+    P = ctypes.c_void_p(1)
+    win = S.skv_window(P, P)
+    kv = _kv(B=2, H=2, L_max=64)
+    big = 1 << 30
+    assert L.sparsekv_topk(P, 2, 2, 64, win, 65, P, P, P, big, None) == S.SKV_EINVAL
+    assert L.sparsekv_topk_resume(P, 2, 2, 64, win, 65, P, P, P, big, None) == S.SKV_EINVAL
+    assert L.sparsekv_topk_prefiltered(P, 2, 2, 64, win, 65, P, 0.5, P, P, None, P, big,
+                                       None) == S.SKV_EINVAL
+    assert L.sparsekv_select(ctypes.byref(kv), P, 4, win, 65, P, P, P, P, big, None) == S.SKV_EINVAL
+    assert L.sparsekv_select_attend(ctypes.byref(kv), P, 4, win, 65, 0.1, P, P, P, P, P, big,
+                                    None) == S.SKV_EINVAL
+    assert L.sparsekv_select_attend_resume(ctypes.byref(kv), P, 4, win, 65, 0.1, P, P, P, P, P,
+                                           big, None) == S.SKV_EINVAL
+    assert L.sparsekv_gather_attend(ctypes.byref(kv), P, 4, P, 65, win, 0.1, P, P, big,
+                                    None) == S.SKV_EINVAL
+    pkv = _kv(B=2, H=2, L_max=64, block=16, block_table=1)
+    assert L.sparsekv_block_select(ctypes.byref(pkv), P, P, 4, win, 5, P, P, P, P, P, big,
+                                   None) == S.SKV_EINVAL
+    # k == L_max stays valid: the top-k then reports the workspace, not k
+    assert L.sparsekv_topk(P, 2, 2, 64, win, 64, P, P, None, 0, None) == S.SKV_EWORKSPACE
+
+
+def test_compact_apply_validates_pool_size():
+    L = S.lib()
+    kv = _kv(B=1, H=1, L_max=64, block=16, token_table=1)
+    mv = ctypes.c_void_p(1)
+    assert L.sparsekv_compact_apply(ctypes.byref(kv), 0, mv, 4, None, None) == S.SKV_EINVAL
+    assert L.sparsekv_compact_apply(ctypes.byref(kv), 8, mv, -1, None, None) == S.SKV_EINVAL
+    assert L.sparsekv_compact_apply(ctypes.byref(kv), 8, None, 4, None, None) == S.SKV_EINVAL
+    assert L.sparsekv_compact_apply(ctypes.byref(kv), 8, None, 0, None, None) == S.SKV_OK

@@ -55,3 +55,31 @@ def test_plan_matches_oracle_on_random_tables_with_shared_blocks():
         for b in range(B):
             _same(tt, sl, n_blocks, b, free, int(rng.integers(0, len(free) + 1)),
                   float(rng.choice([0.0, 0.25, 0.5])), int(rng.integers(1, 10)))
+
+
+def _pool_with_free():
+    st = W.make_token_pool(tag=84, B=2, H=1, d=64, L=512, k=16, sink=4, local=16, spare_blocks=8)
+    kv = st.kv
+    return kv, kv.k.shape[0], [int(x) for x in st.meta["free_blocks"]]
+
+
+def test_plan_rejects_free_blocks_outside_the_pool():
+    kv, n_blocks, free = _pool_with_free()
+    for bad in (-1, n_blocks, n_blocks + 100):
+        with pytest.raises(S.SkvError) as e:
+            S.sparsekv_compact_plan(kv.token_table, kv.seq_len, n_blocks, 0, free[:3] + [bad],
+                                    4, 0.0, 8)
+        assert e.value.status == S.SKV_EINVAL
+
+
+def test_plan_rejects_free_blocks_that_hold_live_tokens_or_repeat():
+    kv, n_blocks, free = _pool_with_free()
+    live_block = int(kv.token_table[0][kv.token_table[0] >= 0][0]) // 16
+    for fb in ([live_block] + free[:2], free[:2] + [free[0]]):
+        with pytest.raises(S.SkvError) as e:
+            S.sparsekv_compact_plan(kv.token_table, kv.seq_len, n_blocks, 0, fb, len(fb), 0.0, 8)
+        assert e.value.status == S.SKV_EINVAL
+    # the entries past n_free are not part of the plan's input
+    moves, src, n_dst = S.sparsekv_compact_plan(kv.token_table, kv.seq_len, n_blocks, 0,
+                                                free + [live_block], len(free), 0.0, 8)
+    assert n_dst <= len(free)

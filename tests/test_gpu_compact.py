@@ -142,3 +142,37 @@ def test_live_hash_every_layout(layout):
         kv = W.make_indexer_mla(tag=994, L=1024, n_heads=16, k=64).kv
     kv_d = S.kv_to_device(kv, DEV)
     assert _hashes(kv_d) == _oracle_hashes(kv)
+
+
+def test_apply_skips_moves_outside_the_table_or_pool():
+    """Moves whose sequence, token or slots fall outside the table or the pool
+    are skipped before any address is formed and counted into err; the valid
+    moves of the same launch are applied exactly as the oracle applies them."""
+    st = W.make_token_pool(tag=97, B=2, H=2, d=128, L=512, k=16, sink=4, local=16,
+                           spare_blocks=16)
+    kv = st.kv
+    n_blocks = kv.k.shape[0]
+    n_slots = n_blocks * 16
+    kv_d = S.kv_to_device(kv, DEV)
+    free = list(st.meta["free_blocks"])
+    moves, src, n_dst = S.sparsekv_compact_plan(kv.token_table, kv.seq_len, n_blocks, 0, free,
+                                                len(free), 0.0, 4)
+    assert len(moves) > 0
+    ref = copy.deepcopy(kv)
+    C.apply(ref, 0, [tuple(m[1:]) for m in moves.tolist()])
+    good = moves.tolist()
+    t_dead = int(np.nonzero(kv.token_table[1] < 0)[0][0])
+    bad = [[0, good[0][1], good[0][2], n_slots],        # dst past the pool
+           [0, good[0][1], n_slots + 5, good[0][3]],    # src past the pool
+           [1, t_dead, -3, good[0][3]],                 # negative src
+           [2, 0, good[0][2], good[0][3]],              # sequence past B
+           [0, kv.L_max, good[0][2], good[0][3]]]       # token past L_max
+    mixed = np.array(bad[:2] + good + bad[2:], np.int32)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    say("compact skip", len(good), "valid moves,", len(bad), "invalid")
+    S.sparsekv_compact_apply(kv_d, torch.from_numpy(mixed).to(DEV), err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == len(bad)
+    k, v, tt = _pool_bytes(kv_d)
+    assert np.array_equal(tt, ref.token_table)
+    assert np.array_equal(k, ref.k) and np.array_equal(v, ref.v)

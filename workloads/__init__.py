@@ -196,6 +196,27 @@ class Paris:
                   seq_len=np.array([self.L], np.int32))
 
 
+def live_tokens(kv: KV, b: int) -> np.ndarray:
+    """Logical positions t < seq_len[b] of sequence b that the storage holds:
+    a token-table entry >= 0, a block-table entry >= 0 for block t // 16, or
+    any t of contiguous storage (a layout property, used for accounting)."""
+    n = int(min(int(kv.seq_len[b]), kv.L_max))
+    t = np.arange(n, dtype=np.int64)
+    if kv.token_table is not None:
+        return t[kv.token_table[b, :n] >= 0]
+    if kv.block_table is not None:
+        return t[kv.block_table[b, t // 16] >= 0]
+    return t
+
+
+def block_occupancy(token_table: np.ndarray, seq_len: np.ndarray, n_blocks: int) -> np.ndarray:
+    """Live tokens per physical 16-token block of a token-table pool."""
+    slots = [token_table[b, : int(seq_len[b])] for b in range(token_table.shape[0])]
+    s = np.concatenate(slots) if slots else np.zeros(0, np.int32)
+    s = s[s >= 0].astype(np.int64)
+    return np.bincount(s // 16, minlength=n_blocks).astype(np.int32)
+
+
 # --------------------------------------------------------------------------
 # Workloads
 # --------------------------------------------------------------------------

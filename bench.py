@@ -250,6 +250,37 @@ def sources_sha256(files):
     return h.hexdigest()
 
 
+def time_isolated(call, args, hip):
+    """Mean duration of one launch of a call (its kernels only), ms: the
+    call(i) of args.steps steps captured back to back in one HIP graph
+    (rotating over the same input copies as the step), replayed once to
+    warm up, then once between two events.  No event node sits between the
+    launches, so the figure carries the kernels and the boundaries between
+    them, not the event overhead of the per-call timing."""
+    import torch
+    K = args.steps
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(K):
+            call(i)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = hip.create(), hip.create()
+    hip.record(e0)
+    g.replay()
+    hip.record(e1)
+    torch.cuda.synchronize()
+    ms = hip.elapsed_ms(e0, e1) / K
+    del g
+    return ms
+
+
 def traffic_entry(workload, kernels):
     """HBM bytes per launch of the named kernels (summed), from the committed
     rocprofv3 counter record of the workload (profiles/pmc_<workload>.json),
@@ -450,6 +481,24 @@ def bench_dense(args, hip):
     wall, gpu_ms, calls, note = timed_steps(step, 2 if fused else 3, args, hip)
     calls = np.array(calls)
     ms_per_step = wall * 1e3 / args.steps
+    # the dominant kernel alone: the scan with its histogram, on a workspace
+    # of its own (the histograms accumulate over the repeated launches)
+    ws_iso = S.workspace(S.sparsekv_workspace_size(S.SKV_OP_SELECT, skv, sG, k), dev)
+    if prefilter:
+        thr_iso = thr.clone()
+        scan_iso_ms = time_isolated(
+            lambda i: S.sparsekv_score_prefilter(pairs[i % len(pairs)][0], sq, sG, lo, hi, thr_iso,
+                                                 scores, ws_iso), args, hip)
+    else:
+        scan_iso_ms = time_isolated(
+            lambda i: S.sparsekv_score_hist(pairs[i % len(pairs)][0], sq, sG, lo, hi, scores,
+                                            ws_iso), args, hip)
+    del ws_iso
+    att_iso_ms = None
+    if mla:
+        att_iso_ms = time_isolated(
+            lambda i: S.sparsekv_gather_attend(pairs[i % len(pairs)][1], q, G, idx, k, lo, hi,
+                                               st.scale, out, ws_att), args, hip)
     # live keys and algorithmic bytes of the scan and the gather, counted
     # from the workload's own tables
     import workloads as W
@@ -466,7 +515,7 @@ def bench_dense(args, hip):
     row_bytes = (kv.d_k * (2 if bf else 4)) * (1 if mla else 2)
     gather_bytes = n_att * row_bytes
     step_bytes = scan_bytes + gather_bytes
-    scan_s = float(np.mean(calls[:, 0])) * 1e-3
+    scan_s = scan_iso_ms * 1e-3
     kname = ("score_stream_kernel" if (bf and skv.d_k % 32 == 0 and skv.d_k <= 256) else
              "score_valu_kernel")
     # the counter record holds the histogram scan; the survivor scan has none
@@ -504,19 +553,24 @@ def bench_dense(args, hip):
                               "the predicted threshold)" if prefilter else
                               "score scan (sparsekv_score_hist: %s with the fused top-k histogram)")
                              % kname, "hbm", scan_bytes, scan_s, tr,
-                             {"algorithmic_bytes_per_launch": scan_bytes, "bytes_per_key": per_key}),
+                             {"algorithmic_bytes_per_launch": scan_bytes, "bytes_per_key": per_key,
+                              "us_per_launch": scan_iso_ms * 1e3,
+                              "timing": "isolated replay of %d back-to-back launches" % args.steps}),
     })
     if mla:
         # the latent attention is a dense contraction on matrix cores:
         # per selected token and head, 576 + 512 multiply-adds
-        att_s = float(np.mean(calls[:, 2])) * 1e-3
+        att_s = att_iso_ms * 1e-3
         flops = 2.0 * n_att * G * (kv.d_k + kv.d_v)
         rec["roofline_attention"] = roofline("latent attention (sparsekv_gather_attend: "
                                              "mla_split_kernel + merge)", "mfma", flops, att_s,
                                              traffic_entry(args.workload, ["mla_split_kernel",
                                                                            "attend_reduce_kernel"]),
                                              {"algorithmic_flops_per_launch": flops,
-                                              "gathered_bytes": gather_bytes})
+                                              "gathered_bytes": gather_bytes,
+                                              "us_per_launch": att_iso_ms * 1e3,
+                                              "timing": "isolated replay of %d back-to-back "
+                                                        "launches" % args.steps})
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = dense_cpu_baseline(st, args.cpu_seconds)
     return rec
@@ -708,11 +762,14 @@ def bench_paris(args, hip):
     wall, gpu_ms, calls, note = timed_steps(step, 2, args, hip)
     calls = np.array(calls)
     ms = wall * 1e3 / args.steps
+    ret_iso_ms = time_isolated(
+        lambda i: S.sparsekv_retrieve(cb, ixs[i % len(ixs)], q, p.G, p.rho, p.beta, p.k_final,
+                                      idx=ridx, n_cand=ncand, ws=ws_r), args, hip)
     n_keys = p.H * p.n
     C = int(math.ceil(p.beta * p.n))
     ret_bytes = n_keys * 16 + p.H * C * 128      # ids scanned + codes and w of the candidates
     gather = p.H * (p.k_final + p.sink + p.local) * 512
-    t_ret = float(np.mean(calls[:, 0])) * 1e-3
+    t_ret = ret_iso_ms * 1e-3
     rec = base_record("history keys voted/s (one compressed-code retrieval decode step)",
                       n_keys / (ms * 1e-3), "keys/s", args, ms, "u8/f32",
                       {"workload": "paris", "B": 1, "H_kv": p.H, "G": p.G, "d": p.d, "L": p.L,
@@ -722,7 +779,8 @@ def bench_paris(args, hip):
     rec.update({
         "us_per_step": ms * 1e3, "us_per_step_gpu": gpu_ms * 1e3, "timing": note,
         "us_per_step_events": step_percentiles(calls),
-        "us_per_call": {"retrieve": t_ret * 1e6, "gather_attend": float(np.mean(calls[:, 1])) * 1e3},
+        "us_per_call": {"retrieve": float(np.mean(calls[:, 0])) * 1e3,
+                        "gather_attend": float(np.mean(calls[:, 1])) * 1e3},
         "keys_voted_per_step": n_keys,
         "step_algorithmic_bytes": ret_bytes + gather,
         "step_GBps": (ret_bytes + gather) / (ms * 1e-3) / 1e9,
@@ -730,7 +788,10 @@ def bench_paris(args, hip):
                              "rerank, top-100; the vote kernel moves 94 % of the bytes)", "hbm",
                              ret_bytes, t_ret, traffic_entry("paris", RETRIEVE_KERNELS),
                              {"algorithmic_bytes_per_launch": ret_bytes,
-                              "traffic_kernels": list(RETRIEVE_KERNELS)}),
+                              "traffic_kernels": list(RETRIEVE_KERNELS),
+                              "us_per_launch": ret_iso_ms * 1e3,
+                              "timing": "isolated replay of %d back-to-back launches"
+                                        % args.steps}),
     })
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = paris_cpu_baseline(args.cpu_seconds)

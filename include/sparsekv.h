@@ -236,6 +236,26 @@ skv_status sparsekv_select_attend_resume(const skv_kv* kv, const void* q, int32_
                                          float* out, void* ws, size_t ws_bytes,
                                          hipStream_t stream);
 
+/* sparsekv_select_attend for callers that cannot allocate device memory or
+ * hand in a workspace (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same kernels and results as
+ * sparsekv_select_attend, with the workspace taken from a scratch area the
+ * library holds on each GPU it runs on (16 MiB, a device global, kept until
+ * the process ends).  The call allocates nothing; it zero-fills the part of
+ * the scratch that must start at zero, so no state carries over from an
+ * earlier call.  It needs sparsekv_select_attend_noalloc_bytes(kv, G) bytes
+ * of scratch (B H 16 KiB of histograms, rounded to 256 bytes, plus
+ * B H G 8 (d_v + 2) 4 bytes of split partials) and returns SKV_EWORKSPACE
+ * when that exceeds 16 MiB.  Every call on one GPU shares that GPU's
+ * scratch: calls that may overlap on one GPU (different streams without
+ * ordering between them) race and must not be issued.  Arguments, supported
+ * shapes and other errors as sparsekv_select_attend. */
+size_t sparsekv_select_attend_noalloc_bytes(const skv_kv* kv, int32_t G);
+skv_status sparsekv_select_attend_noalloc(const skv_kv* kv, const void* q, int32_t G,
+                                          skv_window win, int32_t k, float scale, float* scores,
+                                          int32_t* idx, int32_t* count, float* out,
+                                          hipStream_t stream);
+
 /* -------------------------------------------------- block-summary scoring --
  * OasisKV reading notes, section 3.2 (after Quest): each logical 16-token
  * block keeps, per KV head, the coordinate-wise minimum mn and maximum mx of

@@ -90,6 +90,9 @@ _SIGS = {
     "sparsekv_select_attend_resume": (c_i32, [ctypes.POINTER(skv_kv), c_vp, c_i32, skv_window,
                                               c_i32, c_f32, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz,
                                               c_vp]),
+    "sparsekv_select_attend_noalloc_bytes": (c_sz, [ctypes.POINTER(skv_kv), c_i32]),
+    "sparsekv_select_attend_noalloc": (c_i32, [ctypes.POINTER(skv_kv), c_vp, c_i32, skv_window,
+                                               c_i32, c_f32, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "sparsekv_block_summary_bytes": (c_sz, [c_i32, c_i32, c_i32]),
     "sparsekv_block_summarize": (c_i32, [ctypes.POINTER(skv_kv), c_i32, c_i32, c_i32, c_vp, c_vp]),
     "sparsekv_block_summarize_last": (c_i32, [ctypes.POINTER(skv_kv), c_vp, c_vp]),
@@ -338,6 +341,36 @@ def sparsekv_select_attend_resume(kv: KVTensors, q: torch.Tensor, G: int, lo: to
                                                _ptr(scores), _ptr(idx), _ptr(count), _ptr(out),
                                                _ptr(ws), ws.numel() * ws.element_size(), _stream()))
     return idx, count, out
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def sparsekv_select_attend_noalloc_bytes(kv: KVTensors, G: int) -> int:
+    c = kv.c()
+    return int(lib().sparsekv_select_attend_noalloc_bytes(ctypes.byref(c), G))
+
+
+def sparsekv_select_attend_noalloc(kv: KVTensors, q: torch.Tensor, G: int, lo: torch.Tensor,
+                                   hi: torch.Tensor, k: int, scale: float, scores: torch.Tensor,
+                                   idx: torch.Tensor, count: torch.Tensor, out: torch.Tensor):
+    """sparsekv_select_attend with the library's own per-GPU scratch instead
+    of a workspace; the caller passes every output (nothing is allocated).
+    Returns (scores, idx, count, out)."""
+    _dev(q, "q", kv.torch_dtype)
+    if q.shape != (kv.B, kv.H * G, kv.d_k):
+        raise ValueError("q must be [B][H*G][d_k]")
+    for t, nm, dt in ((scores, "scores", torch.float32), (idx, "idx", torch.int32),
+                      (count, "count", torch.int32), (out, "out", torch.float32),
+                      (lo, "lo", torch.int32), (hi, "hi", torch.int32)):
+        _dev(t, nm, dt)
+    c = kv.c()
+    _check("sparsekv_select_attend_noalloc",
+           lib().sparsekv_select_attend_noalloc(ctypes.byref(c), _ptr(q), G,
+                                                skv_window(_ptr(lo), _ptr(hi)), k, float(scale),
+                                                _ptr(scores), _ptr(idx), _ptr(count), _ptr(out),
+                                                _stream()))
+    return scores, idx, count, out
 
 
 def sparsekv_block_summary_bytes(n_blocks: int, H: int, d_k: int) -> int:

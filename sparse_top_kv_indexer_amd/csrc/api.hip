@@ -3,6 +3,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/sparsekv.h"
 #include "skv_internal.h"
@@ -68,6 +69,43 @@ bool score_supported(const skv_kv* kv, int G) {
 skv_status launched(hipError_t e) {
   if (e == hipErrorInvalidValue) return SKV_EUNSUPPORTED;
   return e == hipSuccess ? SKV_OK : SKV_ELAUNCH;
+}
+
+// Library-owned scratch of sparsekv_select_attend_noalloc: one copy per GPU
+// (a device global), held until the process ends.  Host code never passes
+// `scratch` itself to a kernel -- on the host that name is only a stand-in --
+// but the address hipGetSymbolAddress returns for the current device.
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// This device's copy of scratch, resolved once per device.
+hipError_t scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return e != hipSuccess ? e : hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+// Scratch layout of the fused step without a workspace: the rows' key
+// histograms (must be zero when the scan starts), then the split partials.
+size_t noalloc_hist_bytes(int rows) { return ((size_t)rows * 4096 * 4 + 255) & ~(size_t)255; }
+
+__global__ __launch_bounds__(256) void zero_words_kernel(uint4* p, int64_t n16) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
 }  // namespace
@@ -204,6 +242,39 @@ skv_status sparsekv_select_attend_resume(const skv_kv* kv, const void* q, int32_
   if (!ws || ws_bytes < th + select_attend_partial_bytes(a, G)) return SKV_EWORKSPACE;
   return launched(launch_select_attend(a, q, G, scores, win.lo, win.hi, k, (uint32_t*)ws, scale,
                                        idx, count, (float*)((char*)ws + th), out, stream));
+}
+
+size_t sparsekv_select_attend_noalloc_bytes(const skv_kv* kv, int32_t G) {
+  if (!kv || kv->B < 1 || kv->H < 1 || G < 1 || kv->d_k < 1) return 0;
+  return noalloc_hist_bytes(kv->B * kv->H) + select_attend_partial_bytes(to_args(kv), G);
+}
+
+skv_status sparsekv_select_attend_noalloc(const skv_kv* kv, const void* q, int32_t G,
+                                          skv_window win, int32_t k, float scale, float* scores,
+                                          int32_t* idx, int32_t* count, float* out,
+                                          hipStream_t stream) {
+  if (!kv_ok(kv) || !q || !scores || !idx || !count || !out || G < 1 || k < 1) return SKV_EINVAL;
+  if (k > kv->L_max || !win.lo || !win.hi || !isfinite(scale)) return SKV_EINVAL;
+  const KvArgs a = to_args(kv);
+  if (!score_supported(kv, G) || !select_attend_supported(a, G)) return SKV_EUNSUPPORTED;
+  const int rows = kv->B * kv->H;
+  const size_t hb = noalloc_hist_bytes(rows);
+  if (hb + select_attend_partial_bytes(a, G) > kScratchBytes) return SKV_EWORKSPACE;
+  void* base = nullptr;
+  if (scratch_for_current_device(&base) != hipSuccess) return SKV_ELAUNCH;
+  uint32_t* hist = (uint32_t*)base;
+  float* part = (float*)((char*)base + hb);
+  // the histograms start at zero whatever an earlier call left (a fill
+  // kernel, not a memset node, so the call can be captured in a graph)
+  const int64_t n16 = (int64_t)hb / 16;
+  zero_words_kernel<<<(unsigned)std::min<int64_t>(1024, (n16 + 255) / 256), 256, 0, stream>>>(
+      (uint4*)hist, n16);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return launched(e);
+  e = launch_score(a, q, G, scores, win.lo, win.hi, hist, stream);
+  if (e != hipSuccess) return launched(e);
+  return launched(launch_select_attend(a, q, G, scores, win.lo, win.hi, k, hist, scale, idx, count,
+                                       part, out, stream));
 }
 
 size_t sparsekv_block_summary_bytes(int32_t n_blocks, int32_t H, int32_t d_k) {

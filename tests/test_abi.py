@@ -168,3 +168,19 @@ def test_compact_apply_validates_pool_size():
     assert L.sparsekv_compact_apply(ctypes.byref(kv), 8, mv, -1, None, None) == S.SKV_EINVAL
     assert L.sparsekv_compact_apply(ctypes.byref(kv), 8, None, 4, None, None) == S.SKV_EINVAL
     assert L.sparsekv_compact_apply(ctypes.byref(kv), 8, None, 0, None, None) == S.SKV_OK
+
+
+def test_noalloc_rejects_sizes_beyond_its_scratch_before_any_device_work():
+    L = S.lib()
+    P = ctypes.c_void_p(1)
+    win = S.skv_window(P, P)
+    small = _kv(B=4, H=8, L_max=4096, block=16, block_table=1)
+    need = L.sparsekv_select_attend_noalloc_bytes(ctypes.byref(small), 4)
+    assert need == 4 * 8 * 4096 * 4 + 4 * 8 * 4 * 8 * 130 * 4
+    big = _kv(B=64, H=64, L_max=4096, block=16, block_table=1)
+    assert L.sparsekv_select_attend_noalloc_bytes(ctypes.byref(big), 4) > S.NOALLOC_SCRATCH_BYTES
+    st = L.sparsekv_select_attend_noalloc(ctypes.byref(big), P, 4, win, 64, 0.1, P, P, P, P, None)
+    assert st == S.SKV_EWORKSPACE
+    st = L.sparsekv_select_attend_noalloc(ctypes.byref(small), P, 4, win, 4097, 0.1, P, P, P, P,
+                                          None)
+    assert st == S.SKV_EINVAL

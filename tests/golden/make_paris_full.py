@@ -1,13 +1,16 @@
 #!/usr/bin/env python3
 """Write the oracle's results for the full-size compressed-code retrieval
 workload (8 KV heads x 4 query heads, L = 1,048,576 keys, beta = rho = 0.02,
-top-100, sink 4, local 512) to paris_full_expected.json.
+top-100, sink 4, local 512) to paris_full_expected.json, and the same
+retrieval at the larger tier budgets rho = 0.05 and 0.10 (beta unchanged)
+under "by_rho".
 
 Calls only the seeded input generator and oracle/ (no GPU, no HIP library).
 The oracle's fp32 encode of 8.4 M keys takes several minutes on one core, so
 the KV heads are encoded in parallel processes; each head runs the unchanged
 oracle code.  Usage: python tests/golden/make_paris_full.py
 """
+import dataclasses
 import hashlib
 import json
 import multiprocessing as mp
@@ -28,6 +31,7 @@ from oracle import paris as P  # noqa: E402
 
 OUT = os.path.join(HERE, "paris_full_expected.json")
 SAMPLE_ENTRIES = [0, 1, 4095, 65536, 524287, 1048059]
+RHOS = (0.05, 0.10)      # tier budgets besides the workload's rho = beta = 0.02
 _P = None
 
 
@@ -88,11 +92,24 @@ def main():
             "out": o.tolist(),
         })
         print("head", h, "recall", heads[-1]["recall_at_100"], flush=True)
+    by_rho = {}
+    for rho in RHOS:
+        pr = dataclasses.replace(p, rho=rho)
+        rr = P.retrieve(pr, index, lv)
+        by_rho[repr(rho)] = [{
+            "idx": sorted(int(x) for x in rr["idx"][h]),
+            "votes_sha256": sha(rr["S"][h].astype(np.uint8)),
+            "cand_sha256": sha(rr["cand"][h].astype(np.int32)),
+            "est_sha256": sha(rr["est"][h].astype(np.float32)),
+            "recall_at_100": P.recall_at(rr["idx"][h], true[h]),
+        } for h in range(p.H)]
+        print("rho", rho, "mean recall",
+              sum(x["recall_at_100"] for x in by_rho[repr(rho)]) / p.H, flush=True)
     rec = {"about": "oracle results for the full-size compressed-code retrieval workload "
                     "(workloads.make_paris() defaults), written by tests/golden/make_paris_full.py",
            "L": p.L, "H": p.H, "G": p.G, "n": p.n, "beta": p.beta, "rho": p.rho,
            "k_final": p.k_final, "sink": p.sink, "local": p.local,
-           "levels_bits": lv.view(np.uint32).tolist(), "heads": heads}
+           "levels_bits": lv.view(np.uint32).tolist(), "heads": heads, "by_rho": by_rho}
     json.dump(rec, open(OUT, "w"))
     print("wrote", OUT, time.time() - t0, flush=True)
 

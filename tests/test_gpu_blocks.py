@@ -126,11 +126,11 @@ def test_blocks_unmapped_and_short_rows():
     assert _check_block_step(st, 12, _rows(st)) == 0
 
 
-def test_blocks_full_size_sampled_rows():
+def test_blocks_full_size_every_row():
     """4 sequences x 8 KV heads x 4 query heads, d = 128, 32768 tokens
-    (2048 blocks per row), top-128 blocks; oracle on sampled rows."""
+    (2048 blocks per row), top-128 blocks; oracle on all 32 rows."""
     st = W.make_gqa_paged(tag=2, B=4, H=8, G=4, L=32768, k=2048, sink=4, local=64)
-    assert _check_block_step(st, 128, [(0, 0), (1, 5), (3, 7)]) == 0
+    assert _check_block_step(st, 128, [(b, h) for b in range(4) for h in range(8)]) == 0
 
 
 def test_blocks_incremental_summaries_match_rebuild():

@@ -299,25 +299,30 @@ def test_attend_kernel_on_oracle_selection(G):
 
 # ----------------------------------------------------- full-size workloads
 @pytest.mark.slow
-def test_gqa_paged_full_size_sampled_rows():
+def test_gqa_paged_full_size_every_row():
+    """All 32 (sequence, KV head) rows of the GQA decode at L = 32768."""
     st = W.make_gqa_paged()
-    rows = [(0, 0), (1, 5), (2, 3), (3, 7)]
-    assert _end_to_end(st, rows=rows) == 0
+    assert _end_to_end(st) == 0
 
 
 @pytest.mark.slow
-def test_gqa_paged_long_context_sampled_rows():
-    """The GQA decode at L = 131072: rows longer than one workgroup's sweep go
-    through the sliced top-k."""
+def test_gqa_paged_long_context_every_row():
+    """The GQA decode at L = 131072, all 32 rows: rows longer than one
+    workgroup's sweep go through the sliced top-k."""
     st = W.make_gqa_paged(L=131072)
-    rows = [(0, 2), (3, 6)]
-    assert _end_to_end(st, rows=rows) == 0
+    assert _end_to_end(st) == 0
+
+
+def _token_pool_rows():
+    """64 of the 256 rows: two KV heads of every sequence, each head 8 times."""
+    return [(b, (b + 4 * j) % 8) for b in range(32) for j in range(2)]
 
 
 @pytest.mark.slow
-def test_token_pool_full_size_sampled_rows():
+def test_token_pool_full_size_64_rows_over_every_head():
     st = W.make_token_pool()
-    rows = [(0, 0), (13, 4), (31, 7)]
+    rows = _token_pool_rows()
+    assert sorted(set(h for _, h in rows)) == list(range(8))
     assert _end_to_end(st, rows=rows) == 0
 
 

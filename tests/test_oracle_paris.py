@@ -246,3 +246,50 @@ def test_quantised_pipeline_shapes_and_budget():
         mask = np.zeros(p.n, bool)
         mask[res["cand"][h]] = True
         assert S[mask].min() >= S[~mask].max()
+
+
+# ------------------------------------------------------- verdict-item pins
+def test_histogram_counts_each_subspace_column_separately():
+    """A hand-built id matrix whose subspaces have different counts: a
+    histogram built from one column for every row, or over the flattened
+    matrix, or with the axes swapped, fails this."""
+    ids = np.array([[3, 0, 7],
+                    [3, 1, 7],
+                    [5, 1, 7],
+                    [3, 1, 0],
+                    [0, 2, 7]], np.uint8)
+    h = P.histogram(ids, 8)
+    assert h.shape == (3, 8)
+    assert h[0].tolist() == [1, 0, 0, 3, 0, 1, 0, 0]
+    assert h[1].tolist() == [1, 3, 1, 0, 0, 0, 0, 0]
+    assert h[2].tolist() == [1, 0, 0, 0, 0, 0, 0, 4]
+    assert h.sum(axis=1).tolist() == [5, 5, 5]
+
+
+def test_normalise_zero_rows_give_zero_direction_and_norm():
+    """Reading 17: a zero row normalises to the zero vector with norm 0 (no
+    NaN), and leaves the other rows of the batch untouched."""
+    x = np.zeros((3, 128), F32)
+    x[1, 5] = F32(-3.0)
+    x[2, :] = F32(0.5)
+    xh, nrm = P.normalise(x)
+    assert nrm.dtype == F32 and nrm.tolist() == [0.0, 3.0, float(np.sqrt(F32(32.0)))]
+    assert np.all(xh[0] == 0) and not np.isnan(xh).any()
+    assert xh[1, 5] == F32(-1.0) and np.count_nonzero(xh[1]) == 1
+    np.testing.assert_allclose(np.linalg.norm(xh[2].astype(np.float64)), 1.0, rtol=1e-6)
+    # a zero key encodes to id 0, codes 0 and w 0 (reading 17)
+    lv, th = lloyd.codebook_f32(8)
+    ids, codes, w, _ = P.encode_keys(np.zeros((1, 128), np.uint16), _signs(128, 9), 16, lv, th)
+    assert not ids.any() and not codes.any() and not w.any()
+
+
+def test_candidate_budget_values():
+    """C = ceil(beta n), written out: the full workload's n = 1,048,060 at
+    beta = 0.02 gives 20,962 (2 % of n is 20,961.2); exact multiples are
+    not rounded up; beta = 1 keeps every entry."""
+    assert cf.n_candidates(0.02, 1048060) == 20962
+    assert cf.n_candidates(0.02, 100) == 2
+    assert cf.n_candidates(0.02, 101) == 3
+    assert cf.n_candidates(0.05, 2000) == 100
+    assert cf.n_candidates(1.0, 777) == 777
+    assert cf.n_candidates(0.1, 5) == 1

@@ -432,8 +432,10 @@ def bench_dense(args, hip):
     idx = torch.empty((B, H, k), dtype=torch.int32, device=dev)
     cnt = torch.empty((B, H), dtype=torch.int32, device=dev)
     out = torch.empty((kv.B, kv.H * G, kv.d_v), dtype=torch.float32, device=dev)
-    fused = (args.path == "fused" and skv is kv and sG == G and bf and not mla and kv.d_k == 128
-             and G <= 8 and L <= 32768)
+    # fused: the top-k finished inside the attention kernel (GQA rows of one
+    # sweep; the latent attention at any length)
+    fused = args.path == "fused" and (mla or (skv is kv and sG == G and bf and kv.d_k == 128
+                                              and G <= 8 and L <= 32768))
     prefilter = args.path == "prefilter"
     blocks = args.path == "blocks"
     if blocks:
@@ -441,7 +443,9 @@ def bench_dense(args, hip):
     thr = torch.full((B, H), float("-inf"), dtype=torch.float32, device=dev)
     used = torch.zeros((B, H), dtype=torch.int32, device=dev)
     if fused:
-        ws_sel = S.workspace(S.sparsekv_workspace_size(S.SKV_OP_SELECT_ATTEND, kv, G, k), dev)
+        ws_sel = S.workspace(max(S.sparsekv_workspace_size(S.SKV_OP_SELECT_ATTEND, kv, G, k),
+                                 S.sparsekv_workspace_size(S.SKV_OP_SELECT, skv, sG, k)), dev)
+        ws_att = S.workspace(S.sparsekv_workspace_size(S.SKV_OP_GATHER_ATTEND, kv, G, k), dev)
     else:
         ws_sel = S.workspace(S.sparsekv_workspace_size(S.SKV_OP_SELECT, skv, sG, k), dev)
         ws_att = S.workspace(S.sparsekv_workspace_size(S.SKV_OP_GATHER_ATTEND, kv, G, k), dev)
@@ -559,7 +563,8 @@ def bench_dense(args, hip):
     })
     if mla:
         # the latent attention is a dense contraction on matrix cores:
-        # per selected token and head, 576 + 512 multiply-adds
+        # per selected token and head, 576 + 512 multiply-adds (the isolated
+        # timing is of sparsekv_gather_attend over the step's selection)
         att_s = att_iso_ms * 1e-3
         flops = 2.0 * n_att * G * (kv.d_k + kv.d_v)
         rec["roofline_attention"] = roofline("latent attention (sparsekv_gather_attend: "

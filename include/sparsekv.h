@@ -229,7 +229,17 @@ skv_status sparsekv_select_attend(const skv_kv* kv, const void* q, int32_t G, sk
  * schedule the score scan separately: after sparsekv_score_hist(kv, q, G, win,
  * scores, ws, ...) on the same ws, the exact top-k, gather + attention and
  * split merge (same arguments and results as sparsekv_select_attend; scores
- * is read, not written). */
+ * is read, not written).
+ * Also the indexer + shared-latent step (ECHO-OSDI26 wiki page, problem and
+ * motivation: an indexer scores every key, attention runs over its top-k of
+ * a latent KV): kv a latent KV (v == NULL, bf16, d_k = 576, d_v = 512,
+ * G in {16, 32, 64, 128}) and the scores and ws left by sparsekv_score_hist
+ * of the indexer's own KV, which must have the same B, H and L_max.  Rows
+ * longer than 32768 slots with k <= 4096 finish the exact top-k inside the
+ * attention kernel after one listing pass (every attending workgroup
+ * resolves its row's selection from the list); others take the top-k first.
+ * ws: sparsekv_workspace_size(SKV_OP_SELECT_ATTEND, kv, G, k, NULL) bytes
+ * (for the latent KV), and at least the scoring call's size. */
 skv_status sparsekv_select_attend_resume(const skv_kv* kv, const void* q, int32_t G,
                                          skv_window win, int32_t k, float scale,
                                          const float* scores, int32_t* idx, int32_t* count,

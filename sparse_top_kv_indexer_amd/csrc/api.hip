@@ -237,11 +237,27 @@ skv_status sparsekv_select_attend_resume(const skv_kv* kv, const void* q, int32_
   if (!kv_ok(kv) || !q || !scores || !idx || !count || !out || G < 1 || k < 1) return SKV_EINVAL;
   if (k > kv->L_max || !win.lo || !win.hi || !isfinite(scale)) return SKV_EINVAL;
   const KvArgs a = to_args(kv);
+  const int rows = kv->B * kv->H;
+  const size_t th = topk_workspace_bytes(rows, kv->L_max);
+  float* part = (float*)((char*)ws + th);
+  if (kv->v == nullptr) {
+    // latent KV: rows longer than one sweep finish the top-k inside the
+    // attention kernel; shorter ones take the one-workgroup top-k first
+    if (!mla_supported(a, G) || !topk_supported(kv->L_max)) return SKV_EUNSUPPORTED;
+    if (!ws || ws_bytes < th + mla_select_attend_partial_bytes(a, G, k)) return SKV_EWORKSPACE;
+    if (mla_list_supported(a, G, k))
+      return launched(launch_mla_list_attend(a, q, G, scores, win.lo, win.hi, k, ws, scale, idx,
+                                             count, part, out, stream));
+    const hipError_t e = launch_topk(scores, rows, kv->H, kv->L_max, win.lo, win.hi, k, idx, count,
+                                     ws, true, stream);
+    if (e != hipSuccess) return launched(e);
+    return launched(launch_mla_attend(a, q, G, idx, k, win.lo, win.hi, scale, out, part,
+                                      ws_bytes - th, stream));
+  }
   if (!score_supported(kv, G) || !select_attend_supported(a, G)) return SKV_EUNSUPPORTED;
-  const size_t th = topk_workspace_bytes(kv->B * kv->H, kv->L_max);
   if (!ws || ws_bytes < th + select_attend_partial_bytes(a, G)) return SKV_EWORKSPACE;
   return launched(launch_select_attend(a, q, G, scores, win.lo, win.hi, k, (uint32_t*)ws, scale,
-                                       idx, count, (float*)((char*)ws + th), out, stream));
+                                       idx, count, part, out, stream));
 }
 
 size_t sparsekv_select_attend_noalloc_bytes(const skv_kv* kv, int32_t G) {
@@ -329,7 +345,8 @@ size_t sparsekv_workspace_size(skv_op op, const skv_kv* kv, int32_t G, int32_t k
     case SKV_OP_SELECT_ATTEND:
       if (!kv_ok(kv) || G < 1 || k < 0) return 0;
       return topk_workspace_bytes(kv->B * kv->H, kv->L_max) +
-             select_attend_partial_bytes(to_args(kv), G);
+             (kv->v == nullptr ? mla_select_attend_partial_bytes(to_args(kv), G, k)
+                               : select_attend_partial_bytes(to_args(kv), G));
     case SKV_OP_BLOCK_SELECT:
       if (!kv_ok(kv) || G < 1) return 0;
       return block_select_ws_bytes(to_args(kv), G);

@@ -18,6 +18,7 @@
 // rows and waves are merged by log-sum-exp at the end and written as one
 // partial per split; attend_reduce_kernel merges the splits exactly.
 #include "skv_device.h"
+#include "skv_topk.h"
 
 namespace skv {
 
@@ -403,19 +404,23 @@ __global__ __launch_bounds__(kThreads) void attend_mfma_kernel(
 // from 16 splits at a time, the first 16 in flight while the split weights
 // are formed (n_split <= 64, D <= 512).
 // With zero_hist != nullptr, the workgroup of the first query head of each KV
-// head also zeroes that row's 4096-bin key histogram (the fused select +
-// attend path leaves it for this kernel, which runs after every reader).
+// head also zeroes that row's copies of the 4096-bin key histogram and, with
+// ctr != nullptr, the row's list counter (ctr[row * kCtrStride]): the fused
+// top-k + attention paths leave them for this kernel, which runs after every
+// reader.
 __global__ __launch_bounds__(256) void attend_reduce_kernel(const float* part, int n_split, int D,
                                                            int HG, float* out, uint32_t* zero_hist,
-                                                           int G) {
+                                                           int G, int copies, int32_t* ctr) {
   constexpr int SG = 16;                 // splits whose values are loaded together
   constexpr int ND = 2;                  // dims per thread (D <= 512)
   __shared__ float wts[64];
   __shared__ float inv_l;
   const int hq = blockIdx.x, b = blockIdx.y;
   if (zero_hist && hq % G == 0) {
-    uint4* z = (uint4*)(zero_hist + ((int64_t)b * (HG / G) + hq / G) * 4096);
-    for (int i = threadIdx.x; i < 1024; i += blockDim.x) z[i] = make_uint4(0u, 0u, 0u, 0u);
+    const int64_t row = (int64_t)b * (HG / G) + hq / G;
+    uint4* z = (uint4*)(zero_hist + row * copies * 4096);
+    for (int i = threadIdx.x; i < 1024 * copies; i += blockDim.x) z[i] = make_uint4(0u, 0u, 0u, 0u);
+    if (ctr && threadIdx.x == 0) ctr[row * kCtrStride] = 0;
   }
   const int stride = D + 2;
   const float* base = part + ((int64_t)b * HG + hq) * n_split * stride;
@@ -534,10 +539,11 @@ hipError_t launch_gather_attend(const KvArgs& kv, const void* q, int G, const in
 }
 
 hipError_t launch_attend_reduce(const float* part, int n_split, int D, int HG, int B, float* out,
-                                hipStream_t st, uint32_t* zero_hist, int G) {
+                                hipStream_t st, uint32_t* zero_hist, int G, int copies,
+                                int32_t* ctr) {
   if (n_split > 64 || D > 512) return hipErrorInvalidValue;
   dim3 grid(HG, B);
-  attend_reduce_kernel<<<grid, 256, 0, st>>>(part, n_split, D, HG, out, zero_hist, G);
+  attend_reduce_kernel<<<grid, 256, 0, st>>>(part, n_split, D, HG, out, zero_hist, G, copies, ctr);
   return hipGetLastError();
 }
 

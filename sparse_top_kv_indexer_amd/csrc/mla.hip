@@ -32,6 +32,7 @@
 #include <algorithm>
 
 #include "skv_device.h"
+#include "skv_listsel.h"
 
 namespace skv {
 
@@ -228,6 +229,230 @@ __global__ __launch_bounds__(WAVES * 64) void mla_split_kernel(
 // splits: a multiple of 8 (see the head-group placement), ~64 rows each
 int mla_splits(int k) { return std::max(8, std::min(64, (k + 63) / 64 + 7) / 8 * 8); }
 
+// ------------------------------------------ selection fused with attention --
+// After the slice listing of a long row (the exact top-k's list in the top-k
+// workspace), one kernel finishes the selection and attends: grid (n_split,
+// rows x head parts), 1024 threads.  Every workgroup of a row resolves the
+// row's exact selection from the list by itself (list_select; the row alone
+// when the list overflowed), so no workgroup waits for another; split s takes
+// the selected keys of ranks [s n_sel / n_split, (s + 1) n_sel / n_split) and
+// an equal share of the always-attended tokens (t < lo, t >= hi), stages their
+// latent rows in LDS 64 at a time with the load unit, and attends for its
+// 16 (kRowWaves / DP) query heads, whose rows it also stages in LDS.  The 16
+// waves are 16-head groups x DP parts of the value dims.  Per 32 staged tokens
+// the first wave of a head group forms the logits (2 x 18
+// v_mfma_f32_16x16x32_bf16), updates the online softmax and leaves the
+// probability fragments (bf16 head + tail, the A operand of the value product)
+// and the rescale factors in LDS; after one barrier every wave of the group
+// applies them to its 32 / DP column blocks of 16 value dims.  Per-wave state
+// stays small (the accumulators of 512 / DP dims), which 1024-thread
+// workgroups need.  Split 0 of head part 0 writes idx and count.  The rows'
+// histograms and list counters are zeroed by the merge kernel that follows.
+constexpr int kFuseRows = 64;          // latent rows staged at a time
+constexpr int kFuseSlices = 1024;      // listing slices of a row this kernel reads
+
+// The row's selection when its list overflowed: the row alone, re-read per
+// digit (rare; kept out of line so its registers do not weigh on the
+// attention).
+__device__ __noinline__ int fallback_select(const float* scores, int row, int H, int L_max,
+                                           const int32_t* lo_p, const int32_t* hi_p, int k,
+                                           uint32_t* ghist_row, RowSelLds& L, int& klist_n,
+                                           uint4 gv) {
+  return row_select_alone<false, 3>(scores, row, H, L_max, lo_p, hi_p, k, ghist_row, true, nullptr,
+                                    nullptr, nullptr, nullptr, 0, L, nullptr, klist_n, nullptr,
+                                    true, gv);
+}
+
+template <int DP>
+__global__ __launch_bounds__(kRowThreads) void mla_list_kernel(
+    KvArgs kv, const uint16_t* q, int G, const float* scores, const int32_t* lo_p,
+    const int32_t* hi_p, int k, TopkWs ws, int n_slices, float scale_log2, int n_split,
+    int32_t* idx, int32_t* count, float* part) {
+  constexpr int VB = kVB / DP;                      // value column blocks per wave
+  constexpr int NHG = kRowWaves / DP;               // 16-head groups per workgroup
+  constexpr int kHeadsPerWg = 16 * NHG;
+  __shared__ RowSelLds L;
+  __shared__ int s_off[kFuseSlices + 1], s_at[kFuseSlices];
+  __shared__ int klist_n;
+  __shared__ __attribute__((aligned(16))) uint16_t rows[kFuseRows * kRowPad];
+  __shared__ __attribute__((aligned(16))) uint16_t qs[kHeadsPerWg * kRowPad];
+  __shared__ u32x4_t pfrag[NHG][2][64][2];          // [group][chunk parity][lane][head, tail]
+  __shared__ float cfac[NHG][2][16];                // rescale factor per head
+  __shared__ int64_t roff[kFuseRows];
+  const int n_hp = (G + kHeadsPerWg - 1) / kHeadsPerWg;   // head parts per row
+  const int s = blockIdx.x, row = blockIdx.y / n_hp, hp = blockIdx.y - row * n_hp;
+  const int b = row / kv.H, h = row - b * kv.H;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = row_wave();
+  const int n = lane & 15, g4 = lane >> 4;
+  const int hg = wave / DP, dp = wave - hg * DP;
+  const int head0 = hp * kHeadsPerWg + hg * 16;
+  const bool on = head0 < G;                        // a group past the heads only helps stage
+  const uint16_t* qhead = q + ((int64_t)b * kv.H + h) * G * kDk;   // a finite stand-in row
+
+  // this workgroup's query rows, staged by the load unit while the selection
+  // runs (finite stand-ins past G; no registers involved)
+  for (int r = wave; r < kHeadsPerWg; r += kRowWaves) {
+    const int hd = hp * kHeadsPerWg + r;
+    row_to_lds(qhead + (int64_t)(hd < G ? hd : 0) * kDk, qs + r * kRowPad, lane);
+  }
+
+  // 1. the row's exact selection, positions ascending in L.hist[0 .. n_sel)
+  const uint4 gv = hist_bins_summed(ws, row);
+  int n_sel;
+  if (ws.meta[2 * row + 1] < 0) {
+    n_sel = fallback_select(scores, row, kv.H, kv.L_max, lo_p, hi_p, k,
+                            ws.hist + (int64_t)row * ws.copies * kBins, L, klist_n, gv);
+  } else {
+    n_sel = list_select(ws, row, k, n_slices, gv, L, s_off, s_at,
+                        [&](int dst, int p) { L.hist[dst] = (uint32_t)p; });
+    lds_barrier();
+  }
+  if (s == 0 && hp == 0) {
+    int32_t* orow = idx + (int64_t)row * k;
+    for (int i = tid; i < k; i += kRowThreads) orow[i] = i < n_sel ? (int)L.hist[i] : -1;
+    if (tid == 0) count[row] = n_sel;
+  }
+  // 2. this split's share: selected ranks [r0, r1), always-attended [x0, x1)
+  const int seq = min(kv.seq_len[b], kv.L_max);
+  const int lo = max(0, min(lo_p[b], seq));
+  const int hi = max(lo, min(hi_p[b], seq));
+  const int n_extra = lo + (seq - hi);
+  const int r0 = (int)((int64_t)n_sel * s / n_split), r1 = (int)((int64_t)n_sel * (s + 1) / n_split);
+  const int x0 = (int)((int64_t)n_extra * s / n_split);
+  const int x1 = (int)((int64_t)n_extra * (s + 1) / n_split);
+  const int n_list = r1 - r0, n_att = n_list + (x1 - x0);
+  const uint16_t* kb = (const uint16_t*)kv.k;
+
+  float m_run = -INFINITY, l_run = 0.f;   // first wave of a group: head head0 + n
+  f32x4_t O[VB];
+#pragma unroll
+  for (int c = 0; c < VB; ++c) O[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  int parity = 0;
+  const uint16_t* qrow = qs + (hg * 16 + n) * kRowPad;
+
+  for (int q0 = 0; q0 < n_att; q0 += kFuseRows) {
+    const int cnt = min(kFuseRows, n_att - q0);
+    const int n_rows = (cnt + 31) & ~31;
+    if (tid < kFuseRows) {
+      int64_t ro = -1;
+      if (tid < cnt) {
+        const int i = q0 + tid;
+        int t;
+        if (i < n_list) {
+          t = (int)L.hist[r0 + i];
+        } else {
+          const int x = x0 + (i - n_list);
+          t = x < lo ? x : hi + (x - lo);
+        }
+        const int64_t slot = slot_of(kv, b, t);
+        ro = slot >= 0 ? row_elem(kv, b, h, slot, kDk) : -1;
+      }
+      roff[tid] = ro;
+    }
+    __syncthreads();   // also: every wave is done with the previous block's rows
+    for (int r = wave; r < n_rows; r += kRowWaves) {
+      const int64_t ro = roff[r];
+      row_to_lds(ro >= 0 ? kb + ro : qhead, rows + r * kRowPad, lane);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();   // the staged latent rows (and, the first time, the query rows)
+    for (int c0 = 0; c0 < cnt; c0 += 32) {
+      if (on && dp == 0) {
+        // S^T[token 16 hf + 4 g4 + i][head n] for the two 16-token halves
+        f32x4_t S[2];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          S[hf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int j = 0; j < kNC; ++j) {
+            const bf16x8_t Kf = __builtin_bit_cast(
+                bf16x8_t,
+                *(const u32x4_t*)(rows + (c0 + 16 * hf + n) * kRowPad + 8 * (4 * j + g4)));
+            const bf16x8_t Qf =
+                __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(qrow + 8 * (4 * j + g4)));
+            S[hf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Kf, Qf, S[hf], 0, 0, 0);
+          }
+        }
+        float z[8];
+        float cm = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int tk = c0 + 16 * (e >> 2) + 4 * g4 + (e & 3);
+          const bool ok = tk < cnt && roff[tk] >= 0;
+          z[e] = ok ? S[e >> 2][e & 3] * scale_log2 : -INFINITY;
+          cm = fmaxf(cm, z[e]);
+        }
+        cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
+        cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
+        const float m_new = fmaxf(m_run, cm);
+        float p[8], ps = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          p[e] = m_new == -INFINITY ? 0.f : exp2f(z[e] - m_new);
+          ps += p[e];
+        }
+        ps += __shfl_xor(ps, 16, 64);
+        ps += __shfl_xor(ps, 32, 64);
+        const float corr = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
+        l_run = l_run * corr + ps;
+        m_run = m_new;
+        uint32_t ph[4], pl[4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const uint32_t h0 = f32_to_bf16_rne(p[e]), h1 = f32_to_bf16_rne(p[e + 1]);
+          const uint32_t l0 = f32_to_bf16_rne(p[e] - __uint_as_float(h0 << 16));
+          const uint32_t l1 = f32_to_bf16_rne(p[e + 1] - __uint_as_float(h1 << 16));
+          ph[e >> 1] = h0 | (h1 << 16);
+          pl[e >> 1] = l0 | (l1 << 16);
+        }
+        pfrag[hg][parity][lane][0] = u32x4_t{ph[0], ph[1], ph[2], ph[3]};
+        pfrag[hg][parity][lane][1] = u32x4_t{pl[0], pl[1], pl[2], pl[3]};
+        if (g4 == 0) cfac[hg][parity][n] = corr;
+      }
+      lds_barrier();   // the group's probabilities and rescale factors
+      if (on) {
+        float oc[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) oc[i] = cfac[hg][parity][4 * g4 + i];
+        const bf16x8_t Ph = __builtin_bit_cast(bf16x8_t, pfrag[hg][parity][lane][0]);
+        const bf16x8_t Pl = __builtin_bit_cast(bf16x8_t, pfrag[hg][parity][lane][1]);
+        const uint16_t* v0 =
+            rows + (c0 + 4 * g4 + (n >> 2)) * kRowPad + 4 * (n & 3) + 16 * VB * dp;
+        const uint16_t* v1 = v0 + 16 * kRowPad;
+#pragma unroll
+        for (int c = 0; c < VB; ++c) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) O[c][i] *= oc[i];
+          const u32x2_t a = value_tr(v0 + 16 * c), bb = value_tr(v1 + 16 * c);
+          const bf16x8_t Vf = __builtin_bit_cast(bf16x8_t, u32x4_t{a[0], a[1], bb[0], bb[1]});
+          O[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ph, Vf, O[c], 0, 0, 0);
+          O[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Pl, Vf, O[c], 0, 0, 0);
+        }
+      }
+      parity ^= 1;   // the next chunk writes the other buffer; a barrier lies between
+    }
+  }
+
+  // 3. the split partial: O[head][512], max, sum (lane holds heads 4 g4 + i)
+  if (!on) return;
+  const int stride = kDv + 2;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int hd = head0 + 4 * g4 + i;
+    float* dst = part + (((int64_t)row * G + hd) * n_split + s) * stride + 16 * VB * dp;
+#pragma unroll
+    for (int c = 0; c < VB; ++c) dst[16 * c + n] = O[c][i];
+  }
+  if (dp == 0 && g4 == 0) {
+    float* dst = part + (((int64_t)row * G + head0 + n) * n_split + s) * stride;
+    dst[kDv] = m_run;
+    dst[kDv + 1] = l_run;
+  }
+}
+
+constexpr int kFuseSplits = 32;        // splits of the fused selection + attention
+
 }  // namespace
 
 bool mla_supported(const KvArgs& kv, int G) {
@@ -237,6 +462,50 @@ bool mla_supported(const KvArgs& kv, int G) {
 
 size_t mla_workspace_bytes(const KvArgs& kv, int G, int k) {
   return (size_t)kv.B * kv.H * G * mla_splits(k) * (kDv + 2) * sizeof(float);
+}
+
+// The exact top-k of long rows (more than one 32768-slot sweep) finished
+// from the slice listing inside the attention kernel: G in {16, 32, 64, 128},
+// k <= 4096, at most kFuseSlices listing slices per row.
+bool mla_list_supported(const KvArgs& kv, int G, int k) {
+  return mla_supported(kv, G) && k >= 1 && k <= kBins && row_slots_max(kv.L_max) > kSweep &&
+         topk_slices(kv.L_max) <= kFuseSlices;
+}
+
+size_t mla_list_partial_bytes(const KvArgs& kv, int G) {
+  return (size_t)kv.B * kv.H * G * kFuseSplits * (kDv + 2) * sizeof(float);
+}
+
+size_t mla_select_attend_partial_bytes(const KvArgs& kv, int G, int k) {
+  return std::max(mla_list_partial_bytes(kv, G), mla_workspace_bytes(kv, G, k));
+}
+
+hipError_t launch_mla_list_attend(const KvArgs& kv, const void* q, int G, const float* scores,
+                                  const int32_t* lo, const int32_t* hi, int k, void* topk_ws,
+                                  float scale, int32_t* idx, int32_t* count, float* part,
+                                  float* out, hipStream_t st) {
+  const int rows = kv.B * kv.H;
+  const TopkWs ws = TopkWs::carve(topk_ws, rows, kv.L_max);
+  hipError_t e = launch_topk_listing(scores, rows, kv.H, kv.L_max, lo, hi, k, topk_ws, st);
+  if (e != hipSuccess) return e;
+  const int ns = topk_listing_slices(rows, kv.L_max);
+  if (ns > kFuseSlices) return hipErrorInvalidValue;
+  const float scale_log2 = scale * 1.4426950408889634f;
+  const uint16_t* qq = (const uint16_t*)q;
+  // 32 heads per workgroup (2 head groups x 8 dim parts); 16 heads take 16
+  const int dp = G >= 32 ? 8 : 16;
+  const int n_hp = (G + 16 * (kRowWaves / dp) - 1) / (16 * (kRowWaves / dp));
+  const dim3 grid(kFuseSplits, rows * n_hp);
+  if (dp == 8)
+    mla_list_kernel<8><<<grid, kRowThreads, 0, st>>>(kv, qq, G, scores, lo, hi, k, ws, ns, scale_log2,
+                                                     kFuseSplits, idx, count, part);
+  else
+    mla_list_kernel<16><<<grid, kRowThreads, 0, st>>>(kv, qq, G, scores, lo, hi, k, ws, ns,
+                                                      scale_log2, kFuseSplits, idx, count, part);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_attend_reduce(part, kFuseSplits, kDv, kv.H * G, kv.B, out, st, ws.hist, G,
+                              ws.copies, ws.ctr);
 }
 
 hipError_t launch_mla_attend(const KvArgs& kv, const void* q, int G, const int32_t* idx, int k,

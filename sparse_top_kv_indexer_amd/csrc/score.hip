@@ -42,7 +42,7 @@ constexpr int kTile = 256;  // tokens per workgroup (multiple of 16)
 struct HistArgs {
   const int32_t* lo;
   const int32_t* hi;
-  uint32_t* hist;   // [B*H][4096]
+  uint32_t* hist;   // [B*H][copies][4096]
   // survivors (threshold prefilter): keys of the window with score >= thr[row]
   // go to the row's list [row][cap] through the fill counter ctr[row * kCtrStride]
   const float* thr;
@@ -50,7 +50,13 @@ struct HistArgs {
   int32_t* lpos;
   int32_t* ctr;
   int cap;
+  int copies;       // histogram copies per row (topk_hist_copies)
 };
+
+// The copy of row r's histogram that this workgroup adds into.
+__device__ __forceinline__ uint32_t* hist_copy(const HistArgs& ha, int64_t r) {
+  return ha.hist + (r * ha.copies + (int)(blockIdx.x % (unsigned)ha.copies)) * 4096;
+}
 
 // Survivor staging per workgroup and row segment; a segment with more is
 // reported to the consumer as an overflow (its row then takes the full top-k).
@@ -177,7 +183,7 @@ __global__ __launch_bounds__(kThreads) void score_valu_kernel(KvArgs kv, const v
       }
     }
   }
-  if constexpr (HIST) hist_flush(lh, ha.hist + ((int64_t)b * kv.H + h) * 4096);
+  if constexpr (HIST) hist_flush(lh, hist_copy(ha, (int64_t)b * kv.H + h));
 }
 
 // Persistent pipelined scan (bf16, 2 <= G <= 16, d_k = 32 * NC).  The work is
@@ -390,7 +396,7 @@ __global__ __launch_bounds__(kThreads) void score_stream_kernel(KvArgs kv, const
       for (int s = 0; s < D; ++s)
         if (s < n_w) finish(mfma(s), s);
     }
-    if constexpr (HIST) hist_flush(lh, ha.hist + (int64_t)r * 4096);
+    if constexpr (HIST) hist_flush(lh, hist_copy(ha, r));
     if constexpr (SURV) {
       lds_barrier();
       const int nsv = sv_n;
@@ -465,7 +471,8 @@ hipError_t launch_stream_k(const KvArgs& kv, const void* q, int G, float* scores
   // each workgroup flushes its histogram of a row with one atomic per bin it
   // holds; few long rows spread over every resident workgroup would make
   // hundreds of them contend for the same bins, so a row gets at most 256
-  if (MODE == 1) w = std::min<int64_t>(w, (int64_t)kv.B * kv.H * 256);
+  // workgroups per histogram copy
+  if (MODE == 1) w = std::min<int64_t>(w, (int64_t)kv.B * kv.H * 256 * ha.copies);
   w = std::max<int64_t>(std::max<int64_t>(w, (n_work + cap - 1) / cap), 1);
   if (w > 0x7fffffff) return hipErrorInvalidValue;
   kern<<<dim3((unsigned)w), kThreads, 0, s>>>(kv, (const uint16_t*)q, G, scores, ha, cpr);
@@ -499,6 +506,7 @@ hipError_t launch_score(const KvArgs& kv, const void* q, int G, float* scores, c
                         const int32_t* hi, uint32_t* hist, hipStream_t s) {
   dim3 grid((kv.L_max + kTile - 1) / kTile, kv.H, kv.B);
   HistArgs ha{lo, hi, hist};
+  ha.copies = topk_hist_copies(kv.B * kv.H, kv.L_max);
   if (kv.bf16 && G >= 1 && G <= 16 && kv.d_k % 32 == 0 && (G >= 2 || kv.d_k <= 256)) {
     switch (kv.d_k / 32) {
       case 2: return launch_stream<2, 4>(kv, q, G, scores, ha, s);
@@ -531,7 +539,7 @@ hipError_t launch_score_prefilter(const KvArgs& kv, const void* q, int G, float*
                                   const int32_t* lo, const int32_t* hi, const float* thr,
                                   uint32_t* lkey, int32_t* lpos, int32_t* ctr, int cap,
                                   hipStream_t s) {
-  HistArgs ha{lo, hi, nullptr, thr, lkey, lpos, ctr, cap};
+  HistArgs ha{lo, hi, nullptr, thr, lkey, lpos, ctr, cap, 1};
   switch (kv.d_k / 32) {
     case 2: return launch_stream<2, 4>(kv, q, G, scores, ha, s);
     case 4: return launch_stream<4, 4>(kv, q, G, scores, ha, s);

@@ -63,6 +63,13 @@ hipError_t launch_topk(const float* scores, int rows, int H, int L_max, const in
                        bool hist_ready, hipStream_t s, const int32_t* map_a = nullptr,
                        const int32_t* map_b = nullptr, int map_ld = 0);
 
+// topk.hip: the slice listing of rows longer than one sweep alone (after a
+// scan that left the histograms in ws), for kernels that finish the
+// selection themselves; topk_listing_slices = the slices per row it uses
+int topk_listing_slices(int rows, int L_max);
+hipError_t launch_topk_listing(const float* scores, int rows, int H, int L_max, const int32_t* lo,
+                               const int32_t* hi, int k, void* ws, hipStream_t s);
+
 // attend.hip
 int attend_num_splits(int k);
 size_t attend_workspace_bytes(const KvArgs& kv, int G, int k);
@@ -71,9 +78,11 @@ hipError_t launch_gather_attend(const KvArgs& kv, const void* q, int G, const in
                                 void* ws, size_t ws_bytes, hipStream_t s);
 bool attend_supported(const KvArgs& kv, int G);
 // merge of split partials [B][HG][n_split][D + 2] (acc[D], max, sum; log2
-// domain) into out [B][HG][D]
+// domain) into out [B][HG][D]; with zero_hist, also zeroes each row's
+// `copies` top-k histograms and (ctr != nullptr) its list counter
 hipError_t launch_attend_reduce(const float* part, int n_split, int D, int HG, int B, float* out,
-                                hipStream_t s, uint32_t* zero_hist = nullptr, int G = 1);
+                                hipStream_t s, uint32_t* zero_hist = nullptr, int G = 1,
+                                int copies = 1, int32_t* ctr = nullptr);
 
 // select_attend.hip: exact top-k fused with gather + split attention (after
 // launch_score with a histogram); bf16, d = 128, G <= 8, L_max <= 32768
@@ -90,5 +99,18 @@ size_t mla_workspace_bytes(const KvArgs& kv, int G, int k);
 hipError_t launch_mla_attend(const KvArgs& kv, const void* q, int G, const int32_t* idx, int k,
                              const int32_t* lo, const int32_t* hi, float scale, float* out,
                              void* ws, size_t ws_bytes, hipStream_t s);
+// mla.hip: after a scan that left the rows' histograms in the top-k workspace
+// topk_ws, the slice listing, then the exact top-k finished inside the latent
+// attention kernel (idx, count written), then the merge (rows longer than one
+// sweep, k <= 4096); part: mla_list_partial_bytes
+bool mla_list_supported(const KvArgs& kv, int G, int k);
+size_t mla_list_partial_bytes(const KvArgs& kv, int G);
+// split partials the latent path of sparsekv_select_attend_resume needs
+// (fused or not, whichever is larger)
+size_t mla_select_attend_partial_bytes(const KvArgs& kv, int G, int k);
+hipError_t launch_mla_list_attend(const KvArgs& kv, const void* q, int G, const float* scores,
+                                  const int32_t* lo, const int32_t* hi, int k, void* topk_ws,
+                                  float scale, int32_t* idx, int32_t* count, float* part,
+                                  float* out, hipStream_t s);
 
 }  // namespace skv

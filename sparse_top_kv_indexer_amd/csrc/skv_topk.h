@@ -40,6 +40,19 @@ inline int topk_slice_groups(int rows, int L_max) {
   return ng;
 }
 
+// Copies of a row's first-digit histogram.  A few long rows are scanned by
+// hundreds of workgroups each, and their once-per-workgroup flushes of the
+// histogram queue behind each other on the row's bins (device atomics on few
+// addresses are slow); with several copies, workgroup w adds into copy
+// w % copies -- the copy of its XCD, as workgroups go to the 8 XCDs
+// round-robin -- and every reader sums the copies.  Producer and consumers
+// derive the count from (rows, L_max) alone.
+constexpr int kHistCopiesMax = 8;
+__host__ __device__ inline int topk_hist_copies(int rows, int L_max) {
+  const int64_t slots = L_max % 4 == 0 ? (int64_t)L_max : (int64_t)L_max + 3;
+  return (rows <= 4 && slots > 32768) ? kHistCopiesMax : 1;
+}
+
 // Slice entries a row's workspace holds: the most any call may use.
 __host__ __device__ inline int topk_slices(int L_max) {
   int ng = 1;
@@ -48,26 +61,29 @@ __host__ __device__ inline int topk_slices(int L_max) {
 }
 
 struct TopkWs {
-  uint32_t* hist;   // [rows][4096]
+  uint32_t* hist;   // [rows][copies][4096]
   int32_t* ctr;     // [rows][kCtrStride] keys listed so far (element 0 of each line)
   int32_t* meta;    // [rows][2]: smallest listed key, listed count (-1: too many)
   int32_t* slc;     // [rows][slices][2]: list offset and count of each slice
   uint32_t* lkey;   // [rows][kRowList] listed keys, slice by slice in position order
   int32_t* lpos;    // [rows][kRowList] their positions
+  int copies;       // histogram copies per row (topk_hist_copies)
 
   static size_t align(size_t x) { return (x + 255) & ~(size_t)255; }
-  static size_t zero_bytes(int rows) {
-    return align((size_t)rows * 4096 * 4) + align((size_t)rows * kCtrStride * 4);
+  static size_t zero_bytes(int rows, int L_max) {
+    return align((size_t)rows * topk_hist_copies(rows, L_max) * 4096 * 4) +
+           align((size_t)rows * kCtrStride * 4);
   }
   static size_t bytes(int rows, int L_max) {
-    return zero_bytes(rows) + align((size_t)rows * 8) +
+    return zero_bytes(rows, L_max) + align((size_t)rows * 8) +
            align((size_t)rows * topk_slices(L_max) * 8) + 2 * align((size_t)rows * kRowList * 4);
   }
   static TopkWs carve(void* p, int rows, int L_max) {
     TopkWs w;
     char* c = (char*)p;
+    w.copies = topk_hist_copies(rows, L_max);
     w.hist = (uint32_t*)c;
-    c += align((size_t)rows * 4096 * 4);
+    c += align((size_t)rows * w.copies * 4096 * 4);
     w.ctr = (int32_t*)c;
     c += align((size_t)rows * kCtrStride * 4);
     w.meta = (int32_t*)c;

@@ -40,6 +40,7 @@
 // zero-filled workspace stays valid across calls.
 #include <type_traits>
 
+#include "skv_listsel.h"
 #include "skv_rowsel.h"
 #include "skv_topk.h"
 
@@ -49,7 +50,6 @@ namespace {
 
 constexpr int kSliceThreads = 256;           // 4 waves x 256 NG slots = kSliceUnit NG
 static_assert(kSliceThreads * 4 == kSliceUnit, "slice layout");
-constexpr int kListCap = 16384;              // fallback: LDS list of the threshold bin's keys
 
 // Window of row `row`, its read base and this lane's first slot in slice sl
 // of NG groups per lane (slots sl * kSliceUnit NG + wave * 256 NG + 256 g +
@@ -76,7 +76,8 @@ __device__ __forceinline__ SliceView slice_view(const float* scores, int row, in
 __global__ __launch_bounds__(kSliceThreads) void topk_hist_kernel(const float* scores, int H,
                                                                   int L_max, const int32_t* lo_p,
                                                                   const int32_t* hi_p,
-                                                                  uint32_t* ghist, int n_slices) {
+                                                                  uint32_t* ghist, int n_slices,
+                                                                  int copies) {
   __shared__ uint32_t lh[kBins];
   const int row = blockIdx.x / n_slices, sl = blockIdx.x - row * n_slices;
   const SliceView v = slice_view<kGroups>(scores, row, H, L_max, lo_p, hi_p, sl);
@@ -95,7 +96,7 @@ __global__ __launch_bounds__(kSliceThreads) void topk_hist_kernel(const float* s
       if (key) atomicAdd(&lh[key >> 20], 1u);
     }
   lds_barrier();
-  uint32_t* gh = ghist + (int64_t)row * kBins;
+  uint32_t* gh = ghist + ((int64_t)row * copies + sl % copies) * kBins;
   for (int i = threadIdx.x; i < kBins; i += kSliceThreads) {
     const uint32_t c = lh[i];
     if (c) atomicAdd(&gh[i], c);
@@ -118,15 +119,27 @@ __global__ __launch_bounds__(kSliceThreads) void topk_compact_kernel(
   if (any) slots_load(v.s, v.w, v.vec, v.p0, f);
 
   // the bin of the k-th largest key: thread t holds bins 16 t .. 16 t + 15
-  const uint4* gh = (const uint4*)(ws.hist + (int64_t)row * kBins) + 4 * threadIdx.x;
+  // (summed over the row's histogram copies)
   int c[16];
+  {
+    const uint4* gh = (const uint4*)(ws.hist + (int64_t)row * ws.copies * kBins) + 4 * threadIdx.x;
+    uint4 x[kHistCopiesMax][4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const uint4 x = gh[u];
-    c[4 * u] = (int)x.x;
-    c[4 * u + 1] = (int)x.y;
-    c[4 * u + 2] = (int)x.z;
-    c[4 * u + 3] = (int)x.w;
+    for (int cp = 0; cp < kHistCopiesMax; ++cp)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        x[cp][u] = cp < ws.copies ? gh[cp * (kBins / 4) + u] : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      c[4 * u] = c[4 * u + 1] = c[4 * u + 2] = c[4 * u + 3] = 0;
+#pragma unroll
+      for (int cp = 0; cp < kHistCopiesMax; ++cp) {
+        c[4 * u] += (int)x[cp][u].x;
+        c[4 * u + 1] += (int)x[cp][u].y;
+        c[4 * u + 2] += (int)x[cp][u].z;
+        c[4 * u + 3] += (int)x[cp][u].w;
+      }
+    }
   }
   int tsum = 0;
 #pragma unroll
@@ -231,24 +244,6 @@ __global__ __launch_bounds__(kSliceThreads) void topk_compact_kernel(
 }
 
 // ------------------------------------------------------------ finishing --
-// The score whose order-preserving key is `key`.
-__device__ __forceinline__ float key_score(uint32_t key) {
-  return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
-}
-
-// Minimum of v over the 1024-thread workgroup (two barriers; red: 16 words).
-__device__ __forceinline__ uint32_t block_min_u32(uint32_t v, uint32_t* red) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o, 64));
-  lds_barrier();   // earlier readers of red are done
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  lds_barrier();
-  uint32_t m = 0xffffffffu;
-#pragma unroll
-  for (int i = 0; i < kRowWaves; ++i) m = min(m, red[i]);
-  return m;
-}
-
 // pre[w] = set bits of map[0 .. w) for the W <= 4096 words of a position
 // bitmap, 4 words per thread (two barriers).
 __device__ __forceinline__ void bitmap_prefix(const uint32_t* map, int* pre, int W, RowSelLds& L) {
@@ -275,174 +270,6 @@ __device__ __forceinline__ void bitmap_prefix(const uint32_t* map, int* pre, int
       before += c[u];
     }
   lds_barrier();
-}
-// The whole selection of one row by one workgroup, re-reading the row from
-// memory for every pass (rows whose list would overflow).  The threshold
-// bin's keys are compacted into an LDS list when they fit, so the lower
-// digits need no further pass over the row.
-// RES: the row is one sweep, whose keys stay in registers across the passes.
-// MAP: how a selected position p is written: 0 as p; 1 (k <= 4096) as
-// map_b[map_a[row][p]], the positions gathered in LDS first and mapped in one
-// pass; 2 mapped as each key is emitted.  A compile-time choice, so every
-// instantiation has one kind of store in its emission loop.
-template <bool RES, int MAP, int NG = kGroups>
-__device__ __forceinline__ void row_select_alone(const float* scores, int row, int H, int L_max,
-                                 const int32_t* lo_p, const int32_t* hi_p, int k,
-                                 uint32_t* ghist_row, bool hist_ready, int32_t* orow,
-                                 int32_t* count, const int32_t* map_a, const int32_t* map_b,
-                                 int map_ld, RowSelLds& L, uint32_t* klist, int& klist_n,
-                                 uint32_t* min_key = nullptr) {
-  const int lane = threadIdx.x & 63;
-  RowWindow w = row_window(lo_p, hi_p, row / H, L_max);
-  bool vec;
-  const float* s = row_base(scores, (int64_t)row * L_max, w, &vec);
-  const int n_sweeps = RES ? 1 : (w.ns + kSweep - 1) / kSweep;
-  uint4* gh4 = (uint4*)ghist_row;
-  const uint4 gv = hist_ready ? gh4[threadIdx.x] : make_uint4(0u, 0u, 0u, 0u);
-  // RES: the row's scores are loaded now and turned into keys once the
-  // first digit's search (from the scan's histogram) has overlapped their
-  // arrival
-  static_assert(RES || NG == kGroups, "short rows keep their keys in registers");
-  uint32_t kr[RES ? NG : 1][4];
-  float fr[RES ? NG : 1][4];
-  if constexpr (RES) row_load(s, w, vec, 0, fr);
-
-  // F(keys, sweep) for every sweep, the next sweep's loads in flight while
-  // one is processed
-  auto for_sweeps = [&](auto&& F) {
-    if constexpr (RES) {
-      F(kr, 0);
-      return;
-    }
-    float va[kGroups][4], vb[kGroups][4];
-    row_load(s, w, vec, 0, va);
-    for (int sw = 0; sw < n_sweeps; sw += 2) {
-      if (sw + 1 < n_sweeps) row_load(s, w, vec, sw + 1, vb);
-      {
-        uint32_t kk[kGroups][4];
-        row_keys(va, kk);
-        F(kk, sw);
-      }
-      if (sw + 1 < n_sweeps) {
-        if (sw + 2 < n_sweeps) row_load(s, w, vec, sw + 2, va);
-        uint32_t kk[kGroups][4];
-        row_keys(vb, kk);
-        F(kk, sw + 1);
-      }
-    }
-  };
-  bool use_list = false;
-  auto for_keys = [&](auto&& f) {
-    if (use_list) {
-      const int nl = min(klist_n, kListCap);
-      for (int i = threadIdx.x; i < nl; i += kRowThreads) f(klist[i]);
-    } else {
-      for_sweeps([&](const auto& kk, int) {
-        constexpr int ng = sizeof(kk) / sizeof(kk[0]);
-#pragma unroll
-        for (int g = 0; g < ng; ++g)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) f(kk[g][e]);
-      });
-    }
-  };
-  // one pass compacts the keys of bin b0 into klist (a wave prefix sum of
-  // the lanes' match counts places them; one LDS atomic per wave and sweep)
-  auto prepare = [&](int b0, int in_bin) {
-    if (RES || in_bin > kListCap) return;
-    if (threadIdx.x == 0) klist_n = 0;
-    lds_barrier();
-    for_sweeps([&](const auto& kk, int) {
-      constexpr int ng = sizeof(kk) / sizeof(kk[0]);
-      int c = 0;
-#pragma unroll
-      for (int g = 0; g < ng; ++g)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) c += (kk[g][e] >> 20) == (uint32_t)b0;
-      const int incl = wave_incl_scan(c);
-      int base = 0;
-      if (lane == 63) base = atomicAdd(&klist_n, incl);
-      int o = __builtin_amdgcn_readlane(base, 63) + incl - c;
-      if (c) {
-#pragma unroll
-        for (int g = 0; g < ng; ++g)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if ((kk[g][e] >> 20) == (uint32_t)b0) {
-              if (o < kListCap) klist[o] = kk[g][e];
-              ++o;
-            }
-      }
-    });
-    lds_barrier();
-    use_list = true;
-  };
-
-  *(uint4*)(L.hist + 4 * threadIdx.x) = gv;
-  if (threadIdx.x < 256) L.dh[threadIdx.x] = 0u;
-  lds_barrier();
-  if (!hist_ready) {   // the top-12-bit histogram, with LDS atomics
-    if constexpr (RES) row_keys(fr, kr);
-    for_keys([&](uint32_t key) {
-      if (key) atomicAdd(&L.hist[key >> 20], 1u);
-    });
-    lds_barrier();
-  }
-  uint32_t T;
-  int need_eq, k_sel;
-  row_threshold_p(
-      L, k,
-      [&]() {
-        if constexpr (RES) {
-          if (hist_ready) row_keys(fr, kr);
-        }
-      },
-      prepare, for_keys, &T, &need_eq, &k_sel);
-
-  int a_base = 0, e_base = 0;   // keys above / equal to T in earlier sweeps
-  uint32_t mk = 0xffffffffu;    // smallest selected key of this lane
-  for (int sw = 0; sw < n_sweeps; ++sw) {
-    uint32_t kk[NG][4];
-    if constexpr (RES) {
-#pragma unroll
-      for (int g = 0; g < NG; ++g)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) kk[g][e] = kr[g][e];
-    } else {
-      float f[NG][4];
-      row_load(s, w, vec, sw, f);
-      row_keys(f, kk);
-    }
-    int cg[NG];
-    const int lt = row_counts(kk, T, cg);
-    int oa, oe, ta, te;
-    row_wave_offsets(L, lt, &oa, &oe, &ta, &te);
-    const int pos0 = w.lo - w.o + row_slot0<NG>(sw);
-    row_emit(kk, cg, T, need_eq, a_base + oa, e_base + oe, [&](int dst, int g, int e) {
-      if (dst < k) {
-        const int p = pos0 + 256 * g + e;
-        if constexpr (MAP == 0) orow[dst] = p;
-        else if constexpr (MAP == 1) L.hist[dst] = (uint32_t)p;
-        else orow[dst] = map_b[map_a[(int64_t)row * map_ld + p]];
-        mk = min(mk, kk[g][e]);
-      }
-    });
-    a_base += ta;
-    e_base += te;
-  }
-  const int n_sel = min(k, a_base + min(e_base, need_eq));
-  if constexpr (MAP == 1) {
-    lds_barrier();
-    for (int i = threadIdx.x; i < n_sel; i += kRowThreads)
-      orow[i] = map_b[map_a[(int64_t)row * map_ld + (int)L.hist[i]]];
-  }
-  for (int i = n_sel + threadIdx.x; i < k; i += kRowThreads) orow[i] = -1;
-  if (threadIdx.x == 0) count[row] = n_sel;
-  if (hist_ready) gh4[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
-  if (min_key) {
-    const uint32_t m = block_min_u32(mk, (uint32_t*)L.wt);
-    if (threadIdx.x == 0) *min_key = m;
-  }
 }
 
 // Grid rows, 1024 threads: rows of one sweep, each selected by its workgroup
@@ -472,147 +299,35 @@ __global__ __launch_bounds__(kRowThreads) void topk_finish_kernel(
   __shared__ uint32_t klist[kListCap];
   __shared__ int klist_n;
   __shared__ int s_off[kMaxSlices + 1], s_at[kMaxSlices];
-  constexpr int kPer = kRowList / kRowThreads;   // list entries per lane
   const int row = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = row_wave();
   int32_t* orow = idx + (int64_t)row * k;
-  uint32_t* ghist_row = ws.hist + (int64_t)row * kBins;
-  uint4* gh4 = (uint4*)ghist_row;
-  const uint4 gv = gh4[threadIdx.x];   // issued with the loads below, before the branch
-  const int32_t* slc = ws.slc + (int64_t)row * n_slices * 2;
-  const int sl0 = threadIdx.x;
-  const int n0 = sl0 < n_slices ? slc[2 * sl0 + 1] : 0;
-  const int at0 = sl0 < n_slices ? slc[2 * sl0] : 0;
+  uint4* gh4 = (uint4*)(ws.hist + (int64_t)row * ws.copies * kBins);
+  const uint4 gv = hist_bins_summed(ws, row);
   if (ws.meta[2 * row + 1] < 0) {
-    row_select_alone<false, MAP>(scores, row, H, L_max, lo_p, hi_p, k, ghist_row, true, orow, count,
-                            map_a, map_b, map_ld, L, klist, klist_n);
-    return;
-  }
-
-  // 1. the list, slice by slice: s_off = first list rank of each slice (ranks
-  // count every slice's share padded to a multiple of 4, as stored)
-  int run = 0;
-  for (int b0 = 0; b0 < n_slices; b0 += kRowThreads) {
-    const int sl = b0 + threadIdx.x;
-    const int n = ((b0 == 0 ? n0 : (sl < n_slices ? slc[2 * sl + 1] : 0)) + 3) & ~3;
-    if (sl < n_slices) s_at[sl] = b0 == 0 ? at0 : slc[2 * sl];
-    const int inc = wave_incl_scan(n);
-    if (lane == 63) L.wt[wave] = inc;
-    lds_barrier();
-    int before = run + inc - n, all = 0;
-#pragma unroll
-    for (int u = 0; u < kRowWaves; ++u) {
-      if (u < wave) before += L.wt[u];
-      all += L.wt[u];
-    }
-    if (sl < n_slices) s_off[sl] = before;
-    run += all;
-    lds_barrier();
-  }
-  const int m = min(run, kRowList);
-  if (threadIdx.x == 0) {
-    s_off[n_slices] = run;
-    ws.ctr[(int64_t)row * kCtrStride] = 0;   // for the next call
-  }
-  lds_barrier();
-  // list ranks kPer * tid .. kPer * tid + kPer - 1: the slice holding a rank
-  // is the last one whose first rank is not above it
-  uint32_t key[kPer];
-  int pos[kPer];
-  const uint32_t* lk = ws.lkey + (int64_t)row * kRowList;
-  const int32_t* lp = ws.lpos + (int64_t)row * kRowList;
-  {
-    const int r0 = kPer * threadIdx.x;
-    int sl = 0;
-    if (r0 < m) {
-      int a = 0, b = n_slices - 1;
-      while (a < b) {
-        const int mid = (a + b + 1) >> 1;
-        if (s_off[mid] <= r0) a = mid;
-        else b = mid - 1;
-      }
-      sl = a;
-    }
-    // four ranks at a time: a slice's share starts on a multiple of 4 and
-    // holds a multiple of 4 entries, so they are 16 consecutive bytes
-#pragma unroll
-    for (int u = 0; u < kPer; u += 4) {
-      const int r = r0 + u;
-      uint4 kq = make_uint4(0u, 0u, 0u, 0u);
-      int4 pq = make_int4(0, 0, 0, 0);
-      if (r < m) {
-        while (s_off[sl + 1] <= r) ++sl;
-        const int at = s_at[sl] + (r - s_off[sl]);
-        if (at + 4 <= kRowList) {
-          kq = *(const uint4*)(lk + at);
-          pq = *(const int4*)(lp + at);
-        }
-      }
-      key[u] = kq.x;
-      key[u + 1] = kq.y;
-      key[u + 2] = kq.z;
-      key[u + 3] = kq.w;
-      pos[u] = pq.x;
-      pos[u + 1] = pq.y;
-      pos[u + 2] = pq.z;
-      pos[u + 3] = pq.w;
-    }
-  }
-
-  // 2. threshold over the listed keys (all keys of bins >= b0)
-  *(uint4*)(L.hist + 4 * threadIdx.x) = gv;
-  if (threadIdx.x < 256) L.dh[threadIdx.x] = 0u;
-  lds_barrier();
-  uint32_t T;
-  int need_eq, k_sel;
-  row_threshold(
-      L, k, []() {},
-      [&](auto&& f) {
-#pragma unroll
-        for (int u = 0; u < kPer; ++u) f(key[u]);
-      },
-      &T, &need_eq, &k_sel);
-
-  // 3. ordered write: the lane's entries are consecutive list ranks; the
-  // selection is staged in LDS (the list buffer of the fallback) when it fits
-  const bool stage = k <= kListCap;
-  int c = 0;
-#pragma unroll
-  for (int u = 0; u < kPer; ++u)
-    c += key[u] > T ? 1 : ((key[u] != 0u && key[u] == T) ? 0x10000 : 0);
-  const int inc = wave_incl_scan(c);
-  int oa, oe, ta, te;
-  row_wave_offsets(L, c, &oa, &oe, &ta, &te);
-  int ab = oa + ((inc - c) & 0xffff), eb = oe + ((inc - c) >> 16);
-  if (c) {
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      int dst = -1;
-      if (key[u] > T) {
-        dst = ab + min(eb, need_eq);
-        ++ab;
-      } else if (key[u] != 0u && key[u] == T) {
-        if (eb < need_eq) dst = ab + eb;
-        ++eb;
-      }
-      if (dst >= 0 && dst < k) {
-        if (stage) klist[dst] = (uint32_t)pos[u];
-        else if constexpr (MAP == 0) orow[dst] = pos[u];
-        else orow[dst] = map_b[map_a[(int64_t)row * map_ld + pos[u]]];
+    row_select_alone<false, MAP>(scores, row, H, L_max, lo_p, hi_p, k, (uint32_t*)gh4, true, orow,
+                                 count, map_a, map_b, map_ld, L, klist, klist_n, nullptr, true, gv);
+  } else {
+    // the selection is staged in LDS (the list buffer of the fallback) when
+    // it fits, then written in one coalesced pass
+    const bool stage = k <= kListCap;
+    const int n_sel = list_select(ws, row, k, n_slices, gv, L, s_off, s_at, [&](int dst, int p) {
+      if (stage) klist[dst] = (uint32_t)p;
+      else if constexpr (MAP == 0) orow[dst] = p;
+      else orow[dst] = map_b[map_a[(int64_t)row * map_ld + p]];
+    });
+    if (stage) {
+      lds_barrier();
+      for (int i = threadIdx.x; i < n_sel; i += kRowThreads) {
+        const int p = (int)klist[i];
+        orow[i] = MAP == 0 ? p : map_b[map_a[(int64_t)row * map_ld + p]];
       }
     }
+    for (int i = n_sel + threadIdx.x; i < k; i += kRowThreads) orow[i] = -1;
+    if (threadIdx.x == 0) count[row] = n_sel;
   }
-  const int n_sel = min(k, ta + min(te, need_eq));
-  if (stage) {   // one coalesced pass instead of a lane's 16 scattered stores
-    lds_barrier();
-    for (int i = threadIdx.x; i < n_sel; i += kRowThreads) {
-      const int p = (int)klist[i];
-      orow[i] = MAP == 0 ? p : map_b[map_a[(int64_t)row * map_ld + p]];
-    }
-  }
-  for (int i = n_sel + threadIdx.x; i < k; i += kRowThreads) orow[i] = -1;
-  if (threadIdx.x == 0) count[row] = n_sel;
-  gh4[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);   // zero for the next call
+  // zero for the next call: every copy of the row's histogram, its list counter
+  for (int cp = 0; cp < ws.copies; ++cp) gh4[cp * (kBins / 4) + threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
+  if (threadIdx.x == 0) ws.ctr[(int64_t)row * kCtrStride] = 0;
 }
 
 // --------------------------------------------------- prefiltered top-k --
@@ -753,6 +468,28 @@ size_t topk_workspace_bytes(int rows, int L_max) { return TopkWs::bytes(rows, L_
 
 bool topk_supported(int L_max) { return L_max >= 1 && topk_slices(L_max) <= kMaxSlices; }
 
+int topk_listing_slices(int rows, int L_max) {
+  return topk_slices_ng(L_max, topk_slice_groups(rows, L_max));
+}
+
+hipError_t launch_topk_listing(const float* scores, int rows, int H, int L_max, const int32_t* lo,
+                               const int32_t* hi, int k, void* wsp, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  const TopkWs ws = TopkWs::carve(wsp, rows, L_max);
+  const int ng_l = topk_slice_groups(rows, L_max);
+  const int ns = topk_slices_ng(L_max, ng_l);
+  if (ns > kMaxSlices || ns > topk_slices(L_max) || (int64_t)rows * ns > 0x7fffffff)
+    return hipErrorInvalidValue;
+  auto list = [&](auto kern) {
+    kern<<<(unsigned)(rows * ns), kSliceThreads, 0, s>>>(scores, H, L_max, lo, hi, k, ws, ns);
+  };
+  if (ng_l == 1) list(topk_compact_kernel<1>);
+  else if (ng_l == 2) list(topk_compact_kernel<2>);
+  else if (ng_l == 4) list(topk_compact_kernel<4>);
+  else list(topk_compact_kernel<kGroups>);
+  return hipGetLastError();
+}
+
 hipError_t launch_topk(const float* scores, int rows, int H, int L_max, const int32_t* lo,
                        const int32_t* hi, int k, int32_t* idx, int32_t* count, void* wsp,
                        bool hist_ready, hipStream_t s, const int32_t* map_a,
@@ -792,14 +529,9 @@ hipError_t launch_topk(const float* scores, int rows, int H, int L_max, const in
   }
   if (!hist_ready)
     topk_hist_kernel<<<(unsigned)(rows * ns_h), kSliceThreads, 0, s>>>(scores, H, L_max, lo, hi,
-                                                                         ws.hist, ns_h);
-  auto list = [&](auto kern) {
-    kern<<<(unsigned)(rows * ns), kSliceThreads, 0, s>>>(scores, H, L_max, lo, hi, k, ws, ns);
-  };
-  if (ng_l == 1) list(topk_compact_kernel<1>);
-  else if (ng_l == 2) list(topk_compact_kernel<2>);
-  else if (ng_l == 4) list(topk_compact_kernel<4>);
-  else list(topk_compact_kernel<kGroups>);
+                                                                         ws.hist, ns_h, ws.copies);
+  const hipError_t e = launch_topk_listing(scores, rows, H, L_max, lo, hi, k, wsp, s);
+  if (e != hipSuccess) return e;
   if (map == 0)
     topk_finish_kernel<0><<<rows, kRowThreads, 0, s>>>(scores, H, L_max, lo, hi, k, ws, ns, idx,
                                                        count, map_a, map_b, map_ld);

@@ -1,0 +1,106 @@
+"""GPU parity of the exact top-k finished inside the attention kernel for rows
+longer than one 32768-slot sweep (sparsekv_select_attend_resume after
+sparsekv_score_hist): the slice listing, then every attending workgroup
+resolves the row's selection from the list itself.  Checked against the
+float64 oracle (selection set, attention within 2e-3) and against the
+separate calls, including a row whose candidate list overflows (many tied
+scores) so that the selection falls back to reading the row per digit."""
+import numpy as np
+import pytest
+import torch
+
+import sparse_top_kv_indexer_amd as S
+import workloads as W
+from oracle import dense as D
+
+from gpu_helpers import ATTN_TOL, DEV, Run, check_selection, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _resume(r, ws=None):
+    st = r.st
+    skv, kv = r.skv, r.kv
+    B, H, L = skv.B, skv.H, skv.L_max
+    scores = torch.empty((B, H, L), dtype=torch.float32, device=DEV)
+    idx = torch.full((B, H, st.k), -7, dtype=torch.int32, device=DEV)
+    cnt = torch.full((B, H), -7, dtype=torch.int32, device=DEV)
+    out = torch.full((kv.B, kv.H * st.G, kv.d_v), float("nan"), dtype=torch.float32, device=DEV)
+    if ws is None:
+        ws = S.workspace(max(S.sparsekv_workspace_size(S.SKV_OP_SELECT_ATTEND, kv, st.G, st.k),
+                             S.sparsekv_workspace_size(S.SKV_OP_SELECT, skv, st.score_G, st.k)), DEV)
+    S.sparsekv_score_hist(skv, r.sq, st.score_G, r.lo, r.hi, scores, ws)
+    S.sparsekv_select_attend_resume(kv, r.q, st.G, r.lo, r.hi, st.k, st.scale, scores, idx, cnt,
+                                    out, ws)
+    torch.cuda.synchronize()
+    return scores, idx, cnt, out, ws
+
+
+def _check(st, rows=None):
+    say("fused long case", st.name, "G", st.G, "L", st.kv.L_max, "k", st.k)
+    r = Run(st)
+    sc, idx, cnt, out, ws = _resume(r)
+    idx, cnt, out = idx.cpu().numpy(), cnt.cpu().numpy(), out.cpu().numpy()
+    B, H = st.score_kv.B, st.score_kv.H
+    rows = [(b, h) for b in range(B) for h in range(H)] if rows is None else rows
+    ref = D.step(st, rows=rows)
+    swaps = 0
+    for b, h in rows:
+        sel = ref["idx"][b, h][: ref["count"][b, h]]
+        assert cnt[b, h] == ref["count"][b, h], (b, h)
+        sw = check_selection(ref["scores"][b, h], sel, idx[b, h], cnt[b, h])
+        swaps += sw
+        if sw == 0:
+            hs = list(range(h * st.G, (h + 1) * st.G))
+            err = np.abs(out[b, hs] - ref["out"][b, hs]).max()
+            assert err <= ATTN_TOL, (b, h, err)
+    # the separate calls select the same set
+    _, idx2, cnt2, out2 = r.step(fused=True)
+    assert np.array_equal(idx, idx2.cpu().numpy()) and np.array_equal(cnt, cnt2.cpu().numpy())
+    assert np.abs(out - out2.cpu().numpy()).max() <= ATTN_TOL
+    # the workspace regions that must start the next call at zero are zero
+    rws = B * H
+    copies = 8 if (rws <= 4 and st.score_kv.L_max > 32768) else 1
+    assert torch.count_nonzero(ws[: rws * copies * 4096 * 4]).item() == 0
+    return swaps
+
+
+@pytest.mark.parametrize("L,k,heads", [(65536, 2048, 128), (40000, 77, 16), (50016, 4096, 32),
+                                       (33024, 300, 64)])
+def test_fused_latent_long_rows(L, k, heads):
+    st = W.make_indexer_mla(tag=700 + heads, L=L, k=k, n_heads=heads)
+    assert _check(st) == 0
+
+
+def test_fused_latent_with_sink_local_and_short_sequence():
+    st = W.make_indexer_mla(tag=710, L=65536, k=1000, n_heads=128)
+    st.lo = np.array([7], np.int32)
+    st.hi = np.array([65536 - 300], np.int32)
+    assert _check(st) == 0
+    st = W.make_indexer_mla(tag=711, L=65536, k=512, n_heads=64)
+    st.kv.seq_len[:] = 40001
+    st.score_kv.seq_len[:] = 40001
+    st.hi = np.array([40001 - 100], np.int32)
+    assert _check(st) == 0
+
+
+def test_fused_latent_list_overflow_takes_the_row_fallback():
+    """All indexer keys equal: every score ties, the candidate list overflows
+    and each attending workgroup selects from the row itself (lowest
+    positions win the ties)."""
+    st = W.make_indexer_mla(tag=712, L=40960, k=1024, n_heads=16)
+    st.score_kv.k[:] = st.score_kv.k[0, 0, 0]
+    r = Run(st)
+    sc, idx, cnt, out, _ = _resume(r)
+    idx, cnt = idx.cpu().numpy(), cnt.cpu().numpy()
+    assert cnt[0, 0] == 1024
+    assert idx[0, 0].tolist() == list(range(1024))
+    ref = D.step(st)
+    assert np.abs(out.cpu().numpy() - ref["out"]).max() <= ATTN_TOL
+
+
+@pytest.mark.slow
+def test_fused_latent_full_size():
+    """The indexer + shared-latent workload at L = 131072, top-2048, 128 heads."""
+    st = W.make_indexer_mla()
+    assert _check(st) == 0

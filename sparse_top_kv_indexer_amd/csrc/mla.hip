@@ -434,7 +434,9 @@ __global__ __launch_bounds__(kRowThreads) void mla_list_kernel(
     }
   }
 
-  // 3. the split partial: O[head][512], max, sum (lane holds heads 4 g4 + i)
+  // 3. the split partial: O[head][512], max, sum (lane holds heads 4 g4 + i);
+  // an empty share never waited for the staged query rows
+  __builtin_amdgcn_s_waitcnt(0);
   if (!on) return;
   const int stride = kDv + 2;
 #pragma unroll

@@ -692,6 +692,33 @@ def paris_cpu_baseline(min_seconds):
                       % (n_runs, p.n, dt, cores)}
 
 
+PARIS_RHOS = (0.02, 0.05, 0.10)   # tier budgets rho reported (beta = 0.02)
+
+
+def paris_recall(p, cb, index, kv, q, dev):
+    """recall@100 of the retrieval at each rho of PARIS_RHOS, against the
+    exact top-100 of max_g q_g . k over the index region computed by the
+    library's own exact path (sparsekv_score + sparsekv_topk), mean over the
+    KV heads."""
+    import numpy as np
+    import torch
+    import sparse_top_kv_indexer_amd as S
+    qa = q.view(1, p.H * p.G, p.d)
+    sc = S.sparsekv_score(kv, qa, p.G)
+    lo = torch.tensor([p.sink], dtype=torch.int32, device=dev)
+    hi = torch.tensor([p.L - p.local], dtype=torch.int32, device=dev)
+    true_idx, _ = S.sparsekv_topk(sc, lo, hi, p.k_final)
+    true_idx = true_idx.cpu().numpy()[0]
+    out = {}
+    for rho in PARIS_RHOS:
+        idx, n_cand, _ = S.sparsekv_retrieve(cb, index, q, p.G, rho, p.beta, p.k_final)
+        got = idx.cpu().numpy()
+        r = [len(set(got[h].tolist()) & set(true_idx[h].tolist())) / p.k_final for h in range(p.H)]
+        out[repr(rho)] = float(np.mean(r))
+    del sc
+    return out
+
+
 def bench_paris(args, hip):
     import numpy as np
     import torch
@@ -770,6 +797,7 @@ def bench_paris(args, hip):
     ret_iso_ms = time_isolated(
         lambda i: S.sparsekv_retrieve(cb, ixs[i % len(ixs)], q, p.G, p.rho, p.beta, p.k_final,
                                       idx=ridx, n_cand=ncand, ws=ws_r), args, hip)
+    recall = paris_recall(p, cb, base, kv, q, dev)
     n_keys = p.H * p.n
     C = int(math.ceil(p.beta * p.n))
     ret_bytes = n_keys * 16 + p.H * C * 128      # ids scanned + codes and w of the candidates
@@ -787,6 +815,7 @@ def bench_paris(args, hip):
         "us_per_call": {"retrieve": float(np.mean(calls[:, 0])) * 1e3,
                         "gather_attend": float(np.mean(calls[:, 1])) * 1e3},
         "keys_voted_per_step": n_keys,
+        "recall_at_100": recall,
         "step_algorithmic_bytes": ret_bytes + gather,
         "step_GBps": (ret_bytes + gather) / (ms * 1e-3) / 1e9,
         "roofline": roofline("retrieval (sparsekv_retrieve: query LUT, collision vote, top-C, "

@@ -522,9 +522,8 @@ __global__ __launch_bounds__(256) void cand_write_kernel(const uint8_t* votes, i
 // chain).  The tree16 over the subspaces is a butterfly in which every level
 // halves the candidates a lane carries (lanes b, b ^ m add the same operands
 // as the tree's level m), so a group's 16 sums take 15 lane exchanges per
-// query head and lane u ends with candidate u's.  Each estimate's key also
-// goes into the head's 4096-bin top-12-bit histogram for the exact top-k
-// that follows.
+// query head and lane u ends with candidate u's.  The first workgroup of a
+// head also zeroes the head's vote totals for the next call.
 template <int G>
 __global__ __launch_bounds__(256) void rerank_kernel(const uint8_t* codes, const float* w, int cap,
                                                      int n, const int32_t* cand, int C,

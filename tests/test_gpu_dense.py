@@ -355,3 +355,29 @@ def test_mla_attend_kernel_on_oracle_selection():
 def test_indexer_mla_full_size():
     st = W.make_indexer_mla()
     assert _end_to_end(st) == 0
+
+
+@pytest.mark.parametrize("L,k,seed", [(20962, 100, 0), (20962, 256, 1), (4096, 1, 2),
+                                      (30000, 200, 3), (777, 256, 4)])
+def test_topk_small_k_narrow_score_range(L, k, seed):
+    """Small k over rows of one sweep whose scores span one octave (like the
+    rerank estimates of a retrieval): exact ties, dead slots and ragged
+    windows; the set equals the oracle's exactly."""
+    say("topk small", L, k, seed)
+    rng = np.random.default_rng(50 + seed)
+    B, H = 2, 4
+    s = (1.0 + 0.5 * rng.random((B, H, L))).astype(np.float32)
+    s[0, 1] = np.round(s[0, 1] * 64) / 64                   # exact ties
+    s[1, 2, rng.random(L) < 0.4] = -np.inf                   # dead slots
+    s[1, 3, : L // 2] = 1.25                                 # a tied block
+    lo = np.array([0, 5], np.int32)
+    hi = np.array([L, L - 3], np.int32)
+    sd = torch.from_numpy(s).to(DEV)
+    idx, cnt = S.sparsekv_topk(sd, S.to_device(lo, DEV), S.to_device(hi, DEV), k)
+    idx, cnt = idx.cpu().numpy(), cnt.cpu().numpy()
+    for b in range(B):
+        for h in range(H):
+            ref = D.select_topk(s[b, h].astype(np.float64), int(lo[b]), int(hi[b]), k)
+            assert cnt[b, h] == ref.size
+            assert idx[b, h, : ref.size].tolist() == sorted(ref.tolist()), (b, h)
+            assert np.all(idx[b, h, ref.size:] == -1)

@@ -217,3 +217,33 @@ def test_full_size_against_stored_oracle_results():
         err = np.abs(out[h * p.G:(h + 1) * p.G] - np.array(g["out"])).max()
         assert err <= ATTN_TOL, (h, err)
         say("  recall@100 (oracle and GPU)", g["recall_at_100"])
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("rho", [0.05, 0.10])
+def test_full_size_larger_tier_budgets_against_stored_oracle_results(rho):
+    """The full workload retrieved with tier budgets rho = 0.05 and 0.10
+    (beta = 0.02 unchanged): votes, candidates and estimates by hash and the
+    final ids equal the oracle's stored by tests/golden/make_paris_full.py, so
+    recall@100 is the oracle's."""
+    import hashlib
+    import json
+    import os
+    gold = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                       "paris_full_expected.json")))
+    heads = gold["by_rho"][repr(rho)]
+    p = W.make_paris()
+    cb, lv, th = _codebook(p)
+    kv, index = _gpu_index(p, cb)
+    q = S.to_device(p.q, DEV, bf16=True)
+    idx, n_cand, tr = S.sparsekv_retrieve(cb, index, q, p.G, rho, p.beta, p.k_final, trace=True)
+    torch.cuda.synchronize()
+    sha = lambda a: hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()
+    idx, n_cand = idx.cpu().numpy(), n_cand.cpu().numpy()
+    for h, g in enumerate(heads):
+        assert sha(tr["votes"][h].cpu().numpy()) == g["votes_sha256"], h
+        assert sha(tr["cand"][h].cpu().numpy().astype(np.int32)) == g["cand_sha256"], h
+        assert sha(tr["est"][h].cpu().numpy().astype(np.float32)) == g["est_sha256"], h
+        assert idx[h][: n_cand[h]].tolist() == g["idx"], h
+    say("  rho", rho, "mean recall@100 (oracle and GPU)",
+        sum(g["recall_at_100"] for g in heads) / len(heads))

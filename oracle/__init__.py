@@ -24,6 +24,9 @@ compact       token-table compaction: waste ratio, relocation plan (threshold,
               headroom, net-freeing gates), applying moves, and the I1 / I2
               checks (a position-independent hash of the retained tokens,
               duplicate-slot counts).
+validate      the checks of device-resident data a step takes on trust
+              (sequence lengths, windows, table entries inside the pool, no
+              slot mapped twice, selected positions in range and distinct).
 lloyd         Lloyd-Max levels for |u_j| under the Beta prior, float64.
 closed_forms  byte / capacity formulas the pages state.
 

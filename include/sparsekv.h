@@ -92,6 +92,10 @@ typedef struct {
   const int32_t* block_table;   /* [B][L_max/16] or NULL                      */
   const int32_t* token_table;   /* [B][L_max] slot or -1, or NULL             */
   const int32_t* seq_len;       /* [B] logical lengths                        */
+  int32_t n_blocks;             /* physical 16-token blocks in the pool
+                                   (block == 16), 0 = not given; read only by
+                                   the validation (sparsekv_validate, debug
+                                   builds)                                    */
 } skv_kv;
 
 /* Per-sequence windows (device [B] arrays): candidates for top-k are the live
@@ -502,6 +506,48 @@ skv_status sparsekv_retrieve(const skv_codebook* cb, const skv_index* index, con
  * the second yardstick beside the published HBM peak. */
 skv_status sparsekv_read_probe(const void* buf, size_t bytes, int32_t n_wg, uint32_t* sink,
                                hipStream_t stream);
+
+/* ------------------------------------------------------------ validation --
+ * Checks of the device-resident data the other calls take on trust (vToken
+ * reading notes, section 3.5 invariant I2: every live token maps to a valid
+ * slot inside the pool and no two live tokens to one slot; section 4.6 checks
+ * the invariants around every migration), OR-ed into flags[0] (device int32):
+ *   SKV_FLAG_BAD_SEQ_LEN  seq_len[b] outside [0, L_max]
+ *   SKV_FLAG_BAD_WINDOW   not 0 <= lo[b] <= hi[b] <= seq_len[b] (win given)
+ *   SKV_FLAG_BAD_SLOT     a mapping of a token t < seq_len[b] that is neither
+ *                         -1 nor a valid slot (token table: < -1 or
+ *                         >= 16 n_blocks; block table: < -1 or >= n_blocks;
+ *                         the upper bounds only when kv->n_blocks > 0)
+ *   SKV_FLAG_DUP_SLOT     two live tokens share a slot (token table) or two
+ *                         logical blocks a physical block (block table);
+ *                         only when kv->n_blocks > 0
+ *   SKV_FLAG_BAD_IDX      an idx entry outside [-1, L_max)
+ *   SKV_FLAG_DUP_IDX      an idx row names a position twice
+ * Reads seq_len, the table, win.lo / win.hi (both NULL: not checked) and
+ * idx [B][H][k] (NULL: not checked); never the K/V pools, so invalid tables
+ * form no address into them.  kv->k / kv->v are not read.
+ * ws: sparsekv_validate_ws_bytes(kv, k) bytes (any content).
+ *
+ * Builds compiled with SKV_DEBUG run the same checks at the start of every
+ * call that reads tables, windows or selected positions, into a flag word
+ * the library holds per device; sparsekv_debug_status synchronises the
+ * device, returns that word in *flags (host) and clears it (SKV_EUNSUPPORTED
+ * and 0 in release builds).  Debug builds allocate their check workspace with
+ * hipMalloc, so their calls must not be captured in a graph; the checks
+ * report, they do not stop the call that follows them. */
+enum {
+  SKV_FLAG_BAD_SEQ_LEN = 1,
+  SKV_FLAG_BAD_WINDOW = 2,
+  SKV_FLAG_BAD_SLOT = 4,
+  SKV_FLAG_DUP_SLOT = 8,
+  SKV_FLAG_BAD_IDX = 16,
+  SKV_FLAG_DUP_IDX = 32
+};
+size_t sparsekv_validate_ws_bytes(const skv_kv* kv, int32_t k);
+skv_status sparsekv_validate(const skv_kv* kv, skv_window win, const int32_t* idx, int32_t k,
+                             int32_t* flags, void* ws, size_t ws_bytes, hipStream_t stream);
+skv_status sparsekv_debug_status(int32_t* flags);
+int32_t sparsekv_is_debug_build(void);
 
 /* Workspace bytes for an op.  Arguments an op does not use may be NULL / 0:
  *   SCORE, ENCODE: 0;   TOPK, SELECT: kv->B, kv->H, kv->L_max;

@@ -25,6 +25,9 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsparsekv.so")
+# the checking build (every call first validates tables, windows and selected
+# positions); chosen with SKV_DEBUG=1 in the environment or use_debug_library()
+LIB_DEBUG_PATH = os.path.join(_HERE, "libsparsekv_debug.so")
 
 SKV_OK, SKV_EINVAL, SKV_EUNSUPPORTED, SKV_EWORKSPACE, SKV_ELAUNCH = range(5)
 SKV_F32, SKV_BF16 = 0, 1
@@ -43,7 +46,8 @@ class SkvError(RuntimeError):
 class skv_kv(ctypes.Structure):
     _fields_ = [("k", c_vp), ("v", c_vp), ("dtype", ctypes.c_int), ("B", c_i32), ("H", c_i32),
                 ("d_k", c_i32), ("d_v", c_i32), ("block", c_i32), ("L_max", c_i32),
-                ("block_table", c_vp), ("token_table", c_vp), ("seq_len", c_vp)]
+                ("block_table", c_vp), ("token_table", c_vp), ("seq_len", c_vp),
+                ("n_blocks", c_i32)]
 
 
 class skv_window(ctypes.Structure):
@@ -120,6 +124,11 @@ _SIGS = {
                                        ctypes.POINTER(skv_index)]),
     "sparsekv_retrieve_workspace_size": (c_sz, [ctypes.POINTER(skv_index), c_i32, ctypes.c_double,
                                                 c_i32]),
+    "sparsekv_validate_ws_bytes": (c_sz, [ctypes.POINTER(skv_kv), c_i32]),
+    "sparsekv_validate": (c_i32, [ctypes.POINTER(skv_kv), skv_window, c_vp, c_i32, c_vp, c_vp,
+                                  c_sz, c_vp]),
+    "sparsekv_debug_status": (c_i32, [ctypes.POINTER(c_i32)]),
+    "sparsekv_is_debug_build": (c_i32, []),
     "sparsekv_status_string": (ctypes.c_char_p, [c_i32]),
     "sparsekv_version": (c_i32, []),
 }
@@ -127,18 +136,31 @@ _SIGS = {
 _lib = None
 
 
+def _load(path: str):
+    if not os.path.exists(path):
+        raise RuntimeError("%s is not built (run __graft_entry__.build()); there is no fallback "
+                           "path" % os.path.basename(path))
+    L = ctypes.CDLL(path)
+    for name, (res, args) in _SIGS.items():
+        f = getattr(L, name)
+        f.restype, f.argtypes = res, args
+    return L
+
+
 def lib():
-    """The loaded library; raises if it has not been built."""
+    """The loaded library (the checking build when SKV_DEBUG=1 is set in the
+    environment); raises if it has not been built."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError("libsparsekv.so is not built (run __graft_entry__.build()); "
-                               "there is no fallback path")
-        L = ctypes.CDLL(LIB_PATH)
-        for name, (res, args) in _SIGS.items():
-            f = getattr(L, name)
-            f.restype, f.argtypes = res, args
-        _lib = L
+        _lib = _load(LIB_DEBUG_PATH if os.environ.get("SKV_DEBUG") == "1" else LIB_PATH)
+    return _lib
+
+
+def use_debug_library(on: bool = True):
+    """Route every following call to the checking build (on) or the release
+    build; both may be loaded in one process."""
+    global _lib
+    _lib = _load(LIB_DEBUG_PATH if on else LIB_PATH)
     return _lib
 
 
@@ -196,9 +218,11 @@ class KVTensors:
             t = getattr(self, nm)
             if t is not None:
                 _dev(t, nm, torch.int32)
+        n_blocks = self.k.numel() // (self.H * 16 * self.d_k) if self.block == 16 else 0
         return skv_kv(_ptr(self.k), _ptr(self.v), SKV_BF16 if self.dtype == "bf16" else SKV_F32,
                       self.B, self.H, self.d_k, self.d_v, self.block, self.L_max,
-                      _ptr(self.block_table), _ptr(self.token_table), _ptr(self.seq_len))
+                      _ptr(self.block_table), _ptr(self.token_table), _ptr(self.seq_len),
+                      n_blocks)
 
 
 def to_device(arr: np.ndarray, device, bf16: bool = False) -> torch.Tensor:
@@ -623,6 +647,44 @@ def sparsekv_gather_attend(kv: KVTensors, q: torch.Tensor, G: int, idx: Optional
                                         skv_window(_ptr(lo), _ptr(hi)), float(scale), _ptr(out),
                                         _ptr(ws), ws.numel() * ws.element_size(), _stream()))
     return out
+
+
+SKV_FLAG_BAD_SEQ_LEN, SKV_FLAG_BAD_WINDOW, SKV_FLAG_BAD_SLOT = 1, 2, 4
+SKV_FLAG_DUP_SLOT, SKV_FLAG_BAD_IDX, SKV_FLAG_DUP_IDX = 8, 16, 32
+
+
+def sparsekv_validate(kv: KVTensors, lo: Optional[torch.Tensor] = None,
+                      hi: Optional[torch.Tensor] = None, idx: Optional[torch.Tensor] = None,
+                      flags: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The checks of the device-resident tables, windows and selected
+    positions; returns the device int32 [1] flag word (OR-ed into flags when
+    given, else a zeroed one)."""
+    dev = kv.seq_len.device
+    if flags is None:
+        flags = torch.zeros(1, dtype=torch.int32, device=dev)
+    _dev(flags, "flags", torch.int32)
+    k = 0
+    if idx is not None:
+        _dev(idx, "idx", torch.int32)
+        k = idx.shape[-1]
+    c = kv.c()
+    ws = torch.empty(max(1, int(lib().sparsekv_validate_ws_bytes(ctypes.byref(c), k))),
+                     dtype=torch.uint8, device=dev)
+    _check("sparsekv_validate",
+           lib().sparsekv_validate(ctypes.byref(c), skv_window(_ptr(lo), _ptr(hi)), _ptr(idx), k,
+                                   _ptr(flags), _ptr(ws), ws.numel(), _stream()))
+    return flags
+
+
+def sparsekv_debug_status() -> int:
+    """The checking build's flag word (then cleared); SkvError in release builds."""
+    f = c_i32(0)
+    _check("sparsekv_debug_status", lib().sparsekv_debug_status(ctypes.byref(f)))
+    return int(f.value)
+
+
+def sparsekv_is_debug_build() -> bool:
+    return bool(lib().sparsekv_is_debug_build())
 
 
 def sparsekv_codebook_init(m: int):

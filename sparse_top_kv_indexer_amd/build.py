@@ -1,4 +1,7 @@
-"""Build libsparsekv.so (all HIP sources, gfx950) in-tree with hipcc.
+"""Build libsparsekv.so (all HIP sources, gfx950) in-tree with hipcc, and
+its checking variant libsparsekv_debug.so (compiled with SKV_DEBUG: every
+entry point first validates the device-resident tables, windows and
+selected positions into a flag word the library holds).
 
 Every source is compiled on its own (in parallel) and linked into one shared
 library next to this file.  Flags: -O3, C++17, the packed-fp32 target
@@ -17,7 +20,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libsparsekv.so")
+LIB_DEBUG = os.path.join(HERE, "libsparsekv_debug.so")
 BUILD = os.path.join(ROOT, "_build")
+BUILD_DEBUG = os.path.join(ROOT, "_build_debug")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -32,9 +37,9 @@ def sources():
     return sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-    flags = list(COMMON)
+def _compile(src: str, debug: bool = False) -> str:
+    obj = os.path.join(BUILD_DEBUG if debug else BUILD, src.replace(".hip", ".o"))
+    flags = list(COMMON) + (["-DSKV_DEBUG"] if debug else [])
     if src in NO_CONTRACT:
         flags += ["-ffp-contract=off"]
     cmd = [HIPCC] + flags + ["-c", os.path.join(CSRC, src), "-o", obj]
@@ -47,21 +52,23 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = True, debug: bool = False) -> str:
+    lib = LIB_DEBUG if debug else LIB
+    os.makedirs(BUILD_DEBUG if debug else BUILD, exist_ok=True)
     srcs = sources()
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda f: _compile(f, debug), srcs))
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print("built", LIB)
-    return LIB
+        print("built", lib)
+    return lib
 
 
 if __name__ == "__main__":
     build()
+    build(debug=True)

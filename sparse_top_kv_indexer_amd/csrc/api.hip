@@ -9,9 +9,17 @@
 #include "skv_internal.h"
 #include "skv_topk.h"
 
+namespace skv {
+// validate.hip: the checks of a debug build, run first by the entry points
+// (a no-op in release builds)
+void debug_validate(const skv_kv* kv, skv_window win, const int32_t* idx, int k, hipStream_t st);
+}  // namespace skv
+
 using namespace skv;
 
 namespace {
+
+const skv_window kNoWindow = {nullptr, nullptr};
 
 bool kv_ok(const skv_kv* kv) {
   if (!kv || !kv->k || !kv->seq_len) return false;
@@ -116,6 +124,7 @@ skv_status sparsekv_score(const skv_kv* kv, const void* q, int32_t G, float* sco
                           hipStream_t stream) {
   if (!kv_ok(kv) || !q || !scores || G < 1) return SKV_EINVAL;
   if (!score_supported(kv, G)) return SKV_EUNSUPPORTED;
+  debug_validate(kv, kNoWindow, nullptr, 0, stream);
   return launched(launch_score(to_args(kv), q, G, scores, nullptr, nullptr, nullptr, stream));
 }
 
@@ -135,6 +144,7 @@ skv_status sparsekv_score_hist(const skv_kv* kv, const void* q, int32_t G, skv_w
   if (!kv_ok(kv) || !q || !scores || G < 1 || !win.lo || !win.hi) return SKV_EINVAL;
   if (!score_supported(kv, G) || !topk_supported(kv->L_max)) return SKV_EUNSUPPORTED;
   if (!ws || ws_bytes < topk_workspace_bytes(kv->B * kv->H, kv->L_max)) return SKV_EWORKSPACE;
+  debug_validate(kv, win, nullptr, 0, stream);
   return launched(launch_score(to_args(kv), q, G, scores, win.lo, win.hi, (uint32_t*)ws, stream));
 }
 
@@ -158,6 +168,7 @@ skv_status sparsekv_score_prefilter(const skv_kv* kv, const void* q, int32_t G, 
     return SKV_EUNSUPPORTED;
   const int rows = kv->B * kv->H;
   if (!ws || ws_bytes < topk_workspace_bytes(rows, kv->L_max)) return SKV_EWORKSPACE;
+  debug_validate(kv, win, nullptr, 0, stream);
   const TopkWs w = TopkWs::carve(ws, rows, kv->L_max);
   return launched(launch_score_prefilter(a, q, G, scores, win.lo, win.hi, thr, w.lkey, w.lpos,
                                          w.ctr, kRowList, stream));
@@ -184,6 +195,7 @@ skv_status sparsekv_select(const skv_kv* kv, const void* q, int32_t G, skv_windo
   if (!score_supported(kv, G) || !topk_supported(kv->L_max)) return SKV_EUNSUPPORTED;
   const int rows = kv->B * kv->H;
   if (!ws || ws_bytes < topk_workspace_bytes(rows, kv->L_max)) return SKV_EWORKSPACE;
+  debug_validate(kv, win, nullptr, 0, stream);
   hipError_t e = launch_score(to_args(kv), q, G, scores, win.lo, win.hi, (uint32_t*)ws, stream);
   if (e != hipSuccess) return launched(e);
   return launched(launch_topk(scores, rows, kv->H, kv->L_max, win.lo, win.hi, k, idx, count, ws,
@@ -197,6 +209,7 @@ skv_status sparsekv_gather_attend(const skv_kv* kv, const void* q, int32_t G, co
   if (k > kv->L_max) return SKV_EINVAL;
   if (!win.lo || !win.hi || !isfinite(scale)) return SKV_EINVAL;
   const KvArgs a = to_args(kv);
+  debug_validate(kv, win, idx, k, stream);
   if (kv->v == nullptr) {
     if (!mla_supported(a, G)) return SKV_EUNSUPPORTED;
     const size_t need = mla_workspace_bytes(a, G, k);
@@ -221,6 +234,7 @@ skv_status sparsekv_select_attend(const skv_kv* kv, const void* q, int32_t G, sk
   if (!score_supported(kv, G) || !select_attend_supported(a, G)) return SKV_EUNSUPPORTED;
   const size_t th = topk_workspace_bytes(kv->B * kv->H, kv->L_max);
   if (!ws || ws_bytes < th + select_attend_partial_bytes(a, G)) return SKV_EWORKSPACE;
+  debug_validate(kv, win, nullptr, 0, stream);
   uint32_t* hist = (uint32_t*)ws;
   float* part = (float*)((char*)ws + th);
   const hipError_t e = launch_score(a, q, G, scores, win.lo, win.hi, hist, stream);
@@ -240,6 +254,7 @@ skv_status sparsekv_select_attend_resume(const skv_kv* kv, const void* q, int32_
   const int rows = kv->B * kv->H;
   const size_t th = topk_workspace_bytes(rows, kv->L_max);
   float* part = (float*)((char*)ws + th);
+  debug_validate(kv, win, nullptr, 0, stream);
   if (kv->v == nullptr) {
     // latent KV: rows longer than one sweep finish the top-k inside the
     // attention kernel; shorter ones take the one-workgroup top-k first
@@ -276,6 +291,7 @@ skv_status sparsekv_select_attend_noalloc(const skv_kv* kv, const void* q, int32
   const int rows = kv->B * kv->H;
   const size_t hb = noalloc_hist_bytes(rows);
   if (hb + select_attend_partial_bytes(a, G) > kScratchBytes) return SKV_EWORKSPACE;
+  debug_validate(kv, win, nullptr, 0, stream);
   void* base = nullptr;
   if (scratch_for_current_device(&base) != hipSuccess) return SKV_ELAUNCH;
   uint32_t* hist = (uint32_t*)base;
@@ -322,6 +338,7 @@ skv_status sparsekv_block_select(const skv_kv* kv, void* summ, const void* q, in
   const KvArgs a = to_args(kv);
   if (!block_select_supported(a, G)) return SKV_EUNSUPPORTED;
   if (!ws || ws_bytes < block_select_ws_bytes(a, G)) return SKV_EWORKSPACE;
+  debug_validate(kv, win, nullptr, 0, stream);
   return launched(launch_block_select(a, summ, q, G, win.lo, win.hi, K, blk_scores, blk_idx,
                                       blk_count, tok_idx, ws, stream));
 }

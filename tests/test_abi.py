@@ -57,7 +57,7 @@ def test_codebook_rejects_bad_m():
 
 def _kv(**over):
     base = dict(k=1, v=1, dtype=S.SKV_BF16, B=1, H=1, d_k=128, d_v=128, block=0, L_max=64,
-                block_table=None, token_table=None, seq_len=1)
+                block_table=None, token_table=None, seq_len=1, n_blocks=0)
     base.update(over)
     return S.skv_kv(**base)
 
@@ -184,3 +184,31 @@ def test_noalloc_rejects_sizes_beyond_its_scratch_before_any_device_work():
     st = L.sparsekv_select_attend_noalloc(ctypes.byref(small), P, 4, win, 4097, 0.1, P, P, P, P,
                                           None)
     assert st == S.SKV_EINVAL
+
+
+def test_debug_build_exports_the_same_symbols_and_says_so():
+    names = _declared()
+    D = ctypes.CDLL(S.LIB_DEBUG_PATH)
+    for n in names:
+        assert hasattr(D, n), n
+    D.sparsekv_is_debug_build.restype = ctypes.c_int32
+    assert D.sparsekv_is_debug_build() == 1
+    assert S.lib().sparsekv_is_debug_build() == 0
+    f = ctypes.c_int32(7)
+    assert S.lib().sparsekv_debug_status(ctypes.byref(f)) == S.SKV_EUNSUPPORTED and f.value == 0
+
+
+def test_validate_checks_host_arguments_first():
+    L = S.lib()
+    P = ctypes.c_void_p(1)
+    kv = _kv(B=2, H=2, L_max=64, block=16, token_table=1, n_blocks=8)
+    assert L.sparsekv_validate_ws_bytes(ctypes.byref(kv), 0) == 8 * 16 * 4
+    assert L.sparsekv_validate_ws_bytes(ctypes.byref(kv), 5) == 8 * 16 * 4 + 2 * 2 * 2 * 4
+    win = S.skv_window(P, P)
+    assert L.sparsekv_validate(ctypes.byref(kv), win, None, 0, None, P, 1 << 20, None) == S.SKV_EINVAL
+    assert L.sparsekv_validate(ctypes.byref(kv), S.skv_window(P, None), None, 0, P, P, 1 << 20,
+                               None) == S.SKV_EINVAL
+    assert L.sparsekv_validate(ctypes.byref(kv), win, None, 3, P, P, 1 << 20, None) == S.SKV_EINVAL
+    assert L.sparsekv_validate(ctypes.byref(kv), win, None, 0, P, P, 16, None) == S.SKV_EWORKSPACE
+    bad = _kv(B=2, H=2, L_max=64, block=16, token_table=1, n_blocks=-1)
+    assert L.sparsekv_validate(ctypes.byref(bad), win, None, 0, P, P, 1 << 20, None) == S.SKV_EINVAL

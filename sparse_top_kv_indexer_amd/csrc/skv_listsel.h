@@ -340,21 +340,16 @@ __device__ __forceinline__ int list_select(const TopkWs& ws, int row, int k, int
 }
 
 // This thread's 4 bins (4 t .. 4 t + 3) of row `row`'s first-digit
-// histogram, summed over its copies (one load per copy, all in flight).
+// histogram, summed over its copies (few rows have more than one).
 __device__ __forceinline__ uint4 hist_bins_summed(const TopkWs& ws, int row) {
   const uint4* g = (const uint4*)(ws.hist + (int64_t)row * ws.copies * kBins) + threadIdx.x;
-  if (ws.copies == 1) return g[0];
-  uint4 x[kHistCopiesMax];
-#pragma unroll
-  for (int cp = 0; cp < kHistCopiesMax; ++cp)
-    x[cp] = cp < ws.copies ? g[cp * (kBins / 4)] : make_uint4(0u, 0u, 0u, 0u);
-  uint4 v = x[0];
-#pragma unroll
-  for (int cp = 1; cp < kHistCopiesMax; ++cp) {
-    v.x += x[cp].x;
-    v.y += x[cp].y;
-    v.z += x[cp].z;
-    v.w += x[cp].w;
+  uint4 v = g[0];
+  for (int cp = 1; cp < ws.copies; ++cp) {
+    const uint4 x = g[cp * (kBins / 4)];
+    v.x += x.x;
+    v.y += x.y;
+    v.z += x.z;
+    v.w += x.w;
   }
   return v;
 }

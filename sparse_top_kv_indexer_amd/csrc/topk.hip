@@ -104,8 +104,10 @@ __global__ __launch_bounds__(kSliceThreads) void topk_hist_kernel(const float* s
 }
 
 // -------------------------------------------------------------- listing --
-// Grid rows * slices of NG groups per lane, 256 threads.
-template <int NG>
+// Grid rows * slices of NG groups per lane, 256 threads; COPIES: the rows'
+// histogram copies (ws.copies), a compile-time constant so that one copy
+// costs no registers for the others.
+template <int NG, int COPIES>
 __global__ __launch_bounds__(kSliceThreads) void topk_compact_kernel(
     const float* scores, int H, int L_max, const int32_t* lo_p, const int32_t* hi_p, int k,
     TopkWs ws, int n_slices) {
@@ -122,18 +124,17 @@ __global__ __launch_bounds__(kSliceThreads) void topk_compact_kernel(
   // (summed over the row's histogram copies)
   int c[16];
   {
-    const uint4* gh = (const uint4*)(ws.hist + (int64_t)row * ws.copies * kBins) + 4 * threadIdx.x;
-    uint4 x[kHistCopiesMax][4];
+    const uint4* gh = (const uint4*)(ws.hist + (int64_t)row * COPIES * kBins) + 4 * threadIdx.x;
+    uint4 x[COPIES][4];
 #pragma unroll
-    for (int cp = 0; cp < kHistCopiesMax; ++cp)
+    for (int cp = 0; cp < COPIES; ++cp)
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        x[cp][u] = cp < ws.copies ? gh[cp * (kBins / 4) + u] : make_uint4(0u, 0u, 0u, 0u);
+      for (int u = 0; u < 4; ++u) x[cp][u] = gh[cp * (kBins / 4) + u];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       c[4 * u] = c[4 * u + 1] = c[4 * u + 2] = c[4 * u + 3] = 0;
 #pragma unroll
-      for (int cp = 0; cp < kHistCopiesMax; ++cp) {
+      for (int cp = 0; cp < COPIES; ++cp) {
         c[4 * u] += (int)x[cp][u].x;
         c[4 * u + 1] += (int)x[cp][u].y;
         c[4 * u + 2] += (int)x[cp][u].z;
@@ -480,13 +481,19 @@ hipError_t launch_topk_listing(const float* scores, int rows, int H, int L_max, 
   const int ns = topk_slices_ng(L_max, ng_l);
   if (ns > kMaxSlices || ns > topk_slices(L_max) || (int64_t)rows * ns > 0x7fffffff)
     return hipErrorInvalidValue;
+  if (ws.copies != 1 && ws.copies != kHistCopiesMax) return hipErrorInvalidValue;
   auto list = [&](auto kern) {
     kern<<<(unsigned)(rows * ns), kSliceThreads, 0, s>>>(scores, H, L_max, lo, hi, k, ws, ns);
   };
-  if (ng_l == 1) list(topk_compact_kernel<1>);
-  else if (ng_l == 2) list(topk_compact_kernel<2>);
-  else if (ng_l == 4) list(topk_compact_kernel<4>);
-  else list(topk_compact_kernel<kGroups>);
+  auto by_ng = [&](auto copies_c) {
+    constexpr int CP = decltype(copies_c)::value;
+    if (ng_l == 1) list(topk_compact_kernel<1, CP>);
+    else if (ng_l == 2) list(topk_compact_kernel<2, CP>);
+    else if (ng_l == 4) list(topk_compact_kernel<4, CP>);
+    else list(topk_compact_kernel<kGroups, CP>);
+  };
+  if (ws.copies == 1) by_ng(std::integral_constant<int, 1>{});
+  else by_ng(std::integral_constant<int, kHistCopiesMax>{});
   return hipGetLastError();
 }
 

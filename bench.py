@@ -433,7 +433,8 @@ def bench_dense(args, hip):
     cnt = torch.empty((B, H), dtype=torch.int32, device=dev)
     out = torch.empty((kv.B, kv.H * G, kv.d_v), dtype=torch.float32, device=dev)
     # fused: the top-k finished inside the attention kernel (GQA rows of one
-    # sweep; the latent attention at any length)
+    # 32768-slot sweep; the latent attention at any length -- longer GQA rows
+    # are timed as separate calls, which is what the fused call runs for them)
     fused = args.path == "fused" and (mla or (skv is kv and sG == G and bf and kv.d_k == 128
                                               and G <= 8 and L <= 32768))
     prefilter = args.path == "prefilter"

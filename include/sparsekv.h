@@ -218,9 +218,10 @@ skv_status sparsekv_gather_attend(const skv_kv* kv, const void* q, int32_t G, co
  * count [B][H] and out [B][H*G][d_v] fp32 (definitions above: ParisKV
  * close-reading, section 一, Eqs. (1)-(3); ECHO-OSDI26 wiki page,
  * observation 5; vToken reading notes, section 3.4 Eq. (2)).
- * Supports bf16 keys and values with d_k == d_v == 128, 1 <= G <= 8 and
- * L_max <= 32768, or L_max <= 32765 when L_max is not a multiple of 4
- * (SKV_EUNSUPPORTED otherwise: use the separate calls).
+ * Supports bf16 keys and values with d_k == d_v == 128 and 1 <= G <= 8, any
+ * L_max.  Rows of at most one 32768-slot sweep (L_max <= 32768, or 32765 when
+ * L_max is not a multiple of 4) take the fused kernel; longer rows take the
+ * slice-listing top-k and the split attention inside the same call.
  * ws: sparsekv_workspace_size(SKV_OP_SELECT_ATTEND, kv, G, k, NULL) bytes,
  * zero-filled before its first use; every call leaves its first region (the
  * key histograms) zero again. */

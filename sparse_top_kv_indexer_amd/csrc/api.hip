@@ -107,6 +107,27 @@ hipError_t scratch_for_current_device(void** out) {
   return hipSuccess;
 }
 
+// GQA rows longer than one sweep in the fused calls: the slice-listing top-k
+// (finished by one workgroup per row), then the split attention and merge.
+// Finishing the selection inside the attention kernel instead (every
+// attending workgroup resolving its row from the list) measured no faster
+// for these rows: the repeated selections cost what the boundary saves.
+bool long_select_attend_supported(const KvArgs& a, int G) {
+  return a.bf16 && a.v != nullptr && a.d_k == 128 && a.d_v == 128 && G >= 1 && G <= 8 &&
+         topk_supported(a.L_max) && attend_supported(a, G);
+}
+
+skv_status long_select_attend(const KvArgs& a, const void* q, int G, skv_window win, int k,
+                              float scale, const float* scores, int32_t* idx, int32_t* count,
+                              float* out, void* ws, size_t th, size_t ws_bytes,
+                              hipStream_t stream) {
+  const hipError_t e = launch_topk(scores, a.B * a.H, a.H, a.L_max, win.lo, win.hi, k, idx, count,
+                                   ws, true, stream);
+  if (e != hipSuccess) return launched(e);
+  return launched(launch_gather_attend(a, q, G, idx, k, win.lo, win.hi, scale, out,
+                                       (char*)ws + th, ws_bytes - th, stream));
+}
+
 // Scratch layout of the fused step without a workspace: the rows' key
 // histograms (must be zero when the scan starts), then the split partials.
 size_t noalloc_hist_bytes(int rows) { return ((size_t)rows * 4096 * 4 + 255) & ~(size_t)255; }
@@ -231,14 +252,20 @@ skv_status sparsekv_select_attend(const skv_kv* kv, const void* q, int32_t G, sk
   if (!kv_ok(kv) || !q || !scores || !idx || !count || !out || G < 1 || k < 1) return SKV_EINVAL;
   if (k > kv->L_max || !win.lo || !win.hi || !isfinite(scale)) return SKV_EINVAL;
   const KvArgs a = to_args(kv);
-  if (!score_supported(kv, G) || !select_attend_supported(a, G)) return SKV_EUNSUPPORTED;
+  const bool one_sweep = select_attend_supported(a, G);
+  if (!score_supported(kv, G) || (!one_sweep && !long_select_attend_supported(a, G)))
+    return SKV_EUNSUPPORTED;
   const size_t th = topk_workspace_bytes(kv->B * kv->H, kv->L_max);
-  if (!ws || ws_bytes < th + select_attend_partial_bytes(a, G)) return SKV_EWORKSPACE;
+  const size_t pb = one_sweep ? select_attend_partial_bytes(a, G) : attend_workspace_bytes(a, G, k);
+  if (!ws || ws_bytes < th + pb) return SKV_EWORKSPACE;
   debug_validate(kv, win, nullptr, 0, stream);
   uint32_t* hist = (uint32_t*)ws;
   float* part = (float*)((char*)ws + th);
   const hipError_t e = launch_score(a, q, G, scores, win.lo, win.hi, hist, stream);
   if (e != hipSuccess) return launched(e);
+  if (!one_sweep)
+    return long_select_attend(a, q, G, win, k, scale, scores, idx, count, out, ws, th, ws_bytes,
+                              stream);
   return launched(launch_select_attend(a, q, G, scores, win.lo, win.hi, k, hist, scale, idx, count,
                                        part, out, stream));
 }
@@ -269,10 +296,15 @@ skv_status sparsekv_select_attend_resume(const skv_kv* kv, const void* q, int32_
     return launched(launch_mla_attend(a, q, G, idx, k, win.lo, win.hi, scale, out, part,
                                       ws_bytes - th, stream));
   }
-  if (!score_supported(kv, G) || !select_attend_supported(a, G)) return SKV_EUNSUPPORTED;
-  if (!ws || ws_bytes < th + select_attend_partial_bytes(a, G)) return SKV_EWORKSPACE;
-  return launched(launch_select_attend(a, q, G, scores, win.lo, win.hi, k, (uint32_t*)ws, scale,
-                                       idx, count, part, out, stream));
+  if (select_attend_supported(a, G)) {
+    if (!ws || ws_bytes < th + select_attend_partial_bytes(a, G)) return SKV_EWORKSPACE;
+    return launched(launch_select_attend(a, q, G, scores, win.lo, win.hi, k, (uint32_t*)ws, scale,
+                                         idx, count, part, out, stream));
+  }
+  if (!long_select_attend_supported(a, G)) return SKV_EUNSUPPORTED;
+  if (!ws || ws_bytes < th + attend_workspace_bytes(a, G, k)) return SKV_EWORKSPACE;
+  return long_select_attend(a, q, G, win, k, scale, scores, idx, count, out, ws, th, ws_bytes,
+                            stream);
 }
 
 size_t sparsekv_select_attend_noalloc_bytes(const skv_kv* kv, int32_t G) {
@@ -363,7 +395,8 @@ size_t sparsekv_workspace_size(skv_op op, const skv_kv* kv, int32_t G, int32_t k
       if (!kv_ok(kv) || G < 1 || k < 0) return 0;
       return topk_workspace_bytes(kv->B * kv->H, kv->L_max) +
              (kv->v == nullptr ? mla_select_attend_partial_bytes(to_args(kv), G, k)
-                               : select_attend_partial_bytes(to_args(kv), G));
+                               : std::max(select_attend_partial_bytes(to_args(kv), G),
+                                          attend_workspace_bytes(to_args(kv), G, k)));
     case SKV_OP_BLOCK_SELECT:
       if (!kv_ok(kv) || G < 1) return 0;
       return block_select_ws_bytes(to_args(kv), G);

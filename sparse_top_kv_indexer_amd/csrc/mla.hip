@@ -251,18 +251,6 @@ int mla_splits(int k) { return std::max(8, std::min(64, (k + 63) / 64 + 7) / 8 *
 constexpr int kFuseRows = 64;          // latent rows staged at a time
 constexpr int kFuseSlices = 1024;      // listing slices of a row this kernel reads
 
-// The row's selection when its list overflowed: the row alone, re-read per
-// digit (rare; kept out of line so its registers do not weigh on the
-// attention).
-__device__ __noinline__ int fallback_select(const float* scores, int row, int H, int L_max,
-                                           const int32_t* lo_p, const int32_t* hi_p, int k,
-                                           uint32_t* ghist_row, RowSelLds& L, int& klist_n,
-                                           uint4 gv) {
-  return row_select_alone<false, 3>(scores, row, H, L_max, lo_p, hi_p, k, ghist_row, true, nullptr,
-                                    nullptr, nullptr, nullptr, 0, L, nullptr, klist_n, nullptr,
-                                    true, gv);
-}
-
 template <int DP>
 __global__ __launch_bounds__(kRowThreads) void mla_list_kernel(
     KvArgs kv, const uint16_t* q, int G, const float* scores, const int32_t* lo_p,

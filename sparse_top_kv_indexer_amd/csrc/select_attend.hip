@@ -27,6 +27,8 @@
 // every head.  The 16 waves' (max, sum, weighted values) merge through LDS
 // into the workgroup's split partial; attend_reduce_kernel merges the splits
 // and zeroes the rows' histograms for the next call.
+#include <algorithm>
+
 #include "skv_internal.h"
 #include "skv_rowsel.h"
 
@@ -35,110 +37,25 @@ namespace skv {
 namespace {
 
 constexpr int kSplits = 8;                        // selection workgroups per row
-constexpr int kListCap = kSweep / kSplits;        // listed keys per workgroup (k <= 32768)
+constexpr int kShareCap = kSweep / kSplits;       // selected keys per workgroup (k <= 32768)
 constexpr int kD = 128;
 
+// Attention of one workgroup over its share of a row's tokens (step 3 of
+// the fused kernels) and the merge of its 16 waves into the split partial
+// (step 4): the tokens are lst[0 .. n_list) (selected positions) then the
+// always-attended positions x0 .. of t < a_lo and t >= a_hi, n_att in all;
+// tbl: the row's block-table entries staged in LDS, or null (slots through
+// kv's table).  Qf: the MFMA B operand of the G query rows.
 template <int GMAX>
-__global__ __launch_bounds__(kRowThreads) void select_attend_kernel(
-    KvArgs kv, const uint16_t* q, int G, const float* scores, const int32_t* lo_p,
-    const int32_t* hi_p, int k, const uint32_t* ghist, float scale_log2, int32_t* idx,
-    int32_t* count, float* part) {
-  __shared__ RowSelLds L;
-  __shared__ int32_t lst[kListCap];                 // this workgroup's share of the selection
-  __shared__ int64_t rows_sh[kRowWaves][2][16];     // per wave: key-row offsets of two chunks
-  __shared__ float red[kRowWaves][4][kD + 2];       // merge of the waves, 4 heads a round
-  __shared__ int32_t tbl[kSweep / 16];              // the row's block-table entries (paged)
-  // the kSplits workgroups of a row run on one XCD and share its scores in L2
-  const int vid = xcd_remap(blockIdx.x, gridDim.x);
-  const int s = vid % kSplits, row = vid / kSplits;
-  const int b = row / kv.H, h = row - b * kv.H;
+__device__ __forceinline__ void attend_share(const KvArgs& kv, int G, int row, int b, int h, int s,
+                                             int n_split, const int32_t* lst, int n_list, int x0,
+                                             int n_att, int a_lo, int a_hi, int seq,
+                                             const int32_t* tbl, const bf16x8_t (&Qf)[4],
+                                             float scale_log2, float* part,
+                                             int64_t (&rows_sh)[kRowWaves][2][16],
+                                             float (&red)[kRowWaves][4][kD + 2]) {
   const int lane = threadIdx.x & 63, wave = row_wave();
   const int n = lane & 15, g4 = lane >> 4;
-  RowWindow w = row_window(lo_p, hi_p, b, kv.L_max);
-  bool vec;
-  const float* srow = row_base(scores, (int64_t)row * kv.L_max, w, &vec);
-
-  // 1. the row's threshold (histogram first, then the scores)
-  const uint4 gv = ((const uint4*)(ghist + (int64_t)row * kBins))[threadIdx.x];
-  float fv[kGroups][4];
-  row_load(srow, w, vec, 0, fv);
-  // the block-table row, kept in registers until the attention needs it
-  const int n_blk = kv.block_table ? kv.L_max >> 4 : 0;
-  int32_t tb[kSweep / 16 / kRowThreads];
-#pragma unroll
-  for (int u = 0; u < kSweep / 16 / kRowThreads; ++u) {
-    const int i = threadIdx.x + u * kRowThreads;
-    tb[u] = i < n_blk ? kv.block_table[(int64_t)b * n_blk + i] : -1;
-  }
-  // the query rows (MFMA B operand of the logits), also needed only later
-  bf16x8_t Qf[4];
-  {
-    const uint16_t* qrow = q + ((int64_t)row * G + (n < G ? n : 0)) * kD;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const u32x4_t v = n < G ? ld16((const char*)(qrow + 8 * (4 * j + g4))) : u32x4_t{0, 0, 0, 0};
-      Qf[j] = __builtin_bit_cast(bf16x8_t, v);
-    }
-  }
-  uint32_t kr[kGroups][4];
-  *(uint4*)(L.hist + 4 * threadIdx.x) = gv;
-  if (threadIdx.x < 256) L.dh[threadIdx.x] = 0u;
-  lds_barrier();
-  uint32_t T;
-  int need_eq, k_sel;
-  row_threshold(
-      L, k, [&]() { row_keys(fv, kr); },
-      [&](auto&& f) {
-#pragma unroll
-        for (int g = 0; g < kGroups; ++g)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) f(kr[g][e]);
-      },
-      &T, &need_eq, &k_sel);
-
-  // 2. ranks.  Workgroup s writes idx and lists in LDS the selected keys of
-  //    ranks [r0, r1), an equal share of the k_sel selected keys
-  int32_t* orow = idx + (int64_t)row * k;
-  int n_list;
-  {
-    int cg[kGroups];
-    const int lt = row_counts(kr, T, cg);
-    int oa, oe, ta, te;
-    row_wave_offsets(L, lt, &oa, &oe, &ta, &te);
-    const int r0 = (int)((int64_t)k_sel * s / kSplits);
-    const int r1 = (int)((int64_t)k_sel * (s + 1) / kSplits);
-    n_list = r1 - r0;
-    // ranks of this wave's selected keys: [first, last)
-    const int first = oa + min(oe, need_eq);
-    const int last = oa + L.wa[wave] + min(oe + L.we[wave], need_eq);
-    if (first < r1 && last > r0) {
-      const int pos0 = w.lo - w.o + wave * kSeg + 4 * lane;
-      row_emit(kr, cg, T, need_eq, oa, oe, [&](int dst, int g, int e) {
-        if (dst >= r0 && dst < r1) {
-          const int t = pos0 + 256 * g + e;
-          orow[dst] = t;
-          lst[dst - r0] = t;
-        }
-      });
-    }
-    if (s == 0) {
-      const int n_sel = min(k, ta + min(te, need_eq));   // == k_sel
-      for (int i = n_sel + threadIdx.x; i < k; i += kRowThreads) orow[i] = -1;
-      if (threadIdx.x == 0) count[row] = n_sel;
-    }
-  }
-
-  // 3. attention over the listed keys plus this workgroup's share of the
-  //    always-attended tokens t < lo and t >= hi (live ones)
-  const int seq = min(kv.seq_len[b], kv.L_max);
-  const int a_lo = min(w.lo, seq);
-  const int a_hi = max(a_lo, min(w.hi, seq));
-  const int n_extra = a_lo + (seq - a_hi);
-  const int x0 = (int)((int64_t)n_extra * s / kSplits);
-  const int n_att = n_list + (int)((int64_t)n_extra * (s + 1) / kSplits) - x0;
-#pragma unroll
-  for (int u = 0; u < kSweep / 16 / kRowThreads; ++u) tbl[threadIdx.x + u * kRowThreads] = tb[u];
-  lds_barrier();   // lst and tbl are complete
 
   float m_run = -INFINITY, l_run = 0.f;   // head n (lanes n < G, every g4)
   float acc[GMAX][2];                     // dims 2 lane, 2 lane + 1 of every head
@@ -164,7 +81,7 @@ __global__ __launch_bounds__(kRowThreads) void select_attend_kernel(
       }
       int64_t slot = -1;
       if (t >= 0) {
-        if (n_blk) {
+        if (tbl) {
           const int e = t < seq ? tbl[t >> 4] : -1;
           slot = e < 0 ? -1 : (int64_t)e * 16 + (t & 15);
         } else {
@@ -281,7 +198,7 @@ __global__ __launch_bounds__(kRowThreads) void select_attend_kernel(
           aa += red[v][gi][j] * cw;
         }
       }
-      float* dst = part + (((int64_t)row * G + g) * kSplits + s) * stride;
+      float* dst = part + (((int64_t)row * G + g) * n_split + s) * stride;
       dst[j] = aa;
       if (j == 0) {
         dst[kD] = mm;
@@ -289,6 +206,111 @@ __global__ __launch_bounds__(kRowThreads) void select_attend_kernel(
       }
     }
   }
+}
+
+template <int GMAX>
+__global__ __launch_bounds__(kRowThreads) void select_attend_kernel(
+    KvArgs kv, const uint16_t* q, int G, const float* scores, const int32_t* lo_p,
+    const int32_t* hi_p, int k, const uint32_t* ghist, float scale_log2, int32_t* idx,
+    int32_t* count, float* part) {
+  __shared__ RowSelLds L;
+  __shared__ int32_t lst[kShareCap];                // this workgroup's share of the selection
+  __shared__ int64_t rows_sh[kRowWaves][2][16];     // per wave: key-row offsets of two chunks
+  __shared__ float red[kRowWaves][4][kD + 2];       // merge of the waves, 4 heads a round
+  __shared__ int32_t tbl[kSweep / 16];              // the row's block-table entries (paged)
+  // the kSplits workgroups of a row run on one XCD and share its scores in L2
+  const int vid = xcd_remap(blockIdx.x, gridDim.x);
+  const int s = vid % kSplits, row = vid / kSplits;
+  const int b = row / kv.H, h = row - b * kv.H;
+  const int lane = threadIdx.x & 63, wave = row_wave();
+  const int n = lane & 15, g4 = lane >> 4;
+  RowWindow w = row_window(lo_p, hi_p, b, kv.L_max);
+  bool vec;
+  const float* srow = row_base(scores, (int64_t)row * kv.L_max, w, &vec);
+
+  // 1. the row's threshold (histogram first, then the scores)
+  const uint4 gv = ((const uint4*)(ghist + (int64_t)row * kBins))[threadIdx.x];
+  float fv[kGroups][4];
+  row_load(srow, w, vec, 0, fv);
+  // the block-table row, kept in registers until the attention needs it
+  const int n_blk = kv.block_table ? kv.L_max >> 4 : 0;
+  int32_t tb[kSweep / 16 / kRowThreads];
+#pragma unroll
+  for (int u = 0; u < kSweep / 16 / kRowThreads; ++u) {
+    const int i = threadIdx.x + u * kRowThreads;
+    tb[u] = i < n_blk ? kv.block_table[(int64_t)b * n_blk + i] : -1;
+  }
+  // the query rows (MFMA B operand of the logits), also needed only later
+  bf16x8_t Qf[4];
+  {
+    const uint16_t* qrow = q + ((int64_t)row * G + (n < G ? n : 0)) * kD;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const u32x4_t v = n < G ? ld16((const char*)(qrow + 8 * (4 * j + g4))) : u32x4_t{0, 0, 0, 0};
+      Qf[j] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+  uint32_t kr[kGroups][4];
+  *(uint4*)(L.hist + 4 * threadIdx.x) = gv;
+  if (threadIdx.x < 256) L.dh[threadIdx.x] = 0u;
+  lds_barrier();
+  uint32_t T;
+  int need_eq, k_sel;
+  row_threshold(
+      L, k, [&]() { row_keys(fv, kr); },
+      [&](auto&& f) {
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) f(kr[g][e]);
+      },
+      &T, &need_eq, &k_sel);
+
+  // 2. ranks.  Workgroup s writes idx and lists in LDS the selected keys of
+  //    ranks [r0, r1), an equal share of the k_sel selected keys
+  int32_t* orow = idx + (int64_t)row * k;
+  int n_list;
+  {
+    int cg[kGroups];
+    const int lt = row_counts(kr, T, cg);
+    int oa, oe, ta, te;
+    row_wave_offsets(L, lt, &oa, &oe, &ta, &te);
+    const int r0 = (int)((int64_t)k_sel * s / kSplits);
+    const int r1 = (int)((int64_t)k_sel * (s + 1) / kSplits);
+    n_list = r1 - r0;
+    // ranks of this wave's selected keys: [first, last)
+    const int first = oa + min(oe, need_eq);
+    const int last = oa + L.wa[wave] + min(oe + L.we[wave], need_eq);
+    if (first < r1 && last > r0) {
+      const int pos0 = w.lo - w.o + wave * kSeg + 4 * lane;
+      row_emit(kr, cg, T, need_eq, oa, oe, [&](int dst, int g, int e) {
+        if (dst >= r0 && dst < r1) {
+          const int t = pos0 + 256 * g + e;
+          orow[dst] = t;
+          lst[dst - r0] = t;
+        }
+      });
+    }
+    if (s == 0) {
+      const int n_sel = min(k, ta + min(te, need_eq));   // == k_sel
+      for (int i = n_sel + threadIdx.x; i < k; i += kRowThreads) orow[i] = -1;
+      if (threadIdx.x == 0) count[row] = n_sel;
+    }
+  }
+
+  // 3. attention over the listed keys plus this workgroup's share of the
+  //    always-attended tokens t < lo and t >= hi (live ones)
+  const int seq = min(kv.seq_len[b], kv.L_max);
+  const int a_lo = min(w.lo, seq);
+  const int a_hi = max(a_lo, min(w.hi, seq));
+  const int n_extra = a_lo + (seq - a_hi);
+  const int x0 = (int)((int64_t)n_extra * s / kSplits);
+  const int n_att = n_list + (int)((int64_t)n_extra * (s + 1) / kSplits) - x0;
+#pragma unroll
+  for (int u = 0; u < kSweep / 16 / kRowThreads; ++u) tbl[threadIdx.x + u * kRowThreads] = tb[u];
+  lds_barrier();   // lst and tbl are complete
+  attend_share<GMAX>(kv, G, row, b, h, s, kSplits, lst, n_list, x0, n_att, a_lo, a_hi, seq,
+                     n_blk ? tbl : nullptr, Qf, scale_log2, part, rows_sh, red);
 }
 
 }  // namespace

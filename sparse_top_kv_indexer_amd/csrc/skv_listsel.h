@@ -339,6 +339,19 @@ __device__ __forceinline__ int list_select(const TopkWs& ws, int row, int k, int
   return min(k, ta + min(te, need_eq));
 }
 
+// The selection of a row whose list overflowed, for kernels that finish the
+// selection themselves: the row alone, re-read per digit, the positions left
+// in L.hist[0 .. n) ascending (k <= 4096).  Rare; kept out of line so its
+// registers do not weigh on the attention that follows.
+__device__ __noinline__ int fallback_select(const float* scores, int row, int H, int L_max,
+                                           const int32_t* lo_p, const int32_t* hi_p, int k,
+                                           uint32_t* ghist_row, RowSelLds& L, int& klist_n,
+                                           uint4 gv) {
+  return row_select_alone<false, 3>(scores, row, H, L_max, lo_p, hi_p, k, ghist_row, true, nullptr,
+                                    nullptr, nullptr, nullptr, 0, L, nullptr, klist_n, nullptr,
+                                    true, gv);
+}
+
 // This thread's 4 bins (4 t .. 4 t + 3) of row `row`'s first-digit
 // histogram, summed over its copies (few rows have more than one).
 __device__ __forceinline__ uint4 hist_bins_summed(const TopkWs& ws, int row) {

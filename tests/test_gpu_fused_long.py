@@ -1,10 +1,13 @@
-"""GPU parity of the exact top-k finished inside the attention kernel for rows
-longer than one 32768-slot sweep (sparsekv_select_attend_resume after
-sparsekv_score_hist): the slice listing, then every attending workgroup
-resolves the row's selection from the list itself.  Checked against the
-float64 oracle (selection set, attention within 2e-3) and against the
-separate calls, including a row whose candidate list overflows (many tied
-scores) so that the selection falls back to reading the row per digit."""
+"""GPU parity of the fused decode-step calls for rows longer than one
+32768-slot sweep.  The latent attention (sparsekv_select_attend_resume after
+the indexer's sparsekv_score_hist) finishes the exact top-k inside the
+attention kernel: the slice listing, then every attending workgroup resolves
+the row's selection from the list itself.  GQA rows (sparsekv_select_attend
+and its resume) take the slice-listing top-k and the split attention inside
+the same call.  Checked against the float64 oracle (selection set, attention
+within 2e-3) and against the separate calls, including rows whose candidate
+list overflows (many tied scores) so that the selection falls back to reading
+the row per digit."""
 import numpy as np
 import pytest
 import torch
@@ -104,3 +107,67 @@ def test_fused_latent_full_size():
     """The indexer + shared-latent workload at L = 131072, top-2048, 128 heads."""
     st = W.make_indexer_mla()
     assert _check(st) == 0
+
+
+# ------------------------------------------------------- GQA rows, long
+def _check_gqa(st, rows=None):
+    """The fused call on long GQA rows against the oracle and against
+    resume-after-scan."""
+    say("fused long GQA", st.name, "G", st.G, "L", st.kv.L_max, "k", st.k, st.kv.mode)
+    r = Run(st)
+    sc, idx, cnt, out = [t.cpu().numpy() for t in r.select_attend()]
+    B, H = st.kv.B, st.kv.H
+    rows = [(b, h) for b in range(B) for h in range(H)] if rows is None else rows
+    ref = D.step(st, rows=rows)
+    swaps = 0
+    for b, h in rows:
+        sel = ref["idx"][b, h][: ref["count"][b, h]]
+        assert cnt[b, h] == ref["count"][b, h], (b, h)
+        sw = check_selection(ref["scores"][b, h], sel, idx[b, h], cnt[b, h])
+        swaps += sw
+        if sw == 0:
+            hs = list(range(h * st.G, (h + 1) * st.G))
+            err = np.abs(out[b, hs] - ref["out"][b, hs]).max()
+            assert err <= ATTN_TOL, (b, h, err)
+    _, idx2, cnt2, out2, _ = _resume(r)
+    assert np.array_equal(idx, idx2.cpu().numpy()) and np.array_equal(cnt, cnt2.cpu().numpy())
+    assert np.abs(out - out2.cpu().numpy()).max() <= ATTN_TOL
+    return swaps
+
+
+@pytest.mark.parametrize("G,L,k", [(4, 40000, 2048), (1, 65536, 100), (8, 33024, 4096)])
+def test_fused_gqa_long_paged(G, L, k):
+    st = W.make_gqa_paged(tag=720 + G, B=2, H=2, G=G, L=L, k=k, sink=4, local=64,
+                          seq_len=[L, L - 777])
+    assert _check_gqa(st) == 0
+
+
+def test_fused_gqa_long_token_table():
+    st = W.make_token_pool(tag=730, B=3, H=2, L=65536, k=2048, sink=4, local=128)
+    assert _check_gqa(st) == 0
+
+
+def test_fused_gqa_long_list_overflow_fallback():
+    """Every key of sequence 0 ties: its list overflows and each attending
+    workgroup selects from the row itself (lowest positions win)."""
+    st = W.make_gqa_paged(tag=731, B=2, H=1, G=2, L=40960, k=1500, sink=4, local=64)
+    blocks = st.kv.block_table[0]
+    st.kv.k[blocks] = st.kv.k[blocks[0], :, 0:1, :]
+    assert _check_gqa(st) == 0
+    r = Run(st)
+    _, idx, cnt, _ = r.select_attend()
+    assert int(cnt[0, 0]) == 1500 and idx[0, 0].cpu().numpy().tolist() == list(range(4, 1504))
+
+
+@pytest.mark.slow
+def test_fused_gqa_long_full_size_every_row():
+    """The GQA decode at L = 131072 through the fused call, all 32 rows."""
+    st = W.make_gqa_paged(L=131072)
+    assert _check_gqa(st) == 0
+
+
+@pytest.mark.slow
+def test_fused_token_pool_full_size_64_rows_over_every_head():
+    st = W.make_token_pool()
+    rows = [(b, (b + 4 * j) % 8) for b in range(32) for j in range(2)]
+    assert _check_gqa(st, rows=rows) == 0

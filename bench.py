@@ -345,12 +345,13 @@ def stream_reference():
             t.append(e0.elapsed_time(e1) * 1e-3)
         return nbytes / min(t) / 1e9
 
-    read = max(best(lambda: S.sparsekv_read_probe(x, g, sink), 4 * n) for g in (1024, 2048, 4096, 8192))
+    from sparse_top_kv_indexer_amd import yardstick as Y
+    read = max(best(lambda: Y.read_probe(x, g, sink), 4 * n) for g in (1024, 2048, 4096, 8192))
     copy = best(lambda: y.copy_(x[: n // 2]), 2 * 4 * (n // 2))
     del x, y, sink
     torch.cuda.empty_cache()
     return {"stream_read_GBps": read, "stream_copy_GBps": copy,
-            "stream_note": "sparsekv_read_probe over 2 GiB (reads only, best grid of 1024..8192 "
+            "stream_note": "skv_read_probe (libskv_yardstick) over 2 GiB (reads only, best grid of 1024..8192 "
                            "workgroups) and a torch 1 GiB device copy (read + write), best of 10"}
 
 

@@ -500,14 +500,6 @@ skv_status sparsekv_retrieve(const skv_codebook* cb, const skv_index* index, con
                              int32_t* n_cand, const skv_retrieve_trace* trace, void* ws,
                              size_t ws_bytes, hipStream_t stream);
 
-/* Streaming-read yardstick (not part of the decode step): reads `bytes`
- * (a multiple of 16) of the device buffer once with n_wg workgroups of 256
- * threads and writes one folded word per workgroup to sink (device
- * [n_wg]).  Its duration measures what a plain read reaches on the device,
- * the second yardstick beside the published HBM peak. */
-skv_status sparsekv_read_probe(const void* buf, size_t bytes, int32_t n_wg, uint32_t* sink,
-                               hipStream_t stream);
-
 /* ------------------------------------------------------------ validation --
  * Checks of the device-resident data the other calls take on trust (vToken
  * reading notes, section 3.5 invariant I2: every live token maps to a valid

@@ -110,7 +110,6 @@ _SIGS = {
     "sparsekv_live_hash": (c_i32, [ctypes.POINTER(skv_kv), c_vp, c_vp, c_vp]),
     "sparsekv_check_unique_ws_bytes": (c_sz, [c_i32]),
     "sparsekv_check_unique": (c_i32, [ctypes.POINTER(skv_kv), c_i32, c_vp, c_vp, c_sz, c_vp]),
-    "sparsekv_read_probe": (c_i32, [c_vp, c_sz, c_i32, c_vp, c_vp]),
     "sparsekv_codebook_init": (c_i32, [c_i32, ctypes.POINTER(c_f32), ctypes.POINTER(c_f32)]),
     "sparsekv_encode": (c_i32, [ctypes.POINTER(skv_codebook), ctypes.POINTER(skv_kv), c_i32,
                                 c_i32, c_i32, ctypes.POINTER(skv_index), c_vp]),
@@ -553,17 +552,6 @@ def sparsekv_check_unique(kv: KVTensors, n_blocks: int, result: Optional[torch.T
            lib().sparsekv_check_unique(ctypes.byref(c), n_blocks, _ptr(result), _ptr(ws),
                                        ws.numel() * ws.element_size(), _stream()))
     return result
-
-
-def sparsekv_read_probe(buf: torch.Tensor, n_wg: int, sink: Optional[torch.Tensor] = None):
-    """Read buf once (streaming-read yardstick); returns the sink words."""
-    _dev(buf, "buf")
-    if sink is None:
-        sink = torch.empty(n_wg, dtype=torch.int32, device=buf.device)
-    _check("sparsekv_read_probe",
-           lib().sparsekv_read_probe(_ptr(buf), buf.numel() * buf.element_size(), n_wg, _ptr(sink),
-                                     _stream()))
-    return sink
 
 
 def sparsekv_score_hist(kv: KVTensors, q: torch.Tensor, G: int, lo: torch.Tensor,

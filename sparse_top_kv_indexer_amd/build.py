@@ -21,6 +21,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libsparsekv.so")
 LIB_DEBUG = os.path.join(HERE, "libsparsekv_debug.so")
+YARDSTICK = os.path.join(HERE, "libskv_yardstick.so")
 BUILD = os.path.join(ROOT, "_build")
 BUILD_DEBUG = os.path.join(ROOT, "_build_debug")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -69,6 +70,21 @@ def build(verbose: bool = True, debug: bool = False) -> str:
     return lib
 
 
+def build_yardstick(verbose: bool = True) -> str:
+    """libskv_yardstick.so: the streaming-read probe beside the library."""
+    src = os.path.join(HERE, "yardstick", "read_probe.hip")
+    tmp = YARDSTICK + ".tmp"
+    cmd = [HIPCC] + COMMON + ["-shared", src, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed for read_probe.hip:\n" + r.stdout + r.stderr)
+    os.replace(tmp, YARDSTICK)
+    if verbose:
+        print("built", YARDSTICK)
+    return YARDSTICK
+
+
 if __name__ == "__main__":
     build()
     build(debug=True)
+    build_yardstick()

@@ -1,12 +1,16 @@
 // Streaming-read yardstick: reads a buffer once with 16-byte loads, four in
 // flight per thread, and folds the words into one value per workgroup so the
-// loads are not dead.  Not part of the decode step: it measures what a plain
-// read reaches on the device, the second yardstick beside the HBM peak.
-#include "../../include/sparsekv.h"
-#include "skv_device.h"
+// loads are not dead.  Not part of the decode step or its library: it
+// measures what a plain read reaches on the device, the second yardstick
+// beside the HBM peak (built as libskv_yardstick.so).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
 
-namespace skv {
+#include "../../include/skv_yardstick.h"
+
 namespace {
+
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
 
 __global__ __launch_bounds__(256) void read_probe_kernel(const u32x4_t* p, int64_t n16,
                                                          uint32_t* sink) {
@@ -31,16 +35,14 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const u32x4_t* p, int64
 }
 
 }  // namespace
-}  // namespace skv
 
 extern "C" {
 
-skv_status sparsekv_read_probe(const void* buf, size_t bytes, int32_t n_wg, uint32_t* sink,
-                               hipStream_t stream) {
-  if (!buf || !sink || bytes < 16 || bytes % 16 || n_wg < 1) return SKV_EINVAL;
-  skv::read_probe_kernel<<<n_wg, 256, 0, stream>>>((const skv::u32x4_t*)buf,
-                                                   (int64_t)(bytes / 16), sink);
-  return hipGetLastError() == hipSuccess ? SKV_OK : SKV_ELAUNCH;
+int32_t skv_read_probe(const void* buf, size_t bytes, int32_t n_wg, uint32_t* sink,
+                       hipStream_t stream) {
+  if (!buf || !sink || bytes < 16 || bytes % 16 || n_wg < 1) return 1;
+  read_probe_kernel<<<n_wg, 256, 0, stream>>>((const u32x4_t*)buf, (int64_t)(bytes / 16), sink);
+  return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 
 }  // extern "C"

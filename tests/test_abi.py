@@ -212,3 +212,17 @@ def test_validate_checks_host_arguments_first():
     assert L.sparsekv_validate(ctypes.byref(kv), win, None, 0, P, P, 16, None) == S.SKV_EWORKSPACE
     bad = _kv(B=2, H=2, L_max=64, block=16, token_table=1, n_blocks=-1)
     assert L.sparsekv_validate(ctypes.byref(bad), win, None, 0, P, P, 1 << 20, None) == S.SKV_EINVAL
+
+
+def test_yardstick_is_a_library_of_its_own():
+    """The streaming-read probe is not exported by the decode-step library;
+    its own library exports what its header declares and checks arguments."""
+    txt = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "skv_yardstick.h")).read(),
+                 flags=re.S)
+    names = sorted(set(re.findall(r"\b(skv_\w+)\s*\(", txt)))
+    assert names == ["skv_read_probe"]
+    assert not hasattr(ctypes.CDLL(S.LIB_PATH), "sparsekv_read_probe")
+    from sparse_top_kv_indexer_amd import yardstick as Y
+    L = Y.lib()
+    assert L.skv_read_probe(None, 16, 1, ctypes.c_void_p(1), None) == 1
+    assert L.skv_read_probe(ctypes.c_void_p(1), 24, 1, ctypes.c_void_p(1), None) == 1

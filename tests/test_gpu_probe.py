@@ -1,11 +1,11 @@
-"""The streaming-read yardstick (sparsekv_read_probe) reads every byte once:
+"""The streaming-read yardstick (skv_read_probe, libskv_yardstick) reads every byte once:
 each workgroup's folded word equals the XOR of the 16-byte units it owns
 (unit u belongs to workgroup (u // 256) % n_wg), computed here on the host."""
 import numpy as np
 import pytest
 import torch
 
-import sparse_top_kv_indexer_amd as S
+from sparse_top_kv_indexer_amd import yardstick as Y
 
 from gpu_helpers import DEV
 
@@ -17,7 +17,7 @@ def test_read_probe_folds_every_word(n_units, n_wg):
     rng = np.random.default_rng(n_units)
     host = rng.integers(0, 2 ** 32, size=(n_units, 4), dtype=np.uint64).astype(np.uint32)
     buf = torch.from_numpy(host.view(np.int32)).to(DEV)
-    got = S.sparsekv_read_probe(buf, n_wg).cpu().numpy().view(np.uint32)
+    got = Y.read_probe(buf, n_wg).cpu().numpy().view(np.uint32)
     owner = (np.arange(n_units) // 256) % n_wg
     for g in range(n_wg):
         words = host[owner == g].ravel()

@@ -226,19 +226,21 @@ def timed_steps(step, n_calls, args, hip):
 # while these files are byte-identical to the ones it was taken on.
 CSRC = "sparse_top_kv_indexer_amd/csrc/"
 _COMMON = [CSRC + "skv_device.h", CSRC + "skv_internal.h"]
+_SEL = [CSRC + "skv_rowsel.h", CSRC + "skv_topk.h"]
+_SCAN = [CSRC + "score.hip", CSRC + "skv_topk.h"] + _COMMON
+_TOPK = [CSRC + "topk.hip", CSRC + "skv_listsel.h"] + _SEL + _COMMON
+_ATT = [CSRC + "attend.hip", CSRC + "skv_topk.h"] + _COMMON
+_MLA = [CSRC + "mla.hip", CSRC + "skv_listsel.h"] + _SEL + _COMMON
+_PARIS = [CSRC + "paris.hip", "include/sparsekv.h"] + _SEL + _COMMON
 KERNEL_SOURCES = {
-    "score_stream_kernel": [CSRC + "score.hip", CSRC + "skv_topk.h"] + _COMMON,
-    "score_valu_kernel": [CSRC + "score.hip", CSRC + "skv_topk.h"] + _COMMON,
-    "attend_mfma_kernel": [CSRC + "attend.hip"] + _COMMON,
-    "attend_split_kernel": [CSRC + "attend.hip"] + _COMMON,
-    "attend_reduce_kernel": [CSRC + "attend.hip"] + _COMMON,
-    "select_attend_kernel": [CSRC + "select_attend.hip", CSRC + "skv_rowsel.h",
-                             CSRC + "skv_topk.h"] + _COMMON,
-    "mla_split_kernel": [CSRC + "mla.hip"] + _COMMON,
-    "vote_kernel": [CSRC + "paris.hip"] + _COMMON,
-    "rerank_kernel": [CSRC + "paris.hip"] + _COMMON,
-    "query_lut_kernel": [CSRC + "paris.hip"] + _COMMON,
-    "cand_write_kernel": [CSRC + "paris.hip"] + _COMMON,
+    "score_stream_kernel": _SCAN, "score_valu_kernel": _SCAN,
+    "topk_alone_kernel": _TOPK, "topk_compact_kernel": _TOPK, "topk_finish_kernel": _TOPK,
+    "topk_hist_kernel": _TOPK, "topk_survivor_kernel": _TOPK,
+    "attend_mfma_kernel": _ATT, "attend_split_kernel": _ATT, "attend_reduce_kernel": _ATT,
+    "select_attend_kernel": [CSRC + "select_attend.hip"] + _SEL + _COMMON,
+    "mla_split_kernel": _MLA, "mla_list_kernel": _MLA,
+    "query_lut_kernel": _PARIS, "vote_kernel": _PARIS, "cand_write_kernel": _PARIS,
+    "rerank_kernel": _PARIS, "encode_kernel": _PARIS,
 }
 
 
@@ -664,7 +666,8 @@ def bench_blocks(args, hip, st, kv, q, lo, hi):
 
 
 # ------------------------------------------------------------------ paris
-RETRIEVE_KERNELS = ("query_lut_kernel", "vote_kernel", "cand_write_kernel", "rerank_kernel")
+RETRIEVE_KERNELS = ("query_lut_kernel", "vote_kernel", "cand_write_kernel", "rerank_kernel",
+                    "topk_alone_kernel")
 
 
 def paris_cpu_baseline(min_seconds):

@@ -400,23 +400,24 @@ __global__ __launch_bounds__(kThreads) void attend_mfma_kernel(
 }
 
 // out[b][hq][j] = sum_s acc_s[j] 2^(m_s - M) / sum_s l_s 2^(m_s - M)
-// One workgroup per (b, query head); a thread owns two dims and loads them
-// from 16 splits at a time, the first 16 in flight while the split weights
+// Grid (query heads, B, ceil(D / 256)): a workgroup owns 256 dims of one
+// (b, query head), a thread one dim, whose values it loads from 32 splits at
+// a time -- all of them for n_split <= 32, in flight while the split weights
 // are formed (n_split <= 64, D <= 512).
-// With zero_hist != nullptr, the workgroup of the first query head of each KV
-// head also zeroes that row's copies of the 4096-bin key histogram and, with
-// ctr != nullptr, the row's list counter (ctr[row * kCtrStride]): the fused
-// top-k + attention paths leave them for this kernel, which runs after every
-// reader.
+// With zero_hist != nullptr, the first workgroup of the first query head of
+// each KV head also zeroes that row's copies of the 4096-bin key histogram
+// and, with ctr != nullptr, the row's list counter (ctr[row * kCtrStride]):
+// the fused top-k + attention paths leave them for this kernel, which runs
+// after every reader.
 __global__ __launch_bounds__(256) void attend_reduce_kernel(const float* part, int n_split, int D,
                                                            int HG, float* out, uint32_t* zero_hist,
                                                            int G, int copies, int32_t* ctr) {
-  constexpr int SG = 16;                 // splits whose values are loaded together
-  constexpr int ND = 2;                  // dims per thread (D <= 512)
+  constexpr int SG = 32;                 // splits whose values are loaded together
   __shared__ float wts[64];
   __shared__ float inv_l;
   const int hq = blockIdx.x, b = blockIdx.y;
-  if (zero_hist && hq % G == 0) {
+  const int j = blockIdx.z * 256 + threadIdx.x;
+  if (zero_hist && hq % G == 0 && blockIdx.z == 0) {
     const int64_t row = (int64_t)b * (HG / G) + hq / G;
     uint4* z = (uint4*)(zero_hist + row * copies * 4096);
     for (int i = threadIdx.x; i < 1024 * copies; i += blockDim.x) z[i] = make_uint4(0u, 0u, 0u, 0u);
@@ -424,16 +425,11 @@ __global__ __launch_bounds__(256) void attend_reduce_kernel(const float* part, i
   }
   const int stride = D + 2;
   const float* base = part + ((int64_t)b * HG + hq) * n_split * stride;
-  // the first group's values are in flight while the split weights are formed
-  float v[SG][ND];
+  float v[SG];
   auto load_group = [&](int s0) {
 #pragma unroll
     for (int u = 0; u < SG; ++u)
-#pragma unroll
-      for (int d = 0; d < ND; ++d) {
-        const int j = threadIdx.x + 256 * d;
-        v[u][d] = (s0 + u < n_split && j < D) ? base[(int64_t)(s0 + u) * stride + j] : 0.f;
-      }
+      v[u] = (s0 + u < n_split && j < D) ? base[(int64_t)(s0 + u) * stride + j] : 0.f;
   };
   load_group(0);
   if (threadIdx.x < 64) {
@@ -449,21 +445,13 @@ __global__ __launch_bounds__(256) void attend_reduce_kernel(const float* part, i
     if (s == 0) inv_l = L > 0.f ? 1.f / L : 0.f;
   }
   __syncthreads();
-  float acc[ND] = {0.f, 0.f};
+  float acc = 0.f;
   for (int s0 = 0; s0 < n_split; s0 += SG) {
     if (s0) load_group(s0);
 #pragma unroll
-    for (int u = 0; u < SG; ++u) {
-      const float w = s0 + u < n_split ? wts[s0 + u] : 0.f;
-#pragma unroll
-      for (int d = 0; d < ND; ++d) acc[d] += v[u][d] * w;
-    }
+    for (int u = 0; u < SG; ++u) acc += v[u] * (s0 + u < n_split ? wts[s0 + u] : 0.f);
   }
-#pragma unroll
-  for (int d = 0; d < ND; ++d) {
-    const int j = threadIdx.x + 256 * d;
-    if (j < D) out[((int64_t)b * HG + hq) * D + j] = acc[d] * inv_l;
-  }
+  if (j < D) out[((int64_t)b * HG + hq) * D + j] = acc * inv_l;
 }
 
 template <bool BF16, int NPL>
@@ -542,7 +530,7 @@ hipError_t launch_attend_reduce(const float* part, int n_split, int D, int HG, i
                                 hipStream_t st, uint32_t* zero_hist, int G, int copies,
                                 int32_t* ctr) {
   if (n_split > 64 || D > 512) return hipErrorInvalidValue;
-  dim3 grid(HG, B);
+  dim3 grid(HG, B, (D + 255) / 256);
   attend_reduce_kernel<<<grid, 256, 0, st>>>(part, n_split, D, HG, out, zero_hist, G, copies, ctr);
   return hipGetLastError();
 }

@@ -313,7 +313,11 @@ __global__ __launch_bounds__(256) void query_lut_kernel(const uint16_t* q, int G
 // (a byte never exceeds 96, so the four sums never carry into each other).
 // The workgroup histograms its S values (32 bank-spread copies in LDS) and
 // writes the suffix counts ge[v] = #(S >= v), v = 0..97, of its chunk, which
-// it also adds into the head's totals.
+// it also adds into the head's totals.  A thread takes 4 entries per round
+// (8 rounds), the next round's loads in flight during the lookups: 8 entries
+// per round took 40 us against 37 us on 8 x 1M entries, and spreading a
+// wave's lookups over the 16 tables (ids rotated per lane so that lanes hit
+// different banks) cost more ALU than the bank conflicts it saved (41-52 us).
 __global__ __launch_bounds__(256) void vote_kernel(const uint8_t* ids, int cap, int n,
                                                    const uint32_t* lut, uint8_t* votes, int ldv,
                                                    uint8_t* votes_trace, int32_t* chunk_ge,
@@ -328,7 +332,7 @@ __global__ __launch_bounds__(256) void vote_kernel(const uint8_t* ids, int cap, 
   for (int u = 0; u < 4; ++u) lv[u] = lsrc[u * 256 + tid];
   const int i0 = chunk * kChunk;
   const u32x4_t* idrow = (const u32x4_t*)(ids + (int64_t)h * cap * kSub);
-  constexpr int U = 8;                        // entries per thread per round
+  constexpr int U = 4;                        // entries per thread per round
   constexpr int R = kChunk / (256 * U);       // rounds
   u32x4_t cur[U];
 #pragma unroll

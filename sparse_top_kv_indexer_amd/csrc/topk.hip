@@ -104,16 +104,39 @@ __global__ __launch_bounds__(kSliceThreads) void topk_hist_kernel(const float* s
 }
 
 // -------------------------------------------------------------- listing --
-// Grid rows * slices of NG groups per lane, 256 threads; COPIES: the rows'
-// histogram copies (ws.copies), a compile-time constant so that one copy
-// costs no registers for the others.
+// Workgroups of the listing: rows * slices, or with 8 rows or more
+// ceil(rows / 8) * 8 * slices, mapped so that the slices of a row run on one
+// XCD (workgroups go to the 8 XCDs round-robin by id): every slice reads its
+// row's whole histogram, and each XCD's L2 then fetches the histograms of its
+// own rows only, not of every row.  Fewer rows spread their slices over all
+// XCDs.
+inline int64_t listing_wgs(int rows, int n_slices) {
+  return rows >= 8 ? (int64_t)((rows + 7) / 8) * 8 * n_slices : (int64_t)rows * n_slices;
+}
+__device__ __forceinline__ void listing_slot(int rows, int n_slices, int& row, int& sl) {
+  const int x = blockIdx.x;
+  if (rows >= 8) {
+    const int per = 8 * n_slices, grp = x / per, rem = x - grp * per;
+    row = grp * 8 + (rem & 7);
+    sl = rem >> 3;
+  } else {
+    row = x / n_slices;
+    sl = x - row * n_slices;
+  }
+}
+
+// Grid listing_wgs(rows, slices of NG groups per lane), 256 threads; COPIES:
+// the rows' histogram copies (ws.copies), a compile-time constant so that one
+// copy costs no registers for the others.
 template <int NG, int COPIES>
 __global__ __launch_bounds__(kSliceThreads) void topk_compact_kernel(
-    const float* scores, int H, int L_max, const int32_t* lo_p, const int32_t* hi_p, int k,
-    TopkWs ws, int n_slices) {
+    const float* scores, int rows, int H, int L_max, const int32_t* lo_p, const int32_t* hi_p,
+    int k, TopkWs ws, int n_slices) {
   __shared__ int wsum[4], wlist[4];
   __shared__ int sh[3];   // smallest listed key, listed count, this slice's list offset
-  const int row = blockIdx.x / n_slices, sl = blockIdx.x - row * n_slices;
+  int row, sl;
+  listing_slot(rows, n_slices, row, sl);
+  if (row >= rows) return;   // the padding workgroups of the last group of 8 rows
   const int lane = threadIdx.x & 63, wave = row_wave();
   const SliceView v = slice_view<NG>(scores, row, H, L_max, lo_p, hi_p, sl);
   const bool any = sl * kSliceUnit * NG < v.w.ns;
@@ -479,11 +502,12 @@ hipError_t launch_topk_listing(const float* scores, int rows, int H, int L_max, 
   const TopkWs ws = TopkWs::carve(wsp, rows, L_max);
   const int ng_l = topk_slice_groups(rows, L_max);
   const int ns = topk_slices_ng(L_max, ng_l);
-  if (ns > kMaxSlices || ns > topk_slices(L_max) || (int64_t)rows * ns > 0x7fffffff)
+  if (ns > kMaxSlices || ns > topk_slices(L_max) || listing_wgs(rows, ns) > 0x7fffffff)
     return hipErrorInvalidValue;
   if (ws.copies != 1 && ws.copies != kHistCopiesMax) return hipErrorInvalidValue;
   auto list = [&](auto kern) {
-    kern<<<(unsigned)(rows * ns), kSliceThreads, 0, s>>>(scores, H, L_max, lo, hi, k, ws, ns);
+    kern<<<(unsigned)listing_wgs(rows, ns), kSliceThreads, 0, s>>>(scores, rows, H, L_max, lo, hi,
+                                                                  k, ws, ns);
   };
   auto by_ng = [&](auto copies_c) {
     constexpr int CP = decltype(copies_c)::value;

@@ -772,8 +772,8 @@ def bench_paris(args, hip):
     base = indexes[0]
     ixs = [base]
     for _ in range(max(1, args.kv_copies) - 1):
-        ixs.append(dataclasses.replace(base, ids=base.ids.clone(), codes=base.codes.clone(),
-                                       w=base.w.clone(), hist=base.hist.clone(), pos=base.pos.clone()))
+        ixs.append(dataclasses.replace(base, ids=base.ids.clone(), cw=base.cw.clone(),
+                                       hist=base.hist.clone(), pos=base.pos.clone()))
     kvs = [kv] + [dataclasses.replace(kv, k=kv.k.clone(), v=kv.v.clone())
                   for _ in range(max(1, args.kv_copies) - 1)]
     q = S.to_device(p.q, dev, bf16=True)

@@ -423,8 +423,12 @@ typedef struct {                /* host struct */
 
 typedef struct {                /* host struct, device arrays */
   uint8_t* ids;                 /* [H][cap][n_sub] centroid id per subspace   */
-  uint8_t* codes;               /* [H][cap][d/2]   coordinate 2c = low nibble */
-  float* w;                     /* [H][cap][n_sub] correction weights         */
+  uint32_t* cw;                 /* [H][cap][n_sub][2]: per subspace its codes
+                                   word (coordinate c of the subspace in bits
+                                   4c..4c+3: sign bit 3, magnitude bits 0-2)
+                                   then its correction weight w (fp32 bits);
+                                   an entry's 16 pairs fill one 128-byte line,
+                                   so the rerank reads one line per candidate */
   int32_t* hist;                /* [H][n_sub][256] entries per centroid       */
   int32_t* pos;                 /* [cap] logical position of each entry       */
   int32_t n, cap, H;            /* n entries in use (host-side count)         */

@@ -60,7 +60,7 @@ class skv_codebook(ctypes.Structure):
 
 
 class skv_index(ctypes.Structure):
-    _fields_ = [("ids", c_vp), ("codes", c_vp), ("w", c_vp), ("hist", c_vp), ("pos", c_vp),
+    _fields_ = [("ids", c_vp), ("cw", c_vp), ("hist", c_vp), ("pos", c_vp),
                 ("n", c_i32), ("cap", c_i32), ("H", c_i32)]
 
 
@@ -697,27 +697,36 @@ def sparsekv_version() -> int:
 class IndexTensors:
     """Device arrays of a compressed-code index (skv_index)."""
     ids: torch.Tensor     # uint8 [H][cap][n_sub]
-    codes: torch.Tensor   # uint8 [H][cap][d/2]
-    w: torch.Tensor       # float32 [H][cap][n_sub]
+    cw: torch.Tensor      # int32 [H][cap][n_sub][2]: codes word, then w (fp32 bits)
     hist: torch.Tensor    # int32 [H][n_sub][256]
     pos: torch.Tensor     # int32 [cap]
     n: int
     cap: int
     H: int
 
+    @property
+    def codes(self) -> torch.Tensor:
+        """A copy of the 4-bit codes as uint8 [H][cap][d/2] (coordinate 2c in
+        the low nibble of byte c)."""
+        H, cap, n_sub, _ = self.cw.shape
+        return self.cw[..., 0].contiguous().view(torch.uint8).reshape(H, cap, 4 * n_sub)
+
+    @property
+    def w(self) -> torch.Tensor:
+        """A copy of the correction weights as float32 [H][cap][n_sub]."""
+        return self.cw[..., 1].contiguous().view(torch.float32)
+
     def c(self) -> skv_index:
-        for t, nm in ((self.ids, "ids"), (self.codes, "codes"), (self.w, "w"), (self.hist, "hist"),
-                      (self.pos, "pos")):
+        for t, nm in ((self.ids, "ids"), (self.cw, "cw"), (self.hist, "hist"), (self.pos, "pos")):
             _dev(t, nm)
-        return skv_index(_ptr(self.ids), _ptr(self.codes), _ptr(self.w), _ptr(self.hist),
-                         _ptr(self.pos), self.n, self.cap, self.H)
+        return skv_index(_ptr(self.ids), _ptr(self.cw), _ptr(self.hist), _ptr(self.pos), self.n,
+                         self.cap, self.H)
 
 
 def new_index(H: int, cap: int, d: int = 128, n_sub: int = 16, device="cuda") -> IndexTensors:
     """An empty index (histogram zeroed) with room for `cap` entries per head."""
     return IndexTensors(ids=torch.empty((H, cap, n_sub), dtype=torch.uint8, device=device),
-                        codes=torch.empty((H, cap, d // 2), dtype=torch.uint8, device=device),
-                        w=torch.empty((H, cap, n_sub), dtype=torch.float32, device=device),
+                        cw=torch.empty((H, cap, n_sub, 2), dtype=torch.int32, device=device),
                         hist=torch.zeros((H, n_sub, 256), dtype=torch.int32, device=device),
                         pos=torch.empty((cap,), dtype=torch.int32, device=device),
                         n=0, cap=cap, H=H)

@@ -148,8 +148,8 @@ __device__ __forceinline__ void load_row8(const KvArgs& kv, int b, int h, int t,
 // 16 ids straight to the index histogram.
 __global__ __launch_bounds__(256) void encode_kernel(KvArgs kv, int b, int t0, int n_keys, int n0,
                                                      int cap, int per_wg, const int8_t* signs,
-                                                     CodebookArgs cb, uint8_t* ids, uint8_t* codes,
-                                                     float* w, int32_t* hist, int32_t* pos) {
+                                                     CodebookArgs cb, uint8_t* ids, uint32_t* cw,
+                                                     int32_t* hist, int32_t* pos) {
   __shared__ uint32_t lh[kSub * kCent];
   const int h = blockIdx.y;
   const int j = threadIdx.x & 15, grp = threadIdx.x >> 4;
@@ -197,8 +197,7 @@ __global__ __launch_bounds__(256) void encode_kernel(KvArgs kv, int b, int t0, i
     const float wv = r > 0.f ? __fdiv_rn(nrm * r, alpha) : 0.f;
     const int64_t ent = (int64_t)h * cap + n0 + key;
     ids[ent * kSub + j] = (uint8_t)id;
-    ((uint32_t*)codes)[ent * kSub + j] = code;
-    w[ent * kSub + j] = wv;
+    ((uint2*)cw)[ent * kSub + j] = make_uint2(code, __float_as_uint(wv));
     if (direct)
       atomicAdd(&gh[j * kCent + id], 1);
     else
@@ -521,7 +520,10 @@ __global__ __launch_bounds__(256) void cand_write_kernel(const uint8_t* votes, i
 // ------------------------------------------------------------------ rerank --
 // est_i = max_g fl(|q_g| * tree16_b fl(w_ib * tree8_j fl(v_ibj * q~_gbj))).
 // Grid (ceil(C / 256), H), 256 threads: a 16-lane group takes 16 consecutive
-// candidates, lane b holding subspace b of each.  A nibble's signed level
+// candidates, lane b holding subspace b of each (its codes word and weight,
+// one 8-byte load: a candidate's 16 lanes read one 128-byte line; with codes
+// and weights in separate arrays each candidate cost two lines and the
+// kernel 14.6 us at C = 20,962 x 8 heads).  A nibble's signed level
 // comes from a 16-entry LDS table (one lookup instead of a compare/select
 // chain).  The tree16 over the subspaces is a butterfly in which every level
 // halves the candidates a lane carries (lanes b, b ^ m add the same operands
@@ -529,7 +531,7 @@ __global__ __launch_bounds__(256) void cand_write_kernel(const uint8_t* votes, i
 // query head and lane u ends with candidate u's.  The first workgroup of a
 // head also zeroes the head's vote totals for the next call.
 template <int G>
-__global__ __launch_bounds__(256) void rerank_kernel(const uint8_t* codes, const float* w, int cap,
+__global__ __launch_bounds__(256) void rerank_kernel(const uint32_t* cw, int cap,
                                                      int n, const int32_t* cand, int C,
                                                      const float* qt, const float* qn,
                                                      CodebookArgs cb, float* est,
@@ -562,8 +564,9 @@ __global__ __launch_bounds__(256) void rerank_kernel(const uint8_t* codes, const
 #pragma unroll
   for (int u = 0; u < 16; ++u) {
     const int64_t ent = (int64_t)h * cap + __shfl(mine, base + u, 64);
-    code[u] = ((const uint32_t*)codes)[ent * kSub + j];
-    wb[u] = w[ent * kSub + j];
+    const uint2 pr = ((const uint2*)cw)[ent * kSub + j];
+    code[u] = pr.x;
+    wb[u] = __uint_as_float(pr.y);
   }
   lds_barrier();   // vtab
   float x[G][16];
@@ -604,7 +607,7 @@ void launch_rerank(const skv_index* ix, int n, const int32_t* cand, int C, const
                    const float* qn, const CodebookArgs& ca, float* est, int32_t* tot_ge,
                    hipStream_t st) {
   rerank_kernel<G><<<dim3((C + 255) / 256, ix->H), 256, 0, st>>>(
-      ix->codes, ix->w, ix->cap, n, cand, C, qt, qn, ca, est, tot_ge);
+      ix->cw, ix->cap, n, cand, C, qt, qn, ca, est, tot_ge);
 }
 
 // An empty index retrieves nothing.
@@ -689,7 +692,7 @@ bool codebook_ok(const skv_codebook* cb) {
 }
 
 bool index_ok(const skv_index* ix) {
-  return ix && ix->ids && ix->codes && ix->w && ix->hist && ix->pos && ix->H >= 1 &&
+  return ix && ix->ids && ix->cw && ix->hist && ix->pos && ix->H >= 1 &&
          ix->cap >= 0 && ix->n >= 0 && ix->n <= ix->cap;
 }
 
@@ -731,8 +734,8 @@ skv_status sparsekv_encode(const skv_codebook* cb, const skv_kv* kv, int32_t b, 
   const int per_wg = (int)std::min<int64_t>(kEncPerWG, std::max<int64_t>(16, (want + 15) / 16 * 16));
   dim3 grid((n_keys + per_wg - 1) / per_wg, kv->H);
   encode_kernel<<<grid, 256, 0, stream>>>(a, b, t0, n_keys, index->n, index->cap, per_wg,
-                                          cb->signs, cb_args(cb), index->ids, index->codes,
-                                          index->w, index->hist, index->pos);
+                                          cb->signs, cb_args(cb), index->ids, index->cw,
+                                          index->hist, index->pos);
   if (hipGetLastError() != hipSuccess) return SKV_ELAUNCH;
   index->n += n_keys;
   return SKV_OK;

@@ -353,16 +353,22 @@ __device__ __noinline__ int fallback_select(const float* scores, int row, int H,
 }
 
 // This thread's 4 bins (4 t .. 4 t + 3) of row `row`'s first-digit
-// histogram, summed over its copies (few rows have more than one).
+// histogram, summed over its copies (1 or kHistCopiesMax).  The copies' loads
+// are all issued before the first is used: as a loop over a run-time count
+// they went one round trip at a time (7 more of them for 8 copies).
 __device__ __forceinline__ uint4 hist_bins_summed(const TopkWs& ws, int row) {
   const uint4* g = (const uint4*)(ws.hist + (int64_t)row * ws.copies * kBins) + threadIdx.x;
-  uint4 v = g[0];
-  for (int cp = 1; cp < ws.copies; ++cp) {
-    const uint4 x = g[cp * (kBins / 4)];
-    v.x += x.x;
-    v.y += x.y;
-    v.z += x.z;
-    v.w += x.w;
+  if (ws.copies != kHistCopiesMax) return g[0];
+  uint4 x[kHistCopiesMax];
+#pragma unroll
+  for (int cp = 0; cp < kHistCopiesMax; ++cp) x[cp] = g[cp * (kBins / 4)];
+  uint4 v = x[0];
+#pragma unroll
+  for (int cp = 1; cp < kHistCopiesMax; ++cp) {
+    v.x += x[cp].x;
+    v.y += x[cp].y;
+    v.z += x[cp].z;
+    v.w += x[cp].w;
   }
   return v;
 }

@@ -53,10 +53,13 @@ __device__ __forceinline__ void lse_merge(float& m1, float& l1, float* a1, float
   m1 = m;
 }
 
+// With out != nullptr (n_split == 1) the workgroup writes the normalised
+// output itself, out = acc / l (0 for an empty row) -- what the merge would
+// compute from its one partial -- and no merge kernel follows.
 template <bool BF16, int NPL, int GMAX>
 __global__ __launch_bounds__(kThreads) void attend_split_kernel(
     KvArgs kv, const void* qv, int G, const int32_t* idx, int k, const int32_t* lo_p,
-    const int32_t* hi_p, float scale_log2, int n_split, float* part) {
+    const int32_t* hi_p, float scale_log2, int n_split, float* part, float* out) {
   constexpr int E = BF16 ? 8 : 4;
   constexpr int ES = BF16 ? 2 : 4;
   constexpr int PE = NPL * E;            // elements of a row held by one lane
@@ -210,6 +213,11 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(
         ll += src[D + 1] * c;
         aa += src[j] * c;
       }
+    }
+    if (out) {
+      const float inv_l = ll > 0.f ? 1.f / ll : 0.f;
+      out[(((int64_t)b * kv.H + h) * G + g) * D + j] = aa * inv_l;
+      continue;
     }
     float* dst = part + ((((int64_t)b * kv.H + h) * G + g) * n_split + s) * stride;
     dst[j] = aa;
@@ -457,17 +465,17 @@ __global__ __launch_bounds__(256) void attend_reduce_kernel(const float* part, i
 template <bool BF16, int NPL>
 hipError_t launch_split(const KvArgs& kv, const void* q, int G, const int32_t* idx, int k,
                         const int32_t* lo, const int32_t* hi, float scale_log2, int n_split,
-                        float* part, hipStream_t st) {
+                        float* part, float* out, hipStream_t st) {
   dim3 grid(n_split, kv.H, kv.B);
   const size_t lds = (size_t)4 * G * (kv.d_k + 2) * sizeof(float);
   if (G == 1)
-    attend_split_kernel<BF16, NPL, 1><<<grid, kThreads, lds, st>>>(kv, q, G, idx, k, lo, hi, scale_log2, n_split, part);
+    attend_split_kernel<BF16, NPL, 1><<<grid, kThreads, lds, st>>>(kv, q, G, idx, k, lo, hi, scale_log2, n_split, part, out);
   else if (G == 2)
-    attend_split_kernel<BF16, NPL, 2><<<grid, kThreads, lds, st>>>(kv, q, G, idx, k, lo, hi, scale_log2, n_split, part);
+    attend_split_kernel<BF16, NPL, 2><<<grid, kThreads, lds, st>>>(kv, q, G, idx, k, lo, hi, scale_log2, n_split, part, out);
   else if (G <= 4)
-    attend_split_kernel<BF16, NPL, 4><<<grid, kThreads, lds, st>>>(kv, q, G, idx, k, lo, hi, scale_log2, n_split, part);
+    attend_split_kernel<BF16, NPL, 4><<<grid, kThreads, lds, st>>>(kv, q, G, idx, k, lo, hi, scale_log2, n_split, part, out);
   else if (G <= 8 && NPL == 1)
-    attend_split_kernel<BF16, NPL, (NPL == 1 ? 8 : 4)><<<grid, kThreads, lds, st>>>(kv, q, G, idx, k, lo, hi, scale_log2, n_split, part);
+    attend_split_kernel<BF16, NPL, (NPL == 1 ? 8 : 4)><<<grid, kThreads, lds, st>>>(kv, q, G, idx, k, lo, hi, scale_log2, n_split, part, out);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -482,6 +490,7 @@ int pieces_per_lane(const KvArgs& kv) {
 }  // namespace
 
 int attend_num_splits(int k) { return std::max(1, std::min(64, (k + 511) / 128)); }
+constexpr int kOneSplitK = 128;   // vector-ALU path: single split, no merge kernel
 
 bool attend_supported(const KvArgs& kv, int G) {
   if (kv.v == nullptr || kv.d_k != kv.d_v) return false;
@@ -516,12 +525,21 @@ hipError_t launch_gather_attend(const KvArgs& kv, const void* q, int G, const in
     else
       attend_mfma_kernel<16><<<grid, kThreads, 0, st>>>(kv, qq, G, idx, k, lo, hi, scale_log2, n_split, part);
     e = hipGetLastError();
-  } else if (kv.bf16)
-    e = npl == 1 ? launch_split<true, 1>(kv, q, G, idx, k, lo, hi, scale_log2, n_split, part, st)
-                 : launch_split<true, 2>(kv, q, G, idx, k, lo, hi, scale_log2, n_split, part, st);
-  else
-    e = npl == 1 ? launch_split<false, 1>(kv, q, G, idx, k, lo, hi, scale_log2, n_split, part, st)
-                 : launch_split<false, 2>(kv, q, G, idx, k, lo, hi, scale_log2, n_split, part, st);
+  } else {
+    // the vector-ALU path takes a short selection (k <= 128) in one split
+    // that writes the output itself: 256 threads have such a row's selected
+    // rows in flight at once, and the merge kernel's launch is saved
+    const bool one = k <= kOneSplitK;
+    const int ns = one ? 1 : n_split;
+    float* o1 = one ? out : nullptr;
+    if (kv.bf16)
+      e = npl == 1 ? launch_split<true, 1>(kv, q, G, idx, k, lo, hi, scale_log2, ns, part, o1, st)
+                   : launch_split<true, 2>(kv, q, G, idx, k, lo, hi, scale_log2, ns, part, o1, st);
+    else
+      e = npl == 1 ? launch_split<false, 1>(kv, q, G, idx, k, lo, hi, scale_log2, ns, part, o1, st)
+                   : launch_split<false, 2>(kv, q, G, idx, k, lo, hi, scale_log2, ns, part, o1, st);
+    if (one) return e;
+  }
   if (e != hipSuccess) return e;
   return launch_attend_reduce(part, n_split, kv.d_v, kv.H * G, kv.B, out, st);
 }

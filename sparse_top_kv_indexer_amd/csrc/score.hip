@@ -33,7 +33,19 @@ namespace skv {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTile = 256;  // tokens per workgroup (multiple of 16)
+// Tokens per workgroup of the vector-ALU scan: 256, or down to 64 while the
+// grid has fewer than kTileWgs workgroups, so short rows still spread over
+// the chip: a 4-wave workgroup takes 16 U tokens per load round, and a
+// single 4,096-key row in 16 workgroups of 256 went through 4 dependent
+// rounds per wave (11.7 us) where 64 workgroups of 64 need one.
+constexpr int kTileMax = 256, kTileMin = 64, kTileWgs = 1024;
+int valu_tile(const KvArgs& kv) {
+  int tile = kTileMax;
+  while (tile > kTileMin &&
+         (int64_t)((kv.L_max + tile - 1) / tile) * kv.H * kv.B < kTileWgs)
+    tile /= 2;
+  return tile;
+}
 
 
 // Score-key histogram of the tile (top 12 bits of the order-preserving key),
@@ -86,13 +98,14 @@ __device__ __forceinline__ void hist_flush(uint32_t* lh, uint32_t* g) {
 
 template <bool BF16, int NPL, int GMAX, int U, bool HIST>
 __global__ __launch_bounds__(kThreads) void score_valu_kernel(KvArgs kv, const void* qv, int G,
-                                                               float* scores, HistArgs ha) {
+                                                               float* scores, HistArgs ha,
+                                                               int tile) {
   __shared__ uint32_t lh[HIST ? 4096 : 1];
   constexpr int E = BF16 ? 8 : 4;      // elements per 16-byte piece
   constexpr int ES = BF16 ? 2 : 4;     // bytes per element
   const int b = blockIdx.z, h = blockIdx.y;
-  const int t_begin = blockIdx.x * kTile;
-  const int t_end = min(kv.L_max, t_begin + kTile);
+  const int t_begin = blockIdx.x * tile;
+  const int t_end = min(kv.L_max, t_begin + tile);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int p = lane & 15, sub = lane >> 4;
   const int NP = kv.d_k / E;           // pieces per row
@@ -415,24 +428,26 @@ __global__ __launch_bounds__(kThreads) void score_stream_kernel(KvArgs kv, const
 
 template <bool BF16, int NPL, int GMAX, int U>
 void launch_valu_k(const KvArgs& kv, const void* q, int G, float* scores, const HistArgs& ha,
-                   dim3 grid, hipStream_t s) {
+                   dim3 grid, int tile, hipStream_t s) {
   if (ha.hist)
-    score_valu_kernel<BF16, NPL, GMAX, U, true><<<grid, kThreads, 0, s>>>(kv, q, G, scores, ha);
+    score_valu_kernel<BF16, NPL, GMAX, U, true><<<grid, kThreads, 0, s>>>(kv, q, G, scores, ha,
+                                                                          tile);
   else
-    score_valu_kernel<BF16, NPL, GMAX, U, false><<<grid, kThreads, 0, s>>>(kv, q, G, scores, ha);
+    score_valu_kernel<BF16, NPL, GMAX, U, false><<<grid, kThreads, 0, s>>>(kv, q, G, scores, ha,
+                                                                           tile);
 }
 
 template <bool BF16, int NPL, int GCAP>
 hipError_t launch_valu(const KvArgs& kv, const void* q, int G, float* scores, const HistArgs& ha,
-                       dim3 grid, hipStream_t s) {
+                       dim3 grid, int tile, hipStream_t s) {
   if (G == 1)
-    launch_valu_k<BF16, NPL, 1, 4>(kv, q, G, scores, ha, grid, s);
+    launch_valu_k<BF16, NPL, 1, 4>(kv, q, G, scores, ha, grid, tile, s);
   else if (GCAP >= 2 && G == 2)
-    launch_valu_k<BF16, NPL, (GCAP >= 2 ? 2 : 1), 4>(kv, q, G, scores, ha, grid, s);
+    launch_valu_k<BF16, NPL, (GCAP >= 2 ? 2 : 1), 4>(kv, q, G, scores, ha, grid, tile, s);
   else if (GCAP >= 4 && G <= 4)
-    launch_valu_k<BF16, NPL, (GCAP >= 4 ? 4 : 1), 2>(kv, q, G, scores, ha, grid, s);
+    launch_valu_k<BF16, NPL, (GCAP >= 4 ? 4 : 1), 2>(kv, q, G, scores, ha, grid, tile, s);
   else if (GCAP >= 8 && G <= 8)
-    launch_valu_k<BF16, NPL, (GCAP >= 8 ? 8 : 1), 2>(kv, q, G, scores, ha, grid, s);
+    launch_valu_k<BF16, NPL, (GCAP >= 8 ? 8 : 1), 2>(kv, q, G, scores, ha, grid, tile, s);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -504,7 +519,8 @@ hipError_t launch_stream(const KvArgs& kv, const void* q, int G, float* scores, 
 
 hipError_t launch_score(const KvArgs& kv, const void* q, int G, float* scores, const int32_t* lo,
                         const int32_t* hi, uint32_t* hist, hipStream_t s) {
-  dim3 grid((kv.L_max + kTile - 1) / kTile, kv.H, kv.B);
+  const int tile = valu_tile(kv);
+  dim3 grid((kv.L_max + tile - 1) / tile, kv.H, kv.B);
   HistArgs ha{lo, hi, hist};
   ha.copies = topk_hist_copies(kv.B * kv.H, kv.L_max);
   if (kv.bf16 && G >= 1 && G <= 16 && kv.d_k % 32 == 0 && (G >= 2 || kv.d_k <= 256)) {
@@ -519,13 +535,13 @@ hipError_t launch_score(const KvArgs& kv, const void* q, int G, float* scores, c
   const int E = kv.bf16 ? 8 : 4;
   const int npl = (kv.d_k / E + 15) / 16;
   if (kv.bf16) {
-    if (npl == 1) return launch_valu<true, 1, 8>(kv, q, G, scores, ha, grid, s);
-    if (npl == 2) return launch_valu<true, 2, 4>(kv, q, G, scores, ha, grid, s);
-    if (npl <= 5) return launch_valu<true, 5, 1>(kv, q, G, scores, ha, grid, s);
+    if (npl == 1) return launch_valu<true, 1, 8>(kv, q, G, scores, ha, grid, tile, s);
+    if (npl == 2) return launch_valu<true, 2, 4>(kv, q, G, scores, ha, grid, tile, s);
+    if (npl <= 5) return launch_valu<true, 5, 1>(kv, q, G, scores, ha, grid, tile, s);
   } else {
-    if (npl == 1) return launch_valu<false, 1, 8>(kv, q, G, scores, ha, grid, s);
-    if (npl == 2) return launch_valu<false, 2, 8>(kv, q, G, scores, ha, grid, s);
-    if (npl <= 4) return launch_valu<false, 4, 2>(kv, q, G, scores, ha, grid, s);
+    if (npl == 1) return launch_valu<false, 1, 8>(kv, q, G, scores, ha, grid, tile, s);
+    if (npl == 2) return launch_valu<false, 2, 8>(kv, q, G, scores, ha, grid, tile, s);
+    if (npl <= 4) return launch_valu<false, 4, 2>(kv, q, G, scores, ha, grid, tile, s);
   }
   return hipErrorInvalidValue;
 }

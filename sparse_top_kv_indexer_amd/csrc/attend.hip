@@ -489,7 +489,15 @@ int pieces_per_lane(const KvArgs& kv) {
 
 }  // namespace
 
-int attend_num_splits(int k) { return std::max(1, std::min(64, (k + 511) / 128)); }
+// Splits per row: ~128 selected tokens each (64 at most), and at least enough
+// for 256 workgroups when there are few rows (8 KV heads of one sequence:
+// 32 splits instead of 4), since the sink / local tokens every split also
+// shares are not known on the host.
+int attend_num_splits(int k, int rows) {
+  int n = std::max(1, std::min(64, (k + 511) / 128));
+  if (rows > 0 && (int64_t)rows * n < 256) n = std::min(64, std::max(n, (256 + rows - 1) / rows));
+  return n;
+}
 constexpr int kOneSplitK = 128;   // vector-ALU path: single split, no merge kernel
 
 bool attend_supported(const KvArgs& kv, int G) {
@@ -502,13 +510,13 @@ bool attend_supported(const KvArgs& kv, int G) {
 }
 
 size_t attend_workspace_bytes(const KvArgs& kv, int G, int k) {
-  return (size_t)kv.B * kv.H * G * attend_num_splits(k) * (kv.d_v + 2) * sizeof(float);
+  return (size_t)kv.B * kv.H * G * attend_num_splits(k, kv.B * kv.H) * (kv.d_v + 2) * sizeof(float);
 }
 
 hipError_t launch_gather_attend(const KvArgs& kv, const void* q, int G, const int32_t* idx, int k,
                                 const int32_t* lo, const int32_t* hi, float scale, float* out,
                                 void* ws, size_t ws_bytes, hipStream_t st) {
-  const int n_split = attend_num_splits(k);
+  const int n_split = attend_num_splits(k, kv.B * kv.H);
   float* part = (float*)ws;
   const float scale_log2 = scale * 1.4426950408889634f;
   hipError_t e;

@@ -71,7 +71,7 @@ hipError_t launch_topk_listing(const float* scores, int rows, int H, int L_max, 
                                const int32_t* hi, int k, void* ws, hipStream_t s);
 
 // attend.hip
-int attend_num_splits(int k);
+int attend_num_splits(int k, int rows);
 size_t attend_workspace_bytes(const KvArgs& kv, int G, int k);
 hipError_t launch_gather_attend(const KvArgs& kv, const void* q, int G, const int32_t* idx, int k,
                                 const int32_t* lo, const int32_t* hi, float scale, float* out,

@@ -409,18 +409,18 @@ __global__ __launch_bounds__(kThreads) void attend_mfma_kernel(
 
 // out[b][hq][j] = sum_s acc_s[j] 2^(m_s - M) / sum_s l_s 2^(m_s - M)
 // Grid (query heads, B, ceil(D / 256)): a workgroup owns 256 dims of one
-// (b, query head), a thread one dim, whose values it loads from 32 splits at
-// a time -- all of them for n_split <= 32, in flight while the split weights
+// (b, query head), a thread one dim, whose values it loads from SG splits at
+// a time -- all of them, in flight while the split weights
 // are formed (n_split <= 64, D <= 512).
 // With zero_hist != nullptr, the first workgroup of the first query head of
 // each KV head also zeroes that row's copies of the 4096-bin key histogram
 // and, with ctr != nullptr, the row's list counter (ctr[row * kCtrStride]):
 // the fused top-k + attention paths leave them for this kernel, which runs
 // after every reader.
+template <int SG>   // splits whose values are loaded together (32, or 64 for more splits)
 __global__ __launch_bounds__(256) void attend_reduce_kernel(const float* part, int n_split, int D,
                                                            int HG, float* out, uint32_t* zero_hist,
                                                            int G, int copies, int32_t* ctr) {
-  constexpr int SG = 32;                 // splits whose values are loaded together
   __shared__ float wts[64];
   __shared__ float inv_l;
   const int hq = blockIdx.x, b = blockIdx.y;
@@ -557,7 +557,12 @@ hipError_t launch_attend_reduce(const float* part, int n_split, int D, int HG, i
                                 int32_t* ctr) {
   if (n_split > 64 || D > 512) return hipErrorInvalidValue;
   dim3 grid(HG, B, (D + 255) / 256);
-  attend_reduce_kernel<<<grid, 256, 0, st>>>(part, n_split, D, HG, out, zero_hist, G, copies, ctr);
+  if (n_split > 32)
+    attend_reduce_kernel<64><<<grid, 256, 0, st>>>(part, n_split, D, HG, out, zero_hist, G, copies,
+                                                   ctr);
+  else
+    attend_reduce_kernel<32><<<grid, 256, 0, st>>>(part, n_split, D, HG, out, zero_hist, G, copies,
+                                                   ctr);
   return hipGetLastError();
 }
 

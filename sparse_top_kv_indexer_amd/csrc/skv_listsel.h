@@ -355,7 +355,7 @@ __device__ __noinline__ int fallback_select(const float* scores, int row, int H,
 // This thread's 4 bins (4 t .. 4 t + 3) of row `row`'s first-digit
 // histogram, summed over its copies (1 or kHistCopiesMax).  The copies' loads
 // are all issued before the first is used: as a loop over a run-time count
-// they went one round trip at a time (7 more of them for 8 copies).
+// they went one round trip at a time.
 __device__ __forceinline__ uint4 hist_bins_summed(const TopkWs& ws, int row) {
   const uint4* g = (const uint4*)(ws.hist + (int64_t)row * ws.copies * kBins) + threadIdx.x;
   if (ws.copies != kHistCopiesMax) return g[0];

@@ -44,10 +44,12 @@ inline int topk_slice_groups(int rows, int L_max) {
 // hundreds of workgroups each, and their once-per-workgroup flushes of the
 // histogram queue behind each other on the row's bins (device atomics on few
 // addresses are slow); with several copies, workgroup w adds into copy
-// w % copies -- the copy of its XCD, as workgroups go to the 8 XCDs
-// round-robin -- and every reader sums the copies.  Producer and consumers
-// derive the count from (rows, L_max) alone.
-constexpr int kHistCopiesMax = 8;
+// w % copies and every reader sums the copies.  Two copies: for one row of
+// 131,072 keys the scan took 14.4 us with one copy and 12.0-12.6 us with
+// 2, 4 or 8, while every listing workgroup, which reads all copies, took 5.7,
+// 6.4 and 7.8 us.  Producer and consumers derive the count from (rows, L_max)
+// alone.
+constexpr int kHistCopiesMax = 2;
 __host__ __device__ inline int topk_hist_copies(int rows, int L_max) {
   const int64_t slots = L_max % 4 == 0 ? (int64_t)L_max : (int64_t)L_max + 3;
   return (rows <= 4 && slots > 32768) ? kHistCopiesMax : 1;

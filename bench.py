@@ -237,7 +237,8 @@ KERNEL_SOURCES = {
     "topk_alone_kernel": _TOPK, "topk_compact_kernel": _TOPK, "topk_finish_kernel": _TOPK,
     "topk_hist_kernel": _TOPK, "topk_survivor_kernel": _TOPK,
     "attend_mfma_kernel": _ATT, "attend_split_kernel": _ATT, "attend_reduce_kernel": _ATT,
-    "select_attend_kernel": [CSRC + "select_attend.hip"] + _SEL + _COMMON,
+    "select_attend_kernel": [CSRC + "select_attend.hip", CSRC + "skv_listsel.h"] + _SEL + _COMMON,
+    "finish_attend_kernel": [CSRC + "select_attend.hip", CSRC + "skv_listsel.h"] + _SEL + _COMMON,
     "mla_split_kernel": _MLA, "mla_list_kernel": _MLA,
     "query_lut_kernel": _PARIS, "vote_kernel": _PARIS, "cand_write_kernel": _PARIS,
     "rerank_kernel": _PARIS, "encode_kernel": _PARIS,
@@ -435,11 +436,11 @@ def bench_dense(args, hip):
     idx = torch.empty((B, H, k), dtype=torch.int32, device=dev)
     cnt = torch.empty((B, H), dtype=torch.int32, device=dev)
     out = torch.empty((kv.B, kv.H * G, kv.d_v), dtype=torch.float32, device=dev)
-    # fused: the top-k finished inside the attention kernel (GQA rows of one
-    # 32768-slot sweep; the latent attention at any length -- longer GQA rows
-    # are timed as separate calls, which is what the fused call runs for them)
+    # fused: sparsekv_score_hist + sparsekv_select_attend_resume -- the top-k
+    # finished inside the attention kernel (GQA rows of any length, k <= 4096
+    # beyond one 32768-slot sweep; the latent attention)
     fused = args.path == "fused" and (mla or (skv is kv and sG == G and bf and kv.d_k == 128
-                                              and G <= 8 and L <= 32768))
+                                              and G <= 8 and (L <= 32768 or k <= 4096)))
     prefilter = args.path == "prefilter"
     blocks = args.path == "blocks"
     if blocks:

@@ -121,6 +121,9 @@ skv_status long_select_attend(const KvArgs& a, const void* q, int G, skv_window 
                               float scale, const float* scores, int32_t* idx, int32_t* count,
                               float* out, void* ws, size_t th, size_t ws_bytes,
                               hipStream_t stream) {
+  if (finish_attend_supported(a, G, k))
+    return launched(launch_finish_attend(a, q, G, scores, win.lo, win.hi, k, ws, scale, idx, count,
+                                         out, stream));
   const hipError_t e = launch_topk(scores, a.B * a.H, a.H, a.L_max, win.lo, win.hi, k, idx, count,
                                    ws, true, stream);
   if (e != hipSuccess) return launched(e);

@@ -30,6 +30,7 @@
 #include <algorithm>
 
 #include "skv_internal.h"
+#include "skv_listsel.h"
 #include "skv_rowsel.h"
 
 namespace skv {
@@ -45,7 +46,10 @@ constexpr int kD = 128;
 // (step 4): the tokens are lst[0 .. n_list) (selected positions) then the
 // always-attended positions x0 .. of t < a_lo and t >= a_hi, n_att in all;
 // tbl: the row's block-table entries staged in LDS, or null (slots through
-// kv's table).  Qf: the MFMA B operand of the G query rows.
+// kv's table).  Qf: the MFMA B operand of the G query rows.  With out !=
+// nullptr (a workgroup that attends the row's whole selection) the merged
+// result is written normalised to out[row][g][:] (0 for an empty row) in
+// place of a split partial.
 template <int GMAX>
 __device__ __forceinline__ void attend_share(const KvArgs& kv, int G, int row, int b, int h, int s,
                                              int n_split, const int32_t* lst, int n_list, int x0,
@@ -53,7 +57,8 @@ __device__ __forceinline__ void attend_share(const KvArgs& kv, int G, int row, i
                                              const int32_t* tbl, const bf16x8_t (&Qf)[4],
                                              float scale_log2, float* part,
                                              int64_t (&rows_sh)[kRowWaves][2][16],
-                                             float (&red)[kRowWaves][4][kD + 2]) {
+                                             float (&red)[kRowWaves][4][kD + 2],
+                                             float* out = nullptr) {
   const int lane = threadIdx.x & 63, wave = row_wave();
   const int n = lane & 15, g4 = lane >> 4;
 
@@ -198,11 +203,15 @@ __device__ __forceinline__ void attend_share(const KvArgs& kv, int G, int row, i
           aa += red[v][gi][j] * cw;
         }
       }
-      float* dst = part + (((int64_t)row * G + g) * n_split + s) * stride;
-      dst[j] = aa;
-      if (j == 0) {
-        dst[kD] = mm;
-        dst[kD + 1] = ll;
+      if (out) {
+        out[((int64_t)row * G + g) * kD + j] = aa * (ll > 0.f ? 1.f / ll : 0.f);
+      } else {
+        float* dst = part + (((int64_t)row * G + g) * n_split + s) * stride;
+        dst[j] = aa;
+        if (j == 0) {
+          dst[kD] = mm;
+          dst[kD + 1] = ll;
+        }
       }
     }
   }
@@ -313,6 +322,74 @@ __global__ __launch_bounds__(kRowThreads) void select_attend_kernel(
                      n_blk ? tbl : nullptr, Qf, scale_log2, part, rows_sh, red);
 }
 
+
+// ------------------------------------------ rows longer than one sweep --
+// After the slice listing (the exact top-k's list in the top-k workspace),
+// one workgroup per row finishes the selection from the list (list_select,
+// the row alone when the list overflowed), writes idx and count, and attends
+// over the whole selection plus the sink and local tokens with the 16 waves
+// of attend_share, writing the row's normalised output: no split partials
+// and no merge kernel, so the step is scan, listing and this kernel.  Many
+// rows (one workgroup per CU or more) keep every CU streaming K/V rows; the
+// rows' histograms and list counters are zeroed here, after their last read.
+constexpr int kFinishSlices = 1024;   // listing slices of a row this kernel reads
+constexpr int kFinishK = kBins;       // selected keys it stages (k <= 4096)
+
+template <int GMAX>
+__global__ __launch_bounds__(kRowThreads) void finish_attend_kernel(
+    KvArgs kv, const uint16_t* q, int G, const float* scores, const int32_t* lo_p,
+    const int32_t* hi_p, int k, TopkWs ws, int n_slices, float scale_log2, int32_t* idx,
+    int32_t* count, float* out) {
+  __shared__ RowSelLds L;
+  __shared__ int32_t sel[kFinishK];                 // the selection, ascending
+  __shared__ int s_off[kFinishSlices + 1], s_at[kFinishSlices];
+  __shared__ int klist_n;
+  __shared__ int64_t rows_sh[kRowWaves][2][16];
+  __shared__ float red[kRowWaves][4][kD + 2];
+  const int row = blockIdx.x;
+  const int b = row / kv.H, h = row - b * kv.H;
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15, g4 = lane >> 4;
+  // the query rows (MFMA B operand of the logits), needed only later
+  bf16x8_t Qf[4];
+  {
+    const uint16_t* qrow = q + ((int64_t)row * G + (n < G ? n : 0)) * kD;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const u32x4_t v = n < G ? ld16((const char*)(qrow + 8 * (4 * j + g4))) : u32x4_t{0, 0, 0, 0};
+      Qf[j] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+  uint32_t* ghist = ws.hist + (int64_t)row * ws.copies * kBins;
+  const uint4 gv = hist_bins_summed(ws, row);
+  int n_sel;
+  const int32_t* lst;
+  if (ws.meta[2 * row + 1] < 0) {
+    n_sel = fallback_select(scores, row, kv.H, kv.L_max, lo_p, hi_p, k, ghist, L, klist_n, gv);
+    lst = (const int32_t*)L.hist;   // the positions, ascending
+  } else {
+    n_sel = list_select(ws, row, k, n_slices, gv, L, s_off, s_at,
+                        [&](int dst, int p) { sel[dst] = p; });
+    lst = sel;
+  }
+  lds_barrier();
+  int32_t* orow = idx + (int64_t)row * k;
+  for (int i = threadIdx.x; i < k; i += kRowThreads) orow[i] = i < n_sel ? lst[i] : -1;
+  if (threadIdx.x == 0) {
+    count[row] = n_sel;
+    ws.ctr[(int64_t)row * kCtrStride] = 0;   // zero for the next call
+  }
+  for (int cp = 0; cp < ws.copies; ++cp)
+    ((uint4*)ghist)[cp * (kBins / 4) + threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
+  const RowWindow w = row_window(lo_p, hi_p, b, kv.L_max);
+  const int seq = min(kv.seq_len[b], kv.L_max);
+  const int a_lo = min(w.lo, seq);
+  const int a_hi = max(a_lo, min(w.hi, seq));
+  const int n_att = n_sel + a_lo + (seq - a_hi);
+  attend_share<GMAX>(kv, G, row, b, h, 0, 1, lst, n_sel, 0, n_att, a_lo, a_hi, seq, nullptr, Qf,
+                     scale_log2, nullptr, rows_sh, red, out);
+}
+
 }  // namespace
 
 bool select_attend_supported(const KvArgs& kv, int G) {
@@ -339,6 +416,34 @@ hipError_t launch_select_attend(const KvArgs& kv, const void* q, int G, const fl
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_attend_reduce(part, kSplits, kD, kv.H * G, kv.B, out, st, hist, G);
+}
+
+bool finish_attend_supported(const KvArgs& kv, int G, int k) {
+  return kv.bf16 && kv.v != nullptr && kv.d_k == kD && kv.d_v == kD && G >= 1 && G <= 8 &&
+         k >= 1 && k <= kFinishK && row_slots_max(kv.L_max) > kSweep && topk_supported(kv.L_max) &&
+         topk_listing_slices(kv.B * kv.H, kv.L_max) <= kFinishSlices &&
+         kv.B * kv.H >= kFinishAttendMinRows;
+}
+
+hipError_t launch_finish_attend(const KvArgs& kv, const void* q, int G, const float* scores,
+                                const int32_t* lo, const int32_t* hi, int k, void* topk_ws,
+                                float scale, int32_t* idx, int32_t* count, float* out,
+                                hipStream_t st) {
+  const int rows = kv.B * kv.H;
+  const TopkWs ws = TopkWs::carve(topk_ws, rows, kv.L_max);
+  hipError_t e = launch_topk_listing(scores, rows, kv.H, kv.L_max, lo, hi, k, topk_ws, st);
+  if (e != hipSuccess) return e;
+  const int ns = topk_listing_slices(rows, kv.L_max);
+  if (ns > kFinishSlices || k > kFinishK) return hipErrorInvalidValue;
+  const float scale_log2 = scale * 1.4426950408889634f;
+  const uint16_t* qq = (const uint16_t*)q;
+  if (G <= 4)
+    finish_attend_kernel<4><<<rows, kRowThreads, 0, st>>>(kv, qq, G, scores, lo, hi, k, ws, ns,
+                                                          scale_log2, idx, count, out);
+  else
+    finish_attend_kernel<8><<<rows, kRowThreads, 0, st>>>(kv, qq, G, scores, lo, hi, k, ws, ns,
+                                                          scale_log2, idx, count, out);
+  return hipGetLastError();
 }
 
 }  // namespace skv

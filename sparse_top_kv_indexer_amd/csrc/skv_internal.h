@@ -93,6 +93,21 @@ hipError_t launch_select_attend(const KvArgs& kv, const void* q, int G, const fl
                                 float scale, int32_t* idx, int32_t* count, float* part,
                                 float* out, hipStream_t s);
 
+// select_attend.hip: rows longer than one sweep, after a scan that left the
+// histograms in the top-k workspace: the slice listing, then one workgroup
+// per row that finishes the exact top-k (idx, count) and attends over the
+// whole selection with sink and local, writing out (bf16, d = 128, G <= 8,
+// k <= 4096, at least kFinishAttendMinRows rows: one workgroup per row
+// streams K/V rows at a CU's rate, so with few rows the split attention over
+// every CU is faster -- 32 rows of 131,072 took 46.5 us here against 31.4 us
+// for finish + split attention + merge, 256 rows of 65,536 73.3 against 83.5)
+constexpr int kFinishAttendMinRows = 128;
+bool finish_attend_supported(const KvArgs& kv, int G, int k);
+hipError_t launch_finish_attend(const KvArgs& kv, const void* q, int G, const float* scores,
+                                const int32_t* lo, const int32_t* hi, int k, void* topk_ws,
+                                float scale, int32_t* idx, int32_t* count, float* out,
+                                hipStream_t st);
+
 // mla.hip: shared-latent attention on matrix cores (v == nullptr)
 bool mla_supported(const KvArgs& kv, int G);
 size_t mla_workspace_bytes(const KvArgs& kv, int G, int k);

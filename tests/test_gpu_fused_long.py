@@ -4,7 +4,9 @@ the indexer's sparsekv_score_hist) finishes the exact top-k inside the
 attention kernel: the slice listing, then every attending workgroup resolves
 the row's selection from the list itself.  GQA rows (sparsekv_select_attend
 and its resume) take the slice-listing top-k and the split attention inside
-the same call.  Checked against the float64 oracle (selection set, attention
+the same call: with 128 rows or more one workgroup per row finishes the
+selection and attends over all of it (no split merge), with fewer the split
+attention follows the finish.  Checked against the float64 oracle (selection set, attention
 within 2e-3) and against the separate calls, including rows whose candidate
 list overflows (many tied scores) so that the selection falls back to reading
 the row per digit."""
@@ -159,6 +161,33 @@ def test_fused_gqa_long_list_overflow_fallback():
     r = Run(st)
     _, idx, cnt, _ = r.select_attend()
     assert int(cnt[0, 0]) == 1500 and idx[0, 0].cpu().numpy().tolist() == list(range(4, 1504))
+
+
+def test_fused_gqa_long_many_rows_token_table():
+    """128 rows: the one-workgroup-per-row finish + attention."""
+    st = W.make_token_pool(tag=740, B=16, H=8, L=40000, k=2048, sink=4, local=128)
+    assert _check_gqa(st) == 0
+
+
+def test_fused_gqa_long_many_rows_g8_k4096_ragged():
+    """128 rows, G = 8, k = 4096 (the most the kernel stages), ragged
+    sequence lengths and a paged pool."""
+    seq = [33024 - 1531 * (b % 5) for b in range(16)]
+    st = W.make_gqa_paged(tag=741, B=16, H=8, G=8, L=33024, k=4096, sink=4, local=64, seq_len=seq)
+    assert _check_gqa(st) == 0
+
+
+def test_fused_gqa_long_many_rows_list_overflow_fallback():
+    """128 rows, one of them all ties: that row's list overflows and its
+    workgroup selects from the row itself."""
+    st = W.make_gqa_paged(tag=742, B=16, H=8, G=1, L=40960, k=1500, sink=4, local=64)
+    blocks = st.kv.block_table[3]
+    st.kv.k[blocks, 5] = st.kv.k[blocks[0], 5, 0:1, :]
+    rows = [(3, 5), (3, 4), (0, 0), (15, 7)]
+    assert _check_gqa(st, rows=rows) == 0
+    r = Run(st)
+    _, idx, cnt, _ = r.select_attend()
+    assert int(cnt[3, 5]) == 1500 and idx[3, 5].cpu().numpy().tolist() == list(range(4, 1504))
 
 
 @pytest.mark.slow

@@ -248,7 +248,7 @@ def test_quantised_pipeline_shapes_and_budget():
         assert S[mask].min() >= S[~mask].max()
 
 
-# ------------------------------------------------------- verdict-item pins
+# ------------------------------------------------ histogram and zero-row pins
 def test_histogram_counts_each_subspace_column_separately():
     """A hand-built id matrix whose subspaces have different counts: a
     histogram built from one column for every row, or over the flattened

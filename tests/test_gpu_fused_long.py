@@ -190,6 +190,24 @@ def test_fused_gqa_long_many_rows_list_overflow_fallback():
     assert int(cnt[3, 5]) == 1500 and idx[3, 5].cpu().numpy().tolist() == list(range(4, 1504))
 
 
+def test_fused_gqa_long_many_rows_window_edges():
+    """128 rows through the one-workgroup-per-row kernel with edge windows:
+    no candidates (lo == hi), fewer candidates than k, a sequence of 40
+    tokens, an empty sequence, k = 1."""
+    seq = [40960] * 16
+    seq[3], seq[4] = 40, 0
+    st = W.make_gqa_paged(tag=743, B=16, H=8, G=2, L=40960, k=2048, sink=4, local=64,
+                          seq_len=seq)
+    st.lo[0] = st.hi[0] = 20000             # only the sink and local tokens
+    st.lo[1], st.hi[1] = 1000, 2500         # 1,500 candidates < k
+    st.lo[3], st.hi[3] = 4, 20              # a short sequence
+    st.lo[4], st.hi[4] = 0, 0               # an empty one
+    rows = [(b, h) for b in (0, 1, 2, 3, 4, 15) for h in (0, 7)]
+    assert _check_gqa(st, rows=rows) == 0
+    st.k = 1
+    assert _check_gqa(st, rows=rows) == 0
+
+
 @pytest.mark.slow
 def test_fused_gqa_long_full_size_every_row():
     """The GQA decode at L = 131072 through the fused call, all 32 rows."""

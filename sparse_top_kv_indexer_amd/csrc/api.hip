@@ -107,11 +107,10 @@ hipError_t scratch_for_current_device(void** out) {
   return hipSuccess;
 }
 
-// GQA rows longer than one sweep in the fused calls: the slice-listing top-k
+// GQA rows longer than one sweep in the fused calls: the slice listing, then
+// the kernel that finishes each row's selection and attends over it (k <=
+// 4096, at most 1024 listing slices); other shapes take the sliced top-k
 // (finished by one workgroup per row), then the split attention and merge.
-// Finishing the selection inside the attention kernel instead (every
-// attending workgroup resolving its row from the list) measured no faster
-// for these rows: the repeated selections cost what the boundary saves.
 bool long_select_attend_supported(const KvArgs& a, int G) {
   return a.bf16 && a.v != nullptr && a.d_k == 128 && a.d_v == 128 && G >= 1 && G <= 8 &&
          topk_supported(a.L_max) && attend_supported(a, G);
@@ -123,7 +122,7 @@ skv_status long_select_attend(const KvArgs& a, const void* q, int G, skv_window 
                               hipStream_t stream) {
   if (finish_attend_supported(a, G, k))
     return launched(launch_finish_attend(a, q, G, scores, win.lo, win.hi, k, ws, scale, idx, count,
-                                         out, stream));
+                                         out, (float*)((char*)ws + th), stream));
   const hipError_t e = launch_topk(scores, a.B * a.H, a.H, a.L_max, win.lo, win.hi, k, idx, count,
                                    ws, true, stream);
   if (e != hipSuccess) return launched(e);

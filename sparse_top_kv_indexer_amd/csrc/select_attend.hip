@@ -339,14 +339,18 @@ template <int GMAX>
 __global__ __launch_bounds__(kRowThreads) void finish_attend_kernel(
     KvArgs kv, const uint16_t* q, int G, const float* scores, const int32_t* lo_p,
     const int32_t* hi_p, int k, TopkWs ws, int n_slices, float scale_log2, int32_t* idx,
-    int32_t* count, float* out) {
+    int32_t* count, float* out, int n_split, float* part) {
   __shared__ RowSelLds L;
   __shared__ int32_t sel[kFinishK];                 // the selection, ascending
   __shared__ int s_off[kFinishSlices + 1], s_at[kFinishSlices];
   __shared__ int klist_n;
   __shared__ int64_t rows_sh[kRowWaves][2][16];
   __shared__ float red[kRowWaves][4][kD + 2];
-  const int row = blockIdx.x;
+  // n_split > 1: the row's workgroups run on one XCD (their list and scores
+  // then come from its L2); the grid is padded to a multiple of 8
+  const int vid = n_split > 1 ? xcd_remap(blockIdx.x, gridDim.x) : blockIdx.x;
+  const int row = vid / n_split, s = vid - row * n_split;
+  if (row >= kv.B * kv.H) return;
   const int b = row / kv.H, h = row - b * kv.H;
   const int lane = threadIdx.x & 63;
   const int n = lane & 15, g4 = lane >> 4;
@@ -373,21 +377,28 @@ __global__ __launch_bounds__(kRowThreads) void finish_attend_kernel(
     lst = sel;
   }
   lds_barrier();
-  int32_t* orow = idx + (int64_t)row * k;
-  for (int i = threadIdx.x; i < k; i += kRowThreads) orow[i] = i < n_sel ? lst[i] : -1;
-  if (threadIdx.x == 0) {
-    count[row] = n_sel;
-    ws.ctr[(int64_t)row * kCtrStride] = 0;   // zero for the next call
+  if (s == 0) {
+    int32_t* orow = idx + (int64_t)row * k;
+    for (int i = threadIdx.x; i < k; i += kRowThreads) orow[i] = i < n_sel ? lst[i] : -1;
+    if (threadIdx.x == 0) count[row] = n_sel;
   }
-  for (int cp = 0; cp < ws.copies; ++cp)
-    ((uint4*)ghist)[cp * (kBins / 4) + threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
+  if (n_split == 1) {   // the row's only reader: zero for the next call
+    if (threadIdx.x == 0) ws.ctr[(int64_t)row * kCtrStride] = 0;
+    for (int cp = 0; cp < ws.copies; ++cp)
+      ((uint4*)ghist)[cp * (kBins / 4) + threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
+  }
+  // this workgroup's share: selected ranks [r0, r1) and an equal share of
+  // the sink and local tokens
   const RowWindow w = row_window(lo_p, hi_p, b, kv.L_max);
   const int seq = min(kv.seq_len[b], kv.L_max);
   const int a_lo = min(w.lo, seq);
   const int a_hi = max(a_lo, min(w.hi, seq));
-  const int n_att = n_sel + a_lo + (seq - a_hi);
-  attend_share<GMAX>(kv, G, row, b, h, 0, 1, lst, n_sel, 0, n_att, a_lo, a_hi, seq, nullptr, Qf,
-                     scale_log2, nullptr, rows_sh, red, out);
+  const int n_extra = a_lo + (seq - a_hi);
+  const int r0 = (int)((int64_t)n_sel * s / n_split), r1 = (int)((int64_t)n_sel * (s + 1) / n_split);
+  const int x0 = (int)((int64_t)n_extra * s / n_split);
+  const int n_att = (r1 - r0) + (int)((int64_t)n_extra * (s + 1) / n_split) - x0;
+  attend_share<GMAX>(kv, G, row, b, h, s, n_split, lst + r0, r1 - r0, x0, n_att, a_lo, a_hi, seq,
+                     nullptr, Qf, scale_log2, part, rows_sh, red, n_split == 1 ? out : nullptr);
 }
 
 }  // namespace
@@ -421,13 +432,21 @@ hipError_t launch_select_attend(const KvArgs& kv, const void* q, int G, const fl
 bool finish_attend_supported(const KvArgs& kv, int G, int k) {
   return kv.bf16 && kv.v != nullptr && kv.d_k == kD && kv.d_v == kD && G >= 1 && G <= 8 &&
          k >= 1 && k <= kFinishK && row_slots_max(kv.L_max) > kSweep && topk_supported(kv.L_max) &&
-         topk_listing_slices(kv.B * kv.H, kv.L_max) <= kFinishSlices &&
-         kv.B * kv.H >= kFinishAttendMinRows;
+         topk_listing_slices(kv.B * kv.H, kv.L_max) <= kFinishSlices;
+}
+
+// Workgroups per row: one with many rows (every CU already busy, and no
+// merge kernel), else up to kFinishSplitsFew whose partials the merge adds
+// (within the split partials attend_workspace_bytes reserves).
+int finish_attend_splits(const KvArgs& kv, int G, int k) {
+  const int rows = kv.B * kv.H;
+  if (rows >= kFinishAttendMinRows) return 1;
+  return std::max(1, std::min(kFinishSplitsFew, attend_num_splits(k, rows)));
 }
 
 hipError_t launch_finish_attend(const KvArgs& kv, const void* q, int G, const float* scores,
                                 const int32_t* lo, const int32_t* hi, int k, void* topk_ws,
-                                float scale, int32_t* idx, int32_t* count, float* out,
+                                float scale, int32_t* idx, int32_t* count, float* out, float* part,
                                 hipStream_t st) {
   const int rows = kv.B * kv.H;
   const TopkWs ws = TopkWs::carve(topk_ws, rows, kv.L_max);
@@ -437,13 +456,17 @@ hipError_t launch_finish_attend(const KvArgs& kv, const void* q, int G, const fl
   if (ns > kFinishSlices || k > kFinishK) return hipErrorInvalidValue;
   const float scale_log2 = scale * 1.4426950408889634f;
   const uint16_t* qq = (const uint16_t*)q;
+  const int S = finish_attend_splits(kv, G, k);
+  const unsigned grid = S == 1 ? (unsigned)rows : (unsigned)((rows * S + 7) / 8 * 8);
   if (G <= 4)
-    finish_attend_kernel<4><<<rows, kRowThreads, 0, st>>>(kv, qq, G, scores, lo, hi, k, ws, ns,
-                                                          scale_log2, idx, count, out);
+    finish_attend_kernel<4><<<grid, kRowThreads, 0, st>>>(kv, qq, G, scores, lo, hi, k, ws, ns,
+                                                          scale_log2, idx, count, out, S, part);
   else
-    finish_attend_kernel<8><<<rows, kRowThreads, 0, st>>>(kv, qq, G, scores, lo, hi, k, ws, ns,
-                                                          scale_log2, idx, count, out);
-  return hipGetLastError();
+    finish_attend_kernel<8><<<grid, kRowThreads, 0, st>>>(kv, qq, G, scores, lo, hi, k, ws, ns,
+                                                          scale_log2, idx, count, out, S, part);
+  e = hipGetLastError();
+  if (e != hipSuccess || S == 1) return e;
+  return launch_attend_reduce(part, S, kD, kv.H * G, kv.B, out, st, ws.hist, G, ws.copies, ws.ctr);
 }
 
 }  // namespace skv

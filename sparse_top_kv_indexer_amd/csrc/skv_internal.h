@@ -94,18 +94,18 @@ hipError_t launch_select_attend(const KvArgs& kv, const void* q, int G, const fl
                                 float* out, hipStream_t s);
 
 // select_attend.hip: rows longer than one sweep, after a scan that left the
-// histograms in the top-k workspace: the slice listing, then one workgroup
-// per row that finishes the exact top-k (idx, count) and attends over the
-// whole selection with sink and local, writing out (bf16, d = 128, G <= 8,
-// k <= 4096, at least kFinishAttendMinRows rows: one workgroup per row
-// streams K/V rows at a CU's rate, so with few rows the split attention over
-// every CU is faster -- 32 rows of 131,072 took 46.5 us here against 31.4 us
-// for finish + split attention + merge, 256 rows of 65,536 73.3 against 83.5)
+// histograms in the top-k workspace: the slice listing, then a kernel whose
+// workgroups finish the row's exact top-k (idx, count) and attend over it
+// with sink and local -- one per row writing out directly when there are at
+// least kFinishAttendMinRows rows (one workgroup per row streams K/V rows at
+// a CU's rate, so few rows split the row over kFinishSplitsFew workgroups,
+// whose partials part the merge adds) (bf16, d = 128, G <= 8, k <= 4096)
 constexpr int kFinishAttendMinRows = 128;
+constexpr int kFinishSplitsFew = 8;
 bool finish_attend_supported(const KvArgs& kv, int G, int k);
 hipError_t launch_finish_attend(const KvArgs& kv, const void* q, int G, const float* scores,
                                 const int32_t* lo, const int32_t* hi, int k, void* topk_ws,
-                                float scale, int32_t* idx, int32_t* count, float* out,
+                                float scale, int32_t* idx, int32_t* count, float* out, float* part,
                                 hipStream_t st);
 
 // mla.hip: shared-latent attention on matrix cores (v == nullptr)

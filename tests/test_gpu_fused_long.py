@@ -5,8 +5,8 @@ attention kernel: the slice listing, then every attending workgroup resolves
 the row's selection from the list itself.  GQA rows (sparsekv_select_attend
 and its resume) take the slice-listing top-k and the split attention inside
 the same call: with 128 rows or more one workgroup per row finishes the
-selection and attends over all of it (no split merge), with fewer the split
-attention follows the finish.  Checked against the float64 oracle (selection set, attention
+selection and attends over all of it (no split merge), with fewer 8
+workgroups per row each finish it and attend an eighth, then the merge.  Checked against the float64 oracle (selection set, attention
 within 2e-3) and against the separate calls, including rows whose candidate
 list overflows (many tied scores) so that the selection falls back to reading
 the row per digit."""

@@ -221,9 +221,10 @@ skv_status sparsekv_gather_attend(const skv_kv* kv, const void* q, int32_t G, co
  * Supports bf16 keys and values with d_k == d_v == 128 and 1 <= G <= 8, any
  * L_max.  Rows of at most one 32768-slot sweep (L_max <= 32768, or 32765 when
  * L_max is not a multiple of 4) take the fused kernel; longer rows take the
- * slice-listing top-k, then -- with 128 rows or more and k <= 4096 -- one
- * kernel that finishes each row's selection and attends over all of it,
- * else the finish, the split attention and its merge, inside the same call.
+ * slice listing, then (k <= 4096) one kernel that finishes each row's
+ * selection and attends over it -- one workgroup per row with 128 rows or
+ * more, else 8 per row followed by the split merge -- or else the finish,
+ * the split attention and its merge, all inside the same call.
  * ws: sparsekv_workspace_size(SKV_OP_SELECT_ATTEND, kv, G, k, NULL) bytes,
  * zero-filled before its first use; every call leaves its first region (the
  * key histograms) zero again. */

@@ -190,6 +190,16 @@ def test_fused_gqa_long_many_rows_list_overflow_fallback():
     assert int(cnt[3, 5]) == 1500 and idx[3, 5].cpu().numpy().tolist() == list(range(4, 1504))
 
 
+@pytest.mark.parametrize("B,H,G,L,k", [(127, 1, 2, 33024, 700), (64, 2, 3, 40000, 1024),
+                                       (16, 8, 1, 36000, 33)])
+def test_fused_gqa_long_rows_around_the_one_workgroup_threshold(B, H, G, L, k):
+    """127 rows (8 workgroups per row and the merge) against 128 (one
+    workgroup per row, no merge), with G not a power of two and a small k."""
+    st = W.make_gqa_paged(tag=750 + B, B=B, H=H, G=G, L=L, k=k, sink=4, local=64)
+    rows = [(b, h) for b in range(0, B, max(1, B // 8)) for h in range(H)][:24]
+    assert _check_gqa(st, rows=rows) == 0
+
+
 def test_fused_gqa_long_many_rows_window_edges():
     """128 rows through the one-workgroup-per-row kernel with edge windows:
     no candidates (lo == hi), fewer candidates than k, a sequence of 40

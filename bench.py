@@ -521,7 +521,15 @@ def bench_dense(args, hip):
     for b in range(B):
         t_live = W.live_tokens(st.kv, b)
         n_att += int(((t_live < st.lo[b]) | (t_live >= st.hi[b])).sum()) * kv.H
-    row_bytes = (kv.d_k * (2 if bf else 4)) * (1 if mla else 2)
+    # per attended token: its K and V rows (the latent row once); the fused
+    # call with one query head takes the logit from the scan's score instead
+    # of the K row
+    if mla:
+        row_bytes = kv.d_k * (2 if bf else 4)
+    elif fused and G == 1:
+        row_bytes = kv.d_v * (2 if bf else 4) + 4
+    else:
+        row_bytes = 2 * kv.d_k * (2 if bf else 4)
     gather_bytes = n_att * row_bytes
     step_bytes = scan_bytes + gather_bytes
     scan_s = scan_iso_ms * 1e-3

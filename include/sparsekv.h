@@ -224,7 +224,10 @@ skv_status sparsekv_gather_attend(const skv_kv* kv, const void* q, int32_t G, co
  * slice listing, then (k <= 4096) one kernel that finishes each row's
  * selection and attends over it -- one workgroup per row with 128 rows or
  * more, else 8 per row followed by the split merge -- or else the finish,
- * the split attention and its merge, all inside the same call.
+ * the split attention and its merge, all inside the same call.  With one
+ * query head per KV head (G == 1) a token's score is its attention logit
+ * (q . k), so the attention takes it from scores and reads only the value
+ * rows.
  * ws: sparsekv_workspace_size(SKV_OP_SELECT_ATTEND, kv, G, k, NULL) bytes,
  * zero-filled before its first use; every call leaves its first region (the
  * key histograms) zero again. */
@@ -237,7 +240,8 @@ skv_status sparsekv_select_attend(const skv_kv* kv, const void* q, int32_t G, sk
  * schedule the score scan separately: after sparsekv_score_hist(kv, q, G, win,
  * scores, ws, ...) on the same ws, the exact top-k, gather + attention and
  * split merge (same arguments and results as sparsekv_select_attend; scores
- * is read, not written).
+ * is read, not written: for G == 1 it must hold that scan's q . K of this
+ * kv, since the attention uses it as the logits).
  * Also the indexer + shared-latent step (ECHO-OSDI26 wiki page, problem and
  * motivation: an indexer scores every key, attention runs over its top-k of
  * a latent KV): kv a latent KV (v == NULL, bf16, d_k = 576, d_v = 512,

@@ -49,7 +49,10 @@ constexpr int kD = 128;
 // kv's table).  Qf: the MFMA B operand of the G query rows.  With out !=
 // nullptr (a workgroup that attends the row's whole selection) the merged
 // result is written normalised to out[row][g][:] (0 for an empty row) in
-// place of a split partial.
+// place of a split partial.  lrow (G = 1 only, else null): the row's scores
+// from the scan, which for one query head are the logits q . k themselves,
+// so the key rows are not read again and only the value rows are gathered
+// (the scan's fp32 dot products stand in for the attention's own).
 template <int GMAX>
 __device__ __forceinline__ void attend_share(const KvArgs& kv, int G, int row, int b, int h, int s,
                                              int n_split, const int32_t* lst, int n_list, int x0,
@@ -58,7 +61,8 @@ __device__ __forceinline__ void attend_share(const KvArgs& kv, int G, int row, i
                                              float scale_log2, float* part,
                                              int64_t (&rows_sh)[kRowWaves][2][16],
                                              float (&red)[kRowWaves][4][kD + 2],
-                                             float* out = nullptr) {
+                                             float* out = nullptr, const float* lrow = nullptr,
+                                             float (*zsh)[2][16] = nullptr) {
   const int lane = threadIdx.x & 63, wave = row_wave();
   const int n = lane & 15, g4 = lane >> 4;
 
@@ -94,6 +98,7 @@ __device__ __forceinline__ void attend_share(const KvArgs& kv, int G, int row, i
         }
       }
       rows_sh[wave][u][lane & 15] = slot >= 0 ? row_elem(kv, b, h, slot, kD) : -1;
+      if (lrow) zsh[wave][u][lane & 15] = slot >= 0 ? lrow[t] * scale_log2 : -INFINITY;
     }
     bf16x8_t Kf[2][4];
     uint32_t Vw[2][16];
@@ -102,7 +107,8 @@ __device__ __forceinline__ void attend_share(const KvArgs& kv, int G, int row, i
       const int64_t rk = rows_sh[wave][u][n];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const u32x4_t v = rk >= 0 ? ld16((const char*)(kb + rk + 8 * (4 * j + g4))) : u32x4_t{0, 0, 0, 0};
+        const u32x4_t v = (rk >= 0 && !lrow) ? ld16((const char*)(kb + rk + 8 * (4 * j + g4)))
+                                             : u32x4_t{0, 0, 0, 0};
         Kf[u][j] = __builtin_bit_cast(bf16x8_t, v);
       }
 #pragma unroll
@@ -115,14 +121,17 @@ __device__ __forceinline__ void attend_share(const KvArgs& kv, int G, int row, i
     for (int u = 0; u < 2; ++u) {
       if (c0 + u * kRowWaves >= n_ch) break;
       f32x4_t S = {0.f, 0.f, 0.f, 0.f};
+      if (!lrow) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Kf[u][j], Qf[j], S, 0, 0, 0);
+        for (int j = 0; j < 4; ++j)
+          S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Kf[u][j], Qf[j], S, 0, 0, 0);
+      }
       // lane (n, g4) holds the logits of query head n for tokens 4 g4 .. 4 g4 + 3
       float z[4], cm = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const bool ok = rows_sh[wave][u][4 * g4 + i] >= 0;
-        z[i] = ok ? S[i] * scale_log2 : -INFINITY;
+        z[i] = !ok ? -INFINITY : lrow ? zsh[wave][u][4 * g4 + i] : S[i] * scale_log2;
         cm = fmaxf(cm, z[i]);
       }
       cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
@@ -227,6 +236,7 @@ __global__ __launch_bounds__(kRowThreads) void select_attend_kernel(
   __shared__ int64_t rows_sh[kRowWaves][2][16];     // per wave: key-row offsets of two chunks
   __shared__ float red[kRowWaves][4][kD + 2];       // merge of the waves, 4 heads a round
   __shared__ int32_t tbl[kSweep / 16];              // the row's block-table entries (paged)
+  __shared__ float zsh[kRowWaves][2][16];           // G = 1: the logits from the scores
   // the kSplits workgroups of a row run on one XCD and share its scores in L2
   const int vid = xcd_remap(blockIdx.x, gridDim.x);
   const int s = vid % kSplits, row = vid / kSplits;
@@ -319,7 +329,8 @@ __global__ __launch_bounds__(kRowThreads) void select_attend_kernel(
   for (int u = 0; u < kSweep / 16 / kRowThreads; ++u) tbl[threadIdx.x + u * kRowThreads] = tb[u];
   lds_barrier();   // lst and tbl are complete
   attend_share<GMAX>(kv, G, row, b, h, s, kSplits, lst, n_list, x0, n_att, a_lo, a_hi, seq,
-                     n_blk ? tbl : nullptr, Qf, scale_log2, part, rows_sh, red);
+                     n_blk ? tbl : nullptr, Qf, scale_log2, part, rows_sh, red, nullptr,
+                     G == 1 ? scores + (int64_t)row * kv.L_max : nullptr, zsh);
 }
 
 
@@ -346,6 +357,7 @@ __global__ __launch_bounds__(kRowThreads) void finish_attend_kernel(
   __shared__ int klist_n;
   __shared__ int64_t rows_sh[kRowWaves][2][16];
   __shared__ float red[kRowWaves][4][kD + 2];
+  __shared__ float zsh[kRowWaves][2][16];           // G = 1: the logits from the scores
   // n_split > 1: the row's workgroups run on one XCD (their list and scores
   // then come from its L2); the grid is padded to a multiple of 8
   const int vid = n_split > 1 ? xcd_remap(blockIdx.x, gridDim.x) : blockIdx.x;
@@ -398,7 +410,8 @@ __global__ __launch_bounds__(kRowThreads) void finish_attend_kernel(
   const int x0 = (int)((int64_t)n_extra * s / n_split);
   const int n_att = (r1 - r0) + (int)((int64_t)n_extra * (s + 1) / n_split) - x0;
   attend_share<GMAX>(kv, G, row, b, h, s, n_split, lst + r0, r1 - r0, x0, n_att, a_lo, a_hi, seq,
-                     nullptr, Qf, scale_log2, part, rows_sh, red, n_split == 1 ? out : nullptr);
+                     nullptr, Qf, scale_log2, part, rows_sh, red, n_split == 1 ? out : nullptr,
+                     G == 1 ? scores + (int64_t)row * kv.L_max : nullptr, zsh);
 }
 
 }  // namespace

@@ -293,7 +293,7 @@ __global__ __launch_bounds__(kRowThreads) void mla_list_kernel(
                             ws.hist + (int64_t)row * ws.copies * kBins, L, klist_n, gv);
   } else {
     n_sel = list_select(ws, row, k, n_slices, gv, L, s_off, s_at,
-                        [&](int dst, int p) { L.hist[dst] = (uint32_t)p; });
+                        [&](int dst, int p, uint32_t) { L.hist[dst] = (uint32_t)p; });
     lds_barrier();
   }
   if (s == 0 && hp == 0) {

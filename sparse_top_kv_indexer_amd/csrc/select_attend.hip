@@ -52,7 +52,9 @@ constexpr int kD = 128;
 // place of a split partial.  lrow (G = 1 only, else null): the row's scores
 // from the scan, which for one query head are the logits q . k themselves,
 // so the key rows are not read again and only the value rows are gathered
-// (the scan's fp32 dot products stand in for the attention's own).
+// (the scan's fp32 dot products stand in for the attention's own); lkey
+// (with lrow, or null): the listed tokens' score keys, already in LDS, so
+// only the sink / local tokens' scores are read from lrow.
 template <int GMAX>
 __device__ __forceinline__ void attend_share(const KvArgs& kv, int G, int row, int b, int h, int s,
                                              int n_split, const int32_t* lst, int n_list, int x0,
@@ -62,7 +64,8 @@ __device__ __forceinline__ void attend_share(const KvArgs& kv, int G, int row, i
                                              int64_t (&rows_sh)[kRowWaves][2][16],
                                              float (&red)[kRowWaves][4][kD + 2],
                                              float* out = nullptr, const float* lrow = nullptr,
-                                             float (*zsh)[2][16] = nullptr) {
+                                             float (*zsh)[2][16] = nullptr,
+                                             const uint32_t* lkey = nullptr) {
   const int lane = threadIdx.x & 63, wave = row_wave();
   const int n = lane & 15, g4 = lane >> 4;
 
@@ -98,7 +101,10 @@ __device__ __forceinline__ void attend_share(const KvArgs& kv, int G, int row, i
         }
       }
       rows_sh[wave][u][lane & 15] = slot >= 0 ? row_elem(kv, b, h, slot, kD) : -1;
-      if (lrow) zsh[wave][u][lane & 15] = slot >= 0 ? lrow[t] * scale_log2 : -INFINITY;
+      if (lrow)
+        zsh[wave][u][lane & 15] =
+            slot < 0 ? -INFINITY
+                     : (lkey && i < n_list ? key_score(lkey[i]) : lrow[t]) * scale_log2;
     }
     bf16x8_t Kf[2][4];
     uint32_t Vw[2][16];
@@ -353,6 +359,7 @@ __global__ __launch_bounds__(kRowThreads) void finish_attend_kernel(
     int32_t* count, float* out, int n_split, float* part) {
   __shared__ RowSelLds L;
   __shared__ int32_t sel[kFinishK];                 // the selection, ascending
+  __shared__ uint32_t selk[kFinishK];               // and its score keys
   __shared__ int s_off[kFinishSlices + 1], s_at[kFinishSlices];
   __shared__ int klist_n;
   __shared__ int64_t rows_sh[kRowWaves][2][16];
@@ -380,13 +387,17 @@ __global__ __launch_bounds__(kRowThreads) void finish_attend_kernel(
   const uint4 gv = hist_bins_summed(ws, row);
   int n_sel;
   const int32_t* lst;
+  const uint32_t* lk = nullptr;   // the selection's score keys (not after the fallback)
   if (ws.meta[2 * row + 1] < 0) {
     n_sel = fallback_select(scores, row, kv.H, kv.L_max, lo_p, hi_p, k, ghist, L, klist_n, gv);
     lst = (const int32_t*)L.hist;   // the positions, ascending
   } else {
-    n_sel = list_select(ws, row, k, n_slices, gv, L, s_off, s_at,
-                        [&](int dst, int p) { sel[dst] = p; });
+    n_sel = list_select(ws, row, k, n_slices, gv, L, s_off, s_at, [&](int dst, int p, uint32_t key) {
+      sel[dst] = p;
+      selk[dst] = key;
+    });
     lst = sel;
+    lk = selk;
   }
   lds_barrier();
   if (s == 0) {
@@ -411,7 +422,8 @@ __global__ __launch_bounds__(kRowThreads) void finish_attend_kernel(
   const int n_att = (r1 - r0) + (int)((int64_t)n_extra * (s + 1) / n_split) - x0;
   attend_share<GMAX>(kv, G, row, b, h, s, n_split, lst + r0, r1 - r0, x0, n_att, a_lo, a_hi, seq,
                      nullptr, Qf, scale_log2, part, rows_sh, red, n_split == 1 ? out : nullptr,
-                     G == 1 ? scores + (int64_t)row * kv.L_max : nullptr, zsh);
+                     G == 1 ? scores + (int64_t)row * kv.L_max : nullptr, zsh,
+                     lk ? lk + r0 : nullptr);
 }
 
 }  // namespace

@@ -221,8 +221,9 @@ __device__ __forceinline__ int row_select_alone(const float* scores, int row, in
 // into s_off / s_at (n_slices <= the arrays' room), the list (kPer
 // consecutive ranks per lane, as 16-byte loads), resolves the exact threshold
 // T and the number of keys equal to T to take (lowest positions first) with
-// two more digits over the listed keys, then calls emit(dst, pos) for every
-// selected key with dst < k, dst being its rank in ascending position order.
+// two more digits over the listed keys, then calls emit(dst, pos, key) for
+// every selected key with dst < k, dst being its rank in ascending position
+// order (key: its order-preserving score key, key_score(key) the score).
 // gv: this thread's 4 bins (4 t .. 4 t + 3) of the row's histogram, summed
 // over its copies.  Only reads memory; every workgroup of a row may run it.
 // Returns the number selected, min(k, finite candidates).
@@ -333,7 +334,7 @@ __device__ __forceinline__ int list_select(const TopkWs& ws, int row, int k, int
         if (eb < need_eq) dst = ab + eb;
         ++eb;
       }
-      if (dst >= 0 && dst < k) emit(dst, pos[u]);
+      if (dst >= 0 && dst < k) emit(dst, pos[u], key[u]);
     }
   }
   return min(k, ta + min(te, need_eq));

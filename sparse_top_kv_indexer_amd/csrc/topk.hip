@@ -334,7 +334,8 @@ __global__ __launch_bounds__(kRowThreads) void topk_finish_kernel(
     // the selection is staged in LDS (the list buffer of the fallback) when
     // it fits, then written in one coalesced pass
     const bool stage = k <= kListCap;
-    const int n_sel = list_select(ws, row, k, n_slices, gv, L, s_off, s_at, [&](int dst, int p) {
+    const int n_sel = list_select(ws, row, k, n_slices, gv, L, s_off, s_at, [&](int dst, int p,
+                                                                               uint32_t) {
       if (stage) klist[dst] = (uint32_t)p;
       else if constexpr (MAP == 0) orow[dst] = p;
       else orow[dst] = map_b[map_a[(int64_t)row * map_ld + p]];

@@ -49,12 +49,13 @@ constexpr int kD = 128;
 // kv's table).  Qf: the MFMA B operand of the G query rows.  With out !=
 // nullptr (a workgroup that attends the row's whole selection) the merged
 // result is written normalised to out[row][g][:] (0 for an empty row) in
-// place of a split partial.  lrow (G = 1 only, else null): the row's scores
-// from the scan, which for one query head are the logits q . k themselves,
-// so the key rows are not read again and only the value rows are gathered
-// (the scan's fp32 dot products stand in for the attention's own); lkey
-// (with lrow, or null): the listed tokens' score keys, already in LDS, so
-// only the sink / local tokens' scores are read from lrow.
+// place of a split partial.  GMAX = 1 (G = 1, one query head): lrow is the
+// row's scores from the scan, which for one query head are the logits q . k
+// themselves, so the key rows are not read again and only the value rows are
+// gathered (the scan's fp32 dot products stand in for the attention's own),
+// and the key-row and matrix-core code is not compiled in; lkey (or null):
+// the listed tokens' score keys, already in LDS, so only the sink / local
+// tokens' scores are read from lrow.  GMAX > 1: lrow and lkey are unused.
 template <int GMAX>
 __device__ __forceinline__ void attend_share(const KvArgs& kv, int G, int row, int b, int h, int s,
                                              int n_split, const int32_t* lst, int n_list, int x0,
@@ -66,6 +67,7 @@ __device__ __forceinline__ void attend_share(const KvArgs& kv, int G, int row, i
                                              float* out = nullptr, const float* lrow = nullptr,
                                              float (*zsh)[2][16] = nullptr,
                                              const uint32_t* lkey = nullptr) {
+  constexpr bool kFromScores = GMAX == 1;
   const int lane = threadIdx.x & 63, wave = row_wave();
   const int n = lane & 15, g4 = lane >> 4;
 
@@ -101,21 +103,23 @@ __device__ __forceinline__ void attend_share(const KvArgs& kv, int G, int row, i
         }
       }
       rows_sh[wave][u][lane & 15] = slot >= 0 ? row_elem(kv, b, h, slot, kD) : -1;
-      if (lrow)
+      if constexpr (kFromScores)
         zsh[wave][u][lane & 15] =
             slot < 0 ? -INFINITY
                      : (lkey && i < n_list ? key_score(lkey[i]) : lrow[t]) * scale_log2;
     }
-    bf16x8_t Kf[2][4];
+    bf16x8_t Kf[kFromScores ? 1 : 2][4];
     uint32_t Vw[2][16];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int64_t rk = rows_sh[wave][u][n];
+      if constexpr (!kFromScores) {
+        const int64_t rk = rows_sh[wave][u][n];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const u32x4_t v = (rk >= 0 && !lrow) ? ld16((const char*)(kb + rk + 8 * (4 * j + g4)))
-                                             : u32x4_t{0, 0, 0, 0};
-        Kf[u][j] = __builtin_bit_cast(bf16x8_t, v);
+        for (int j = 0; j < 4; ++j) {
+          const u32x4_t v = rk >= 0 ? ld16((const char*)(kb + rk + 8 * (4 * j + g4)))
+                                    : u32x4_t{0, 0, 0, 0};
+          Kf[u][j] = __builtin_bit_cast(bf16x8_t, v);
+        }
       }
 #pragma unroll
       for (int t = 0; t < 16; ++t) {
@@ -127,7 +131,7 @@ __device__ __forceinline__ void attend_share(const KvArgs& kv, int G, int row, i
     for (int u = 0; u < 2; ++u) {
       if (c0 + u * kRowWaves >= n_ch) break;
       f32x4_t S = {0.f, 0.f, 0.f, 0.f};
-      if (!lrow) {
+      if constexpr (!kFromScores) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Kf[u][j], Qf[j], S, 0, 0, 0);
@@ -137,7 +141,7 @@ __device__ __forceinline__ void attend_share(const KvArgs& kv, int G, int row, i
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const bool ok = rows_sh[wave][u][4 * g4 + i] >= 0;
-        z[i] = !ok ? -INFINITY : lrow ? zsh[wave][u][4 * g4 + i] : S[i] * scale_log2;
+        z[i] = !ok ? -INFINITY : kFromScores ? zsh[wave][u][4 * g4 + i] : S[i] * scale_log2;
         cm = fmaxf(cm, z[i]);
       }
       cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
@@ -342,13 +346,15 @@ __global__ __launch_bounds__(kRowThreads) void select_attend_kernel(
 
 // ------------------------------------------ rows longer than one sweep --
 // After the slice listing (the exact top-k's list in the top-k workspace),
-// one workgroup per row finishes the selection from the list (list_select,
-// the row alone when the list overflowed), writes idx and count, and attends
-// over the whole selection plus the sink and local tokens with the 16 waves
-// of attend_share, writing the row's normalised output: no split partials
-// and no merge kernel, so the step is scan, listing and this kernel.  Many
-// rows (one workgroup per CU or more) keep every CU streaming K/V rows; the
-// rows' histograms and list counters are zeroed here, after their last read.
+// every one of a row's n_split workgroups finishes the selection from the
+// list (list_select; the row alone, fallback_select, when the list
+// overflowed), and attends over its share of the selection plus the sink and
+// local tokens with the 16 waves of attend_share.  Many rows: one workgroup
+// per row, which writes idx, count and the row's normalised output (no split
+// partials, no merge kernel, so the step is scan, listing and this kernel)
+// and zeroes the row's histogram and list counter after their last read;
+// every CU streams K/V rows.  Fewer rows: n_split workgroups per row and the
+// merge, which zeroes them.
 constexpr int kFinishSlices = 1024;   // listing slices of a row this kernel reads
 constexpr int kFinishK = kBins;       // selected keys it stages (k <= 4096)
 
@@ -443,7 +449,10 @@ hipError_t launch_select_attend(const KvArgs& kv, const void* q, int G, const fl
                                 float* out, hipStream_t st) {
   const float scale_log2 = scale * 1.4426950408889634f;
   const dim3 grid(kSplits * kv.B * kv.H);   // a multiple of 8
-  if (G <= 4)
+  if (G == 1)
+    select_attend_kernel<1><<<grid, kRowThreads, 0, st>>>(kv, (const uint16_t*)q, G, scores, lo, hi,
+                                                          k, hist, scale_log2, idx, count, part);
+  else if (G <= 4)
     select_attend_kernel<4><<<grid, kRowThreads, 0, st>>>(kv, (const uint16_t*)q, G, scores, lo, hi,
                                                           k, hist, scale_log2, idx, count, part);
   else
@@ -483,7 +492,10 @@ hipError_t launch_finish_attend(const KvArgs& kv, const void* q, int G, const fl
   const uint16_t* qq = (const uint16_t*)q;
   const int S = finish_attend_splits(kv, G, k);
   const unsigned grid = S == 1 ? (unsigned)rows : (unsigned)((rows * S + 7) / 8 * 8);
-  if (G <= 4)
+  if (G == 1)
+    finish_attend_kernel<1><<<grid, kRowThreads, 0, st>>>(kv, qq, G, scores, lo, hi, k, ws, ns,
+                                                          scale_log2, idx, count, out, S, part);
+  else if (G <= 4)
     finish_attend_kernel<4><<<grid, kRowThreads, 0, st>>>(kv, qq, G, scores, lo, hi, k, ws, ns,
                                                           scale_log2, idx, count, out, S, part);
   else

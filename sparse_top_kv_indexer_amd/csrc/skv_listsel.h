@@ -215,6 +215,59 @@ __device__ __forceinline__ int row_select_alone(const float* scores, int row, in
 }
 
 
+// Steps 2 and 3 of a list selection: the listed keys (every key of the bins
+// at or above the k-th key's bin, in position order) are held KPER
+// consecutive list ranks per lane (lane t: ranks KPER t .. KPER t + KPER - 1,
+// key 0 past the list's end, which is never selected), pos their positions.
+// Resolves the exact threshold T and the number of keys equal to T to take
+// (lowest positions first) with two more digits over the listed keys, then
+// calls emit(dst, pos, key) for every selected key with dst < k, dst being
+// its rank in ascending position order.  gv: this thread's 4 bins of the
+// row's first-digit histogram.  Returns min(k, finite candidates).
+template <int KPER, typename Emit>
+__device__ __forceinline__ int select_listed(int k, uint4 gv, RowSelLds& L,
+                                             const uint32_t (&key)[KPER], const int (&pos)[KPER],
+                                             Emit&& emit) {
+  // threshold over the listed keys
+  *(uint4*)(L.hist + 4 * threadIdx.x) = gv;
+  if (threadIdx.x < 256) L.dh[threadIdx.x] = 0u;
+  lds_barrier();
+  uint32_t T;
+  int need_eq, k_sel;
+  row_threshold(
+      L, k, []() {},
+      [&](auto&& f) {
+#pragma unroll
+        for (int u = 0; u < KPER; ++u) f(key[u]);
+      },
+      &T, &need_eq, &k_sel);
+
+  // ranks: the lane's entries are consecutive list ranks
+  int c = 0;
+#pragma unroll
+  for (int u = 0; u < KPER; ++u)
+    c += key[u] > T ? 1 : ((key[u] != 0u && key[u] == T) ? 0x10000 : 0);
+  const int inc = wave_incl_scan(c);
+  int oa, oe, ta, te;
+  row_wave_offsets(L, c, &oa, &oe, &ta, &te);
+  int ab = oa + ((inc - c) & 0xffff), eb = oe + ((inc - c) >> 16);
+  if (c) {
+#pragma unroll
+    for (int u = 0; u < KPER; ++u) {
+      int dst = -1;
+      if (key[u] > T) {
+        dst = ab + min(eb, need_eq);
+        ++ab;
+      } else if (key[u] != 0u && key[u] == T) {
+        if (eb < need_eq) dst = ab + eb;
+        ++eb;
+      }
+      if (dst >= 0 && dst < k) emit(dst, pos[u], key[u]);
+    }
+  }
+  return min(k, ta + min(te, need_eq));
+}
+
 // Exact selection of row `row` from the list the slice-listing kernel left in
 // ws (every key of the bins at or above the k-th key's bin, slice by slice in
 // position order; ws.meta[2 row + 1] >= 0): reads the slices' list offsets
@@ -300,44 +353,7 @@ __device__ __forceinline__ int list_select(const TopkWs& ws, int row, int k, int
     }
   }
 
-  // 2. threshold over the listed keys (all keys of bins >= b0)
-  *(uint4*)(L.hist + 4 * threadIdx.x) = gv;
-  if (threadIdx.x < 256) L.dh[threadIdx.x] = 0u;
-  lds_barrier();
-  uint32_t T;
-  int need_eq, k_sel;
-  row_threshold(
-      L, k, []() {},
-      [&](auto&& f) {
-#pragma unroll
-        for (int u = 0; u < kPer; ++u) f(key[u]);
-      },
-      &T, &need_eq, &k_sel);
-
-  // 3. ranks: the lane's entries are consecutive list ranks
-  int c = 0;
-#pragma unroll
-  for (int u = 0; u < kPer; ++u)
-    c += key[u] > T ? 1 : ((key[u] != 0u && key[u] == T) ? 0x10000 : 0);
-  const int inc = wave_incl_scan(c);
-  int oa, oe, ta, te;
-  row_wave_offsets(L, c, &oa, &oe, &ta, &te);
-  int ab = oa + ((inc - c) & 0xffff), eb = oe + ((inc - c) >> 16);
-  if (c) {
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      int dst = -1;
-      if (key[u] > T) {
-        dst = ab + min(eb, need_eq);
-        ++ab;
-      } else if (key[u] != 0u && key[u] == T) {
-        if (eb < need_eq) dst = ab + eb;
-        ++eb;
-      }
-      if (dst >= 0 && dst < k) emit(dst, pos[u], key[u]);
-    }
-  }
-  return min(k, ta + min(te, need_eq));
+  return select_listed<kPer>(k, gv, L, key, pos, emit);
 }
 
 // The selection of a row whose list overflowed, for kernels that finish the

@@ -190,6 +190,21 @@ def test_fused_gqa_long_many_rows_list_overflow_fallback():
     assert int(cnt[3, 5]) == 1500 and idx[3, 5].cpu().numpy().tolist() == list(range(4, 1504))
 
 
+def test_fused_gqa_long_many_rows_tied_run():
+    """128 rows, one query head; in one row 10,000 tokens tie for the top
+    score, so its list holds 10,000 keys of one value (fewer than the 16,384
+    a list holds) and the k taken are the lowest positions."""
+    st = W.make_gqa_paged(tag=744, B=16, H=8, G=1, L=40960, k=1500, sink=4, local=64)
+    qf = (st.q[3, 5].astype(np.uint32) << 16).view(np.float32)
+    kb = (((qf * 4).view(np.uint32) + 0x8000) >> 16).astype(np.uint16)   # bf16 of 4 q
+    st.kv.k[st.kv.block_table[3][:625], 5] = kb                          # tokens 0 .. 9999
+    rows = [(3, 5), (3, 4), (0, 0), (15, 7)]
+    assert _check_gqa(st, rows=rows) == 0
+    r = Run(st)
+    _, idx, cnt, _ = r.select_attend()
+    assert int(cnt[3, 5]) == 1500 and idx[3, 5].cpu().numpy().tolist() == list(range(4, 1504))
+
+
 @pytest.mark.parametrize("B,H,G,L,k", [(127, 1, 2, 33024, 700), (64, 2, 3, 40000, 1024),
                                        (16, 8, 1, 36000, 33)])
 def test_fused_gqa_long_rows_around_the_one_workgroup_threshold(B, H, G, L, k):

@@ -220,11 +220,14 @@ skv_status sparsekv_gather_attend(const skv_kv* kv, const void* q, int32_t G, co
  * observation 5; vToken reading notes, section 3.4 Eq. (2)).
  * Supports bf16 keys and values with d_k == d_v == 128 and 1 <= G <= 8, any
  * L_max.  Rows of at most one 32768-slot sweep (L_max <= 32768, or 32765 when
- * L_max is not a multiple of 4) take the fused kernel; longer rows take the
- * slice listing, then (k <= 4096) one kernel that finishes each row's
- * selection and attends over it -- one workgroup per row with 128 rows or
- * more, else 8 per row followed by the split merge -- or else the finish,
- * the split attention and its merge, all inside the same call.  With one
+ * L_max is not a multiple of 4) take the fused kernel; longer rows with
+ * k <= 4096 take one kernel that selects each row and attends over it: with
+ * 128 rows or more one workgroup per row lists the row's candidates itself
+ * (one pass over its scores), selects and attends; with fewer, a slice
+ * listing first, then 8 workgroups per row that each finish the selection
+ * and attend an eighth, and the split merge.  Larger k takes the slice
+ * listing, the finish, the split attention and its merge, all inside the
+ * same call.  With one
  * query head per KV head (G == 1) a token's score is its attention logit
  * (q . k), so the attention takes it from scores and reads only the value
  * rows.

@@ -356,6 +356,125 @@ __device__ __forceinline__ int list_select(const TopkWs& ws, int row, int k, int
   return select_listed<kPer>(k, gv, L, key, pos, emit);
 }
 
+// Exact selection of row `row` by a workgroup that lists the row itself, for
+// kernels that own a whole row (no slice-listing kernel before them): the bin
+// b0 of the k-th largest key from the row's histogram (gv: this thread's 4
+// bins, summed over the copies), then one pass over the window's scores (the
+// next sweep's loads in flight while one is listed) keeps every key of the
+// bins >= b0 with its position in LDS (lk, lp: KPER * kRowThreads entries), in
+// position order, and select_listed finishes over them: emit(dst, pos, key)
+// for every selected key, dst its rank in ascending position order.  Returns
+// the number selected, or -1 when the listed keys would not fit (the caller
+// then selects the row alone).
+template <int KPER, typename Emit>
+__device__ __forceinline__ int local_list_select(const float* scores, int row, int H, int L_max,
+                                                 const int32_t* lo_p, const int32_t* hi_p, int k,
+                                                 uint4 gv, RowSelLds& L, uint32_t* lk, int32_t* lp,
+                                                 Emit&& emit) {
+  constexpr int kCap = KPER * kRowThreads;
+  constexpr int NG = 4;                                // groups of 4 slots per lane per sweep
+  constexpr int kSw = kRowWaves * 256 * NG;            // slots per sweep
+  static_assert(KPER % 4 == 0, "16-byte list reads");
+  const int lane = threadIdx.x & 63, wave = row_wave();
+  RowWindow w = row_window(lo_p, hi_p, row / H, L_max);
+  bool vec;
+  const float* s = row_base(scores, (int64_t)row * L_max, w, &vec);
+  const int n_sweeps = (w.ns + kSw - 1) / kSw;
+  float va[NG][4], vb[NG][4];
+  if (n_sweeps > 0) row_load(s, w, vec, 0, va);
+
+  // 1. the bin of the k-th largest key; every key of the bins above it and of
+  //    the bin itself is listed (lower = its first key)
+  *(uint4*)(L.hist + 4 * threadIdx.x) = gv;
+  lds_barrier();
+  int total;
+  const int k_sel = row_search4096(L, -k, &total);   // min(k, total)
+  if (k_sel <= 0) return 0;
+  uint32_t lower = 1u;   // k_sel == total: every finite key (finite keys are >= 1)
+  int listed = total;
+  if (k_sel < total) {
+    lower = (uint32_t)L.trio[0] << 20;
+    listed = L.trio[1] + L.trio[2];
+  }
+  if (listed > kCap) return -1;
+
+  // 2. the listing, sweep by sweep; in a sweep wave w holds slots
+  //    w 256 NG + 256 g + 4 lane + e, so ranks go wave, group, lane, element
+  //    (the keys are formed twice, for the counts and for the stores, rather
+  //    than held)
+  int base = 0;
+  auto list_sweep = [&](const float (&f)[NG][4], int sw) {
+    int cg[NG], ig[NG], wt = 0;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      int c = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) c += score_key(f[g][e]) >= lower;
+      cg[g] = c;
+      ig[g] = wave_incl_scan(c);
+      wt += wave_total(ig[g]);
+    }
+    lds_barrier();   // earlier readers of L.wt are done
+    if (lane == 0) L.wt[wave] = wt;
+    lds_barrier();
+    int o = base, all = 0;
+#pragma unroll
+    for (int u = 0; u < kRowWaves; ++u) {
+      if (u < wave) o += L.wt[u];
+      all += L.wt[u];
+    }
+    const int pos0 = w.lo - w.o + row_slot0<NG>(sw);
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      int d = o + ig[g] - cg[g];
+      if (cg[g]) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t key = score_key(f[g][e]);
+          if (key >= lower) {
+            if (d < kCap) {
+              lk[d] = key;
+              lp[d] = pos0 + 256 * g + e;
+            }
+            ++d;
+          }
+        }
+      }
+      o += wave_total(ig[g]);
+    }
+    base += all;
+  };
+  for (int sw = 0; sw < n_sweeps; sw += 2) {
+    if (sw + 1 < n_sweeps) row_load(s, w, vec, sw + 1, vb);
+    list_sweep(va, sw);
+    if (sw + 1 < n_sweeps) {
+      if (sw + 2 < n_sweeps) row_load(s, w, vec, sw + 2, va);
+      list_sweep(vb, sw + 1);
+    }
+  }
+  if (base > kCap) return -1;   // (the histogram promised fewer)
+  lds_barrier();                // the list is complete
+
+  // 3. ranks KPER t .. KPER t + KPER - 1 per lane, then the exact threshold
+  uint32_t key[KPER];
+  int pos[KPER];
+#pragma unroll
+  for (int u = 0; u < KPER; u += 4) {
+    const int r = KPER * threadIdx.x + u;
+    const uint4 kq = r < base ? *(const uint4*)(lk + r) : make_uint4(0u, 0u, 0u, 0u);
+    const int4 pq = r < base ? *(const int4*)(lp + r) : make_int4(0, 0, 0, 0);
+    key[u] = r < base ? kq.x : 0u;
+    key[u + 1] = r + 1 < base ? kq.y : 0u;
+    key[u + 2] = r + 2 < base ? kq.z : 0u;
+    key[u + 3] = r + 3 < base ? kq.w : 0u;
+    pos[u] = pq.x;
+    pos[u + 1] = pq.y;
+    pos[u + 2] = pq.z;
+    pos[u + 3] = pq.w;
+  }
+  return select_listed<KPER>(k, gv, L, key, pos, emit);
+}
+
 // The selection of a row whose list overflowed, for kernels that finish the
 // selection themselves: the row alone, re-read per digit, the positions left
 // in L.hist[0 .. n) ascending (k <= 4096).  Rare; kept out of line so its

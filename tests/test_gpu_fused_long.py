@@ -4,8 +4,9 @@ the indexer's sparsekv_score_hist) finishes the exact top-k inside the
 attention kernel: the slice listing, then every attending workgroup resolves
 the row's selection from the list itself.  GQA rows (sparsekv_select_attend
 and its resume) take the slice-listing top-k and the split attention inside
-the same call: with 128 rows or more one workgroup per row finishes the
-selection and attends over all of it (no split merge), with fewer 8
+the same call: with 128 rows or more one workgroup per row lists its row
+itself (no listing kernel), selects and attends over all of the selection
+(no split merge), with fewer 8
 workgroups per row each finish it and attend an eighth, then the merge.  Checked against the float64 oracle (selection set, attention
 within 2e-3) and against the separate calls, including rows whose candidate
 list overflows (many tied scores) so that the selection falls back to reading
@@ -190,14 +191,17 @@ def test_fused_gqa_long_many_rows_list_overflow_fallback():
     assert int(cnt[3, 5]) == 1500 and idx[3, 5].cpu().numpy().tolist() == list(range(4, 1504))
 
 
-def test_fused_gqa_long_many_rows_tied_run():
-    """128 rows, one query head; in one row 10,000 tokens tie for the top
-    score, so its list holds 10,000 keys of one value (fewer than the 16,384
-    a list holds) and the k taken are the lowest positions."""
+@pytest.mark.parametrize("n_blocks", [188, 625])
+def test_fused_gqa_long_many_rows_tied_run(n_blocks):
+    """128 rows, one query head; in one row the first 16 n_blocks tokens tie
+    for the top score, and the k taken must be the lowest positions.  With
+    3,008 tied tokens the row's own listing holds them all (at most 4,096
+    keys) and resolves the tie; with 10,000 it would overflow, so the row is
+    selected from the scores alone."""
     st = W.make_gqa_paged(tag=744, B=16, H=8, G=1, L=40960, k=1500, sink=4, local=64)
     qf = (st.q[3, 5].astype(np.uint32) << 16).view(np.float32)
     kb = (((qf * 4).view(np.uint32) + 0x8000) >> 16).astype(np.uint16)   # bf16 of 4 q
-    st.kv.k[st.kv.block_table[3][:625], 5] = kb                          # tokens 0 .. 9999
+    st.kv.k[st.kv.block_table[3][:n_blocks], 5] = kb                     # tokens 0 .. 16 n_blocks - 1
     rows = [(3, 5), (3, 4), (0, 0), (15, 7)]
     assert _check_gqa(st, rows=rows) == 0
     r = Run(st)

@@ -445,6 +445,10 @@ def bench_dense(args, hip):
     blocks = args.path == "blocks"
     if blocks:
         return bench_blocks(args, hip, st, kv, q, lo, hi)
+    # long rows with k <= 2048: the scan lists segment candidates and the
+    # selecting kernel takes them (sparsekv_score_segments +
+    # sparsekv_select_attend_segments); else the histogram scan + resume
+    seg = fused and S.sparsekv_segments(kv, G, k) > 0
     thr = torch.full((B, H), float("-inf"), dtype=torch.float32, device=dev)
     used = torch.zeros((B, H), dtype=torch.int32, device=dev)
     if fused:
@@ -467,6 +471,8 @@ def bench_dense(args, hip):
         s_kv, a_kv = pairs[i % len(pairs)]
         if prefilter:
             S.sparsekv_score_prefilter(s_kv, sq, sG, lo, hi, thr, scores, ws_sel)
+        elif seg:
+            S.sparsekv_score_segments(s_kv, sq, sG, lo, hi, k, scores, ws_sel)
         else:
             S.sparsekv_score_hist(s_kv, sq, sG, lo, hi, scores, ws_sel)
         if mark:
@@ -476,6 +482,9 @@ def bench_dense(args, hip):
             if mark:
                 mark(1)
             S.sparsekv_gather_attend(a_kv, q, G, idx, k, lo, hi, st.scale, out, ws_att)
+        elif seg:
+            S.sparsekv_select_attend_segments(a_kv, q, G, lo, hi, k, st.scale, scores, idx, cnt,
+                                              out, ws_sel)
         elif fused:
             S.sparsekv_select_attend_resume(a_kv, q, G, lo, hi, k, st.scale, scores, idx, cnt, out,
                                             ws_sel)
@@ -498,6 +507,10 @@ def bench_dense(args, hip):
         scan_iso_ms = time_isolated(
             lambda i: S.sparsekv_score_prefilter(pairs[i % len(pairs)][0], sq, sG, lo, hi, thr_iso,
                                                  scores, ws_iso), args, hip)
+    elif seg:
+        scan_iso_ms = time_isolated(
+            lambda i: S.sparsekv_score_segments(pairs[i % len(pairs)][0], sq, sG, lo, hi, k, scores,
+                                                ws_iso), args, hip)
     else:
         scan_iso_ms = time_isolated(
             lambda i: S.sparsekv_score_hist(pairs[i % len(pairs)][0], sq, sG, lo, hi, scores,
@@ -540,7 +553,9 @@ def bench_dense(args, hip):
     cfg = {"workload": args.workload, "B": B, "H_kv": kv.H, "G": G, "d": kv.d_k,
            "L": L, "k": k, "layout": st.kv.mode, "kv_dtype": st.kv.dtype,
            "kv_copies": len(pairs), "launch": "eager" if args.eager else "hip_graph",
-           "path": "fused" if fused else ("prefilter" if prefilter else "separate")}
+           "path": "fused" if fused else ("prefilter" if prefilter else "separate"),
+           "candidates": ("scan segments (%d per row)" % S.sparsekv_segments(kv, G, k) if seg else
+                          "key histogram" if not prefilter else "predicted threshold")}
     if args.workload != "indexer_mla":
         cfg.update(sink=int(st.lo[0]), local=int(st.kv.seq_len[0] - st.hi[0]))
     else:
@@ -568,6 +583,8 @@ def bench_dense(args, hip):
         "step_frac_of_hbm_peak": step_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,
         "roofline": roofline(("score scan (sparsekv_score_prefilter: %s listing the keys above "
                               "the predicted threshold)" if prefilter else
+                              "score scan (sparsekv_score_segments: %s listing segment candidates)"
+                              if seg else
                               "score scan (sparsekv_score_hist: %s with the fused top-k histogram)")
                              % kname, "hbm", scan_bytes, scan_s, tr,
                              {"algorithmic_bytes_per_launch": scan_bytes, "bytes_per_key": per_key,

@@ -223,11 +223,14 @@ skv_status sparsekv_gather_attend(const skv_kv* kv, const void* q, int32_t G, co
  * L_max is not a multiple of 4) take the fused kernel; longer rows with
  * k <= 4096 take one kernel that selects each row and attends over it: with
  * 128 rows or more one workgroup per row lists the row's candidates itself
- * (one pass over its scores), selects and attends; with fewer, a slice
- * listing first, then 8 workgroups per row that each finish the selection
- * and attend an eighth, and the split merge.  Larger k takes the slice
- * listing, the finish, the split attention and its merge, all inside the
- * same call.  With one
+ * (one pass over its scores), selects and attends; with fewer, 8 workgroups
+ * per row each finish the selection and attend an eighth, then the split
+ * merge -- for k <= 2048 from candidates the scan itself lists (each scan
+ * workgroup keeps its segment's highest keys; the exact top-k of those is
+ * the row's whenever no key left out could rank among it, else the row is
+ * selected from its scores), otherwise after a slice listing.  Larger k
+ * takes the slice listing, the finish, the split attention and its merge,
+ * all inside the same call.  With one
  * query head per KV head (G == 1) a token's score is its attention logit
  * (q . k), so the attention takes it from scores and reads only the value
  * rows.
@@ -260,6 +263,70 @@ skv_status sparsekv_select_attend_resume(const skv_kv* kv, const void* q, int32_
                                          const float* scores, int32_t* idx, int32_t* count,
                                          float* out, void* ws, size_t ws_bytes,
                                          hipStream_t stream);
+
+/* The indexer + shared-latent decode step in one call (ECHO-OSDI26 wiki
+ * page, problem and motivation: a separate indexer key cache scores every
+ * history token, and attention over the latent KV runs on the indexer's
+ * top-k only): scores[B][H][L_max] = max over the iG indexer heads of
+ * iq . ikey (as sparsekv_score on ikv), idx / count = the exact top-k of
+ * each row's window by those scores (ascending positions, ties to the lower
+ * position, -1 padded), out[B][H*G][512] = the latent attention of the G
+ * query heads q over the selected tokens plus sink and local (as
+ * sparsekv_gather_attend on kv).  Results equal sparsekv_score_hist(ikv, iq,
+ * iG, ...) followed by sparsekv_select_attend_resume(kv, q, G, ...).
+ * ikv: the indexer's keys (bf16, d_k in {64, 128, 256}; v unused); kv: the
+ * latent KV (v == NULL, bf16, d_k = 576, d_v = 512, G in {16, 32, 64, 128});
+ * both with the same B, H and L_max, and the same table layout per
+ * sequence.  Rows longer than 32768 slots with k <= 2048 take the scan that
+ * lists segment candidates and the latent attention kernel that selects
+ * from them (3 kernels with the merge); others take the histogram scan and
+ * the resume path.
+ * ws: sparsekv_workspace_size(SKV_OP_SELECT_ATTEND, kv, G, k, NULL) bytes,
+ * zero-filled before its first use (the histogram path leaves its first
+ * region zero again).  Errors: SKV_EINVAL for null pointers, k outside
+ * [1, L_max], a non-latent kv or mismatched shapes; SKV_EUNSUPPORTED for
+ * other shapes or dtypes; SKV_EWORKSPACE for a short ws. */
+skv_status sparsekv_indexer_attend(const skv_kv* ikv, const void* iq, int32_t iG,
+                                   const skv_kv* kv, const void* q, int32_t G, skv_window win,
+                                   int32_t k, float scale, float* scores, int32_t* idx,
+                                   int32_t* count, float* out, void* ws, size_t ws_bytes,
+                                   hipStream_t stream);
+
+/* The two halves of sparsekv_select_attend and sparsekv_indexer_attend on
+ * long rows, for callers that time or schedule the score scan separately
+ * (as sparsekv_score_hist and sparsekv_select_attend_resume are on the
+ * histogram path).  sparsekv_segments(akv, aG, k) is the number of scan
+ * segments per row the pair uses when the selecting half attends over akv
+ * with aG query heads and top-k k -- rows longer than 32768 slots with
+ * k <= 2048, a selecting kernel that supports the shape -- or 0 when the
+ * pair does not apply (then use the histogram path).
+ * sparsekv_score_segments(kv, q, G, win, k, scores, ws, ...): scores
+ * [B][H][L_max] as sparsekv_score, and in ws, per row, the candidates of
+ * each of its segments: the segment's highest window keys that fit its
+ * share of 8192 slots (whole top histogram bins, in position order), their
+ * count, and a cut that every key left out lies below (ECHO-OSDI26 wiki page,
+ * observation 5: the selection must stay exact).  kv is the scored KV (the
+ * indexer's for the latent step) with the same B, H, L_max as akv.
+ * sparsekv_select_attend_segments(akv, q, aG, win, k, scale, scores, ...):
+ * the exact top-k of each row from those candidates when no cut lies above
+ * the k-th of them and no segment left keys out while fewer than k were
+ * listed (else that row is selected from its scores alone), then the gather
+ * + attention and the split merge; results as sparsekv_select_attend (GQA)
+ * or sparsekv_select_attend_resume (latent akv).  Nothing in ws needs to
+ * be zero for either call, and they leave the histogram region as they find
+ * it.  ws: sparsekv_workspace_size(SKV_OP_SELECT_ATTEND, akv, aG, k, NULL).
+ * Errors: SKV_EINVAL for null pointers or k outside [1, L_max];
+ * SKV_EUNSUPPORTED where sparsekv_segments is 0 (or the scan's shape is
+ * not supported); SKV_EWORKSPACE for a short ws. */
+int32_t sparsekv_segments(const skv_kv* akv, int32_t aG, int32_t k);
+skv_status sparsekv_score_segments(const skv_kv* kv, const void* q, int32_t G, skv_window win,
+                                   int32_t k, float* scores, void* ws, size_t ws_bytes,
+                                   hipStream_t stream);
+skv_status sparsekv_select_attend_segments(const skv_kv* akv, const void* q, int32_t aG,
+                                           skv_window win, int32_t k, float scale,
+                                           const float* scores, int32_t* idx, int32_t* count,
+                                           float* out, void* ws, size_t ws_bytes,
+                                           hipStream_t stream);
 
 /* sparsekv_select_attend for callers that cannot allocate device memory or
  * hand in a workspace (code under HIP graph capture, tight serving loops,

@@ -94,6 +94,15 @@ _SIGS = {
     "sparsekv_select_attend_resume": (c_i32, [ctypes.POINTER(skv_kv), c_vp, c_i32, skv_window,
                                               c_i32, c_f32, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz,
                                               c_vp]),
+    "sparsekv_indexer_attend": (c_i32, [ctypes.POINTER(skv_kv), c_vp, c_i32, ctypes.POINTER(skv_kv),
+                                        c_vp, c_i32, skv_window, c_i32, c_f32, c_vp, c_vp, c_vp,
+                                        c_vp, c_vp, c_sz, c_vp]),
+    "sparsekv_segments": (c_i32, [ctypes.POINTER(skv_kv), c_i32, c_i32]),
+    "sparsekv_score_segments": (c_i32, [ctypes.POINTER(skv_kv), c_vp, c_i32, skv_window, c_i32,
+                                        c_vp, c_vp, c_sz, c_vp]),
+    "sparsekv_select_attend_segments": (c_i32, [ctypes.POINTER(skv_kv), c_vp, c_i32, skv_window,
+                                                c_i32, c_f32, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz,
+                                                c_vp]),
     "sparsekv_select_attend_noalloc_bytes": (c_sz, [ctypes.POINTER(skv_kv), c_i32]),
     "sparsekv_select_attend_noalloc": (c_i32, [ctypes.POINTER(skv_kv), c_vp, c_i32, skv_window,
                                                c_i32, c_f32, c_vp, c_vp, c_vp, c_vp, c_vp]),
@@ -363,6 +372,66 @@ def sparsekv_select_attend_resume(kv: KVTensors, q: torch.Tensor, G: int, lo: to
                                                skv_window(_ptr(lo), _ptr(hi)), k, float(scale),
                                                _ptr(scores), _ptr(idx), _ptr(count), _ptr(out),
                                                _ptr(ws), ws.numel() * ws.element_size(), _stream()))
+    return idx, count, out
+
+
+def sparsekv_indexer_attend(ikv: KVTensors, iq: torch.Tensor, iG: int, kv: KVTensors,
+                            q: torch.Tensor, G: int, lo: torch.Tensor, hi: torch.Tensor, k: int,
+                            scale: float, scores: torch.Tensor, idx: torch.Tensor,
+                            count: torch.Tensor, out: torch.Tensor, ws: torch.Tensor):
+    """The indexer + shared-latent step: the indexer's score scan over ikv,
+    the exact top-k, and the latent attention over kv; returns (scores, idx,
+    count, out), equal to sparsekv_score_hist + sparsekv_select_attend_resume."""
+    _dev(iq, "iq", ikv.torch_dtype)
+    _dev(q, "q", kv.torch_dtype)
+    for t, nm, dt in ((scores, "scores", torch.float32), (idx, "idx", torch.int32),
+                      (count, "count", torch.int32), (out, "out", torch.float32),
+                      (lo, "lo", torch.int32), (hi, "hi", torch.int32)):
+        _dev(t, nm, dt)
+    ic, c = ikv.c(), kv.c()
+    _check("sparsekv_indexer_attend",
+           lib().sparsekv_indexer_attend(ctypes.byref(ic), _ptr(iq), iG, ctypes.byref(c), _ptr(q), G,
+                                         skv_window(_ptr(lo), _ptr(hi)), k, float(scale),
+                                         _ptr(scores), _ptr(idx), _ptr(count), _ptr(out), _ptr(ws),
+                                         ws.numel() * ws.element_size(), _stream()))
+    return scores, idx, count, out
+
+
+def sparsekv_segments(kv: KVTensors, G: int, k: int) -> int:
+    """Scan segments per row of the segment-candidate path for attending
+    over kv with G query heads and top-k k (0: the path does not apply)."""
+    c = kv.c()
+    return int(lib().sparsekv_segments(ctypes.byref(c), G, k))
+
+
+def sparsekv_score_segments(kv: KVTensors, q: torch.Tensor, G: int, lo: torch.Tensor,
+                            hi: torch.Tensor, k: int, scores: torch.Tensor, ws: torch.Tensor):
+    """sparsekv_score that also lists each row's segment candidates into ws."""
+    _dev(q, "q", kv.torch_dtype)
+    _dev(scores, "scores", torch.float32)
+    c = kv.c()
+    _check("sparsekv_score_segments",
+           lib().sparsekv_score_segments(ctypes.byref(c), _ptr(q), G, skv_window(_ptr(lo), _ptr(hi)),
+                                         k, _ptr(scores), _ptr(ws), ws.numel() * ws.element_size(),
+                                         _stream()))
+    return scores
+
+
+def sparsekv_select_attend_segments(kv: KVTensors, q: torch.Tensor, G: int, lo: torch.Tensor,
+                                    hi: torch.Tensor, k: int, scale: float, scores: torch.Tensor,
+                                    idx: torch.Tensor, count: torch.Tensor, out: torch.Tensor,
+                                    ws: torch.Tensor):
+    """The selecting half after sparsekv_score_segments on ws."""
+    for t, nm, dt in ((scores, "scores", torch.float32), (idx, "idx", torch.int32),
+                      (count, "count", torch.int32), (out, "out", torch.float32)):
+        _dev(t, nm, dt)
+    c = kv.c()
+    _check("sparsekv_select_attend_segments",
+           lib().sparsekv_select_attend_segments(ctypes.byref(c), _ptr(q), G,
+                                                 skv_window(_ptr(lo), _ptr(hi)), k, float(scale),
+                                                 _ptr(scores), _ptr(idx), _ptr(count), _ptr(out),
+                                                 _ptr(ws), ws.numel() * ws.element_size(),
+                                                 _stream()))
     return idx, count, out
 
 

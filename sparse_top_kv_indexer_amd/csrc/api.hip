@@ -263,6 +263,15 @@ skv_status sparsekv_select_attend(const skv_kv* kv, const void* q, int32_t G, sk
   debug_validate(kv, win, nullptr, 0, stream);
   uint32_t* hist = (uint32_t*)ws;
   float* part = (float*)((char*)ws + th);
+  // long rows: the scan lists segment candidates instead of the histogram,
+  // and the finishing kernel selects from them (no listing kernel)
+  if (!one_sweep && sparsekv_segments(kv, G, k) > 0) {
+    const skv_status st =
+        sparsekv_score_segments(kv, q, G, win, k, scores, ws, ws_bytes, stream);
+    if (st != SKV_OK) return st;
+    return sparsekv_select_attend_segments(kv, q, G, win, k, scale, scores, idx, count, out, ws,
+                                           ws_bytes, stream);
+  }
   const hipError_t e = launch_score(a, q, G, scores, win.lo, win.hi, hist, stream);
   if (e != hipSuccess) return launched(e);
   if (!one_sweep)
@@ -307,6 +316,91 @@ skv_status sparsekv_select_attend_resume(const skv_kv* kv, const void* q, int32_
   if (!ws || ws_bytes < th + attend_workspace_bytes(a, G, k)) return SKV_EWORKSPACE;
   return long_select_attend(a, q, G, win, k, scale, scores, idx, count, out, ws, th, ws_bytes,
                             stream);
+}
+
+skv_status sparsekv_indexer_attend(const skv_kv* ikv, const void* iq, int32_t iG,
+                                   const skv_kv* kv, const void* q, int32_t G, skv_window win,
+                                   int32_t k, float scale, float* scores, int32_t* idx,
+                                   int32_t* count, float* out, void* ws, size_t ws_bytes,
+                                   hipStream_t stream) {
+  if (!kv_ok(ikv) || !kv_ok(kv) || !iq || !q || !scores || !idx || !count || !out) return SKV_EINVAL;
+  if (iG < 1 || G < 1 || k < 1 || k > kv->L_max || !win.lo || !win.hi || !isfinite(scale))
+    return SKV_EINVAL;
+  if (kv->v != nullptr || ikv->B != kv->B || ikv->H != kv->H || ikv->L_max != kv->L_max)
+    return SKV_EINVAL;
+  const KvArgs ia = to_args(ikv), a = to_args(kv);
+  if (!score_supported(ikv, iG) || !mla_supported(a, G) || !topk_supported(kv->L_max))
+    return SKV_EUNSUPPORTED;
+  const int rows = kv->B * kv->H;
+  const size_t th = topk_workspace_bytes(rows, kv->L_max);
+  if (!ws || ws_bytes < th + mla_select_attend_partial_bytes(a, G, k)) return SKV_EWORKSPACE;
+  // long rows: the indexer's scan lists segment candidates and the latent
+  // attention kernel selects from them; otherwise the histogram scan and
+  // sparsekv_select_attend_resume
+  if (sparsekv_segments(kv, G, k) > 0 && score_seg_supported(ia, iG)) {
+    const skv_status st =
+        sparsekv_score_segments(ikv, iq, iG, win, k, scores, ws, ws_bytes, stream);
+    if (st != SKV_OK) return st;
+    return sparsekv_select_attend_segments(kv, q, G, win, k, scale, scores, idx, count, out, ws,
+                                           ws_bytes, stream);
+  }
+  const skv_status st = sparsekv_score_hist(ikv, iq, iG, win, scores, ws, ws_bytes, stream);
+  if (st != SKV_OK) return st;
+  return sparsekv_select_attend_resume(kv, q, G, win, k, scale, scores, idx, count, out, ws,
+                                       ws_bytes, stream);
+}
+
+int32_t sparsekv_segments(const skv_kv* kv, int32_t G, int32_t k) {
+  if (!kv_ok(kv) || G < 1 || k < 1 || k > kv->L_max) return 0;
+  const KvArgs a = to_args(kv);
+  const int rows = kv->B * kv->H;
+  // GQA rows: only when several workgroups share a row (fewer than
+  // kFinishAttendMinRows rows).  With one workgroup per row, the row's own
+  // listing is cheaper than the segment lists: the token pool's scan took
+  // 517 against 488 us with them (4,096 workgroups, each ending with the
+  // segment's listing) and the selecting kernel 49.7 against 67.3 us
+  const bool consumer = kv->v == nullptr ? mla_list_supported(a, G, k)
+                                         : finish_attend_supported(a, G, k) &&
+                                               rows < kFinishAttendMinRows;
+  return consumer ? topk_seg_count(rows, kv->L_max, k) : 0;
+}
+
+skv_status sparsekv_score_segments(const skv_kv* kv, const void* q, int32_t G, skv_window win,
+                                   int32_t k, float* scores, void* ws, size_t ws_bytes,
+                                   hipStream_t stream) {
+  if (!kv_ok(kv) || !q || !scores || G < 1 || k < 1 || k > kv->L_max || !win.lo || !win.hi)
+    return SKV_EINVAL;
+  const KvArgs a = to_args(kv);
+  const int rows = kv->B * kv->H;
+  const int n_seg = topk_seg_count(rows, kv->L_max, k);
+  if (n_seg == 0 || !score_seg_supported(a, G)) return SKV_EUNSUPPORTED;
+  if (!ws || ws_bytes < topk_workspace_bytes(rows, kv->L_max)) return SKV_EWORKSPACE;
+  debug_validate(kv, win, nullptr, 0, stream);
+  return launched(launch_score_seg(a, q, G, scores, win.lo, win.hi, ws, n_seg, stream));
+}
+
+skv_status sparsekv_select_attend_segments(const skv_kv* kv, const void* q, int32_t G,
+                                           skv_window win, int32_t k, float scale,
+                                           const float* scores, int32_t* idx, int32_t* count,
+                                           float* out, void* ws, size_t ws_bytes,
+                                           hipStream_t stream) {
+  if (!kv_ok(kv) || !q || !scores || !idx || !count || !out || G < 1 || k < 1) return SKV_EINVAL;
+  if (k > kv->L_max || !win.lo || !win.hi || !isfinite(scale)) return SKV_EINVAL;
+  const int n_seg = sparsekv_segments(kv, G, k);
+  if (n_seg == 0) return SKV_EUNSUPPORTED;
+  const KvArgs a = to_args(kv);
+  const int rows = kv->B * kv->H;
+  const size_t th = topk_workspace_bytes(rows, kv->L_max);
+  const size_t pb = kv->v == nullptr ? mla_select_attend_partial_bytes(a, G, k)
+                                     : attend_workspace_bytes(a, G, k);
+  if (!ws || ws_bytes < th + pb) return SKV_EWORKSPACE;
+  debug_validate(kv, win, nullptr, 0, stream);
+  float* part = (float*)((char*)ws + th);
+  if (kv->v == nullptr)
+    return launched(launch_mla_list_attend(a, q, G, scores, win.lo, win.hi, k, ws, scale, idx,
+                                           count, part, out, stream, n_seg));
+  return launched(launch_finish_attend(a, q, G, scores, win.lo, win.hi, k, ws, scale, idx, count,
+                                       out, part, stream, n_seg));
 }
 
 size_t sparsekv_select_attend_noalloc_bytes(const skv_kv* kv, int32_t G) {

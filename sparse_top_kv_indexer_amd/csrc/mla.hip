@@ -251,11 +251,11 @@ int mla_splits(int k) { return std::max(8, std::min(64, (k + 63) / 64 + 7) / 8 *
 constexpr int kFuseRows = 64;          // latent rows staged at a time
 constexpr int kFuseSlices = 1024;      // listing slices of a row this kernel reads
 
-template <int DP>
+template <int DP, bool SEG>
 __global__ __launch_bounds__(kRowThreads) void mla_list_kernel(
     KvArgs kv, const uint16_t* q, int G, const float* scores, const int32_t* lo_p,
     const int32_t* hi_p, int k, TopkWs ws, int n_slices, float scale_log2, int n_split,
-    int32_t* idx, int32_t* count, float* part) {
+    int32_t* idx, int32_t* count, float* part, int n_seg) {
   constexpr int VB = kVB / DP;                      // value column blocks per wave
   constexpr int NHG = kRowWaves / DP;               // 16-head groups per workgroup
   constexpr int kHeadsPerWg = 16 * NHG;
@@ -286,14 +286,23 @@ __global__ __launch_bounds__(kRowThreads) void mla_list_kernel(
   }
 
   // 1. the row's exact selection, positions ascending in L.hist[0 .. n_sel)
-  const uint4 gv = hist_bins_summed(ws, row);
-  int n_sel;
-  if (ws.meta[2 * row + 1] < 0) {
-    n_sel = fallback_select(scores, row, kv.H, kv.L_max, lo_p, hi_p, k,
-                            ws.hist + (int64_t)row * ws.copies * kBins, L, klist_n, gv);
+  // (from the scan's segment candidates with SEG, else from the slice
+  // listing's list; the row alone when those do not settle it)
+  auto keep = [&](int dst, int p, uint32_t) { L.hist[dst] = (uint32_t)p; };
+  const uint4 gv = SEG ? make_uint4(0u, 0u, 0u, 0u) : hist_bins_summed(ws, row);
+  int n_sel = -1;
+  if constexpr (SEG)
+    n_sel = seg_select(ws, row, n_seg, k, L, keep);
+  else if (ws.meta[2 * row + 1] >= 0)
+    n_sel = list_select(ws, row, k, n_slices, gv, L, s_off, s_at, keep);
+  if (n_sel < 0) {
+    lds_barrier();   // every thread is past its reads of L
+    if constexpr (SEG)
+      n_sel = fallback_select_nohist(scores, row, kv.H, kv.L_max, lo_p, hi_p, k, L, klist_n);
+    else
+      n_sel = fallback_select(scores, row, kv.H, kv.L_max, lo_p, hi_p, k,
+                              ws.hist + (int64_t)row * ws.copies * kBins, L, klist_n, gv);
   } else {
-    n_sel = list_select(ws, row, k, n_slices, gv, L, s_off, s_at,
-                        [&](int dst, int p, uint32_t) { L.hist[dst] = (uint32_t)p; });
     lds_barrier();
   }
   if (s == 0 && hp == 0) {
@@ -473,27 +482,38 @@ size_t mla_select_attend_partial_bytes(const KvArgs& kv, int G, int k) {
 hipError_t launch_mla_list_attend(const KvArgs& kv, const void* q, int G, const float* scores,
                                   const int32_t* lo, const int32_t* hi, int k, void* topk_ws,
                                   float scale, int32_t* idx, int32_t* count, float* part,
-                                  float* out, hipStream_t st) {
+                                  float* out, hipStream_t st, int n_seg) {
   const int rows = kv.B * kv.H;
   const TopkWs ws = TopkWs::carve(topk_ws, rows, kv.L_max);
-  hipError_t e = launch_topk_listing(scores, rows, kv.H, kv.L_max, lo, hi, k, topk_ws, st);
-  if (e != hipSuccess) return e;
   const int ns = topk_listing_slices(rows, kv.L_max);
   if (ns > kFuseSlices) return hipErrorInvalidValue;
+  if (n_seg > kSegMax || (n_seg > 0 && k > kSegMaxK)) return hipErrorInvalidValue;
+  hipError_t e = hipSuccess;
+  if (n_seg <= 0) {
+    e = launch_topk_listing(scores, rows, kv.H, kv.L_max, lo, hi, k, topk_ws, st);
+    if (e != hipSuccess) return e;
+  }
   const float scale_log2 = scale * 1.4426950408889634f;
   const uint16_t* qq = (const uint16_t*)q;
   // 32 heads per workgroup (2 head groups x 8 dim parts); 16 heads take 16
   const int dp = G >= 32 ? 8 : 16;
   const int n_hp = (G + 16 * (kRowWaves / dp) - 1) / (16 * (kRowWaves / dp));
   const dim3 grid(kFuseSplits, rows * n_hp);
-  if (dp == 8)
-    mla_list_kernel<8><<<grid, kRowThreads, 0, st>>>(kv, qq, G, scores, lo, hi, k, ws, ns, scale_log2,
-                                                     kFuseSplits, idx, count, part);
-  else
-    mla_list_kernel<16><<<grid, kRowThreads, 0, st>>>(kv, qq, G, scores, lo, hi, k, ws, ns,
-                                                      scale_log2, kFuseSplits, idx, count, part);
+#define SKV_MLA_LIST(D, SG)                                                                     \
+  mla_list_kernel<D, SG><<<grid, kRowThreads, 0, st>>>(kv, qq, G, scores, lo, hi, k, ws, ns,     \
+                                                       scale_log2, kFuseSplits, idx, count, part, \
+                                                       n_seg)
+  if (dp == 8) {
+    if (n_seg > 0) SKV_MLA_LIST(8, true); else SKV_MLA_LIST(8, false);
+  } else {
+    if (n_seg > 0) SKV_MLA_LIST(16, true); else SKV_MLA_LIST(16, false);
+  }
+#undef SKV_MLA_LIST
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (n_seg > 0)   // nothing of the histograms or list counters was used
+    return launch_attend_reduce(part, kFuseSplits, kDv, kv.H * G, kv.B, out, st, nullptr, G, 1,
+                                nullptr);
   return launch_attend_reduce(part, kFuseSplits, kDv, kv.H * G, kv.B, out, st, ws.hist, G,
                               ws.copies, ws.ctr);
 }

@@ -63,6 +63,10 @@ struct HistArgs {
   int32_t* ctr;
   int cap;
   int copies;       // histogram copies per row (topk_hist_copies)
+  // segment candidates (MODE 3): row r's workgroups are r S .. r S + S - 1,
+  // workgroup r S + j lists segment j of row r into the top-k workspace
+  TopkWs seg;
+  int seg_s, seg_m;
 };
 
 // The copy of row r's histogram that this workgroup adds into.
@@ -81,6 +85,100 @@ __device__ __forceinline__ void hist_add(uint32_t* lh, float s, int t, int lo, i
   if (u == 0x80000000u) u = 0u;
   const uint32_t key = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
   atomicAdd(&lh[key >> 20], 1u);
+}
+
+// The order-preserving key of a window score (0 outside the window and for
+// inf / nan, which are never candidates; -0 counts as +0).
+__device__ __forceinline__ uint32_t window_key(float s, int t, int lo, int hi) {
+  uint32_t u = __float_as_uint(s);
+  if (t < lo || t >= hi || (u & 0x7f800000u) == 0x7f800000u) return 0u;
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// The segment's candidates (MODE 3), once lh holds the histogram of the
+// segment's window keys and sk their keys (sk[i]: token tok0 + i, i < n_tok,
+// 0 outside the window): the lowest bin cb such that the keys of cb and of
+// every bin above fit in m slots; the keys of bins >= cb, in position order,
+// go to slots [seg m, seg m + count) of row r; count and cut (cb << 20, or 0
+// when every window key was listed) to the segment's entries.
+__device__ __forceinline__ void seg_flush(const uint32_t* lh, const uint32_t* sk, int n_tok,
+                                          int tok0, const HistArgs& ha, int64_t r, int seg,
+                                          int* sh) {
+  lds_barrier();   // lh and sk are complete
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int m = ha.seg_m;
+  int c[16], ts = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const uint4 v = ((const uint4*)lh)[4 * threadIdx.x + u];
+    c[4 * u] = (int)v.x;
+    c[4 * u + 1] = (int)v.y;
+    c[4 * u + 2] = (int)v.z;
+    c[4 * u + 3] = (int)v.w;
+    ts += c[4 * u] + c[4 * u + 1] + c[4 * u + 2] + c[4 * u + 3];
+  }
+  // this thread's 16 keys (read now, used once the cut is known)
+  uint32_t kk[16];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int i = 16 * threadIdx.x + 4 * u;
+    const uint4 v = i < n_tok ? ((const uint4*)sk)[4 * threadIdx.x + u] : make_uint4(0u, 0u, 0u, 0u);
+    kk[4 * u] = v.x;
+    kk[4 * u + 1] = i + 1 < n_tok ? v.y : 0u;
+    kk[4 * u + 2] = i + 2 < n_tok ? v.z : 0u;
+    kk[4 * u + 3] = i + 3 < n_tok ? v.w : 0u;
+  }
+  const int incl = wave_incl_scan(ts);
+  if (lane == 63) sh[wave] = incl;
+  lds_barrier();
+  int below = incl - ts, total = 0;   // keys in the bins below this thread's; all keys
+#pragma unroll
+  for (int u = 0; u < kThreads / 64; ++u) {
+    if (u < wave) below += sh[u];
+    total += sh[u];
+  }
+  if (total <= m) {
+    if (threadIdx.x == 0) sh[4] = 0;
+  } else {
+    // the one bin where the count from the top first exceeds m
+    int above = total - below - ts;
+#pragma unroll
+    for (int j = 15; j >= 0; --j) {
+      if (above <= m && above + c[j] > m) sh[4] = 16 * threadIdx.x + j + 1;
+      above += c[j];
+    }
+  }
+  lds_barrier();
+  const uint32_t cb = (uint32_t)sh[4];
+  int cnt = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) cnt += kk[j] != 0u && (kk[j] >> 20) >= cb;
+  const int ci = wave_incl_scan(cnt);
+  if (lane == 63) sh[5 + wave] = ci;   // (sh[0..4] stay as read above)
+  lds_barrier();
+  int off = ci - cnt, listed = 0;
+#pragma unroll
+  for (int u = 0; u < kThreads / 64; ++u) {
+    if (u < wave) off += sh[5 + u];
+    listed += sh[5 + u];
+  }
+  const int64_t base = r * kRowList + (int64_t)seg * m;
+  uint32_t* key = ha.seg.seg_key() + base;
+  int32_t* pos = ha.seg.seg_pos() + base;
+  if (cnt) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (kk[j] != 0u && (kk[j] >> 20) >= cb) {
+        key[off] = kk[j];
+        pos[off] = tok0 + 16 * threadIdx.x + j;
+        ++off;
+      }
+  }
+  if (threadIdx.x == 0) {
+    ha.seg.seg_n()[r * kRowList + seg] = listed;
+    ha.seg.seg_cut()[r * kRowList + seg] = cb ? cb << 20 : 0u;
+  }
 }
 
 __device__ __forceinline__ void hist_begin(uint32_t* lh) {
@@ -223,8 +321,10 @@ template <int NC, int D, int GMAX, int MODE, bool VALU>
 __global__ __launch_bounds__(kThreads) void score_stream_kernel(KvArgs kv, const uint16_t* q, int G,
                                                                  float* scores, HistArgs ha,
                                                                  int cpr) {
-  constexpr bool HIST = MODE == 1, SURV = MODE == 2;
-  __shared__ uint32_t lh[HIST ? 4096 : 1];
+  constexpr bool HIST = MODE == 1, SURV = MODE == 2, SEG = MODE == 3;
+  __shared__ __attribute__((aligned(16))) uint32_t lh[(HIST || SEG) ? 4096 : 1];
+  __shared__ __attribute__((aligned(16))) uint32_t sk[SEG ? kSegMaxKeys : 1];   // window keys
+  __shared__ int seg_sh[SEG ? 12 : 1];
   __shared__ int32_t tab[kStageEntries];
   __shared__ uint32_t svk[SURV ? kSvCap : 1];
   __shared__ int32_t svp[SURV ? kSvCap : 1];
@@ -259,7 +359,7 @@ __global__ __launch_bounds__(kThreads) void score_stream_kernel(KvArgs kv, const
     }
     int wlo = 0, whi = 0;
     float thr = 0.f;
-    if constexpr (HIST) {
+    if constexpr (HIST || SEG) {
       for (int i = threadIdx.x; i < 4096; i += kThreads) lh[i] = 0u;
       wlo = ha.lo[b];
       whi = ha.hi[b];
@@ -364,6 +464,11 @@ __global__ __launch_bounds__(kThreads) void score_stream_kernel(KvArgs kv, const
         if constexpr (HIST) {
           if (ok) hist_add(lh, sc, t, wlo, whi);
         }
+        if constexpr (SEG) {
+          const uint32_t key = ok ? window_key(sc, t, wlo, whi) : 0u;
+          if (key) atomicAdd(&lh[key >> 20], 1u);
+          sk[t - c_lo * 16] = key;
+        }
         if constexpr (SURV) {
           uint32_t u = __float_as_uint(sc);
           if (ok && t >= wlo && t < whi && sc >= thr && (u & 0x7f800000u) != 0x7f800000u) {
@@ -410,6 +515,9 @@ __global__ __launch_bounds__(kThreads) void score_stream_kernel(KvArgs kv, const
         if (s < n_w) finish(mfma(s), s);
     }
     if constexpr (HIST) hist_flush(lh, hist_copy(ha, r));
+    if constexpr (SEG)
+      seg_flush(lh, sk, min(c_hi * 16, kv.L_max) - c_lo * 16, c_lo * 16, ha, r,
+                (int)blockIdx.x - r * ha.seg_s, seg_sh);
     if constexpr (SURV) {
       lds_barrier();
       const int nsv = sv_n;
@@ -489,6 +597,8 @@ hipError_t launch_stream_k(const KvArgs& kv, const void* q, int G, float* scores
   // workgroups per histogram copy
   if (MODE == 1) w = std::min<int64_t>(w, (int64_t)kv.B * kv.H * 256 * ha.copies);
   w = std::max<int64_t>(std::max<int64_t>(w, (n_work + cap - 1) / cap), 1);
+  // segment candidates: exactly S workgroups per row, each within its row
+  if (MODE == 3) w = (int64_t)kv.B * kv.H * ha.seg_s;
   if (w > 0x7fffffff) return hipErrorInvalidValue;
   kern<<<dim3((unsigned)w), kThreads, 0, s>>>(kv, (const uint16_t*)q, G, scores, ha, cpr);
   return hipGetLastError();
@@ -507,6 +617,10 @@ hipError_t launch_stream_m(const KvArgs& kv, const void* q, int G, float* scores
 template <int NC, int D>
 hipError_t launch_stream(const KvArgs& kv, const void* q, int G, float* scores, const HistArgs& ha,
                          hipStream_t s) {
+  if (ha.seg_s > 0) {
+    if constexpr (NC <= 8) return launch_stream_m<NC, D, 3>(kv, q, G, scores, ha, s);
+    return hipErrorInvalidValue;
+  }
   if (ha.lkey) {
     if constexpr (NC <= 8) return launch_stream_m<NC, D, 2>(kv, q, G, scores, ha, s);
     return hipErrorInvalidValue;
@@ -544,6 +658,27 @@ hipError_t launch_score(const KvArgs& kv, const void* q, int G, float* scores, c
     if (npl <= 4) return launch_valu<false, 4, 2>(kv, q, G, scores, ha, grid, tile, s);
   }
   return hipErrorInvalidValue;
+}
+
+bool score_seg_supported(const KvArgs& kv, int G) {
+  const int nc = kv.d_k / 32;
+  return kv.bf16 && G >= 1 && G <= 16 && kv.d_k % 32 == 0 && (nc == 2 || nc == 4 || nc == 8) &&
+         (G >= 2 || kv.d_k <= 256);
+}
+
+hipError_t launch_score_seg(const KvArgs& kv, const void* q, int G, float* scores,
+                            const int32_t* lo, const int32_t* hi, void* topk_ws, int S,
+                            hipStream_t s) {
+  if (!score_seg_supported(kv, G) || S < 1 || S > kSegMax) return hipErrorInvalidValue;
+  HistArgs ha{lo, hi, nullptr};
+  ha.seg = TopkWs::carve(topk_ws, kv.B * kv.H, kv.L_max);
+  ha.seg_s = S;
+  ha.seg_m = kSegSlots / S;
+  switch (kv.d_k / 32) {
+    case 2: return launch_stream<2, 4>(kv, q, G, scores, ha, s);
+    case 4: return launch_stream<4, 4>(kv, q, G, scores, ha, s);
+    default: return launch_stream<8, 2>(kv, q, G, scores, ha, s);
+  }
 }
 
 bool score_prefilter_supported(const KvArgs& kv, int G) {

@@ -364,11 +364,16 @@ constexpr int kFinishSlices = 1024;   // listing slices of a row this kernel rea
 constexpr int kFinishK = kBins;       // selected keys it stages (k <= 4096)
 constexpr int kLocalList = 4096;      // keys a row's own listing holds (one workgroup per row)
 
-template <int GMAX, bool LOCAL>
+// SRC: where a workgroup's candidates come from -- kFromList (the slice
+// listing's list), kFromRow (its own listing of the row) or kFromSegs (the
+// scan's segment candidates, n_seg segments per row).
+constexpr int kFromList = 0, kFromRow = 1, kFromSegs = 2;
+
+template <int GMAX, int SRC>
 __global__ __launch_bounds__(kRowThreads) void finish_attend_kernel(
     KvArgs kv, const uint16_t* q, int G, const float* scores, const int32_t* lo_p,
     const int32_t* hi_p, int k, TopkWs ws, int n_slices, float scale_log2, int32_t* idx,
-    int32_t* count, float* out, int n_split, float* part) {
+    int32_t* count, float* out, int n_split, float* part, int n_seg) {
   __shared__ RowSelLds L;
   __shared__ int32_t sel[kFinishK];                 // the selection, ascending
   __shared__ uint32_t selk[kFinishK];               // and its score keys
@@ -402,7 +407,7 @@ __global__ __launch_bounds__(kRowThreads) void finish_attend_kernel(
     }
   }
   uint32_t* ghist = ws.hist + (int64_t)row * ws.copies * kBins;
-  const uint4 gv = hist_bins_summed(ws, row);
+  const uint4 gv = SRC == kFromSegs ? make_uint4(0u, 0u, 0u, 0u) : hist_bins_summed(ws, row);
   int n_sel;
   const int32_t* lst;
   const uint32_t* lk = nullptr;   // the selection's score keys (not after the fallback)
@@ -411,15 +416,20 @@ __global__ __launch_bounds__(kRowThreads) void finish_attend_kernel(
     selk[dst] = key;
   };
   n_sel = -1;
-  if constexpr (LOCAL) {
+  if constexpr (SRC == kFromRow) {
     n_sel = local_list_select<kLocalList / kRowThreads>(scores, row, kv.H, kv.L_max, lo_p, hi_p, k,
                                                         gv, L, U.list.k, U.list.p, keep);
+  } else if constexpr (SRC == kFromSegs) {
+    n_sel = seg_select(ws, row, n_seg, k, L, keep);
   } else if (ws.meta[2 * row + 1] >= 0) {
     n_sel = list_select(ws, row, k, n_slices, gv, L, s_off, s_at, keep);
   }
   if (n_sel < 0) {
     lds_barrier();   // every thread is past its reads of L
-    n_sel = fallback_select(scores, row, kv.H, kv.L_max, lo_p, hi_p, k, ghist, L, klist_n, gv);
+    if constexpr (SRC == kFromSegs)
+      n_sel = fallback_select_nohist(scores, row, kv.H, kv.L_max, lo_p, hi_p, k, L, klist_n);
+    else
+      n_sel = fallback_select(scores, row, kv.H, kv.L_max, lo_p, hi_p, k, ghist, L, klist_n, gv);
     lst = (const int32_t*)L.hist;   // the positions, ascending
   } else {
     lst = sel;
@@ -431,7 +441,7 @@ __global__ __launch_bounds__(kRowThreads) void finish_attend_kernel(
     for (int i = threadIdx.x; i < k; i += kRowThreads) orow[i] = i < n_sel ? lst[i] : -1;
     if (threadIdx.x == 0) count[row] = n_sel;
   }
-  if (n_split == 1) {   // the row's only reader: zero for the next call
+  if (SRC != kFromSegs && n_split == 1) {   // the row's only reader: zero for the next call
     if (threadIdx.x == 0) ws.ctr[(int64_t)row * kCtrStride] = 0;
     for (int cp = 0; cp < ws.copies; ++cp)
       ((uint4*)ghist)[cp * (kBins / 4) + threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
@@ -501,38 +511,46 @@ int finish_attend_splits(const KvArgs& kv, int G, int k) {
 hipError_t launch_finish_attend(const KvArgs& kv, const void* q, int G, const float* scores,
                                 const int32_t* lo, const int32_t* hi, int k, void* topk_ws,
                                 float scale, int32_t* idx, int32_t* count, float* out, float* part,
-                                hipStream_t st) {
+                                hipStream_t st, int n_seg) {
   const int rows = kv.B * kv.H;
   const TopkWs ws = TopkWs::carve(topk_ws, rows, kv.L_max);
   const int ns = topk_listing_slices(rows, kv.L_max);
   if (ns > kFinishSlices || k > kFinishK) return hipErrorInvalidValue;
   const int S = finish_attend_splits(kv, G, k);
-  // one workgroup per row lists the row itself; several per row share the
-  // slice listing's list (each of them streaming the row from L2 took the
-  // long-context GQA step from 245 to 275 us: a workgroup streams 512 KB of
-  // scores at one CU's rate)
-  const int local = S == 1;
+  // the scan's segment candidates (n_seg > 0); else one workgroup per row
+  // lists the row itself, several per row share the slice listing's list
+  // (each of them streaming the row from L2 took the long-context GQA step
+  // from 245 to 275 us: a workgroup streams 512 KB of scores at one CU's
+  // rate)
+  const int src = n_seg > 0 ? kFromSegs : S == 1 ? kFromRow : kFromList;
+  if (src == kFromSegs && (n_seg > kSegMax || k > kSegMaxK)) return hipErrorInvalidValue;
   hipError_t e = hipSuccess;
-  if (!local) {
+  if (src == kFromList) {
     e = launch_topk_listing(scores, rows, kv.H, kv.L_max, lo, hi, k, topk_ws, st);
     if (e != hipSuccess) return e;
   }
   const float scale_log2 = scale * 1.4426950408889634f;
   const uint16_t* qq = (const uint16_t*)q;
   const unsigned grid = S == 1 ? (unsigned)rows : (unsigned)((rows * S + 7) / 8 * 8);
-#define SKV_FINISH(GM, LOC)                                                                     \
-  finish_attend_kernel<GM, LOC><<<grid, kRowThreads, 0, st>>>(kv, qq, G, scores, lo, hi, k, ws, ns, \
-                                                              scale_log2, idx, count, out, S, part)
-  if (G == 1) {
-    if (local) SKV_FINISH(1, true); else SKV_FINISH(1, false);
-  } else if (G <= 4) {
-    if (local) SKV_FINISH(4, true); else SKV_FINISH(4, false);
-  } else {
-    if (local) SKV_FINISH(8, true); else SKV_FINISH(8, false);
-  }
+#define SKV_FINISH(GM, SR)                                                                      \
+  finish_attend_kernel<GM, SR><<<grid, kRowThreads, 0, st>>>(kv, qq, G, scores, lo, hi, k, ws, ns, \
+                                                             scale_log2, idx, count, out, S, part, \
+                                                             n_seg)
+#define SKV_FINISH_G(GM)                                                                        \
+  do {                                                                                          \
+    if (src == kFromRow) SKV_FINISH(GM, kFromRow);                                             \
+    else if (src == kFromSegs) SKV_FINISH(GM, kFromSegs);                                      \
+    else SKV_FINISH(GM, kFromList);                                                            \
+  } while (0)
+  if (G == 1) SKV_FINISH_G(1);
+  else if (G <= 4) SKV_FINISH_G(4);
+  else SKV_FINISH_G(8);
+#undef SKV_FINISH_G
 #undef SKV_FINISH
   e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
+  if (src == kFromSegs)   // nothing of the histograms or list counters was used
+    return launch_attend_reduce(part, S, kD, kv.H * G, kv.B, out, st, nullptr, G, 1, nullptr);
   return launch_attend_reduce(part, S, kD, kv.H * G, kv.B, out, st, ws.hist, G, ws.copies, ws.ctr);
 }
 

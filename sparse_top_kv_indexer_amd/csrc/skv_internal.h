@@ -25,6 +25,14 @@ struct KvArgs {
 hipError_t launch_score(const KvArgs& kv, const void* q, int G, float* scores, const int32_t* lo,
                         const int32_t* hi, uint32_t* hist, hipStream_t s);
 
+// score.hip, segment candidates: S workgroups per row, each scoring one
+// segment of its row and listing the segment's highest keys into the top-k
+// workspace (topk_seg_count, skv_topk.h); no histogram
+bool score_seg_supported(const KvArgs& kv, int G);
+hipError_t launch_score_seg(const KvArgs& kv, const void* q, int G, float* scores,
+                            const int32_t* lo, const int32_t* hi, void* topk_ws, int S,
+                            hipStream_t s);
+
 // score.hip, threshold prefilter: the scan also lists, per row, the keys of
 // [lo, hi) whose score is >= thr[row] (into the top-k workspace's lists)
 bool score_prefilter_supported(const KvArgs& kv, int G);
@@ -103,10 +111,12 @@ hipError_t launch_select_attend(const KvArgs& kv, const void* q, int G, const fl
 constexpr int kFinishAttendMinRows = 128;
 constexpr int kFinishSplitsFew = 8;
 bool finish_attend_supported(const KvArgs& kv, int G, int k);
+// n_seg > 0: the candidates are the segment candidates of a launch_score_seg
+// with n_seg = topk_seg_count(rows, L_max, k) segments per row (no histogram)
 hipError_t launch_finish_attend(const KvArgs& kv, const void* q, int G, const float* scores,
                                 const int32_t* lo, const int32_t* hi, int k, void* topk_ws,
                                 float scale, int32_t* idx, int32_t* count, float* out, float* part,
-                                hipStream_t st);
+                                hipStream_t st, int n_seg = 0);
 
 // mla.hip: shared-latent attention on matrix cores (v == nullptr)
 bool mla_supported(const KvArgs& kv, int G);
@@ -123,9 +133,11 @@ size_t mla_list_partial_bytes(const KvArgs& kv, int G);
 // split partials the latent path of sparsekv_select_attend_resume needs
 // (fused or not, whichever is larger)
 size_t mla_select_attend_partial_bytes(const KvArgs& kv, int G, int k);
+// (n_seg > 0: after launch_score_seg of the indexer with n_seg =
+// topk_seg_count(rows, L_max, k) segments per row, no listing)
 hipError_t launch_mla_list_attend(const KvArgs& kv, const void* q, int G, const float* scores,
                                   const int32_t* lo, const int32_t* hi, int k, void* topk_ws,
                                   float scale, int32_t* idx, int32_t* count, float* part,
-                                  float* out, hipStream_t s);
+                                  float* out, hipStream_t s, int n_seg = 0);
 
 }  // namespace skv

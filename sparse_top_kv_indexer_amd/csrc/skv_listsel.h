@@ -475,6 +475,60 @@ __device__ __forceinline__ int local_list_select(const float* scores, int row, i
   return select_listed<KPER>(k, gv, L, key, pos, emit);
 }
 
+// Exact selection of row `row` from the segment candidates the score scan
+// listed in ws (topk_seg_count: S segments of m = kSegSlots / S slots, keys
+// in position order): lane t takes slots KPER t .. KPER t + KPER - 1, all in
+// one segment (keys past the segment's count read as 0, never selected), the
+// first digit's histogram is built from the listed keys in LDS, and
+// select_listed finishes: emit(dst, pos, key) for every selected key, dst its
+// rank in ascending position order.  That is the row's exact top-k when no
+// key left out can rank among it: every segment's cut (all its unlisted keys
+// are below it) is at most the k-th selected key, and no segment left keys
+// out if fewer than k were listed.  Returns the number selected, or -1 when
+// that does not hold (the caller then selects the row alone).
+template <typename Emit>
+__device__ __forceinline__ int seg_select(const TopkWs& ws, int row, int S, int k, RowSelLds& L,
+                                          Emit&& emit) {
+  constexpr int KPER = kSegSlots / kRowThreads;
+  static_assert(KPER == 8, "two 16-byte loads of keys and of positions per lane");
+  const int m = kSegSlots / S;   // a power of two >= 16
+  const int64_t rb = (int64_t)row * kRowList;
+  const int slot0 = KPER * threadIdx.x;
+  const int seg = slot0 / m, o = slot0 - seg * m;
+  const int n_in = ws.seg_n()[rb + seg];
+  const uint4 ka = *(const uint4*)(ws.seg_key() + rb + slot0);
+  const uint4 kb = *(const uint4*)(ws.seg_key() + rb + slot0 + 4);
+  const int4 pa = *(const int4*)(ws.seg_pos() + rb + slot0);
+  const int4 pb = *(const int4*)(ws.seg_pos() + rb + slot0 + 4);
+  const uint32_t cut = (int)threadIdx.x < S ? ws.seg_cut()[rb + threadIdx.x] : 0u;
+  const uint32_t kv8[8] = {ka.x, ka.y, ka.z, ka.w, kb.x, kb.y, kb.z, kb.w};
+  const int pv8[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+  uint32_t key[KPER];
+  int pos[KPER];
+#pragma unroll
+  for (int u = 0; u < KPER; ++u) {
+    key[u] = o + u < n_in ? kv8[u] : 0u;
+    pos[u] = pv8[u];
+  }
+  // the listed keys' top-12-bit histogram
+  *(uint4*)(L.hist + 4 * threadIdx.x) = make_uint4(0u, 0u, 0u, 0u);
+  lds_barrier();
+#pragma unroll
+  for (int u = 0; u < KPER; ++u)
+    if (key[u]) atomicAdd(&L.hist[key[u] >> 20], 1u);
+  lds_barrier();
+  const uint4 gv = *(const uint4*)(L.hist + 4 * threadIdx.x);
+  uint32_t mk = 0xffffffffu;   // smallest key this lane selected
+  const int n_sel = select_listed<KPER>(k, gv, L, key, pos, [&](int dst, int p, uint32_t kk) {
+    mk = min(mk, kk);
+    emit(dst, p, kk);
+  });
+  const uint32_t kth = block_min_u32(mk, (uint32_t*)L.wt);
+  const uint32_t max_cut = ~block_min_u32(~cut, (uint32_t*)L.wa);
+  if (max_cut == 0u) return n_sel;                 // every window key was listed
+  return (n_sel == k && kth >= max_cut) ? n_sel : -1;
+}
+
 // The selection of a row whose list overflowed, for kernels that finish the
 // selection themselves: the row alone, re-read per digit, the positions left
 // in L.hist[0 .. n) ascending (k <= 4096).  Rare; kept out of line so its
@@ -486,6 +540,15 @@ __device__ __noinline__ int fallback_select(const float* scores, int row, int H,
   return row_select_alone<false, 3>(scores, row, H, L_max, lo_p, hi_p, k, ghist_row, true, nullptr,
                                     nullptr, nullptr, nullptr, 0, L, nullptr, klist_n, nullptr,
                                     true, gv);
+}
+
+// The same without a first-digit histogram in memory (the segment
+// candidates' scan leaves none): the histogram is counted from the row.
+__device__ __noinline__ int fallback_select_nohist(const float* scores, int row, int H, int L_max,
+                                                  const int32_t* lo_p, const int32_t* hi_p, int k,
+                                                  RowSelLds& L, int& klist_n) {
+  return row_select_alone<false, 3>(scores, row, H, L_max, lo_p, hi_p, k, nullptr, false, nullptr,
+                                    nullptr, nullptr, nullptr, 0, L, nullptr, klist_n);
 }
 
 // This thread's 4 bins (4 t .. 4 t + 3) of row `row`'s first-digit

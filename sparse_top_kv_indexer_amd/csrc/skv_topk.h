@@ -62,6 +62,33 @@ __host__ __device__ inline int topk_slices(int L_max) {
   return topk_slices_ng(L_max, ng);
 }
 
+// Segment candidates of few long rows (k <= kSegMaxK): the score scan gives
+// each of a row's S workgroups one segment of at most kSegMaxKeys keys, and
+// each lists the segment's keys of its highest histogram bins that fit in
+// m = kSegSlots / S slots, in position order, with the count listed and a cut
+// (0: the segment listed every key of the window; else every key it left
+// out is below the cut).  A row's exact top-k is the top-k of its listed keys
+// whenever no cut lies above the k-th of them.  The lists live in the row's
+// key-list region of the workspace: keys and positions in slots
+// [0, kSegSlots) of lkey / lpos, counts and cuts after the keys.
+constexpr int kSegSlots = 8192;     // listed slots per row
+constexpr int kSegMaxKeys = 4096;   // keys per segment
+constexpr int kSegMax = 512;        // segments per row
+constexpr int kSegMaxK = 2048;      // k served (a quarter of the slots)
+
+// Segments per row for `rows` rows of L_max slots and k, or 0 when the
+// segment candidates do not serve the call: a power of two giving about 1024
+// workgroups in all, at most kSegMax, each segment at most kSegMaxKeys keys.
+inline int topk_seg_count(int rows, int L_max, int k) {
+  const int64_t slots = L_max % 4 == 0 ? (int64_t)L_max : (int64_t)L_max + 3;
+  if (rows < 1 || k < 1 || k > kSegMaxK || slots <= 32768) return 0;
+  int S = kSegMax;
+  while (S > 1 && (int64_t)rows * S > 1024) S >>= 1;
+  const int64_t cpr = ((int64_t)L_max + 15) / 16;
+  while (S < kSegMax && cpr > (int64_t)S * (kSegMaxKeys / 16)) S <<= 1;
+  return cpr <= (int64_t)S * (kSegMaxKeys / 16) ? S : 0;
+}
+
 struct TopkWs {
   uint32_t* hist;   // [rows][copies][4096]
   int32_t* ctr;     // [rows][kCtrStride] keys listed so far (element 0 of each line)
@@ -80,6 +107,12 @@ struct TopkWs {
     return zero_bytes(rows, L_max) + align((size_t)rows * 8) +
            align((size_t)rows * topk_slices(L_max) * 8) + 2 * align((size_t)rows * kRowList * 4);
   }
+  // segment candidates of row r: key / pos slot i at r * kRowList + i,
+  // count and cut of segment j at r * kRowList + j
+  __host__ __device__ uint32_t* seg_key() const { return lkey; }
+  __host__ __device__ int32_t* seg_pos() const { return lpos; }
+  __host__ __device__ int32_t* seg_n() const { return (int32_t*)(lkey + kSegSlots); }
+  __host__ __device__ uint32_t* seg_cut() const { return lkey + kSegSlots + kSegMax; }
   static TopkWs carve(void* p, int rows, int L_max) {
     TopkWs w;
     char* c = (char*)p;

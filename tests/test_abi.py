@@ -160,6 +160,30 @@ def test_every_selecting_call_rejects_k_above_L_max():
     assert L.sparsekv_topk(P, 2, 2, 64, win, 64, P, P, None, 0, None) == S.SKV_EWORKSPACE
 
 
+def test_indexer_attend_validates_before_any_launch():
+    """The indexer + latent call checks its arguments on the host: k range,
+    a latent KV, matching shapes of the two KVs, and the workspace size (the
+    pointers below are never dereferenced)."""
+    L = S.lib()
+    P = ctypes.c_void_p(1)
+    win = S.skv_window(P, P)
+    ikv = _kv(B=1, H=1, L_max=65536, block=16, block_table=1)
+    lat = _kv(B=1, H=1, L_max=65536, block=16, block_table=1, v=None, d_k=576, d_v=512)
+    big = 1 << 34
+
+    def call(ikv_, lat_, k, ws_bytes=big, iG=1, G=128):
+        return L.sparsekv_indexer_attend(ctypes.byref(ikv_), P, iG, ctypes.byref(lat_), P, G, win,
+                                         k, 0.05, P, P, P, P, P, ws_bytes, None)
+
+    assert call(ikv, lat, 0) == S.SKV_EINVAL
+    assert call(ikv, lat, 65537) == S.SKV_EINVAL
+    assert call(ikv, ikv, 2048) == S.SKV_EINVAL          # the attended KV must be latent
+    other = _kv(B=1, H=1, L_max=32768, block=16, block_table=1)
+    assert call(other, lat, 2048) == S.SKV_EINVAL        # shapes must match
+    assert call(ikv, lat, 2048, G=24) == S.SKV_EUNSUPPORTED
+    assert call(ikv, lat, 2048, ws_bytes=1024) == S.SKV_EWORKSPACE
+
+
 def test_compact_apply_validates_pool_size():
     L = S.lib()
     kv = _kv(B=1, H=1, L_max=64, block=16, token_table=1)

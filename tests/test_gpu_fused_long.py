@@ -42,11 +42,34 @@ def _resume(r, ws=None):
     return scores, idx, cnt, out, ws
 
 
+def _indexer(r, ws=None):
+    """sparsekv_indexer_attend: the indexer scan, top-k and latent attention
+    in one call (segment candidates for rows longer than one sweep, k <= 2048)."""
+    st = r.st
+    skv, kv = r.skv, r.kv
+    B, H, L = skv.B, skv.H, skv.L_max
+    scores = torch.empty((B, H, L), dtype=torch.float32, device=DEV)
+    idx = torch.full((B, H, st.k), -7, dtype=torch.int32, device=DEV)
+    cnt = torch.full((B, H), -7, dtype=torch.int32, device=DEV)
+    out = torch.full((kv.B, kv.H * st.G, kv.d_v), float("nan"), dtype=torch.float32, device=DEV)
+    if ws is None:
+        ws = S.workspace(S.sparsekv_workspace_size(S.SKV_OP_SELECT_ATTEND, kv, st.G, st.k), DEV)
+    S.sparsekv_indexer_attend(skv, r.sq, st.score_G, kv, r.q, st.G, r.lo, r.hi, st.k, st.scale,
+                              scores, idx, cnt, out, ws)
+    torch.cuda.synchronize()
+    return scores, idx, cnt, out, ws
+
+
 def _check(st, rows=None):
     say("fused long case", st.name, "G", st.G, "L", st.kv.L_max, "k", st.k)
     r = Run(st)
+    # the one-call indexer step against the oracle and the two-call path
+    _, iidx, icnt, iout, _ = _indexer(r)
+    iidx, icnt, iout = iidx.cpu().numpy(), icnt.cpu().numpy(), iout.cpu().numpy()
     sc, idx, cnt, out, ws = _resume(r)
     idx, cnt, out = idx.cpu().numpy(), cnt.cpu().numpy(), out.cpu().numpy()
+    assert np.array_equal(iidx, idx) and np.array_equal(icnt, cnt)
+    assert np.abs(iout - out).max() <= ATTN_TOL
     B, H = st.score_kv.B, st.score_kv.H
     rows = [(b, h) for b in range(B) for h in range(H)] if rows is None else rows
     ref = D.step(st, rows=rows)
@@ -93,18 +116,59 @@ def test_fused_latent_with_sink_local_and_short_sequence():
 
 
 def test_fused_latent_list_overflow_takes_the_row_fallback():
-    """All indexer keys equal: every score ties, the candidate list overflows
-    and each attending workgroup selects from the row itself (lowest
-    positions win the ties)."""
+    """All indexer keys equal: every score ties, the candidate list (and
+    every scan segment's candidates) overflows and each attending workgroup
+    selects from the row itself (lowest positions win the ties)."""
     st = W.make_indexer_mla(tag=712, L=40960, k=1024, n_heads=16)
     st.score_kv.k[:] = st.score_kv.k[0, 0, 0]
     r = Run(st)
-    sc, idx, cnt, out, _ = _resume(r)
-    idx, cnt = idx.cpu().numpy(), cnt.cpu().numpy()
-    assert cnt[0, 0] == 1024
-    assert idx[0, 0].tolist() == list(range(1024))
     ref = D.step(st)
-    assert np.abs(out.cpu().numpy() - ref["out"]).max() <= ATTN_TOL
+    for call in (_resume, _indexer):
+        sc, idx, cnt, out, _ = call(r)
+        idx, cnt = idx.cpu().numpy(), cnt.cpu().numpy()
+        assert cnt[0, 0] == 1024
+        assert idx[0, 0].tolist() == list(range(1024))
+        assert np.abs(out.cpu().numpy() - ref["out"]).max() <= ATTN_TOL
+
+
+def test_indexer_segments_crowded_by_a_run_of_top_keys():
+    """1,500 consecutive tokens carry the highest indexer scores, so the scan
+    segments holding them cannot list all of their keys that rank in the
+    top-k: their cuts lie above the k-th candidate and the row is selected
+    from its scores; the result is still the exact top-k."""
+    st = W.make_indexer_mla(tag=713, L=65536, k=2048, n_heads=32)
+    qf = (st.score_q[0, 0].astype(np.uint32) << 16).view(np.float32)
+    kb = (((qf * 4).view(np.uint32) + 0x8000) >> 16).astype(np.uint16)   # bf16 of 4 q
+    blocks = st.score_kv.block_table[0]
+    for t in range(3000, 4500):
+        st.score_kv.k[blocks[t // 16], 0, t % 16] = kb
+    assert _check(st) == 0
+    r = Run(st)
+    _, idx, cnt, _, _ = _indexer(r)
+    sel = set(idx[0, 0].cpu().numpy().tolist())
+    assert int(cnt[0, 0]) == 2048 and set(range(3000, 4500)) <= sel
+
+
+def test_indexer_attend_repeated_calls_and_short_k():
+    """Two calls in a row on one workspace (the segment lists are rewritten
+    whole by every scan), then k = 1 and a window that leaves fewer
+    candidates than k."""
+    st = W.make_indexer_mla(tag=714, L=49152, k=700, n_heads=16)
+    r = Run(st)
+    ref = D.step(st)
+    ws = None
+    for _ in range(2):
+        _, idx, cnt, out, ws = _indexer(r, ws)
+        sel = ref["idx"][0, 0][: ref["count"][0, 0]]
+        assert check_selection(ref["scores"][0, 0], sel, idx[0, 0].cpu().numpy(),
+                               int(cnt[0, 0])) == 0
+        assert np.abs(out.cpu().numpy() - ref["out"]).max() <= ATTN_TOL
+    st.k = 1
+    assert _check(st) == 0
+    st.k = 2000
+    st.lo = np.array([30000], np.int32)
+    st.hi = np.array([31500], np.int32)   # 1,500 candidates < k
+    assert _check(st) == 0
 
 
 @pytest.mark.slow
@@ -150,6 +214,22 @@ def test_fused_gqa_long_paged(G, L, k):
 def test_fused_gqa_long_token_table():
     st = W.make_token_pool(tag=730, B=3, H=2, L=65536, k=2048, sink=4, local=128)
     assert _check_gqa(st) == 0
+
+
+def test_fused_gqa_long_segments_crowded_by_a_run_of_top_keys():
+    """Few long GQA rows take the scan's segment candidates: a run of 3,000
+    top-scoring tokens in one row overflows its segments, so that row is
+    selected from its scores; the other rows keep the candidates."""
+    st = W.make_gqa_paged(tag=732, B=2, H=2, G=1, L=65536, k=2048, sink=4, local=64)
+    qf = (st.q[1, 1].astype(np.uint32) << 16).view(np.float32)
+    kb = (((qf * 4).view(np.uint32) + 0x8000) >> 16).astype(np.uint16)   # bf16 of 4 q
+    blocks = st.kv.block_table[1]
+    for t in range(10000, 13000):
+        st.kv.k[blocks[t // 16], 1, t % 16] = kb
+    assert _check_gqa(st) == 0
+    r = Run(st)
+    _, idx, cnt, _ = r.select_attend()
+    assert int(cnt[1, 1]) == 2048 and idx[1, 1].cpu().numpy().tolist() == list(range(10000, 12048))
 
 
 def test_fused_gqa_long_list_overflow_fallback():

@@ -64,6 +64,36 @@ __device__ __forceinline__ void row_to_lds(const uint16_t* src, uint16_t* dst, i
                                      16, 0, 0);
 }
 
+// S^T of one 32-token chunk for 16 heads: S[hf] (lane (n, g4): tokens
+// 16 hf + 4 g4 + i of the chunk, head n) = sum over the 18 k-steps j of
+// K_hf[16 x 32] . Q^T[32 x 16], K_hf from the token-major LDS rows (krow:
+// this lane's piece of token n, k-step 0) and the B operand qf(j).  The
+// LDS reads go in batches of 6 k-steps, all issued before their products:
+// one k-step at a time, each product waited for its own reads (1.9 us per
+// chunk for the 36 products).
+template <class QF>
+__device__ __forceinline__ void logits_from_lds(const uint16_t* krow, QF&& qf, f32x4_t (&S)[2]) {
+  constexpr int kBatch = 6;
+  static_assert(kNC % kBatch == 0, "k-step batches");
+  S[0] = S[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j0 = 0; j0 < kNC; j0 += kBatch) {
+    bf16x8_t k0[kBatch], k1[kBatch], qb[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int j = j0 + u;
+      k0[u] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(krow + 32 * j));
+      k1[u] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(krow + 16 * kRowPad + 32 * j));
+      qb[u] = qf(j);
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      S[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0[u], qb[u], S[0], 0, 0, 0);
+      S[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1[u], qb[u], S[1], 0, 0, 0);
+    }
+  }
+}
+
 // 4 tokens x 1 dim of the value operand from token-major LDS rows
 __device__ __forceinline__ u32x2_t value_tr(const uint16_t* p) {
   const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)p);
@@ -145,17 +175,7 @@ __global__ __launch_bounds__(WAVES * 64) void mla_split_kernel(
     for (int c0 = 0; c0 < cnt; c0 += 32) {
       // S^T[token 16 hf + 4 g4 + i][head n] for the two 16-token halves
       f32x4_t S[2];
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        S[hf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < kNC; ++j) {
-          const bf16x8_t Kf = __builtin_bit_cast(
-              bf16x8_t,
-              *(const u32x4_t*)(rows + (c0 + 16 * hf + n) * kRowPad + 8 * (4 * j + g4)));
-          S[hf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Kf, Qf[j], S[hf], 0, 0, 0);
-        }
-      }
+      logits_from_lds(rows + (c0 + n) * kRowPad + 8 * g4, [&](int j) { return Qf[j]; }, S);
       float z[8];
       float cm = -INFINITY;
 #pragma unroll
@@ -358,19 +378,10 @@ __global__ __launch_bounds__(kRowThreads) void mla_list_kernel(
       if (on && dp == 0) {
         // S^T[token 16 hf + 4 g4 + i][head n] for the two 16-token halves
         f32x4_t S[2];
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          S[hf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int j = 0; j < kNC; ++j) {
-            const bf16x8_t Kf = __builtin_bit_cast(
-                bf16x8_t,
-                *(const u32x4_t*)(rows + (c0 + 16 * hf + n) * kRowPad + 8 * (4 * j + g4)));
-            const bf16x8_t Qf =
-                __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(qrow + 8 * (4 * j + g4)));
-            S[hf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Kf, Qf, S[hf], 0, 0, 0);
-          }
-        }
+        const uint16_t* qg = qrow + 8 * g4;
+        logits_from_lds(rows + (c0 + n) * kRowPad + 8 * g4, [&](int j) {
+          return __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(qg + 32 * j));
+        }, S);
         float z[8];
         float cm = -INFINITY;
 #pragma unroll

@@ -227,7 +227,7 @@ __device__ __forceinline__ int row_select_alone(const float* scores, int row, in
 template <int KPER, typename Emit>
 __device__ __forceinline__ int select_listed(int k, uint4 gv, RowSelLds& L,
                                              const uint32_t (&key)[KPER], const int (&pos)[KPER],
-                                             Emit&& emit) {
+                                             Emit&& emit, int* first_bin = nullptr) {
   // threshold over the listed keys
   *(uint4*)(L.hist + 4 * threadIdx.x) = gv;
   if (threadIdx.x < 256) L.dh[threadIdx.x] = 0u;
@@ -240,7 +240,7 @@ __device__ __forceinline__ int select_listed(int k, uint4 gv, RowSelLds& L,
 #pragma unroll
         for (int u = 0; u < KPER; ++u) f(key[u]);
       },
-      &T, &need_eq, &k_sel);
+      &T, &need_eq, &k_sel, first_bin);
 
   // ranks: the lane's entries are consecutive list ranks
   int c = 0;
@@ -478,19 +478,27 @@ __device__ __forceinline__ int local_list_select(const float* scores, int row, i
 // Exact selection of row `row` from the segment candidates the score scan
 // listed in ws (topk_seg_count: S segments of m = kSegSlots / S slots, keys
 // in position order): lane t takes slots KPER t .. KPER t + KPER - 1, all in
-// one segment (keys past the segment's count read as 0, never selected), the
-// first digit's histogram is built from the listed keys in LDS, and
-// select_listed finishes: emit(dst, pos, key) for every selected key, dst its
-// rank in ascending position order.  That is the row's exact top-k when no
-// key left out can rank among it: every segment's cut (all its unlisted keys
-// are below it) is at most the k-th selected key, and no segment left keys
-// out if fewer than k were listed.  Returns the number selected, or -1 when
-// that does not hold (the caller then selects the row alone).
+// one segment (keys past the segment's count read as 0, never selected), and
+// select_listed finishes over them: emit(dst, pos, key) for every selected
+// key, dst its rank in ascending position order.  The candidates are the top
+// of every segment, so their keys share their leading bits and would crowd
+// into a few bins of the first 12-bit digit (same-address LDS atomics: 2.6 us
+// for 7,000 candidates in about 4 bins); the keys are shifted left past the
+// bits all candidates share but one, whose place takes a set top bit (order
+// and distinctness kept, no key 0 or in a low bin), which spreads them over
+// the digit's bins.  The result
+// is the row's exact top-k when no key left out can rank among it: every
+// segment's cut (all its unlisted keys are below it, a multiple of 2^20) is
+// at most the smallest key of the k-th candidate's first-digit bin, and no
+// segment left keys out if fewer than k were listed.  Returns the number
+// selected, or -1 when that does not hold (the caller then selects the row
+// alone).
 template <typename Emit>
 __device__ __forceinline__ int seg_select(const TopkWs& ws, int row, int S, int k, RowSelLds& L,
                                           Emit&& emit) {
   constexpr int KPER = kSegSlots / kRowThreads;
   static_assert(KPER == 8, "two 16-byte loads of keys and of positions per lane");
+  const int lane = threadIdx.x & 63, wave = row_wave();
   const int m = kSegSlots / S;   // a power of two >= 16
   const int64_t rb = (int64_t)row * kRowList;
   const int slot0 = KPER * threadIdx.x;
@@ -500,33 +508,61 @@ __device__ __forceinline__ int seg_select(const TopkWs& ws, int row, int S, int 
   const uint4 kb = *(const uint4*)(ws.seg_key() + rb + slot0 + 4);
   const int4 pa = *(const int4*)(ws.seg_pos() + rb + slot0);
   const int4 pb = *(const int4*)(ws.seg_pos() + rb + slot0 + 4);
-  const uint32_t cut = (int)threadIdx.x < S ? ws.seg_cut()[rb + threadIdx.x] : 0u;
+  uint32_t cut = (int)threadIdx.x < S ? ws.seg_cut()[rb + threadIdx.x] : 0u;
+  *(uint4*)(L.hist + 4 * threadIdx.x) = make_uint4(0u, 0u, 0u, 0u);
   const uint32_t kv8[8] = {ka.x, ka.y, ka.z, ka.w, kb.x, kb.y, kb.z, kb.w};
   const int pv8[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
   uint32_t key[KPER];
   int pos[KPER];
+  uint32_t kand = 0xffffffffu, kor = 0u;   // over the candidates
 #pragma unroll
   for (int u = 0; u < KPER; ++u) {
     key[u] = o + u < n_in ? kv8[u] : 0u;
     pos[u] = pv8[u];
+    if (key[u]) {
+      kand &= key[u];
+      kor |= key[u];
+    }
   }
-  // the listed keys' top-12-bit histogram
-  *(uint4*)(L.hist + 4 * threadIdx.x) = make_uint4(0u, 0u, 0u, 0u);
-  lds_barrier();
 #pragma unroll
-  for (int u = 0; u < KPER; ++u)
+  for (int d = 32; d >= 1; d >>= 1) {
+    cut = max(cut, (uint32_t)__shfl_xor((int)cut, d, 64));
+    kand &= (uint32_t)__shfl_xor((int)kand, d, 64);
+    kor |= (uint32_t)__shfl_xor((int)kor, d, 64);
+  }
+  if (lane == 0) {
+    L.wa[wave] = (int)cut;
+    L.we[wave] = (int)kand;
+    L.wt[wave] = (int)kor;
+  }
+  lds_barrier();   // L.hist is zero, the waves' reductions are in
+  uint32_t max_cut = 0u;
+  kand = 0xffffffffu;
+  kor = 0u;
+#pragma unroll
+  for (int v = 0; v < kRowWaves; ++v) {
+    max_cut = max(max_cut, (uint32_t)L.wa[v]);
+    kand &= (uint32_t)L.we[v];
+    kor |= (uint32_t)L.wt[v];
+  }
+  const uint32_t diff = kand ^ kor;                  // bits where some candidates differ
+  const int sh = kor == 0u ? 0 : min(diff ? __clz(diff) : 32, 24);
+  const uint32_t prefix = sh ? (kand & ~(0xffffffffu >> sh)) : 0u;
+  // shifted keys keep the top bit set: never 0 and never in a low bin,
+  // which the later digits take as empty slots
+#pragma unroll
+  for (int u = 0; u < KPER; ++u) {
+    if (sh && key[u]) key[u] = 0x80000000u | (key[u] << (sh - 1));
     if (key[u]) atomicAdd(&L.hist[key[u] >> 20], 1u);
+  }
   lds_barrier();
   const uint4 gv = *(const uint4*)(L.hist + 4 * threadIdx.x);
-  uint32_t mk = 0xffffffffu;   // smallest key this lane selected
-  const int n_sel = select_listed<KPER>(k, gv, L, key, pos, [&](int dst, int p, uint32_t kk) {
-    mk = min(mk, kk);
-    emit(dst, p, kk);
-  });
-  const uint32_t kth = block_min_u32(mk, (uint32_t*)L.wt);
-  const uint32_t max_cut = ~block_min_u32(~cut, (uint32_t*)L.wa);
-  if (max_cut == 0u) return n_sel;                 // every window key was listed
-  return (n_sel == k && kth >= max_cut) ? n_sel : -1;
+  auto orig = [&](uint32_t kk) { return sh ? (prefix | ((kk & 0x7fffffffu) >> (sh - 1))) : kk; };
+  int b0;   // the first-digit bin of the k-th candidate (-1: not below every candidate)
+  const int n_sel = select_listed<KPER>(
+      k, gv, L, key, pos, [&](int dst, int p, uint32_t kk) { emit(dst, p, orig(kk)); }, &b0);
+  if (max_cut == 0u) return n_sel;   // every window key was listed
+  return (n_sel == k && b0 >= 0 && max_cut <= orig((uint32_t)b0 << 20)) ? n_sel : -1;
 }
 
 // The selection of a row whose list overflowed, for kernels that finish the

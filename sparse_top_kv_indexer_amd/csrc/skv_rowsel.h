@@ -211,17 +211,19 @@ template <class KeysReady, class Prepare, class ForKeys>
 __device__ __forceinline__ void row_threshold_p(RowSelLds& L, int k, KeysReady&& keys_ready,
                                                 Prepare&& prepare, ForKeys&& for_keys,
                                                 uint32_t* T_out, int* need_eq_out,
-                                                int* k_sel_out) {
+                                                int* k_sel_out, int* first_bin = nullptr) {
   const int lane = threadIdx.x & 63, wave = row_wave();
   int n_cand;
   const int k_sel = row_search4096(L, -k, &n_cand);   // min(k, n_cand)
   keys_ready();
   uint32_t T = 0u;   // k_sel == n_cand: every finite key (key > 0)
   int need_eq = 0;
+  if (first_bin) *first_bin = -1;
   if (k_sel <= 0) {
     T = 0xffffffffu;   // nothing: finite keys are below 0xff800000
   } else if (k_sel < n_cand) {
     const int b0 = L.trio[0], above = L.trio[1], in_bin = L.trio[2];
+    if (first_bin) *first_bin = b0;
     int need = k_sel - above;
     T = ((uint32_t)b0 << 20) - 1u;   // the whole bin b0 is taken
     if (need < in_bin) {
@@ -274,8 +276,10 @@ __device__ __forceinline__ void row_threshold_p(RowSelLds& L, int k, KeysReady&&
 template <class KeysReady, class ForKeys>
 __device__ __forceinline__ void row_threshold(RowSelLds& L, int k, KeysReady&& keys_ready,
                                               ForKeys&& for_keys, uint32_t* T_out,
-                                              int* need_eq_out, int* k_sel_out) {
-  row_threshold_p(L, k, keys_ready, [](int, int) {}, for_keys, T_out, need_eq_out, k_sel_out);
+                                              int* need_eq_out, int* k_sel_out,
+                                              int* first_bin = nullptr) {
+  row_threshold_p(L, k, keys_ready, [](int, int) {}, for_keys, T_out, need_eq_out, k_sel_out,
+                  first_bin);
 }
 
 // Per group g, the lane's counts of keys above T (low 16 bits) and equal to T

@@ -251,23 +251,27 @@ int mla_splits(int k) { return std::max(8, std::min(64, (k + 63) / 64 + 7) / 8 *
 
 // ------------------------------------------ selection fused with attention --
 // After the slice listing of a long row (the exact top-k's list in the top-k
-// workspace), one kernel finishes the selection and attends: grid (n_split,
-// rows x head parts), 1024 threads.  Every workgroup of a row resolves the
-// row's exact selection from the list by itself (list_select; the row alone
-// when the list overflowed), so no workgroup waits for another; split s takes
-// the selected keys of ranks [s n_sel / n_split, (s + 1) n_sel / n_split) and
-// an equal share of the always-attended tokens (t < lo, t >= hi), stages their
-// latent rows in LDS 64 at a time with the load unit, and attends for its
-// 16 (kRowWaves / DP) query heads, whose rows it also stages in LDS.  The 16
-// waves are 16-head groups x DP parts of the value dims.  Per 32 staged tokens
-// the first wave of a head group forms the logits (2 x 18
-// v_mfma_f32_16x16x32_bf16), updates the online softmax and leaves the
-// probability fragments (bf16 head + tail, the A operand of the value product)
-// and the rescale factors in LDS; after one barrier every wave of the group
-// applies them to its 32 / DP column blocks of 16 value dims.  Per-wave state
-// stays small (the accumulators of 512 / DP dims), which 1024-thread
-// workgroups need.  Split 0 of head part 0 writes idx and count.  The rows'
-// histograms and list counters are zeroed by the merge kernel that follows.
+// workspace) or a scan that listed segment candidates (SEG), one kernel
+// finishes the selection and attends: grid (n_split, rows x head parts), 1024
+// threads.  Every workgroup of a row resolves the row's exact selection by
+// itself (list_select or seg_select; the row alone when those do not settle
+// it), so no workgroup waits for another; split s takes the selected keys of
+// ranks [s n_sel / n_split, (s + 1) n_sel / n_split) and an equal share of
+// the always-attended tokens (t < lo, t >= hi), stages their latent rows in
+// LDS 64 at a time with the load unit, and attends for its 16 (kRowWaves /
+// DP) query heads, whose rows it also stages in LDS.  The 16 waves are
+// 16-head groups x DP parts of the value dims.  Per staged block (up to two
+// 32-token chunks) waves 0 and 1 of a head group form the logits of one chunk
+// each at the same time (2 x 18 v_mfma_f32_16x16x32_bf16), exchange their
+// maxima through LDS (one barrier), update the online softmax with the
+// block's max and leave the probability fragments (bf16 head + tail, the A
+// operand of the value product) and the rescale factor in LDS; after a second
+// barrier every wave of the group applies them to its 32 / DP column blocks
+// of 16 value dims for both chunks (one chunk's logits after another took
+// 1.56 us each).  Per-wave state stays small (the accumulators of 512 / DP
+// dims), which 1024-thread workgroups need.  Split 0 of head part 0 writes
+// idx and count.  The rows' histograms and list counters are zeroed by the
+// merge kernel that follows.
 constexpr int kFuseRows = 64;          // latent rows staged at a time
 constexpr int kFuseSlices = 1024;      // listing slices of a row this kernel reads
 
@@ -284,8 +288,10 @@ __global__ __launch_bounds__(kRowThreads) void mla_list_kernel(
   __shared__ int klist_n;
   __shared__ __attribute__((aligned(16))) uint16_t rows[kFuseRows * kRowPad];
   __shared__ __attribute__((aligned(16))) uint16_t qs[kHeadsPerWg * kRowPad];
-  __shared__ u32x4_t pfrag[NHG][2][64][2];          // [group][chunk parity][lane][head, tail]
-  __shared__ float cfac[NHG][2][16];                // rescale factor per head
+  __shared__ u32x4_t pfrag[NHG][2][64][2];          // [group][chunk][lane][head, tail]
+  __shared__ float cfac[NHG][16];                   // rescale factor per head
+  __shared__ float cmax[NHG][2][16];                // the chunks' logit maxima per head
+  __shared__ float lsum[NHG][16];                   // the second logit wave's weight sums
   __shared__ int64_t roff[kFuseRows];
   const int n_hp = (G + kHeadsPerWg - 1) / kHeadsPerWg;   // head parts per row
   const int s = blockIdx.x, row = blockIdx.y / n_hp, hp = blockIdx.y - row * n_hp;
@@ -303,6 +309,19 @@ __global__ __launch_bounds__(kRowThreads) void mla_list_kernel(
   for (int r = wave; r < kHeadsPerWg; r += kRowWaves) {
     const int hd = hp * kHeadsPerWg + r;
     row_to_lds(qhead + (int64_t)(hd < G ? hd : 0) * kDk, qs + r * kRowPad, lane);
+  }
+  // the sequence's block table too, into the latent-row area (free until the
+  // first block of rows is staged), so the first block's addresses need no
+  // table load after the selection (1.6 us of dependent loads otherwise)
+  const int n_bt = kv.block_table && !kv.token_table ? (kv.L_max >> 4) : 0;
+  const bool bt_lds = n_bt > 0 && n_bt % 256 == 0 && n_bt * 4 <= (int)sizeof(rows) &&
+                      ((uintptr_t)kv.block_table & 15) == 0;
+  const int32_t* btl = (const int32_t*)rows;
+  if (bt_lds) {
+    const int32_t* src = kv.block_table + (int64_t)b * n_bt;
+    for (int c = wave; c < n_bt / 256; c += kRowWaves)
+      __builtin_amdgcn_global_load_lds((gbl_void_t)(src + c * 256 + 4 * lane),
+                                       (lds_void_t)(rows + c * 512), 16, 0, 0);
   }
 
   // 1. the row's exact selection, positions ascending in L.hist[0 .. n_sel)
@@ -341,16 +360,22 @@ __global__ __launch_bounds__(kRowThreads) void mla_list_kernel(
   const int n_list = r1 - r0, n_att = n_list + (x1 - x0);
   const uint16_t* kb = (const uint16_t*)kv.k;
 
-  float m_run = -INFINITY, l_run = 0.f;   // first wave of a group: head head0 + n
+  // online softmax state of head head0 + n, kept by the group's two logit
+  // waves (dp 0 and 1: the two 32-token chunks of a staged block); both
+  // track the same running max, each the sum of its own chunks' weights
+  float m_run = -INFINITY, l_run = 0.f;
   f32x4_t O[VB];
 #pragma unroll
   for (int c = 0; c < VB; ++c) O[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  int parity = 0;
   const uint16_t* qrow = qs + (hg * 16 + n) * kRowPad;
+  const bool logit_wave = on && dp < 2;
+  if (bt_lds) __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();   // the block table is in LDS
 
   for (int q0 = 0; q0 < n_att; q0 += kFuseRows) {
     const int cnt = min(kFuseRows, n_att - q0);
     const int n_rows = (cnt + 31) & ~31;
+    const int nch = n_rows >> 5;   // 32-token chunks of this block (1 or 2)
     if (tid < kFuseRows) {
       int64_t ro = -1;
       if (tid < cnt) {
@@ -362,7 +387,11 @@ __global__ __launch_bounds__(kRowThreads) void mla_list_kernel(
           const int x = x0 + (i - n_list);
           t = x < lo ? x : hi + (x - lo);
         }
-        const int64_t slot = slot_of(kv, b, t);
+        int64_t slot;
+        if (bt_lds && q0 == 0)   // slot_of with the table entry from LDS (seq <= L_max)
+          slot = (t < 0 || t >= seq) ? -1 : (int64_t)btl[t >> 4] * 16 + (t & 15);
+        else
+          slot = slot_of(kv, b, t);
         ro = slot >= 0 ? row_elem(kv, b, h, slot, kDk) : -1;
       }
       roff[tid] = ro;
@@ -374,37 +403,46 @@ __global__ __launch_bounds__(kRowThreads) void mla_list_kernel(
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();   // the staged latent rows (and, the first time, the query rows)
-    for (int c0 = 0; c0 < cnt; c0 += 32) {
-      if (on && dp == 0) {
-        // S^T[token 16 hf + 4 g4 + i][head n] for the two 16-token halves
-        f32x4_t S[2];
-        const uint16_t* qg = qrow + 8 * g4;
-        logits_from_lds(rows + (c0 + n) * kRowPad + 8 * g4, [&](int j) {
-          return __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(qg + 32 * j));
-        }, S);
-        float z[8];
-        float cm = -INFINITY;
+    // logits of chunk dp by the group's waves dp < 2, both chunks at once:
+    // S^T[token 16 hf + 4 g4 + i][head n] for the chunk's two 16-token halves
+    float z[8];
+    float cm = -INFINITY;
+    if (logit_wave && dp < nch) {
+      const int c0 = 32 * dp;
+      f32x4_t S[2];
+      const uint16_t* qg = qrow + 8 * g4;
+      logits_from_lds(rows + (c0 + n) * kRowPad + 8 * g4, [&](int j) {
+        return __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(qg + 32 * j));
+      }, S);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int tk = c0 + 16 * (e >> 2) + 4 * g4 + (e & 3);
-          const bool ok = tk < cnt && roff[tk] >= 0;
-          z[e] = ok ? S[e >> 2][e & 3] * scale_log2 : -INFINITY;
-          cm = fmaxf(cm, z[e]);
-        }
-        cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
-        cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
-        const float m_new = fmaxf(m_run, cm);
-        float p[8], ps = 0.f;
+      for (int e = 0; e < 8; ++e) {
+        const int tk = c0 + 16 * (e >> 2) + 4 * g4 + (e & 3);
+        const bool ok = tk < cnt && roff[tk] >= 0;
+        z[e] = ok ? S[e >> 2][e & 3] * scale_log2 : -INFINITY;
+        cm = fmaxf(cm, z[e]);
+      }
+      cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
+      cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
+    } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          p[e] = m_new == -INFINITY ? 0.f : exp2f(z[e] - m_new);
-          ps += p[e];
-        }
-        ps += __shfl_xor(ps, 16, 64);
-        ps += __shfl_xor(ps, 32, 64);
-        const float corr = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
-        l_run = l_run * corr + ps;
-        m_run = m_new;
+      for (int e = 0; e < 8; ++e) z[e] = -INFINITY;
+    }
+    if (logit_wave && g4 == 0) cmax[hg][dp][n] = cm;
+    lds_barrier();   // the two chunks' maxima
+    if (logit_wave) {
+      const float m_new = fmaxf(m_run, fmaxf(cmax[hg][0][n], cmax[hg][1][n]));
+      float p[8], ps = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = m_new == -INFINITY ? 0.f : exp2f(z[e] - m_new);
+        ps += p[e];
+      }
+      ps += __shfl_xor(ps, 16, 64);
+      ps += __shfl_xor(ps, 32, 64);
+      const float corr = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
+      l_run = l_run * corr + ps;
+      m_run = m_new;
+      if (dp < nch) {
         uint32_t ph[4], pl[4];
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
@@ -414,33 +452,40 @@ __global__ __launch_bounds__(kRowThreads) void mla_list_kernel(
           ph[e >> 1] = h0 | (h1 << 16);
           pl[e >> 1] = l0 | (l1 << 16);
         }
-        pfrag[hg][parity][lane][0] = u32x4_t{ph[0], ph[1], ph[2], ph[3]};
-        pfrag[hg][parity][lane][1] = u32x4_t{pl[0], pl[1], pl[2], pl[3]};
-        if (g4 == 0) cfac[hg][parity][n] = corr;
+        pfrag[hg][dp][lane][0] = u32x4_t{ph[0], ph[1], ph[2], ph[3]};
+        pfrag[hg][dp][lane][1] = u32x4_t{pl[0], pl[1], pl[2], pl[3]};
       }
-      lds_barrier();   // the group's probabilities and rescale factors
-      if (on) {
-        float oc[4];
+      if (dp == 0 && g4 == 0) cfac[hg][n] = corr;
+    }
+    lds_barrier();   // the group's probabilities of both chunks and the rescale factor
+    if (on) {
+      float oc[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) oc[i] = cfac[hg][parity][4 * g4 + i];
-        const bf16x8_t Ph = __builtin_bit_cast(bf16x8_t, pfrag[hg][parity][lane][0]);
-        const bf16x8_t Pl = __builtin_bit_cast(bf16x8_t, pfrag[hg][parity][lane][1]);
+      for (int i = 0; i < 4; ++i) oc[i] = cfac[hg][4 * g4 + i];
+#pragma unroll
+      for (int c = 0; c < VB; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) O[c][i] *= oc[i];
+      for (int ch = 0; ch < nch; ++ch) {
+        const bf16x8_t Ph = __builtin_bit_cast(bf16x8_t, pfrag[hg][ch][lane][0]);
+        const bf16x8_t Pl = __builtin_bit_cast(bf16x8_t, pfrag[hg][ch][lane][1]);
         const uint16_t* v0 =
-            rows + (c0 + 4 * g4 + (n >> 2)) * kRowPad + 4 * (n & 3) + 16 * VB * dp;
+            rows + (32 * ch + 4 * g4 + (n >> 2)) * kRowPad + 4 * (n & 3) + 16 * VB * dp;
         const uint16_t* v1 = v0 + 16 * kRowPad;
 #pragma unroll
         for (int c = 0; c < VB; ++c) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) O[c][i] *= oc[i];
           const u32x2_t a = value_tr(v0 + 16 * c), bb = value_tr(v1 + 16 * c);
           const bf16x8_t Vf = __builtin_bit_cast(bf16x8_t, u32x4_t{a[0], a[1], bb[0], bb[1]});
           O[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ph, Vf, O[c], 0, 0, 0);
           O[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Pl, Vf, O[c], 0, 0, 0);
         }
       }
-      parity ^= 1;   // the next chunk writes the other buffer; a barrier lies between
     }
   }
+  // the second logit wave's weight sum joins the first's
+  if (logit_wave && dp == 1 && g4 == 0) lsum[hg][n] = l_run;
+  lds_barrier();
+  if (logit_wave && dp == 0) l_run += lsum[hg][n];
 
   // 3. the split partial: O[head][512], max, sum (lane holds heads 4 g4 + i);
   // an empty share never waited for the staged query rows

@@ -226,7 +226,42 @@ __device__ __forceinline__ void row_threshold_p(RowSelLds& L, int k, KeysReady&&
     if (first_bin) *first_bin = b0;
     int need = k_sel - above;
     T = ((uint32_t)b0 << 20) - 1u;   // the whole bin b0 is taken
-    if (need < in_bin) {
+    if (need < in_bin && in_bin <= 64) {
+      // few keys in bin b0: one wave sorts them (bitonic, one key per lane)
+      // and reads the need-th largest, instead of two more digit passes
+      lds_barrier();   // everyone has read trio
+      if (threadIdx.x == 0) L.wa[0] = 0;
+      lds_barrier();
+      for_keys([&](uint32_t key) {
+        if ((key >> 20) == (uint32_t)b0) {
+          const int i = atomicAdd(&L.wa[0], 1);
+          if (i < 64) L.dh[i] = key;
+        }
+      });
+      lds_barrier();
+      if (wave == 0) {
+        uint32_t v = lane < in_bin ? L.dh[lane] : 0u;
+#pragma unroll
+        for (int sz = 2; sz <= 64; sz <<= 1)
+#pragma unroll
+          for (int j = sz >> 1; j >= 1; j >>= 1) {
+            const uint32_t o = (uint32_t)__shfl_xor((int)v, j, 64);
+            // descending runs where (lane & sz) == 0; the lower lane keeps the larger
+            const bool lower = (lane & j) == 0;
+            const bool desc = (lane & sz) == 0;
+            v = (lower == desc) ? max(v, o) : min(v, o);
+          }
+        const uint32_t t_key = (uint32_t)__shfl((int)v, need - 1, 64);
+        const int gt = __popcll(__ballot(v > t_key));
+        if (lane == 0) {
+          L.trio[0] = (int)t_key;
+          L.trio[1] = need - gt;
+        }
+      }
+      lds_barrier();
+      T = (uint32_t)L.trio[0];
+      need_eq = L.trio[1];
+    } else if (need < in_bin) {
       prepare(b0, in_bin);
       // bits 19..8 of the keys of bin b0 (finite keys have top bits >= 8, so
       // b0 >= 8 and empty slots never match)

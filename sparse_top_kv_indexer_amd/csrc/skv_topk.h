@@ -78,11 +78,12 @@ constexpr int kSegMaxK = 2048;      // k served (a quarter of the slots)
 
 // Segments per row for `rows` rows of L_max slots and k, or 0 when the
 // segment candidates do not serve the call: a power of two giving about 1024
-// workgroups in all, at most kSegMax, each segment at most kSegMaxKeys keys.
+// workgroups in all, at most 256 unless a segment would exceed kSegMaxKeys
+// keys (one row of 131,072: 256 segments scanned in 12.0 us, 512 in 12.6).
 inline int topk_seg_count(int rows, int L_max, int k) {
   const int64_t slots = L_max % 4 == 0 ? (int64_t)L_max : (int64_t)L_max + 3;
   if (rows < 1 || k < 1 || k > kSegMaxK || slots <= 32768) return 0;
-  int S = kSegMax;
+  int S = 256;
   while (S > 1 && (int64_t)rows * S > 1024) S >>= 1;
   const int64_t cpr = ((int64_t)L_max + 15) / 16;
   while (S < kSegMax && cpr > (int64_t)S * (kSegMaxKeys / 16)) S <<= 1;

@@ -184,6 +184,37 @@ def test_indexer_attend_validates_before_any_launch():
     assert call(ikv, lat, 2048, ws_bytes=1024) == S.SKV_EWORKSPACE
 
 
+def test_segment_pair_applies_to_long_rows_and_validates_first():
+    """sparsekv_segments says where the segment path applies (long rows,
+    k <= 2048, a selecting kernel for the shape; GQA only below 128 rows);
+    both halves check their arguments before any launch."""
+    L = S.lib()
+    P = ctypes.c_void_p(1)
+    win = S.skv_window(P, P)
+    gqa = _kv(B=2, H=2, L_max=131072, block=16, block_table=1)
+    lat = _kv(B=1, H=1, L_max=131072, block=16, block_table=1, v=None, d_k=576, d_v=512)
+    assert L.sparsekv_segments(ctypes.byref(gqa), 4, 2048) > 0
+    assert L.sparsekv_segments(ctypes.byref(gqa), 4, 2049) == 0        # k above 2048
+    assert L.sparsekv_segments(ctypes.byref(lat), 128, 2048) > 0
+    assert L.sparsekv_segments(ctypes.byref(lat), 24, 2048) == 0       # no latent kernel for G = 24
+    short = _kv(B=2, H=2, L_max=32768, block=16, block_table=1)
+    assert L.sparsekv_segments(ctypes.byref(short), 4, 2048) == 0      # one sweep: the fused kernel
+    many = _kv(B=16, H=8, L_max=65536, block=16, block_table=1)
+    assert L.sparsekv_segments(ctypes.byref(many), 1, 2048) == 0       # 128 rows: own listing
+    big = 1 << 34
+    assert L.sparsekv_score_segments(ctypes.byref(gqa), P, 4, win, 0, P, P, big, None) == S.SKV_EINVAL
+    assert L.sparsekv_score_segments(ctypes.byref(gqa), P, 4, win, 4096, P, P, big,
+                                     None) == S.SKV_EUNSUPPORTED
+    assert L.sparsekv_score_segments(ctypes.byref(gqa), P, 4, win, 2048, P, P, 16,
+                                     None) == S.SKV_EWORKSPACE
+    assert L.sparsekv_select_attend_segments(ctypes.byref(gqa), P, 4, win, 131073, 0.1, P, P, P,
+                                             P, P, big, None) == S.SKV_EINVAL
+    assert L.sparsekv_select_attend_segments(ctypes.byref(short), P, 4, win, 2048, 0.1, P, P, P,
+                                             P, P, big, None) == S.SKV_EUNSUPPORTED
+    assert L.sparsekv_select_attend_segments(ctypes.byref(lat), P, 128, win, 2048, 0.1, P, P, P,
+                                             P, P, 16, None) == S.SKV_EWORKSPACE
+
+
 def test_compact_apply_validates_pool_size():
     L = S.lib()
     kv = _kv(B=1, H=1, L_max=64, block=16, token_table=1)

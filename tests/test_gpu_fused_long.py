@@ -329,3 +329,40 @@ def test_fused_token_pool_full_size_64_rows_over_every_head():
     st = W.make_token_pool()
     rows = [(b, (b + 4 * j) % 8) for b in range(32) for j in range(2)]
     assert _check_gqa(st, rows=rows) == 0
+
+
+def test_segment_pair_equals_the_one_call_step():
+    """The two halves of the segment path (sparsekv_score_segments, then
+    sparsekv_select_attend_segments) give what sparsekv_select_attend gives,
+    for GQA rows and for the latent step (the scan over the indexer's KV)."""
+    st = W.make_gqa_paged(tag=760, B=2, H=2, G=4, L=65536, k=2048, sink=4, local=64)
+    r = Run(st)
+    sc1, idx1, cnt1, out1 = r.select_attend()
+    kv = r.kv
+    assert S.sparsekv_segments(kv, st.G, st.k) > 0
+    ws = S.workspace(S.sparsekv_workspace_size(S.SKV_OP_SELECT_ATTEND, kv, st.G, st.k), DEV)
+    sc = torch.empty_like(sc1)
+    idx = torch.empty_like(idx1)
+    cnt = torch.empty_like(cnt1)
+    out = torch.empty_like(out1)
+    S.sparsekv_score_segments(kv, r.q, st.G, r.lo, r.hi, st.k, sc, ws)
+    S.sparsekv_select_attend_segments(kv, r.q, st.G, r.lo, r.hi, st.k, st.scale, sc, idx, cnt,
+                                      out, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(sc, sc1) and torch.equal(idx, idx1) and torch.equal(cnt, cnt1)
+    assert float((out - out1).abs().max()) <= ATTN_TOL
+    # latent: the scan over the indexer's keys, the selection from its segments
+    st = W.make_indexer_mla(tag=761, L=65536, k=2048, n_heads=64)
+    r = Run(st)
+    _, iidx, icnt, iout, _ = _indexer(r)
+    ws = S.workspace(S.sparsekv_workspace_size(S.SKV_OP_SELECT_ATTEND, r.kv, st.G, st.k), DEV)
+    sc = torch.empty((1, 1, 65536), dtype=torch.float32, device=DEV)
+    idx = torch.empty_like(iidx)
+    cnt = torch.empty_like(icnt)
+    out = torch.empty_like(iout)
+    S.sparsekv_score_segments(r.skv, r.sq, st.score_G, r.lo, r.hi, st.k, sc, ws)
+    S.sparsekv_select_attend_segments(r.kv, r.q, st.G, r.lo, r.hi, st.k, st.scale, sc, idx, cnt,
+                                      out, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, iidx) and torch.equal(cnt, icnt)
+    assert float((out - iout).abs().max()) <= ATTN_TOL

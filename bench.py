@@ -325,15 +325,18 @@ def roofline(kernel, bound, alg, seconds, traffic, extra=None):
 
 def stream_reference():
     """Streaming rates measured on this GPU, a second yardstick beside the
-    8 TB/s peak: the library's read probe over 2 GiB (reads only; best over
-    a few grid sizes) and torch's 1 GiB device copy (reads + writes), best
-    of 10 runs each."""
+    8 TB/s peak: the library's read probe over 2 GiB in grid-stride order
+    (reads only; plain and non-temporal loads, best over a few grid sizes),
+    the same 2 GiB as 4 KB pieces in a seeded random order (the access
+    pattern of a scan over a pool of 4 KB runs in permuted block order), and
+    torch's 1 GiB device copy (reads + writes), best of 10 runs each."""
     import torch
-    import sparse_top_kv_indexer_amd as S
     n = (2 << 30) // 4
     x = torch.ones(n, dtype=torch.float32, device="cuda")
     y = torch.empty(n // 2, dtype=torch.float32, device="cuda")
     sink = torch.empty(8192, dtype=torch.int32, device="cuda")
+    g = torch.Generator(device="cpu").manual_seed(12345)
+    order = torch.randperm((2 << 30) // 4096, generator=g).to(torch.int32).cuda()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
     def best(fn, nbytes):
@@ -349,13 +352,20 @@ def stream_reference():
         return nbytes / min(t) / 1e9
 
     from sparse_top_kv_indexer_amd import yardstick as Y
-    read = max(best(lambda: Y.read_probe(x, g, sink), 4 * n) for g in (1024, 2048, 4096, 8192))
+    grids = (1024, 2048, 4096, 8192)
+    plain = max(best(lambda: Y.read_probe(x, gr, sink), 4 * n) for gr in grids)
+    nt = max(best(lambda: Y.read_probe(x, gr, sink, nontemporal=True), 4 * n) for gr in grids)
+    pieces = max(best(lambda: Y.read_pieces(x, order, gr, sink), 4 * n) for gr in grids)
     copy = best(lambda: y.copy_(x[: n // 2]), 2 * 4 * (n // 2))
-    del x, y, sink
+    del x, y, sink, order
     torch.cuda.empty_cache()
-    return {"stream_read_GBps": read, "stream_copy_GBps": copy,
-            "stream_note": "skv_read_probe (libskv_yardstick) over 2 GiB (reads only, best grid of 1024..8192 "
-                           "workgroups) and a torch 1 GiB device copy (read + write), best of 10"}
+    return {"stream_read_GBps": max(plain, nt), "stream_read_plain_GBps": plain,
+            "stream_read_nontemporal_GBps": nt, "read_4k_pieces_random_GBps": pieces,
+            "stream_copy_GBps": copy,
+            "stream_note": "skv_read_probe_ex (libskv_yardstick) over 2 GiB in grid-stride order "
+                           "(reads only, plain and non-temporal loads, best grid of 1024..8192 "
+                           "workgroups); skv_read_pieces over the same 2 GiB as 4 KB pieces in a "
+                           "seeded random order; a torch 1 GiB device copy (read + write); best of 10"}
 
 
 def host_cpu():
@@ -1103,6 +1113,7 @@ def add_stream_reference(rec, ref):
         if ro and ro.get("bound") == "hbm" and ref:
             ro.update(ref)
             ro["frac_of_stream_read"] = ro["achieved"] / ref["stream_read_GBps"]
+            ro["frac_of_4k_pieces_read"] = ro["achieved"] / ref["read_4k_pieces_random_GBps"]
 
 
 def summary(rec):

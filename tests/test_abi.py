@@ -275,9 +275,13 @@ def test_yardstick_is_a_library_of_its_own():
     txt = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "skv_yardstick.h")).read(),
                  flags=re.S)
     names = sorted(set(re.findall(r"\b(skv_\w+)\s*\(", txt)))
-    assert names == ["skv_read_probe"]
+    assert names == ["skv_read_pieces", "skv_read_probe", "skv_read_probe_ex"]
     assert not hasattr(ctypes.CDLL(S.LIB_PATH), "sparsekv_read_probe")
     from sparse_top_kv_indexer_amd import yardstick as Y
     L = Y.lib()
     assert L.skv_read_probe(None, 16, 1, ctypes.c_void_p(1), None) == 1
     assert L.skv_read_probe(ctypes.c_void_p(1), 24, 1, ctypes.c_void_p(1), None) == 1
+    assert L.skv_read_probe_ex(ctypes.c_void_p(1), 24, 1, 1, ctypes.c_void_p(1), None) == 1
+    assert L.skv_read_pieces(ctypes.c_void_p(1), None, 4, 1, ctypes.c_void_p(1), None) == 1
+    assert L.skv_read_pieces(ctypes.c_void_p(1), ctypes.c_void_p(1), 0, 1, ctypes.c_void_p(1),
+                             None) == 1

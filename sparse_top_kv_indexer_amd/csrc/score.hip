@@ -97,15 +97,16 @@ __device__ __forceinline__ uint32_t window_key(float s, int t, int lo, int hi) {
 }
 
 // The segment's candidates (MODE 3), once lh holds the histogram of the
-// segment's window keys and sk their keys (sk[i]: token tok0 + i, i < n_tok,
-// 0 outside the window): the lowest bin cb such that the keys of cb and of
-// every bin above fit in m slots; the keys of bins >= cb, in position order,
-// go to slots [seg m, seg m + count) of row r; count and cut (cb << 20, or 0
-// when every window key was listed) to the segment's entries.
-__device__ __forceinline__ void seg_flush(const uint32_t* lh, const uint32_t* sk, int n_tok,
-                                          int tok0, const HistArgs& ha, int64_t r, int seg,
-                                          int* sh) {
-  lds_barrier();   // lh and sk are complete
+// segment's window keys and ss its scores (ss[i]: token tok0 + i, i < n_tok;
+// a token's key is window_key of its score, 0 outside [lo, hi)): the lowest
+// bin cb such that the keys of cb and of every bin above fit in m slots; the
+// keys of bins >= cb, in position order, go to slots [seg m, seg m + count)
+// of row r; count and cut (cb << 20, or 0 when every window key was listed)
+// to the segment's entries.
+__device__ __forceinline__ void seg_flush(const uint32_t* lh, const float* ss, int n_tok,
+                                          int tok0, int lo, int hi, const HistArgs& ha, int64_t r,
+                                          int seg, int* sh) {
+  lds_barrier();   // lh and ss are complete
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int m = ha.seg_m;
   int c[16], ts = 0;
@@ -123,11 +124,12 @@ __device__ __forceinline__ void seg_flush(const uint32_t* lh, const uint32_t* sk
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int i = 16 * threadIdx.x + 4 * u;
-    const uint4 v = i < n_tok ? ((const uint4*)sk)[4 * threadIdx.x + u] : make_uint4(0u, 0u, 0u, 0u);
-    kk[4 * u] = v.x;
-    kk[4 * u + 1] = i + 1 < n_tok ? v.y : 0u;
-    kk[4 * u + 2] = i + 2 < n_tok ? v.z : 0u;
-    kk[4 * u + 3] = i + 3 < n_tok ? v.w : 0u;
+    const float4 v = i < n_tok ? ((const float4*)ss)[4 * threadIdx.x + u] : make_float4(0.f, 0.f, 0.f, 0.f);
+    const int t = tok0 + i;
+    kk[4 * u] = i < n_tok ? window_key(v.x, t, lo, hi) : 0u;
+    kk[4 * u + 1] = i + 1 < n_tok ? window_key(v.y, t + 1, lo, hi) : 0u;
+    kk[4 * u + 2] = i + 2 < n_tok ? window_key(v.z, t + 2, lo, hi) : 0u;
+    kk[4 * u + 3] = i + 3 < n_tok ? window_key(v.w, t + 3, lo, hi) : 0u;
   }
   const int incl = wave_incl_scan(ts);
   if (lane == 63) sh[wave] = incl;
@@ -178,6 +180,26 @@ __device__ __forceinline__ void seg_flush(const uint32_t* lh, const uint32_t* sk
   if (threadIdx.x == 0) {
     ha.seg.seg_n()[r * kRowList + seg] = listed;
     ha.seg.seg_cut()[r * kRowList + seg] = cb ? cb << 20 : 0u;
+  }
+}
+
+// Write a row segment's n_tok scores, staged in LDS, to dst with one burst of
+// 16-byte stores: the same scores stored as each 16-key chunk is finished
+// (64 bytes per wave, spread over the whole scan between the key reads) cost
+// the L = 131,072 GQA scan 10 % and the token-pool scan 8 %; as one burst per
+// segment, about half of that.
+__device__ __forceinline__ void stage_out(const float* ss, float* dst, int n_tok) {
+  lds_barrier();   // every wave's scores are staged
+  if (((uintptr_t)dst & 15) == 0) {
+    for (int i = 4 * threadIdx.x; i < n_tok; i += 4 * kThreads) {
+      if (i + 4 <= n_tok) {
+        *(float4*)(dst + i) = *(const float4*)(ss + i);
+      } else {
+        for (int e = i; e < n_tok; ++e) dst[e] = ss[e];
+      }
+    }
+  } else {
+    for (int i = threadIdx.x; i < n_tok; i += kThreads) dst[i] = ss[i];
   }
 }
 
@@ -306,6 +328,7 @@ __global__ __launch_bounds__(kThreads) void score_valu_kernel(KvArgs kv, const v
 // of the segment with D chunks of loads in flight.  Lanes whose token is dead
 // load the query row instead (always valid memory) and their score is -inf.
 constexpr int kStageEntries = 4096;
+constexpr int kStageTok = kSegMaxKeys;   // staged scores per workgroup (HIST, SEG)
 
 //
 // VALU (G = 1): one query row is no contraction, so the same pipeline feeds
@@ -316,14 +339,18 @@ constexpr int kStageEntries = 4096;
 // MODE 1 adds the top-12-bit key histogram of the window (first digit of the
 // exact top-k); MODE 2 lists the window's keys whose score reaches the row's
 // predicted threshold (threshold-prefiltered top-k), staged in LDS and added
-// to the row's list with one atomic per workgroup and row segment.
+// to the row's list with one atomic per workgroup and row segment; MODE 3
+// lists the segment candidates (seg_flush).  In MODES 1 and 3 a row segment
+// is at most kStageTok tokens: its scores are staged in LDS and written in
+// one burst at its end (stage_out).
 template <int NC, int D, int GMAX, int MODE, bool VALU>
 __global__ __launch_bounds__(kThreads) void score_stream_kernel(KvArgs kv, const uint16_t* q, int G,
                                                                  float* scores, HistArgs ha,
                                                                  int cpr) {
   constexpr bool HIST = MODE == 1, SURV = MODE == 2, SEG = MODE == 3;
   __shared__ __attribute__((aligned(16))) uint32_t lh[(HIST || SEG) ? 4096 : 1];
-  __shared__ __attribute__((aligned(16))) uint32_t sk[SEG ? kSegMaxKeys : 1];   // window keys
+  // the row segment's scores (HIST, SEG), written out together at its end
+  __shared__ __attribute__((aligned(16))) float ss[(HIST || SEG) ? kStageTok : 1];
   __shared__ int seg_sh[SEG ? 12 : 1];
   __shared__ int32_t tab[kStageEntries];
   __shared__ uint32_t svk[SURV ? kSvCap : 1];
@@ -340,6 +367,7 @@ __global__ __launch_bounds__(kThreads) void score_stream_kernel(KvArgs kv, const
   const int mode = kv.token_table ? 2 : kv.block_table ? 1 : 0;   // token / block table / none
   const int per_chunk = mode == 2 ? 16 : 1;                        // staged entries per chunk
   if ((w1 - w0) * per_chunk > kStageEntries) return;               // the host never launches this
+  if ((HIST || SEG) && (w1 - w0) * 16 > kStageTok) return;          // nor this
 
   for (int64_t wu = w0; wu < w1;) {
     const int r = (int)(wu / cpr);
@@ -460,14 +488,18 @@ __global__ __launch_bounds__(kThreads) void score_stream_kernel(KvArgs kv, const
       const int t = (c_lo + i_lo + i) * 16 + n;
       const bool ok = key_row(i) >= 0;
       if (g4 == 0 && t < kv.L_max) {
-        srow[t] = ok ? sc : -INFINITY;
+        const float val = ok ? sc : -INFINITY;
+        if constexpr (HIST || SEG) {
+          ss[t - c_lo * 16] = val;
+        } else {
+          srow[t] = val;
+        }
         if constexpr (HIST) {
           if (ok) hist_add(lh, sc, t, wlo, whi);
         }
         if constexpr (SEG) {
           const uint32_t key = ok ? window_key(sc, t, wlo, whi) : 0u;
           if (key) atomicAdd(&lh[key >> 20], 1u);
-          sk[t - c_lo * 16] = key;
         }
         if constexpr (SURV) {
           uint32_t u = __float_as_uint(sc);
@@ -514,9 +546,11 @@ __global__ __launch_bounds__(kThreads) void score_stream_kernel(KvArgs kv, const
       for (int s = 0; s < D; ++s)
         if (s < n_w) finish(mfma(s), s);
     }
+    if constexpr (HIST || SEG)
+      stage_out(ss, srow + c_lo * 16, min(c_hi * 16, kv.L_max) - c_lo * 16);
     if constexpr (HIST) hist_flush(lh, hist_copy(ha, r));
     if constexpr (SEG)
-      seg_flush(lh, sk, min(c_hi * 16, kv.L_max) - c_lo * 16, c_lo * 16, ha, r,
+      seg_flush(lh, ss, min(c_hi * 16, kv.L_max) - c_lo * 16, c_lo * 16, wlo, whi, ha, r,
                 (int)blockIdx.x - r * ha.seg_s, seg_sh);
     if constexpr (SURV) {
       lds_barrier();
@@ -588,8 +622,9 @@ hipError_t launch_stream_k(const KvArgs& kv, const void* q, int G, float* scores
   const int cpr = (kv.L_max + 15) / 16;
   const int64_t n_work = (int64_t)kv.B * kv.H * cpr;
   // at least 16 chunks per workgroup and at most one workgroup per resident
-  // slot, unless a slice would then stage more table entries than fit in LDS
-  const int64_t cap = kStageEntries / (kv.token_table ? 16 : 1);
+  // slot, unless a slice would then stage more table entries (or, with the
+  // histogram, more scores) than fit in LDS
+  const int64_t cap = MODE == 1 ? kStageTok / 16 : kStageEntries / (kv.token_table ? 16 : 1);
   int64_t w = std::min<int64_t>(resident_wgs(kern, cache, 64), (n_work + 15) / 16);
   // each workgroup flushes its histogram of a row with one atomic per bin it
   // holds; few long rows spread over every resident workgroup would make

@@ -97,16 +97,15 @@ __device__ __forceinline__ uint32_t window_key(float s, int t, int lo, int hi) {
 }
 
 // The segment's candidates (MODE 3), once lh holds the histogram of the
-// segment's window keys and ss its scores (ss[i]: token tok0 + i, i < n_tok;
-// a token's key is window_key of its score, 0 outside [lo, hi)): the lowest
-// bin cb such that the keys of cb and of every bin above fit in m slots; the
-// keys of bins >= cb, in position order, go to slots [seg m, seg m + count)
-// of row r; count and cut (cb << 20, or 0 when every window key was listed)
-// to the segment's entries.
-__device__ __forceinline__ void seg_flush(const uint32_t* lh, const float* ss, int n_tok,
-                                          int tok0, int lo, int hi, const HistArgs& ha, int64_t r,
-                                          int seg, int* sh) {
-  lds_barrier();   // lh and ss are complete
+// segment's window keys and sk their keys (sk[i]: token tok0 + i, i < n_tok,
+// 0 outside the window): the lowest bin cb such that the keys of cb and of
+// every bin above fit in m slots; the keys of bins >= cb, in position order,
+// go to slots [seg m, seg m + count) of row r; count and cut (cb << 20, or 0
+// when every window key was listed) to the segment's entries.
+__device__ __forceinline__ void seg_flush(const uint32_t* lh, const uint32_t* sk, int n_tok,
+                                          int tok0, const HistArgs& ha, int64_t r, int seg,
+                                          int* sh) {
+  lds_barrier();   // lh and sk are complete
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int m = ha.seg_m;
   int c[16], ts = 0;
@@ -124,12 +123,11 @@ __device__ __forceinline__ void seg_flush(const uint32_t* lh, const float* ss, i
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int i = 16 * threadIdx.x + 4 * u;
-    const float4 v = i < n_tok ? ((const float4*)ss)[4 * threadIdx.x + u] : make_float4(0.f, 0.f, 0.f, 0.f);
-    const int t = tok0 + i;
-    kk[4 * u] = i < n_tok ? window_key(v.x, t, lo, hi) : 0u;
-    kk[4 * u + 1] = i + 1 < n_tok ? window_key(v.y, t + 1, lo, hi) : 0u;
-    kk[4 * u + 2] = i + 2 < n_tok ? window_key(v.z, t + 2, lo, hi) : 0u;
-    kk[4 * u + 3] = i + 3 < n_tok ? window_key(v.w, t + 3, lo, hi) : 0u;
+    const uint4 v = i < n_tok ? ((const uint4*)sk)[4 * threadIdx.x + u] : make_uint4(0u, 0u, 0u, 0u);
+    kk[4 * u] = v.x;
+    kk[4 * u + 1] = i + 1 < n_tok ? v.y : 0u;
+    kk[4 * u + 2] = i + 2 < n_tok ? v.z : 0u;
+    kk[4 * u + 3] = i + 3 < n_tok ? v.w : 0u;
   }
   const int incl = wave_incl_scan(ts);
   if (lane == 63) sh[wave] = incl;
@@ -329,6 +327,7 @@ __global__ __launch_bounds__(kThreads) void score_valu_kernel(KvArgs kv, const v
 // load the query row instead (always valid memory) and their score is -inf.
 constexpr int kStageEntries = 4096;
 constexpr int kStageTok = kSegMaxKeys;   // staged scores per workgroup (HIST, SEG)
+constexpr int kBurstTok = 1024;          // SEG: longer segments write their scores in one burst
 
 //
 // VALU (G = 1): one query row is no contraction, so the same pipeline feeds
@@ -340,9 +339,10 @@ constexpr int kStageTok = kSegMaxKeys;   // staged scores per workgroup (HIST, S
 // exact top-k); MODE 2 lists the window's keys whose score reaches the row's
 // predicted threshold (threshold-prefiltered top-k), staged in LDS and added
 // to the row's list with one atomic per workgroup and row segment; MODE 3
-// lists the segment candidates (seg_flush).  In MODES 1 and 3 a row segment
-// is at most kStageTok tokens: its scores are staged in LDS and written in
-// one burst at its end (stage_out).
+// lists the segment candidates (seg_flush), their keys kept in LDS.  In
+// MODES 1 and 3 a row segment is at most kStageTok tokens, and its scores
+// are staged in LDS and written in one burst at its end (stage_out) — in
+// MODE 3 only for segments over kBurstTok tokens.
 template <int NC, int D, int GMAX, int MODE, bool VALU>
 __global__ __launch_bounds__(kThreads) void score_stream_kernel(KvArgs kv, const uint16_t* q, int G,
                                                                  float* scores, HistArgs ha,
@@ -351,6 +351,7 @@ __global__ __launch_bounds__(kThreads) void score_stream_kernel(KvArgs kv, const
   __shared__ __attribute__((aligned(16))) uint32_t lh[(HIST || SEG) ? 4096 : 1];
   // the row segment's scores (HIST, SEG), written out together at its end
   __shared__ __attribute__((aligned(16))) float ss[(HIST || SEG) ? kStageTok : 1];
+  __shared__ __attribute__((aligned(16))) uint32_t sk[SEG ? kStageTok : 1];   // window keys (SEG)
   __shared__ int seg_sh[SEG ? 12 : 1];
   __shared__ int32_t tab[kStageEntries];
   __shared__ uint32_t svk[SURV ? kSvCap : 1];
@@ -376,6 +377,11 @@ __global__ __launch_bounds__(kThreads) void score_stream_kernel(KvArgs kv, const
     wu = (int64_t)r * cpr + c_hi;
     const int b = r / kv.H, h = r - b * kv.H;
     const int n_seg = c_hi - c_lo;
+    // HIST, and SEG over kBurstTok tokens: the segment's scores go out in one
+    // burst at its end.  Shorter SEG segments (one long row in 256 segments
+    // of 512 tokens, whose workgroups all end together) store them as they
+    // go: 12.5 against 13.1 us for that row's scan.
+    const bool burst = HIST || (SEG && n_seg * 16 > kBurstTok);
 
     lds_barrier();   // the previous segment is done with lh and tab
     if (mode == 1) {
@@ -489,8 +495,11 @@ __global__ __launch_bounds__(kThreads) void score_stream_kernel(KvArgs kv, const
       const bool ok = key_row(i) >= 0;
       if (g4 == 0 && t < kv.L_max) {
         const float val = ok ? sc : -INFINITY;
-        if constexpr (HIST || SEG) {
+        if constexpr (HIST) {
           ss[t - c_lo * 16] = val;
+        } else if constexpr (SEG) {
+          if (burst) ss[t - c_lo * 16] = val;
+          else srow[t] = val;
         } else {
           srow[t] = val;
         }
@@ -500,6 +509,7 @@ __global__ __launch_bounds__(kThreads) void score_stream_kernel(KvArgs kv, const
         if constexpr (SEG) {
           const uint32_t key = ok ? window_key(sc, t, wlo, whi) : 0u;
           if (key) atomicAdd(&lh[key >> 20], 1u);
+          sk[t - c_lo * 16] = key;
         }
         if constexpr (SURV) {
           uint32_t u = __float_as_uint(sc);
@@ -546,11 +556,10 @@ __global__ __launch_bounds__(kThreads) void score_stream_kernel(KvArgs kv, const
       for (int s = 0; s < D; ++s)
         if (s < n_w) finish(mfma(s), s);
     }
-    if constexpr (HIST || SEG)
-      stage_out(ss, srow + c_lo * 16, min(c_hi * 16, kv.L_max) - c_lo * 16);
+    if (burst) stage_out(ss, srow + c_lo * 16, min(c_hi * 16, kv.L_max) - c_lo * 16);
     if constexpr (HIST) hist_flush(lh, hist_copy(ha, r));
     if constexpr (SEG)
-      seg_flush(lh, ss, min(c_hi * 16, kv.L_max) - c_lo * 16, c_lo * 16, wlo, whi, ha, r,
+      seg_flush(lh, sk, min(c_hi * 16, kv.L_max) - c_lo * 16, c_lo * 16, ha, r,
                 (int)blockIdx.x - r * ha.seg_s, seg_sh);
     if constexpr (SURV) {
       lds_barrier();

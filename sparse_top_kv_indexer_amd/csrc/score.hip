@@ -182,16 +182,21 @@ __device__ __forceinline__ void seg_flush(const uint32_t* lh, const uint32_t* sk
 }
 
 // Write a row segment's n_tok scores, staged in LDS, to dst with one burst of
-// 16-byte stores: the same scores stored as each 16-key chunk is finished
-// (64 bytes per wave, spread over the whole scan between the key reads) cost
-// the L = 131,072 GQA scan 10 % and the token-pool scan 8 %; as one burst per
-// segment, about half of that.
+// non-temporal 16-byte stores: the same scores stored as each 16-key chunk
+// is finished (64 bytes per wave, spread over the whole scan between the key
+// reads) cost the L = 131,072 GQA scan 10 % and the token-pool scan 8 %; as
+// one burst per segment, about half of that (plain stores in the burst: the
+// token-pool scan 453 against 444 us).
 __device__ __forceinline__ void stage_out(const float* ss, float* dst, int n_tok) {
   lds_barrier();   // every wave's scores are staged
   if (((uintptr_t)dst & 15) == 0) {
     for (int i = 4 * threadIdx.x; i < n_tok; i += 4 * kThreads) {
       if (i + 4 <= n_tok) {
-        *(float4*)(dst + i) = *(const float4*)(ss + i);
+        const float4 v4 = *(const float4*)(ss + i);   // one non-temporal 16-byte store
+        __builtin_nontemporal_store(v4.x, dst + i);
+        __builtin_nontemporal_store(v4.y, dst + i + 1);
+        __builtin_nontemporal_store(v4.z, dst + i + 2);
+        __builtin_nontemporal_store(v4.w, dst + i + 3);
       } else {
         for (int e = i; e < n_tok; ++e) dst[e] = ss[e];
       }

@@ -202,13 +202,15 @@ void debug_validate(const skv_kv* kv, skv_window win, const int32_t* idx, int k,
   if (!flags) return;
   const size_t need = validate_ws(kv, idx ? k : 0);
   if (need > g_ws_bytes[dev]) {
-    if (g_ws[dev]) hipFree(g_ws[dev]);
+    if (g_ws[dev]) (void)hipFree(g_ws[dev]);   // a failure here only leaks the old buffer
     g_ws[dev] = nullptr;
     g_ws_bytes[dev] = 0;
     if (hipMalloc(&g_ws[dev], need) != hipSuccess) return;
     g_ws_bytes[dev] = need;
   }
-  launch_validate(kv, win, idx, idx ? k : 0, flags, g_ws[dev], st);
+  // a failed launch stays the thread's last HIP error, which the calling
+  // entry point's own launch check reports
+  (void)launch_validate(kv, win, idx, idx ? k : 0, flags, g_ws[dev], st);
 #else
   (void)kv; (void)win; (void)idx; (void)k; (void)st;
 #endif

@@ -219,16 +219,19 @@ skv_status sparsekv_gather_attend(const skv_kv* kv, const void* q, int32_t G, co
  * close-reading, section 一, Eqs. (1)-(3); ECHO-OSDI26 wiki page,
  * observation 5; vToken reading notes, section 3.4 Eq. (2)).
  * Supports bf16 keys and values with d_k == d_v == 128 and 1 <= G <= 8, any
- * L_max.  Rows of at most one 32768-slot sweep (L_max <= 32768, or 32765 when
- * L_max is not a multiple of 4) take the fused kernel; longer rows with
+ * L_max.  Fewer than 128 rows longer than 16384 slots with k <= 2048 take
+ * the scan that lists segment candidates and one kernel that selects each
+ * row from them and attends over it (8 workgroups per row, each finishing
+ * the selection and attending an eighth), then the split merge: the exact
+ * top-k of the candidates is the row's whenever no key a segment left out
+ * could rank among it, else the row is selected from its scores.  Other
+ * rows of at most one 32768-slot sweep (L_max <= 32768, or 32765 when L_max
+ * is not a multiple of 4) take the fused kernel; longer rows with
  * k <= 4096 take one kernel that selects each row and attends over it: with
  * 128 rows or more one workgroup per row lists the row's candidates itself
  * (one pass over its scores), selects and attends; with fewer, 8 workgroups
- * per row each finish the selection and attend an eighth, then the split
- * merge -- for k <= 2048 from candidates the scan itself lists (each scan
- * workgroup keeps its segment's highest keys; the exact top-k of those is
- * the row's whenever no key left out could rank among it, else the row is
- * selected from its scores), otherwise after a slice listing.  Larger k
+ * per row each finish the selection after a slice listing and attend an
+ * eighth, then the split merge.  Larger k
  * takes the slice listing, the finish, the split attention and its merge,
  * all inside the same call.  With one
  * query head per KV head (G == 1) a token's score is its attention logit
@@ -297,9 +300,10 @@ skv_status sparsekv_indexer_attend(const skv_kv* ikv, const void* iq, int32_t iG
  * (as sparsekv_score_hist and sparsekv_select_attend_resume are on the
  * histogram path).  sparsekv_segments(akv, aG, k) is the number of scan
  * segments per row the pair uses when the selecting half attends over akv
- * with aG query heads and top-k k -- rows longer than 32768 slots with
- * k <= 2048, a selecting kernel that supports the shape -- or 0 when the
- * pair does not apply (then use the histogram path).
+ * with aG query heads and top-k k -- k <= 2048 and a selecting kernel that
+ * supports the shape: fewer than 128 rows longer than 16384 slots for a GQA
+ * akv, rows longer than 32768 slots for a latent one -- or 0 when the pair
+ * does not apply (then use the histogram path).
  * sparsekv_score_segments(kv, q, G, win, k, scores, ws, ...): scores
  * [B][H][L_max] as sparsekv_score, and in ws, per row, the candidates of
  * each of its segments: the segment's highest window keys that fit its

@@ -263,9 +263,9 @@ skv_status sparsekv_select_attend(const skv_kv* kv, const void* q, int32_t G, sk
   debug_validate(kv, win, nullptr, 0, stream);
   uint32_t* hist = (uint32_t*)ws;
   float* part = (float*)((char*)ws + th);
-  // long rows: the scan lists segment candidates instead of the histogram,
-  // and the finishing kernel selects from them (no listing kernel)
-  if (!one_sweep && sparsekv_segments(kv, G, k) > 0) {
+  // few long rows: the scan lists segment candidates instead of the
+  // histogram, and the finishing kernel selects from them (no listing kernel)
+  if (sparsekv_segments(kv, G, k) > 0) {
     const skv_status st =
         sparsekv_score_segments(kv, q, G, win, k, scores, ws, ws_bytes, stream);
     if (st != SKV_OK) return st;
@@ -360,7 +360,7 @@ int32_t sparsekv_segments(const skv_kv* kv, int32_t G, int32_t k) {
   // 517 against 488 us with them (4,096 workgroups, each ending with the
   // segment's listing) and the selecting kernel 49.7 against 67.3 us
   const bool consumer = kv->v == nullptr ? mla_list_supported(a, G, k)
-                                         : finish_attend_supported(a, G, k) &&
+                                         : finish_attend_seg_supported(a, G, k) &&
                                                rows < kFinishAttendMinRows;
   return consumer ? topk_seg_count(rows, kv->L_max, k) : 0;
 }

@@ -386,7 +386,7 @@ __global__ __launch_bounds__(kThreads) void score_stream_kernel(KvArgs kv, const
     // burst at its end.  Shorter SEG segments (one long row in 256 segments
     // of 512 tokens, whose workgroups all end together) store them as they
     // go: 12.5 against 13.1 us for that row's scan.
-    const bool burst = HIST || (SEG && n_seg * 16 > kBurstTok);
+    const bool burst = HIST || (SEG && n_seg * 16 >= kBurstTok);
 
     lds_barrier();   // the previous segment is done with lh and tab
     if (mode == 1) {

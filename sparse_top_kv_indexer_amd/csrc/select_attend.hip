@@ -494,8 +494,14 @@ hipError_t launch_select_attend(const KvArgs& kv, const void* q, int G, const fl
 }
 
 bool finish_attend_supported(const KvArgs& kv, int G, int k) {
+  return finish_attend_seg_supported(kv, G, k) && row_slots_max(kv.L_max) > kSweep;
+}
+
+// The same kernel fed by the scan's segment candidates also serves rows of
+// one sweep.
+bool finish_attend_seg_supported(const KvArgs& kv, int G, int k) {
   return kv.bf16 && kv.v != nullptr && kv.d_k == kD && kv.d_v == kD && G >= 1 && G <= 8 &&
-         k >= 1 && k <= kFinishK && row_slots_max(kv.L_max) > kSweep && topk_supported(kv.L_max) &&
+         k >= 1 && k <= kFinishK && topk_supported(kv.L_max) &&
          topk_listing_slices(kv.B * kv.H, kv.L_max) <= kFinishSlices;
 }
 

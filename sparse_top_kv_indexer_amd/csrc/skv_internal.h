@@ -111,6 +111,7 @@ hipError_t launch_select_attend(const KvArgs& kv, const void* q, int G, const fl
 constexpr int kFinishAttendMinRows = 128;
 constexpr int kFinishSplitsFew = 8;
 bool finish_attend_supported(const KvArgs& kv, int G, int k);
+bool finish_attend_seg_supported(const KvArgs& kv, int G, int k);
 // n_seg > 0: the candidates are the segment candidates of a launch_score_seg
 // with n_seg = topk_seg_count(rows, L_max, k) segments per row (no histogram)
 hipError_t launch_finish_attend(const KvArgs& kv, const void* q, int G, const float* scores,

@@ -77,14 +77,16 @@ constexpr int kSegMax = 512;        // segments per row
 constexpr int kSegMaxK = 2048;      // k served (a quarter of the slots)
 
 // Segments per row for `rows` rows of L_max slots and k, or 0 when the
-// segment candidates do not serve the call: a power of two giving about 1024
-// workgroups in all, at most 256 unless a segment would exceed kSegMaxKeys
-// keys (one row of 131,072: 256 segments scanned in 12.0 us, 512 in 12.6).
+// segment candidates do not serve the call (rows of at most 16,384 slots):
+// a power of two giving about 512 workgroups in all (one per resident slot
+// of the scan), at most 256 unless a segment would exceed kSegMaxKeys keys
+// (one row of 131,072: 256 segments scanned in 12.0 us, 512 in 12.6; 32
+// rows of 32,768: 16 segments 54.8 us, 32 segments 56.4 us).
 inline int topk_seg_count(int rows, int L_max, int k) {
   const int64_t slots = L_max % 4 == 0 ? (int64_t)L_max : (int64_t)L_max + 3;
-  if (rows < 1 || k < 1 || k > kSegMaxK || slots <= 32768) return 0;
+  if (rows < 1 || k < 1 || k > kSegMaxK || slots <= 16384) return 0;
   int S = 256;
-  while (S > 1 && (int64_t)rows * S > 1024) S >>= 1;
+  while (S > 1 && (int64_t)rows * S > 512) S >>= 1;
   const int64_t cpr = ((int64_t)L_max + 15) / 16;
   while (S < kSegMax && cpr > (int64_t)S * (kSegMaxKeys / 16)) S <<= 1;
   return cpr <= (int64_t)S * (kSegMaxKeys / 16) ? S : 0;

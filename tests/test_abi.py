@@ -185,9 +185,10 @@ def test_indexer_attend_validates_before_any_launch():
 
 
 def test_segment_pair_applies_to_long_rows_and_validates_first():
-    """sparsekv_segments says where the segment path applies (long rows,
-    k <= 2048, a selecting kernel for the shape; GQA only below 128 rows);
-    both halves check their arguments before any launch."""
+    """sparsekv_segments says where the segment path applies (rows over
+    16384 slots, over 32768 for the latent kernel; k <= 2048; a selecting
+    kernel for the shape; GQA only below 128 rows); both halves check their
+    arguments before any launch."""
     L = S.lib()
     P = ctypes.c_void_p(1)
     win = S.skv_window(P, P)
@@ -197,8 +198,12 @@ def test_segment_pair_applies_to_long_rows_and_validates_first():
     assert L.sparsekv_segments(ctypes.byref(gqa), 4, 2049) == 0        # k above 2048
     assert L.sparsekv_segments(ctypes.byref(lat), 128, 2048) > 0
     assert L.sparsekv_segments(ctypes.byref(lat), 24, 2048) == 0       # no latent kernel for G = 24
-    short = _kv(B=2, H=2, L_max=32768, block=16, block_table=1)
-    assert L.sparsekv_segments(ctypes.byref(short), 4, 2048) == 0      # one sweep: the fused kernel
+    one_sweep = _kv(B=2, H=2, L_max=32768, block=16, block_table=1)
+    assert L.sparsekv_segments(ctypes.byref(one_sweep), 4, 2048) > 0
+    short = _kv(B=2, H=2, L_max=16384, block=16, block_table=1)
+    assert L.sparsekv_segments(ctypes.byref(short), 4, 2048) == 0      # the fused kernel
+    lat_sweep = _kv(B=1, H=1, L_max=32768, block=16, block_table=1, v=None, d_k=576, d_v=512)
+    assert L.sparsekv_segments(ctypes.byref(lat_sweep), 128, 2048) == 0   # top-k, then attention
     many = _kv(B=16, H=8, L_max=65536, block=16, block_table=1)
     assert L.sparsekv_segments(ctypes.byref(many), 1, 2048) == 0       # 128 rows: own listing
     big = 1 << 34

@@ -232,6 +232,29 @@ def test_fused_gqa_long_segments_crowded_by_a_run_of_top_keys():
     assert int(cnt[1, 1]) == 2048 and idx[1, 1].cpu().numpy().tolist() == list(range(10000, 12048))
 
 
+@pytest.mark.parametrize("G,L,k,run", [(4, 32768, 2048, 0), (2, 20000, 1000, 1500),
+                                       (1, 16400, 64, 0)])
+def test_fused_gqa_one_sweep_rows_take_segments(G, L, k, run):
+    """Few rows of one sweep but over 16384 slots also take the segment
+    candidates (the exact top-k of every row against the oracle); a run of
+    top-scoring tokens in row (1, 1) overflows its segments, so that row is
+    selected from its scores."""
+    st = W.make_gqa_paged(tag=770 + G, B=2, H=2, G=G, L=L, k=k, sink=4, local=64,
+                          seq_len=[L, L - 333])
+    if run:
+        qf = (st.q[1, G].astype(np.uint32) << 16).view(np.float32)   # head (h = 1, g = 0)
+        kb = (((qf * 4).view(np.uint32) + 0x8000) >> 16).astype(np.uint16)
+        blocks = st.kv.block_table[1]
+        for t in range(5000, 5000 + run):
+            st.kv.k[blocks[t // 16], 1, t % 16] = kb
+    r = Run(st)
+    assert S.sparsekv_segments(r.kv, G, k) > 0
+    assert _check_gqa(st) == 0
+    if run:
+        _, idx, cnt, _ = r.select_attend()
+        assert int(cnt[1, 1]) == k and idx[1, 1].cpu().numpy().tolist() == list(range(5000, 5000 + k))
+
+
 def test_fused_gqa_long_list_overflow_fallback():
     """Every key of sequence 0 ties: its list overflows and each attending
     workgroup selects from the row itself (lowest positions win)."""

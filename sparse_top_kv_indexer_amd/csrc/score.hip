@@ -663,18 +663,33 @@ hipError_t launch_stream_m(const KvArgs& kv, const void* q, int G, float* scores
   return launch_stream_k<NC, D, 16, MODE>(kv, q, G, scores, ha, s);
 }
 
+// Chunks in flight per wave: D, or at d = 128 two for the histogram with one
+// query head and for candidate segments of at least kBurstTok tokens.  Two
+// chunks leave the vector-ALU kernel (G = 1) 136 VGPRs, so three waves share
+// a SIMD instead of two: token-pool scan 443 -> 405 us; long GQA rows from
+// candidates 1-2 % faster.  The plain scan is faster with four (token pool
+// 463 against 523 us), and so are the MFMA histogram scan (by 1 us of 193)
+// and short latency-bound segments.
 template <int NC, int D>
 hipError_t launch_stream(const KvArgs& kv, const void* q, int G, float* scores, const HistArgs& ha,
                          hipStream_t s) {
+  constexpr int D2 = NC == 4 ? 2 : D;
   if (ha.seg_s > 0) {
-    if constexpr (NC <= 8) return launch_stream_m<NC, D, 3>(kv, q, G, scores, ha, s);
+    if constexpr (NC <= 8) {
+      const int64_t cpr = ((int64_t)kv.L_max + 15) / 16;
+      if (cpr / ha.seg_s * 16 >= kBurstTok) return launch_stream_m<NC, D2, 3>(kv, q, G, scores, ha, s);
+      return launch_stream_m<NC, D, 3>(kv, q, G, scores, ha, s);
+    }
     return hipErrorInvalidValue;
   }
   if (ha.lkey) {
     if constexpr (NC <= 8) return launch_stream_m<NC, D, 2>(kv, q, G, scores, ha, s);
     return hipErrorInvalidValue;
   }
-  if (ha.hist) return launch_stream_m<NC, D, 1>(kv, q, G, scores, ha, s);
+  if (ha.hist) {
+    if (G == 1) return launch_stream_m<NC, D2, 1>(kv, q, G, scores, ha, s);
+    return launch_stream_m<NC, D, 1>(kv, q, G, scores, ha, s);
+  }
   return launch_stream_m<NC, D, 0>(kv, q, G, scores, ha, s);
 }
 

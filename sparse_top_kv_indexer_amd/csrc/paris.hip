@@ -313,7 +313,9 @@ __global__ __launch_bounds__(256) void query_lut_kernel(const uint16_t* q, int G
 // The workgroup histograms its S values (32 bank-spread copies in LDS) and
 // writes the suffix counts ge[v] = #(S >= v), v = 0..97, of its chunk, which
 // it also adds into the head's totals.  A thread takes 4 entries per round
-// (8 rounds), the next round's loads in flight during the lookups: 8 entries
+// (8 rounds), the next round's loads in flight during the lookups; the ids
+// are read once, with non-temporal loads (each wave load is 1 KB of whole
+// lines; plain loads: retrieval 80.2 against 78 us).  8 entries
 // per round took 40 us against 37 us on 8 x 1M entries, and spreading a
 // wave's lookups over the 16 tables (ids rotated per lane so that lanes hit
 // different banks) cost more ALU than the bank conflicts it saved (41-52 us).
@@ -337,7 +339,7 @@ __global__ __launch_bounds__(256) void vote_kernel(const uint8_t* ids, int cap, 
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int i = i0 + u * 256 + tid;
-    cur[u] = i < n ? idrow[i] : u32x4_t{0, 0, 0, 0};
+    cur[u] = i < n ? __builtin_nontemporal_load(idrow + i) : u32x4_t{0, 0, 0, 0};
   }
   for (int i = tid; i < kVoteBins * 32; i += 256) vh[i] = 0u;
 #pragma unroll
@@ -353,7 +355,7 @@ __global__ __launch_bounds__(256) void vote_kernel(const uint8_t* ids, int cap, 
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int i = i0 + ((r + 1) * U + u) * 256 + tid;
-        nxt[u] = i < n ? idrow[i] : u32x4_t{0, 0, 0, 0};
+        nxt[u] = i < n ? __builtin_nontemporal_load(idrow + i) : u32x4_t{0, 0, 0, 0};
       }
     }
 #pragma unroll
@@ -521,7 +523,7 @@ __global__ __launch_bounds__(256) void cand_write_kernel(const uint8_t* votes, i
 // est_i = max_g fl(|q_g| * tree16_b fl(w_ib * tree8_j fl(v_ibj * q~_gbj))).
 // Grid (ceil(C / 256), H), 256 threads: a 16-lane group takes 16 consecutive
 // candidates, lane b holding subspace b of each (its codes word and weight,
-// one 8-byte load: a candidate's 16 lanes read one 128-byte line; with codes
+// one non-temporal 8-byte load: a candidate's 16 lanes read one 128-byte line; with codes
 // and weights in separate arrays each candidate cost two lines and the
 // kernel 14.6 us at C = 20,962 x 8 heads).  A nibble's signed level
 // comes from a 16-entry LDS table (one lookup instead of a compare/select
@@ -564,9 +566,9 @@ __global__ __launch_bounds__(256) void rerank_kernel(const uint32_t* cw, int cap
 #pragma unroll
   for (int u = 0; u < 16; ++u) {
     const int64_t ent = (int64_t)h * cap + __shfl(mine, base + u, 64);
-    const uint2 pr = ((const uint2*)cw)[ent * kSub + j];
-    code[u] = pr.x;
-    wb[u] = __uint_as_float(pr.y);
+    const uint64_t pr = __builtin_nontemporal_load((const uint64_t*)cw + ent * kSub + j);
+    code[u] = (uint32_t)pr;
+    wb[u] = __uint_as_float((uint32_t)(pr >> 32));
   }
   lds_barrier();   // vtab
   float x[G][16];

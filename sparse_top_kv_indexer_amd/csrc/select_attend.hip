@@ -124,7 +124,9 @@ __device__ __forceinline__ void attend_share(const KvArgs& kv, int G, int row, i
 #pragma unroll
       for (int t = 0; t < 16; ++t) {
         const int64_t rv = rows_sh[wave][u][t];
-        Vw[u][t] = rv >= 0 ? *(const uint32_t*)(vb + rv + 2 * lane) : 0u;
+        // one wave load per V row (its two whole lines), read once: non-temporal
+        // (token-pool select + attend 68.5 -> 67.3 us)
+        Vw[u][t] = rv >= 0 ? __builtin_nontemporal_load((const uint32_t*)(vb + rv + 2 * lane)) : 0u;
       }
     }
 #pragma unroll

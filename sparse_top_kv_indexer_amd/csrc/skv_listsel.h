@@ -381,7 +381,7 @@ __device__ __forceinline__ int local_list_select(const float* scores, int row, i
   const float* s = row_base(scores, (int64_t)row * L_max, w, &vec);
   const int n_sweeps = (w.ns + kSw - 1) / kSw;
   float va[NG][4], vb[NG][4];
-  if (n_sweeps > 0) row_load(s, w, vec, 0, va);
+  if (n_sweeps > 0) row_load<NG, true>(s, w, vec, 0, va);
 
   // 1. the bin of the k-th largest key; every key of the bins above it and of
   //    the bin itself is listed (lower = its first key)
@@ -445,10 +445,10 @@ __device__ __forceinline__ int local_list_select(const float* scores, int row, i
     base += all;
   };
   for (int sw = 0; sw < n_sweeps; sw += 2) {
-    if (sw + 1 < n_sweeps) row_load(s, w, vec, sw + 1, vb);
+    if (sw + 1 < n_sweeps) row_load<NG, true>(s, w, vec, sw + 1, vb);
     list_sweep(va, sw);
     if (sw + 1 < n_sweeps) {
-      if (sw + 2 < n_sweeps) row_load(s, w, vec, sw + 2, va);
+      if (sw + 2 < n_sweeps) row_load<NG, true>(s, w, vec, sw + 2, va);
       list_sweep(vb, sw + 1);
     }
   }

@@ -112,7 +112,19 @@ struct RowSelLds {
 // before the window end, so nothing past the row is read; that form compiles
 // to branches that wait for each group's load before issuing the next
 // (the token pool's listing: 26.0 us that way, 24.9 us with the first form).
-template <int NG>
+// NT: non-temporal loads, for a row this workgroup alone reads, once.
+template <bool NT>
+__device__ __forceinline__ float4 load_f4(const float* p) {
+  if constexpr (NT) {
+    typedef float f32x4n_t __attribute__((ext_vector_type(4)));
+    const f32x4n_t v = __builtin_nontemporal_load((const f32x4n_t*)p);
+    return make_float4(v.x, v.y, v.z, v.w);
+  } else {
+    return *(const float4*)p;
+  }
+}
+
+template <int NG, bool NT = false>
 __device__ __forceinline__ void slots_load(const float* s, const RowWindow& w, bool vec, int p0,
                                            float (&v)[NG][4]) {
   if (vec && w.whole) {
@@ -120,7 +132,7 @@ __device__ __forceinline__ void slots_load(const float* s, const RowWindow& w, b
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       const int p = p0 + 256 * g;
-      f[g] = p < w.ns ? *(const float4*)(s + p)
+      f[g] = p < w.ns ? load_f4<NT>(s + p)
                       : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
     }
 #pragma unroll
@@ -136,7 +148,7 @@ __device__ __forceinline__ void slots_load(const float* s, const RowWindow& w, b
   for (int g = 0; g < NG; ++g) {
     const int p = p0 + 256 * g;
     if (vec && p + 4 <= w.ns) {
-      const float4 f = *(const float4*)(s + p);
+      const float4 f = load_f4<NT>(s + p);
       v[g][0] = f.x;
       v[g][1] = f.y;
       v[g][2] = f.z;
@@ -162,10 +174,10 @@ __device__ __forceinline__ int row_slot0(int sw) {
 }
 
 // The slots p0 + 256 g + e of sweep sw for this lane (see the layout above).
-template <int NG>
+template <int NG, bool NT = false>
 __device__ __forceinline__ void row_load(const float* s, const RowWindow& w, bool vec, int sw,
                                          float (&v)[NG][4]) {
-  slots_load(s, w, vec, row_slot0<NG>(sw), v);
+  slots_load<NG, NT>(s, w, vec, row_slot0<NG>(sw), v);
 }
 
 template <int NG>

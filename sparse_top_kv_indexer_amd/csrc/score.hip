@@ -665,8 +665,8 @@ hipError_t launch_stream_m(const KvArgs& kv, const void* q, int G, float* scores
 
 // Chunks in flight per wave: D, or at d = 128 two for the histogram with one
 // query head and for candidate segments of at least kBurstTok tokens.  Two
-// chunks leave the vector-ALU kernel (G = 1) 136 VGPRs, so three waves share
-// a SIMD instead of two: token-pool scan 443 -> 405 us; long GQA rows from
+// chunks leave the vector-ALU kernel (G = 1) 149 VGPRs instead of 216, so
+// three waves share a SIMD instead of two: token-pool scan 443 -> 405 us; long GQA rows from
 // candidates 1-2 % faster.  The plain scan is faster with four (token pool
 // 463 against 523 us), and so are the MFMA histogram scan (by 1 us of 193)
 // and short latency-bound segments.

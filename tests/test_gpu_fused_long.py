@@ -389,3 +389,30 @@ def test_segment_pair_equals_the_one_call_step():
     torch.cuda.synchronize()
     assert torch.equal(idx, iidx) and torch.equal(cnt, icnt)
     assert float((out - iout).abs().max()) <= ATTN_TOL
+
+
+def test_scan_scores_at_an_unaligned_address():
+    """The scan stages a row segment's scores in LDS and writes them out with
+    16-byte stores when the row starts on a 16-byte boundary, one by one
+    otherwise: scores written 4 bytes past such a boundary equal the aligned
+    ones, on the histogram path and on the segment-candidate path."""
+    st = W.make_gqa_paged(tag=780, B=2, H=2, G=4, L=20000, k=500, sink=4, local=64,
+                          seq_len=[20000, 19001])
+    r = Run(st)
+    B, H, L = r.kv.B, r.kv.H, r.kv.L_max
+    n_ws = S.sparsekv_workspace_size(S.SKV_OP_SELECT_ATTEND, r.kv, st.G, st.k)
+    ref = torch.empty((B, H, L), dtype=torch.float32, device=DEV)
+    base = torch.full((B * H * L + 1,), 7.0, dtype=torch.float32, device=DEV)
+    odd = base[1:].view(B, H, L)
+    assert odd.data_ptr() % 16 == 4
+    ws = S.workspace(n_ws, DEV)
+    S.sparsekv_score_hist(r.kv, r.q, st.G, r.lo, r.hi, ref, ws)
+    ws.zero_()
+    S.sparsekv_score_hist(r.kv, r.q, st.G, r.lo, r.hi, odd, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(odd, ref) and float(base[0]) == 7.0
+    assert S.sparsekv_segments(r.kv, st.G, st.k) > 0
+    base.fill_(7.0)
+    S.sparsekv_score_segments(r.kv, r.q, st.G, r.lo, r.hi, st.k, odd, S.workspace(n_ws, DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(odd, ref) and float(base[0]) == 7.0
